@@ -1,0 +1,288 @@
+"""CPU oracle for the MXFP4 W4A4 linear layer with an online per-channel
+scale and a 32-element block Hadamard transform.
+
+TEST INFRASTRUCTURE ONLY.  Nothing in the library imports this module; only
+the test suite, the smoke check and the benchmark's CPU-baseline leg use it.
+It is a plain, slow, step-by-step restatement of what the layer computes,
+written from these sources (cited by page title and section):
+
+* [abstract]  "MACaQ: Fast, Model Agnostic Calibrated Quantization for
+  Low-Precision Weights and Activations" (Hugging Face Daily Papers mirror),
+  Abstract: a per-channel scale and a block-Hadamard transform are applied
+  online to each layer's activations; the inverse transforms are absorbed
+  into the weights.
+* [mechanism] "MACaQ Enables Streaming W4A4 Quantization with 32.5GB GPU
+  Memory" (zicq.com, English), section "Quantization mechanism: absorbing
+  online transforms into weights": the layer is y = x W^T; the transformed
+  weight is prepared offline; at inference the activation is scaled and
+  transformed, then goes through the FP4 matrix multiplication.
+* [mxfp4-def] "华为开源MACaQ:本地量化提速3倍" (openai-hub.com news),
+  section "量化不是单纯把模型“压小”": OCP MXFP4 splits data into groups of 32
+  elements sharing one E8M0 scale; each element is E2M1.
+* [block-32]  same article, section "MACaQ 真正解决的是跨层耦合": the
+  Hadamard rotation is an orthogonal add/subtract transform restricted to
+  32-element blocks that coincide with the MXFP4 scale groups; the inverse is
+  absorbed into the weights so the layer's external basis is unchanged.
+* [rtn]       "MACaQ Enables Streaming ..." section "Flip-Refinement":
+  round-to-nearest maps a value to the numerically closest FP4 code.
+
+Readings taken where the pages are silent (each is also listed in the
+design notes):
+
+* R1  y = (x diag(s) H)(W diag(1/s) H)^T with H the block-diagonal of K/32
+      normalized 32x32 Hadamards; the garbled printed form "y=(Hs)(HW^T)^T"
+      is read this way because it is the only form that keeps y = x W^T
+      while absorbing the inverses into W.
+* R2  H32 is the Sylvester Hadamard, H32[i][j] = (-1)^popcount(i & j),
+      natural order, no random signs; normalized by C = RNE_f32(1/sqrt(32)).
+* R3  order: t = fp32(x) * s (one fp32 rounding); then the unnormalized
+      butterfly with stages h = 1, 2, 4, 8, 16, lower index gets a + b and
+      upper index gets a - b (fp32, round-to-nearest-even, no fused
+      multiply-add); then x' = t * C (one rounding).
+* R7  E8M0 exponent: e = floor(log2(amax)) - 2 (2 = largest exponent of
+      E2M1), clamped to [-127, 127]; the stored byte is e + 127.  An all-zero
+      group stores 0.
+* R8  element rounding: nearest E2M1 value of |x'| / 2^e, ties to the value
+      with an even mantissa bit; R9: values above 6 saturate to 6;
+      R10: the sign bit is kept, also for values that round to zero.
+* R14 code = sign << 3 | magnitude index (0..7 -> 0, .5, 1, 1.5, 2, 3, 4, 6);
+      two codes per byte, the even element in the low nibble.
+* R15 row-major layouts: codes [rows][K/2], scales [rows][K/32].
+* R5  weights use r = fp32(1 / s) (IEEE division) in place of s.
+
+Floating-point arithmetic that decides a code (the transform) is done in
+fp32 exactly as stated above, because the codes must be bit-exact; the GEMM
+is the dequantized product in fp64.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+GROUP = 32
+
+# E2M1 magnitudes by 3-bit index (OCP MX v1.0 E2M1: bias 1, one subnormal).
+E2M1_VALUES = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0], dtype=np.float64)
+E2M1_EMAX = 2  # floor(log2(6))
+
+# Normalization of the 32-point Hadamard: 1/sqrt(32) rounded to fp32.
+C_NORM = np.float32(1.0 / np.sqrt(32.0))
+
+
+# --------------------------------------------------------------------------
+# transform  ([abstract], [mechanism], [block-32]; readings R1-R3)
+# --------------------------------------------------------------------------
+
+def sylvester_hadamard(n: int = GROUP) -> np.ndarray:
+    """Integer Sylvester Hadamard matrix of order n (a power of two), built by
+    the doubling recursion H_{2m} = [[H_m, H_m], [H_m, -H_m]]."""
+    h = np.ones((1, 1), dtype=np.int64)
+    while h.shape[0] < n:
+        h = np.block([[h, h], [h, -h]])
+    return h
+
+
+def fwht32(t: np.ndarray) -> np.ndarray:
+    """Unnormalized 32-point Walsh-Hadamard butterfly on the last axis (fp32).
+
+    Stages h = 1, 2, 4, 8, 16 in that order; in each stage every index i with
+    (i & h) == 0 is paired with i + h and the pair (a, b) becomes
+    (a + b, a - b).  Each add/subtract is one fp32 operation rounded to
+    nearest even.
+    """
+    assert t.dtype == np.float32 and t.shape[-1] == GROUP
+    t = t.copy()
+    for h in (1, 2, 4, 8, 16):
+        lo = [i for i in range(GROUP) if (i & h) == 0]
+        hi = [i + h for i in lo]
+        a = t[..., lo]
+        b = t[..., hi]
+        t[..., lo] = a + b
+        t[..., hi] = a - b
+    return t
+
+
+def transform(x_f32: np.ndarray, scale: np.ndarray) -> np.ndarray:
+    """x' = ((x * scale) H32) * C per 32-element group, in fp32 (R3).
+
+    x_f32: [R, K] float32 activations (or weights); scale: [R, K] or [K]
+    float32 per-channel factors (s for activations, fp32(1/s) for weights).
+    """
+    R, K = x_f32.shape
+    assert K % GROUP == 0
+    t = (x_f32 * scale).astype(np.float32)                 # one fp32 multiply
+    u = fwht32(t.reshape(R, K // GROUP, GROUP))
+    return (u * C_NORM).astype(np.float32).reshape(R, K)    # one fp32 multiply
+
+
+def transform_dense_fp64(x: np.ndarray, scale: np.ndarray) -> np.ndarray:
+    """The same transform in fp64 as a dense product with the block-diagonal
+    normalized Hadamard (R1, R2); independent of the butterfly."""
+    x = np.asarray(x, dtype=np.float64) * np.asarray(scale, dtype=np.float64)
+    R, K = x.shape
+    h = sylvester_hadamard(GROUP).astype(np.float64) / np.sqrt(float(GROUP))
+    return (x.reshape(R, K // GROUP, GROUP) @ h).reshape(R, K)
+
+
+# --------------------------------------------------------------------------
+# OCP MXFP4 quantization ([mxfp4-def], [rtn]; readings R7-R14)
+# --------------------------------------------------------------------------
+
+def e8m0_scale(amax: np.ndarray) -> np.ndarray:
+    """Shared-exponent byte of each group: floor(log2(amax)) - 2 + 127,
+    clamped to [0, 254]; 0 for an all-zero group (R7, R11, R12)."""
+    amax = np.asarray(amax, dtype=np.float64)
+    _, ex = np.frexp(amax)               # amax = m * 2^ex, m in [0.5, 1)
+    e = ex.astype(np.int64) - 1 - E2M1_EMAX
+    e = np.clip(e, -127, 127)
+    return np.where(amax > 0, e + 127, 0).astype(np.uint8)
+
+
+def e2m1_nearest(v: np.ndarray) -> np.ndarray:
+    """Index (0..7) of the E2M1 magnitude nearest to v >= 0; a tie goes to
+    the even index (even mantissa bit); values above 6 land on 6 (R8, R9)."""
+    v = np.asarray(v, dtype=np.float64)[..., None]
+    dist = np.abs(v - E2M1_VALUES)
+    best = dist == dist.min(axis=-1, keepdims=True)
+    even = (np.arange(8) % 2 == 0)
+    preference = best * np.where(even, 2, 1)
+    return preference.argmax(axis=-1).astype(np.uint8)
+
+
+def quantize_mxfp4(xp: np.ndarray) -> tuple[np.ndarray, np.ndarray]:
+    """Quantize fp32 rows x' [R, K] to packed E2M1 codes [R, K/2] and E8M0
+    scale bytes [R, K/32] (R7-R15)."""
+    assert xp.dtype == np.float32
+    R, K = xp.shape
+    g = xp.reshape(R, K // GROUP, GROUP)
+    amax = np.abs(g).max(axis=-1)
+    scales = e8m0_scale(amax)
+    # |x'| / 2^(b-127), computed as a multiply by an exact power of two in fp32
+    inv = np.ldexp(np.float32(1.0), 127 - scales.astype(np.int32)).astype(np.float32)
+    v = (np.abs(g) * inv[..., None]).astype(np.float32)
+    mag = e2m1_nearest(v)
+    code = (np.signbit(g).astype(np.uint8) << 3) | mag
+    code = code.reshape(R, K)
+    packed = (code[:, 0::2] | (code[:, 1::2] << 4)).astype(np.uint8)
+    return packed, scales
+
+
+def unpack_codes(packed: np.ndarray) -> np.ndarray:
+    """[R, K/2] bytes -> [R, K] 4-bit codes (even element in the low nibble)."""
+    R, H = packed.shape
+    out = np.empty((R, 2 * H), dtype=np.uint8)
+    out[:, 0::2] = packed & 0xF
+    out[:, 1::2] = packed >> 4
+    return out
+
+
+def dequantize_mxfp4(packed: np.ndarray, scales: np.ndarray) -> np.ndarray:
+    """Exact fp64 values of MXFP4 rows: (-1)^s * E2M1 * 2^(b - 127)."""
+    code = unpack_codes(packed)
+    R, K = code.shape
+    mag = E2M1_VALUES[code & 7]
+    sign = np.where(code & 8, -1.0, 1.0)
+    scale = np.ldexp(1.0, scales.astype(np.int64) - 127)
+    return (sign * mag).reshape(R, K // GROUP, GROUP).__mul__(scale[..., None]).reshape(R, K)
+
+
+# --------------------------------------------------------------------------
+# layer entry points ([mechanism], [abstract])
+# --------------------------------------------------------------------------
+
+def as_f32(x) -> np.ndarray:
+    """Activations/weights to fp32: bfloat16 bit patterns (uint16) are widened
+    exactly (bits << 16); float32 arrays pass through."""
+    x = np.asarray(x)
+    if x.dtype == np.uint16:
+        return (x.astype(np.uint32) << 16).view(np.float32)
+    assert x.dtype == np.float32, x.dtype
+    return x
+
+
+def expert_of_rows(offsets: np.ndarray, M: int) -> np.ndarray:
+    """Expert index of every row, from sorted row offsets [E+1]."""
+    offsets = np.asarray(offsets, dtype=np.int64)
+    rows = np.arange(M)
+    return np.searchsorted(offsets, rows, side="right") - 1
+
+
+def quant_act(x, s: np.ndarray, offsets=None) -> tuple[np.ndarray, np.ndarray]:
+    """Online activation path: x' = (x * s_e) H_blk, then MXFP4.
+
+    x: [M, K] bf16 bits (uint16) or float32; s: [E, K] float32;
+    offsets: [E+1] row offsets (rows sorted by expert), None for E = 1.
+    """
+    xf = as_f32(x)
+    s = np.asarray(s, dtype=np.float32).reshape(-1, xf.shape[1])
+    if offsets is None:
+        assert s.shape[0] == 1
+        row_scale = np.broadcast_to(s[0], xf.shape)
+    else:
+        row_scale = s[expert_of_rows(offsets, xf.shape[0])]
+    return quantize_mxfp4(transform(xf, row_scale))
+
+
+def weight_reciprocal(s: np.ndarray) -> np.ndarray:
+    """r = 1 / s as an IEEE fp32 division."""
+    s = np.asarray(s, dtype=np.float32)
+    return (np.float32(1.0) / s).astype(np.float32)
+
+
+def prepare_weights(w, s: np.ndarray) -> tuple[np.ndarray, np.ndarray]:
+    """Offline weights W' = quant(W diag(1/s) H_blk) for one expert.
+
+    w: [N, K] bf16 bits or float32; s: [K] float32.
+    Returns codes [N, K/2] and scales [N, K/32].
+    """
+    wf = as_f32(w)
+    r = weight_reciprocal(np.asarray(s).reshape(-1))
+    return quantize_mxfp4(transform(wf, np.broadcast_to(r, wf.shape)))
+
+
+def gemm(a_codes, a_scales, w_codes, w_scales, offsets=None):
+    """Dequantized fp64 product y = A' W'^T per expert.
+
+    a_*: [M, ...] activation codes/scales; w_*: [E, N, ...] or [N, ...].
+    Returns (y, S) with S = |A'| |W'|^T, the componentwise magnitude used to
+    bound floating-point accumulation error.
+    """
+    a = dequantize_mxfp4(a_codes, a_scales)
+    w_codes = np.asarray(w_codes)
+    w_scales = np.asarray(w_scales)
+    if w_codes.ndim == 2:
+        w_codes, w_scales = w_codes[None], w_scales[None]
+    E, N = w_codes.shape[:2]
+    M = a.shape[0]
+    if offsets is None:
+        offsets = np.array([0, M])
+    offsets = np.asarray(offsets, dtype=np.int64)
+    y = np.zeros((M, N), dtype=np.float64)
+    S = np.zeros((M, N), dtype=np.float64)
+    for e in range(E):
+        r0, r1 = int(offsets[e]), int(offsets[e + 1])
+        if r1 <= r0:
+            continue
+        we = dequantize_mxfp4(w_codes[e], w_scales[e])
+        y[r0:r1] = a[r0:r1] @ we.T
+        S[r0:r1] = np.abs(a[r0:r1]) @ np.abs(we).T
+    return y, S
+
+
+def linear(x, s, w_codes, w_scales, offsets=None):
+    """Whole online layer: quant_act, then the MXFP4 GEMM."""
+    ac, asc = quant_act(x, s, offsets)
+    return gemm(ac, asc, w_codes, w_scales, offsets)
+
+
+def within_tolerance(y: np.ndarray, y_ref: np.ndarray, S: np.ndarray, rtol: float = 1e-5):
+    """GEMM acceptance: |y - y_ref| <= rtol * S elementwise (S = 0 demands an
+    exact 0) and ||y - y_ref||_F <= rtol * ||y_ref||_F.  Returns (ok, worst
+    elementwise ratio, normwise ratio)."""
+    y = np.asarray(y, dtype=np.float64)
+    d = np.abs(y - y_ref)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        ratio = np.where(S > 0, d / np.where(S > 0, S, 1.0), np.where(d > 0, np.inf, 0.0))
+    worst = float(ratio.max()) if ratio.size else 0.0
+    nref = float(np.linalg.norm(y_ref))
+    normwise = float(np.linalg.norm(y - y_ref) / nref) if nref > 0 else float(np.linalg.norm(y))
+    return (worst <= rtol and normwise <= rtol), worst, normwise
