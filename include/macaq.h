@@ -1,0 +1,188 @@
+/*
+ * macaq.h — C ABI of the MXFP4 W4A4 linear layer with an online per-channel
+ * scale and a 32-element block Hadamard transform, for AMD Instinct MI355X
+ * (gfx950).
+ *
+ * What the layer computes (sources cited by page title and section):
+ *
+ *   y = x W^T                          "MACaQ Enables Streaming W4A4
+ *                                       Quantization with 32.5GB GPU Memory",
+ *                                       section "Quantization mechanism"
+ *   y = (x diag(s) H)(W diag(1/s) H)^T  same section (its printed formula is
+ *                                       garbled; this is the form that keeps
+ *                                       y = x W^T), and the abstract of "MACaQ:
+ *                                       Fast, Model Agnostic Calibrated
+ *                                       Quantization for Low-Precision Weights
+ *                                       and Activations": scale and block
+ *                                       Hadamard online on the activations,
+ *                                       inverses absorbed into the weights.
+ *   H = block-diagonal of K/32 normalized Sylvester 32x32 Hadamards, the
+ *       block equal to the MXFP4 scale group ("华为开源MACaQ:本地量化提速3倍",
+ *       section "MACaQ 真正解决的是跨层耦合").
+ *   Both operands are OCP MXFP4: 32-element groups, one E8M0 scale byte per
+ *       group, E2M1 elements (same article, section "量化不是单纯把模型“压小”").
+ *
+ * Exact arithmetic contract (shared by every entry point that quantizes):
+ *   per 32-element group along K, t = fp32(x) * s (fp32 multiply), then the
+ *   unnormalized butterfly with stages h = 1,2,4,8,16 (lower index a+b, upper
+ *   index a-b, fp32 round-to-nearest-even, no fused multiply-add), then
+ *   x' = t * C with C = fp32 0x3E3504F3 (1/sqrt(32)).
+ *   scale byte b = max(exponent_field(max|x'|) - 2, 0); element code =
+ *   sign<<3 | RNE(|x'| * 2^(127-b)) onto {0,.5,1,1.5,2,3,4,6} (ties to even
+ *   mantissa, saturating at 6, sign kept for zero).
+ *   Packed codes: two per byte, even K index in the low nibble.
+ *   Codes and scale bytes are bit-exact to that contract.
+ *
+ * Layouts (row-major, no padding):
+ *   activations x      [M][K]    bf16 or fp32, rows sorted by expert
+ *   per-channel s      [E][K]    fp32, finite and > 0
+ *   expert_offsets     [E+1]     int32, offsets[0] = 0, non-decreasing,
+ *                                offsets[E] = M (may be NULL when E == 1)
+ *   weights W          [E][N][K] bf16 or fp32
+ *   weight codes       [E][N][K/2]  uint8
+ *   weight scales      [E][N][K/32] uint8
+ *   activation codes   [M][K/2]     uint8
+ *   activation scales  [M][K/32]    uint8
+ *   output y           [M][N]    fp32
+ *
+ * Ownership and execution: every pointer argument except those documented
+ * as host pointers is a device pointer owned by the caller; the library
+ * never allocates device memory and keeps no per-call state.  Every call
+ * enqueues work on `stream` (a hipStream_t passed as void*, NULL = the
+ * default stream) and returns without synchronizing.  Outputs must not alias
+ * inputs.  Arguments are validated on the host before anything is launched;
+ * device-resident values (s > 0, sorted offsets, finite inputs) are
+ * preconditions that are not checked.
+ *
+ * Errors: a negative macaq_status.  macaq_last_error() returns a
+ * thread-local description of the most recent failure on that thread.
+ */
+#ifndef MACAQ_H
+#define MACAQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MACAQ_OK = 0,
+  MACAQ_ERR_INVALID_ARG = -1, /* null pointer, bad size, misaligned pointer */
+  MACAQ_ERR_UNSUPPORTED = -2, /* valid but not handled (dtype, K not a multiple of 128 for a GEMM) */
+  MACAQ_ERR_NO_DEVICE = -3,   /* no HIP device visible */
+  MACAQ_ERR_HIP = -4,         /* a HIP runtime call or a launch failed */
+  MACAQ_ERR_WORKSPACE = -5    /* workspace missing or too small */
+} macaq_status;
+
+typedef enum { MACAQ_BF16 = 0, MACAQ_F32 = 1 } macaq_dtype;
+
+/* flags of macaq_linear: which path computes the layer */
+enum {
+  MACAQ_PATH_AUTO = 0,    /* choose by M */
+  MACAQ_PATH_FUSED = 1,   /* decode path: transform + quantization inside the GEMM kernel */
+  MACAQ_PATH_UNFUSED = 2  /* macaq_quant_act into the workspace, then macaq_gemm */
+};
+
+/* Library version as major*10000 + minor*100 + patch. */
+int macaq_version(void);
+
+/* Static description of a status code (never NULL). */
+const char* macaq_status_string(int status);
+
+/* Thread-local description of the last failure on the calling thread ("" if none). */
+const char* macaq_last_error(void);
+
+/*
+ * Offline weight preparation W' = quant(W diag(1/s) H) ("Quantization
+ * mechanism": the transformed weight is prepared offline; abstract: the
+ * inverse transforms are absorbed into the weights).
+ * The per-channel factor is r = 1.0f / s[e][k] (IEEE fp32 division); the
+ * rest follows the arithmetic contract above.
+ *   w        [E][N][K] in w_dtype;  s [E][K] fp32
+ *   w_codes  [E][N][K/2] out;       w_scales [E][N][K/32] out
+ * Requires E >= 1, N >= 1, K >= 32, K % 32 == 0, w and w_codes 16-byte
+ * aligned.
+ */
+int macaq_prepare_weights(const void* w, macaq_dtype w_dtype, const float* s,
+                          int64_t E, int64_t N, int64_t K,
+                          uint8_t* w_codes, uint8_t* w_scales, void* stream);
+
+/*
+ * Online activation transform and MXFP4 quantization x' = (x diag(s_e) H),
+ * codes/scales of x' ("Quantization mechanism": at inference the activation
+ * is scaled and transformed before the FP4 matrix multiplication).
+ *   x [M][K] in x_dtype, rows sorted by expert; s [E][K] fp32;
+ *   expert_offsets [E+1] device int32 (NULL allowed when E == 1)
+ *   a_codes [M][K/2] out; a_scales [M][K/32] out
+ * Requires E >= 1, M >= 0, K >= 32, K % 32 == 0, x and a_codes 16-byte
+ * aligned.  M == 0 is a no-op.
+ */
+int macaq_quant_act(const void* x, macaq_dtype x_dtype, const float* s,
+                    const int32_t* expert_offsets, int64_t E, int64_t M, int64_t K,
+                    uint8_t* a_codes, uint8_t* a_scales, void* stream);
+
+/*
+ * MXFP4 x MXFP4 GEMM y = A' W'^T per expert ("Quantization mechanism": the
+ * FP4 matrix multiplication; "华为开源MACaQ:本地量化提速3倍", section
+ * "现在还不能把它当成通用量化工厂": dense and grouped W4A4 matmul).
+ * y[m][n] = sum_k a(m,k) w(e(m),n,k) with exact FP4 x FP4 products scaled by
+ * both E8M0 scales and accumulated in fp32 (the order of the fp32 sums is
+ * the kernel's; results are deterministic run to run).
+ *   a_codes [M][K/2], a_scales [M][K/32]; w_codes [E][N][K/2],
+ *   w_scales [E][N][K/32]; expert_offsets [E+1] device (NULL when E == 1);
+ *   y [M][N] fp32 out.
+ * workspace: device scratch of at least macaq_linear_workspace_bytes(M, N,
+ * K, E, MACAQ_PATH_UNFUSED) - macaq_quant_act_bytes(M, K) bytes (may be 0
+ * and NULL for the current kernels).
+ * Requires K % 128 == 0; K >= 128; all code pointers 16-byte aligned and
+ * scale pointers 4-byte aligned.
+ */
+int macaq_gemm(const uint8_t* a_codes, const uint8_t* a_scales,
+               const int32_t* expert_offsets, int64_t E,
+               const uint8_t* w_codes, const uint8_t* w_scales,
+               int64_t M, int64_t N, int64_t K, float* y,
+               void* workspace, size_t workspace_bytes, void* stream);
+
+/* Bytes of activation codes + scales for M rows of width K (M*K/2 + M*K/32),
+ * rounded up to 256-byte alignment of the scale part. */
+size_t macaq_quant_act_bytes(int64_t M, int64_t K);
+
+/*
+ * Device workspace needed by macaq_linear for this shape and flags.  0 means
+ * no workspace is needed (workspace may then be NULL).
+ */
+size_t macaq_linear_workspace_bytes(int64_t M, int64_t N, int64_t K, int64_t E, uint32_t flags);
+
+/*
+ * The whole online layer: y = quant(x diag(s_e) H) quant(W_e diag(1/s_e) H)^T
+ * with weights already prepared by macaq_prepare_weights.
+ *   x [M][K] (rows sorted by expert), s [E][K], expert_offsets [E+1] device
+ *   (NULL when E == 1), w_codes/w_scales as produced by
+ *   macaq_prepare_weights, y [M][N] fp32 out.
+ * flags: MACAQ_PATH_AUTO / _FUSED / _UNFUSED.  Both paths produce the same
+ * activation codes; y may differ between paths only by fp32 summation order.
+ * The fused path serves E == 1 and M <= 32.
+ * Requires the argument rules of macaq_quant_act and macaq_gemm and a
+ * workspace of macaq_linear_workspace_bytes(M, N, K, E, flags) bytes.
+ */
+int macaq_linear(const void* x, macaq_dtype x_dtype, const float* s,
+                 const int32_t* expert_offsets, int64_t E,
+                 const uint8_t* w_codes, const uint8_t* w_scales,
+                 int64_t M, int64_t N, int64_t K, float* y,
+                 void* workspace, size_t workspace_bytes, uint32_t flags, void* stream);
+
+/*
+ * Element encoder alone, for exhaustive tests of the E2M1 rounding: codes[i]
+ * = the 4-bit E2M1 code (sign<<3 | magnitude index) of v[i] with scale byte
+ * 127 (no scaling), by the same device routine the quantizing kernels use.
+ *   v [n] fp32 device in, codes [n] uint8 device out (one code per byte).
+ */
+int macaq_encode_e2m1(const float* v, int64_t n, uint8_t* codes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MACAQ_H */

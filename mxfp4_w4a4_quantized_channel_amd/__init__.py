@@ -1,0 +1,220 @@
+"""Python binding of libmacaq.so, the MI355X (gfx950) MXFP4 W4A4 linear layer
+with an online per-channel scale and a 32-element block Hadamard transform.
+
+The binding only marshals arguments: it checks tensor dtypes, devices,
+shapes and contiguity, allocates outputs with torch, and passes raw device
+pointers and torch's current HIP stream to the C ABI declared in
+include/macaq.h.  Every step of the layer runs in the library's HIP kernels;
+there is no fallback.  If the library is missing or fails to load, every
+call raises.
+
+Raw C entry points are available under their C names (``macaq_linear`` ...);
+the tensor-level functions below carry the same names without the prefix.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+__all__ = [
+    "lib", "MacaqError", "BF16", "F32", "PATH_AUTO", "PATH_FUSED", "PATH_UNFUSED",
+    "prepare_weights", "quant_act", "gemm", "linear", "linear_workspace_bytes",
+    "encode_e2m1", "version", "library_path",
+]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+library_path = os.path.join(_HERE, "libmacaq.so")
+
+BF16, F32 = 0, 1
+PATH_AUTO, PATH_FUSED, PATH_UNFUSED = 0, 1, 2
+STATUS = {0: "ok", -1: "invalid argument", -2: "unsupported", -3: "no device", -4: "HIP error",
+          -5: "workspace too small"}
+
+
+class MacaqError(RuntimeError):
+    def __init__(self, status: int, where: str, detail: str):
+        self.status = status
+        super().__init__(f"{where}: {STATUS.get(status, status)} ({detail})")
+
+
+_lib = None
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(library_path):
+        raise ImportError(f"{library_path} is missing: build it with "
+                          f"`python -c 'import __graft_entry__ as g; g.build()'` "
+                          f"or `python {os.path.join(_HERE, 'build.py')}`")
+    L = ctypes.CDLL(library_path)
+    vp, i64, u32, sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_uint32, ctypes.c_size_t
+    ci = ctypes.c_int
+    sig = {
+        "macaq_version": (ci, []),
+        "macaq_status_string": (ctypes.c_char_p, [ci]),
+        "macaq_last_error": (ctypes.c_char_p, []),
+        "macaq_prepare_weights": (ci, [vp, ci, vp, i64, i64, i64, vp, vp, vp]),
+        "macaq_quant_act": (ci, [vp, ci, vp, vp, i64, i64, i64, vp, vp, vp]),
+        "macaq_gemm": (ci, [vp, vp, vp, i64, vp, vp, i64, i64, i64, vp, vp, sz, vp]),
+        "macaq_quant_act_bytes": (sz, [i64, i64]),
+        "macaq_linear_workspace_bytes": (sz, [i64, i64, i64, i64, u32]),
+        "macaq_linear": (ci, [vp, ci, vp, vp, i64, vp, vp, i64, i64, i64, vp, vp, sz, u32, vp]),
+        "macaq_encode_e2m1": (ci, [vp, i64, vp, vp]),
+    }
+    for name, (res, args) in sig.items():
+        f = getattr(L, name)
+        f.restype = res
+        f.argtypes = args
+        globals()[name] = f
+    _lib = L
+    return L
+
+
+def lib():
+    """The loaded ctypes library (raises ImportError if it is not built)."""
+    return _load()
+
+
+def version() -> int:
+    return _load().macaq_version()
+
+
+def _check(status: int, where: str):
+    if status != 0:
+        detail = _load().macaq_last_error().decode(errors="replace")
+        raise MacaqError(status, where, detail)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device) -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return BF16
+    if t.dtype == torch.float32:
+        return F32
+    raise TypeError(f"activations/weights must be bfloat16 or float32, got {t.dtype}")
+
+
+def _need(t: torch.Tensor, name: str, dtype=None, dim=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if dim is not None and t.dim() != dim:
+        raise ValueError(f"{name} must have {dim} dims, got {t.dim()}")
+
+
+def prepare_weights(w: torch.Tensor, s: torch.Tensor):
+    """W' = quant(W diag(1/s) H) -> (codes [E,N,K/2] uint8, scales [E,N,K/32] uint8).
+
+    w: [N, K] or [E, N, K] bf16/fp32; s: [K] or [E, K] fp32.
+    """
+    _load()
+    if w.dim() == 2:
+        w = w[None]
+    if s.dim() == 1:
+        s = s[None]
+    _need(w, "w", dim=3)
+    _need(s, "s", torch.float32, 2)
+    E, N, K = w.shape
+    if tuple(s.shape) != (E, K):
+        raise ValueError(f"s must be [{E}, {K}], got {tuple(s.shape)}")
+    codes = torch.empty((E, N, K // 2), dtype=torch.uint8, device=w.device)
+    scales = torch.empty((E, N, K // 32), dtype=torch.uint8, device=w.device)
+    _check(macaq_prepare_weights(_ptr(w), _dtype_code(w), _ptr(s), E, N, K, _ptr(codes), _ptr(scales),
+                                 _stream(w.device)), "macaq_prepare_weights")
+    return codes, scales
+
+
+def quant_act(x: torch.Tensor, s: torch.Tensor, offsets: torch.Tensor | None = None):
+    """Online transform + MXFP4 of activations -> (codes [M,K/2], scales [M,K/32]).
+
+    x: [M, K] bf16/fp32 (rows sorted by expert); s: [K] or [E, K] fp32;
+    offsets: [E+1] int32 GPU tensor (None when E == 1).
+    """
+    _load()
+    if s.dim() == 1:
+        s = s[None]
+    _need(x, "x", dim=2)
+    _need(s, "s", torch.float32, 2)
+    M, K = x.shape
+    E = s.shape[0]
+    if offsets is not None:
+        _need(offsets, "offsets", torch.int32, 1)
+        if offsets.numel() != E + 1:
+            raise ValueError("offsets must have E+1 entries")
+    codes = torch.empty((M, K // 2), dtype=torch.uint8, device=x.device)
+    scales = torch.empty((M, K // 32), dtype=torch.uint8, device=x.device)
+    _check(macaq_quant_act(_ptr(x), _dtype_code(x), _ptr(s), _ptr(offsets), E, M, K, _ptr(codes),
+                           _ptr(scales), _stream(x.device)), "macaq_quant_act")
+    return codes, scales
+
+
+def _w_shape(w_codes, w_scales):
+    if w_codes.dim() == 2:
+        w_codes, w_scales = w_codes[None], w_scales[None]
+    _need(w_codes, "w_codes", torch.uint8, 3)
+    _need(w_scales, "w_scales", torch.uint8, 3)
+    return w_codes, w_scales
+
+
+def gemm(a_codes, a_scales, w_codes, w_scales, offsets=None, out=None):
+    """y = A' W'^T (fp32 [M, N]) from MXFP4 operands."""
+    _load()
+    w_codes, w_scales = _w_shape(w_codes, w_scales)
+    _need(a_codes, "a_codes", torch.uint8, 2)
+    _need(a_scales, "a_scales", torch.uint8, 2)
+    E, N, KH = w_codes.shape
+    M = a_codes.shape[0]
+    K = 2 * KH
+    y = out if out is not None else torch.empty((M, N), dtype=torch.float32, device=a_codes.device)
+    _check(macaq_gemm(_ptr(a_codes), _ptr(a_scales), _ptr(offsets), E, _ptr(w_codes), _ptr(w_scales),
+                      M, N, K, _ptr(y), None, 0, _stream(a_codes.device)), "macaq_gemm")
+    return y
+
+
+def linear_workspace_bytes(M, N, K, E=1, flags=PATH_AUTO) -> int:
+    return int(_load().macaq_linear_workspace_bytes(M, N, K, E, flags))
+
+
+def linear(x, s, w_codes, w_scales, offsets=None, flags=PATH_AUTO, out=None, workspace=None):
+    """The whole online layer y = quant(x diag(s) H) W'^T, fp32 [M, N]."""
+    _load()
+    if s.dim() == 1:
+        s = s[None]
+    w_codes, w_scales = _w_shape(w_codes, w_scales)
+    _need(x, "x", dim=2)
+    _need(s, "s", torch.float32, 2)
+    M, K = x.shape
+    E, N, _ = w_codes.shape
+    need = linear_workspace_bytes(M, N, K, E, flags)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
+    y = out if out is not None else torch.empty((M, N), dtype=torch.float32, device=x.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(macaq_linear(_ptr(x), _dtype_code(x), _ptr(s), _ptr(offsets), E, _ptr(w_codes), _ptr(w_scales),
+                        M, N, K, _ptr(y), _ptr(workspace), ws_bytes, flags, _stream(x.device)), "macaq_linear")
+    return y
+
+
+def encode_e2m1(v: torch.Tensor) -> torch.Tensor:
+    """E2M1 code (one per byte) of each fp32 value, by the library's encoder."""
+    _load()
+    _need(v, "v", torch.float32)
+    out = torch.empty(v.shape, dtype=torch.uint8, device=v.device)
+    _check(macaq_encode_e2m1(_ptr(v), v.numel(), _ptr(out), _stream(v.device)), "macaq_encode_e2m1")
+    return out

@@ -1,0 +1,230 @@
+// C ABI of the layer (declared in include/macaq.h): host-side argument
+// validation, workspace sizing and dispatch to the gfx950 kernels.
+// Validation happens before any HIP call, so argument errors are reported
+// the same way with or without a device.
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cstdio>
+#include <cstdlib>
+#include <string>
+
+#include "macaq.h"
+
+namespace macaq {
+hipError_t launch_act_quant(const void* x, bool x_f32, bool reciprocal, const float* s,
+                            const int32_t* offsets, int E, int64_t rows_per_expert, int64_t M,
+                            int64_t K, uint8_t* codes, uint8_t* scales, hipStream_t stream);
+hipError_t launch_encode_e2m1(const float* v, int64_t n, uint8_t* codes, hipStream_t stream);
+hipError_t launch_gemm(const uint8_t* A, const uint8_t* As, const int32_t* offsets, int E,
+                       const uint8_t* B, const uint8_t* Bs, int64_t M, int64_t N, int64_t K,
+                       float* Y, hipStream_t stream);
+hipError_t launch_linear_fused(const void* x, bool x_f32, const float* s, const uint8_t* B,
+                               const uint8_t* Bs, int64_t M, int64_t N, int64_t K, float* Y,
+                               void* workspace, size_t workspace_bytes, hipStream_t stream);
+size_t linear_fused_workspace_bytes(int64_t M, int64_t N, int64_t K);
+bool linear_fused_supported(int64_t M, int64_t N, int64_t K, int64_t E);
+}  // namespace macaq
+
+namespace {
+
+constexpr int kVersion = 10000;  // 1.0.0
+constexpr int64_t kMaxFusedM = 32;
+
+thread_local std::string g_last_error;
+
+int fail(int status, const std::string& what) {
+  g_last_error = what;
+  return status;
+}
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+std::atomic<int> g_device_ok{0};
+
+int check_device() {
+  if (g_device_ok.load(std::memory_order_relaxed)) return MACAQ_OK;
+  int n = 0;
+  const hipError_t e = hipGetDeviceCount(&n);
+  if (e != hipSuccess || n <= 0)
+    return fail(MACAQ_ERR_NO_DEVICE, std::string("no HIP device: ") +
+                                         (e == hipSuccess ? "device count is 0" : hipGetErrorString(e)));
+  g_device_ok.store(1, std::memory_order_relaxed);
+  return MACAQ_OK;
+}
+
+int hip_status(hipError_t e, const char* where) {
+  if (e == hipSuccess) return MACAQ_OK;
+  return fail(MACAQ_ERR_HIP, std::string(where) + ": " + hipGetErrorString(e));
+}
+
+size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+int check_dtype(macaq_dtype d, const char* name) {
+  if (d != MACAQ_BF16 && d != MACAQ_F32)
+    return fail(MACAQ_ERR_UNSUPPORTED, std::string(name) + ": dtype must be MACAQ_BF16 or MACAQ_F32");
+  return MACAQ_OK;
+}
+
+int check_k(int64_t K, const char* fn) {
+  if (K < 32 || K % 32 != 0)
+    return fail(MACAQ_ERR_INVALID_ARG, std::string(fn) + ": K must be a positive multiple of 32 (got " +
+                                           std::to_string(K) + ")");
+  return MACAQ_OK;
+}
+
+int validate_gemm(const uint8_t* a_codes, const uint8_t* a_scales, const int32_t* offsets, int64_t E,
+                  const uint8_t* w_codes, const uint8_t* w_scales, int64_t M, int64_t N, int64_t K,
+                  const float* y, const char* fn) {
+  if (E < 1) return fail(MACAQ_ERR_INVALID_ARG, std::string(fn) + ": E must be >= 1");
+  if (E > 1 && offsets == nullptr)
+    return fail(MACAQ_ERR_INVALID_ARG, std::string(fn) + ": expert_offsets required when E > 1");
+  if (M < 0 || N < 1) return fail(MACAQ_ERR_INVALID_ARG, std::string(fn) + ": need M >= 0 and N >= 1");
+  if (int st = check_k(K, fn)) return st;
+  if (K % 128 != 0)
+    return fail(MACAQ_ERR_UNSUPPORTED, std::string(fn) + ": K must be a multiple of 128 for the MFMA GEMM");
+  if (M > 0 && (!a_codes || !a_scales || !y))
+    return fail(MACAQ_ERR_INVALID_ARG, std::string(fn) + ": null activation or output pointer");
+  if (!w_codes || !w_scales) return fail(MACAQ_ERR_INVALID_ARG, std::string(fn) + ": null weight pointer");
+  if (!aligned(a_codes, 16) || !aligned(w_codes, 16))
+    return fail(MACAQ_ERR_INVALID_ARG, std::string(fn) + ": code pointers must be 16-byte aligned");
+  if (!aligned(a_scales, 4) || !aligned(w_scales, 4))
+    return fail(MACAQ_ERR_INVALID_ARG, std::string(fn) + ": scale pointers must be 4-byte aligned");
+  if (!aligned(y, 4)) return fail(MACAQ_ERR_INVALID_ARG, std::string(fn) + ": y must be 4-byte aligned");
+  if (M > INT32_MAX || N > INT32_MAX || E > 4096)
+    return fail(MACAQ_ERR_UNSUPPORTED, std::string(fn) + ": sizes beyond the supported range");
+  return MACAQ_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int macaq_version(void) { return kVersion; }
+
+const char* macaq_status_string(int status) {
+  switch (status) {
+    case MACAQ_OK: return "ok";
+    case MACAQ_ERR_INVALID_ARG: return "invalid argument";
+    case MACAQ_ERR_UNSUPPORTED: return "unsupported";
+    case MACAQ_ERR_NO_DEVICE: return "no device";
+    case MACAQ_ERR_HIP: return "HIP error";
+    case MACAQ_ERR_WORKSPACE: return "workspace too small";
+    default: return "unknown status";
+  }
+}
+
+const char* macaq_last_error(void) { return g_last_error.c_str(); }
+
+int macaq_prepare_weights(const void* w, macaq_dtype w_dtype, const float* s, int64_t E, int64_t N,
+                          int64_t K, uint8_t* w_codes, uint8_t* w_scales, void* stream) {
+  const char* fn = "macaq_prepare_weights";
+  if (int st = check_dtype(w_dtype, fn)) return st;
+  if (E < 1 || N < 1) return fail(MACAQ_ERR_INVALID_ARG, std::string(fn) + ": need E >= 1 and N >= 1");
+  if (int st = check_k(K, fn)) return st;
+  if (!w || !s || !w_codes || !w_scales) return fail(MACAQ_ERR_INVALID_ARG, std::string(fn) + ": null pointer");
+  if (!aligned(w, 16) || !aligned(w_codes, 16) || !aligned(s, 16))
+    return fail(MACAQ_ERR_INVALID_ARG, std::string(fn) + ": w, s and w_codes must be 16-byte aligned");
+  if (int st = check_device()) return st;
+  return hip_status(macaq::launch_act_quant(w, w_dtype == MACAQ_F32, true, s, nullptr, (int)E, N, E * N, K,
+                                            w_codes, w_scales, (hipStream_t)stream),
+                    fn);
+}
+
+int macaq_quant_act(const void* x, macaq_dtype x_dtype, const float* s, const int32_t* expert_offsets,
+                    int64_t E, int64_t M, int64_t K, uint8_t* a_codes, uint8_t* a_scales, void* stream) {
+  const char* fn = "macaq_quant_act";
+  if (int st = check_dtype(x_dtype, fn)) return st;
+  if (E < 1 || M < 0) return fail(MACAQ_ERR_INVALID_ARG, std::string(fn) + ": need E >= 1 and M >= 0");
+  if (E > 1 && expert_offsets == nullptr)
+    return fail(MACAQ_ERR_INVALID_ARG, std::string(fn) + ": expert_offsets required when E > 1");
+  if (int st = check_k(K, fn)) return st;
+  if (M == 0) return MACAQ_OK;
+  if (!x || !s || !a_codes || !a_scales) return fail(MACAQ_ERR_INVALID_ARG, std::string(fn) + ": null pointer");
+  if (!aligned(x, 16) || !aligned(a_codes, 16) || !aligned(s, 16))
+    return fail(MACAQ_ERR_INVALID_ARG, std::string(fn) + ": x, s and a_codes must be 16-byte aligned");
+  if (E > INT32_MAX) return fail(MACAQ_ERR_UNSUPPORTED, std::string(fn) + ": too many experts");
+  if (int st = check_device()) return st;
+  return hip_status(macaq::launch_act_quant(x, x_dtype == MACAQ_F32, false, s, E > 1 ? expert_offsets : nullptr,
+                                            (int)E, 0, M, K, a_codes, a_scales, (hipStream_t)stream),
+                    fn);
+}
+
+size_t macaq_quant_act_bytes(int64_t M, int64_t K) {
+  if (M <= 0 || K <= 0) return 0;
+  return round_up((size_t)M * (size_t)K / 2, 256) + round_up((size_t)M * (size_t)K / 32, 256);
+}
+
+size_t macaq_linear_workspace_bytes(int64_t M, int64_t N, int64_t K, int64_t E, uint32_t flags) {
+  if (M <= 0 || N <= 0 || K <= 0 || E <= 0) return 0;
+  const bool fused_ok = macaq::linear_fused_supported(M, N, K, E);
+  const bool fused = flags == MACAQ_PATH_FUSED || (flags == MACAQ_PATH_AUTO && fused_ok && M <= kMaxFusedM);
+  if (fused) return macaq::linear_fused_workspace_bytes(M, N, K);
+  return macaq_quant_act_bytes(M, K);
+}
+
+int macaq_gemm(const uint8_t* a_codes, const uint8_t* a_scales, const int32_t* expert_offsets, int64_t E,
+               const uint8_t* w_codes, const uint8_t* w_scales, int64_t M, int64_t N, int64_t K, float* y,
+               void* workspace, size_t workspace_bytes, void* stream) {
+  (void)workspace;
+  (void)workspace_bytes;
+  const char* fn = "macaq_gemm";
+  if (int st = validate_gemm(a_codes, a_scales, expert_offsets, E, w_codes, w_scales, M, N, K, y, fn)) return st;
+  if (M == 0) return MACAQ_OK;
+  if (int st = check_device()) return st;
+  return hip_status(macaq::launch_gemm(a_codes, a_scales, E > 1 ? expert_offsets : nullptr, (int)E, w_codes,
+                                       w_scales, M, N, K, y, (hipStream_t)stream),
+                    fn);
+}
+
+int macaq_linear(const void* x, macaq_dtype x_dtype, const float* s, const int32_t* expert_offsets, int64_t E,
+                 const uint8_t* w_codes, const uint8_t* w_scales, int64_t M, int64_t N, int64_t K, float* y,
+                 void* workspace, size_t workspace_bytes, uint32_t flags, void* stream) {
+  const char* fn = "macaq_linear";
+  if (int st = check_dtype(x_dtype, fn)) return st;
+  if (flags > MACAQ_PATH_UNFUSED) return fail(MACAQ_ERR_INVALID_ARG, std::string(fn) + ": unknown flags");
+  if (!x && M > 0) return fail(MACAQ_ERR_INVALID_ARG, std::string(fn) + ": null x");
+  if (!s) return fail(MACAQ_ERR_INVALID_ARG, std::string(fn) + ": null s");
+  if (M > 0 && (!aligned(x, 16) || !aligned(s, 16)))
+    return fail(MACAQ_ERR_INVALID_ARG, std::string(fn) + ": x and s must be 16-byte aligned");
+  // the GEMM's rules (E, offsets, K, weights, y); activation buffers are internal
+  const uint8_t* dummy = reinterpret_cast<const uint8_t*>(w_codes);
+  if (int st = validate_gemm(dummy, w_scales, expert_offsets, E, w_codes, w_scales, M, N, K, y, fn)) return st;
+  if (M == 0) return MACAQ_OK;
+  const bool fused_ok = macaq::linear_fused_supported(M, N, K, E);
+  if (flags == MACAQ_PATH_FUSED && !fused_ok)
+    return fail(MACAQ_ERR_UNSUPPORTED, std::string(fn) + ": the fused path serves E == 1 and M <= 32");
+  const bool fused = flags == MACAQ_PATH_FUSED || (flags == MACAQ_PATH_AUTO && fused_ok && M <= kMaxFusedM);
+  const size_t need = fused ? macaq::linear_fused_workspace_bytes(M, N, K) : macaq_quant_act_bytes(M, K);
+  if (need > 0 && (workspace == nullptr || workspace_bytes < need))
+    return fail(MACAQ_ERR_WORKSPACE, std::string(fn) + ": workspace of " + std::to_string(need) +
+                                         " bytes required, got " + std::to_string(workspace_bytes));
+  if (need > 0 && !aligned(workspace, 256))
+    return fail(MACAQ_ERR_INVALID_ARG, std::string(fn) + ": workspace must be 256-byte aligned");
+  if (int st = check_device()) return st;
+  hipStream_t st = (hipStream_t)stream;
+  if (fused)
+    return hip_status(macaq::launch_linear_fused(x, x_dtype == MACAQ_F32, s, w_codes, w_scales, M, N, K, y,
+                                                 workspace, workspace_bytes, st),
+                      "macaq_linear (fused)");
+  uint8_t* a_codes = static_cast<uint8_t*>(workspace);
+  uint8_t* a_scales = a_codes + round_up((size_t)M * (size_t)K / 2, 256);
+  const int32_t* off = E > 1 ? expert_offsets : nullptr;
+  if (int r = hip_status(macaq::launch_act_quant(x, x_dtype == MACAQ_F32, false, s, off, (int)E, 0, M, K,
+                                                 a_codes, a_scales, st),
+                         "macaq_linear (transform)"))
+    return r;
+  return hip_status(macaq::launch_gemm(a_codes, a_scales, off, (int)E, w_codes, w_scales, M, N, K, y, st),
+                    "macaq_linear (gemm)");
+}
+
+int macaq_encode_e2m1(const float* v, int64_t n, uint8_t* codes, void* stream) {
+  const char* fn = "macaq_encode_e2m1";
+  if (n < 0) return fail(MACAQ_ERR_INVALID_ARG, std::string(fn) + ": n must be >= 0");
+  if (n == 0) return MACAQ_OK;
+  if (!v || !codes) return fail(MACAQ_ERR_INVALID_ARG, std::string(fn) + ": null pointer");
+  if (int st = check_device()) return st;
+  return hip_status(macaq::launch_encode_e2m1(v, n, codes, (hipStream_t)stream), fn);
+}
+
+}  // extern "C"

@@ -1,0 +1,113 @@
+"""The C ABI library loads, exports every function include/macaq.h declares,
+and validates arguments on the host (no GPU needed: nothing is launched)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import mxfp4_w4a4_quantized_channel_amd as mx
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "macaq.h")
+
+OK, INVALID, UNSUPPORTED, NO_DEVICE, HIPERR, WORKSPACE = 0, -1, -2, -3, -4, -5
+A16 = 0x10000  # a fake, 256-byte aligned, non-null "device pointer" (never dereferenced)
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(macaq_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for n in ["macaq_prepare_weights", "macaq_quant_act", "macaq_linear", "macaq_gemm",
+              "macaq_linear_workspace_bytes", "macaq_status_string", "macaq_last_error", "macaq_version"]:
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    L = mx.lib()
+    for n in declared_functions():
+        assert hasattr(L, n), n
+    out = os.popen(f"nm -D --defined-only {mx.library_path}").read()
+    for n in declared_functions():
+        assert re.search(rf"\bT {n}\b", out), n
+
+
+def test_version_and_status_strings():
+    assert mx.version() == 10000
+    L = mx.lib()
+    for code in (OK, INVALID, UNSUPPORTED, NO_DEVICE, HIPERR, WORKSPACE, 12345):
+        assert isinstance(L.macaq_status_string(code), bytes)
+    assert L.macaq_status_string(WORKSPACE) == b"workspace too small"
+
+
+def qa(x=A16, dt=0, s=A16, off=None, E=1, M=4, K=64, c=A16, sc=A16):
+    return mx.macaq_quant_act(x, dt, s, off, E, M, K, c, sc, None)
+
+
+def test_quant_act_validation():
+    mx.lib()
+    assert qa(K=48) == INVALID           # K % 32 != 0
+    assert qa(K=0) == INVALID
+    assert qa(E=0) == INVALID
+    assert qa(M=-1) == INVALID
+    assert qa(E=2, off=None) == INVALID  # offsets needed for E > 1
+    assert qa(x=None) == INVALID
+    assert qa(x=A16 + 2) == INVALID      # misaligned
+    assert qa(dt=7) == UNSUPPORTED
+    assert qa(M=0) == OK                 # no-op, no device touched
+    assert b"K must be" in (mx.lib().macaq_quant_act(A16, 0, A16, None, 1, 4, 40, A16, A16, None) and
+                            mx.macaq_last_error())
+
+
+def gm(a=A16, asc=A16, off=None, E=1, w=A16, ws=A16, M=4, N=8, K=256, y=A16):
+    return mx.macaq_gemm(a, asc, off, E, w, ws, M, N, K, y, None, 0, None)
+
+
+def test_gemm_validation():
+    mx.lib()
+    assert gm(K=96) == UNSUPPORTED       # multiple of 32 but not of 128
+    assert gm(K=100) == INVALID
+    assert gm(N=0) == INVALID
+    assert gm(w=None) == INVALID
+    assert gm(a=A16 + 8) == INVALID
+    assert gm(asc=A16 + 1) == INVALID
+    assert gm(E=3) == INVALID            # no offsets
+    assert gm(M=0) == OK
+
+
+def test_linear_validation_and_workspace():
+    L = mx.lib()
+    need = L.macaq_linear_workspace_bytes(64, 128, 256, 1, mx.PATH_UNFUSED)
+    assert need == L.macaq_quant_act_bytes(64, 256) > 0
+    assert L.macaq_quant_act_bytes(64, 256) >= 64 * 256 * 17 // 32
+    r = mx.macaq_linear(A16, 0, A16, None, 1, A16, A16, 64, 128, 256, A16, A16, need - 1,
+                        mx.PATH_UNFUSED, None)
+    assert r == WORKSPACE
+    r = mx.macaq_linear(A16, 0, A16, None, 1, A16, A16, 64, 128, 256, A16, None, 0,
+                        mx.PATH_UNFUSED, None)
+    assert r == WORKSPACE
+    r = mx.macaq_linear(A16, 0, A16, None, 1, A16, A16, 64, 128, 256, A16, A16, need, 9, None)
+    assert r == INVALID
+
+
+def test_prepare_weights_validation():
+    mx.lib()
+    pw = mx.macaq_prepare_weights
+    assert pw(A16, 0, A16, 1, 8, 33, A16, A16, None) == INVALID
+    assert pw(A16, 0, A16, 0, 8, 64, A16, A16, None) == INVALID
+    assert pw(None, 0, A16, 1, 8, 64, A16, A16, None) == INVALID
+    assert pw(A16, 3, A16, 1, 8, 64, A16, A16, None) == UNSUPPORTED
+
+
+def test_valid_calls_without_a_device_report_no_device():
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a device is present")
+    assert qa() == NO_DEVICE
+    assert gm() == NO_DEVICE
+    assert b"no HIP device" in mx.lib().macaq_last_error()

@@ -1,0 +1,245 @@
+"""Parity of the HIP path (through the C ABI) with the CPU oracle.
+
+Codes and scale bytes must be bit-exact.  GEMM / layer outputs must satisfy
+|y - y_ref| <= 1e-5 * S elementwise, S = sum_k |a_k w_k| of the dequantized
+operands (the componentwise bound of an fp32 dot product of exact FP4
+products), and ||y - y_ref||_F <= 1e-5 ||y_ref||_F.
+
+Small cases are compared element by element; full-size workloads on sampled
+rows / outputs that the oracle computes one by one.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+import mxfp4_w4a4_quantized_channel_amd as mx
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+RTOL = 1e-5
+
+
+def host(t: torch.Tensor) -> np.ndarray:
+    t = t.detach().cpu().contiguous()
+    if t.dtype == torch.bfloat16:
+        return workloads.bf16_bits(t)
+    return t.numpy()
+
+
+def say(msg):
+    print(f"[case] {msg}", flush=True)
+
+
+def assert_codes(got, want, values):
+    bad = np.nonzero(got != want)[0]
+    if bad.size:
+        rows = [f"v={values[i]!r} bits=0x{np.float32(values[i]).view(np.uint32):08x} got={got[i]} want={want[i]}"
+                for i in bad[:12]]
+        raise AssertionError(f"{bad.size} mismatches:\n" + "\n".join(rows))
+
+
+def gpu_prepare(wl):
+    return mx.prepare_weights(wl.w.to(DEV), wl.s.to(DEV))
+
+
+def oracle_prepare(wl, e, rows=None):
+    w = host(wl.w[e])
+    if rows is not None:
+        w = w[rows]
+    return oracle.prepare_weights(w, wl.s[e].numpy())
+
+
+# ------------------------------------------------------------ element encoder
+
+def test_encode_e2m1_exhaustive():
+    """Every fp32 in [0.25, 8) and its negation, denormals, zeros, large values."""
+    say("encode_e2m1 exhaustive [0.25, 8)")
+    lo = int(np.float32(0.25).view(np.uint32))
+    hi = int(np.float32(8.0).view(np.uint32))
+    bits = np.arange(lo, hi, dtype=np.uint32)
+    v = bits.view(np.float32)
+    got = mx.encode_e2m1(torch.from_numpy(v).to(DEV)).cpu().numpy()
+    want = oracle.e2m1_nearest(v)
+    assert_codes(got, want, v)
+    got_neg = mx.encode_e2m1(torch.from_numpy(-v).to(DEV)).cpu().numpy()
+    assert_codes(got_neg, want | 8, -v)
+    rng = np.random.default_rng(0)
+    extra = np.concatenate([
+        rng.integers(0, lo, 200000, dtype=np.uint32).view(np.float32),       # tiny incl. denormals
+        np.array([0.0, -0.0, 8.0, 100.0, 6.0, 5.0, 7.0, 3.4e38], np.float32),
+        -rng.integers(0, lo, 200000, dtype=np.uint32).view(np.float32),
+    ]).astype(np.float32)
+    got = mx.encode_e2m1(torch.from_numpy(extra).to(DEV)).cpu().numpy()
+    want = oracle.e2m1_nearest(np.abs(extra)) | (np.signbit(extra).astype(np.uint8) << 3)
+    assert_codes(got, want, extra)
+
+
+# ------------------------------------------------------------ activation transform + quant
+
+SMALL_ACT = [
+    ("tiny fp32", dict(cfg=1)),
+    ("cfg2-shaped ragged K", dict(cfg=2, shape=(37, 64, 1312))),
+    ("cfg3-shaped t4", dict(cfg=3, shape=(19, 64, 2048))),
+    ("cfg4-shaped M1", dict(cfg=4, shape=(1, 64, 5120))),
+    ("cfg5 token routing", dict(cfg=5, shape=(300, 32, 256), routing="token_zipf")),
+    ("cfg5 expert routing", dict(cfg=5, shape=(333, 32, 256))),
+    ("literal scale rule", dict(cfg=2, shape=(9, 64, 512), scale_rule="literal")),
+]
+
+
+@pytest.mark.parametrize("name,kw", SMALL_ACT, ids=[n for n, _ in SMALL_ACT])
+def test_quant_act_bit_exact(name, kw):
+    say(f"quant_act {name}")
+    wl = workloads.make(**kw)
+    off = wl.offsets.to(DEV) if wl.E > 1 else None
+    codes, scales = mx.quant_act(wl.x.to(DEV), wl.s.to(DEV), off)
+    rc, rs = oracle.quant_act(host(wl.x), wl.s.numpy(), wl.offsets.numpy() if wl.E > 1 else None)
+    assert np.array_equal(scales.cpu().numpy(), rs)
+    assert np.array_equal(codes.cpu().numpy(), rc)
+
+
+def test_quant_act_empty_is_noop():
+    say("quant_act M=0")
+    x = torch.empty((0, 256), dtype=torch.bfloat16, device=DEV)
+    codes, scales = mx.quant_act(x, torch.ones(256, device=DEV))
+    assert codes.shape == (0, 128) and scales.shape == (0, 8)
+
+
+def test_quant_act_special_groups():
+    """Spike, constant, zero, signed zero, saturation and tie groups."""
+    say("quant_act special groups")
+    K = 32 * 8
+    x = np.zeros((4, K), np.float32)
+    x[0, 0:32] = 0.0
+    x[0, 32 + 5] = 6.0
+    x[0, 64:96] = 0.25
+    x[0, 96:128] = -0.0
+    x[0, 128:160] = np.linspace(-3, 3, 32)
+    x[0, 160:192] = 3.0e38 / 64
+    x[0, 192:224] = 1e-40  # denormal inputs
+    x[1] = np.random.default_rng(1).standard_normal(K) * 1e-30
+    x[2] = np.random.default_rng(2).standard_normal(K) * 1e30
+    x[3, ::7] = -1.0
+    s = np.ones((1, K), np.float32)
+    codes, scales = mx.quant_act(torch.from_numpy(x).to(DEV), torch.from_numpy(s).to(DEV))
+    rc, rs = oracle.quant_act(x, s)
+    assert np.array_equal(scales.cpu().numpy(), rs)
+    assert np.array_equal(codes.cpu().numpy(), rc)
+
+
+# ------------------------------------------------------------ weight preparation
+
+SMALL_W = [
+    ("tiny fp32", dict(cfg=1)),
+    ("cfg2-shaped", dict(cfg=2, shape=(8, 200, 1024))),
+    ("cfg5 experts", dict(cfg=5, shape=(64, 48, 256))),
+]
+
+
+@pytest.mark.parametrize("name,kw", SMALL_W, ids=[n for n, _ in SMALL_W])
+def test_prepare_weights_bit_exact(name, kw):
+    say(f"prepare_weights {name}")
+    wl = workloads.make(**kw)
+    codes, scales = gpu_prepare(wl)
+    for e in range(wl.E):
+        rc, rs = oracle_prepare(wl, e)
+        assert np.array_equal(scales[e].cpu().numpy(), rs), e
+        assert np.array_equal(codes[e].cpu().numpy(), rc), e
+
+
+# ------------------------------------------------------------ GEMM
+
+def _check_y(y, y_ref, S):
+    ok, worst, normwise = oracle.within_tolerance(y, y_ref, S, RTOL)
+    assert ok, f"worst elementwise {worst:.3g}, normwise {normwise:.3g}"
+
+
+SMALL_GEMM = [
+    ("one tile", (128, 128, 256)),
+    ("ragged M N, K tail 128", (200, 300, 640)),
+    ("M=1", (1, 96, 384)),
+    ("several tiles", (300, 260, 1024)),
+]
+
+
+@pytest.mark.parametrize("name,shape", SMALL_GEMM, ids=[n for n, _ in SMALL_GEMM])
+def test_gemm_dense(name, shape):
+    say(f"gemm {name} {shape}")
+    M, N, K = shape
+    rng = np.random.default_rng(M * 7 + N)
+    ac = rng.integers(0, 256, (M, K // 2), dtype=np.uint8)
+    asc = rng.integers(110, 140, (M, K // 32), dtype=np.uint8)
+    wc = rng.integers(0, 256, (N, K // 2), dtype=np.uint8)
+    wsc = rng.integers(110, 140, (N, K // 32), dtype=np.uint8)
+    y = mx.gemm(*(torch.from_numpy(a).to(DEV) for a in (ac, asc, wc, wsc)))
+    y_ref, S = oracle.gemm(ac, asc, wc, wsc)
+    _check_y(y.cpu().numpy(), y_ref, S)
+
+
+def test_gemm_exact_small_integers():
+    """One group per row with unit scales: every product and sum is a small
+    integer multiple of 2^-2, so fp32 accumulation is exact -> bit-exact."""
+    say("gemm exact small integers")
+    M, N, K = 64, 64, 128
+    rng = np.random.default_rng(5)
+    ac = rng.integers(0, 256, (M, K // 2), dtype=np.uint8)
+    wc = rng.integers(0, 256, (N, K // 2), dtype=np.uint8)
+    asc = np.full((M, K // 32), 127, np.uint8)
+    wsc = np.full((N, K // 32), 127, np.uint8)
+    y = mx.gemm(*(torch.from_numpy(a).to(DEV) for a in (ac, asc, wc, wsc))).cpu().numpy()
+    y_ref, _ = oracle.gemm(ac, asc, wc, wsc)
+    assert np.array_equal(y.astype(np.float64), y_ref)
+
+
+def test_gemm_grouped_ragged_with_empty_experts():
+    say("gemm grouped ragged")
+    E, N, K = 6, 160, 256
+    counts = np.array([0, 130, 1, 0, 257, 3])
+    off = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    M = int(off[-1])
+    rng = np.random.default_rng(6)
+    ac = rng.integers(0, 256, (M, K // 2), dtype=np.uint8)
+    asc = rng.integers(110, 140, (M, K // 32), dtype=np.uint8)
+    wc = rng.integers(0, 256, (E, N, K // 2), dtype=np.uint8)
+    wsc = rng.integers(110, 140, (E, N, K // 32), dtype=np.uint8)
+    t = [torch.from_numpy(a).to(DEV) for a in (ac, asc, wc, wsc)]
+    y = mx.gemm(*t, offsets=torch.from_numpy(off).to(DEV))
+    y_ref, S = oracle.gemm(ac, asc, wc, wsc, off)
+    _check_y(y.cpu().numpy(), y_ref, S)
+
+
+# ------------------------------------------------------------ whole layer, small
+
+SMALL_LINEAR = [
+    ("tiny fp32", dict(cfg=1)),
+    ("cfg2-shaped", dict(cfg=2, shape=(150, 200, 768))),
+    ("cfg3-shaped", dict(cfg=3, shape=(64, 96, 2048))),
+    ("cfg4-shaped M8", dict(cfg=4, shape=(8, 320, 1024))),
+    ("cfg5 token routing", dict(cfg=5, shape=(512, 64, 256), routing="token_zipf")),
+]
+
+
+@pytest.mark.parametrize("flags", [mx.PATH_AUTO, mx.PATH_UNFUSED])
+@pytest.mark.parametrize("name,kw", SMALL_LINEAR, ids=[n for n, _ in SMALL_LINEAR])
+def test_linear_small(name, kw, flags):
+    say(f"linear {name} flags={flags}")
+    wl = workloads.make(**kw)
+    off_np = wl.offsets.numpy() if wl.E > 1 else None
+    wc, wsc = gpu_prepare(wl)
+    y = mx.linear(wl.x.to(DEV), wl.s.to(DEV), wc, wsc,
+                  wl.offsets.to(DEV) if wl.E > 1 else None, flags=flags).cpu().numpy()
+    rwc, rws = zip(*(oracle_prepare(wl, e) for e in range(wl.E)))
+    y_ref, S = oracle.linear(host(wl.x), wl.s.numpy(), np.stack(rwc), np.stack(rws), off_np)
+    _check_y(y, y_ref, S)
+
+
+def test_linear_deterministic():
+    say("linear determinism")
+    wl = workloads.make(2, shape=(256, 256, 1024))
+    wc, wsc = gpu_prepare(wl)
+    x, s = wl.x.to(DEV), wl.s.to(DEV)
+    y1 = mx.linear(x, s, wc, wsc)
+    y2 = mx.linear(x, s, wc, wsc)
+    assert torch.equal(y1, y2)
