@@ -140,7 +140,9 @@ def e8m0_scale(amax: np.ndarray) -> np.ndarray:
 def e2m1_nearest(v: np.ndarray) -> np.ndarray:
     """Index (0..7) of the E2M1 magnitude nearest to v >= 0; a tie goes to
     the even index (even mantissa bit); values above 6 land on 6 (R8, R9)."""
-    v = np.asarray(v, dtype=np.float64)[..., None]
+    # Every v >= 5 has 6 as its nearest value; clamping at 8 keeps that and
+    # keeps the fp64 distances below exact (no absorption for huge v).
+    v = np.minimum(np.asarray(v, dtype=np.float64), 8.0)[..., None]
     dist = np.abs(v - E2M1_VALUES)
     best = dist == dist.min(axis=-1, keepdims=True)
     even = (np.arange(8) % 2 == 0)

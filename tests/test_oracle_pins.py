@@ -178,6 +178,9 @@ def test_e2m1_rounding_exhaustive():
     assert np.all(oracle.e2m1_nearest(small) == 0)
     ties = np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0, 7.0, 100.0])
     assert list(oracle.E2M1_VALUES[oracle.e2m1_nearest(ties)]) == [0, 1, 1, 2, 2, 4, 4, 6, 6]
+    # saturation holds for every finite magnitude up to the fp32 maximum
+    big = np.array([8.0, 1e10, 2.0 ** 100, 3.4e38, np.finfo(np.float32).max], dtype=np.float32)
+    assert np.all(oracle.e2m1_nearest(big) == 7)
 
 
 def test_quantizer_round_trip_of_representable_groups():
