@@ -1,0 +1,263 @@
+#!/usr/bin/env python3
+"""Benchmark of the online MXFP4 W4A4 linear layer on one MI355X.
+
+A step is one pass of the whole online layer over one batch: the activation
+transform + MXFP4 quantization kernel, then the MXFP4 GEMM against weights
+prepared offline (untimed, like the pages' offline weight preparation).
+The default workload is the attention projection M2048 N4096 K4096 with
+bf16 activations.  Inputs are seeded synthetic tensors (module `workloads`)
+resident in HBM before the timed region; R replicas of (x, W', y) are
+cycled so that the working set exceeds the 256 MB Infinity Cache.
+
+Prints one JSON line:
+  value        = 2*M*N*K / (wall time per step)      [TFLOP/s]
+  act_transform= algorithmic bytes / act-kernel time  [GB/s]
+  roofline     = the GEMM kernel (dominant) against the dense MXFP4 MFMA peak
+  cpu_baseline = the CPU oracle on a bounded row sample of the same layer
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "W4A4 linear TFLOP/s + act-transform GB/s, % of MI355X roofline, 1 GPU"
+PEAK_MXFP4_TFLOPS = 10100.0   # MI355X dense FP4/FP6 MFMA
+PEAK_HBM_GBPS = 8000.0        # MI355X HBM3E
+MALL_BYTES = 256 << 20
+
+WORKLOADS = {
+    # name: (config, variant, M, description)
+    "attn": (2, 0, None, "attn-proj M2048 N4096 K4096 bf16"),
+    "down": (3, 0, None, "down-prefill M4096 N4096 K14336 bf16"),
+    "decode-gateup-m1": (4, 0, 1, "decode gate/up M1 N25600 K5120 bf16"),
+    "decode-gateup-m8": (4, 0, 8, "decode gate/up M8 N25600 K5120 bf16"),
+    "decode-gateup-m32": (4, 0, 32, "decode gate/up M32 N25600 K5120 bf16"),
+    "decode-down-m1": (4, 1, 1, "decode down M1 N5120 K25600 bf16"),
+    "decode-down-m32": (4, 1, 32, "decode down M32 N5120 K25600 bf16"),
+    "moe": (5, 0, None, "MoE E64 T8192 N1024 K3072 bf16, Zipf(1.1) per-expert routing"),
+    "moe-token": (5, 0, None, "MoE E64 T8192 N1024 K3072 bf16, per-token Zipf(1.1) routing"),
+}
+
+
+def parse():
+    p = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=200)
+    p.add_argument("--warmup", type=int, default=20)
+    p.add_argument("--workload", default="attn", choices=sorted(WORKLOADS))
+    p.add_argument("--path", default="auto", choices=["auto", "fused", "unfused"])
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-rows", type=int, default=256, help="row sample of the CPU oracle baseline")
+    return p.parse_args()
+
+
+def sha(path):
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def traffic_record(kernel_key):
+    """HBM bytes per launch from the committed counter summary, or None when
+    the kernel source changed since the counters were taken."""
+    path = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+    try:
+        rec = json.load(open(path))[kernel_key]
+    except (OSError, KeyError, ValueError):
+        return None
+    src = os.path.join(ROOT, rec["source"])
+    if not os.path.exists(src) or sha(src) != rec["source_sha256"]:
+        return None
+    return rec["bytes_per_launch"]
+
+
+def cpu_baseline(wl, rows):
+    """The oracle as it stands on `rows` activation rows of the same layer:
+    transform + quantization of the rows, then the fp64 dequantized GEMM
+    against the full prepared weight (prepared untimed)."""
+    import numpy as np
+    import oracle
+    import workloads
+    from threadpoolctl import threadpool_info
+
+    import torch
+    xb = workloads.bf16_bits(wl.x[:rows]) if wl.x.dtype == torch.bfloat16 else wl.x[:rows].numpy()
+    off = wl.offsets.numpy()
+    e0 = int(np.searchsorted(off, 0, side="right") - 1)
+    w = workloads.bf16_bits(wl.w[e0]) if wl.w.dtype == torch.bfloat16 else wl.w[e0].numpy()
+    wc, ws = oracle.prepare_weights(w, wl.s[e0].numpy())
+    s = wl.s[e0:e0 + 1].numpy()
+    t0 = time.perf_counter()
+    reps = 0
+    while True:
+        ac, asc = oracle.quant_act(xb, s)
+        oracle.gemm(ac, asc, wc, ws)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el > 10.0 or reps >= 50:
+            break
+    flops = 2.0 * rows * wl.N * wl.K * reps
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    return {"value": round(flops / el / 1e12, 6), "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{rows} of {wl.M} rows x {reps} reps (transform+quant of the rows, fp64 GEMM vs full W')",
+            "seconds": round(el, 2)}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (the layer is data-parallel: "
+              f"run one process per GPU on its own rows)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import workloads
+    import mxfp4_w4a4_quantized_channel_amd as mx
+
+    cfg, variant, Mdec, desc = WORKLOADS[args.workload]
+    kw = dict(variant=variant)
+    if Mdec is not None:
+        kw["M"] = Mdec
+    if args.workload == "moe-token":
+        kw["routing"] = "token_zipf"
+    wl = workloads.make(cfg, **kw)
+    M, N, K, E = wl.M, wl.N, wl.K, wl.E
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    L = mx.lib()
+    flags = {"auto": mx.PATH_AUTO, "fused": mx.PATH_FUSED, "unfused": mx.PATH_UNFUSED}[args.path]
+
+    # ---- resident inputs, R replicas so the rotation defeats the MALL
+    x0 = wl.x.to(dev)
+    s0 = wl.s.to(dev)
+    off = wl.offsets.to(dev) if E > 1 else None
+    wc0, ws0 = mx.prepare_weights(wl.w.to(dev), s0)
+    set_bytes = x0.numel() * x0.element_size() + wc0.numel() + ws0.numel() + M * N * 4
+    R = max(2, min(64, -(-(4 * MALL_BYTES) // set_bytes)))
+    xs = [x0] + [x0.clone() for _ in range(R - 1)]
+    wcs = [wc0] + [wc0.clone() for _ in range(R - 1)]
+    wss = [ws0] + [ws0.clone() for _ in range(R - 1)]
+    ys = [torch.empty((M, N), dtype=torch.float32, device=dev) for _ in range(R)]
+    need = L.macaq_linear_workspace_bytes(M, N, K, E, flags)
+    ws_buf = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
+    a_codes = ws_buf[: M * K // 2]
+    fused = L.macaq_linear_path(M, N, K, E, flags) == mx.PATH_FUSED
+    a_scales = ws_buf[(M * K // 2 + 255) // 256 * 256:]
+    stream = torch.cuda.current_stream(dev)
+    sp = ctypes.c_void_p(stream.cuda_stream)
+    xdt = mx.BF16 if x0.dtype == torch.bfloat16 else mx.F32
+    p = ctypes.c_void_p
+    off_p = p(off.data_ptr()) if off is not None else None
+    split = not fused  # two launches that are timed separately
+
+    def step_args(i):
+        j = i % R
+        return (p(xs[j].data_ptr()), p(wcs[j].data_ptr()), p(wss[j].data_ptr()), p(ys[j].data_ptr()))
+
+    def run_linear(i):
+        xp, wcp, wsp, yp = step_args(i)
+        st = mx.macaq_linear(xp, xdt, p(s0.data_ptr()), off_p, E, wcp, wsp, M, N, K, yp,
+                             p(ws_buf.data_ptr()), ws_buf.numel(), flags, sp)
+        if st != 0:
+            raise RuntimeError(mx.lib().macaq_last_error().decode())
+
+    def run_split(i, ev):
+        xp, wcp, wsp, yp = step_args(i)
+        ev[0].record(stream)
+        st = mx.macaq_quant_act(xp, xdt, p(s0.data_ptr()), off_p, E, M, K, p(a_codes.data_ptr()),
+                                p(a_scales.data_ptr()), sp)
+        ev[1].record(stream)
+        st |= mx.macaq_gemm(p(a_codes.data_ptr()), p(a_scales.data_ptr()), off_p, E, wcp, wsp, M, N, K, yp,
+                            None, 0, sp)
+        ev[2].record(stream)
+        if st != 0:
+            raise RuntimeError(mx.lib().macaq_last_error().decode())
+
+    # ---- warmup
+    for i in range(args.warmup):
+        run_linear(i)
+    torch.cuda.synchronize()
+
+    # ---- timed region: exactly K steps of the layer
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        run_linear(i)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = wall / args.steps * 1e3
+    flops = 2.0 * M * N * K
+    value = flops / (wall / args.steps) / 1e12
+
+    # ---- per-kernel durations with HIP events on the launch stream
+    act_us = gemm_us = None
+    if split:
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+        for i in range(args.steps):
+            run_split(i, evs[i])
+        torch.cuda.synchronize()
+        act_us = sum(e[0].elapsed_time(e[1]) for e in evs) / args.steps * 1e3
+        gemm_us = sum(e[1].elapsed_time(e[2]) for e in evs) / args.steps * 1e3
+    else:
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+        for i in range(args.steps):
+            evs[i][0].record(stream)
+            run_linear(i)
+            evs[i][1].record(stream)
+        torch.cuda.synchronize()
+        gemm_us = sum(e[0].elapsed_time(e[1]) for e in evs) / args.steps * 1e3
+
+    # algorithmic bytes
+    xb = M * K * x0.element_size()
+    act_alg = xb + M * K // 2 + M * K // 32 + 4 * E * K
+    if E > 1:
+        counts = wl.offsets.diff().numpy()
+        w_alg = int((counts > 0).sum()) * N * K * 17 // 32
+    else:
+        w_alg = N * K * 17 // 32
+    out = {
+        "metric": METRIC,
+        "value": round(value, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "mxfp4",
+        "data": "synthetic",
+        "config": {"workload": desc, "M": M, "N": N, "K": K, "experts": E, "x_dtype": str(x0.dtype).split(".")[-1],
+                   "path": "fused" if fused else "unfused", "replicas": R,
+                   "parallelism": "none (one GPU)"},
+    }
+    if act_us is not None:
+        out["act_transform"] = {"GBps": round(act_alg / act_us / 1e3, 1), "us": round(act_us, 2),
+                                "bytes": act_alg, "frac_of_hbm_peak": round(act_alg / act_us / 1e3 / PEAK_HBM_GBPS, 4)}
+    gemm_name = "fused transform+GEMM" if fused else "MXFP4 GEMM"
+    if fused or M <= 32:
+        gemm_bytes = w_alg + xb + M * N * 4
+        ach = gemm_bytes / gemm_us / 1e3
+        out["roofline"] = {"kernel": gemm_name, "bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBPS,
+                           "unit": "GB/s", "frac": round(ach / PEAK_HBM_GBPS, 4), "us": round(gemm_us, 2),
+                           "traffic": traffic_record(f"{args.workload}:{'fused' if fused else 'gemm'}")}
+    else:
+        ach = flops / gemm_us / 1e6
+        out["roofline"] = {"kernel": gemm_name, "bound": "mfma", "achieved": round(ach, 1),
+                           "peak": PEAK_MXFP4_TFLOPS, "unit": "TFLOP/s", "frac": round(ach / PEAK_MXFP4_TFLOPS, 4),
+                           "us": round(gemm_us, 2), "traffic": traffic_record(f"{args.workload}:gemm")}
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(wl, min(args.cpu_rows, M))
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -156,6 +156,12 @@ size_t macaq_quant_act_bytes(int64_t M, int64_t K);
 size_t macaq_linear_workspace_bytes(int64_t M, int64_t N, int64_t K, int64_t E, uint32_t flags);
 
 /*
+ * Path macaq_linear takes for this shape and flags: MACAQ_PATH_FUSED or
+ * MACAQ_PATH_UNFUSED (a negative status for invalid flags).
+ */
+int macaq_linear_path(int64_t M, int64_t N, int64_t K, int64_t E, uint32_t flags);
+
+/*
  * The whole online layer: y = quant(x diag(s_e) H) quant(W_e diag(1/s_e) H)^T
  * with weights already prepared by macaq_prepare_weights.
  *   x [M][K] (rows sorted by expert), s [E][K], expert_offsets [E+1] device

@@ -62,6 +62,7 @@ def _load():
         "macaq_gemm": (ci, [vp, vp, vp, i64, vp, vp, i64, i64, i64, vp, vp, sz, vp]),
         "macaq_quant_act_bytes": (sz, [i64, i64]),
         "macaq_linear_workspace_bytes": (sz, [i64, i64, i64, i64, u32]),
+        "macaq_linear_path": (ci, [i64, i64, i64, i64, u32]),
         "macaq_linear": (ci, [vp, ci, vp, vp, i64, vp, vp, i64, i64, i64, vp, vp, sz, u32, vp]),
         "macaq_encode_e2m1": (ci, [vp, i64, vp, vp]),
     }

@@ -155,12 +155,18 @@ size_t macaq_quant_act_bytes(int64_t M, int64_t K) {
   return round_up((size_t)M * (size_t)K / 2, 256) + round_up((size_t)M * (size_t)K / 32, 256);
 }
 
+int macaq_linear_path(int64_t M, int64_t N, int64_t K, int64_t E, uint32_t flags) {
+  if (flags > MACAQ_PATH_UNFUSED) return fail(MACAQ_ERR_INVALID_ARG, "macaq_linear_path: unknown flags");
+  if (flags != MACAQ_PATH_AUTO) return (int)flags;
+  return (macaq::linear_fused_supported(M, N, K, E) && M <= kMaxFusedM) ? MACAQ_PATH_FUSED : MACAQ_PATH_UNFUSED;
+}
+
 size_t macaq_linear_workspace_bytes(int64_t M, int64_t N, int64_t K, int64_t E, uint32_t flags) {
   if (M <= 0 || N <= 0 || K <= 0 || E <= 0) return 0;
-  const bool fused_ok = macaq::linear_fused_supported(M, N, K, E);
-  const bool fused = flags == MACAQ_PATH_FUSED || (flags == MACAQ_PATH_AUTO && fused_ok && M <= kMaxFusedM);
-  if (fused) return macaq::linear_fused_workspace_bytes(M, N, K);
-  return macaq_quant_act_bytes(M, K);
+  const int path = macaq_linear_path(M, N, K, E, flags);
+  if (path == MACAQ_PATH_FUSED) return macaq::linear_fused_workspace_bytes(M, N, K);
+  if (path == MACAQ_PATH_UNFUSED) return macaq_quant_act_bytes(M, K);
+  return 0;
 }
 
 int macaq_gemm(const uint8_t* a_codes, const uint8_t* a_scales, const int32_t* expert_offsets, int64_t E,
@@ -191,10 +197,9 @@ int macaq_linear(const void* x, macaq_dtype x_dtype, const float* s, const int32
   const uint8_t* dummy = reinterpret_cast<const uint8_t*>(w_codes);
   if (int st = validate_gemm(dummy, w_scales, expert_offsets, E, w_codes, w_scales, M, N, K, y, fn)) return st;
   if (M == 0) return MACAQ_OK;
-  const bool fused_ok = macaq::linear_fused_supported(M, N, K, E);
-  if (flags == MACAQ_PATH_FUSED && !fused_ok)
+  if (flags == MACAQ_PATH_FUSED && !macaq::linear_fused_supported(M, N, K, E))
     return fail(MACAQ_ERR_UNSUPPORTED, std::string(fn) + ": the fused path serves E == 1 and M <= 32");
-  const bool fused = flags == MACAQ_PATH_FUSED || (flags == MACAQ_PATH_AUTO && fused_ok && M <= kMaxFusedM);
+  const bool fused = macaq_linear_path(M, N, K, E, flags) == MACAQ_PATH_FUSED;
   const size_t need = fused ? macaq::linear_fused_workspace_bytes(M, N, K) : macaq_quant_act_bytes(M, K);
   if (need > 0 && (workspace == nullptr || workspace_bytes < need))
     return fail(MACAQ_ERR_WORKSPACE, std::string(fn) + ": workspace of " + std::to_string(need) +
