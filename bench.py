@@ -56,7 +56,22 @@ def parse():
     p.add_argument("--path", default="auto", choices=["auto", "fused", "unfused"])
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-rows", type=int, default=256, help="row sample of the CPU oracle baseline")
+    p.add_argument("--copy-calibration", action="store_true",
+                   help="only run a plain 512 MiB device-to-device copy (5 times) so that HBM byte "
+                        "counters can be scaled against a transfer of known size")
     return p.parse_args()
+
+
+def copy_calibration():
+    import torch
+    n = 512 << 20
+    src = torch.empty(n, dtype=torch.uint8, device="cuda:0").fill_(1)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration": {"bytes_read_per_copy": n, "bytes_written_per_copy": n, "copies": 5}}))
 
 
 def sha(path):
@@ -112,6 +127,9 @@ def cpu_baseline(wl, rows):
 
 def main():
     args = parse()
+    if args.copy_calibration:
+        copy_calibration()
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (the layer is data-parallel: "
               f"run one process per GPU on its own rows)", file=sys.stderr)
@@ -146,10 +164,11 @@ def main():
     wss = [ws0] + [ws0.clone() for _ in range(R - 1)]
     ys = [torch.empty((M, N), dtype=torch.float32, device=dev) for _ in range(R)]
     need = L.macaq_linear_workspace_bytes(M, N, K, E, flags)
-    ws_buf = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
+    ws_buf = torch.zeros(max(need, 256), dtype=torch.uint8, device=dev)
     a_codes = ws_buf[: M * K // 2]
     fused = L.macaq_linear_path(M, N, K, E, flags) == mx.PATH_FUSED
     a_scales = ws_buf[(M * K // 2 + 255) // 256 * 256:]
+    gemm_ws = torch.zeros(max(int(L.macaq_gemm_workspace_bytes(M, N, K, E)), 256), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream(dev)
     sp = ctypes.c_void_p(stream.cuda_stream)
     xdt = mx.BF16 if x0.dtype == torch.bfloat16 else mx.F32
@@ -175,7 +194,7 @@ def main():
                                 p(a_scales.data_ptr()), sp)
         ev[1].record(stream)
         st |= mx.macaq_gemm(p(a_codes.data_ptr()), p(a_scales.data_ptr()), off_p, E, wcp, wsp, M, N, K, yp,
-                            None, 0, sp)
+                            p(gemm_ws.data_ptr()), gemm_ws.numel(), sp)
         ev[2].record(stream)
         if st != 0:
             raise RuntimeError(mx.lib().macaq_last_error().decode())

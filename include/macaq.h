@@ -133,9 +133,8 @@ int macaq_quant_act(const void* x, macaq_dtype x_dtype, const float* s,
  *   a_codes [M][K/2], a_scales [M][K/32]; w_codes [E][N][K/2],
  *   w_scales [E][N][K/32]; expert_offsets [E+1] device (NULL when E == 1);
  *   y [M][N] fp32 out.
- * workspace: device scratch of at least macaq_linear_workspace_bytes(M, N,
- * K, E, MACAQ_PATH_UNFUSED) - macaq_quant_act_bytes(M, K) bytes (may be 0
- * and NULL for the current kernels).
+ * workspace: device scratch of macaq_gemm_workspace_bytes(M, N, K, E) bytes,
+ * 256-byte aligned; NULL when that is 0 (the current kernels need none).
  * Requires K % 128 == 0; K >= 128; all code pointers 16-byte aligned and
  * scale pointers 4-byte aligned.
  */
@@ -145,13 +144,18 @@ int macaq_gemm(const uint8_t* a_codes, const uint8_t* a_scales,
                int64_t M, int64_t N, int64_t K, float* y,
                void* workspace, size_t workspace_bytes, void* stream);
 
+/* Workspace bytes macaq_gemm needs for this shape (0: none). */
+size_t macaq_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, int64_t E);
+
 /* Bytes of activation codes + scales for M rows of width K (M*K/2 + M*K/32),
- * rounded up to 256-byte alignment of the scale part. */
+ * each part rounded up to 256 bytes. */
 size_t macaq_quant_act_bytes(int64_t M, int64_t K);
 
 /*
  * Device workspace needed by macaq_linear for this shape and flags.  0 means
- * no workspace is needed (workspace may then be NULL).
+ * no workspace is needed (workspace may then be NULL).  The unfused path
+ * keeps the activation codes and scales there between its two kernels, so
+ * calls sharing one workspace must not overlap in time.
  */
 size_t macaq_linear_workspace_bytes(int64_t M, int64_t N, int64_t K, int64_t E, uint32_t flags);
 
@@ -169,7 +173,10 @@ int macaq_linear_path(int64_t M, int64_t N, int64_t K, int64_t E, uint32_t flags
  *   macaq_prepare_weights, y [M][N] fp32 out.
  * flags: MACAQ_PATH_AUTO / _FUSED / _UNFUSED.  Both paths produce the same
  * activation codes; y may differ between paths only by fp32 summation order.
- * The fused path serves E == 1 and M <= 32.
+ * The fused path serves E == 1, M <= 32, K % 256 == 0 and the M*K*17/32
+ * bytes of quantized activations fitting in LDS beside the kernel's
+ * reduction buffer (about 96 to 144 KiB depending on K); AUTO takes it for
+ * M <= 2, where one launch beats two.
  * Requires the argument rules of macaq_quant_act and macaq_gemm and a
  * workspace of macaq_linear_workspace_bytes(M, N, K, E, flags) bytes.
  */

@@ -61,6 +61,7 @@ def _load():
         "macaq_quant_act": (ci, [vp, ci, vp, vp, i64, i64, i64, vp, vp, vp]),
         "macaq_gemm": (ci, [vp, vp, vp, i64, vp, vp, i64, i64, i64, vp, vp, sz, vp]),
         "macaq_quant_act_bytes": (sz, [i64, i64]),
+        "macaq_gemm_workspace_bytes": (sz, [i64, i64, i64, i64]),
         "macaq_linear_workspace_bytes": (sz, [i64, i64, i64, i64, u32]),
         "macaq_linear_path": (ci, [i64, i64, i64, i64, u32]),
         "macaq_linear": (ci, [vp, ci, vp, vp, i64, vp, vp, i64, i64, i64, vp, vp, sz, u32, vp]),
@@ -173,8 +174,9 @@ def _w_shape(w_codes, w_scales):
     return w_codes, w_scales
 
 
-def gemm(a_codes, a_scales, w_codes, w_scales, offsets=None, out=None):
-    """y = A' W'^T (fp32 [M, N]) from MXFP4 operands."""
+def gemm(a_codes, a_scales, w_codes, w_scales, offsets=None, out=None, workspace=None):
+    """y = A' W'^T (fp32 [M, N]) from MXFP4 operands.  A workspace, when one
+    is needed, is zero-filled here; a caller-provided one must start zeroed."""
     _load()
     w_codes, w_scales = _w_shape(w_codes, w_scales)
     _need(a_codes, "a_codes", torch.uint8, 2)
@@ -183,8 +185,12 @@ def gemm(a_codes, a_scales, w_codes, w_scales, offsets=None, out=None):
     M = a_codes.shape[0]
     K = 2 * KH
     y = out if out is not None else torch.empty((M, N), dtype=torch.float32, device=a_codes.device)
+    need = int(_load().macaq_gemm_workspace_bytes(M, N, K, E))
+    if workspace is None and need > 0:
+        workspace = torch.zeros(need, dtype=torch.uint8, device=a_codes.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(macaq_gemm(_ptr(a_codes), _ptr(a_scales), _ptr(offsets), E, _ptr(w_codes), _ptr(w_scales),
-                      M, N, K, _ptr(y), None, 0, _stream(a_codes.device)), "macaq_gemm")
+                      M, N, K, _ptr(y), _ptr(workspace), ws_bytes, _stream(a_codes.device)), "macaq_gemm")
     return y
 
 
@@ -204,7 +210,7 @@ def linear(x, s, w_codes, w_scales, offsets=None, flags=PATH_AUTO, out=None, wor
     E, N, _ = w_codes.shape
     need = linear_workspace_bytes(M, N, K, E, flags)
     if workspace is None and need > 0:
-        workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
+        workspace = torch.zeros(need, dtype=torch.uint8, device=x.device)
     y = out if out is not None else torch.empty((M, N), dtype=torch.float32, device=x.device)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(macaq_linear(_ptr(x), _dtype_code(x), _ptr(s), _ptr(offsets), E, _ptr(w_codes), _ptr(w_scales),

@@ -21,15 +21,17 @@ hipError_t launch_gemm(const uint8_t* A, const uint8_t* As, const int32_t* offse
                        float* Y, hipStream_t stream);
 hipError_t launch_linear_fused(const void* x, bool x_f32, const float* s, const uint8_t* B,
                                const uint8_t* Bs, int64_t M, int64_t N, int64_t K, float* Y,
-                               void* workspace, size_t workspace_bytes, hipStream_t stream);
-size_t linear_fused_workspace_bytes(int64_t M, int64_t N, int64_t K);
+                               hipStream_t stream);
 bool linear_fused_supported(int64_t M, int64_t N, int64_t K, int64_t E);
+bool decode_supported(int64_t M, int64_t N, int64_t K, int64_t E);
+hipError_t launch_decode_gemm(const uint8_t* A, const uint8_t* As, const uint8_t* W, const uint8_t* Ws, int64_t M,
+                              int64_t N, int64_t K, float* Y, hipStream_t stream);
 }  // namespace macaq
 
 namespace {
 
 constexpr int kVersion = 10000;  // 1.0.0
-constexpr int64_t kMaxFusedM = 32;
+constexpr int64_t kMaxFusedM = 2;  // AUTO takes the fused path up to this M
 
 thread_local std::string g_last_error;
 
@@ -155,6 +157,11 @@ size_t macaq_quant_act_bytes(int64_t M, int64_t K) {
   return round_up((size_t)M * (size_t)K / 2, 256) + round_up((size_t)M * (size_t)K / 32, 256);
 }
 
+size_t macaq_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, int64_t E) {
+  (void)M; (void)N; (void)K; (void)E;
+  return 0;  // no GEMM kernel needs scratch memory
+}
+
 int macaq_linear_path(int64_t M, int64_t N, int64_t K, int64_t E, uint32_t flags) {
   if (flags > MACAQ_PATH_UNFUSED) return fail(MACAQ_ERR_INVALID_ARG, "macaq_linear_path: unknown flags");
   if (flags != MACAQ_PATH_AUTO) return (int)flags;
@@ -164,23 +171,44 @@ int macaq_linear_path(int64_t M, int64_t N, int64_t K, int64_t E, uint32_t flags
 size_t macaq_linear_workspace_bytes(int64_t M, int64_t N, int64_t K, int64_t E, uint32_t flags) {
   if (M <= 0 || N <= 0 || K <= 0 || E <= 0) return 0;
   const int path = macaq_linear_path(M, N, K, E, flags);
-  if (path == MACAQ_PATH_FUSED) return macaq::linear_fused_workspace_bytes(M, N, K);
-  if (path == MACAQ_PATH_UNFUSED) return macaq_quant_act_bytes(M, K);
+  if (path == MACAQ_PATH_FUSED) return 0;
+  if (path == MACAQ_PATH_UNFUSED) return macaq_quant_act_bytes(M, K) + macaq_gemm_workspace_bytes(M, N, K, E);
   return 0;
 }
+
+namespace {
+int run_gemm(const uint8_t* a_codes, const uint8_t* a_scales, const int32_t* expert_offsets, int64_t E,
+             const uint8_t* w_codes, const uint8_t* w_scales, int64_t M, int64_t N, int64_t K, float* y,
+             void* workspace, hipStream_t stream, const char* fn) {
+  (void)workspace;
+  if (macaq::decode_supported(M, N, K, E))
+    return hip_status(macaq::launch_decode_gemm(a_codes, a_scales, w_codes, w_scales, M, N, K, y, stream), fn);
+  return hip_status(macaq::launch_gemm(a_codes, a_scales, E > 1 ? expert_offsets : nullptr, (int)E, w_codes,
+                                       w_scales, M, N, K, y, stream),
+                    fn);
+}
+
+int check_workspace(void* workspace, size_t have, size_t need, const char* fn) {
+  if (need == 0) return MACAQ_OK;
+  if (workspace == nullptr || have < need)
+    return fail(MACAQ_ERR_WORKSPACE, std::string(fn) + ": workspace of " + std::to_string(need) +
+                                         " bytes required, got " + std::to_string(workspace ? have : 0));
+  if (!aligned(workspace, 256))
+    return fail(MACAQ_ERR_INVALID_ARG, std::string(fn) + ": workspace must be 256-byte aligned");
+  return MACAQ_OK;
+}
+}  // namespace
 
 int macaq_gemm(const uint8_t* a_codes, const uint8_t* a_scales, const int32_t* expert_offsets, int64_t E,
                const uint8_t* w_codes, const uint8_t* w_scales, int64_t M, int64_t N, int64_t K, float* y,
                void* workspace, size_t workspace_bytes, void* stream) {
-  (void)workspace;
-  (void)workspace_bytes;
   const char* fn = "macaq_gemm";
   if (int st = validate_gemm(a_codes, a_scales, expert_offsets, E, w_codes, w_scales, M, N, K, y, fn)) return st;
   if (M == 0) return MACAQ_OK;
+  if (int st = check_workspace(workspace, workspace_bytes, macaq_gemm_workspace_bytes(M, N, K, E), fn)) return st;
   if (int st = check_device()) return st;
-  return hip_status(macaq::launch_gemm(a_codes, a_scales, E > 1 ? expert_offsets : nullptr, (int)E, w_codes,
-                                       w_scales, M, N, K, y, (hipStream_t)stream),
-                    fn);
+  return run_gemm(a_codes, a_scales, expert_offsets, E, w_codes, w_scales, M, N, K, y, workspace,
+                  (hipStream_t)stream, fn);
 }
 
 int macaq_linear(const void* x, macaq_dtype x_dtype, const float* s, const int32_t* expert_offsets, int64_t E,
@@ -200,17 +228,12 @@ int macaq_linear(const void* x, macaq_dtype x_dtype, const float* s, const int32
   if (flags == MACAQ_PATH_FUSED && !macaq::linear_fused_supported(M, N, K, E))
     return fail(MACAQ_ERR_UNSUPPORTED, std::string(fn) + ": the fused path serves E == 1 and M <= 32");
   const bool fused = macaq_linear_path(M, N, K, E, flags) == MACAQ_PATH_FUSED;
-  const size_t need = fused ? macaq::linear_fused_workspace_bytes(M, N, K) : macaq_quant_act_bytes(M, K);
-  if (need > 0 && (workspace == nullptr || workspace_bytes < need))
-    return fail(MACAQ_ERR_WORKSPACE, std::string(fn) + ": workspace of " + std::to_string(need) +
-                                         " bytes required, got " + std::to_string(workspace_bytes));
-  if (need > 0 && !aligned(workspace, 256))
-    return fail(MACAQ_ERR_INVALID_ARG, std::string(fn) + ": workspace must be 256-byte aligned");
+  const size_t need = macaq_linear_workspace_bytes(M, N, K, E, flags);
+  if (int st = check_workspace(workspace, workspace_bytes, need, fn)) return st;
   if (int st = check_device()) return st;
   hipStream_t st = (hipStream_t)stream;
   if (fused)
-    return hip_status(macaq::launch_linear_fused(x, x_dtype == MACAQ_F32, s, w_codes, w_scales, M, N, K, y,
-                                                 workspace, workspace_bytes, st),
+    return hip_status(macaq::launch_linear_fused(x, x_dtype == MACAQ_F32, s, w_codes, w_scales, M, N, K, y, st),
                       "macaq_linear (fused)");
   uint8_t* a_codes = static_cast<uint8_t*>(workspace);
   uint8_t* a_scales = a_codes + round_up((size_t)M * (size_t)K / 2, 256);
@@ -219,8 +242,8 @@ int macaq_linear(const void* x, macaq_dtype x_dtype, const float* s, const int32
                                                  a_codes, a_scales, st),
                          "macaq_linear (transform)"))
     return r;
-  return hip_status(macaq::launch_gemm(a_codes, a_scales, off, (int)E, w_codes, w_scales, M, N, K, y, st),
-                    "macaq_linear (gemm)");
+  void* gemm_ws = static_cast<uint8_t*>(workspace) + macaq_quant_act_bytes(M, K);
+  return run_gemm(a_codes, a_scales, off, E, w_codes, w_scales, M, N, K, y, gemm_ws, st, "macaq_linear (gemm)");
 }
 
 int macaq_encode_e2m1(const float* v, int64_t n, uint8_t* codes, void* stream) {

@@ -1,0 +1,920 @@
+// MXFP4 x MXFP4 GEMM on CDNA4 block-scaled MFMA, dense and grouped.
+//
+// Sources: "MACaQ Enables Streaming W4A4 Quantization with 32.5GB GPU
+// Memory", section "Quantization mechanism" (the transformed, quantized
+// activation goes through an FP4 matrix multiplication with the offline
+// weight, y = x W^T); "华为开源MACaQ:本地量化提速3倍", section
+// "现在还不能把它当成通用量化工厂" (dense and grouped W4A4 matmul operators).
+//
+// y[m][n] = sum_k a(m,k) w(e(m),n,k), both operands MXFP4 row-major along K
+// (codes [rows][K/2], E8M0 scales [rows][K/32]).
+//
+// Instruction: v_mfma_scale_f32_32x32x64_f8f6f4 with both operands FP4.
+// Each lane feeds 16 bytes = 32 FP4 values of one row and the E8M0 byte of
+// exactly those 32 values, so one lane's operand is one MXFP4 group and the
+// row-major MXFP4 layout is the MFMA operand layout.  The sum over K is
+// invariant under a permutation of K applied to both operands, so within a
+// K-tile of 256 (8 groups) lane half h (lanes 32h..32h+31) of sub-step j
+// takes group 4h + j: a lane's four sub-steps read one contiguous 64-byte
+// run of its row and one scale dword whose byte j the instruction's op_sel
+// picks.
+//
+// Tiling: a block computes a BM x BN tile of y with WAVES_M x WAVES_N waves;
+// each wave owns a (BM/WAVES_M) x (BN/WAVES_N) sub-tile of 32x32 MFMA
+// blocks with fp32 accumulators in registers.  K-tiles of 256 are staged in
+// LDS, double-buffered: the global loads of tile k+1 are in flight while
+// tile k feeds the MFMAs.  In LDS each 128-byte tile row holds 8 chunks of
+// 16 bytes, chunk c of row r stored at position c ^ (r & 7), so the
+// fragment reads of 8 consecutive rows hit 8 different bank groups.
+//
+// Grouped (mixture-of-experts) operation: rows are sorted by expert and the
+// block index enumerates (expert, row-tile) pairs on the device from the
+// expert offsets, so no host synchronization is needed; slots past the last
+// expert's tiles exit at once.
+#pragma once
+
+#include "mx_common.h"
+
+namespace macaq {
+
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef float v16f __attribute__((ext_vector_type(16)));
+
+__device__ __forceinline__ v8i as_operand(const uint4& q) {
+  v8i r;
+  r[0] = (int)q.x; r[1] = (int)q.y; r[2] = (int)q.z; r[3] = (int)q.w;
+  r[4] = 0; r[5] = 0; r[6] = 0; r[7] = 0;
+  return r;
+}
+
+template <int BM, int BN, int WAVES_M, int WAVES_N>
+struct GemmTile {
+  static constexpr int kThreads = 64 * WAVES_M * WAVES_N;
+  static constexpr int kTM = BM / WAVES_M;
+  static constexpr int kTN = BN / WAVES_N;
+  static constexpr int kFM = kTM / 32;
+  static constexpr int kFN = kTN / 32;
+  static constexpr int kAChunks = BM * 8 / kThreads;
+  static constexpr int kBChunks = BN * 8 / kThreads;
+  static constexpr int kASc = (BM * 2 + kThreads - 1) / kThreads;
+  static constexpr int kBSc = (BN * 2 + kThreads - 1) / kThreads;
+  static_assert(kTM % 32 == 0 && kTN % 32 == 0, "wave tile must be a multiple of 32");
+  static_assert(BM * 8 % kThreads == 0 && BN * 8 % kThreads == 0, "chunks must divide evenly");
+};
+
+template <int J, int FM, int FN>
+__device__ __forceinline__ void mfma_substep(v16f (&acc)[FM][FN], const uint4 (&fa)[FM],
+                                             const uint4 (&fb)[FN], const uint32_t (&sa)[FM],
+                                             const uint32_t (&sb)[FN]) {
+#pragma unroll
+  for (int mi = 0; mi < FM; ++mi)
+#pragma unroll
+    for (int ni = 0; ni < FN; ++ni)
+      acc[mi][ni] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+          as_operand(fa[mi]), as_operand(fb[ni]), acc[mi][ni], 4, 4, J, (int)sa[mi], J, (int)sb[ni]);
+}
+
+template <int BM, int BN, int WAVES_M, int WAVES_N>
+__global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_mxfp4_kernel(
+    const uint8_t* __restrict__ A, const uint8_t* __restrict__ As, const uint8_t* __restrict__ B,
+    const uint8_t* __restrict__ Bs, const int32_t* __restrict__ offsets, int E, int64_t M,
+    int64_t N, int64_t K, float* __restrict__ Y, int n_tiles_n) {
+  using T = GemmTile<BM, BN, WAVES_M, WAVES_N>;
+  __shared__ __attribute__((aligned(16))) uint8_t smA[2][BM * 128];
+  __shared__ __attribute__((aligned(16))) uint8_t smB[2][BN * 128];
+  __shared__ uint32_t smAs[2][BM * 2];
+  __shared__ uint32_t smBs[2][BN * 2];
+
+  // ---- tile -> (expert, rows, columns)
+  const int tn = (int)(blockIdx.x % (unsigned)n_tiles_n);
+  int64_t slot = blockIdx.x / (unsigned)n_tiles_n;
+  int e = 0;
+  int64_t row_begin = 0, row_end = M;
+  if (offsets != nullptr) {
+    for (e = 0; e < E; ++e) {
+      const int64_t b = offsets[e], en = offsets[e + 1];
+      const int64_t t = (en - b + BM - 1) / BM;
+      if (slot < t) {
+        row_begin = b + slot * BM;
+        row_end = en;
+        break;
+      }
+      slot -= t;
+    }
+    if (e == E) return;
+  } else {
+    row_begin = slot * BM;
+    if (row_begin >= M) return;
+  }
+  const int64_t n0 = (int64_t)tn * BN;
+  const int64_t KB = K >> 1;   // code bytes per row
+  const int64_t KG = K >> 5;   // groups (scale bytes) per row
+  const uint8_t* Bx = B + (int64_t)e * N * KB;
+  const uint8_t* Bsx = Bs + (int64_t)e * N * KG;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int wm = wave / WAVES_N;
+  const int wn = wave % WAVES_N;
+  const int r32 = lane & 31;
+  const int h = lane >> 5;
+
+  // ---- per-thread global source offsets (rows clamped into the valid range)
+  int64_t offA[T::kAChunks], offB[T::kBChunks];
+  int ldsA[T::kAChunks], ldsB[T::kBChunks];
+#pragma unroll
+  for (int i = 0; i < T::kAChunks; ++i) {
+    const int idx = tid + i * T::kThreads;
+    const int row = idx >> 3;
+    int64_t gr = row_begin + row;
+    if (gr >= row_end) gr = row_end - 1;
+    offA[i] = gr * KB + (idx & 7) * 16;
+    ldsA[i] = row * 128 + (((idx & 7) ^ (row & 7)) << 4);
+  }
+#pragma unroll
+  for (int i = 0; i < T::kBChunks; ++i) {
+    const int idx = tid + i * T::kThreads;
+    const int row = idx >> 3;
+    int64_t gn = n0 + row;
+    if (gn >= N) gn = N - 1;
+    offB[i] = gn * KB + (idx & 7) * 16;
+    ldsB[i] = row * 128 + (((idx & 7) ^ (row & 7)) << 4);
+  }
+  // chunk c of a thread is the same for all its chunks: idx & 7 == tid & 7
+  const int my_c = tid & 7;
+  int64_t offAs[T::kASc], offBs[T::kBSc];
+#pragma unroll
+  for (int i = 0; i < T::kASc; ++i) {
+    const int idx = tid + i * T::kThreads;
+    const int row = idx < BM * 2 ? (idx >> 1) : 0;
+    int64_t gr = row_begin + row;
+    if (gr >= row_end) gr = row_end - 1;
+    offAs[i] = gr * KG + (idx & 1) * 4;
+  }
+#pragma unroll
+  for (int i = 0; i < T::kBSc; ++i) {
+    const int idx = tid + i * T::kThreads;
+    const int row = idx < BN * 2 ? (idx >> 1) : 0;
+    int64_t gn = n0 + row;
+    if (gn >= N) gn = N - 1;
+    offBs[i] = gn * KG + (idx & 1) * 4;
+  }
+  const int my_half = tid & 1;
+
+  uint4 ra[T::kAChunks], rb[T::kBChunks];
+  uint32_t ras[T::kASc], rbs[T::kBSc];
+
+#define MACAQ_LOAD_TILE(KT)                                                                          \
+  {                                                                                                  \
+    const int64_t g0 = (int64_t)(KT) * 8;                                                            \
+    const bool cok = g0 + my_c < KG;                                                                 \
+    const bool sok = g0 + my_half * 4 < KG;                                                          \
+    _Pragma("unroll") for (int i = 0; i < T::kAChunks; ++i) {                                        \
+      ra[i] = cok ? *reinterpret_cast<const uint4*>(A + offA[i] + g0 * 16) : make_uint4(0, 0, 0, 0); \
+    }                                                                                                \
+    _Pragma("unroll") for (int i = 0; i < T::kBChunks; ++i) {                                        \
+      rb[i] = cok ? *reinterpret_cast<const uint4*>(Bx + offB[i] + g0 * 16) : make_uint4(0, 0, 0, 0); \
+    }                                                                                                \
+    _Pragma("unroll") for (int i = 0; i < T::kASc; ++i) {                                            \
+      ras[i] = sok ? *reinterpret_cast<const uint32_t*>(As + offAs[i] + g0) : 0u;                    \
+    }                                                                                                \
+    _Pragma("unroll") for (int i = 0; i < T::kBSc; ++i) {                                            \
+      rbs[i] = sok ? *reinterpret_cast<const uint32_t*>(Bsx + offBs[i] + g0) : 0u;                   \
+    }                                                                                                \
+  }
+#define MACAQ_STORE_TILE(ST)                                                                         \
+  {                                                                                                  \
+    _Pragma("unroll") for (int i = 0; i < T::kAChunks; ++i)                                          \
+        *reinterpret_cast<uint4*>(&smA[ST][ldsA[i]]) = ra[i];                                        \
+    _Pragma("unroll") for (int i = 0; i < T::kBChunks; ++i)                                          \
+        *reinterpret_cast<uint4*>(&smB[ST][ldsB[i]]) = rb[i];                                        \
+    _Pragma("unroll") for (int i = 0; i < T::kASc; ++i) {                                            \
+      if (tid + i * T::kThreads < BM * 2) smAs[ST][tid + i * T::kThreads] = ras[i];                  \
+    }                                                                                                \
+    _Pragma("unroll") for (int i = 0; i < T::kBSc; ++i) {                                            \
+      if (tid + i * T::kThreads < BN * 2) smBs[ST][tid + i * T::kThreads] = rbs[i];                  \
+    }                                                                                                \
+  }
+
+  v16f acc[T::kFM][T::kFN];
+#pragma unroll
+  for (int mi = 0; mi < T::kFM; ++mi)
+#pragma unroll
+    for (int ni = 0; ni < T::kFN; ++ni)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[mi][ni][r] = 0.0f;
+
+  const int nk = (int)((K + 255) / 256);
+  MACAQ_LOAD_TILE(0)
+  MACAQ_STORE_TILE(0)
+  __syncthreads();
+
+  for (int kt = 0; kt < nk; ++kt) {
+    const int st = kt & 1;
+    if (kt + 1 < nk) MACAQ_LOAD_TILE(kt + 1)
+
+    uint32_t sa[T::kFM], sb[T::kFN];
+    int rowA[T::kFM], rowB[T::kFN];
+#pragma unroll
+    for (int mi = 0; mi < T::kFM; ++mi) {
+      rowA[mi] = wm * T::kTM + mi * 32 + r32;
+      sa[mi] = smAs[st][rowA[mi] * 2 + h];
+    }
+#pragma unroll
+    for (int ni = 0; ni < T::kFN; ++ni) {
+      rowB[ni] = wn * T::kTN + ni * 32 + r32;
+      sb[ni] = smBs[st][rowB[ni] * 2 + h];
+    }
+    const int sw = r32 & 7;
+    uint4 fa[T::kFM], fb[T::kFN];
+#define MACAQ_SUBSTEP(J)                                                                      \
+  {                                                                                           \
+    _Pragma("unroll") for (int mi = 0; mi < T::kFM; ++mi) fa[mi] =                            \
+        *reinterpret_cast<const uint4*>(&smA[st][rowA[mi] * 128 + (((4 * h + (J)) ^ sw) << 4)]); \
+    _Pragma("unroll") for (int ni = 0; ni < T::kFN; ++ni) fb[ni] =                            \
+        *reinterpret_cast<const uint4*>(&smB[st][rowB[ni] * 128 + (((4 * h + (J)) ^ sw) << 4)]); \
+    mfma_substep<J>(acc, fa, fb, sa, sb);                                                     \
+  }
+    MACAQ_SUBSTEP(0)
+    MACAQ_SUBSTEP(1)
+    MACAQ_SUBSTEP(2)
+    MACAQ_SUBSTEP(3)
+#undef MACAQ_SUBSTEP
+
+    if (kt + 1 < nk) MACAQ_STORE_TILE(st ^ 1)
+    __syncthreads();
+  }
+
+#undef MACAQ_LOAD_TILE
+#undef MACAQ_STORE_TILE
+
+  // ---- epilogue: lane (r32, h) of 32x32 block holds column r32 and rows
+  // 8*(r/4) + 4*h + (r%4) for accumulator register r.
+#pragma unroll
+  for (int mi = 0; mi < T::kFM; ++mi) {
+#pragma unroll
+    for (int ni = 0; ni < T::kFN; ++ni) {
+      const int64_t n = n0 + wn * T::kTN + ni * 32 + r32;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int64_t m = row_begin + wm * T::kTM + mi * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
+        if (m < row_end && n < N) Y[m * N + n] = acc[mi][ni][r];
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Direct-to-LDS variant.  Global -> LDS copies use gfx950's
+// global_load_lds_dwordx4 / _dword: lane i of one instruction writes bytes
+// [16i, 16i+16) (or [4i, 4i+4)) of a wave-uniform LDS destination, so a
+// 64-lane instruction fills one 1 KiB block (8 rows of a 128-byte K-tile
+// row) and no registers stage the data.  The lane picks its global source so
+// that the block receives the swizzled layout (position p of row r holds
+// chunk p ^ (r & 7)).  Rows past the tile's valid range and groups past K
+// read clamped (valid) addresses; their results are discarded (rows) or
+// their A codes are zeroed before the MFMA (groups of a K tail).
+// LDS per stage: A codes [BM][128], B codes [BN][128], A scales [BM][8],
+// B scales [BN][8]; two stages.
+template <int BM, int BN>
+struct LdsLayout {
+  static constexpr int kA = 0;
+  static constexpr int kB = BM * 128;
+  static constexpr int kAs = (BM + BN) * 128;
+  static constexpr int kBs = kAs + BM * 8;
+  static constexpr int kStage = kBs + BN * 8;
+};
+
+__device__ __forceinline__ void lds_copy16(const uint8_t* g, uint8_t* lds_block) {
+  __builtin_amdgcn_global_load_lds((const void*)g, (void*)lds_block, 16, 0, 0);
+}
+__device__ __forceinline__ void lds_copy4(const uint8_t* g, uint8_t* lds_block) {
+  __builtin_amdgcn_global_load_lds((const void*)g, (void*)lds_block, 4, 0, 0);
+}
+
+template <int BM, int BN, int WAVES_M, int WAVES_N>
+__global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void gemm_mxfp4_dlds_kernel(
+    const uint8_t* __restrict__ A, const uint8_t* __restrict__ As, const uint8_t* __restrict__ B,
+    const uint8_t* __restrict__ Bs, const int32_t* __restrict__ offsets, int E, int64_t M,
+    int64_t N, int64_t K, float* __restrict__ Y, int n_tiles_n) {
+  using T = GemmTile<BM, BN, WAVES_M, WAVES_N>;
+  using L = LdsLayout<BM, BN>;
+  constexpr int kWaves = WAVES_M * WAVES_N;
+  constexpr int kCodeBlocks = (BM + BN) / 8;        // 1 KiB blocks per stage
+  constexpr int kScaleBlocks = (BM + BN) * 8 / 256; // 256-byte blocks per stage
+  static_assert(kCodeBlocks % kWaves == 0 && kScaleBlocks % kWaves == 0, "blocks must split over waves");
+  extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];
+
+  // ---- tile -> (expert, rows, columns)
+  const int tn = (int)(blockIdx.x % (unsigned)n_tiles_n);
+  int64_t slot = blockIdx.x / (unsigned)n_tiles_n;
+  int e = 0;
+  int64_t row_begin = 0, row_end = M;
+  if (offsets != nullptr) {
+    for (e = 0; e < E; ++e) {
+      const int64_t b = offsets[e], en = offsets[e + 1];
+      const int64_t t = (en - b + BM - 1) / BM;
+      if (slot < t) {
+        row_begin = b + slot * BM;
+        row_end = en;
+        break;
+      }
+      slot -= t;
+    }
+    if (e == E) return;
+  } else {
+    row_begin = slot * BM;
+    if (row_begin >= M) return;
+  }
+  const int64_t n0 = (int64_t)tn * BN;
+  const int64_t KB = K >> 1;
+  const int64_t KG = K >> 5;
+  const uint8_t* Bx = B + (int64_t)e * N * KB;
+  const uint8_t* Bsx = Bs + (int64_t)e * N * KG;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int wm = wave / WAVES_N;
+  const int wn = wave % WAVES_N;
+  const int r32 = lane & 31;
+  const int h = lane >> 5;
+
+  // ---- per-lane sources of this wave's copy blocks (K-tile 0; +128 B per tile)
+  constexpr int kCB = kCodeBlocks / kWaves;
+  constexpr int kSB = kScaleBlocks / kWaves;
+  const uint8_t* csrc[kCB];
+  int cdst[kCB];
+#pragma unroll
+  for (int i = 0; i < kCB; ++i) {
+    const int blk = wave * kCB + i;
+    const int row = blk * 8 + (lane >> 3);           // row within A rows then B rows
+    const int c = (lane & 7) ^ (lane >> 3);          // chunk stored at position lane & 7
+    if (row < BM) {
+      int64_t gr = row_begin + row;
+      if (gr >= row_end) gr = row_end - 1;
+      csrc[i] = A + gr * KB + c * 16;
+    } else {
+      int64_t gn = n0 + (row - BM);
+      if (gn >= N) gn = N - 1;
+      csrc[i] = Bx + gn * KB + c * 16;
+    }
+    cdst[i] = blk * 1024;
+  }
+  const uint8_t* ssrc[kSB];
+  int sdst[kSB];
+#pragma unroll
+  for (int i = 0; i < kSB; ++i) {
+    const int blk = wave * kSB + i;
+    const int d = blk * 64 + lane;                   // dword index over A then B scale rows
+    const int row = d >> 1, half = d & 1;
+    if (row < BM) {
+      int64_t gr = row_begin + row;
+      if (gr >= row_end) gr = row_end - 1;
+      ssrc[i] = As + gr * KG + half * 4;
+    } else {
+      int64_t gn = n0 + (row - BM);
+      if (gn >= N) gn = N - 1;
+      ssrc[i] = Bsx + gn * KG + half * 4;
+    }
+    sdst[i] = L::kAs + blk * 256;
+  }
+  const int my_chunk_c = (lane & 7) ^ (lane >> 3);
+  const int my_half = lane & 1;
+
+  auto issue = [&](int kt, int st) {
+    uint8_t* base = smem + st * L::kStage;
+    const int64_t g0 = (int64_t)kt * 8;
+    // clamp groups past K to the last group (their A codes are zeroed later)
+    const int64_t cg = (g0 + my_chunk_c < KG) ? g0 : (KG - 1 - my_chunk_c);
+    const int64_t sg = (g0 + my_half * 4 < KG) ? g0 : (KG - 4 - my_half * 4);
+#pragma unroll
+    for (int i = 0; i < kCB; ++i) lds_copy16(csrc[i] + cg * 16, base + cdst[i]);
+#pragma unroll
+    for (int i = 0; i < kSB; ++i) lds_copy4(ssrc[i] + sg, base + sdst[i]);
+  };
+
+  v16f acc[T::kFM][T::kFN];
+#pragma unroll
+  for (int mi = 0; mi < T::kFM; ++mi)
+#pragma unroll
+    for (int ni = 0; ni < T::kFN; ++ni)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[mi][ni][r] = 0.0f;
+
+  const int nk = (int)((K + 255) / 256);
+  issue(0, 0);
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+
+  const int sw = r32 & 7;
+  for (int kt = 0; kt < nk; ++kt) {
+    const int st = kt & 1;
+    if (kt + 1 < nk) issue(kt + 1, st ^ 1);
+    const uint8_t* base = smem + st * L::kStage;
+    // groups 4..7 of a K tail of 128 are past K: zero lane half 1's A codes
+    const bool zero_hi = (h == 1) && ((int64_t)kt * 8 + 4 >= KG);
+
+    uint32_t sa[T::kFM], sb[T::kFN];
+    int rowA[T::kFM], rowB[T::kFN];
+#pragma unroll
+    for (int mi = 0; mi < T::kFM; ++mi) {
+      rowA[mi] = wm * T::kTM + mi * 32 + r32;
+      sa[mi] = *reinterpret_cast<const uint32_t*>(base + L::kAs + rowA[mi] * 8 + h * 4);
+    }
+#pragma unroll
+    for (int ni = 0; ni < T::kFN; ++ni) {
+      rowB[ni] = wn * T::kTN + ni * 32 + r32;
+      sb[ni] = *reinterpret_cast<const uint32_t*>(base + L::kBs + rowB[ni] * 8 + h * 4);
+    }
+    uint4 fa[T::kFM], fb[T::kFN];
+#define MACAQ_DLDS_SUBSTEP(J)                                                                        \
+  {                                                                                                  \
+    _Pragma("unroll") for (int mi = 0; mi < T::kFM; ++mi) {                                          \
+      fa[mi] = *reinterpret_cast<const uint4*>(base + L::kA + rowA[mi] * 128 + (((4 * h + (J)) ^ sw) << 4)); \
+      if (zero_hi) fa[mi] = make_uint4(0, 0, 0, 0);                                                  \
+    }                                                                                                \
+    _Pragma("unroll") for (int ni = 0; ni < T::kFN; ++ni) fb[ni] =                                   \
+        *reinterpret_cast<const uint4*>(base + L::kB + rowB[ni] * 128 + (((4 * h + (J)) ^ sw) << 4)); \
+    mfma_substep<J>(acc, fa, fb, sa, sb);                                                            \
+  }
+    MACAQ_DLDS_SUBSTEP(0)
+    MACAQ_DLDS_SUBSTEP(1)
+    MACAQ_DLDS_SUBSTEP(2)
+    MACAQ_DLDS_SUBSTEP(3)
+#undef MACAQ_DLDS_SUBSTEP
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+  }
+
+#pragma unroll
+  for (int mi = 0; mi < T::kFM; ++mi) {
+#pragma unroll
+    for (int ni = 0; ni < T::kFN; ++ni) {
+      const int64_t n = n0 + wn * T::kTN + ni * 32 + r32;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int64_t m = row_begin + wm * T::kTM + mi * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
+        if (m < row_end && n < N) Y[m * N + n] = acc[mi][ni][r];
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Pipelined variant: a ring of STAGES LDS buffers of K-tiles of BK (128 or
+// 256) filled by direct-to-LDS copies issued with inline assembly.  The
+// copies have no register results; their completion is tracked explicitly
+// with s_waitcnt vmcnt(n), so up to STAGES-1 K-tiles are in flight while a
+// tile is consumed (the builtin form makes the compiler wait for every
+// outstanding copy before any LDS read, which serializes the ring).  One
+// s_barrier per K-tile both publishes the newest tile and retires the buffer
+// the next copy overwrites.
+//
+// LDS row of a K-tile: BK/2 bytes = CPR chunks of 16 bytes (CPR = BK/32
+// groups); chunk c of row r sits at position c ^ f(r), f(r) = (r / (8/CPR))
+// mod CPR, so the 16-byte fragment reads of 8 consecutive rows fall into 8
+// different 16-byte bank groups.  Scale bytes: [rows][CPR].
+// Lane half h of MFMA sub-step j takes group h*CPR/2 + j; its CPR/2 scale
+// bytes are contiguous and the instruction's op_sel picks byte j.
+//
+// Block order: consecutive block indices go to different XCDs (round
+// robin), so the index is remapped so that the blocks resident on one XCD
+// form compact groups of tiles (GROUP_M tile rows) that share A and B
+// panels in that XCD's L2.
+
+constexpr int kNumXcd = 8;
+
+template <int VM>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(VM >= 0 && VM < 64, "vmcnt range");
+  // gfx9 s_waitcnt: vmcnt[3:0] at bits 3:0, vmcnt[5:4] at bits 15:14,
+  // expcnt (7) and lgkmcnt (15) left at their maxima (no wait).
+  __builtin_amdgcn_s_waitcnt((VM & 0xF) | ((VM >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+__device__ __forceinline__ void dma16(const uint8_t* g, uint32_t lds_addr) {
+  asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(g), "{m0}"(lds_addr) : "memory");
+}
+__device__ __forceinline__ void dma4(const uint8_t* g, uint32_t lds_addr) {
+  asm volatile("global_load_lds_dword %0, off" ::"v"(g), "{m0}"(lds_addr) : "memory");
+}
+
+template <int BM, int BN, int BK, int SWZ = 0>
+struct PipeLayout {
+  static constexpr int kCPR = BK / 32;              // chunks (groups) per tile row
+  static constexpr int kRowBytes = BK / 2;
+  static constexpr int kRowsPerBankRow = 8 / kCPR;  // rows sharing one 128-byte bank row
+  static constexpr int kA = 0;
+  static constexpr int kB = BM * kRowBytes;
+  static constexpr int kAs = (BM + BN) * kRowBytes;
+  static constexpr int kBs = kAs + BM * kCPR;
+  static constexpr int kStage = kBs + BN * kCPR;
+  static constexpr int kCodeBlocks = (BM + BN) * kRowBytes / 1024;
+  static constexpr int kScaleBlocks = (BM + BN) * kCPR / 256;
+  __host__ __device__ static constexpr int swz(int r) { return ((r >> SWZ) / kRowsPerBankRow) & (kCPR - 1); }
+};
+
+// Tile coordinates from the block index (XCD-aware order).
+__device__ __forceinline__ void tile_of_block(int bid, int nblocks, int tiles_m, int tiles_n, int group_m,
+                                              int* tm, int* tn) {
+  int logical = bid;
+  if (nblocks % kNumXcd == 0) logical = (bid % kNumXcd) * (nblocks / kNumXcd) + bid / kNumXcd;
+  const int per_group = group_m * tiles_n;
+  const int g = logical / per_group;
+  const int first_m = g * group_m;
+  const int gm = (tiles_m - first_m) < group_m ? (tiles_m - first_m) : group_m;
+  const int in = logical - g * per_group;
+  *tm = first_m + in % gm;
+  *tn = in / gm;
+}
+
+template <int BM, int BN, int WAVES_M, int WAVES_N, int BK, int STAGES>
+__global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void gemm_mxfp4_pipe_kernel(
+    const uint8_t* __restrict__ A, const uint8_t* __restrict__ As, const uint8_t* __restrict__ B,
+    const uint8_t* __restrict__ Bs, const int32_t* __restrict__ offsets, int E, int64_t M,
+    int64_t N, int64_t K, float* __restrict__ Y, int tiles_m, int tiles_n, int group_m) {
+  using T = GemmTile<BM, BN, WAVES_M, WAVES_N>;
+  using L = PipeLayout<BM, BN, BK, 1>;
+  constexpr int kWaves = WAVES_M * WAVES_N;
+  constexpr int kCPR = L::kCPR;
+  // Copies per wave per K-tile.  When a stage's blocks do not split evenly
+  // over the waves, the last waves repeat blocks of the first ones (identical
+  // bytes to the same LDS place), so every wave issues the same number of
+  // copies and one vmcnt threshold fits all waves.
+  constexpr int kCB = (L::kCodeBlocks + kWaves - 1) / kWaves;
+  constexpr int kSB = (L::kScaleBlocks + kWaves - 1) / kWaves;
+  constexpr int kLPT = kCB + kSB;
+  static_assert((STAGES - 2) * kLPT < 64, "vmcnt range");
+  extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];
+
+  // ---- tile -> (expert, rows, columns)
+  int tm, tn;
+  tile_of_block((int)blockIdx.x, (int)gridDim.x, tiles_m, tiles_n, group_m, &tm, &tn);
+  int64_t slot = tm;
+  int e = 0;
+  int64_t row_begin = 0, row_end = M;
+  if (offsets != nullptr) {
+    for (e = 0; e < E; ++e) {
+      const int64_t b = offsets[e], en = offsets[e + 1];
+      const int64_t t = (en - b + BM - 1) / BM;
+      if (slot < t) {
+        row_begin = b + slot * BM;
+        row_end = en;
+        break;
+      }
+      slot -= t;
+    }
+    if (e == E) return;
+  } else {
+    row_begin = slot * BM;
+    if (row_begin >= M) return;
+  }
+  const int64_t n0 = (int64_t)tn * BN;
+  if (n0 >= N) return;
+  const int64_t KB = K >> 1;
+  const int64_t KG = K >> 5;
+  const uint8_t* Bx = B + (int64_t)e * N * KB;
+  const uint8_t* Bsx = Bs + (int64_t)e * N * KG;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (SGPR)
+  const int wm = wave / WAVES_N;
+  const int wn = wave % WAVES_N;
+  const int r32 = lane & 31;
+  const int h = lane >> 5;
+  const uint32_t lds_base = (uint32_t)(uintptr_t)smem;
+
+  // ---- per-lane copy sources for K-tile 0 (advance by BK/2 code bytes and
+  // CPR scale bytes per K-tile) and wave-uniform LDS offsets within a stage
+  const uint8_t* csrc[kCB];
+#pragma unroll
+  for (int i = 0; i < kCB; ++i) {
+    const int blk = (wave * kCB + i) % L::kCodeBlocks;
+    constexpr int rows_per_blk = 1024 / L::kRowBytes;
+    const int row = blk * rows_per_blk + lane / kCPR;
+    const int c = (lane % kCPR) ^ L::swz(row);
+    if (row < BM) {
+      int64_t gr = row_begin + row;
+      if (gr >= row_end) gr = row_end - 1;
+      csrc[i] = A + gr * KB + c * 16;
+    } else {
+      int64_t gn = n0 + (row - BM);
+      if (gn >= N) gn = N - 1;
+      csrc[i] = Bx + gn * KB + c * 16;
+    }
+  }
+  const uint8_t* ssrc[kSB];
+#pragma unroll
+  for (int i = 0; i < kSB; ++i) {
+    const int blk = (wave * kSB + i) % L::kScaleBlocks;
+    const int d = blk * 64 + lane;            // dword of the [rows][CPR] scale tile
+    const int row = d / (kCPR / 4), part = d % (kCPR / 4);
+    if (row < BM) {
+      int64_t gr = row_begin + row;
+      if (gr >= row_end) gr = row_end - 1;
+      ssrc[i] = As + gr * KG + part * 4;
+    } else {
+      int64_t gn = n0 + (row - BM);
+      if (gn >= N) gn = N - 1;
+      ssrc[i] = Bsx + gn * KG + part * 4;
+    }
+  }
+
+  auto issue = [&](int kt, int st) {
+    const uint32_t base = lds_base + (uint32_t)(st * L::kStage);
+    const int64_t cofs = (int64_t)kt * L::kRowBytes;
+    const int64_t sofs = (int64_t)kt * kCPR;
+#pragma unroll
+    for (int i = 0; i < kCB; ++i)
+      dma16(csrc[i] + cofs, base + (uint32_t)(L::kA + ((wave * kCB + i) % L::kCodeBlocks) * 1024));
+#pragma unroll
+    for (int i = 0; i < kSB; ++i)
+      dma4(ssrc[i] + sofs, base + (uint32_t)(L::kAs + ((wave * kSB + i) % L::kScaleBlocks) * 256));
+  };
+
+  v16f acc[T::kFM][T::kFN];
+#pragma unroll
+  for (int mi = 0; mi < T::kFM; ++mi)
+#pragma unroll
+    for (int ni = 0; ni < T::kFN; ++ni)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[mi][ni][r] = 0.0f;
+
+  const int nk = (int)(K / BK);
+#pragma unroll
+  for (int s = 0; s < STAGES - 1; ++s)
+    if (s < nk) issue(s, s);
+
+  int rowA[T::kFM], rowB[T::kFN];
+#pragma unroll
+  for (int mi = 0; mi < T::kFM; ++mi) rowA[mi] = wm * T::kTM + mi * 32 + r32;
+#pragma unroll
+  for (int ni = 0; ni < T::kFN; ++ni) rowB[ni] = wn * T::kTN + ni * 32 + r32;
+  const int sw = L::swz(r32);
+  const int sshift = (kCPR == 4) ? 16 * h : 0;   // scale bytes of lane half h
+  const int sofs_h = (kCPR == 8) ? 4 * h : 0;
+
+  for (int kt = 0; kt < nk; ++kt) {
+    // tile kt has landed once at most min(STAGES-2, nk-1-kt) later tiles remain in flight
+    const int ahead = nk - 1 - kt;
+    if (ahead >= STAGES - 2) {
+      wait_vmcnt<(STAGES - 2) * kLPT>();
+    } else if (STAGES > 3 && ahead == 2) {
+      wait_vmcnt<(STAGES > 3 ? 2 : 0) * kLPT>();
+    } else if (STAGES > 2 && ahead == 1) {
+      wait_vmcnt<kLPT>();
+    } else {
+      wait_vmcnt<0>();
+    }
+    __builtin_amdgcn_s_barrier();
+    if (kt + STAGES - 1 < nk) issue(kt + STAGES - 1, (kt + STAGES - 1) % STAGES);
+
+    const uint8_t* base = smem + (kt % STAGES) * L::kStage;
+    uint32_t sa[T::kFM], sb[T::kFN];
+#pragma unroll
+    for (int mi = 0; mi < T::kFM; ++mi)
+      sa[mi] = *reinterpret_cast<const uint32_t*>(base + L::kAs + rowA[mi] * kCPR + sofs_h) >> sshift;
+#pragma unroll
+    for (int ni = 0; ni < T::kFN; ++ni)
+      sb[ni] = *reinterpret_cast<const uint32_t*>(base + L::kBs + rowB[ni] * kCPR + sofs_h) >> sshift;
+    uint4 fa[T::kFM], fb[T::kFN];
+#define MACAQ_PIPE_SUBSTEP(J)                                                                         \
+  {                                                                                                   \
+    _Pragma("unroll") for (int mi = 0; mi < T::kFM; ++mi) fa[mi] = *reinterpret_cast<const uint4*>(   \
+        base + L::kA + rowA[mi] * L::kRowBytes + (((h * (kCPR / 2) + (J)) ^ sw) << 4));               \
+    _Pragma("unroll") for (int ni = 0; ni < T::kFN; ++ni) fb[ni] = *reinterpret_cast<const uint4*>(   \
+        base + L::kB + rowB[ni] * L::kRowBytes + (((h * (kCPR / 2) + (J)) ^ sw) << 4));               \
+    mfma_substep<J>(acc, fa, fb, sa, sb);                                                             \
+  }
+    MACAQ_PIPE_SUBSTEP(0)
+    MACAQ_PIPE_SUBSTEP(1)
+    if constexpr (kCPR == 8) {
+      MACAQ_PIPE_SUBSTEP(2)
+      MACAQ_PIPE_SUBSTEP(3)
+    }
+#undef MACAQ_PIPE_SUBSTEP
+  }
+
+  // ---- epilogue: lane (r32, h) of a 32x32 block holds column r32 and rows
+  // 8*(r/4) + 4*h + (r%4) of accumulator register r
+  const bool interior = (row_begin + BM <= row_end) && (n0 + BN <= N);
+#pragma unroll
+  for (int mi = 0; mi < T::kFM; ++mi) {
+#pragma unroll
+    for (int ni = 0; ni < T::kFN; ++ni) {
+      const int64_t n = n0 + wn * T::kTN + ni * 32 + r32;
+      const int64_t mb = row_begin + wm * T::kTM + mi * 32 + 4 * h;
+      if (interior) {
+        float* yp = Y + mb * N + n;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) yp[(8 * (r >> 2) + (r & 3)) * N] = acc[mi][ni][r];
+      } else {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int64_t m = mb + 8 * (r >> 2) + (r & 3);
+          if (m < row_end && n < N) Y[m * N + n] = acc[mi][ni][r];
+        }
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Two-stage, BK = 256 variant with register double-buffering of the MFMA
+// fragments: the LDS reads of sub-step j+1 are issued before the MFMAs of
+// sub-step j, so with one wave per SIMD the LDS latency hides behind the
+// matrix cores.  The copy of the next K-tile is issued unconditionally (the
+// last iteration re-reads the final tile into the idle buffer) so that the
+// loop body is a single basic block the scheduler can interleave.
+// SCHED != 0 adds scheduling groups that alternate LDS reads and MFMAs.
+template <int BM, int BN, int WAVES_M, int WAVES_N, int SCHED>
+__global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void gemm_mxfp4_db_kernel(
+    const uint8_t* __restrict__ A, const uint8_t* __restrict__ As, const uint8_t* __restrict__ B,
+    const uint8_t* __restrict__ Bs, const int32_t* __restrict__ offsets, int E, int64_t M,
+    int64_t N, int64_t K, float* __restrict__ Y, int tiles_m, int tiles_n, int group_m) {
+  constexpr int BK = 256;
+  using T = GemmTile<BM, BN, WAVES_M, WAVES_N>;
+  using L = PipeLayout<BM, BN, BK, 1>;
+  constexpr int kWaves = WAVES_M * WAVES_N;
+  constexpr int kCB = (L::kCodeBlocks + kWaves - 1) / kWaves;
+  constexpr int kSB = (L::kScaleBlocks + kWaves - 1) / kWaves;
+  extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];
+
+  int tm, tn;
+  tile_of_block((int)blockIdx.x, (int)gridDim.x, tiles_m, tiles_n, group_m, &tm, &tn);
+  int64_t slot = tm;
+  int e = 0;
+  int64_t row_begin = 0, row_end = M;
+  if (offsets != nullptr) {
+    for (e = 0; e < E; ++e) {
+      const int64_t b = offsets[e], en = offsets[e + 1];
+      const int64_t t = (en - b + BM - 1) / BM;
+      if (slot < t) {
+        row_begin = b + slot * BM;
+        row_end = en;
+        break;
+      }
+      slot -= t;
+    }
+    if (e == E) return;
+  } else {
+    row_begin = slot * BM;
+    if (row_begin >= M) return;
+  }
+  const int64_t n0 = (int64_t)tn * BN;
+  if (n0 >= N) return;
+  const int64_t KB = K >> 1;
+  const int64_t KG = K >> 5;
+  const uint8_t* Bx = B + (int64_t)e * N * KB;
+  const uint8_t* Bsx = Bs + (int64_t)e * N * KG;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave / WAVES_N;
+  const int wn = wave % WAVES_N;
+  const int r32 = lane & 31;
+  const int h = lane >> 5;
+  const uint32_t lds_base = (uint32_t)(uintptr_t)smem;
+
+  const uint8_t* csrc[kCB];
+#pragma unroll
+  for (int i = 0; i < kCB; ++i) {
+    const int blk = (wave * kCB + i) % L::kCodeBlocks;
+    const int row = blk * 8 + (lane >> 3);
+    const int c = (lane & 7) ^ L::swz(row);
+    if (row < BM) {
+      int64_t gr = row_begin + row;
+      if (gr >= row_end) gr = row_end - 1;
+      csrc[i] = A + gr * KB + c * 16;
+    } else {
+      int64_t gn = n0 + (row - BM);
+      if (gn >= N) gn = N - 1;
+      csrc[i] = Bx + gn * KB + c * 16;
+    }
+  }
+  const uint8_t* ssrc[kSB];
+#pragma unroll
+  for (int i = 0; i < kSB; ++i) {
+    const int blk = (wave * kSB + i) % L::kScaleBlocks;
+    const int d = blk * 64 + lane;
+    const int row = d >> 1, part = d & 1;
+    if (row < BM) {
+      int64_t gr = row_begin + row;
+      if (gr >= row_end) gr = row_end - 1;
+      ssrc[i] = As + gr * KG + part * 4;
+    } else {
+      int64_t gn = n0 + (row - BM);
+      if (gn >= N) gn = N - 1;
+      ssrc[i] = Bsx + gn * KG + part * 4;
+    }
+  }
+  // K tail of 128 (K % 256 == 128): chunks / scale dwords past K read the
+  // last valid ones instead; lane half 1's A codes are zeroed for that tile.
+  const int my_c = (lane & 7) ^ L::swz(lane >> 3);
+  const int nk = (int)((K + BK - 1) / BK);
+
+  auto issue = [&](int kt, int st) {
+    const uint32_t base = lds_base + (uint32_t)(st * L::kStage);
+    const int64_t g0 = (int64_t)kt * 8;
+    const int64_t cofs = ((g0 + my_c < KG) ? g0 : (KG - 1 - my_c)) * 16;
+#pragma unroll
+    for (int i = 0; i < kCB; ++i)
+      dma16(csrc[i] + cofs, base + (uint32_t)(L::kA + ((wave * kCB + i) % L::kCodeBlocks) * 1024));
+#pragma unroll
+    for (int i = 0; i < kSB; ++i) {
+      const int part = lane & 1;
+      const int64_t sofs = (g0 + part * 4 < KG) ? g0 : (KG - 4 - part * 4);
+      dma4(ssrc[i] + sofs, base + (uint32_t)(L::kAs + ((wave * kSB + i) % L::kScaleBlocks) * 256));
+    }
+  };
+
+  v16f acc[T::kFM][T::kFN];
+#pragma unroll
+  for (int mi = 0; mi < T::kFM; ++mi)
+#pragma unroll
+    for (int ni = 0; ni < T::kFN; ++ni)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[mi][ni][r] = 0.0f;
+
+  int rowA[T::kFM], rowB[T::kFN];
+#pragma unroll
+  for (int mi = 0; mi < T::kFM; ++mi) rowA[mi] = wm * T::kTM + mi * 32 + r32;
+#pragma unroll
+  for (int ni = 0; ni < T::kFN; ++ni) rowB[ni] = wn * T::kTN + ni * 32 + r32;
+  const int sw = L::swz(r32);
+
+  issue(0, 0);
+  for (int kt = 0; kt < nk; ++kt) {
+    wait_vmcnt<0>();
+    __builtin_amdgcn_s_barrier();
+    issue(kt + 1 < nk ? kt + 1 : kt, (kt + 1) & 1);
+    const uint8_t* base = smem + (kt & 1) * L::kStage;
+    const bool zero_hi = (h == 1) && ((int64_t)kt * 8 + 4 >= KG);
+    uint32_t sa[T::kFM], sb[T::kFN];
+#pragma unroll
+    for (int mi = 0; mi < T::kFM; ++mi) sa[mi] = *reinterpret_cast<const uint32_t*>(base + L::kAs + rowA[mi] * 8 + h * 4);
+#pragma unroll
+    for (int ni = 0; ni < T::kFN; ++ni) sb[ni] = *reinterpret_cast<const uint32_t*>(base + L::kBs + rowB[ni] * 8 + h * 4);
+    uint4 fa[2][T::kFM], fb[2][T::kFN];
+    auto load_frags = [&](int j, int buf) {
+#pragma unroll
+      for (int mi = 0; mi < T::kFM; ++mi) {
+        fa[buf][mi] = *reinterpret_cast<const uint4*>(base + L::kA + rowA[mi] * 128 + (((4 * h + j) ^ sw) << 4));
+        if (zero_hi) fa[buf][mi] = make_uint4(0, 0, 0, 0);
+      }
+#pragma unroll
+      for (int ni = 0; ni < T::kFN; ++ni)
+        fb[buf][ni] = *reinterpret_cast<const uint4*>(base + L::kB + rowB[ni] * 128 + (((4 * h + j) ^ sw) << 4));
+    };
+    load_frags(0, 0);
+    load_frags(1, 1);
+    mfma_substep<0>(acc, fa[0], fb[0], sa, sb);
+    if (SCHED) {
+#pragma unroll
+      for (int q = 0; q < T::kFM + T::kFN; ++q) {
+        __builtin_amdgcn_sched_group_barrier(0x008, (T::kFM * T::kFN) / (T::kFM + T::kFN), 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+    }
+    load_frags(2, 0);
+    mfma_substep<1>(acc, fa[1], fb[1], sa, sb);
+    if (SCHED) {
+#pragma unroll
+      for (int q = 0; q < T::kFM + T::kFN; ++q) {
+        __builtin_amdgcn_sched_group_barrier(0x008, (T::kFM * T::kFN) / (T::kFM + T::kFN), 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+    }
+    load_frags(3, 1);
+    mfma_substep<2>(acc, fa[0], fb[0], sa, sb);
+    mfma_substep<3>(acc, fa[1], fb[1], sa, sb);
+  }
+  wait_vmcnt<0>();
+
+  const bool interior = (row_begin + BM <= row_end) && (n0 + BN <= N);
+#pragma unroll
+  for (int mi = 0; mi < T::kFM; ++mi) {
+#pragma unroll
+    for (int ni = 0; ni < T::kFN; ++ni) {
+      const int64_t n = n0 + wn * T::kTN + ni * 32 + r32;
+      const int64_t mb = row_begin + wm * T::kTM + mi * 32 + 4 * h;
+      if (interior) {
+        float* yp = Y + mb * N + n;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) yp[(8 * (r >> 2) + (r & 3)) * N] = acc[mi][ni][r];
+      } else {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int64_t m = mb + 8 * (r >> 2) + (r & 3);
+          if (m < row_end && n < N) Y[m * N + n] = acc[mi][ni][r];
+        }
+      }
+    }
+  }
+}
+
+}  // namespace macaq

@@ -243,3 +243,103 @@ def test_linear_deterministic():
     y1 = mx.linear(x, s, wc, wsc)
     y2 = mx.linear(x, s, wc, wsc)
     assert torch.equal(y1, y2)
+
+
+# ------------------------------------------------------------ every GEMM kernel variant
+
+TILES = ["256x256", "256x128", "128x128"]
+TILE_SHAPES = [
+    ("ragged M N", (300, 260, 1024)),
+    ("K tail 128", (257, 129, 640)),
+    ("single row tile", (5, 384, 256)),
+]
+
+
+@pytest.mark.parametrize("tile", TILES)
+@pytest.mark.parametrize("name,shape", TILE_SHAPES, ids=[n for n, _ in TILE_SHAPES])
+def test_gemm_each_tile_variant(tile, name, shape, monkeypatch):
+    say(f"gemm tile={tile} {name} {shape}")
+    monkeypatch.setenv("MACAQ_GEMM_TILE", tile)
+    M, N, K = shape
+    rng = np.random.default_rng(M + N + K)
+    ac = rng.integers(0, 256, (M, K // 2), dtype=np.uint8)
+    asc = rng.integers(110, 140, (M, K // 32), dtype=np.uint8)
+    wc = rng.integers(0, 256, (N, K // 2), dtype=np.uint8)
+    wsc = rng.integers(110, 140, (N, K // 32), dtype=np.uint8)
+    y = mx.gemm(*(torch.from_numpy(a).to(DEV) for a in (ac, asc, wc, wsc)))
+    y_ref, S = oracle.gemm(ac, asc, wc, wsc)
+    _check_y(y.cpu().numpy(), y_ref, S)
+
+
+@pytest.mark.parametrize("tile", TILES)
+def test_gemm_grouped_each_tile_variant(tile, monkeypatch):
+    say(f"gemm grouped tile={tile}")
+    monkeypatch.setenv("MACAQ_GEMM_TILE", tile)
+    E, N, K = 5, 200, 512
+    counts = np.array([3, 0, 270, 1, 300])
+    off = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    M = int(off[-1])
+    rng = np.random.default_rng(11)
+    ac = rng.integers(0, 256, (M, K // 2), dtype=np.uint8)
+    asc = rng.integers(110, 140, (M, K // 32), dtype=np.uint8)
+    wc = rng.integers(0, 256, (E, N, K // 2), dtype=np.uint8)
+    wsc = rng.integers(110, 140, (E, N, K // 32), dtype=np.uint8)
+    t = [torch.from_numpy(a).to(DEV) for a in (ac, asc, wc, wsc)]
+    y = mx.gemm(*t, offsets=torch.from_numpy(off).to(DEV))
+    y_ref, S = oracle.gemm(ac, asc, wc, wsc, off)
+    _check_y(y.cpu().numpy(), y_ref, S)
+
+
+# ------------------------------------------------------------ decode-sized GEMM (M <= 32)
+
+DECODE_SHAPES = [
+    ("M1 8 chunks", (1, 200, 2048)),
+    ("M3 4 chunks", (3, 5000, 1024)),
+    ("M12 ragged N", (12, 1000, 2560)),
+    ("M32 2 chunks", (32, 20000, 512)),
+    ("M8 odd chunks", (8, 96, 256 * 7)),
+    ("M5 16 waves", (5, 70, 256 * 65)),
+    ("M32 8 waves", (32, 64, 256 * 25)),
+]
+
+
+@pytest.mark.parametrize("name,shape", DECODE_SHAPES, ids=[n for n, _ in DECODE_SHAPES])
+def test_gemm_decode(name, shape):
+    say(f"gemm decode {name} {shape}")
+    M, N, K = shape
+    rng = np.random.default_rng(M * 131 + N)
+    ac = rng.integers(0, 256, (M, K // 2), dtype=np.uint8)
+    asc = rng.integers(110, 140, (M, K // 32), dtype=np.uint8)
+    wc = rng.integers(0, 256, (N, K // 2), dtype=np.uint8)
+    wsc = rng.integers(110, 140, (N, K // 32), dtype=np.uint8)
+    t = [torch.from_numpy(a).to(DEV) for a in (ac, asc, wc, wsc)]
+    assert mx.lib().macaq_gemm_workspace_bytes(M, N, K, 1) == 0
+    y1 = mx.gemm(*t)
+    y2 = mx.gemm(*t)
+    y_ref, S = oracle.gemm(ac, asc, wc, wsc)
+    _check_y(y1.cpu().numpy(), y_ref, S)
+    assert torch.equal(y1, y2)
+
+
+DECODE_LINEAR = [
+    ("M1 fp32 tiny-shaped", dict(cfg=1, shape=(1, 96, 512))),
+    ("M1", dict(cfg=4, shape=(1, 640, 2048))),
+    ("M2 16 waves", dict(cfg=4, shape=(2, 300, 256 * 70))),
+    ("M8", dict(cfg=4, shape=(8, 512, 1024))),
+    ("M32", dict(cfg=4, shape=(32, 256, 2560))),
+]
+
+
+@pytest.mark.parametrize("flags", [mx.PATH_FUSED, mx.PATH_UNFUSED, mx.PATH_AUTO])
+@pytest.mark.parametrize("name,kw", DECODE_LINEAR, ids=[n for n, _ in DECODE_LINEAR])
+def test_linear_decode_paths(name, kw, flags):
+    say(f"linear decode {name} flags={flags}")
+    wl = workloads.make(**kw)
+    wc, wsc = gpu_prepare(wl)
+    x, s = wl.x.to(DEV), wl.s.to(DEV)
+    y = mx.linear(x, s, wc, wsc, flags=flags)
+    y_again = mx.linear(x, s, wc, wsc, flags=flags)
+    rwc, rws = oracle_prepare(wl, 0)
+    y_ref, S = oracle.linear(host(wl.x), wl.s.numpy(), rwc, rws)
+    _check_y(y.cpu().numpy(), y_ref, S)
+    assert torch.equal(y, y_again)
