@@ -19,6 +19,8 @@
 //
 // The kernel is HBM-bound: per element it reads 2 bytes (bf16) and writes
 // 17/32 bytes.
+#include <cstdlib>
+
 #include "mx_common.h"
 
 namespace macaq {
@@ -159,25 +161,215 @@ __global__ void encode_e2m1_kernel(const float* __restrict__ v, int64_t n, uint8
     if (i0 + j < n) out[i0 + j] = (uint8_t)((p >> (4 * j)) & 0xFu);
 }
 
+// ---------------------------------------------------------------------------
+// One-lane-per-group kernel (the launcher's choice).  A wave covers 64
+// groups (2048 columns) of a row; the row segment is read with coalesced
+// 16-byte loads (lane l, instruction i: bytes 1024i + 16l), written to a
+// wave-private LDS buffer whose 32-value groups sit 16 bytes apart more than
+// their size (no bank conflicts on the per-group reads), and each lane then
+// reads its own group.  All five butterfly stages run in the lane's
+// registers.  The next row's loads are in flight while a row is
+// transformed.
+//
+// Normalization folded into the quantization multiply: amax(x') equals
+// RNE(max|u| * C) because rounding is monotone, and for scale bytes 3..250
+// RNE(u * C * 2^(127-b)) equals RNE(u * C) * 2^(127-b) for every value that
+// can reach a nonzero code (C * 2^(127-b) is an exact normal float; values
+// whose x' would be subnormal land below 0.25 either way and keep their
+// sign).  Lanes with other scale bytes take the two-multiply path.
+template <int EB>  // bytes per input element (2 = bf16, 4 = fp32)
+struct GroupIo {
+  static constexpr int kGroupBytes = 32 * EB;
+  static constexpr int kLdsGroup = kGroupBytes + 16;         // padded stride
+  static constexpr int kWaveLds = 64 * kLdsGroup;            // one row segment
+  static constexpr int kLoads = 64 * kGroupBytes / 1024;     // 16-byte loads per lane
+};
+
+template <int EB>
+__device__ __forceinline__ void widen_group(const uint4 (&q)[EB * 2], float (&t)[32]) {
+  if constexpr (EB == 2) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      t[8 * i + 0] = bf16_lo(q[i].x); t[8 * i + 1] = bf16_hi(q[i].x);
+      t[8 * i + 2] = bf16_lo(q[i].y); t[8 * i + 3] = bf16_hi(q[i].y);
+      t[8 * i + 4] = bf16_lo(q[i].z); t[8 * i + 5] = bf16_hi(q[i].z);
+      t[8 * i + 6] = bf16_lo(q[i].w); t[8 * i + 7] = bf16_hi(q[i].w);
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      t[4 * i + 0] = __uint_as_float(q[i].x); t[4 * i + 1] = __uint_as_float(q[i].y);
+      t[4 * i + 2] = __uint_as_float(q[i].z); t[4 * i + 3] = __uint_as_float(q[i].w);
+    }
+  }
+}
+
+// Unnormalized butterfly, stages h = 1, 2, 4, 8, 16 (lower a+b, upper a-b).
+__device__ __forceinline__ void fwht32_regs(float (&t)[32]) {
+#pragma unroll
+  for (int h = 1; h < 32; h <<= 1) {
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+      if ((i & h) == 0) {
+        const float a = t[i], b = t[i + h];
+        t[i] = a + b;
+        t[i + h] = a - b;
+      }
+    }
+  }
+}
+
+// Quantize the lane's group u (unnormalized butterfly output): 16 code bytes
+// and the E8M0 byte.
+__device__ __forceinline__ void quantize_group(const float (&u)[32], uint4* codes_out, uint32_t* b_out) {
+  float m = fabsf(u[0]);
+#pragma unroll
+  for (int i = 1; i < 32; ++i) m = fmaxf(m, fabsf(u[i]));
+  const float c = hadamard_norm();
+  const uint32_t b = e8m0_from_amax(m * c);  // = amax of x' (monotone rounding)
+  float v[32];
+  if (b >= 3u && b <= 250u) {
+    const float cs = __uint_as_float(__float_as_uint(c) + ((127u - b) << 23));  // C * 2^(127-b), exact
+#pragma unroll
+    for (int i = 0; i < 32; ++i) v[i] = u[i] * cs;
+  } else {
+    const float inv = inv_scale(b);
+#pragma unroll
+    for (int i = 0; i < 32; ++i) v[i] = (u[i] * c) * inv;
+  }
+  uint32_t w[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    uint32_t r = 0;
+    r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, v[8 * q + 0], v[8 * q + 1], 1.0f, 0);
+    r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, v[8 * q + 2], v[8 * q + 3], 1.0f, 1);
+    r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, v[8 * q + 4], v[8 * q + 5], 1.0f, 2);
+    r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, v[8 * q + 6], v[8 * q + 7], 1.0f, 3);
+    w[q] = r;
+  }
+  *codes_out = make_uint4(w[0], w[1], w[2], w[3]);
+  *b_out = b;
+}
+
+template <int EB, bool RECIP>
+__global__ __launch_bounds__(256) void act_quant_lane_kernel(
+    const void* __restrict__ x, const float* __restrict__ s, const int32_t* __restrict__ offsets, int E,
+    int64_t rows_per_expert, int64_t M, int64_t K, uint8_t* __restrict__ codes, uint8_t* __restrict__ scales,
+    int rows_per_wave) {
+  using IO = GroupIo<EB>;
+  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+  const int lane = threadIdx.x & 63;
+  const int wave_in_block = threadIdx.x >> 6;
+  const int64_t wave = (int64_t)blockIdx.x * 4 + wave_in_block;
+  const int64_t KG = K >> 5;
+  const int64_t nseg = ceil_div(KG, 64);
+  const int64_t seg = wave % nseg;
+  const int64_t r0 = (wave / nseg) * rows_per_wave;
+  if (r0 >= M) return;
+  const int64_t r1 = (r0 + rows_per_wave) < M ? (r0 + rows_per_wave) : M;
+  const int64_t g = seg * 64 + lane;           // this lane's group
+  const bool active = g < KG;
+  const int64_t seg_bytes_valid = (KG - seg * 64 < 64 ? KG - seg * 64 : 64) * IO::kGroupBytes;
+  uint8_t* buf = lds + wave_in_block * IO::kWaveLds;
+
+  // loads of one row segment: lane l, load i -> segment bytes 1024 i + 16 l
+  uint4 ld[IO::kLoads];
+  auto issue_loads = [&](int64_t r) {
+    const uint8_t* src = reinterpret_cast<const uint8_t*>(x) + (r * K + seg * 2048) * EB;
+#pragma unroll
+    for (int i = 0; i < IO::kLoads; ++i) {
+      const int off = 1024 * i + 16 * lane;
+      ld[i] = off < seg_bytes_valid ? *reinterpret_cast<const uint4*>(src + off) : make_uint4(0, 0, 0, 0);
+    }
+  };
+  int e = 0;
+  if (rows_per_expert == 0 && offsets != nullptr) {
+    int lo = 0, hi = E - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi) >> 1;
+      if ((int64_t)offsets[mid + 1] > r0) hi = mid; else lo = mid + 1;
+    }
+    e = lo;
+  } else if (rows_per_expert > 0) {
+    e = (int)(r0 / rows_per_expert);
+  }
+  int cur_e = -1;
+  float sc[32];
+
+  issue_loads(r0);
+  for (int64_t r = r0; r < r1; ++r) {
+    // scatter the segment into the padded per-group layout
+#pragma unroll
+    for (int i = 0; i < IO::kLoads; ++i) {
+      const int off = 1024 * i + 16 * lane;
+      const int grp = off / IO::kGroupBytes, part = off % IO::kGroupBytes;
+      *reinterpret_cast<uint4*>(buf + grp * IO::kLdsGroup + part) = ld[i];
+    }
+    if (r + 1 < r1) issue_loads(r + 1);
+    // expert of row r and its scale factors for this lane's group
+    if (rows_per_expert > 0) e = (int)(r / rows_per_expert);
+    else if (offsets != nullptr) while (e + 1 < E && r >= (int64_t)offsets[e + 1]) ++e;
+    if (e != cur_e) {
+      cur_e = e;
+      if (active) {
+        const float4* sp = reinterpret_cast<const float4*>(s + (int64_t)e * K + g * 32);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const float4 q = sp[i];
+          sc[4 * i] = q.x; sc[4 * i + 1] = q.y; sc[4 * i + 2] = q.z; sc[4 * i + 3] = q.w;
+        }
+        if (RECIP) {
+#pragma unroll
+          for (int i = 0; i < 32; ++i) sc[i] = 1.0f / sc[i];  // IEEE-correct fp32 division
+        }
+      }
+    }
+    uint4 q[EB * 2];
+#pragma unroll
+    for (int i = 0; i < EB * 2; ++i) q[i] = *reinterpret_cast<const uint4*>(buf + lane * IO::kLdsGroup + 16 * i);
+    float t[32];
+    widen_group<EB>(q, t);
+#pragma unroll
+    for (int i = 0; i < 32; ++i) t[i] = t[i] * sc[i];
+    fwht32_regs(t);
+    uint4 cw;
+    uint32_t b;
+    quantize_group(t, &cw, &b);
+    if (active) {
+      *reinterpret_cast<uint4*>(codes + r * (K >> 1) + g * 16) = cw;
+      scales[r * KG + g] = (uint8_t)b;
+    }
+  }
+}
+
 // ---------------------------------------------------------------- launchers
 
 hipError_t launch_act_quant(const void* x, bool x_f32, bool reciprocal, const float* s,
                             const int32_t* offsets, int E, int64_t rows_per_expert, int64_t M,
                             int64_t K, uint8_t* codes, uint8_t* scales, hipStream_t stream) {
   if (M <= 0) return hipSuccess;
-  const int64_t waves = ceil_div(K, 512) * ceil_div(M, kActRowsPerWave);
-  const int64_t blocks = ceil_div(waves, kActWavesPerBlock);
-  const dim3 grid((unsigned)blocks), block(64 * kActWavesPerBlock);
+  // rows per wave: 2 to 4 (measured best on MI355X for 4K..30K row segments)
+  const int64_t nseg = ceil_div(K / 32, 64);
+  const int64_t segs = M * nseg;
+  int64_t rpw = (segs + 4096) / 8192;
+  if (rpw < 2) rpw = 2;
+  if (rpw > 4) rpw = 4;
+  if (rpw > M) rpw = M;
+  if (const char* force = getenv("MACAQ_ACT_ROWS_PER_WAVE")) rpw = atoi(force) > 0 ? atoi(force) : rpw;  // tuning knob
+  const int64_t waves = nseg * ceil_div(M, rpw);
+  const dim3 grid((unsigned)ceil_div(waves, 4)), block(256);
   if (x_f32) {
+    const size_t lds = 4 * GroupIo<4>::kWaveLds;
     if (reciprocal)
-      act_quant_kernel<float, true><<<grid, block, 0, stream>>>(x, s, offsets, E, rows_per_expert, M, K, codes, scales);
+      act_quant_lane_kernel<4, true><<<grid, block, lds, stream>>>(x, s, offsets, E, rows_per_expert, M, K, codes, scales, (int)rpw);
     else
-      act_quant_kernel<float, false><<<grid, block, 0, stream>>>(x, s, offsets, E, rows_per_expert, M, K, codes, scales);
+      act_quant_lane_kernel<4, false><<<grid, block, lds, stream>>>(x, s, offsets, E, rows_per_expert, M, K, codes, scales, (int)rpw);
   } else {
+    const size_t lds = 4 * GroupIo<2>::kWaveLds;
     if (reciprocal)
-      act_quant_kernel<Bf16Tag, true><<<grid, block, 0, stream>>>(x, s, offsets, E, rows_per_expert, M, K, codes, scales);
+      act_quant_lane_kernel<2, true><<<grid, block, lds, stream>>>(x, s, offsets, E, rows_per_expert, M, K, codes, scales, (int)rpw);
     else
-      act_quant_kernel<Bf16Tag, false><<<grid, block, 0, stream>>>(x, s, offsets, E, rows_per_expert, M, K, codes, scales);
+      act_quant_lane_kernel<2, false><<<grid, block, lds, stream>>>(x, s, offsets, E, rows_per_expert, M, K, codes, scales, (int)rpw);
   }
   return hipGetLastError();
 }

@@ -516,11 +516,15 @@ struct PipeLayout {
   __host__ __device__ static constexpr int swz(int r) { return ((r >> SWZ) / kRowsPerBankRow) & (kCPR - 1); }
 };
 
-// Tile coordinates from the block index (XCD-aware order).
-__device__ __forceinline__ void tile_of_block(int bid, int nblocks, int tiles_m, int tiles_n, int group_m,
+// Tile coordinates of block `bid` among `ntiles` = tiles_m * tiles_n active
+// tiles (XCD-aware order: the hardware deals consecutive block indices to the
+// XCDs in turn, so XCD x receives blocks x, x+8, ...; those are given one
+// contiguous range of logical tiles, which the group_m grouping turns into a
+// compact block of tiles sharing A and B panels).
+__device__ __forceinline__ void tile_of_block(int bid, int ntiles, int tiles_m, int tiles_n, int group_m,
                                               int* tm, int* tn) {
-  int logical = bid;
-  if (nblocks % kNumXcd == 0) logical = (bid % kNumXcd) * (nblocks / kNumXcd) + bid / kNumXcd;
+  const int x = bid % kNumXcd, q = ntiles / kNumXcd, rem = ntiles % kNumXcd;
+  const int logical = x * q + (x < rem ? x : rem) + bid / kNumXcd;
   const int per_group = group_m * tiles_n;
   const int g = logical / per_group;
   const int first_m = g * group_m;
@@ -549,9 +553,17 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void gemm_mxfp4_pipe_ker
   static_assert((STAGES - 2) * kLPT < 64, "vmcnt range");
   extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];
 
-  // ---- tile -> (expert, rows, columns)
+  // ---- tile -> (expert, rows, columns).  Grouped: the active row tiles are
+  // counted from the device-side offsets, so that the XCD-aware order spreads
+  // only real tiles over the XCDs; surplus blocks exit.
+  int active_m = tiles_m;
+  if (offsets != nullptr) {
+    active_m = 0;
+    for (int e2 = 0; e2 < E; ++e2) active_m += (int)((offsets[e2 + 1] - offsets[e2] + BM - 1) / BM);
+  }
+  if ((int)blockIdx.x >= active_m * tiles_n) return;
   int tm, tn;
-  tile_of_block((int)blockIdx.x, (int)gridDim.x, tiles_m, tiles_n, group_m, &tm, &tn);
+  tile_of_block((int)blockIdx.x, active_m * tiles_n, active_m, tiles_n, group_m, &tm, &tn);
   int64_t slot = tm;
   int e = 0;
   int64_t row_begin = 0, row_end = M;
@@ -743,8 +755,9 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void gemm_mxfp4_db_kerne
   constexpr int kSB = (L::kScaleBlocks + kWaves - 1) / kWaves;
   extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];
 
+  if ((int)blockIdx.x >= tiles_m * tiles_n) return;
   int tm, tn;
-  tile_of_block((int)blockIdx.x, (int)gridDim.x, tiles_m, tiles_n, group_m, &tm, &tn);
+  tile_of_block((int)blockIdx.x, tiles_m * tiles_n, tiles_m, tiles_n, group_m, &tm, &tn);
   int64_t slot = tm;
   int e = 0;
   int64_t row_begin = 0, row_end = M;
