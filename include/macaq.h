@@ -187,6 +187,19 @@ int macaq_linear(const void* x, macaq_dtype x_dtype, const float* s,
                  void* workspace, size_t workspace_bytes, uint32_t flags, void* stream);
 
 /*
+ * Plain OCP MXFP4 quantization of rows, without the scale and the Hadamard
+ * transform (s = 1, H = I): the "pure MXFP4" baseline the pages compare the
+ * online transform against ("MACaQ: Fast, Model Agnostic Calibrated
+ * Quantization ...", Abstract: the overhead is quoted over pure MXFP4).
+ * Same E8M0 and E2M1 rules as above.  Applied to both x and W it gives the
+ * operands of a transform-free W4A4 layer for the macaq_gemm call.
+ *   x [M][K] in x_dtype; codes [M][K/2] out; scales [M][K/32] out.
+ * Requires M >= 0, K % 32 == 0, x and codes 16-byte aligned.
+ */
+int macaq_quant_mxfp4(const void* x, macaq_dtype x_dtype, int64_t M, int64_t K, uint8_t* codes, uint8_t* scales,
+                      void* stream);
+
+/*
  * Element encoder alone, for exhaustive tests of the E2M1 rounding: codes[i]
  * = the 4-bit E2M1 code (sign<<3 | magnitude index) of v[i] with scale byte
  * 127 (no scaling), by the same device routine the quantizing kernels use.

@@ -21,7 +21,7 @@ import torch
 __all__ = [
     "lib", "MacaqError", "BF16", "F32", "PATH_AUTO", "PATH_FUSED", "PATH_UNFUSED",
     "prepare_weights", "quant_act", "gemm", "linear", "linear_workspace_bytes",
-    "encode_e2m1", "version", "library_path",
+    "encode_e2m1", "quant_mxfp4", "version", "library_path",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -66,6 +66,7 @@ def _load():
         "macaq_linear_path": (ci, [i64, i64, i64, i64, u32]),
         "macaq_linear": (ci, [vp, ci, vp, vp, i64, vp, vp, i64, i64, i64, vp, vp, sz, u32, vp]),
         "macaq_encode_e2m1": (ci, [vp, i64, vp, vp]),
+        "macaq_quant_mxfp4": (ci, [vp, ci, i64, i64, vp, vp, vp]),
     }
     for name, (res, args) in sig.items():
         f = getattr(L, name)
@@ -216,6 +217,18 @@ def linear(x, s, w_codes, w_scales, offsets=None, flags=PATH_AUTO, out=None, wor
     _check(macaq_linear(_ptr(x), _dtype_code(x), _ptr(s), _ptr(offsets), E, _ptr(w_codes), _ptr(w_scales),
                         M, N, K, _ptr(y), _ptr(workspace), ws_bytes, flags, _stream(x.device)), "macaq_linear")
     return y
+
+
+def quant_mxfp4(x: torch.Tensor):
+    """Plain OCP MXFP4 of rows (no scale, no transform) -> (codes [M,K/2], scales [M,K/32])."""
+    _load()
+    _need(x, "x", dim=2)
+    M, K = x.shape
+    codes = torch.empty((M, K // 2), dtype=torch.uint8, device=x.device)
+    scales = torch.empty((M, K // 32), dtype=torch.uint8, device=x.device)
+    _check(macaq_quant_mxfp4(_ptr(x), _dtype_code(x), M, K, _ptr(codes), _ptr(scales), _stream(x.device)),
+           "macaq_quant_mxfp4")
+    return codes, scales
 
 
 def encode_e2m1(v: torch.Tensor) -> torch.Tensor:

@@ -8,146 +8,14 @@
 // MXFP4: 32-element groups, E8M0 scale, E2M1 elements) and "MACaQ
 // 真正解决的是跨层耦合" (32-element Hadamard blocks aligned to the groups).
 //
-// Work layout: one wave covers 512 consecutive columns (16 groups; lane l
-// owns columns 8l .. 8l+7, a quad of lanes owns a group) of ROWS_PER_WAVE
-// consecutive rows.  Each lane issues one 16-byte load per row (bf16) or two
-// (fp32), so a wave's loads are fully coalesced 1 KiB (2 KiB) segments; all
-// rows' loads are issued before the first row is transformed.  The 8 scale
-// factors of the lane stay in registers across the rows (reloaded only when
-// the expert changes).  Codes leave as one dword per lane per row (coalesced
-// 256-byte segments); the scale byte is written by lane 0 of each quad.
-//
-// The kernel is HBM-bound: per element it reads 2 bytes (bf16) and writes
-// 17/32 bytes.
+// One lane owns one 32-value group: a wave covers 64 groups (2048 columns)
+// of a few consecutive rows (see act_quant_lane_kernel below).  The kernel is
+// HBM-bound: per element it reads 2 bytes (bf16) and writes 17/32 bytes.
 #include <cstdlib>
 
 #include "mx_common.h"
 
 namespace macaq {
-
-constexpr int kActRowsPerWave = 8;
-constexpr int kActWavesPerBlock = 4;
-
-// Element type tag of bf16 activations (raw 16-bit patterns).
-struct Bf16Tag {};
-
-template <typename XT>
-struct RowLoad;
-
-template <>
-struct RowLoad<Bf16Tag> {
-  uint4 v;
-  __device__ __forceinline__ void load(const void* base, int64_t elem_off) {
-    v = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(base) + elem_off);
-  }
-  __device__ __forceinline__ void widen(float (&t)[8]) const {
-    t[0] = bf16_lo(v.x); t[1] = bf16_hi(v.x);
-    t[2] = bf16_lo(v.y); t[3] = bf16_hi(v.y);
-    t[4] = bf16_lo(v.z); t[5] = bf16_hi(v.z);
-    t[6] = bf16_lo(v.w); t[7] = bf16_hi(v.w);
-  }
-};
-
-template <>
-struct RowLoad<float> {
-  float4 a, b;
-  __device__ __forceinline__ void load(const void* base, int64_t elem_off) {
-    const float4* p = reinterpret_cast<const float4*>(reinterpret_cast<const float*>(base) + elem_off);
-    a = p[0];
-    b = p[1];
-  }
-  __device__ __forceinline__ void widen(float (&t)[8]) const {
-    t[0] = a.x; t[1] = a.y; t[2] = a.z; t[3] = a.w;
-    t[4] = b.x; t[5] = b.y; t[6] = b.z; t[7] = b.w;
-  }
-};
-
-// Expert of row r: rows_per_expert > 0 gives r / rows_per_expert (weights);
-// otherwise the sorted offsets are scanned forward from `hint`.
-__device__ __forceinline__ int expert_of(int64_t r, const int32_t* __restrict__ offsets, int E,
-                                         int64_t rows_per_expert, int hint) {
-  if (rows_per_expert > 0) return (int)(r / rows_per_expert);
-  if (offsets == nullptr) return 0;
-  int e = hint;
-  while (e + 1 < E && r >= (int64_t)offsets[e + 1]) ++e;
-  return e;
-}
-
-template <typename XT, bool RECIP>
-__global__ __launch_bounds__(64 * kActWavesPerBlock) void act_quant_kernel(
-    const void* __restrict__ x, const float* __restrict__ s, const int32_t* __restrict__ offsets,
-    int E, int64_t rows_per_expert, int64_t M, int64_t K, uint8_t* __restrict__ codes,
-    uint8_t* __restrict__ scales) {
-  const int lane = threadIdx.x & 63;
-  const int64_t wave = (int64_t)blockIdx.x * kActWavesPerBlock + (threadIdx.x >> 6);
-  const int64_t nchunk = ceil_div(K, 512);
-  const int64_t chunk = wave % nchunk;
-  const int64_t r0 = (wave / nchunk) * kActRowsPerWave;
-  if (r0 >= M) return;
-  const int64_t col = chunk * 512 + (int64_t)lane * 8;
-  const bool active = col < K;  // K % 32 == 0: whole quads are in or out
-  const uint32_t quad = (uint32_t)lane & 3u;
-  const int nrows = (int)((M - r0) < kActRowsPerWave ? (M - r0) : kActRowsPerWave);
-
-  RowLoad<XT> ld[kActRowsPerWave];
-#pragma unroll
-  for (int i = 0; i < kActRowsPerWave; ++i)
-    if (active && i < nrows) ld[i].load(x, (r0 + i) * K + col);
-
-  // Expert of the first row: the first e with offsets[e+1] > r0.
-  int e = 0;
-  if (rows_per_expert == 0 && offsets != nullptr) {
-    int lo = 0, hi = E - 1;
-    while (lo < hi) {
-      const int mid = (lo + hi) >> 1;
-      if ((int64_t)offsets[mid + 1] > r0) hi = mid; else lo = mid + 1;
-    }
-    e = lo;
-  } else {
-    e = expert_of(r0, offsets, E, rows_per_expert, 0);
-  }
-  int cur_e = -1;
-  float sc[8];
-
-#pragma unroll
-  for (int i = 0; i < kActRowsPerWave; ++i) {
-    if (i >= nrows) break;
-    const int64_t r = r0 + i;
-    e = expert_of(r, offsets, E, rows_per_expert, e);
-    if (e != cur_e) {
-      cur_e = e;
-      if (active) {
-        const float4* sp = reinterpret_cast<const float4*>(s + (int64_t)e * K + col);
-        const float4 s0 = sp[0], s1 = sp[1];
-        sc[0] = s0.x; sc[1] = s0.y; sc[2] = s0.z; sc[3] = s0.w;
-        sc[4] = s1.x; sc[5] = s1.y; sc[6] = s1.z; sc[7] = s1.w;
-        if (RECIP) {
-#pragma unroll
-          for (int j = 0; j < 8; ++j) sc[j] = 1.0f / sc[j];  // IEEE-correct fp32 division
-        }
-      } else {
-#pragma unroll
-        for (int j = 0; j < 8; ++j) sc[j] = 0.0f;
-      }
-    }
-    float t[8];
-    if (active) {
-      ld[i].widen(t);
-    } else {
-#pragma unroll
-      for (int j = 0; j < 8; ++j) t[j] = 0.0f;
-    }
-#pragma unroll
-    for (int j = 0; j < 8; ++j) t[j] = t[j] * sc[j];
-    hadamard32_quad(t, quad);
-    uint32_t b;
-    const uint32_t packed = quantize_quad(t, &b);
-    if (active) {
-      *reinterpret_cast<uint32_t*>(codes + r * (K >> 1) + (col >> 1)) = packed;
-      if (quad == 0) scales[r * (K >> 5) + (col >> 5)] = (uint8_t)b;
-    }
-  }
-}
 
 __global__ void encode_e2m1_kernel(const float* __restrict__ v, int64_t n, uint8_t* __restrict__ out) {
   const int64_t i0 = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) * 8;
@@ -251,7 +119,34 @@ __device__ __forceinline__ void quantize_group(const float (&u)[32], uint4* code
   *b_out = b;
 }
 
-template <int EB, bool RECIP>
+// Plain OCP MXFP4 quantization of a group (no scale, no transform): the
+// E8M0 byte comes from max|x| and the codes from x * 2^(127-b).
+__device__ __forceinline__ void quantize_group_plain(const float (&u)[32], uint4* codes_out, uint32_t* b_out) {
+  float m = fabsf(u[0]);
+#pragma unroll
+  for (int i = 1; i < 32; ++i) m = fmaxf(m, fabsf(u[i]));
+  const uint32_t b = e8m0_from_amax(m);
+  const float inv = inv_scale(b);
+  float v[32];
+#pragma unroll
+  for (int i = 0; i < 32; ++i) v[i] = u[i] * inv;
+  uint32_t w[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    uint32_t r = 0;
+    r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, v[8 * q + 0], v[8 * q + 1], 1.0f, 0);
+    r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, v[8 * q + 2], v[8 * q + 3], 1.0f, 1);
+    r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, v[8 * q + 4], v[8 * q + 5], 1.0f, 2);
+    r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, v[8 * q + 6], v[8 * q + 7], 1.0f, 3);
+    w[q] = r;
+  }
+  *codes_out = make_uint4(w[0], w[1], w[2], w[3]);
+  *b_out = b;
+}
+
+// PLAIN: quantize the rows as they are (s = 1, H = I), the "pure MXFP4"
+// baseline against which the online transform's cost is measured.
+template <int EB, bool RECIP, bool PLAIN = false>
 __global__ __launch_bounds__(256) void act_quant_lane_kernel(
     const void* __restrict__ x, const float* __restrict__ s, const int32_t* __restrict__ offsets, int E,
     int64_t rows_per_expert, int64_t M, int64_t K, uint8_t* __restrict__ codes, uint8_t* __restrict__ scales,
@@ -309,7 +204,7 @@ __global__ __launch_bounds__(256) void act_quant_lane_kernel(
     // expert of row r and its scale factors for this lane's group
     if (rows_per_expert > 0) e = (int)(r / rows_per_expert);
     else if (offsets != nullptr) while (e + 1 < E && r >= (int64_t)offsets[e + 1]) ++e;
-    if (e != cur_e) {
+    if (!PLAIN && e != cur_e) {
       cur_e = e;
       if (active) {
         const float4* sp = reinterpret_cast<const float4*>(s + (int64_t)e * K + g * 32);
@@ -329,12 +224,16 @@ __global__ __launch_bounds__(256) void act_quant_lane_kernel(
     for (int i = 0; i < EB * 2; ++i) q[i] = *reinterpret_cast<const uint4*>(buf + lane * IO::kLdsGroup + 16 * i);
     float t[32];
     widen_group<EB>(q, t);
-#pragma unroll
-    for (int i = 0; i < 32; ++i) t[i] = t[i] * sc[i];
-    fwht32_regs(t);
     uint4 cw;
     uint32_t b;
-    quantize_group(t, &cw, &b);
+    if constexpr (PLAIN) {
+      quantize_group_plain(t, &cw, &b);
+    } else {
+#pragma unroll
+      for (int i = 0; i < 32; ++i) t[i] = t[i] * sc[i];
+      fwht32_regs(t);
+      quantize_group(t, &cw, &b);
+    }
     if (active) {
       *reinterpret_cast<uint4*>(codes + r * (K >> 1) + g * 16) = cw;
       scales[r * KG + g] = (uint8_t)b;
@@ -371,6 +270,26 @@ hipError_t launch_act_quant(const void* x, bool x_f32, bool reciprocal, const fl
     else
       act_quant_lane_kernel<2, false><<<grid, block, lds, stream>>>(x, s, offsets, E, rows_per_expert, M, K, codes, scales, (int)rpw);
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_quant_plain(const void* x, bool x_f32, int64_t M, int64_t K, uint8_t* codes, uint8_t* scales,
+                              hipStream_t stream) {
+  if (M <= 0) return hipSuccess;
+  const int64_t nseg = ceil_div(K / 32, 64);
+  const int64_t segs = M * nseg;
+  int64_t rpw = (segs + 4096) / 8192;
+  if (rpw < 2) rpw = 2;
+  if (rpw > 4) rpw = 4;
+  if (rpw > M) rpw = M;
+  const int64_t waves = nseg * ceil_div(M, rpw);
+  const dim3 grid((unsigned)ceil_div(waves, 4)), block(256);
+  if (x_f32)
+    act_quant_lane_kernel<4, false, true><<<grid, block, 4 * GroupIo<4>::kWaveLds, stream>>>(
+        x, nullptr, nullptr, 1, 0, M, K, codes, scales, (int)rpw);
+  else
+    act_quant_lane_kernel<2, false, true><<<grid, block, 4 * GroupIo<2>::kWaveLds, stream>>>(
+        x, nullptr, nullptr, 1, 0, M, K, codes, scales, (int)rpw);
   return hipGetLastError();
 }
 

@@ -16,6 +16,8 @@ hipError_t launch_act_quant(const void* x, bool x_f32, bool reciprocal, const fl
                             const int32_t* offsets, int E, int64_t rows_per_expert, int64_t M,
                             int64_t K, uint8_t* codes, uint8_t* scales, hipStream_t stream);
 hipError_t launch_encode_e2m1(const float* v, int64_t n, uint8_t* codes, hipStream_t stream);
+hipError_t launch_quant_plain(const void* x, bool x_f32, int64_t M, int64_t K, uint8_t* codes, uint8_t* scales,
+                              hipStream_t stream);
 hipError_t launch_gemm(const uint8_t* A, const uint8_t* As, const int32_t* offsets, int E,
                        const uint8_t* B, const uint8_t* Bs, int64_t M, int64_t N, int64_t K,
                        float* Y, hipStream_t stream);
@@ -244,6 +246,21 @@ int macaq_linear(const void* x, macaq_dtype x_dtype, const float* s, const int32
     return r;
   void* gemm_ws = static_cast<uint8_t*>(workspace) + macaq_quant_act_bytes(M, K);
   return run_gemm(a_codes, a_scales, off, E, w_codes, w_scales, M, N, K, y, gemm_ws, st, "macaq_linear (gemm)");
+}
+
+int macaq_quant_mxfp4(const void* x, macaq_dtype x_dtype, int64_t M, int64_t K, uint8_t* codes, uint8_t* scales,
+                      void* stream) {
+  const char* fn = "macaq_quant_mxfp4";
+  if (int st = check_dtype(x_dtype, fn)) return st;
+  if (M < 0) return fail(MACAQ_ERR_INVALID_ARG, std::string(fn) + ": need M >= 0");
+  if (int st = check_k(K, fn)) return st;
+  if (M == 0) return MACAQ_OK;
+  if (!x || !codes || !scales) return fail(MACAQ_ERR_INVALID_ARG, std::string(fn) + ": null pointer");
+  if (!aligned(x, 16) || !aligned(codes, 16))
+    return fail(MACAQ_ERR_INVALID_ARG, std::string(fn) + ": x and codes must be 16-byte aligned");
+  if (int st = check_device()) return st;
+  return hip_status(macaq::launch_quant_plain(x, x_dtype == MACAQ_F32, M, K, codes, scales, (hipStream_t)stream),
+                    fn);
 }
 
 int macaq_encode_e2m1(const float* v, int64_t n, uint8_t* codes, void* stream) {

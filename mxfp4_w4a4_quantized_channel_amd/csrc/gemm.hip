@@ -8,19 +8,20 @@ namespace macaq {
 
 namespace {
 
-template <int BM, int BN, int WM, int WN, int BK, int S>
+template <int BM, int BN, int WM, int WN, int BK, int S, int MINB = 1>
 hipError_t launch_pipe(const uint8_t* A, const uint8_t* As, const int32_t* offsets, int E, const uint8_t* B,
                        const uint8_t* Bs, int64_t M, int64_t N, int64_t K, float* Y, hipStream_t stream) {
   using L = PipeLayout<BM, BN, BK, 1>;
   constexpr int lds = S * L::kStage;
-  static const hipError_t attr = hipFuncSetAttribute(
-      (const void*)gemm_mxfp4_pipe_kernel<BM, BN, WM, WN, BK, S>, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+  static const hipError_t attr =
+      hipFuncSetAttribute((const void*)gemm_mxfp4_pipe_kernel<BM, BN, WM, WN, BK, S, MINB>,
+                          hipFuncAttributeMaxDynamicSharedMemorySize, lds);
   if (attr != hipSuccess) return attr;
   const int tiles_n = (int)ceil_div(N, BN);
   int64_t tiles_m = ceil_div(M, BM);
   if (offsets != nullptr) tiles_m += E;  // each expert may add one partial row tile
   const int64_t blocks = tiles_m * tiles_n;
-  gemm_mxfp4_pipe_kernel<BM, BN, WM, WN, BK, S><<<dim3((unsigned)blocks), dim3(64 * WM * WN), lds, stream>>>(
+  gemm_mxfp4_pipe_kernel<BM, BN, WM, WN, BK, S, MINB><<<dim3((unsigned)blocks), dim3(64 * WM * WN), lds, stream>>>(
       A, As, B, Bs, offsets, E, M, N, K, Y, (int)tiles_m, tiles_n, 4);
   return hipGetLastError();
 }
@@ -31,22 +32,37 @@ hipError_t launch_gemm(const uint8_t* A, const uint8_t* As, const int32_t* offse
                        const uint8_t* B, const uint8_t* Bs, int64_t M, int64_t N, int64_t K,
                        float* Y, hipStream_t stream) {
   if (M <= 0) return hipSuccess;
-  // Tile choice: the largest tile that still gives about one tile per CU.
-  // MACAQ_GEMM_TILE=256x256 | 256x128 | 128x128 forces one (tests use it to
-  // cover every kernel on small shapes).
-  int64_t t256 = ceil_div(M, 256) * ceil_div(N, 256);
-  int64_t t128 = ceil_div(M, 256) * ceil_div(N, 128);
+  // Tile choice (measured on MI355X): 256x256 when that still gives about one
+  // tile per CU (largest tiles, least LDS and L2 traffic per FLOP); else
+  // 256x128; grouped layers and small shapes use 128x128 with two blocks per
+  // CU, whose finer granularity keeps ragged experts from leaving CUs idle.
+  // MACAQ_GEMM_TILE=256x256 | 256x128 | 128x128 | 128x128v1 forces one (the
+  // tests use it to cover every kernel on small shapes).
+  const int64_t t256 = ceil_div(M, 256) * ceil_div(N, 256);
+  const int64_t t128 = ceil_div(M, 256) * ceil_div(N, 128);
+  int choice;  // 0: 256x256, 1: 256x128, 2: 128x128 pipelined, 3: 128x128 register-staged
+  if (offsets != nullptr) choice = 2;
+  else if (t256 >= 240) choice = 0;
+  else if (t128 >= 200) choice = 1;
+  else choice = 2;
   if (const char* force = getenv("MACAQ_GEMM_TILE")) {
-    const bool f256 = strcmp(force, "256x256") == 0, f128 = strcmp(force, "256x128") == 0;
-    t256 = f256 ? INT64_MAX : 0;
-    t128 = f128 ? INT64_MAX : 0;
+    if (strcmp(force, "256x256") == 0) choice = 0;
+    else if (strcmp(force, "256x128") == 0) choice = 1;
+    else if (strcmp(force, "128x128") == 0) choice = 2;
+    else if (strcmp(force, "128x128v1") == 0) choice = 3;
   }
-  if (K % 256 == 0) {
-    if (t256 >= 240) return launch_pipe<256, 256, 2, 2, 256, 2>(A, As, offsets, E, B, Bs, M, N, K, Y, stream);
-    if (t128 >= 120) return launch_pipe<256, 128, 2, 2, 256, 2>(A, As, offsets, E, B, Bs, M, N, K, Y, stream);
-  } else {
-    if (t256 >= 240) return launch_pipe<256, 256, 2, 2, 128, 4>(A, As, offsets, E, B, Bs, M, N, K, Y, stream);
-    if (t128 >= 120) return launch_pipe<256, 128, 2, 2, 128, 4>(A, As, offsets, E, B, Bs, M, N, K, Y, stream);
+  const bool k256 = K % 256 == 0;
+  switch (choice) {
+    case 0:
+      return k256 ? launch_pipe<256, 256, 2, 2, 256, 2>(A, As, offsets, E, B, Bs, M, N, K, Y, stream)
+                  : launch_pipe<256, 256, 2, 2, 128, 4>(A, As, offsets, E, B, Bs, M, N, K, Y, stream);
+    case 1:
+      return k256 ? launch_pipe<256, 128, 2, 2, 256, 2>(A, As, offsets, E, B, Bs, M, N, K, Y, stream)
+                  : launch_pipe<256, 128, 2, 2, 128, 4>(A, As, offsets, E, B, Bs, M, N, K, Y, stream);
+    case 2:
+      return k256 ? launch_pipe<128, 128, 2, 2, 256, 2, 2>(A, As, offsets, E, B, Bs, M, N, K, Y, stream)
+                  : launch_pipe<128, 128, 2, 2, 128, 4, 2>(A, As, offsets, E, B, Bs, M, N, K, Y, stream);
+    default: break;
   }
   constexpr int BM = 128, BN = 128;
   const int n_tiles_n = (int)ceil_div(N, BN);

@@ -534,8 +534,8 @@ __device__ __forceinline__ void tile_of_block(int bid, int ntiles, int tiles_m, 
   *tn = in / gm;
 }
 
-template <int BM, int BN, int WAVES_M, int WAVES_N, int BK, int STAGES>
-__global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void gemm_mxfp4_pipe_kernel(
+template <int BM, int BN, int WAVES_M, int WAVES_N, int BK, int STAGES, int MINB = 1>
+__global__ __launch_bounds__(64 * WAVES_M * WAVES_N, MINB) void gemm_mxfp4_pipe_kernel(
     const uint8_t* __restrict__ A, const uint8_t* __restrict__ As, const uint8_t* __restrict__ B,
     const uint8_t* __restrict__ Bs, const int32_t* __restrict__ offsets, int E, int64_t M,
     int64_t N, int64_t K, float* __restrict__ Y, int tiles_m, int tiles_n, int group_m) {

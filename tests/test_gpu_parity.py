@@ -247,7 +247,7 @@ def test_linear_deterministic():
 
 # ------------------------------------------------------------ every GEMM kernel variant
 
-TILES = ["256x256", "256x128", "128x128"]
+TILES = ["256x256", "256x128", "128x128", "128x128v1"]
 TILE_SHAPES = [
     ("ragged M N", (300, 260, 1024)),
     ("K tail 128", (257, 129, 640)),
@@ -343,3 +343,15 @@ def test_linear_decode_paths(name, kw, flags):
     y_ref, S = oracle.linear(host(wl.x), wl.s.numpy(), rwc, rws)
     _check_y(y.cpu().numpy(), y_ref, S)
     assert torch.equal(y, y_again)
+
+
+# ------------------------------------------------------------ pure MXFP4 (no transform)
+
+@pytest.mark.parametrize("name,kw", SMALL_ACT[:4], ids=[n for n, _ in SMALL_ACT[:4]])
+def test_quant_mxfp4_plain_bit_exact(name, kw):
+    say(f"quant_mxfp4 plain {name}")
+    wl = workloads.make(**kw)
+    codes, scales = mx.quant_mxfp4(wl.x.to(DEV))
+    rc, rs = oracle.quantize_mxfp4(oracle.as_f32(host(wl.x)))
+    assert np.array_equal(scales.cpu().numpy(), rs)
+    assert np.array_equal(codes.cpu().numpy(), rc)
