@@ -12,24 +12,35 @@
 // weight is the MFMA's A operand (32 weight rows per instruction) and the
 // <= 32 activation rows are the B operand:
 //   D[n][m] = sum_k w'(n,k) a(m,k),  v_mfma_scale_f32_32x32x64_f8f6f4.
-// Operands go straight from global memory into registers; W' never passes
-// through LDS.  K permutation (the same on both operands): in a 256-wide K
-// chunk, lane half h of sub-step j takes group 2j + h, so for each weight
-// row the two lanes of one instruction read 32 contiguous bytes and the four
-// instructions of a chunk read the row's 128-byte line in order.  A lane's
-// four scale bytes (groups h, 2+h, 4+h, 6+h) are gathered with one byte
-// permute so that op_sel byte j is sub-step j's scale.
+// K permutation (the same on both operands): in a 256-wide K chunk, lane
+// half h of sub-step j takes group 2j + h.  A lane's four scale bytes
+// (groups h, 2+h, 4+h, 6+h) are gathered with one byte permute so that
+// op_sel byte j is sub-step j's scale.
 //
-// Work split: a block owns 32 weight rows and the whole K range, which its
-// WAVES waves split; each wave issues the loads of two chunks at a time and
-// the waves' 32x32 partial sums are added in LDS in wave order
-// (deterministic).  No cross-block
-// reduction is needed, so the path needs no workspace.
+// Memory path: a block owns 32 weight rows and the whole K range, which its
+// waves split into contiguous chunk ranges.  Each wave copies its chunks
+// from global memory straight into a private, double-buffered LDS stage with
+// global_load_lds: one dwordx4 copy instruction reads 8 whole 128-byte rows
+// of a chunk (whole cache lines; reading the MFMA's own lane layout from
+// global memory instead touches 32 lines per instruction and streams about a
+// third slower).  Slots are XOR-swizzled by row so the MFMA-layout reads
+// from LDS spread over the banks.  The copy of chunk c + 1 is in flight
+// while chunk c is multiplied.  In the unfused path the activation codes
+// and scales of the chunk travel the same way, so that the loop holds no
+// compiler-visible global load (whose compiler-inserted wait would also
+// wait for the next chunk's copy).
+//
+// The waves' 32x32 partial sums are added in LDS in wave order
+// (deterministic).  No cross-block reduction is needed, so the path needs no
+// workspace.
 //
 // Fused variant: before the GEMM the block transforms and quantizes x[0:M,
-// :] (the quad-per-group routine of the activation kernel) into LDS; the B
-// fragments then come from LDS.  Every block repeats that transform, so the
-// fused variant pays off only for very small M.
+// :] (the quad-per-group routine of the activation kernel) into LDS while the
+// first weight chunk is in flight; the B fragments then come from LDS.
+// Every block repeats that transform, so the fused variant pays off only for
+// very small M.
+#include <cstdlib>
+
 #include "mx_common.h"
 
 namespace macaq {
@@ -63,17 +74,6 @@ __device__ __forceinline__ uint32_t gather_scales(uint32_t lo, uint32_t hi, int 
   return __builtin_amdgcn_perm(hi, lo, sel);
 }
 
-// One chunk of one operand row: lane (r, h) takes the 16-byte groups 2j + h.
-__device__ __forceinline__ void load_chunk(const uint8_t* row, int64_t chunk, int h, uint4 (&v)[4]) {
-  const uint4* p = reinterpret_cast<const uint4*>(row + chunk * 128) + h;
-#pragma unroll
-  for (int j = 0; j < 4; ++j) v[j] = p[2 * j];
-}
-__device__ __forceinline__ uint32_t load_scales(const uint8_t* srow, int64_t chunk, int h) {
-  const uint32_t* p = reinterpret_cast<const uint32_t*>(srow + chunk * 8);
-  return gather_scales(p[0], p[1], h);
-}
-
 // Element type tag of bf16 activations for the fused prologue.
 struct DecBf16 {};
 
@@ -96,12 +96,59 @@ __device__ __forceinline__ void dec_load8<float>(const void* x, int64_t off, flo
 __host__ __device__ constexpr int64_t dec_xrow_bytes(int64_t K) { return K / 2 + 16; }
 __host__ __device__ constexpr int64_t dec_xrow_groups(int64_t K) { return K / 32 + 8; }
 
-template <int WAVES, bool FUSED, typename XT>
+// Layout of one staged 256-wide K chunk in a wave's LDS ring slot: W' codes
+// of the block's 32 rows (4 x 1 KiB, row r at (r / 8) KiB + (r % 8) * 128
+// with 16-byte slot p holding piece p ^ (r % 8)), then the activation's part
+// of the chunk.  Activation kinds AK:
+//   0      resident: the whole activation sits in LDS (fused transform);
+//   1      M <= 2: codes of rows 0..1 (2 x 128 B, plain layout) copied by one
+//          dword instruction;
+//   8,16,32  M <= AK: codes of AK rows in the swizzled layout (AK / 8
+//          dwordx4 instructions);
+// and for AK > 0 the activation scales (32 rows x 8 bytes, one dword
+// instruction; rows past M repeat row M - 1).
+//
+// W' scales do not travel per chunk (32 rows x 8 bytes would touch 32 cache
+// lines per instruction, and with long rows those lines leave L1 before
+// their next use).  They are staged per segment of SEG chunks into a slab of
+// 32 rows x 8 SEG bytes, one dword copy instruction (64 / (2 SEG) rows x 8 SEG
+// bytes) riding along with each chunk's copies and filling the slab of the
+// next segment.  Three slabs rotate: the slab being filled was last read two
+// segments ago.  SEG = 8, or 4 where 32 staged activation rows leave less
+// LDS.
+constexpr int kSlabs = 3;
+
+template <int AK>
+struct DecStage {
+  static constexpr int kW = 0;
+  static constexpr int kA = 4096;
+  static constexpr int kABytes = AK == 0 ? 0 : (AK == 1 ? 256 : AK * 128);
+  static constexpr int kAs = kA + kABytes;
+  static constexpr int kBytes = kAs + (AK == 0 ? 0 : 256);
+  static constexpr int kACopies = AK == 0 ? 0 : (AK == 1 ? 2 : AK / 8 + 1);
+  static constexpr int kCopies = 5 + kACopies;   // copy instructions per chunk (4 codes + 1 slab + activation)
+};
+
+template <int STAGES, int AK>
+struct DecWaveLds {
+  static constexpr int kSeg = AK == 32 ? 4 : 8;          // chunks per scale segment
+  static constexpr int kRowDwords = 2 * kSeg;            // slab row: 8 kSeg bytes
+  static constexpr int kSlabBytes = 32 * 8 * kSeg;
+  static constexpr int kSlab0 = STAGES * DecStage<AK>::kBytes;
+  static constexpr int kBytes = kSlab0 + kSlabs * kSlabBytes;
+};
+
+__device__ __forceinline__ int dec_slot(int row, int piece) { return (row >> 3) * 1024 + (row & 7) * 128 + 16 * (piece ^ (row & 7)); }
+
+template <int WAVES, int STAGES, int AK, typename XT>
 __global__ __launch_bounds__(64 * WAVES) void decode_gemm_kernel(
     const uint8_t* __restrict__ A, const uint8_t* __restrict__ As,     // activation codes/scales (unfused)
     const void* __restrict__ x, const float* __restrict__ s,           // activations and scale (fused)
     const uint8_t* __restrict__ W, const uint8_t* __restrict__ Ws, int64_t M, int64_t N, int64_t K,
     float* __restrict__ Y) {
+  using S = DecStage<AK>;
+  constexpr bool FUSED = AK == 0;
+  constexpr int AI = AK >= 8 ? AK / 8 : 1;
   extern __shared__ __attribute__((aligned(16))) uint8_t dsm[];
   constexpr int kThreads = 64 * WAVES;
   const int64_t n0 = (int64_t)blockIdx.x * kDecRows;
@@ -109,86 +156,187 @@ __global__ __launch_bounds__(64 * WAVES) void decode_gemm_kernel(
   const int kc = (int)(K >> 8);
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int r32 = lane & 31;
   const int h = lane >> 5;
 
-  // LDS: [WAVES][32][32] fp32 partials, then (fused) the activation codes
-  // [M][K/2 + 16] and scales [M][K/32 + 8].
+  using WL = DecWaveLds<STAGES, AK>;
+  // LDS: per wave STAGES ring slots and kSlabs scale slabs (all reused for
+  // the [WAVES][32][32] fp32 partial sums after the loop), then (fused) the
+  // activation codes [M][K/2 + 16] and scales [M][K/32 + 8].
+  uint8_t* ring = dsm + wave * WL::kBytes;
+  const uint32_t ring_addr = (uint32_t)(uintptr_t)ring;
+  const uint8_t* slabs = ring + WL::kSlab0;
   float* red = reinterpret_cast<float*>(dsm);
   const int64_t xrb = dec_xrow_bytes(K), xrg = dec_xrow_groups(K);
-  uint8_t* xcodes = dsm + WAVES * 32 * 32 * 4;
+  uint8_t* xcodes = dsm + WAVES * WL::kBytes;
   uint8_t* xscales = xcodes + M * xrb;
 
+  // ---- this wave's chunks and the copy sources of chunk 0 (rows past N or
+  // M repeat the last row; their results are not stored)
+  const int per_wave = (kc + WAVES - 1) / WAVES;
+  const int c0 = wave * per_wave;
+  const int c1 = (c0 + per_wave) < kc ? (c0 + per_wave) : kc;
+  const uint8_t* wsrc[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int row = 8 * i + (lane >> 3);
+    const int64_t wn = n0 + row < N ? n0 + row : N - 1;
+    wsrc[i] = W + wn * KB + 16 * ((lane & 7) ^ (row & 7));
+  }
+  // slab copy instruction t of a segment: lane l takes row
+  // t * (64 / D) + l / D, dword l % D of the segment's D dwords (clamped
+  // inside the row)
+  constexpr int kSeg = WL::kSeg, kD = WL::kRowDwords;
+  const int slab_lrow = lane / kD;
+  const int64_t slab_lofs = 4 * (lane % kD);
+  const uint8_t* asrc[AI];
+  const uint8_t* assrc = As;
+  if constexpr (AK == 1) {
+    const int64_t am = (lane >> 5) < M ? (lane >> 5) : M - 1;
+    asrc[0] = A + am * KB + 4 * (lane & 31);
+  } else if constexpr (AK >= 8) {
+#pragma unroll
+    for (int i = 0; i < AI; ++i) {
+      const int row = 8 * i + (lane >> 3);
+      const int64_t am = row < M ? row : M - 1;
+      asrc[i] = A + am * KB + 16 * ((lane & 7) ^ (row & 7));
+    }
+  }
+  if constexpr (AK > 0) {
+    const int64_t ams = (lane >> 1) < M ? (lane >> 1) : M - 1;
+    assrc = As + ams * KG + 4 * (lane & 1);
+  }
+  // copy t of the W' scale slab of segment seg (relative to c0)
+  auto issue_slab = [&](int seg, int t) {
+    const int row = t * (64 / kD) + slab_lrow;
+    const int64_t wn = n0 + row < N ? n0 + row : N - 1;
+    int64_t ofs = (int64_t)(c0 + seg * kSeg) * 8 + slab_lofs;
+    if (ofs > KG - 4) ofs = KG - 4;
+    dma4(Ws + wn * KG + ofs, ring_addr + (uint32_t)(WL::kSlab0 + (seg % kSlabs) * WL::kSlabBytes + t * 256));
+  };
+  // chunk c's copies, plus one slab copy for the segment after c's
+  auto issue = [&](int c) {
+    const uint32_t base = ring_addr + (uint32_t)(((c - c0) % STAGES) * S::kBytes);
+    const int64_t co = (int64_t)c * 128, so = (int64_t)c * 8;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) dma16(wsrc[i] + co, base + S::kW + i * 1024);
+    issue_slab((c - c0) / kSeg + 1, (c - c0) % kSeg);
+    if constexpr (AK == 1) {
+      dma4(asrc[0] + co, base + S::kA);
+    } else if constexpr (AK >= 8) {
+#pragma unroll
+      for (int i = 0; i < AI; ++i) dma16(asrc[i] + co, base + S::kA + i * 1024);
+    }
+    if constexpr (AK > 0) dma4(assrc + so, base + S::kAs);
+  };
+  // segment 0's slab, then fill the ring (before the fused transform, which
+  // then overlaps the copies)
+  if (c0 < c1) {
+#pragma unroll
+    for (int t = 0; t < kSeg; ++t) issue_slab(0, t);
+  }
+#pragma unroll
+  for (int q = 0; q < STAGES - 1; ++q)
+    if (c0 + q < c1) issue(c0 + q);
+
   if constexpr (FUSED) {
+    // one quad of lanes per 32-element group; each quad loads the inputs of
+    // up to kBatch groups before transforming them, so their load latencies
+    // overlap
+    constexpr int kBatch = 4;
+    constexpr int kQuads = kThreads / 4;
     const int groups_per_row = (int)KG;
-    const int tasks = (int)M * groups_per_row;      // one quad of lanes per 32-element group
+    const int tasks = (int)M * groups_per_row;
     const uint32_t quad = (uint32_t)lane & 3u;
-    for (int t0 = tid >> 2; t0 < tasks; t0 += kThreads / 4) {
-      const int m = t0 / groups_per_row, g = t0 % groups_per_row;
-      const int64_t col = (int64_t)g * 32 + quad * 8;
-      float t[8];
-      dec_load8<XT>(x, m * K + col, t);
-      const float4* sp = reinterpret_cast<const float4*>(s + col);
-      const float4 s0 = sp[0], s1 = sp[1];
-      t[0] = t[0] * s0.x; t[1] = t[1] * s0.y; t[2] = t[2] * s0.z; t[3] = t[3] * s0.w;
-      t[4] = t[4] * s1.x; t[5] = t[5] * s1.y; t[6] = t[6] * s1.z; t[7] = t[7] * s1.w;
-      hadamard32_quad(t, quad);
-      uint32_t b;
-      const uint32_t packed = quantize_quad(t, &b);
-      *reinterpret_cast<uint32_t*>(xcodes + m * xrb + g * 16 + quad * 4) = packed;
-      if (quad == 0) xscales[m * xrg + g] = (uint8_t)b;
+    for (int base = tid >> 2; base < tasks; base += kBatch * kQuads) {
+      float t[kBatch][8];
+      float4 sa[kBatch], sb[kBatch];
+#pragma unroll
+      for (int b = 0; b < kBatch; ++b) {
+        const int t0 = base + b * kQuads;   // the same for the quad's four lanes
+        if (t0 < tasks) {
+          const int m = t0 / groups_per_row, g = t0 % groups_per_row;
+          const int64_t col = (int64_t)g * 32 + quad * 8;
+          dec_load8<XT>(x, m * K + col, t[b]);
+          const float4* sp = reinterpret_cast<const float4*>(s + col);
+          sa[b] = sp[0];
+          sb[b] = sp[1];
+        }
+      }
+#pragma unroll
+      for (int b = 0; b < kBatch; ++b) {
+        const int t0 = base + b * kQuads;
+        if (t0 < tasks) {
+          const int m = t0 / groups_per_row, g = t0 % groups_per_row;
+          float* v = t[b];
+          v[0] = v[0] * sa[b].x; v[1] = v[1] * sa[b].y; v[2] = v[2] * sa[b].z; v[3] = v[3] * sa[b].w;
+          v[4] = v[4] * sb[b].x; v[5] = v[5] * sb[b].y; v[6] = v[6] * sb[b].z; v[7] = v[7] * sb[b].w;
+          hadamard32_quad(t[b], quad);
+          uint32_t e;
+          const uint32_t packed = quantize_quad(t[b], &e);
+          *reinterpret_cast<uint32_t*>(xcodes + m * xrb + g * 16 + quad * 4) = packed;
+          if (quad == 0) xscales[m * xrg + g] = (uint8_t)e;
+        }
+      }
     }
     __syncthreads();
   }
 
-  // ---- this wave's chunks
-  const int per_wave = (kc + WAVES - 1) / WAVES;
-  const int c0 = wave * per_wave;
-  const int c1 = (c0 + per_wave) < kc ? (c0 + per_wave) : kc;
-  int64_t wn = n0 + r32;
-  if (wn >= N) wn = N - 1;
-  const int64_t am = r32 < M ? r32 : M - 1;
-  const uint8_t* wrow = W + wn * KB;
-  const uint8_t* wsrow = Ws + wn * KG;
-  const uint8_t* arow = FUSED ? xcodes + am * xrb : A + am * KB;
-  const uint8_t* asrow = FUSED ? xscales + am * xrg : As + am * KG;
+  const int ar = r32 < M ? r32 : (int)M - 1;   // activation row of this lane's B column
+  const uint8_t* xrow = xcodes + ar * xrb;
+  const uint8_t* xsrow = xscales + ar * xrg;
 
   v16f_d acc;
 #pragma unroll
   for (int r = 0; r < 16; ++r) acc[r] = 0.0f;
 
-  // Two chunks per step: all their loads are issued before the first MFMA;
-  // no registers carry over between steps (other waves of the CU cover the
-  // load latency of this one).
-  for (int c = c0; c < c1; c += 2) {
-    const bool two = c + 1 < c1;
-    uint4 wa0[4], xb0[4], wa1[4], xb1[4];
-    load_chunk(wrow, c, h, wa0);
-    load_chunk(arow, c, h, xb0);
-    const uint32_t ws0 = load_scales(wsrow, c, h);
-    const uint32_t xs0 = load_scales(asrow, c, h);
-    uint32_t ws1 = 0, xs1 = 0;
-    if (two) {
-      load_chunk(wrow, c + 1, h, wa1);
-      load_chunk(arow, c + 1, h, xb1);
-      ws1 = load_scales(wsrow, c + 1, h);
-      xs1 = load_scales(asrow, c + 1, h);
+  for (int c = c0; c < c1; ++c) {
+    // the slot about to be refilled was read (into registers) one chunk ago;
+    // make sure those LDS reads have returned before the copy lands
+    wait_lgkmcnt0();
+    if (c + STAGES - 1 < c1) issue(c + STAGES - 1);
+    // wait until chunk c has landed: the copies of the chunks after it may
+    // stay in flight
+    const int ahead = (c1 - 1 - c) < (STAGES - 1) ? (c1 - 1 - c) : (STAGES - 1);
+    if (STAGES > 3 && ahead == 3) wait_vmcnt<(STAGES > 3 ? 3 : 0) * S::kCopies>();
+    else if (STAGES > 2 && ahead == 2) wait_vmcnt<(STAGES > 2 ? 2 : 0) * S::kCopies>();
+    else if (ahead == 1) wait_vmcnt<S::kCopies>();
+    else wait_vmcnt<0>();
+    const uint8_t* st = ring + ((c - c0) % STAGES) * S::kBytes;
+    uint4 wa[4], xb[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) wa[j] = *reinterpret_cast<const uint4*>(st + S::kW + dec_slot(r32, 2 * j + h));
+    const int cs = c - c0;
+    const uint2 wsv = *reinterpret_cast<const uint2*>(
+        slabs + ((cs / kSeg) % kSlabs) * WL::kSlabBytes + r32 * (8 * kSeg) + (cs % kSeg) * 8);
+    uint2 xsv;
+    if constexpr (AK == 1) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) xb[j] = *reinterpret_cast<const uint4*>(st + S::kA + ar * 128 + 16 * (2 * j + h));
+      xsv = *reinterpret_cast<const uint2*>(st + S::kAs + ar * 8);
+    } else if constexpr (AK >= 8) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) xb[j] = *reinterpret_cast<const uint4*>(st + S::kA + dec_slot(ar, 2 * j + h));
+      xsv = *reinterpret_cast<const uint2*>(st + S::kAs + ar * 8);
+    } else {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) xb[j] = *reinterpret_cast<const uint4*>(xrow + (int64_t)c * 128 + 16 * (2 * j + h));
+      xsv = *reinterpret_cast<const uint2*>(xsrow + (int64_t)c * 8);
     }
-    dec_mfma<0>(acc, wa0, xb0, ws0, xs0);
-    dec_mfma<1>(acc, wa0, xb0, ws0, xs0);
-    dec_mfma<2>(acc, wa0, xb0, ws0, xs0);
-    dec_mfma<3>(acc, wa0, xb0, ws0, xs0);
-    if (two) {
-      dec_mfma<0>(acc, wa1, xb1, ws1, xs1);
-      dec_mfma<1>(acc, wa1, xb1, ws1, xs1);
-      dec_mfma<2>(acc, wa1, xb1, ws1, xs1);
-      dec_mfma<3>(acc, wa1, xb1, ws1, xs1);
-    }
+    const uint32_t ws = gather_scales(wsv.x, wsv.y, h);
+    const uint32_t xs = gather_scales(xsv.x, xsv.y, h);
+    dec_mfma<0>(acc, wa, xb, ws, xs);
+    dec_mfma<1>(acc, wa, xb, ws, xs);
+    dec_mfma<2>(acc, wa, xb, ws, xs);
+    dec_mfma<3>(acc, wa, xb, ws, xs);
   }
 
   // ---- add the waves' 32x32 tiles in wave order.  Lane (r32, h), register r
-  // holds D[n = 8*(r/4) + 4*h + r%4][m = r32].
+  // holds D[n = 8*(r/4) + 4*h + r%4][m = r32].  Every wave's copies have
+  // landed (its last chunk waited for all of them), so after the barrier the
+  // rings and slabs can hold the partial sums.
+  __syncthreads();
 #pragma unroll
   for (int r = 0; r < 16; ++r) {
     const int n = 8 * (r >> 2) + 4 * h + (r & 3);
@@ -206,65 +354,111 @@ __global__ __launch_bounds__(64 * WAVES) void decode_gemm_kernel(
 
 // ---------------------------------------------------------------- host side
 
-static int decode_waves(int64_t K) {
-  const int64_t kc = K / 256;
-  if (kc >= 64) return 16;
-  if (kc >= 24) return 8;
-  return 4;
+static int decode_ak(int64_t M, bool fused) {
+  if (fused) return 0;
+  return M <= 2 ? 1 : (M <= 8 ? 8 : (M <= 16 ? 16 : 32));
 }
 
-static size_t decode_lds_bytes(int waves, int64_t M, int64_t K, bool fused) {
-  size_t b = (size_t)waves * 32 * 32 * 4;
-  if (fused) b += (size_t)M * (size_t)(dec_xrow_bytes(K) + dec_xrow_groups(K));
+static int stage_bytes(int ak) {
+  switch (ak) {
+    case 0: return DecStage<0>::kBytes;
+    case 1: return DecStage<1>::kBytes;
+    case 8: return DecStage<8>::kBytes;
+    case 16: return DecStage<16>::kBytes;
+    default: return DecStage<32>::kBytes;
+  }
+}
+
+static size_t wave_lds_bytes(int stages, int ak) {
+  return (size_t)stages * stage_bytes(ak) + kSlabs * 32 * 8 * (ak == 32 ? 4 : 8);
+}
+
+struct DecodeConfig {
+  int waves, stages, ak;
+};
+
+static size_t decode_lds_bytes(const DecodeConfig& d, int64_t M, int64_t K) {
+  size_t b = (size_t)d.waves * wave_lds_bytes(d.stages, d.ak);
+  if (d.ak == 0) b += (size_t)M * (size_t)(dec_xrow_bytes(K) + dec_xrow_groups(K));
   return b;
+}
+
+// Waves split K; each keeps STAGES - 1 chunks in flight.  The ring is made as
+// deep as LDS allows (2 to 4 slots), within half of the CU's LDS when the
+// grid has more blocks than CUs (two resident blocks per CU), within all of
+// it otherwise.
+static DecodeConfig decode_config(int64_t M, int64_t N, int64_t K, bool fused) {
+  DecodeConfig d;
+  d.ak = decode_ak(M, fused);
+  d.waves = K / 256 >= 24 ? 8 : 4;
+  const size_t budget = ceil_div(N, kDecRows) > 256 ? kDecLdsMax / 2 : kDecLdsMax;
+  d.stages = 4;
+  while (d.stages > 2 && decode_lds_bytes(d, M, K) > budget) --d.stages;
+  if (decode_lds_bytes(d, M, K) > kDecLdsMax && d.waves > 4) {   // e.g. 32 staged activation rows
+    d.waves = 4;
+    d.stages = 4;
+    while (d.stages > 2 && decode_lds_bytes(d, M, K) > budget) --d.stages;
+  }
+  if (const char* e = getenv("MACAQ_DECODE_WAVES")) d.waves = atoi(e) == 8 ? 8 : 4;      // tuning knobs
+  if (const char* e = getenv("MACAQ_DECODE_STAGES")) d.stages = atoi(e) >= 4 ? 4 : (atoi(e) == 3 ? 3 : 2);
+  return d;
 }
 
 bool decode_supported(int64_t M, int64_t N, int64_t K, int64_t E) {
   return E == 1 && M >= 1 && M <= kDecMaxM && N >= 1 && K % 256 == 0;
 }
 
-template <int WAVES, bool FUSED, typename XT>
+template <int WAVES, int STAGES, int AK, typename XT>
 static hipError_t launch_decode_w(const uint8_t* A, const uint8_t* As, const void* x, const float* s,
                                   const uint8_t* W, const uint8_t* Ws, int64_t M, int64_t N, int64_t K, float* Y,
-                                  hipStream_t stream) {
-  const size_t lds = decode_lds_bytes(WAVES, M, K, FUSED);
-  if (FUSED) {
-    static const hipError_t attr = hipFuncSetAttribute((const void*)decode_gemm_kernel<WAVES, FUSED, XT>,
-                                                       hipFuncAttributeMaxDynamicSharedMemorySize,
-                                                       (int)kDecLdsMax);
-    if (attr != hipSuccess) return attr;
-  }
-  decode_gemm_kernel<WAVES, FUSED, XT><<<dim3((unsigned)ceil_div(N, kDecRows)), dim3(64 * WAVES), lds, stream>>>(
+                                  size_t lds, hipStream_t stream) {
+  static_assert(DecWaveLds<STAGES, AK>::kBytes >= 32 * 32 * 4, "partial sums must fit in the rings");
+  static const hipError_t attr = hipFuncSetAttribute((const void*)decode_gemm_kernel<WAVES, STAGES, AK, XT>,
+                                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)kDecLdsMax);
+  if (attr != hipSuccess) return attr;
+  decode_gemm_kernel<WAVES, STAGES, AK, XT><<<dim3((unsigned)ceil_div(N, kDecRows)), dim3(64 * WAVES), lds, stream>>>(
       A, As, x, s, W, Ws, M, N, K, Y);
   return hipGetLastError();
 }
 
-template <bool FUSED, typename XT>
-static hipError_t launch_decode_impl(const uint8_t* A, const uint8_t* As, const void* x, const float* s,
-                                     const uint8_t* W, const uint8_t* Ws, int64_t M, int64_t N, int64_t K,
-                                     float* Y, hipStream_t stream) {
-  switch (decode_waves(K)) {
-    case 16: return launch_decode_w<16, FUSED, XT>(A, As, x, s, W, Ws, M, N, K, Y, stream);
-    case 8: return launch_decode_w<8, FUSED, XT>(A, As, x, s, W, Ws, M, N, K, Y, stream);
-    default: return launch_decode_w<4, FUSED, XT>(A, As, x, s, W, Ws, M, N, K, Y, stream);
+template <int AK, typename XT>
+static hipError_t launch_decode_impl(const DecodeConfig& d, const uint8_t* A, const uint8_t* As, const void* x,
+                                     const float* s, const uint8_t* W, const uint8_t* Ws, int64_t M, int64_t N,
+                                     int64_t K, float* Y, hipStream_t stream) {
+  const size_t lds = decode_lds_bytes(d, M, K);
+  if (lds > kDecLdsMax) return hipErrorInvalidValue;
+  if (d.waves == 8) {
+    if (d.stages == 4) return launch_decode_w<8, 4, AK, XT>(A, As, x, s, W, Ws, M, N, K, Y, lds, stream);
+    if (d.stages == 3) return launch_decode_w<8, 3, AK, XT>(A, As, x, s, W, Ws, M, N, K, Y, lds, stream);
+    return launch_decode_w<8, 2, AK, XT>(A, As, x, s, W, Ws, M, N, K, Y, lds, stream);
   }
+  if (d.stages == 4) return launch_decode_w<4, 4, AK, XT>(A, As, x, s, W, Ws, M, N, K, Y, lds, stream);
+  if (d.stages == 3) return launch_decode_w<4, 3, AK, XT>(A, As, x, s, W, Ws, M, N, K, Y, lds, stream);
+  return launch_decode_w<4, 2, AK, XT>(A, As, x, s, W, Ws, M, N, K, Y, lds, stream);
 }
 
 hipError_t launch_decode_gemm(const uint8_t* A, const uint8_t* As, const uint8_t* W, const uint8_t* Ws, int64_t M,
                               int64_t N, int64_t K, float* Y, hipStream_t stream) {
-  return launch_decode_impl<false, DecBf16>(A, As, nullptr, nullptr, W, Ws, M, N, K, Y, stream);
+  const DecodeConfig d = decode_config(M, N, K, false);
+  switch (d.ak) {
+    case 1: return launch_decode_impl<1, DecBf16>(d, A, As, nullptr, nullptr, W, Ws, M, N, K, Y, stream);
+    case 8: return launch_decode_impl<8, DecBf16>(d, A, As, nullptr, nullptr, W, Ws, M, N, K, Y, stream);
+    case 16: return launch_decode_impl<16, DecBf16>(d, A, As, nullptr, nullptr, W, Ws, M, N, K, Y, stream);
+    default: return launch_decode_impl<32, DecBf16>(d, A, As, nullptr, nullptr, W, Ws, M, N, K, Y, stream);
+  }
 }
 
 // -------- fused transform + GEMM entry used by macaq_linear
 
 bool linear_fused_supported(int64_t M, int64_t N, int64_t K, int64_t E) {
-  return decode_supported(M, N, K, E) && decode_lds_bytes(decode_waves(K), M, K, true) <= kDecLdsMax;
+  return decode_supported(M, N, K, E) && decode_lds_bytes(decode_config(M, N, K, true), M, K) <= kDecLdsMax;
 }
 
 hipError_t launch_linear_fused(const void* x, bool x_f32, const float* s, const uint8_t* B, const uint8_t* Bs,
                                int64_t M, int64_t N, int64_t K, float* Y, hipStream_t stream) {
-  if (x_f32) return launch_decode_impl<true, float>(nullptr, nullptr, x, s, B, Bs, M, N, K, Y, stream);
-  return launch_decode_impl<true, DecBf16>(nullptr, nullptr, x, s, B, Bs, M, N, K, Y, stream);
+  const DecodeConfig d = decode_config(M, N, K, true);
+  if (x_f32) return launch_decode_impl<0, float>(d, nullptr, nullptr, x, s, B, Bs, M, N, K, Y, stream);
+  return launch_decode_impl<0, DecBf16>(d, nullptr, nullptr, x, s, B, Bs, M, N, K, Y, stream);
 }
 
 }  // namespace macaq

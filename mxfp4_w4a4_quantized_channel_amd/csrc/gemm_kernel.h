@@ -486,21 +486,6 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void gemm_mxfp4_dlds_ker
 
 constexpr int kNumXcd = 8;
 
-template <int VM>
-__device__ __forceinline__ void wait_vmcnt() {
-  static_assert(VM >= 0 && VM < 64, "vmcnt range");
-  // gfx9 s_waitcnt: vmcnt[3:0] at bits 3:0, vmcnt[5:4] at bits 15:14,
-  // expcnt (7) and lgkmcnt (15) left at their maxima (no wait).
-  __builtin_amdgcn_s_waitcnt((VM & 0xF) | ((VM >> 4) << 14) | (0x7 << 4) | (0xF << 8));
-}
-
-__device__ __forceinline__ void dma16(const uint8_t* g, uint32_t lds_addr) {
-  asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(g), "{m0}"(lds_addr) : "memory");
-}
-__device__ __forceinline__ void dma4(const uint8_t* g, uint32_t lds_addr) {
-  asm volatile("global_load_lds_dword %0, off" ::"v"(g), "{m0}"(lds_addr) : "memory");
-}
-
 template <int BM, int BN, int BK, int SWZ = 0>
 struct PipeLayout {
   static constexpr int kCPR = BK / 32;              // chunks (groups) per tile row

@@ -118,6 +118,35 @@ __device__ __forceinline__ uint32_t quantize_quad(float (&t)[8], uint32_t* scale
   return e2m1_pack8(v);
 }
 
+// ---- direct global -> LDS copies and explicit wait counts
+//
+// global_load_lds_dword(x4): every lane copies 4 (16) bytes from its own
+// global address to LDS at M0 + 4 (16) * lane.  The copies count in vmcnt
+// like other vector loads and complete in issue order with them; the
+// compiler does not see them, so code that overlaps them with compute waits
+// for them explicitly with wait_vmcnt.  A compiler-visible vector load
+// issued after such copies makes the compiler's own waits stricter (it does
+// not count the copies), never weaker.
+
+template <int VM>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(VM >= 0 && VM < 64, "vmcnt range");
+  // gfx9 s_waitcnt: vmcnt[3:0] at bits 3:0, vmcnt[5:4] at bits 15:14,
+  // expcnt (7) and lgkmcnt (15) left at their maxima (no wait).
+  __builtin_amdgcn_s_waitcnt((VM & 0xF) | ((VM >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+// Wait until every LDS (and scalar-memory) access of this wave completed;
+// vmcnt and expcnt are left at their maxima.
+__device__ __forceinline__ void wait_lgkmcnt0() { __builtin_amdgcn_s_waitcnt(0xF | (0x3 << 14) | (0x7 << 4)); }
+
+__device__ __forceinline__ void dma16(const uint8_t* g, uint32_t lds_addr) {
+  asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(g), "{m0}"(lds_addr) : "memory");
+}
+__device__ __forceinline__ void dma4(const uint8_t* g, uint32_t lds_addr) {
+  asm volatile("global_load_lds_dword %0, off" ::"v"(g), "{m0}"(lds_addr) : "memory");
+}
+
 __host__ __device__ constexpr int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 }  // namespace macaq
