@@ -92,6 +92,11 @@ __device__ __forceinline__ void dec_load8<float>(const void* x, int64_t off, flo
   t[0] = a.x; t[1] = a.y; t[2] = a.z; t[3] = a.w; t[4] = b.x; t[5] = b.y; t[6] = b.z; t[7] = b.w;
 }
 
+template <typename XT>
+constexpr int dec_eb = 2;          // bytes per activation element
+template <>
+constexpr int dec_eb<float> = 4;
+
 // LDS row strides of the fused activation copy (padded against bank conflicts)
 __host__ __device__ constexpr int64_t dec_xrow_bytes(int64_t K) { return K / 2 + 16; }
 __host__ __device__ constexpr int64_t dec_xrow_groups(int64_t K) { return K / 32 + 8; }
@@ -100,7 +105,12 @@ __host__ __device__ constexpr int64_t dec_xrow_groups(int64_t K) { return K / 32
 // of the block's 32 rows (4 x 1 KiB, row r at (r / 8) KiB + (r % 8) * 128
 // with 16-byte slot p holding piece p ^ (r % 8)), then the activation's part
 // of the chunk.  Activation kinds AK:
-//   0      resident: the whole activation sits in LDS (fused transform);
+//   -1     streamed fused transform, M <= 2: the chunk's 256 values of s
+//          (1 KiB, one dwordx4 instruction) and of x rows 0..1 (2 x 256 x EB
+//          bytes, EB / 2 dwordx4 instructions); the wave transforms and
+//          quantizes them after the chunk lands;
+//   0      resident: the whole activation sits in LDS (fused transform by the
+//          block before the loop);
 //   1      M <= 2: codes of rows 0..1 (2 x 128 B, plain layout) copied by one
 //          dword instruction;
 //   8,16,32  M <= AK: codes of AK rows in the swizzled layout (AK / 8
@@ -118,24 +128,30 @@ __host__ __device__ constexpr int64_t dec_xrow_groups(int64_t K) { return K / 32
 // LDS.
 constexpr int kSlabs = 3;
 
-template <int AK>
+template <int AK, int EB = 2>
 struct DecStage {
   static constexpr int kW = 0;
-  static constexpr int kA = 4096;
-  static constexpr int kABytes = AK == 0 ? 0 : (AK == 1 ? 256 : AK * 128);
+  static constexpr int kA = 4096;                  // streamed: s chunk; else activation codes
+  static constexpr int kX = kA + 1024;             // streamed: x chunk of rows 0..1
+  static constexpr int kABytes = AK < 0 ? 1024 + 512 * EB : (AK == 0 ? 0 : (AK == 1 ? 256 : AK * 128));
   static constexpr int kAs = kA + kABytes;
-  static constexpr int kBytes = kAs + (AK == 0 ? 0 : 256);
-  static constexpr int kACopies = AK == 0 ? 0 : (AK == 1 ? 2 : AK / 8 + 1);
+  static constexpr int kBytes = kAs + (AK > 0 ? 256 : 0);
+  static constexpr int kACopies = AK < 0 ? 1 + EB / 2 : (AK == 0 ? 0 : (AK == 1 ? 2 : AK / 8 + 1));
   static constexpr int kCopies = 5 + kACopies;   // copy instructions per chunk (4 codes + 1 slab + activation)
 };
 
-template <int STAGES, int AK>
+// Per wave: STAGES ring slots, the scale slabs, and (streamed) the wave's
+// quantized activation chunk: codes of rows 0..1 (2 x 128 B) and their 2 x 8
+// scale bytes.
+template <int STAGES, int AK, int EB = 2>
 struct DecWaveLds {
   static constexpr int kSeg = AK == 32 ? 4 : 8;          // chunks per scale segment
   static constexpr int kRowDwords = 2 * kSeg;            // slab row: 8 kSeg bytes
   static constexpr int kSlabBytes = 32 * 8 * kSeg;
-  static constexpr int kSlab0 = STAGES * DecStage<AK>::kBytes;
-  static constexpr int kBytes = kSlab0 + kSlabs * kSlabBytes;
+  static constexpr int kSlab0 = STAGES * DecStage<AK, EB>::kBytes;
+  static constexpr int kXq = kSlab0 + kSlabs * kSlabBytes;
+  static constexpr int kXqBytes = AK < 0 ? 288 : 0;
+  static constexpr int kBytes = kXq + kXqBytes;
 };
 
 __device__ __forceinline__ int dec_slot(int row, int piece) { return (row >> 3) * 1024 + (row & 7) * 128 + 16 * (piece ^ (row & 7)); }
@@ -146,8 +162,10 @@ __global__ __launch_bounds__(64 * WAVES) void decode_gemm_kernel(
     const void* __restrict__ x, const float* __restrict__ s,           // activations and scale (fused)
     const uint8_t* __restrict__ W, const uint8_t* __restrict__ Ws, int64_t M, int64_t N, int64_t K,
     float* __restrict__ Y) {
-  using S = DecStage<AK>;
-  constexpr bool FUSED = AK == 0;
+  constexpr int EB = dec_eb<XT>;
+  using S = DecStage<AK, EB>;
+  constexpr bool FUSED = AK == 0;     // resident activation, transformed before the loop
+  constexpr bool STREAM = AK < 0;     // activation transformed chunk by chunk in the loop
   constexpr int AI = AK >= 8 ? AK / 8 : 1;
   extern __shared__ __attribute__((aligned(16))) uint8_t dsm[];
   constexpr int kThreads = 64 * WAVES;
@@ -160,13 +178,14 @@ __global__ __launch_bounds__(64 * WAVES) void decode_gemm_kernel(
   const int r32 = lane & 31;
   const int h = lane >> 5;
 
-  using WL = DecWaveLds<STAGES, AK>;
+  using WL = DecWaveLds<STAGES, AK, EB>;
   // LDS: per wave STAGES ring slots and kSlabs scale slabs (all reused for
   // the [WAVES][32][32] fp32 partial sums after the loop), then (fused) the
   // activation codes [M][K/2 + 16] and scales [M][K/32 + 8].
   uint8_t* ring = dsm + wave * WL::kBytes;
   const uint32_t ring_addr = (uint32_t)(uintptr_t)ring;
   const uint8_t* slabs = ring + WL::kSlab0;
+  uint8_t* xq = ring + WL::kXq;   // streamed: this chunk's quantized activation
   float* red = reinterpret_cast<float*>(dsm);
   const int64_t xrb = dec_xrow_bytes(K), xrg = dec_xrow_groups(K);
   uint8_t* xcodes = dsm + WAVES * WL::kBytes;
@@ -207,6 +226,17 @@ __global__ __launch_bounds__(64 * WAVES) void decode_gemm_kernel(
     const int64_t ams = (lane >> 1) < M ? (lane >> 1) : M - 1;
     assrc = As + ams * KG + 4 * (lane & 1);
   }
+  // streamed: copy i of the x chunk covers bytes 1024 i + 16 l of the
+  // [2 rows][256 EB bytes] area; rows past M repeat row M - 1
+  const uint8_t* xsrc[STREAM ? EB / 2 : 1];
+  if constexpr (STREAM) {
+#pragma unroll
+    for (int i = 0; i < EB / 2; ++i) {
+      const int p = 1024 * i + 16 * lane;
+      const int64_t row = p / (256 * EB) < M ? p / (256 * EB) : M - 1;
+      xsrc[i] = reinterpret_cast<const uint8_t*>(x) + row * K * EB + p % (256 * EB);
+    }
+  }
   // copy t of the W' scale slab of segment seg (relative to c0)
   auto issue_slab = [&](int seg, int t) {
     const int row = t * (64 / kD) + slab_lrow;
@@ -229,6 +259,11 @@ __global__ __launch_bounds__(64 * WAVES) void decode_gemm_kernel(
       for (int i = 0; i < AI; ++i) dma16(asrc[i] + co, base + S::kA + i * 1024);
     }
     if constexpr (AK > 0) dma4(assrc + so, base + S::kAs);
+    if constexpr (STREAM) {
+      dma16(reinterpret_cast<const uint8_t*>(s) + (int64_t)c * 1024 + 16 * lane, base + S::kA);
+#pragma unroll
+      for (int i = 0; i < EB / 2; ++i) dma16(xsrc[i] + (int64_t)c * 256 * EB, base + S::kX + i * 1024);
+    }
   };
   // segment 0's slab, then fill the ring (before the fused transform, which
   // then overlaps the copies)
@@ -319,6 +354,29 @@ __global__ __launch_bounds__(64 * WAVES) void decode_gemm_kernel(
 #pragma unroll
       for (int j = 0; j < 4; ++j) xb[j] = *reinterpret_cast<const uint4*>(st + S::kA + dec_slot(ar, 2 * j + h));
       xsv = *reinterpret_cast<const uint2*>(st + S::kAs + ar * 8);
+    } else if constexpr (STREAM) {
+      // quad q of the wave: group q % 8 of row q / 8 (lanes 4q..4q+3, eight
+      // values each), from the staged x and s; results to xq
+      const int q = lane >> 2, m = q >> 3, g = q & 7;
+      const uint32_t quad = (uint32_t)lane & 3u;
+      if (m < M) {   // the same for the quad's four lanes
+        float t[8];
+        dec_load8<XT>(st + S::kX + m * 256 * EB, g * 32 + quad * 8, t);
+        const float4* sp = reinterpret_cast<const float4*>(st + S::kA + (g * 32 + quad * 8) * 4);
+        const float4 sa = sp[0], sb = sp[1];
+        t[0] = t[0] * sa.x; t[1] = t[1] * sa.y; t[2] = t[2] * sa.z; t[3] = t[3] * sa.w;
+        t[4] = t[4] * sb.x; t[5] = t[5] * sb.y; t[6] = t[6] * sb.z; t[7] = t[7] * sb.w;
+        hadamard32_quad(t, quad);
+        uint32_t e;
+        const uint32_t packed = quantize_quad(t, &e);
+        *reinterpret_cast<uint32_t*>(xq + m * 128 + g * 16 + quad * 4) = packed;
+        if (quad == 0) xq[256 + m * 8 + g] = (uint8_t)e;
+      }
+      // the wave's LDS accesses complete in order: the reads below see the
+      // writes above
+#pragma unroll
+      for (int j = 0; j < 4; ++j) xb[j] = *reinterpret_cast<const uint4*>(xq + ar * 128 + 16 * (2 * j + h));
+      xsv = *reinterpret_cast<const uint2*>(xq + 256 + ar * 8);
     } else {
 #pragma unroll
       for (int j = 0; j < 4; ++j) xb[j] = *reinterpret_cast<const uint4*>(xrow + (int64_t)c * 128 + 16 * (2 * j + h));
@@ -354,13 +412,16 @@ __global__ __launch_bounds__(64 * WAVES) void decode_gemm_kernel(
 
 // ---------------------------------------------------------------- host side
 
+// Activation kind: fused M <= 2 streams the transform through the loop;
+// larger fused M transforms the whole activation into LDS first.
 static int decode_ak(int64_t M, bool fused) {
-  if (fused) return 0;
+  if (fused) return M <= 2 ? -1 : 0;
   return M <= 2 ? 1 : (M <= 8 ? 8 : (M <= 16 ? 16 : 32));
 }
 
-static int stage_bytes(int ak) {
+static int stage_bytes(int ak, int eb) {
   switch (ak) {
+    case -1: return eb == 4 ? DecStage<-1, 4>::kBytes : DecStage<-1, 2>::kBytes;
     case 0: return DecStage<0>::kBytes;
     case 1: return DecStage<1>::kBytes;
     case 8: return DecStage<8>::kBytes;
@@ -369,16 +430,16 @@ static int stage_bytes(int ak) {
   }
 }
 
-static size_t wave_lds_bytes(int stages, int ak) {
-  return (size_t)stages * stage_bytes(ak) + kSlabs * 32 * 8 * (ak == 32 ? 4 : 8);
+static size_t wave_lds_bytes(int stages, int ak, int eb) {
+  return (size_t)stages * stage_bytes(ak, eb) + kSlabs * 32 * 8 * (ak == 32 ? 4 : 8) + (ak < 0 ? 288 : 0);
 }
 
 struct DecodeConfig {
-  int waves, stages, ak;
+  int waves, stages, ak, eb;
 };
 
 static size_t decode_lds_bytes(const DecodeConfig& d, int64_t M, int64_t K) {
-  size_t b = (size_t)d.waves * wave_lds_bytes(d.stages, d.ak);
+  size_t b = (size_t)d.waves * wave_lds_bytes(d.stages, d.ak, d.eb);
   if (d.ak == 0) b += (size_t)M * (size_t)(dec_xrow_bytes(K) + dec_xrow_groups(K));
   return b;
 }
@@ -386,15 +447,16 @@ static size_t decode_lds_bytes(const DecodeConfig& d, int64_t M, int64_t K) {
 // Waves split K; each keeps STAGES - 1 chunks in flight.  The ring is made as
 // deep as LDS allows (2 to 4 slots), within half of the CU's LDS when the
 // grid has more blocks than CUs (two resident blocks per CU), within all of
-// it otherwise.
-static DecodeConfig decode_config(int64_t M, int64_t N, int64_t K, bool fused) {
+// it otherwise; 8 waves drop to 4 where even 2 slots do not fit.
+static DecodeConfig decode_config(int64_t M, int64_t N, int64_t K, bool fused, int eb) {
   DecodeConfig d;
   d.ak = decode_ak(M, fused);
+  d.eb = eb;
   d.waves = K / 256 >= 24 ? 8 : 4;
   const size_t budget = ceil_div(N, kDecRows) > 256 ? kDecLdsMax / 2 : kDecLdsMax;
   d.stages = 4;
   while (d.stages > 2 && decode_lds_bytes(d, M, K) > budget) --d.stages;
-  if (decode_lds_bytes(d, M, K) > kDecLdsMax && d.waves > 4) {   // e.g. 32 staged activation rows
+  if (decode_lds_bytes(d, M, K) > kDecLdsMax && d.waves > 4) {
     d.waves = 4;
     d.stages = 4;
     while (d.stages > 2 && decode_lds_bytes(d, M, K) > budget) --d.stages;
@@ -412,7 +474,7 @@ template <int WAVES, int STAGES, int AK, typename XT>
 static hipError_t launch_decode_w(const uint8_t* A, const uint8_t* As, const void* x, const float* s,
                                   const uint8_t* W, const uint8_t* Ws, int64_t M, int64_t N, int64_t K, float* Y,
                                   size_t lds, hipStream_t stream) {
-  static_assert(DecWaveLds<STAGES, AK>::kBytes >= 32 * 32 * 4, "partial sums must fit in the rings");
+  static_assert(DecWaveLds<STAGES, AK, dec_eb<XT>>::kBytes >= 32 * 32 * 4, "partial sums must fit in the rings");
   static const hipError_t attr = hipFuncSetAttribute((const void*)decode_gemm_kernel<WAVES, STAGES, AK, XT>,
                                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)kDecLdsMax);
   if (attr != hipSuccess) return attr;
@@ -439,7 +501,7 @@ static hipError_t launch_decode_impl(const DecodeConfig& d, const uint8_t* A, co
 
 hipError_t launch_decode_gemm(const uint8_t* A, const uint8_t* As, const uint8_t* W, const uint8_t* Ws, int64_t M,
                               int64_t N, int64_t K, float* Y, hipStream_t stream) {
-  const DecodeConfig d = decode_config(M, N, K, false);
+  const DecodeConfig d = decode_config(M, N, K, false, 2);
   switch (d.ak) {
     case 1: return launch_decode_impl<1, DecBf16>(d, A, As, nullptr, nullptr, W, Ws, M, N, K, Y, stream);
     case 8: return launch_decode_impl<8, DecBf16>(d, A, As, nullptr, nullptr, W, Ws, M, N, K, Y, stream);
@@ -450,13 +512,21 @@ hipError_t launch_decode_gemm(const uint8_t* A, const uint8_t* As, const uint8_t
 
 // -------- fused transform + GEMM entry used by macaq_linear
 
+// Whether the fused path fits, for either activation dtype.
 bool linear_fused_supported(int64_t M, int64_t N, int64_t K, int64_t E) {
-  return decode_supported(M, N, K, E) && decode_lds_bytes(decode_config(M, N, K, true), M, K) <= kDecLdsMax;
+  if (!decode_supported(M, N, K, E)) return false;
+  for (int eb : {2, 4})
+    if (decode_lds_bytes(decode_config(M, N, K, true, eb), M, K) > kDecLdsMax) return false;
+  return true;
 }
 
 hipError_t launch_linear_fused(const void* x, bool x_f32, const float* s, const uint8_t* B, const uint8_t* Bs,
                                int64_t M, int64_t N, int64_t K, float* Y, hipStream_t stream) {
-  const DecodeConfig d = decode_config(M, N, K, true);
+  const DecodeConfig d = decode_config(M, N, K, true, x_f32 ? 4 : 2);
+  if (d.ak < 0) {
+    if (x_f32) return launch_decode_impl<-1, float>(d, nullptr, nullptr, x, s, B, Bs, M, N, K, Y, stream);
+    return launch_decode_impl<-1, DecBf16>(d, nullptr, nullptr, x, s, B, Bs, M, N, K, Y, stream);
+  }
   if (x_f32) return launch_decode_impl<0, float>(d, nullptr, nullptr, x, s, B, Bs, M, N, K, Y, stream);
   return launch_decode_impl<0, DecBf16>(d, nullptr, nullptr, x, s, B, Bs, M, N, K, Y, stream);
 }
