@@ -238,18 +238,6 @@ def main():
         if st != 0:
             raise RuntimeError(mx.lib().macaq_last_error().decode())
 
-    def run_split(i, ev):
-        xp, wcp, wsp, yp = step_args(i)
-        ev[0].record(stream)
-        st = mx.macaq_quant_act(xp, xdt, p(s0.data_ptr()), off_p, E, M, K, p(a_codes.data_ptr()),
-                                p(a_scales.data_ptr()), sp)
-        ev[1].record(stream)
-        st |= mx.macaq_gemm(p(a_codes.data_ptr()), p(a_scales.data_ptr()), off_p, E, wcp, wsp, M, N, K, yp,
-                            p(gemm_ws.data_ptr()), gemm_ws.numel(), sp)
-        ev[2].record(stream)
-        if st != 0:
-            raise RuntimeError(mx.lib().macaq_last_error().decode())
-
     # ---- warmup
     for i in range(args.warmup):
         run_linear(i)
@@ -266,23 +254,38 @@ def main():
     flops = 2.0 * M * N * K
     value = flops / (wall / args.steps) / 1e12
 
-    # ---- per-kernel durations with HIP events on the launch stream
-    act_us = gemm_us = None
+    # ---- per-kernel durations: a timed region of K back-to-back launches of
+    # one kernel on the launch stream, bracketed by HIP events (an unfused
+    # step is the activation kernel then the GEMM, the two launches
+    # macaq_linear makes on that path)
+    def act_only(i):
+        xp = step_args(i)[0]
+        if mx.macaq_quant_act(xp, xdt, p(s0.data_ptr()), off_p, E, M, K, p(a_codes.data_ptr()),
+                              p(a_scales.data_ptr()), sp) != 0:
+            raise RuntimeError(mx.lib().macaq_last_error().decode())
+
+    def gemm_only(i):
+        _, wcp, wsp, yp = step_args(i)
+        if mx.macaq_gemm(p(a_codes.data_ptr()), p(a_scales.data_ptr()), off_p, E, wcp, wsp, M, N, K, yp,
+                         p(gemm_ws.data_ptr()), gemm_ws.numel(), sp) != 0:
+            raise RuntimeError(mx.lib().macaq_last_error().decode())
+
+    def kernel_us(fn):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for i in range(args.steps):
+            fn(i)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / args.steps * 1e3
+
+    act_us = None
     if split:
-        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
-        for i in range(args.steps):
-            run_split(i, evs[i])
-        torch.cuda.synchronize()
-        act_us = sum(e[0].elapsed_time(e[1]) for e in evs) / args.steps * 1e3
-        gemm_us = sum(e[1].elapsed_time(e[2]) for e in evs) / args.steps * 1e3
+        act_us = kernel_us(act_only)
+        gemm_us = kernel_us(gemm_only)
     else:
-        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
-        for i in range(args.steps):
-            evs[i][0].record(stream)
-            run_linear(i)
-            evs[i][1].record(stream)
-        torch.cuda.synchronize()
-        gemm_us = sum(e[0].elapsed_time(e[1]) for e in evs) / args.steps * 1e3
+        gemm_us = kernel_us(run_linear)
 
     # algorithmic bytes
     xb = M * K * x0.element_size()
@@ -314,7 +317,10 @@ def main():
                                 "bytes": act_alg, "frac_of_hbm_peak": round(act_alg / act_us / 1e3 / PEAK_HBM_GBPS, 4)}
     gemm_name = "fused transform+GEMM" if fused else "MXFP4 GEMM"
     if fused or M <= 32:
-        gemm_bytes = w_alg + xb + M * N * 4
+        # the kernel's algorithmic HBM bytes: W' codes+scales, its activation
+        # input (x and s when fused, else the MXFP4 codes+scales), y
+        a_in = xb + 4 * K if fused else M * K // 2 + M * K // 32
+        gemm_bytes = w_alg + a_in + M * N * 4
         ach = gemm_bytes / gemm_us / 1e3
         out["roofline"] = {"kernel": gemm_name, "bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBPS,
                            "unit": "GB/s", "frac": round(ach / PEAK_HBM_GBPS, 4), "us": round(gemm_us, 2),

@@ -8,9 +8,10 @@
 // MXFP4: 32-element groups, E8M0 scale, E2M1 elements) and "MACaQ
 // 真正解决的是跨层耦合" (32-element Hadamard blocks aligned to the groups).
 //
-// One lane owns one 32-value group: a wave covers 64 groups (2048 columns)
-// of a few consecutive rows (see act_quant_lane_kernel below).  The kernel is
-// HBM-bound: per element it reads 2 bytes (bf16) and writes 17/32 bytes.
+// One lane owns one 32-value group: a wave covers 64 groups at a time, a
+// segment of 64, 32 or 16 groups in each of 1, 2 or 4 consecutive rows (see
+// act_quant_lane_kernel below).  The kernel is HBM-bound: per element it
+// reads 2 bytes (bf16) and writes 17/32 bytes.
 #include <cstdlib>
 
 #include "mx_common.h"
@@ -30,14 +31,12 @@ __global__ void encode_e2m1_kernel(const float* __restrict__ v, int64_t n, uint8
 }
 
 // ---------------------------------------------------------------------------
-// One-lane-per-group kernel (the launcher's choice).  A wave covers 64
-// groups (2048 columns) of a row; the row segment is read with coalesced
-// 16-byte loads (lane l, instruction i: bytes 1024i + 16l), written to a
-// wave-private LDS buffer whose 32-value groups sit 16 bytes apart more than
-// their size (no bank conflicts on the per-group reads), and each lane then
-// reads its own group.  All five butterfly stages run in the lane's
-// registers.  The next row's loads are in flight while a row is
-// transformed.
+// One-lane-per-group kernel.  A wave's 64 groups are read with coalesced
+// 16-byte loads, written to a wave-private LDS buffer whose 32-value groups
+// sit 16 bytes apart more than their size (no bank conflicts on the
+// per-group reads), and each lane then reads its own group.  All five
+// butterfly stages run in the lane's registers.  The next rows' loads are in
+// flight while the current ones are transformed.
 //
 // Normalization folded into the quantization multiply: amax(x') equals
 // RNE(max|u| * C) because rounding is monotone, and for scale bytes 3..250
@@ -144,79 +143,94 @@ __device__ __forceinline__ void quantize_group_plain(const float (&u)[32], uint4
   *b_out = b;
 }
 
+// One wave processes a segment of GS consecutive groups (GS * 32 columns) of
+// 64 / GS consecutive rows at a time (GS = 64, 32 or 16, chosen so that the
+// segments tile a row with the fewest idle lanes), for `steps` such row
+// blocks.  Lane l owns group (l % GS) of the segment in row l / GS of the
+// block.  A block's row segments are loaded with coalesced 16-byte loads
+// (load i covers bytes 1024 i + 16 l of the concatenated segments; a segment
+// is at least 1 KiB, so no load straddles two rows).
+//
 // PLAIN: quantize the rows as they are (s = 1, H = I), the "pure MXFP4"
 // baseline against which the online transform's cost is measured.
 template <int EB, bool RECIP, bool PLAIN = false>
 __global__ __launch_bounds__(256) void act_quant_lane_kernel(
     const void* __restrict__ x, const float* __restrict__ s, const int32_t* __restrict__ offsets, int E,
     int64_t rows_per_expert, int64_t M, int64_t K, uint8_t* __restrict__ codes, uint8_t* __restrict__ scales,
-    int rows_per_wave) {
+    int gs_log2, int steps) {
   using IO = GroupIo<EB>;
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
   const int lane = threadIdx.x & 63;
   const int wave_in_block = threadIdx.x >> 6;
   const int64_t wave = (int64_t)blockIdx.x * 4 + wave_in_block;
   const int64_t KG = K >> 5;
-  const int64_t nseg = ceil_div(KG, 64);
+  const int gs = 1 << gs_log2;
+  const int rw = 64 >> gs_log2;                      // rows per block step
+  const int64_t nseg = ceil_div(KG, gs);
   const int64_t seg = wave % nseg;
-  const int64_t r0 = (wave / nseg) * rows_per_wave;
+  const int64_t r0 = (wave / nseg) * steps * rw;
   if (r0 >= M) return;
-  const int64_t r1 = (r0 + rows_per_wave) < M ? (r0 + rows_per_wave) : M;
-  const int64_t g = seg * 64 + lane;           // this lane's group
-  const bool active = g < KG;
-  const int64_t seg_bytes_valid = (KG - seg * 64 < 64 ? KG - seg * 64 : 64) * IO::kGroupBytes;
+  const int64_t r1 = (r0 + (int64_t)steps * rw) < M ? (r0 + (int64_t)steps * rw) : M;
+  const int lr = lane >> gs_log2;                    // this lane's row within a block step
+  const int64_t g = seg * gs + (lane & (gs - 1));    // this lane's group
+  const bool g_ok = g < KG;
+  const int seg_log2 = gs_log2 + 5 + (EB == 4 ? 2 : 1);   // log2 bytes of one row's segment
+  const int64_t seg_valid = (KG - seg * gs < gs ? KG - seg * gs : gs) * IO::kGroupBytes;
   uint8_t* buf = lds + wave_in_block * IO::kWaveLds;
 
-  // loads of one row segment: lane l, load i -> segment bytes 1024 i + 16 l
   uint4 ld[IO::kLoads];
-  auto issue_loads = [&](int64_t r) {
-    const uint8_t* src = reinterpret_cast<const uint8_t*>(x) + (r * K + seg * 2048) * EB;
+  auto issue_loads = [&](int64_t ra) {
+    const uint8_t* base = reinterpret_cast<const uint8_t*>(x) + (ra * K + seg * gs * 32) * EB;
 #pragma unroll
     for (int i = 0; i < IO::kLoads; ++i) {
-      const int off = 1024 * i + 16 * lane;
-      ld[i] = off < seg_bytes_valid ? *reinterpret_cast<const uint4*>(src + off) : make_uint4(0, 0, 0, 0);
+      const int bpos = 1024 * i + 16 * lane;
+      const int row_l = bpos >> seg_log2, o = bpos & ((1 << seg_log2) - 1);
+      ld[i] = (ra + row_l < r1 && o < seg_valid)
+                  ? *reinterpret_cast<const uint4*>(base + (int64_t)row_l * K * EB + o)
+                  : make_uint4(0, 0, 0, 0);
     }
   };
+  // expert of this lane's first row
   int e = 0;
-  if (rows_per_expert == 0 && offsets != nullptr) {
+  if (rows_per_expert > 0) {
+    e = (int)((r0 + lr) / rows_per_expert);
+  } else if (offsets != nullptr) {
     int lo = 0, hi = E - 1;
     while (lo < hi) {
       const int mid = (lo + hi) >> 1;
-      if ((int64_t)offsets[mid + 1] > r0) hi = mid; else lo = mid + 1;
+      if ((int64_t)offsets[mid + 1] > r0 + lr) hi = mid; else lo = mid + 1;
     }
     e = lo;
-  } else if (rows_per_expert > 0) {
-    e = (int)(r0 / rows_per_expert);
   }
   int cur_e = -1;
   float sc[32];
 
   issue_loads(r0);
-  for (int64_t r = r0; r < r1; ++r) {
-    // scatter the segment into the padded per-group layout
+  for (int64_t ra = r0; ra < r1; ra += rw) {
+    // scatter the block's segments into the padded per-group layout
 #pragma unroll
     for (int i = 0; i < IO::kLoads; ++i) {
       const int off = 1024 * i + 16 * lane;
       const int grp = off / IO::kGroupBytes, part = off % IO::kGroupBytes;
       *reinterpret_cast<uint4*>(buf + grp * IO::kLdsGroup + part) = ld[i];
     }
-    if (r + 1 < r1) issue_loads(r + 1);
+    if (ra + rw < r1) issue_loads(ra + rw);
+    const int64_t r = ra + lr;                       // this lane's row
+    const bool active = g_ok && r < r1;
     // expert of row r and its scale factors for this lane's group
     if (rows_per_expert > 0) e = (int)(r / rows_per_expert);
     else if (offsets != nullptr) while (e + 1 < E && r >= (int64_t)offsets[e + 1]) ++e;
-    if (!PLAIN && e != cur_e) {
+    if (!PLAIN && active && e != cur_e) {
       cur_e = e;
-      if (active) {
-        const float4* sp = reinterpret_cast<const float4*>(s + (int64_t)e * K + g * 32);
+      const float4* sp = reinterpret_cast<const float4*>(s + (int64_t)e * K + g * 32);
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          const float4 q = sp[i];
-          sc[4 * i] = q.x; sc[4 * i + 1] = q.y; sc[4 * i + 2] = q.z; sc[4 * i + 3] = q.w;
-        }
-        if (RECIP) {
+      for (int i = 0; i < 8; ++i) {
+        const float4 q = sp[i];
+        sc[4 * i] = q.x; sc[4 * i + 1] = q.y; sc[4 * i + 2] = q.z; sc[4 * i + 3] = q.w;
+      }
+      if (RECIP) {
 #pragma unroll
-          for (int i = 0; i < 32; ++i) sc[i] = 1.0f / sc[i];  // IEEE-correct fp32 division
-        }
+        for (int i = 0; i < 32; ++i) sc[i] = 1.0f / sc[i];  // IEEE-correct fp32 division
       }
     }
     uint4 q[EB * 2];
@@ -243,32 +257,66 @@ __global__ __launch_bounds__(256) void act_quant_lane_kernel(
 
 // ---------------------------------------------------------------- launchers
 
+// Segment width (log2 of 64, 32 or 16 groups) that leaves the fewest idle
+// lanes on a row of KG groups; ties go to the wider segment.
+static int act_gs_log2(int64_t KG) {
+  int best = 6;
+  int64_t best_idle = ceil_div(KG, 64) * 64 - KG;
+  for (int l = 5; l >= 4; --l) {
+    const int64_t idle = ceil_div(KG, (int64_t)1 << l) * ((int64_t)1 << l) - KG;
+    if (idle < best_idle) {
+      best = l;
+      best_idle = idle;
+    }
+  }
+  return best;
+}
+
+struct ActLaunch {
+  int gs_log2, steps;
+  dim3 grid;
+};
+
+// Block steps per wave: units / 3072 clamped to 2..6 (measured on MI355X
+// for 4K..30K units; longer waves also amortise the per-lane load of s).
+static ActLaunch act_launch(int64_t M, int64_t K) {
+  ActLaunch a;
+  a.gs_log2 = act_gs_log2(K / 32);
+  const int64_t rw = 64 >> a.gs_log2;
+  const int64_t nseg = ceil_div(K / 32, (int64_t)1 << a.gs_log2);
+  const int64_t blocks = ceil_div(M, rw);
+  int64_t steps = nseg * blocks / 3072;
+  if (steps < 2) steps = 2;
+  if (steps > 6) steps = 6;
+  if (steps > blocks) steps = blocks;
+  if (const char* force = getenv("MACAQ_ACT_ROWS_PER_WAVE")) steps = atoi(force) > 0 ? atoi(force) : steps;  // tuning knob
+  a.steps = (int)steps;
+  a.grid = dim3((unsigned)ceil_div(nseg * ceil_div(blocks, steps), 4));
+  return a;
+}
+
 hipError_t launch_act_quant(const void* x, bool x_f32, bool reciprocal, const float* s,
                             const int32_t* offsets, int E, int64_t rows_per_expert, int64_t M,
                             int64_t K, uint8_t* codes, uint8_t* scales, hipStream_t stream) {
   if (M <= 0) return hipSuccess;
-  // rows per wave: 2 to 4 (measured best on MI355X for 4K..30K row segments)
-  const int64_t nseg = ceil_div(K / 32, 64);
-  const int64_t segs = M * nseg;
-  int64_t rpw = (segs + 4096) / 8192;
-  if (rpw < 2) rpw = 2;
-  if (rpw > 4) rpw = 4;
-  if (rpw > M) rpw = M;
-  if (const char* force = getenv("MACAQ_ACT_ROWS_PER_WAVE")) rpw = atoi(force) > 0 ? atoi(force) : rpw;  // tuning knob
-  const int64_t waves = nseg * ceil_div(M, rpw);
-  const dim3 grid((unsigned)ceil_div(waves, 4)), block(256);
+  const ActLaunch a = act_launch(M, K);
+  const dim3 block(256);
   if (x_f32) {
     const size_t lds = 4 * GroupIo<4>::kWaveLds;
     if (reciprocal)
-      act_quant_lane_kernel<4, true><<<grid, block, lds, stream>>>(x, s, offsets, E, rows_per_expert, M, K, codes, scales, (int)rpw);
+      act_quant_lane_kernel<4, true><<<a.grid, block, lds, stream>>>(x, s, offsets, E, rows_per_expert, M, K, codes,
+                                                                       scales, a.gs_log2, a.steps);
     else
-      act_quant_lane_kernel<4, false><<<grid, block, lds, stream>>>(x, s, offsets, E, rows_per_expert, M, K, codes, scales, (int)rpw);
+      act_quant_lane_kernel<4, false><<<a.grid, block, lds, stream>>>(x, s, offsets, E, rows_per_expert, M, K, codes,
+                                                                        scales, a.gs_log2, a.steps);
   } else {
     const size_t lds = 4 * GroupIo<2>::kWaveLds;
     if (reciprocal)
-      act_quant_lane_kernel<2, true><<<grid, block, lds, stream>>>(x, s, offsets, E, rows_per_expert, M, K, codes, scales, (int)rpw);
+      act_quant_lane_kernel<2, true><<<a.grid, block, lds, stream>>>(x, s, offsets, E, rows_per_expert, M, K, codes,
+                                                                       scales, a.gs_log2, a.steps);
     else
-      act_quant_lane_kernel<2, false><<<grid, block, lds, stream>>>(x, s, offsets, E, rows_per_expert, M, K, codes, scales, (int)rpw);
+      act_quant_lane_kernel<2, false><<<a.grid, block, lds, stream>>>(x, s, offsets, E, rows_per_expert, M, K, codes,
+                                                                        scales, a.gs_log2, a.steps);
   }
   return hipGetLastError();
 }
@@ -276,20 +324,13 @@ hipError_t launch_act_quant(const void* x, bool x_f32, bool reciprocal, const fl
 hipError_t launch_quant_plain(const void* x, bool x_f32, int64_t M, int64_t K, uint8_t* codes, uint8_t* scales,
                               hipStream_t stream) {
   if (M <= 0) return hipSuccess;
-  const int64_t nseg = ceil_div(K / 32, 64);
-  const int64_t segs = M * nseg;
-  int64_t rpw = (segs + 4096) / 8192;
-  if (rpw < 2) rpw = 2;
-  if (rpw > 4) rpw = 4;
-  if (rpw > M) rpw = M;
-  const int64_t waves = nseg * ceil_div(M, rpw);
-  const dim3 grid((unsigned)ceil_div(waves, 4)), block(256);
+  const ActLaunch a = act_launch(M, K);
   if (x_f32)
-    act_quant_lane_kernel<4, false, true><<<grid, block, 4 * GroupIo<4>::kWaveLds, stream>>>(
-        x, nullptr, nullptr, 1, 0, M, K, codes, scales, (int)rpw);
+    act_quant_lane_kernel<4, false, true><<<a.grid, dim3(256), 4 * GroupIo<4>::kWaveLds, stream>>>(
+        x, nullptr, nullptr, 1, 0, M, K, codes, scales, a.gs_log2, a.steps);
   else
-    act_quant_lane_kernel<2, false, true><<<grid, block, 4 * GroupIo<2>::kWaveLds, stream>>>(
-        x, nullptr, nullptr, 1, 0, M, K, codes, scales, (int)rpw);
+    act_quant_lane_kernel<2, false, true><<<a.grid, dim3(256), 4 * GroupIo<2>::kWaveLds, stream>>>(
+        x, nullptr, nullptr, 1, 0, M, K, codes, scales, a.gs_log2, a.steps);
   return hipGetLastError();
 }
 
