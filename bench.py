@@ -75,21 +75,24 @@ def copy_calibration():
     print(json.dumps({"copy_calibration": {"bytes_read_per_copy": n, "bytes_written_per_copy": n, "copies": 5}}))
 
 
-def sha(path):
-    with open(path, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()
+def sources_sha256(paths):
+    h = hashlib.sha256()
+    for rel in paths:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
 
 
 def traffic_record(kernel_key):
-    """HBM bytes per launch from the committed counter summary, or None when
-    the kernel source changed since the counters were taken."""
+    """HBM bytes per launch (counter-measured, copy-calibrated) from the
+    committed summary profiles/hbm_traffic.json, or None when a source the
+    kernel is built from changed since the counters were taken."""
     path = os.path.join(ROOT, "profiles", "hbm_traffic.json")
     try:
         rec = json.load(open(path))[kernel_key]
+        if sources_sha256(rec["sources"]) != rec["sources_sha256"]:
+            return None
     except (OSError, KeyError, ValueError):
-        return None
-    src = os.path.join(ROOT, rec["source"])
-    if not os.path.exists(src) or sha(src) != rec["source_sha256"]:
         return None
     return rec["bytes_per_launch"]
 
@@ -314,7 +317,8 @@ def main():
     }
     if act_us is not None:
         out["act_transform"] = {"GBps": round(act_alg / act_us / 1e3, 1), "us": round(act_us, 2),
-                                "bytes": act_alg, "frac_of_hbm_peak": round(act_alg / act_us / 1e3 / PEAK_HBM_GBPS, 4)}
+                                "bytes": act_alg, "frac_of_hbm_peak": round(act_alg / act_us / 1e3 / PEAK_HBM_GBPS, 4),
+                                "traffic": traffic_record(f"{args.workload}:act")}
     gemm_name = "fused transform+GEMM" if fused else "MXFP4 GEMM"
     if fused or M <= 32:
         # the kernel's algorithmic HBM bytes: W' codes+scales, its activation
