@@ -86,6 +86,7 @@ SMALL_ACT = [
     ("cfg5 token routing", dict(cfg=5, shape=(300, 32, 256), routing="token_zipf")),
     ("cfg5 expert routing", dict(cfg=5, shape=(333, 32, 256))),
     ("literal scale rule", dict(cfg=2, shape=(9, 64, 512), scale_rule="literal")),
+    ("cfg5 K3072 two rows per wave step", dict(cfg=5, shape=(500, 32, 3072))),
 ]
 
 
@@ -96,6 +97,19 @@ def test_quant_act_bit_exact(name, kw):
     off = wl.offsets.to(DEV) if wl.E > 1 else None
     codes, scales = mx.quant_act(wl.x.to(DEV), wl.s.to(DEV), off)
     rc, rs = oracle.quant_act(host(wl.x), wl.s.numpy(), wl.offsets.numpy() if wl.E > 1 else None)
+    assert np.array_equal(scales.cpu().numpy(), rs)
+    assert np.array_equal(codes.cpu().numpy(), rc)
+
+
+@pytest.mark.parametrize("steps", [1, 5])
+def test_quant_act_rows_per_wave(steps, monkeypatch):
+    """Waves of 1 and of 5 row steps (segments of 16 groups over 4 rows), with
+    expert boundaries inside a step and inside a wave."""
+    say(f"quant_act steps={steps}")
+    monkeypatch.setenv("MACAQ_ACT_ROWS_PER_WAVE", str(steps))
+    wl = workloads.make(cfg=5, shape=(333, 32, 256))
+    codes, scales = mx.quant_act(wl.x.to(DEV), wl.s.to(DEV), wl.offsets.to(DEV))
+    rc, rs = oracle.quant_act(host(wl.x), wl.s.numpy(), wl.offsets.numpy())
     assert np.array_equal(scales.cpu().numpy(), rs)
     assert np.array_equal(codes.cpu().numpy(), rc)
 
