@@ -128,27 +128,28 @@ __host__ __device__ constexpr int64_t dec_xrow_groups(int64_t K) { return K / 32
 // LDS.
 constexpr int kSlabs = 3;
 
-template <int AK, int EB = 2>
+template <int AK, int EB = 2, int RT = 1>
 struct DecStage {
-  static constexpr int kW = 0;
-  static constexpr int kA = 4096;                  // streamed: s chunk; else activation codes
+  static constexpr int kW = 0;                     // RT x 4 KiB of W' codes (RT 32-row tiles)
+  static constexpr int kA = 4096 * RT;             // streamed: s chunk; else activation codes
   static constexpr int kX = kA + 1024;             // streamed: x chunk of rows 0..1
   static constexpr int kABytes = AK < 0 ? 1024 + 512 * EB : (AK == 0 ? 0 : (AK == 1 ? 256 : AK * 128));
   static constexpr int kAs = kA + kABytes;
   static constexpr int kBytes = kAs + (AK > 0 ? 256 : 0);
   static constexpr int kACopies = AK < 0 ? 1 + EB / 2 : (AK == 0 ? 0 : (AK == 1 ? 2 : AK / 8 + 1));
-  static constexpr int kCopies = 5 + kACopies;   // copy instructions per chunk (4 codes + 1 slab + activation)
+  // copy instructions per chunk: 4 RT codes, RT slab copies, the activation's
+  static constexpr int kCopies = 5 * RT + kACopies;
 };
 
 // Per wave: STAGES ring slots, the scale slabs, and (streamed) the wave's
 // quantized activation chunk: codes of rows 0..1 (2 x 128 B) and their 2 x 8
 // scale bytes.
-template <int STAGES, int AK, int EB = 2>
+template <int STAGES, int AK, int EB = 2, int RT = 1>
 struct DecWaveLds {
   static constexpr int kSeg = AK == 32 ? 4 : 8;          // chunks per scale segment
   static constexpr int kRowDwords = 2 * kSeg;            // slab row: 8 kSeg bytes
-  static constexpr int kSlabBytes = 32 * 8 * kSeg;
-  static constexpr int kSlab0 = STAGES * DecStage<AK, EB>::kBytes;
+  static constexpr int kSlabBytes = 32 * RT * 8 * kSeg;
+  static constexpr int kSlab0 = STAGES * DecStage<AK, EB, RT>::kBytes;
   static constexpr int kXq = kSlab0 + kSlabs * kSlabBytes;
   static constexpr int kXqBytes = AK < 0 ? 288 : 0;
   static constexpr int kBytes = kXq + kXqBytes;
@@ -156,20 +157,22 @@ struct DecWaveLds {
 
 __device__ __forceinline__ int dec_slot(int row, int piece) { return (row >> 3) * 1024 + (row & 7) * 128 + 16 * (piece ^ (row & 7)); }
 
-template <int WAVES, int STAGES, int AK, typename XT>
+// A block owns RT x 32 weight rows (RT MFMA row tiles sharing each
+// activation chunk).
+template <int WAVES, int STAGES, int AK, typename XT, int RT = 1>
 __global__ __launch_bounds__(64 * WAVES) void decode_gemm_kernel(
     const uint8_t* __restrict__ A, const uint8_t* __restrict__ As,     // activation codes/scales (unfused)
     const void* __restrict__ x, const float* __restrict__ s,           // activations and scale (fused)
     const uint8_t* __restrict__ W, const uint8_t* __restrict__ Ws, int64_t M, int64_t N, int64_t K,
     float* __restrict__ Y) {
   constexpr int EB = dec_eb<XT>;
-  using S = DecStage<AK, EB>;
+  using S = DecStage<AK, EB, RT>;
   constexpr bool FUSED = AK == 0;     // resident activation, transformed before the loop
   constexpr bool STREAM = AK < 0;     // activation transformed chunk by chunk in the loop
   constexpr int AI = AK >= 8 ? AK / 8 : 1;
   extern __shared__ __attribute__((aligned(16))) uint8_t dsm[];
   constexpr int kThreads = 64 * WAVES;
-  const int64_t n0 = (int64_t)blockIdx.x * kDecRows;
+  const int64_t n0 = (int64_t)blockIdx.x * kDecRows * RT;
   const int64_t KB = K >> 1, KG = K >> 5;
   const int kc = (int)(K >> 8);
   const int tid = threadIdx.x;
@@ -178,10 +181,10 @@ __global__ __launch_bounds__(64 * WAVES) void decode_gemm_kernel(
   const int r32 = lane & 31;
   const int h = lane >> 5;
 
-  using WL = DecWaveLds<STAGES, AK, EB>;
+  using WL = DecWaveLds<STAGES, AK, EB, RT>;
   // LDS: per wave STAGES ring slots and kSlabs scale slabs (all reused for
-  // the [WAVES][32][32] fp32 partial sums after the loop), then (fused) the
-  // activation codes [M][K/2 + 16] and scales [M][K/32 + 8].
+  // the [WAVES][32 RT][32] fp32 partial sums after the loop), then (fused)
+  // the activation codes [M][K/2 + 16] and scales [M][K/32 + 8].
   uint8_t* ring = dsm + wave * WL::kBytes;
   const uint32_t ring_addr = (uint32_t)(uintptr_t)ring;
   const uint8_t* slabs = ring + WL::kSlab0;
@@ -196,9 +199,9 @@ __global__ __launch_bounds__(64 * WAVES) void decode_gemm_kernel(
   const int per_wave = (kc + WAVES - 1) / WAVES;
   const int c0 = wave * per_wave;
   const int c1 = (c0 + per_wave) < kc ? (c0 + per_wave) : kc;
-  const uint8_t* wsrc[4];
+  const uint8_t* wsrc[4 * RT];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
+  for (int i = 0; i < 4 * RT; ++i) {
     const int row = 8 * i + (lane >> 3);
     const int64_t wn = n0 + row < N ? n0 + row : N - 1;
     wsrc[i] = W + wn * KB + 16 * ((lane & 7) ^ (row & 7));
@@ -237,7 +240,7 @@ __global__ __launch_bounds__(64 * WAVES) void decode_gemm_kernel(
       xsrc[i] = reinterpret_cast<const uint8_t*>(x) + row * K * EB + p % (256 * EB);
     }
   }
-  // copy t of the W' scale slab of segment seg (relative to c0)
+  // copy t (of RT kSeg) of the W' scale slab of segment seg (relative to c0)
   auto issue_slab = [&](int seg, int t) {
     const int row = t * (64 / kD) + slab_lrow;
     const int64_t wn = n0 + row < N ? n0 + row : N - 1;
@@ -245,13 +248,14 @@ __global__ __launch_bounds__(64 * WAVES) void decode_gemm_kernel(
     if (ofs > KG - 4) ofs = KG - 4;
     dma4(Ws + wn * KG + ofs, ring_addr + (uint32_t)(WL::kSlab0 + (seg % kSlabs) * WL::kSlabBytes + t * 256));
   };
-  // chunk c's copies, plus one slab copy for the segment after c's
+  // chunk c's copies, plus RT slab copies for the segment after c's
   auto issue = [&](int c) {
     const uint32_t base = ring_addr + (uint32_t)(((c - c0) % STAGES) * S::kBytes);
     const int64_t co = (int64_t)c * 128, so = (int64_t)c * 8;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) dma16(wsrc[i] + co, base + S::kW + i * 1024);
-    issue_slab((c - c0) / kSeg + 1, (c - c0) % kSeg);
+    for (int i = 0; i < 4 * RT; ++i) dma16(wsrc[i] + co, base + S::kW + i * 1024);
+#pragma unroll
+    for (int i = 0; i < RT; ++i) issue_slab((c - c0) / kSeg + 1, ((c - c0) % kSeg) * RT + i);
     if constexpr (AK == 1) {
       dma4(asrc[0] + co, base + S::kA);
     } else if constexpr (AK >= 8) {
@@ -269,7 +273,7 @@ __global__ __launch_bounds__(64 * WAVES) void decode_gemm_kernel(
   // then overlaps the copies)
   if (c0 < c1) {
 #pragma unroll
-    for (int t = 0; t < kSeg; ++t) issue_slab(0, t);
+    for (int t = 0; t < kSeg * RT; ++t) issue_slab(0, t);
   }
 #pragma unroll
   for (int q = 0; q < STAGES - 1; ++q)
@@ -322,9 +326,11 @@ __global__ __launch_bounds__(64 * WAVES) void decode_gemm_kernel(
   const uint8_t* xrow = xcodes + ar * xrb;
   const uint8_t* xsrow = xscales + ar * xrg;
 
-  v16f_d acc;
+  v16f_d acc[RT];
 #pragma unroll
-  for (int r = 0; r < 16; ++r) acc[r] = 0.0f;
+  for (int tt = 0; tt < RT; ++tt)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[tt][r] = 0.0f;
 
   for (int c = c0; c < c1; ++c) {
     // the slot about to be refilled was read (into registers) one chunk ago;
@@ -339,12 +345,18 @@ __global__ __launch_bounds__(64 * WAVES) void decode_gemm_kernel(
     else if (ahead == 1) wait_vmcnt<S::kCopies>();
     else wait_vmcnt<0>();
     const uint8_t* st = ring + ((c - c0) % STAGES) * S::kBytes;
-    uint4 wa[4], xb[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) wa[j] = *reinterpret_cast<const uint4*>(st + S::kW + dec_slot(r32, 2 * j + h));
+    uint4 wa[RT][4], xb[4];
+    uint32_t ws[RT];
     const int cs = c - c0;
-    const uint2 wsv = *reinterpret_cast<const uint2*>(
-        slabs + ((cs / kSeg) % kSlabs) * WL::kSlabBytes + r32 * (8 * kSeg) + (cs % kSeg) * 8);
+#pragma unroll
+    for (int tt = 0; tt < RT; ++tt) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        wa[tt][j] = *reinterpret_cast<const uint4*>(st + S::kW + dec_slot(32 * tt + r32, 2 * j + h));
+      const uint2 wsv = *reinterpret_cast<const uint2*>(slabs + ((cs / kSeg) % kSlabs) * WL::kSlabBytes +
+                                                        (32 * tt + r32) * (8 * kSeg) + (cs % kSeg) * 8);
+      ws[tt] = gather_scales(wsv.x, wsv.y, h);
+    }
     uint2 xsv;
     if constexpr (AK == 1) {
 #pragma unroll
@@ -382,30 +394,36 @@ __global__ __launch_bounds__(64 * WAVES) void decode_gemm_kernel(
       for (int j = 0; j < 4; ++j) xb[j] = *reinterpret_cast<const uint4*>(xrow + (int64_t)c * 128 + 16 * (2 * j + h));
       xsv = *reinterpret_cast<const uint2*>(xsrow + (int64_t)c * 8);
     }
-    const uint32_t ws = gather_scales(wsv.x, wsv.y, h);
     const uint32_t xs = gather_scales(xsv.x, xsv.y, h);
-    dec_mfma<0>(acc, wa, xb, ws, xs);
-    dec_mfma<1>(acc, wa, xb, ws, xs);
-    dec_mfma<2>(acc, wa, xb, ws, xs);
-    dec_mfma<3>(acc, wa, xb, ws, xs);
+#pragma unroll
+    for (int tt = 0; tt < RT; ++tt) {
+      dec_mfma<0>(acc[tt], wa[tt], xb, ws[tt], xs);
+      dec_mfma<1>(acc[tt], wa[tt], xb, ws[tt], xs);
+      dec_mfma<2>(acc[tt], wa[tt], xb, ws[tt], xs);
+      dec_mfma<3>(acc[tt], wa[tt], xb, ws[tt], xs);
+    }
   }
 
   // ---- add the waves' 32x32 tiles in wave order.  Lane (r32, h), register r
   // holds D[n = 8*(r/4) + 4*h + r%4][m = r32].  Every wave's copies have
   // landed (its last chunk waited for all of them), so after the barrier the
   // rings and slabs can hold the partial sums.
+  constexpr int kRows = 32 * RT;
   __syncthreads();
 #pragma unroll
-  for (int r = 0; r < 16; ++r) {
-    const int n = 8 * (r >> 2) + 4 * h + (r & 3);
-    red[(wave * 32 + n) * 32 + r32] = acc[r];
+  for (int tt = 0; tt < RT; ++tt) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int n = 32 * tt + 8 * (r >> 2) + 4 * h + (r & 3);
+      red[(wave * kRows + n) * 32 + r32] = acc[tt][r];
+    }
   }
   __syncthreads();
-  for (int idx = tid; idx < 32 * 32; idx += kThreads) {
-    const int n = idx & 31, m = idx >> 5;   // consecutive threads: consecutive n of one row of y
+  for (int idx = tid; idx < kRows * 32; idx += kThreads) {
+    const int n = idx % kRows, m = idx / kRows;   // consecutive threads: consecutive n of one row of y
     float v = red[n * 32 + m];
 #pragma unroll
-    for (int w = 1; w < WAVES; ++w) v = v + red[(w * 32 + n) * 32 + m];
+    for (int w = 1; w < WAVES; ++w) v = v + red[(w * kRows + n) * 32 + m];
     if (m < M && n0 + n < N) Y[(int64_t)m * N + n0 + n] = v;
   }
 }
@@ -419,50 +437,62 @@ static int decode_ak(int64_t M, bool fused) {
   return M <= 2 ? 1 : (M <= 8 ? 8 : (M <= 16 ? 16 : 32));
 }
 
-static int stage_bytes(int ak, int eb) {
+template <int RT>
+static int stage_bytes_rt(int ak, int eb) {
   switch (ak) {
-    case -1: return eb == 4 ? DecStage<-1, 4>::kBytes : DecStage<-1, 2>::kBytes;
-    case 0: return DecStage<0>::kBytes;
-    case 1: return DecStage<1>::kBytes;
-    case 8: return DecStage<8>::kBytes;
-    case 16: return DecStage<16>::kBytes;
-    default: return DecStage<32>::kBytes;
+    case -1: return eb == 4 ? DecStage<-1, 4, RT>::kBytes : DecStage<-1, 2, RT>::kBytes;
+    case 0: return DecStage<0, 2, RT>::kBytes;
+    case 1: return DecStage<1, 2, RT>::kBytes;
+    case 8: return DecStage<8, 2, RT>::kBytes;
+    case 16: return DecStage<16, 2, RT>::kBytes;
+    default: return DecStage<32, 2, RT>::kBytes;
   }
 }
 
-static size_t wave_lds_bytes(int stages, int ak, int eb) {
-  return (size_t)stages * stage_bytes(ak, eb) + kSlabs * 32 * 8 * (ak == 32 ? 4 : 8) + (ak < 0 ? 288 : 0);
+static size_t wave_lds_bytes(int stages, int ak, int eb, int rt) {
+  const int stage = rt == 2 ? stage_bytes_rt<2>(ak, eb) : stage_bytes_rt<1>(ak, eb);
+  return (size_t)stages * stage + kSlabs * 32 * rt * 8 * (ak == 32 ? 4 : 8) + (ak < 0 ? 288 : 0);
 }
 
 struct DecodeConfig {
-  int waves, stages, ak, eb;
+  int waves, stages, ak, eb, rt;
 };
 
 static size_t decode_lds_bytes(const DecodeConfig& d, int64_t M, int64_t K) {
-  size_t b = (size_t)d.waves * wave_lds_bytes(d.stages, d.ak, d.eb);
+  size_t b = (size_t)d.waves * wave_lds_bytes(d.stages, d.ak, d.eb, d.rt);
   if (d.ak == 0) b += (size_t)M * (size_t)(dec_xrow_bytes(K) + dec_xrow_groups(K));
   return b;
 }
 
-// Waves split K; each keeps STAGES - 1 chunks in flight.  The ring is made as
+// Block height: 64 weight rows (two MFMA row tiles sharing each activation
+// chunk, which halves the activation's L2-to-LDS traffic) for more than 8
+// staged activation rows when 32-row blocks would number more than two per
+// CU; then 2 waves per block, so that two blocks stay resident per CU.
+// Otherwise 32 rows and 4 or 8 waves (for small activations the extra waves
+// keep more of W' in flight, which matters more).  Each wave keeps STAGES - 1 chunks in flight; the ring is made as
 // deep as LDS allows (2 to 4 slots), within half of the CU's LDS when the
-// grid has more blocks than CUs (two resident blocks per CU), within all of
-// it otherwise; 8 waves drop to 4 where even 2 slots do not fit.
+// grid has more blocks than CUs, within all of it otherwise; 8 waves drop to
+// 4 where even 2 slots do not fit.
 static DecodeConfig decode_config(int64_t M, int64_t N, int64_t K, bool fused, int eb) {
   DecodeConfig d;
   d.ak = decode_ak(M, fused);
   d.eb = eb;
-  d.waves = K / 256 >= 24 ? 8 : 4;
-  const size_t budget = ceil_div(N, kDecRows) > 256 ? kDecLdsMax / 2 : kDecLdsMax;
-  d.stages = 4;
+  d.rt = (d.ak > 8 && ceil_div(N, kDecRows) > 512) ? 2 : 1;
+  if (const char* e = getenv("MACAQ_DECODE_ROWS")) d.rt = atoi(e) == 64 ? 2 : 1;   // tuning knob
+  const int max_stages = d.rt == 2 ? 3 : 4;
+  d.waves = d.rt == 2 ? 2 : (K / 256 >= 24 ? 8 : 4);
+  const size_t budget = ceil_div(N, kDecRows * d.rt) > 256 ? kDecLdsMax / 2 : kDecLdsMax;
+  d.stages = max_stages;
   while (d.stages > 2 && decode_lds_bytes(d, M, K) > budget) --d.stages;
   if (decode_lds_bytes(d, M, K) > kDecLdsMax && d.waves > 4) {
     d.waves = 4;
-    d.stages = 4;
+    d.stages = max_stages;
     while (d.stages > 2 && decode_lds_bytes(d, M, K) > budget) --d.stages;
   }
-  if (const char* e = getenv("MACAQ_DECODE_WAVES")) d.waves = atoi(e) == 8 ? 8 : 4;      // tuning knobs
-  if (const char* e = getenv("MACAQ_DECODE_STAGES")) d.stages = atoi(e) >= 4 ? 4 : (atoi(e) == 3 ? 3 : 2);
+  if (d.rt == 1) {   // tuning knobs
+    if (const char* e = getenv("MACAQ_DECODE_WAVES")) d.waves = atoi(e) == 8 ? 8 : 4;
+    if (const char* e = getenv("MACAQ_DECODE_STAGES")) d.stages = atoi(e) >= 4 ? 4 : (atoi(e) == 3 ? 3 : 2);
+  }
   return d;
 }
 
@@ -470,16 +500,17 @@ bool decode_supported(int64_t M, int64_t N, int64_t K, int64_t E) {
   return E == 1 && M >= 1 && M <= kDecMaxM && N >= 1 && K % 256 == 0;
 }
 
-template <int WAVES, int STAGES, int AK, typename XT>
+template <int WAVES, int STAGES, int AK, typename XT, int RT>
 static hipError_t launch_decode_w(const uint8_t* A, const uint8_t* As, const void* x, const float* s,
                                   const uint8_t* W, const uint8_t* Ws, int64_t M, int64_t N, int64_t K, float* Y,
                                   size_t lds, hipStream_t stream) {
-  static_assert(DecWaveLds<STAGES, AK, dec_eb<XT>>::kBytes >= 32 * 32 * 4, "partial sums must fit in the rings");
-  static const hipError_t attr = hipFuncSetAttribute((const void*)decode_gemm_kernel<WAVES, STAGES, AK, XT>,
+  static_assert(DecWaveLds<STAGES, AK, dec_eb<XT>, RT>::kBytes >= 32 * RT * 32 * 4,
+                "partial sums must fit in the rings");
+  static const hipError_t attr = hipFuncSetAttribute((const void*)decode_gemm_kernel<WAVES, STAGES, AK, XT, RT>,
                                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)kDecLdsMax);
   if (attr != hipSuccess) return attr;
-  decode_gemm_kernel<WAVES, STAGES, AK, XT><<<dim3((unsigned)ceil_div(N, kDecRows)), dim3(64 * WAVES), lds, stream>>>(
-      A, As, x, s, W, Ws, M, N, K, Y);
+  decode_gemm_kernel<WAVES, STAGES, AK, XT, RT>
+      <<<dim3((unsigned)ceil_div(N, kDecRows * RT)), dim3(64 * WAVES), lds, stream>>>(A, As, x, s, W, Ws, M, N, K, Y);
   return hipGetLastError();
 }
 
@@ -489,14 +520,18 @@ static hipError_t launch_decode_impl(const DecodeConfig& d, const uint8_t* A, co
                                      int64_t K, float* Y, hipStream_t stream) {
   const size_t lds = decode_lds_bytes(d, M, K);
   if (lds > kDecLdsMax) return hipErrorInvalidValue;
-  if (d.waves == 8) {
-    if (d.stages == 4) return launch_decode_w<8, 4, AK, XT>(A, As, x, s, W, Ws, M, N, K, Y, lds, stream);
-    if (d.stages == 3) return launch_decode_w<8, 3, AK, XT>(A, As, x, s, W, Ws, M, N, K, Y, lds, stream);
-    return launch_decode_w<8, 2, AK, XT>(A, As, x, s, W, Ws, M, N, K, Y, lds, stream);
+  if (d.rt == 2) {
+    if (d.stages >= 3) return launch_decode_w<2, 3, AK, XT, 2>(A, As, x, s, W, Ws, M, N, K, Y, lds, stream);
+    return launch_decode_w<2, 2, AK, XT, 2>(A, As, x, s, W, Ws, M, N, K, Y, lds, stream);
   }
-  if (d.stages == 4) return launch_decode_w<4, 4, AK, XT>(A, As, x, s, W, Ws, M, N, K, Y, lds, stream);
-  if (d.stages == 3) return launch_decode_w<4, 3, AK, XT>(A, As, x, s, W, Ws, M, N, K, Y, lds, stream);
-  return launch_decode_w<4, 2, AK, XT>(A, As, x, s, W, Ws, M, N, K, Y, lds, stream);
+  if (d.waves == 8) {
+    if (d.stages == 4) return launch_decode_w<8, 4, AK, XT, 1>(A, As, x, s, W, Ws, M, N, K, Y, lds, stream);
+    if (d.stages == 3) return launch_decode_w<8, 3, AK, XT, 1>(A, As, x, s, W, Ws, M, N, K, Y, lds, stream);
+    return launch_decode_w<8, 2, AK, XT, 1>(A, As, x, s, W, Ws, M, N, K, Y, lds, stream);
+  }
+  if (d.stages == 4) return launch_decode_w<4, 4, AK, XT, 1>(A, As, x, s, W, Ws, M, N, K, Y, lds, stream);
+  if (d.stages == 3) return launch_decode_w<4, 3, AK, XT, 1>(A, As, x, s, W, Ws, M, N, K, Y, lds, stream);
+  return launch_decode_w<4, 2, AK, XT, 1>(A, As, x, s, W, Ws, M, N, K, Y, lds, stream);
 }
 
 hipError_t launch_decode_gemm(const uint8_t* A, const uint8_t* As, const uint8_t* W, const uint8_t* Ws, int64_t M,

@@ -359,6 +359,45 @@ def test_linear_decode_paths(name, kw, flags):
     assert torch.equal(y, y_again)
 
 
+ROWS64_GEMM = [(1, 1000, 2560), (3, 200, 2048), (12, 70, 256 * 7), (32, 1000, 2560)]
+ROWS64_LINEAR = [
+    ("M1 fp32 tiny-shaped", dict(cfg=1, shape=(1, 96, 512))),
+    ("M1", dict(cfg=4, shape=(1, 1000, 2560))),
+    ("M2", dict(cfg=4, shape=(2, 300, 256 * 9))),
+    ("M8", dict(cfg=4, shape=(8, 200, 1024))),
+]
+
+
+@pytest.mark.parametrize("shape", ROWS64_GEMM, ids=[f"M{m} N{n} K{k}" for m, n, k in ROWS64_GEMM])
+def test_gemm_decode_64_row_blocks(shape, monkeypatch):
+    """Blocks of 64 weight rows (two MFMA row tiles per activation chunk),
+    ragged N included."""
+    say(f"gemm decode 64-row blocks {shape}")
+    monkeypatch.setenv("MACAQ_DECODE_ROWS", "64")
+    M, N, K = shape
+    rng = np.random.default_rng(M * 17 + N)
+    ac = rng.integers(0, 256, (M, K // 2), dtype=np.uint8)
+    asc = rng.integers(110, 140, (M, K // 32), dtype=np.uint8)
+    wc = rng.integers(0, 256, (N, K // 2), dtype=np.uint8)
+    wsc = rng.integers(110, 140, (N, K // 32), dtype=np.uint8)
+    y = mx.gemm(*[torch.from_numpy(a).to(DEV) for a in (ac, asc, wc, wsc)])
+    y_ref, S = oracle.gemm(ac, asc, wc, wsc)
+    _check_y(y.cpu().numpy(), y_ref, S)
+
+
+@pytest.mark.parametrize("flags", [mx.PATH_FUSED, mx.PATH_UNFUSED])
+@pytest.mark.parametrize("name,kw", ROWS64_LINEAR, ids=[n for n, _ in ROWS64_LINEAR])
+def test_linear_decode_64_row_blocks(name, kw, flags, monkeypatch):
+    say(f"linear decode 64-row blocks {name} flags={flags}")
+    monkeypatch.setenv("MACAQ_DECODE_ROWS", "64")
+    wl = workloads.make(**kw)
+    wc, wsc = gpu_prepare(wl)
+    y = mx.linear(wl.x.to(DEV), wl.s.to(DEV), wc, wsc, flags=flags)
+    rwc, rws = oracle_prepare(wl, 0)
+    y_ref, S = oracle.linear(host(wl.x), wl.s.numpy(), rwc, rws)
+    _check_y(y.cpu().numpy(), y_ref, S)
+
+
 # ------------------------------------------------------------ pure MXFP4 (no transform)
 
 @pytest.mark.parametrize("name,kw", SMALL_ACT[:4], ids=[n for n, _ in SMALL_ACT[:4]])
