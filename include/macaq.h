@@ -173,9 +173,12 @@ int macaq_linear_path(int64_t M, int64_t N, int64_t K, int64_t E, uint32_t flags
  *   macaq_prepare_weights, y [M][N] fp32 out.
  * flags: MACAQ_PATH_AUTO / _FUSED / _UNFUSED.  Both paths produce the same
  * activation codes; y may differ between paths only by fp32 summation order.
- * The fused path serves E == 1, M <= 32, K % 256 == 0 and the M*K*17/32
- * bytes of quantized activations fitting in LDS beside the kernel's
- * reduction buffer (about 96 to 144 KiB depending on K); AUTO takes it for
+ * The fused path serves E == 1, M <= 32 and K % 256 == 0.  For M <= 2 the
+ * kernel transforms each 256-wide chunk of the activation as the weights
+ * stream past (any such K); for larger M it first transforms the whole
+ * activation into LDS, so it serves only when M * (K/2 + K/32 + 24) bytes fit
+ * beside the weight staging in the 160 KiB of LDS (otherwise a forced
+ * MACAQ_PATH_FUSED returns MACAQ_ERR_UNSUPPORTED).  AUTO takes it for
  * M <= 2, where one launch beats two.
  * Requires the argument rules of macaq_quant_act and macaq_gemm and a
  * workspace of macaq_linear_workspace_bytes(M, N, K, E, flags) bytes.
@@ -202,7 +205,8 @@ int macaq_quant_mxfp4(const void* x, macaq_dtype x_dtype, int64_t M, int64_t K, 
 /*
  * Element encoder alone, for exhaustive tests of the E2M1 rounding: codes[i]
  * = the 4-bit E2M1 code (sign<<3 | magnitude index) of v[i] with scale byte
- * 127 (no scaling), by the same device routine the quantizing kernels use.
+ * 127 (no scaling), by the same hardware conversion
+ * (v_cvt_scalef32_pk_fp4_f32, scale 1.0) the quantizing kernels use.
  *   v [n] fp32 device in, codes [n] uint8 device out (one code per byte).
  */
 int macaq_encode_e2m1(const float* v, int64_t n, uint8_t* codes, void* stream);

@@ -228,7 +228,9 @@ int macaq_linear(const void* x, macaq_dtype x_dtype, const float* s, const int32
   if (int st = validate_gemm(dummy, w_scales, expert_offsets, E, w_codes, w_scales, M, N, K, y, fn)) return st;
   if (M == 0) return MACAQ_OK;
   if (flags == MACAQ_PATH_FUSED && !macaq::linear_fused_supported(M, N, K, E))
-    return fail(MACAQ_ERR_UNSUPPORTED, std::string(fn) + ": the fused path serves E == 1 and M <= 32");
+    return fail(MACAQ_ERR_UNSUPPORTED, std::string(fn) +
+                                           ": the fused path serves E == 1, M <= 32, K % 256 == 0 and, for M > 2, "
+                                           "the quantized activation fitting in LDS");
   const bool fused = macaq_linear_path(M, N, K, E, flags) == MACAQ_PATH_FUSED;
   const size_t need = macaq_linear_workspace_bytes(M, N, K, E, flags);
   if (int st = check_workspace(workspace, workspace_bytes, need, fn)) return st;
