@@ -111,3 +111,36 @@ def test_valid_calls_without_a_device_report_no_device():
     assert qa() == NO_DEVICE
     assert gm() == NO_DEVICE
     assert b"no HIP device" in mx.lib().macaq_last_error()
+
+
+def test_linear_path_choice_and_workspace():
+    """AUTO takes the one-launch fused path for M <= 2 on a dense layer with
+    K % 256 == 0, the two-launch path otherwise; only the latter needs a
+    workspace (the activation codes and scales)."""
+    L = mx.lib()
+    P = L.macaq_linear_path
+    assert P(1, 25600, 5120, 1, mx.PATH_AUTO) == mx.PATH_FUSED
+    assert P(2, 5120, 25600, 1, mx.PATH_AUTO) == mx.PATH_FUSED
+    assert P(3, 5120, 25600, 1, mx.PATH_AUTO) == mx.PATH_UNFUSED
+    assert P(1, 4096, 4096 + 128, 1, mx.PATH_AUTO) == mx.PATH_UNFUSED   # K % 256 != 0
+    assert P(1, 1024, 3072, 64, mx.PATH_AUTO) == mx.PATH_UNFUSED        # grouped
+    assert P(2048, 4096, 4096, 1, mx.PATH_AUTO) == mx.PATH_UNFUSED
+    assert P(8, 128, 256, 1, mx.PATH_FUSED) == mx.PATH_FUSED
+    assert P(8, 128, 256, 1, mx.PATH_UNFUSED) == mx.PATH_UNFUSED
+    assert P(8, 128, 256, 1, 7) == INVALID
+    assert L.macaq_linear_workspace_bytes(1, 25600, 5120, 1, mx.PATH_AUTO) == 0
+    assert L.macaq_linear_workspace_bytes(8, 25600, 5120, 1, mx.PATH_AUTO) == L.macaq_quant_act_bytes(8, 5120)
+    assert L.macaq_linear_workspace_bytes(1, 25600, 5120, 1, mx.PATH_UNFUSED) == L.macaq_quant_act_bytes(1, 5120)
+
+
+def test_forced_fused_path_refuses_what_it_cannot_serve():
+    mx.lib()
+    lin = mx.macaq_linear
+    # 32 rows of a 25600-wide activation do not fit in LDS beside the weight staging
+    assert lin(A16, 0, A16, None, 1, A16, A16, 32, 5120, 25600, A16, None, 0, mx.PATH_FUSED, None) == UNSUPPORTED
+    assert b"fused path" in mx.macaq_last_error()
+    # grouped layers and K % 256 != 0 take the two-launch path only
+    assert lin(A16, 0, A16, A16, 2, A16, A16, 1, 512, 1024, A16, None, 0, mx.PATH_FUSED, None) == UNSUPPORTED
+    assert lin(A16, 0, A16, None, 1, A16, A16, 1, 512, 384, A16, None, 0, mx.PATH_FUSED, None) == UNSUPPORTED
+    # M > 32 is not a decode shape
+    assert lin(A16, 0, A16, None, 1, A16, A16, 33, 512, 1024, A16, None, 0, mx.PATH_FUSED, None) == UNSUPPORTED
