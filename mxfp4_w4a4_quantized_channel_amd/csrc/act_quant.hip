@@ -185,9 +185,15 @@ __global__ __launch_bounds__(256) void act_quant_lane_kernel(
     for (int i = 0; i < IO::kLoads; ++i) {
       const int bpos = 1024 * i + 16 * lane;
       const int row_l = bpos >> seg_log2, o = bpos & ((1 << seg_log2) - 1);
-      ld[i] = (ra + row_l < r1 && o < seg_valid)
-                  ? *reinterpret_cast<const uint4*>(base + (int64_t)row_l * K * EB + o)
-                  : make_uint4(0, 0, 0, 0);
+      if (ra + row_l < r1 && o < seg_valid) {
+        // x is read once: non-temporal loads (measured: the GEMM that follows
+        // starts sooner, e.g. the MoE layer step 67.7 -> 62 us)
+        typedef unsigned v4u __attribute__((ext_vector_type(4)));
+        const v4u v = __builtin_nontemporal_load(reinterpret_cast<const v4u*>(base + (int64_t)row_l * K * EB + o));
+        ld[i] = make_uint4(v.x, v.y, v.z, v.w);
+      } else {
+        ld[i] = make_uint4(0, 0, 0, 0);
+      }
     }
   };
   // expert of this lane's first row
