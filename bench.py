@@ -54,6 +54,9 @@ def parse():
     p.add_argument("--warmup", type=int, default=20)
     p.add_argument("--workload", default="attn", choices=sorted(WORKLOADS))
     p.add_argument("--path", default="auto", choices=["auto", "fused", "unfused"])
+    p.add_argument("--out", default="f32", choices=["f32", "bf16"], help="dtype of y")
+    p.add_argument("--epilogue", default="none", choices=["none", "swiglu"],
+                   help="swiglu: weight rows are (gate, up) pairs and y is [M][N/2] = silu(gate) * up")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-ablation", action="store_true", help="skip the pure-MXFP4 comparison")
     p.add_argument("--cpu-rows", type=int, default=256, help="row sample of the CPU oracle baseline")
@@ -130,12 +133,13 @@ def cpu_baseline(wl, rows):
 
 
 def transform_overhead(args, mx, L, wl, xs, wss, wcs, ys, s0, off_p, stream, sp, a_codes, a_scales, gemm_ws,
-                       M, N, K, E, R):
+                       M, N, K, E, R, ydt, epi):
     """The pages quote MACaQ's cost over pure MXFP4 (same W4A4 layer without
     the scale and the block Hadamard).  Time the online layer both ways on the
     same inputs: MACaQ = transform+quant kernel, then the GEMM against W';
     pure = plain MXFP4 quantization kernel, then the same GEMM against plainly
-    quantized W.  overhead = t_macaq / t_pure - 1 (layer level)."""
+    quantized W.  overhead = t_macaq / t_pure - 1 (layer level).  Both write
+    y with the step's output dtype and epilogue (ydt, epi)."""
     import torch
     p = ctypes.c_void_p
     xdt = mx.BF16 if xs[0].dtype == torch.bfloat16 else mx.F32
@@ -148,17 +152,17 @@ def transform_overhead(args, mx, L, wl, xs, wss, wcs, ys, s0, off_p, stream, sp,
         j = i % R
         st = mx.macaq_quant_act(p(xs[j].data_ptr()), xdt, p(s0.data_ptr()), off_p, E, M, K, p(a_codes.data_ptr()),
                                 p(a_scales.data_ptr()), sp)
-        st |= mx.macaq_gemm(p(a_codes.data_ptr()), p(a_scales.data_ptr()), off_p, E, p(wcs[j].data_ptr()),
-                            p(wss[j].data_ptr()), M, N, K, p(ys[j].data_ptr()), p(gemm_ws.data_ptr()),
-                            gemm_ws.numel(), sp)
+        st |= mx.macaq_gemm_ex(p(a_codes.data_ptr()), p(a_scales.data_ptr()), off_p, E, p(wcs[j].data_ptr()),
+                               p(wss[j].data_ptr()), M, N, K, p(ys[j].data_ptr()), ydt, epi, p(gemm_ws.data_ptr()),
+                               gemm_ws.numel(), sp)
         assert st == 0, mx.lib().macaq_last_error()
 
     def pure_step(i):
         j = i % R
         st = mx.macaq_quant_mxfp4(p(xs[j].data_ptr()), xdt, M, K, p(a_codes.data_ptr()), p(a_scales.data_ptr()), sp)
-        st |= mx.macaq_gemm(p(a_codes.data_ptr()), p(a_scales.data_ptr()), off_p, E, p(pcs[j].data_ptr()),
-                            p(pss[j].data_ptr()), M, N, K, p(ys[j].data_ptr()), p(gemm_ws.data_ptr()),
-                            gemm_ws.numel(), sp)
+        st |= mx.macaq_gemm_ex(p(a_codes.data_ptr()), p(a_scales.data_ptr()), off_p, E, p(pcs[j].data_ptr()),
+                               p(pss[j].data_ptr()), M, N, K, p(ys[j].data_ptr()), ydt, epi, p(gemm_ws.data_ptr()),
+                               gemm_ws.numel(), sp)
         assert st == 0, mx.lib().macaq_last_error()
 
     def timed(fn):
@@ -211,12 +215,16 @@ def main():
     s0 = wl.s.to(dev)
     off = wl.offsets.to(dev) if E > 1 else None
     wc0, ws0 = mx.prepare_weights(wl.w.to(dev), s0)
-    set_bytes = x0.numel() * x0.element_size() + wc0.numel() + ws0.numel() + M * N * 4
+    set_bytes = x0.numel() * x0.element_size() + wc0.numel() + ws0.numel() + M * N * 4   # y at most fp32 [M][N]
     R = max(2, min(64, -(-(4 * MALL_BYTES) // set_bytes)))
     xs = [x0] + [x0.clone() for _ in range(R - 1)]
     wcs = [wc0] + [wc0.clone() for _ in range(R - 1)]
     wss = [ws0] + [ws0.clone() for _ in range(R - 1)]
-    ys = [torch.empty((M, N), dtype=torch.float32, device=dev) for _ in range(R)]
+    y_dtype = torch.float32 if args.out == "f32" else torch.bfloat16
+    ydt = mx.F32 if args.out == "f32" else mx.BF16
+    epi = mx.EPI_SWIGLU if args.epilogue == "swiglu" else mx.EPI_NONE
+    y_cols = N // 2 if epi == mx.EPI_SWIGLU else N
+    ys = [torch.empty((M, y_cols), dtype=y_dtype, device=dev) for _ in range(R)]
     need = L.macaq_linear_workspace_bytes(M, N, K, E, flags)
     ws_buf = torch.zeros(max(need, 256), dtype=torch.uint8, device=dev)
     a_codes = ws_buf[: M * K // 2]
@@ -236,8 +244,8 @@ def main():
 
     def run_linear(i):
         xp, wcp, wsp, yp = step_args(i)
-        st = mx.macaq_linear(xp, xdt, p(s0.data_ptr()), off_p, E, wcp, wsp, M, N, K, yp,
-                             p(ws_buf.data_ptr()), ws_buf.numel(), flags, sp)
+        st = mx.macaq_linear_ex(xp, xdt, p(s0.data_ptr()), off_p, E, wcp, wsp, M, N, K, yp, ydt, epi,
+                                p(ws_buf.data_ptr()), ws_buf.numel(), flags, sp)
         if st != 0:
             raise RuntimeError(mx.lib().macaq_last_error().decode())
 
@@ -269,8 +277,8 @@ def main():
 
     def gemm_only(i):
         _, wcp, wsp, yp = step_args(i)
-        if mx.macaq_gemm(p(a_codes.data_ptr()), p(a_scales.data_ptr()), off_p, E, wcp, wsp, M, N, K, yp,
-                         p(gemm_ws.data_ptr()), gemm_ws.numel(), sp) != 0:
+        if mx.macaq_gemm_ex(p(a_codes.data_ptr()), p(a_scales.data_ptr()), off_p, E, wcp, wsp, M, N, K, yp, ydt,
+                            epi, p(gemm_ws.data_ptr()), gemm_ws.numel(), sp) != 0:
             raise RuntimeError(mx.lib().macaq_last_error().decode())
 
     def kernel_us(fn):
@@ -313,30 +321,33 @@ def main():
         "data": "synthetic",
         "config": {"workload": desc, "M": M, "N": N, "K": K, "experts": E, "x_dtype": str(x0.dtype).split(".")[-1],
                    "path": "fused" if fused else "unfused", "replicas": R,
+                   "y": f"{args.out} [{M}][{y_cols}]" + (" swiglu" if epi == mx.EPI_SWIGLU else ""),
                    "parallelism": "none (one GPU)"},
     }
     if act_us is not None:
         out["act_transform"] = {"GBps": round(act_alg / act_us / 1e3, 1), "us": round(act_us, 2),
                                 "bytes": act_alg, "frac_of_hbm_peak": round(act_alg / act_us / 1e3 / PEAK_HBM_GBPS, 4),
                                 "traffic": traffic_record(f"{args.workload}:act")}
+    # counter records are keyed by workload, kernel and (when not fp32 / no epilogue) the output variant
+    out_key = "" if (args.out == "f32" and epi == mx.EPI_NONE) else f":{args.out}:{args.epilogue}"
     gemm_name = "fused transform+GEMM" if fused else "MXFP4 GEMM"
     if fused or M <= 32:
         # the kernel's algorithmic HBM bytes: W' codes+scales, its activation
         # input (x and s when fused, else the MXFP4 codes+scales), y
         a_in = xb + 4 * K if fused else M * K // 2 + M * K // 32
-        gemm_bytes = w_alg + a_in + M * N * 4
+        gemm_bytes = w_alg + a_in + M * y_cols * ys[0].element_size()
         ach = gemm_bytes / gemm_us / 1e3
         out["roofline"] = {"kernel": gemm_name, "bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBPS,
                            "unit": "GB/s", "frac": round(ach / PEAK_HBM_GBPS, 4), "us": round(gemm_us, 2),
-                           "traffic": traffic_record(f"{args.workload}:{'fused' if fused else 'gemm'}")}
+                           "traffic": traffic_record(f"{args.workload}:{'fused' if fused else 'gemm'}{out_key}")}
     else:
         ach = flops / gemm_us / 1e6
         out["roofline"] = {"kernel": gemm_name, "bound": "mfma", "achieved": round(ach, 1),
                            "peak": PEAK_MXFP4_TFLOPS, "unit": "TFLOP/s", "frac": round(ach / PEAK_MXFP4_TFLOPS, 4),
-                           "us": round(gemm_us, 2), "traffic": traffic_record(f"{args.workload}:gemm")}
+                           "us": round(gemm_us, 2), "traffic": traffic_record(f"{args.workload}:gemm{out_key}")}
     if not args.no_ablation and not fused:
         out["transform_overhead"] = transform_overhead(args, mx, L, wl, xs, wss, wcs, ys, s0, off_p, stream, sp,
-                                                       a_codes, a_scales, gemm_ws, M, N, K, E, R)
+                                                       a_codes, a_scales, gemm_ws, M, N, K, E, R, ydt, epi)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(wl, min(args.cpu_rows, M))
     print(json.dumps(out), flush=True)

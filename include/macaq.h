@@ -85,6 +85,12 @@ enum {
   MACAQ_PATH_UNFUSED = 2  /* macaq_quant_act into the workspace, then macaq_gemm */
 };
 
+/* epilogue of macaq_gemm_ex / macaq_linear_ex */
+enum {
+  MACAQ_EPI_NONE = 0,   /* y[m][n] = the layer output */
+  MACAQ_EPI_SWIGLU = 1  /* weight rows are (gate, up) pairs: y[m][j] = silu(out[m][2j]) * out[m][2j+1] */
+};
+
 /* Library version as major*10000 + minor*100 + patch. */
 int macaq_version(void);
 
@@ -188,6 +194,31 @@ int macaq_linear(const void* x, macaq_dtype x_dtype, const float* s,
                  const uint8_t* w_codes, const uint8_t* w_scales,
                  int64_t M, int64_t N, int64_t K, float* y,
                  void* workspace, size_t workspace_bytes, uint32_t flags, void* stream);
+
+/*
+ * macaq_gemm and macaq_linear with a chosen output (the layer's consumer
+ * step, after the pages' y = x W^T: a bf16 output and a SwiGLU over the
+ * gate/up projection are what a decoder layer does with it).
+ *   y_dtype MACAQ_F32: y as fp32; MACAQ_BF16: y rounded to bf16 (nearest,
+ *   ties to even) from the same fp32 value.
+ *   epilogue MACAQ_EPI_NONE: y [M][N].  MACAQ_EPI_SWIGLU: N must be even and
+ *   weight row 2j is the gate and row 2j+1 the up projection of output
+ *   column j; y [M][N/2] = silu(g) * u with g, u the fp32 results of those
+ *   rows and silu(g) = g / (1 + exp(-g)) in fp32 (expf, IEEE division).
+ * Other arguments, rules and errors as macaq_gemm / macaq_linear; y must be
+ * aligned to its element size.  macaq_gemm and macaq_linear are these calls
+ * with MACAQ_F32 and MACAQ_EPI_NONE.
+ */
+int macaq_gemm_ex(const uint8_t* a_codes, const uint8_t* a_scales,
+                  const int32_t* expert_offsets, int64_t E,
+                  const uint8_t* w_codes, const uint8_t* w_scales,
+                  int64_t M, int64_t N, int64_t K, void* y, macaq_dtype y_dtype, uint32_t epilogue,
+                  void* workspace, size_t workspace_bytes, void* stream);
+int macaq_linear_ex(const void* x, macaq_dtype x_dtype, const float* s,
+                    const int32_t* expert_offsets, int64_t E,
+                    const uint8_t* w_codes, const uint8_t* w_scales,
+                    int64_t M, int64_t N, int64_t K, void* y, macaq_dtype y_dtype, uint32_t epilogue,
+                    void* workspace, size_t workspace_bytes, uint32_t flags, void* stream);
 
 /*
  * Plain OCP MXFP4 quantization of rows, without the scale and the Hadamard

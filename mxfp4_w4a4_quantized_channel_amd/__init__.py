@@ -21,7 +21,7 @@ import torch
 __all__ = [
     "lib", "MacaqError", "BF16", "F32", "PATH_AUTO", "PATH_FUSED", "PATH_UNFUSED",
     "prepare_weights", "quant_act", "gemm", "linear", "linear_workspace_bytes",
-    "encode_e2m1", "quant_mxfp4", "version", "library_path",
+    "encode_e2m1", "quant_mxfp4", "version", "library_path", "EPI_NONE", "EPI_SWIGLU",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -29,6 +29,7 @@ library_path = os.path.join(_HERE, "libmacaq.so")
 
 BF16, F32 = 0, 1
 PATH_AUTO, PATH_FUSED, PATH_UNFUSED = 0, 1, 2
+EPI_NONE, EPI_SWIGLU = 0, 1
 STATUS = {0: "ok", -1: "invalid argument", -2: "unsupported", -3: "no device", -4: "HIP error",
           -5: "workspace too small"}
 
@@ -65,6 +66,8 @@ def _load():
         "macaq_linear_workspace_bytes": (sz, [i64, i64, i64, i64, u32]),
         "macaq_linear_path": (ci, [i64, i64, i64, i64, u32]),
         "macaq_linear": (ci, [vp, ci, vp, vp, i64, vp, vp, i64, i64, i64, vp, vp, sz, u32, vp]),
+        "macaq_gemm_ex": (ci, [vp, vp, vp, i64, vp, vp, i64, i64, i64, vp, ci, u32, vp, sz, vp]),
+        "macaq_linear_ex": (ci, [vp, ci, vp, vp, i64, vp, vp, i64, i64, i64, vp, ci, u32, vp, sz, u32, vp]),
         "macaq_encode_e2m1": (ci, [vp, i64, vp, vp]),
         "macaq_quant_mxfp4": (ci, [vp, ci, i64, i64, vp, vp, vp]),
     }
@@ -175,9 +178,23 @@ def _w_shape(w_codes, w_scales):
     return w_codes, w_scales
 
 
-def gemm(a_codes, a_scales, w_codes, w_scales, offsets=None, out=None, workspace=None):
-    """y = A' W'^T (fp32 [M, N]) from MXFP4 operands.  A workspace, when one
-    is needed, is zero-filled here; a caller-provided one must start zeroed."""
+def _out(M, N, out_dtype, epilogue, device, out):
+    if out_dtype not in (torch.float32, torch.bfloat16):
+        raise TypeError(f"out_dtype must be float32 or bfloat16, got {out_dtype}")
+    width = N // 2 if epilogue == EPI_SWIGLU else N
+    if out is None:
+        return torch.empty((M, width), dtype=out_dtype, device=device)
+    _need(out, "out", out_dtype, 2)
+    if tuple(out.shape) != (M, width):
+        raise ValueError(f"out must be [{M}, {width}], got {tuple(out.shape)}")
+    return out
+
+
+def gemm(a_codes, a_scales, w_codes, w_scales, offsets=None, out=None, workspace=None,
+         out_dtype=torch.float32, epilogue=EPI_NONE):
+    """y = A' W'^T from MXFP4 operands: [M, N] (or [M, N/2] with EPI_SWIGLU)
+    in out_dtype (float32 or bfloat16).  A workspace, when one is needed, is
+    zero-filled here; a caller-provided one must start zeroed."""
     _load()
     w_codes, w_scales = _w_shape(w_codes, w_scales)
     _need(a_codes, "a_codes", torch.uint8, 2)
@@ -185,13 +202,15 @@ def gemm(a_codes, a_scales, w_codes, w_scales, offsets=None, out=None, workspace
     E, N, KH = w_codes.shape
     M = a_codes.shape[0]
     K = 2 * KH
-    y = out if out is not None else torch.empty((M, N), dtype=torch.float32, device=a_codes.device)
+    y = _out(M, N, out_dtype, epilogue, a_codes.device, out)
     need = int(_load().macaq_gemm_workspace_bytes(M, N, K, E))
     if workspace is None and need > 0:
         workspace = torch.zeros(need, dtype=torch.uint8, device=a_codes.device)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    _check(macaq_gemm(_ptr(a_codes), _ptr(a_scales), _ptr(offsets), E, _ptr(w_codes), _ptr(w_scales),
-                      M, N, K, _ptr(y), _ptr(workspace), ws_bytes, _stream(a_codes.device)), "macaq_gemm")
+    ydt = F32 if out_dtype == torch.float32 else BF16
+    _check(macaq_gemm_ex(_ptr(a_codes), _ptr(a_scales), _ptr(offsets), E, _ptr(w_codes), _ptr(w_scales),
+                         M, N, K, _ptr(y), ydt, epilogue, _ptr(workspace), ws_bytes, _stream(a_codes.device)),
+           "macaq_gemm")
     return y
 
 
@@ -199,8 +218,10 @@ def linear_workspace_bytes(M, N, K, E=1, flags=PATH_AUTO) -> int:
     return int(_load().macaq_linear_workspace_bytes(M, N, K, E, flags))
 
 
-def linear(x, s, w_codes, w_scales, offsets=None, flags=PATH_AUTO, out=None, workspace=None):
-    """The whole online layer y = quant(x diag(s) H) W'^T, fp32 [M, N]."""
+def linear(x, s, w_codes, w_scales, offsets=None, flags=PATH_AUTO, out=None, workspace=None,
+           out_dtype=torch.float32, epilogue=EPI_NONE):
+    """The whole online layer y = quant(x diag(s) H) W'^T: [M, N] (or
+    [M, N/2] with EPI_SWIGLU) in out_dtype (float32 or bfloat16)."""
     _load()
     if s.dim() == 1:
         s = s[None]
@@ -212,10 +233,12 @@ def linear(x, s, w_codes, w_scales, offsets=None, flags=PATH_AUTO, out=None, wor
     need = linear_workspace_bytes(M, N, K, E, flags)
     if workspace is None and need > 0:
         workspace = torch.zeros(need, dtype=torch.uint8, device=x.device)
-    y = out if out is not None else torch.empty((M, N), dtype=torch.float32, device=x.device)
+    y = _out(M, N, out_dtype, epilogue, x.device, out)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    _check(macaq_linear(_ptr(x), _dtype_code(x), _ptr(s), _ptr(offsets), E, _ptr(w_codes), _ptr(w_scales),
-                        M, N, K, _ptr(y), _ptr(workspace), ws_bytes, flags, _stream(x.device)), "macaq_linear")
+    ydt = F32 if out_dtype == torch.float32 else BF16
+    _check(macaq_linear_ex(_ptr(x), _dtype_code(x), _ptr(s), _ptr(offsets), E, _ptr(w_codes), _ptr(w_scales),
+                           M, N, K, _ptr(y), ydt, epilogue, _ptr(workspace), ws_bytes, flags, _stream(x.device)),
+           "macaq_linear")
     return y
 
 

@@ -20,14 +20,17 @@ hipError_t launch_quant_plain(const void* x, bool x_f32, int64_t M, int64_t K, u
                               hipStream_t stream);
 hipError_t launch_gemm(const uint8_t* A, const uint8_t* As, const int32_t* offsets, int E,
                        const uint8_t* B, const uint8_t* Bs, int64_t M, int64_t N, int64_t K,
-                       float* Y, hipStream_t stream);
+                       void* Y, int mode, hipStream_t stream);
 hipError_t launch_linear_fused(const void* x, bool x_f32, const float* s, const uint8_t* B,
-                               const uint8_t* Bs, int64_t M, int64_t N, int64_t K, float* Y,
+                               const uint8_t* Bs, int64_t M, int64_t N, int64_t K, void* Y, int mode,
                                hipStream_t stream);
 bool linear_fused_supported(int64_t M, int64_t N, int64_t K, int64_t E);
 bool decode_supported(int64_t M, int64_t N, int64_t K, int64_t E);
 hipError_t launch_decode_gemm(const uint8_t* A, const uint8_t* As, const uint8_t* W, const uint8_t* Ws, int64_t M,
-                              int64_t N, int64_t K, float* Y, hipStream_t stream);
+                              int64_t N, int64_t K, void* Y, int mode, hipStream_t stream);
+// output mode bits of the GEMM kernels (mx_common.h)
+constexpr int kOutBf16 = 1;
+constexpr int kOutSwiGLU = 2;
 }  // namespace macaq
 
 namespace {
@@ -77,9 +80,23 @@ int check_k(int64_t K, const char* fn) {
   return MACAQ_OK;
 }
 
+// Output of the GEMM-based entry points: dtype and epilogue -> kernel mode.
+int output_mode(macaq_dtype y_dtype, uint32_t epilogue, int64_t N, const void* y, const char* fn, int* mode) {
+  if (y_dtype != MACAQ_F32 && y_dtype != MACAQ_BF16)
+    return fail(MACAQ_ERR_UNSUPPORTED, std::string(fn) + ": y dtype must be MACAQ_F32 or MACAQ_BF16");
+  if (epilogue != MACAQ_EPI_NONE && epilogue != MACAQ_EPI_SWIGLU)
+    return fail(MACAQ_ERR_INVALID_ARG, std::string(fn) + ": unknown epilogue");
+  if (epilogue == MACAQ_EPI_SWIGLU && N % 2 != 0)
+    return fail(MACAQ_ERR_INVALID_ARG, std::string(fn) + ": SwiGLU needs an even N (gate/up row pairs)");
+  if (!aligned(y, y_dtype == MACAQ_F32 ? 4 : 2))
+    return fail(MACAQ_ERR_INVALID_ARG, std::string(fn) + ": y misaligned for its dtype");
+  *mode = (y_dtype == MACAQ_BF16 ? macaq::kOutBf16 : 0) | (epilogue == MACAQ_EPI_SWIGLU ? macaq::kOutSwiGLU : 0);
+  return MACAQ_OK;
+}
+
 int validate_gemm(const uint8_t* a_codes, const uint8_t* a_scales, const int32_t* offsets, int64_t E,
                   const uint8_t* w_codes, const uint8_t* w_scales, int64_t M, int64_t N, int64_t K,
-                  const float* y, const char* fn) {
+                  const void* y, const char* fn) {
   if (E < 1) return fail(MACAQ_ERR_INVALID_ARG, std::string(fn) + ": E must be >= 1");
   if (E > 1 && offsets == nullptr)
     return fail(MACAQ_ERR_INVALID_ARG, std::string(fn) + ": expert_offsets required when E > 1");
@@ -94,7 +111,6 @@ int validate_gemm(const uint8_t* a_codes, const uint8_t* a_scales, const int32_t
     return fail(MACAQ_ERR_INVALID_ARG, std::string(fn) + ": code pointers must be 16-byte aligned");
   if (!aligned(a_scales, 4) || !aligned(w_scales, 4))
     return fail(MACAQ_ERR_INVALID_ARG, std::string(fn) + ": scale pointers must be 4-byte aligned");
-  if (!aligned(y, 4)) return fail(MACAQ_ERR_INVALID_ARG, std::string(fn) + ": y must be 4-byte aligned");
   if (M > INT32_MAX || N > INT32_MAX || E > 4096)
     return fail(MACAQ_ERR_UNSUPPORTED, std::string(fn) + ": sizes beyond the supported range");
   return MACAQ_OK;
@@ -180,13 +196,13 @@ size_t macaq_linear_workspace_bytes(int64_t M, int64_t N, int64_t K, int64_t E, 
 
 namespace {
 int run_gemm(const uint8_t* a_codes, const uint8_t* a_scales, const int32_t* expert_offsets, int64_t E,
-             const uint8_t* w_codes, const uint8_t* w_scales, int64_t M, int64_t N, int64_t K, float* y,
+             const uint8_t* w_codes, const uint8_t* w_scales, int64_t M, int64_t N, int64_t K, void* y, int mode,
              void* workspace, hipStream_t stream, const char* fn) {
   (void)workspace;
   if (macaq::decode_supported(M, N, K, E))
-    return hip_status(macaq::launch_decode_gemm(a_codes, a_scales, w_codes, w_scales, M, N, K, y, stream), fn);
+    return hip_status(macaq::launch_decode_gemm(a_codes, a_scales, w_codes, w_scales, M, N, K, y, mode, stream), fn);
   return hip_status(macaq::launch_gemm(a_codes, a_scales, E > 1 ? expert_offsets : nullptr, (int)E, w_codes,
-                                       w_scales, M, N, K, y, stream),
+                                       w_scales, M, N, K, y, mode, stream),
                     fn);
 }
 
@@ -201,21 +217,31 @@ int check_workspace(void* workspace, size_t have, size_t need, const char* fn) {
 }
 }  // namespace
 
-int macaq_gemm(const uint8_t* a_codes, const uint8_t* a_scales, const int32_t* expert_offsets, int64_t E,
-               const uint8_t* w_codes, const uint8_t* w_scales, int64_t M, int64_t N, int64_t K, float* y,
-               void* workspace, size_t workspace_bytes, void* stream) {
+int macaq_gemm_ex(const uint8_t* a_codes, const uint8_t* a_scales, const int32_t* expert_offsets, int64_t E,
+                  const uint8_t* w_codes, const uint8_t* w_scales, int64_t M, int64_t N, int64_t K, void* y,
+                  macaq_dtype y_dtype, uint32_t epilogue, void* workspace, size_t workspace_bytes, void* stream) {
   const char* fn = "macaq_gemm";
   if (int st = validate_gemm(a_codes, a_scales, expert_offsets, E, w_codes, w_scales, M, N, K, y, fn)) return st;
+  int mode = 0;
+  if (int st = output_mode(y_dtype, epilogue, N, y, fn, &mode)) return st;
   if (M == 0) return MACAQ_OK;
   if (int st = check_workspace(workspace, workspace_bytes, macaq_gemm_workspace_bytes(M, N, K, E), fn)) return st;
   if (int st = check_device()) return st;
-  return run_gemm(a_codes, a_scales, expert_offsets, E, w_codes, w_scales, M, N, K, y, workspace,
+  return run_gemm(a_codes, a_scales, expert_offsets, E, w_codes, w_scales, M, N, K, y, mode, workspace,
                   (hipStream_t)stream, fn);
 }
 
-int macaq_linear(const void* x, macaq_dtype x_dtype, const float* s, const int32_t* expert_offsets, int64_t E,
-                 const uint8_t* w_codes, const uint8_t* w_scales, int64_t M, int64_t N, int64_t K, float* y,
-                 void* workspace, size_t workspace_bytes, uint32_t flags, void* stream) {
+int macaq_gemm(const uint8_t* a_codes, const uint8_t* a_scales, const int32_t* expert_offsets, int64_t E,
+               const uint8_t* w_codes, const uint8_t* w_scales, int64_t M, int64_t N, int64_t K, float* y,
+               void* workspace, size_t workspace_bytes, void* stream) {
+  return macaq_gemm_ex(a_codes, a_scales, expert_offsets, E, w_codes, w_scales, M, N, K, y, MACAQ_F32,
+                       MACAQ_EPI_NONE, workspace, workspace_bytes, stream);
+}
+
+int macaq_linear_ex(const void* x, macaq_dtype x_dtype, const float* s, const int32_t* expert_offsets, int64_t E,
+                    const uint8_t* w_codes, const uint8_t* w_scales, int64_t M, int64_t N, int64_t K, void* y,
+                    macaq_dtype y_dtype, uint32_t epilogue, void* workspace, size_t workspace_bytes, uint32_t flags,
+                    void* stream) {
   const char* fn = "macaq_linear";
   if (int st = check_dtype(x_dtype, fn)) return st;
   if (flags > MACAQ_PATH_UNFUSED) return fail(MACAQ_ERR_INVALID_ARG, std::string(fn) + ": unknown flags");
@@ -226,6 +252,8 @@ int macaq_linear(const void* x, macaq_dtype x_dtype, const float* s, const int32
   // the GEMM's rules (E, offsets, K, weights, y); activation buffers are internal
   const uint8_t* dummy = reinterpret_cast<const uint8_t*>(w_codes);
   if (int st = validate_gemm(dummy, w_scales, expert_offsets, E, w_codes, w_scales, M, N, K, y, fn)) return st;
+  int mode = 0;
+  if (int st = output_mode(y_dtype, epilogue, N, y, fn, &mode)) return st;
   if (M == 0) return MACAQ_OK;
   if (flags == MACAQ_PATH_FUSED && !macaq::linear_fused_supported(M, N, K, E))
     return fail(MACAQ_ERR_UNSUPPORTED, std::string(fn) +
@@ -237,8 +265,9 @@ int macaq_linear(const void* x, macaq_dtype x_dtype, const float* s, const int32
   if (int st = check_device()) return st;
   hipStream_t st = (hipStream_t)stream;
   if (fused)
-    return hip_status(macaq::launch_linear_fused(x, x_dtype == MACAQ_F32, s, w_codes, w_scales, M, N, K, y, st),
-                      "macaq_linear (fused)");
+    return hip_status(
+        macaq::launch_linear_fused(x, x_dtype == MACAQ_F32, s, w_codes, w_scales, M, N, K, y, mode, st),
+        "macaq_linear (fused)");
   uint8_t* a_codes = static_cast<uint8_t*>(workspace);
   uint8_t* a_scales = a_codes + round_up((size_t)M * (size_t)K / 2, 256);
   const int32_t* off = E > 1 ? expert_offsets : nullptr;
@@ -247,7 +276,15 @@ int macaq_linear(const void* x, macaq_dtype x_dtype, const float* s, const int32
                          "macaq_linear (transform)"))
     return r;
   void* gemm_ws = static_cast<uint8_t*>(workspace) + macaq_quant_act_bytes(M, K);
-  return run_gemm(a_codes, a_scales, off, E, w_codes, w_scales, M, N, K, y, gemm_ws, st, "macaq_linear (gemm)");
+  return run_gemm(a_codes, a_scales, off, E, w_codes, w_scales, M, N, K, y, mode, gemm_ws, st,
+                  "macaq_linear (gemm)");
+}
+
+int macaq_linear(const void* x, macaq_dtype x_dtype, const float* s, const int32_t* expert_offsets, int64_t E,
+                 const uint8_t* w_codes, const uint8_t* w_scales, int64_t M, int64_t N, int64_t K, float* y,
+                 void* workspace, size_t workspace_bytes, uint32_t flags, void* stream) {
+  return macaq_linear_ex(x, x_dtype, s, expert_offsets, E, w_codes, w_scales, M, N, K, y, MACAQ_F32, MACAQ_EPI_NONE,
+                         workspace, workspace_bytes, flags, stream);
 }
 
 int macaq_quant_mxfp4(const void* x, macaq_dtype x_dtype, int64_t M, int64_t K, uint8_t* codes, uint8_t* scales,

@@ -8,21 +8,51 @@ namespace macaq {
 
 namespace {
 
-template <int BM, int BN, int WM, int WN, int BK, int S, int MINB = 1>
-hipError_t launch_pipe(const uint8_t* A, const uint8_t* As, const int32_t* offsets, int E, const uint8_t* B,
-                       const uint8_t* Bs, int64_t M, int64_t N, int64_t K, float* Y, hipStream_t stream) {
+template <int BM, int BN, int WM, int WN, int BK, int S, int MINB, int OUT>
+hipError_t launch_pipe_out(const uint8_t* A, const uint8_t* As, const int32_t* offsets, int E, const uint8_t* B,
+                           const uint8_t* Bs, int64_t M, int64_t N, int64_t K, void* Y, hipStream_t stream) {
   using L = PipeLayout<BM, BN, BK, 1>;
   constexpr int lds = S * L::kStage;
   static const hipError_t attr =
-      hipFuncSetAttribute((const void*)gemm_mxfp4_pipe_kernel<BM, BN, WM, WN, BK, S, MINB>,
+      hipFuncSetAttribute((const void*)gemm_mxfp4_pipe_kernel<BM, BN, WM, WN, BK, S, MINB, OUT>,
                           hipFuncAttributeMaxDynamicSharedMemorySize, lds);
   if (attr != hipSuccess) return attr;
   const int tiles_n = (int)ceil_div(N, BN);
   int64_t tiles_m = ceil_div(M, BM);
   if (offsets != nullptr) tiles_m += E;  // each expert may add one partial row tile
   const int64_t blocks = tiles_m * tiles_n;
-  gemm_mxfp4_pipe_kernel<BM, BN, WM, WN, BK, S, MINB><<<dim3((unsigned)blocks), dim3(64 * WM * WN), lds, stream>>>(
-      A, As, B, Bs, offsets, E, M, N, K, Y, (int)tiles_m, tiles_n, 4);
+  gemm_mxfp4_pipe_kernel<BM, BN, WM, WN, BK, S, MINB, OUT>
+      <<<dim3((unsigned)blocks), dim3(64 * WM * WN), lds, stream>>>(A, As, B, Bs, offsets, E, M, N, K, Y,
+                                                                    (int)tiles_m, tiles_n, 4);
+  return hipGetLastError();
+}
+
+// output mode (run time) -> kernel instantiation
+template <int BM, int BN, int WM, int WN, int BK, int S, int MINB = 1>
+hipError_t launch_pipe(const uint8_t* A, const uint8_t* As, const int32_t* offsets, int E, const uint8_t* B,
+                       const uint8_t* Bs, int64_t M, int64_t N, int64_t K, void* Y, int mode, hipStream_t stream) {
+  switch (mode) {
+    case 0: return launch_pipe_out<BM, BN, WM, WN, BK, S, MINB, 0>(A, As, offsets, E, B, Bs, M, N, K, Y, stream);
+    case kOutBf16:
+      return launch_pipe_out<BM, BN, WM, WN, BK, S, MINB, kOutBf16>(A, As, offsets, E, B, Bs, M, N, K, Y, stream);
+    case kOutSwiGLU:
+      return launch_pipe_out<BM, BN, WM, WN, BK, S, MINB, kOutSwiGLU>(A, As, offsets, E, B, Bs, M, N, K, Y, stream);
+    default:
+      return launch_pipe_out<BM, BN, WM, WN, BK, S, MINB, kOutBf16 | kOutSwiGLU>(A, As, offsets, E, B, Bs, M, N, K,
+                                                                                  Y, stream);
+  }
+}
+
+template <int OUT>
+hipError_t launch_v1(const uint8_t* A, const uint8_t* As, const int32_t* offsets, int E, const uint8_t* B,
+                     const uint8_t* Bs, int64_t M, int64_t N, int64_t K, void* Y, hipStream_t stream) {
+  constexpr int BM = 128, BN = 128;
+  const int n_tiles_n = (int)ceil_div(N, BN);
+  int64_t m_slots = ceil_div(M, BM);
+  if (offsets != nullptr) m_slots += E;  // each expert may add one partial tile
+  const int64_t blocks = m_slots * n_tiles_n;
+  gemm_mxfp4_kernel<BM, BN, 2, 2, OUT><<<dim3((unsigned)blocks), dim3(256), 0, stream>>>(A, As, B, Bs, offsets, E, M,
+                                                                                        N, K, Y, n_tiles_n);
   return hipGetLastError();
 }
 
@@ -30,7 +60,7 @@ hipError_t launch_pipe(const uint8_t* A, const uint8_t* As, const int32_t* offse
 
 hipError_t launch_gemm(const uint8_t* A, const uint8_t* As, const int32_t* offsets, int E,
                        const uint8_t* B, const uint8_t* Bs, int64_t M, int64_t N, int64_t K,
-                       float* Y, hipStream_t stream) {
+                       void* Y, int mode, hipStream_t stream) {
   if (M <= 0) return hipSuccess;
   // Tile choice (measured on MI355X): 256x256 when that still gives about one
   // tile per CU (largest tiles, least LDS and L2 traffic per FLOP); else
@@ -54,24 +84,22 @@ hipError_t launch_gemm(const uint8_t* A, const uint8_t* As, const int32_t* offse
   const bool k256 = K % 256 == 0;
   switch (choice) {
     case 0:
-      return k256 ? launch_pipe<256, 256, 2, 2, 256, 2>(A, As, offsets, E, B, Bs, M, N, K, Y, stream)
-                  : launch_pipe<256, 256, 2, 2, 128, 4>(A, As, offsets, E, B, Bs, M, N, K, Y, stream);
+      return k256 ? launch_pipe<256, 256, 2, 2, 256, 2>(A, As, offsets, E, B, Bs, M, N, K, Y, mode, stream)
+                  : launch_pipe<256, 256, 2, 2, 128, 4>(A, As, offsets, E, B, Bs, M, N, K, Y, mode, stream);
     case 1:
-      return k256 ? launch_pipe<256, 128, 2, 2, 256, 2>(A, As, offsets, E, B, Bs, M, N, K, Y, stream)
-                  : launch_pipe<256, 128, 2, 2, 128, 4>(A, As, offsets, E, B, Bs, M, N, K, Y, stream);
+      return k256 ? launch_pipe<256, 128, 2, 2, 256, 2>(A, As, offsets, E, B, Bs, M, N, K, Y, mode, stream)
+                  : launch_pipe<256, 128, 2, 2, 128, 4>(A, As, offsets, E, B, Bs, M, N, K, Y, mode, stream);
     case 2:
-      return k256 ? launch_pipe<128, 128, 2, 2, 256, 2, 2>(A, As, offsets, E, B, Bs, M, N, K, Y, stream)
-                  : launch_pipe<128, 128, 2, 2, 128, 4, 2>(A, As, offsets, E, B, Bs, M, N, K, Y, stream);
+      return k256 ? launch_pipe<128, 128, 2, 2, 256, 2, 2>(A, As, offsets, E, B, Bs, M, N, K, Y, mode, stream)
+                  : launch_pipe<128, 128, 2, 2, 128, 4, 2>(A, As, offsets, E, B, Bs, M, N, K, Y, mode, stream);
     default: break;
   }
-  constexpr int BM = 128, BN = 128;
-  const int n_tiles_n = (int)ceil_div(N, BN);
-  int64_t m_slots = ceil_div(M, BM);
-  if (offsets != nullptr) m_slots += E;  // each expert may add one partial tile
-  const int64_t blocks = m_slots * n_tiles_n;
-  gemm_mxfp4_kernel<BM, BN, 2, 2><<<dim3((unsigned)blocks), dim3(256), 0, stream>>>(
-      A, As, B, Bs, offsets, E, M, N, K, Y, n_tiles_n);
-  return hipGetLastError();
+  switch (mode) {
+    case 0: return launch_v1<0>(A, As, offsets, E, B, Bs, M, N, K, Y, stream);
+    case kOutBf16: return launch_v1<kOutBf16>(A, As, offsets, E, B, Bs, M, N, K, Y, stream);
+    case kOutSwiGLU: return launch_v1<kOutSwiGLU>(A, As, offsets, E, B, Bs, M, N, K, Y, stream);
+    default: return launch_v1<kOutBf16 | kOutSwiGLU>(A, As, offsets, E, B, Bs, M, N, K, Y, stream);
+  }
 }
 
 }  // namespace macaq

@@ -164,7 +164,7 @@ __global__ __launch_bounds__(64 * WAVES) void decode_gemm_kernel(
     const uint8_t* __restrict__ A, const uint8_t* __restrict__ As,     // activation codes/scales (unfused)
     const void* __restrict__ x, const float* __restrict__ s,           // activations and scale (fused)
     const uint8_t* __restrict__ W, const uint8_t* __restrict__ Ws, int64_t M, int64_t N, int64_t K,
-    float* __restrict__ Y) {
+    void* __restrict__ Y, int out_mode) {
   constexpr int EB = dec_eb<XT>;
   using S = DecStage<AK, EB, RT>;
   constexpr bool FUSED = AK == 0;     // resident activation, transformed before the loop
@@ -419,12 +419,27 @@ __global__ __launch_bounds__(64 * WAVES) void decode_gemm_kernel(
     }
   }
   __syncthreads();
+  if (out_mode & kOutSwiGLU) {
+    // columns (2j, 2j+1) = (gate, up) -> column n0/2 + j of the [M][N/2] output
+    constexpr int kPairs = kRows / 2;
+    for (int idx = tid; idx < kPairs * 32; idx += kThreads) {
+      const int j = idx % kPairs, m = idx / kPairs;
+      float g = red[(2 * j) * 32 + m], u = red[(2 * j + 1) * 32 + m];
+#pragma unroll
+      for (int w = 1; w < WAVES; ++w) {
+        g = g + red[(w * kRows + 2 * j) * 32 + m];
+        u = u + red[(w * kRows + 2 * j + 1) * 32 + m];
+      }
+      if (m < M && n0 + 2 * j < N) store_out(Y, (int64_t)m * (N >> 1) + (n0 >> 1) + j, silu_times(g, u), out_mode);
+    }
+    return;
+  }
   for (int idx = tid; idx < kRows * 32; idx += kThreads) {
     const int n = idx % kRows, m = idx / kRows;   // consecutive threads: consecutive n of one row of y
     float v = red[n * 32 + m];
 #pragma unroll
     for (int w = 1; w < WAVES; ++w) v = v + red[(w * kRows + n) * 32 + m];
-    if (m < M && n0 + n < N) Y[(int64_t)m * N + n0 + n] = v;
+    if (m < M && n0 + n < N) store_out(Y, (int64_t)m * N + n0 + n, v, out_mode);
   }
 }
 
@@ -502,46 +517,47 @@ bool decode_supported(int64_t M, int64_t N, int64_t K, int64_t E) {
 
 template <int WAVES, int STAGES, int AK, typename XT, int RT>
 static hipError_t launch_decode_w(const uint8_t* A, const uint8_t* As, const void* x, const float* s,
-                                  const uint8_t* W, const uint8_t* Ws, int64_t M, int64_t N, int64_t K, float* Y,
-                                  size_t lds, hipStream_t stream) {
+                                  const uint8_t* W, const uint8_t* Ws, int64_t M, int64_t N, int64_t K, void* Y,
+                                  int mode, size_t lds, hipStream_t stream) {
   static_assert(DecWaveLds<STAGES, AK, dec_eb<XT>, RT>::kBytes >= 32 * RT * 32 * 4,
                 "partial sums must fit in the rings");
   static const hipError_t attr = hipFuncSetAttribute((const void*)decode_gemm_kernel<WAVES, STAGES, AK, XT, RT>,
                                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)kDecLdsMax);
   if (attr != hipSuccess) return attr;
   decode_gemm_kernel<WAVES, STAGES, AK, XT, RT>
-      <<<dim3((unsigned)ceil_div(N, kDecRows * RT)), dim3(64 * WAVES), lds, stream>>>(A, As, x, s, W, Ws, M, N, K, Y);
+      <<<dim3((unsigned)ceil_div(N, kDecRows * RT)), dim3(64 * WAVES), lds, stream>>>(A, As, x, s, W, Ws, M, N, K, Y,
+                                                                                      mode);
   return hipGetLastError();
 }
 
 template <int AK, typename XT>
 static hipError_t launch_decode_impl(const DecodeConfig& d, const uint8_t* A, const uint8_t* As, const void* x,
                                      const float* s, const uint8_t* W, const uint8_t* Ws, int64_t M, int64_t N,
-                                     int64_t K, float* Y, hipStream_t stream) {
+                                     int64_t K, void* Y, int mode, hipStream_t stream) {
   const size_t lds = decode_lds_bytes(d, M, K);
   if (lds > kDecLdsMax) return hipErrorInvalidValue;
   if (d.rt == 2) {
-    if (d.stages >= 3) return launch_decode_w<2, 3, AK, XT, 2>(A, As, x, s, W, Ws, M, N, K, Y, lds, stream);
-    return launch_decode_w<2, 2, AK, XT, 2>(A, As, x, s, W, Ws, M, N, K, Y, lds, stream);
+    if (d.stages >= 3) return launch_decode_w<2, 3, AK, XT, 2>(A, As, x, s, W, Ws, M, N, K, Y, mode, lds, stream);
+    return launch_decode_w<2, 2, AK, XT, 2>(A, As, x, s, W, Ws, M, N, K, Y, mode, lds, stream);
   }
   if (d.waves == 8) {
-    if (d.stages == 4) return launch_decode_w<8, 4, AK, XT, 1>(A, As, x, s, W, Ws, M, N, K, Y, lds, stream);
-    if (d.stages == 3) return launch_decode_w<8, 3, AK, XT, 1>(A, As, x, s, W, Ws, M, N, K, Y, lds, stream);
-    return launch_decode_w<8, 2, AK, XT, 1>(A, As, x, s, W, Ws, M, N, K, Y, lds, stream);
+    if (d.stages == 4) return launch_decode_w<8, 4, AK, XT, 1>(A, As, x, s, W, Ws, M, N, K, Y, mode, lds, stream);
+    if (d.stages == 3) return launch_decode_w<8, 3, AK, XT, 1>(A, As, x, s, W, Ws, M, N, K, Y, mode, lds, stream);
+    return launch_decode_w<8, 2, AK, XT, 1>(A, As, x, s, W, Ws, M, N, K, Y, mode, lds, stream);
   }
-  if (d.stages == 4) return launch_decode_w<4, 4, AK, XT, 1>(A, As, x, s, W, Ws, M, N, K, Y, lds, stream);
-  if (d.stages == 3) return launch_decode_w<4, 3, AK, XT, 1>(A, As, x, s, W, Ws, M, N, K, Y, lds, stream);
-  return launch_decode_w<4, 2, AK, XT, 1>(A, As, x, s, W, Ws, M, N, K, Y, lds, stream);
+  if (d.stages == 4) return launch_decode_w<4, 4, AK, XT, 1>(A, As, x, s, W, Ws, M, N, K, Y, mode, lds, stream);
+  if (d.stages == 3) return launch_decode_w<4, 3, AK, XT, 1>(A, As, x, s, W, Ws, M, N, K, Y, mode, lds, stream);
+  return launch_decode_w<4, 2, AK, XT, 1>(A, As, x, s, W, Ws, M, N, K, Y, mode, lds, stream);
 }
 
 hipError_t launch_decode_gemm(const uint8_t* A, const uint8_t* As, const uint8_t* W, const uint8_t* Ws, int64_t M,
-                              int64_t N, int64_t K, float* Y, hipStream_t stream) {
+                              int64_t N, int64_t K, void* Y, int mode, hipStream_t stream) {
   const DecodeConfig d = decode_config(M, N, K, false, 2);
   switch (d.ak) {
-    case 1: return launch_decode_impl<1, DecBf16>(d, A, As, nullptr, nullptr, W, Ws, M, N, K, Y, stream);
-    case 8: return launch_decode_impl<8, DecBf16>(d, A, As, nullptr, nullptr, W, Ws, M, N, K, Y, stream);
-    case 16: return launch_decode_impl<16, DecBf16>(d, A, As, nullptr, nullptr, W, Ws, M, N, K, Y, stream);
-    default: return launch_decode_impl<32, DecBf16>(d, A, As, nullptr, nullptr, W, Ws, M, N, K, Y, stream);
+    case 1: return launch_decode_impl<1, DecBf16>(d, A, As, nullptr, nullptr, W, Ws, M, N, K, Y, mode, stream);
+    case 8: return launch_decode_impl<8, DecBf16>(d, A, As, nullptr, nullptr, W, Ws, M, N, K, Y, mode, stream);
+    case 16: return launch_decode_impl<16, DecBf16>(d, A, As, nullptr, nullptr, W, Ws, M, N, K, Y, mode, stream);
+    default: return launch_decode_impl<32, DecBf16>(d, A, As, nullptr, nullptr, W, Ws, M, N, K, Y, mode, stream);
   }
 }
 
@@ -556,14 +572,14 @@ bool linear_fused_supported(int64_t M, int64_t N, int64_t K, int64_t E) {
 }
 
 hipError_t launch_linear_fused(const void* x, bool x_f32, const float* s, const uint8_t* B, const uint8_t* Bs,
-                               int64_t M, int64_t N, int64_t K, float* Y, hipStream_t stream) {
+                               int64_t M, int64_t N, int64_t K, void* Y, int mode, hipStream_t stream) {
   const DecodeConfig d = decode_config(M, N, K, true, x_f32 ? 4 : 2);
   if (d.ak < 0) {
-    if (x_f32) return launch_decode_impl<-1, float>(d, nullptr, nullptr, x, s, B, Bs, M, N, K, Y, stream);
-    return launch_decode_impl<-1, DecBf16>(d, nullptr, nullptr, x, s, B, Bs, M, N, K, Y, stream);
+    if (x_f32) return launch_decode_impl<-1, float>(d, nullptr, nullptr, x, s, B, Bs, M, N, K, Y, mode, stream);
+    return launch_decode_impl<-1, DecBf16>(d, nullptr, nullptr, x, s, B, Bs, M, N, K, Y, mode, stream);
   }
-  if (x_f32) return launch_decode_impl<0, float>(d, nullptr, nullptr, x, s, B, Bs, M, N, K, Y, stream);
-  return launch_decode_impl<0, DecBf16>(d, nullptr, nullptr, x, s, B, Bs, M, N, K, Y, stream);
+  if (x_f32) return launch_decode_impl<0, float>(d, nullptr, nullptr, x, s, B, Bs, M, N, K, Y, mode, stream);
+  return launch_decode_impl<0, DecBf16>(d, nullptr, nullptr, x, s, B, Bs, M, N, K, Y, mode, stream);
 }
 
 }  // namespace macaq

@@ -74,11 +74,166 @@ __device__ __forceinline__ void mfma_substep(v16f (&acc)[FM][FN], const uint4 (&
           as_operand(fa[mi]), as_operand(fb[ni]), acc[mi][ni], 4, 4, J, (int)sa[mi], J, (int)sb[ni]);
 }
 
-template <int BM, int BN, int WAVES_M, int WAVES_N>
+// Epilogue of a wave's FM x FN block of 32x32 accumulators whose first row
+// is m0 and first column n0 (rows below row_end and columns below N are
+// stored): lane (r32, h) holds column r32 and rows 8*(r/4) + 4*h + (r%4) of
+// accumulator register r.  OUT: output bits (fp32/bf16, SwiGLU), a template
+// parameter so that the fp32 kernel carries none of the other modes' code.
+//
+// bf16 and SwiGLU work on column pairs (2j, 2j+1), which sit in lanes
+// (2i, 2i+1).  The two lanes swap one register with a DPP move: the even lane
+// then holds both columns of rows 0..7 of the register file, the odd lane
+// both columns of rows 8..15, and each lane stores one result per row: a
+// packed pair of bf16 values, or silu(gate) * up for output column j of the
+// [M][N/2] SwiGLU output.
+template <int OUT, int FM, int FN>
+__device__ __forceinline__ void store_wave_tile(const v16f (&acc)[FM][FN], void* __restrict__ Y,
+                                                int64_t m0, int64_t row_end, int64_t n0, int64_t N, int r32, int h) {
+  const bool interior = (m0 + FM * 32 <= row_end) && (n0 + FN * 32 <= N);
+  if constexpr (OUT == 0) {
+    if (interior) {
+#pragma unroll
+      for (int mi = 0; mi < FM; ++mi)
+#pragma unroll
+        for (int ni = 0; ni < FN; ++ni) {
+          float* yp = reinterpret_cast<float*>(Y) + (m0 + mi * 32 + 4 * h) * N + n0 + ni * 32 + r32;
+#pragma unroll
+          for (int r = 0; r < 16; ++r) yp[(8 * (r >> 2) + (r & 3)) * N] = acc[mi][ni][r];
+        }
+      return;
+    }
+#pragma unroll
+    for (int mi = 0; mi < FM; ++mi)
+#pragma unroll
+      for (int ni = 0; ni < FN; ++ni) {
+        const int64_t n = n0 + ni * 32 + r32;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int64_t m = m0 + mi * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
+          if (m < row_end && n < N) reinterpret_cast<float*>(Y)[m * N + n] = acc[mi][ni][r];
+        }
+      }
+  } else {
+    const bool odd = (r32 & 1) != 0;
+#pragma unroll
+    for (int mi = 0; mi < FM; ++mi) {
+#pragma unroll
+      for (int ni = 0; ni < FN; ++ni) {
+        const int64_t np = n0 + ni * 32 + (r32 & ~1);   // even column of this lane's pair
+#pragma unroll
+        for (int r = 0; r < 8; ++r) {
+          // even lane: row register r; odd lane: row register r + 8
+          const float give = odd ? acc[mi][ni][r] : acc[mi][ni][r + 8];
+          const float got = quad_xor1(give);
+          const float own = odd ? acc[mi][ni][r + 8] : acc[mi][ni][r];
+          const float lo = odd ? got : own;   // column np
+          const float hi = odd ? own : got;   // column np + 1
+          const int rr = odd ? r + 8 : r;
+          const int64_t m = m0 + mi * 32 + 8 * (rr >> 2) + 4 * h + (rr & 3);
+          if (m >= row_end || np >= N) continue;
+          if constexpr ((OUT & kOutSwiGLU) != 0) {
+            store_out(Y, m * (N >> 1) + (np >> 1), silu_times(lo, hi), OUT);
+          } else {   // bf16 pair
+            uint16_t* y16 = reinterpret_cast<uint16_t*>(Y) + m * N + np;
+            if (np + 1 < N && (N & 1) == 0 && (reinterpret_cast<uintptr_t>(Y) & 3) == 0) {   // 4-byte aligned pair
+              *reinterpret_cast<uint32_t*>(y16) = (uint32_t)f32_to_bf16_rne(lo) | ((uint32_t)f32_to_bf16_rne(hi) << 16);
+            } else {
+              y16[0] = f32_to_bf16_rne(lo);
+              if (np + 1 < N) y16[1] = f32_to_bf16_rne(hi);
+            }
+          }
+        }
+      }
+    }
+  }
+}
+
+// bf16 / SwiGLU epilogue staged through LDS (the pipelined kernel's stages
+// are free after its K loop): per 32x32 accumulator block, the wave writes
+// its values to a [32][36]-float LDS tile (row-major, rows padded to keep
+// 16-byte alignment), then each lane reads 8 consecutive columns of one row
+// (two such pieces per lane) and stores them as 8 bf16 values (one 16-byte
+// store) or, for SwiGLU, the 4 results silu(gate) * up of those 4 (gate, up)
+// column pairs.  Two tiles per wave alternate, so one block's reads overlap
+// the next block's writes; the wave's LDS accesses complete in order, so a
+// tile is reused without a barrier.
+constexpr int kEpiStride = 36;                        // floats per LDS tile row
+constexpr int kEpiLdsBytes = 2 * 32 * kEpiStride * 4;  // per wave (two tiles)
+
+template <int OUT, int FM, int FN>
+__device__ __forceinline__ void store_wave_tile_lds(const v16f (&acc)[FM][FN], float* __restrict__ t,
+                                                    void* __restrict__ Y, int64_t m0, int64_t row_end, int64_t n0,
+                                                    int64_t N, int lane) {
+  static_assert(OUT != 0, "fp32 output is stored from the registers");
+  const int r32 = lane & 31, h = lane >> 5;
+#pragma unroll
+  for (int mi = 0; mi < FM; ++mi) {
+#pragma unroll
+    for (int ni = 0; ni < FN; ++ni) {
+      float* tt = t + ((mi * FN + ni) & 1) * (32 * kEpiStride);
+#pragma unroll
+      for (int r = 0; r < 16; ++r) tt[(8 * (r >> 2) + 4 * h + (r & 3)) * kEpiStride + r32] = acc[mi][ni][r];
+#pragma unroll
+      for (int it = 0; it < 2; ++it) {
+        const int item = lane + 64 * it;        // 32 rows x 4 pieces of 8 columns
+        const int row = item >> 2, c = (item & 3) * 8;
+        const float4 p0 = *reinterpret_cast<const float4*>(tt + row * kEpiStride + c);
+        const float4 p1 = *reinterpret_cast<const float4*>(tt + row * kEpiStride + c + 4);
+        const float v[8] = {p0.x, p0.y, p0.z, p0.w, p1.x, p1.y, p1.z, p1.w};
+        const int64_t m = m0 + mi * 32 + row, n = n0 + ni * 32 + c;
+        if (m >= row_end || n >= N) continue;
+        if constexpr ((OUT & kOutSwiGLU) != 0) {
+          const int64_t ldo = N >> 1, j0 = n >> 1;   // 4 output columns j0..j0+3
+          float o[4];
+#pragma unroll
+          for (int k = 0; k < 4; ++k) o[k] = silu_times(v[2 * k], v[2 * k + 1]);
+          if constexpr ((OUT & kOutBf16) != 0) {
+            uint16_t* yp = reinterpret_cast<uint16_t*>(Y) + m * ldo + j0;
+            if (n + 8 <= N && (reinterpret_cast<uintptr_t>(yp) & 7) == 0) {
+              uint2 q;
+              q.x = (uint32_t)f32_to_bf16_rne(o[0]) | ((uint32_t)f32_to_bf16_rne(o[1]) << 16);
+              q.y = (uint32_t)f32_to_bf16_rne(o[2]) | ((uint32_t)f32_to_bf16_rne(o[3]) << 16);
+              *reinterpret_cast<uint2*>(yp) = q;
+            } else {
+#pragma unroll
+              for (int k = 0; k < 4; ++k)
+                if (n + 2 * k < N) yp[k] = f32_to_bf16_rne(o[k]);
+            }
+          } else {
+            float* yp = reinterpret_cast<float*>(Y) + m * ldo + j0;
+            if (n + 8 <= N && (reinterpret_cast<uintptr_t>(yp) & 15) == 0) {
+              *reinterpret_cast<float4*>(yp) = make_float4(o[0], o[1], o[2], o[3]);
+            } else {
+#pragma unroll
+              for (int k = 0; k < 4; ++k)
+                if (n + 2 * k < N) yp[k] = o[k];
+            }
+          }
+        } else {   // bf16
+          uint16_t* yp = reinterpret_cast<uint16_t*>(Y) + m * N + n;
+          if (n + 8 <= N && (reinterpret_cast<uintptr_t>(yp) & 15) == 0) {
+            uint4 q;
+            q.x = (uint32_t)f32_to_bf16_rne(v[0]) | ((uint32_t)f32_to_bf16_rne(v[1]) << 16);
+            q.y = (uint32_t)f32_to_bf16_rne(v[2]) | ((uint32_t)f32_to_bf16_rne(v[3]) << 16);
+            q.z = (uint32_t)f32_to_bf16_rne(v[4]) | ((uint32_t)f32_to_bf16_rne(v[5]) << 16);
+            q.w = (uint32_t)f32_to_bf16_rne(v[6]) | ((uint32_t)f32_to_bf16_rne(v[7]) << 16);
+            *reinterpret_cast<uint4*>(yp) = q;
+          } else {
+#pragma unroll
+            for (int k = 0; k < 8; ++k)
+              if (n + k < N) yp[k] = f32_to_bf16_rne(v[k]);
+          }
+        }
+      }
+    }
+  }
+}
+
+template <int BM, int BN, int WAVES_M, int WAVES_N, int OUT = 0>
 __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_mxfp4_kernel(
     const uint8_t* __restrict__ A, const uint8_t* __restrict__ As, const uint8_t* __restrict__ B,
     const uint8_t* __restrict__ Bs, const int32_t* __restrict__ offsets, int E, int64_t M,
-    int64_t N, int64_t K, float* __restrict__ Y, int n_tiles_n) {
+    int64_t N, int64_t K, void* __restrict__ Y, int n_tiles_n) {
   using T = GemmTile<BM, BN, WAVES_M, WAVES_N>;
   __shared__ __attribute__((aligned(16))) uint8_t smA[2][BM * 128];
   __shared__ __attribute__((aligned(16))) uint8_t smB[2][BN * 128];
@@ -249,217 +404,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_mxfp4_kernel(
 #undef MACAQ_LOAD_TILE
 #undef MACAQ_STORE_TILE
 
-  // ---- epilogue: lane (r32, h) of 32x32 block holds column r32 and rows
-  // 8*(r/4) + 4*h + (r%4) for accumulator register r.
-#pragma unroll
-  for (int mi = 0; mi < T::kFM; ++mi) {
-#pragma unroll
-    for (int ni = 0; ni < T::kFN; ++ni) {
-      const int64_t n = n0 + wn * T::kTN + ni * 32 + r32;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int64_t m = row_begin + wm * T::kTM + mi * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
-        if (m < row_end && n < N) Y[m * N + n] = acc[mi][ni][r];
-      }
-    }
-  }
-}
-
-// ---------------------------------------------------------------------------
-// Direct-to-LDS variant.  Global -> LDS copies use gfx950's
-// global_load_lds_dwordx4 / _dword: lane i of one instruction writes bytes
-// [16i, 16i+16) (or [4i, 4i+4)) of a wave-uniform LDS destination, so a
-// 64-lane instruction fills one 1 KiB block (8 rows of a 128-byte K-tile
-// row) and no registers stage the data.  The lane picks its global source so
-// that the block receives the swizzled layout (position p of row r holds
-// chunk p ^ (r & 7)).  Rows past the tile's valid range and groups past K
-// read clamped (valid) addresses; their results are discarded (rows) or
-// their A codes are zeroed before the MFMA (groups of a K tail).
-// LDS per stage: A codes [BM][128], B codes [BN][128], A scales [BM][8],
-// B scales [BN][8]; two stages.
-template <int BM, int BN>
-struct LdsLayout {
-  static constexpr int kA = 0;
-  static constexpr int kB = BM * 128;
-  static constexpr int kAs = (BM + BN) * 128;
-  static constexpr int kBs = kAs + BM * 8;
-  static constexpr int kStage = kBs + BN * 8;
-};
-
-__device__ __forceinline__ void lds_copy16(const uint8_t* g, uint8_t* lds_block) {
-  __builtin_amdgcn_global_load_lds((const void*)g, (void*)lds_block, 16, 0, 0);
-}
-__device__ __forceinline__ void lds_copy4(const uint8_t* g, uint8_t* lds_block) {
-  __builtin_amdgcn_global_load_lds((const void*)g, (void*)lds_block, 4, 0, 0);
-}
-
-template <int BM, int BN, int WAVES_M, int WAVES_N>
-__global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void gemm_mxfp4_dlds_kernel(
-    const uint8_t* __restrict__ A, const uint8_t* __restrict__ As, const uint8_t* __restrict__ B,
-    const uint8_t* __restrict__ Bs, const int32_t* __restrict__ offsets, int E, int64_t M,
-    int64_t N, int64_t K, float* __restrict__ Y, int n_tiles_n) {
-  using T = GemmTile<BM, BN, WAVES_M, WAVES_N>;
-  using L = LdsLayout<BM, BN>;
-  constexpr int kWaves = WAVES_M * WAVES_N;
-  constexpr int kCodeBlocks = (BM + BN) / 8;        // 1 KiB blocks per stage
-  constexpr int kScaleBlocks = (BM + BN) * 8 / 256; // 256-byte blocks per stage
-  static_assert(kCodeBlocks % kWaves == 0 && kScaleBlocks % kWaves == 0, "blocks must split over waves");
-  extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];
-
-  // ---- tile -> (expert, rows, columns)
-  const int tn = (int)(blockIdx.x % (unsigned)n_tiles_n);
-  int64_t slot = blockIdx.x / (unsigned)n_tiles_n;
-  int e = 0;
-  int64_t row_begin = 0, row_end = M;
-  if (offsets != nullptr) {
-    for (e = 0; e < E; ++e) {
-      const int64_t b = offsets[e], en = offsets[e + 1];
-      const int64_t t = (en - b + BM - 1) / BM;
-      if (slot < t) {
-        row_begin = b + slot * BM;
-        row_end = en;
-        break;
-      }
-      slot -= t;
-    }
-    if (e == E) return;
-  } else {
-    row_begin = slot * BM;
-    if (row_begin >= M) return;
-  }
-  const int64_t n0 = (int64_t)tn * BN;
-  const int64_t KB = K >> 1;
-  const int64_t KG = K >> 5;
-  const uint8_t* Bx = B + (int64_t)e * N * KB;
-  const uint8_t* Bsx = Bs + (int64_t)e * N * KG;
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = tid >> 6;
-  const int wm = wave / WAVES_N;
-  const int wn = wave % WAVES_N;
-  const int r32 = lane & 31;
-  const int h = lane >> 5;
-
-  // ---- per-lane sources of this wave's copy blocks (K-tile 0; +128 B per tile)
-  constexpr int kCB = kCodeBlocks / kWaves;
-  constexpr int kSB = kScaleBlocks / kWaves;
-  const uint8_t* csrc[kCB];
-  int cdst[kCB];
-#pragma unroll
-  for (int i = 0; i < kCB; ++i) {
-    const int blk = wave * kCB + i;
-    const int row = blk * 8 + (lane >> 3);           // row within A rows then B rows
-    const int c = (lane & 7) ^ (lane >> 3);          // chunk stored at position lane & 7
-    if (row < BM) {
-      int64_t gr = row_begin + row;
-      if (gr >= row_end) gr = row_end - 1;
-      csrc[i] = A + gr * KB + c * 16;
-    } else {
-      int64_t gn = n0 + (row - BM);
-      if (gn >= N) gn = N - 1;
-      csrc[i] = Bx + gn * KB + c * 16;
-    }
-    cdst[i] = blk * 1024;
-  }
-  const uint8_t* ssrc[kSB];
-  int sdst[kSB];
-#pragma unroll
-  for (int i = 0; i < kSB; ++i) {
-    const int blk = wave * kSB + i;
-    const int d = blk * 64 + lane;                   // dword index over A then B scale rows
-    const int row = d >> 1, half = d & 1;
-    if (row < BM) {
-      int64_t gr = row_begin + row;
-      if (gr >= row_end) gr = row_end - 1;
-      ssrc[i] = As + gr * KG + half * 4;
-    } else {
-      int64_t gn = n0 + (row - BM);
-      if (gn >= N) gn = N - 1;
-      ssrc[i] = Bsx + gn * KG + half * 4;
-    }
-    sdst[i] = L::kAs + blk * 256;
-  }
-  const int my_chunk_c = (lane & 7) ^ (lane >> 3);
-  const int my_half = lane & 1;
-
-  auto issue = [&](int kt, int st) {
-    uint8_t* base = smem + st * L::kStage;
-    const int64_t g0 = (int64_t)kt * 8;
-    // clamp groups past K to the last group (their A codes are zeroed later)
-    const int64_t cg = (g0 + my_chunk_c < KG) ? g0 : (KG - 1 - my_chunk_c);
-    const int64_t sg = (g0 + my_half * 4 < KG) ? g0 : (KG - 4 - my_half * 4);
-#pragma unroll
-    for (int i = 0; i < kCB; ++i) lds_copy16(csrc[i] + cg * 16, base + cdst[i]);
-#pragma unroll
-    for (int i = 0; i < kSB; ++i) lds_copy4(ssrc[i] + sg, base + sdst[i]);
-  };
-
-  v16f acc[T::kFM][T::kFN];
-#pragma unroll
-  for (int mi = 0; mi < T::kFM; ++mi)
-#pragma unroll
-    for (int ni = 0; ni < T::kFN; ++ni)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[mi][ni][r] = 0.0f;
-
-  const int nk = (int)((K + 255) / 256);
-  issue(0, 0);
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
-
-  const int sw = r32 & 7;
-  for (int kt = 0; kt < nk; ++kt) {
-    const int st = kt & 1;
-    if (kt + 1 < nk) issue(kt + 1, st ^ 1);
-    const uint8_t* base = smem + st * L::kStage;
-    // groups 4..7 of a K tail of 128 are past K: zero lane half 1's A codes
-    const bool zero_hi = (h == 1) && ((int64_t)kt * 8 + 4 >= KG);
-
-    uint32_t sa[T::kFM], sb[T::kFN];
-    int rowA[T::kFM], rowB[T::kFN];
-#pragma unroll
-    for (int mi = 0; mi < T::kFM; ++mi) {
-      rowA[mi] = wm * T::kTM + mi * 32 + r32;
-      sa[mi] = *reinterpret_cast<const uint32_t*>(base + L::kAs + rowA[mi] * 8 + h * 4);
-    }
-#pragma unroll
-    for (int ni = 0; ni < T::kFN; ++ni) {
-      rowB[ni] = wn * T::kTN + ni * 32 + r32;
-      sb[ni] = *reinterpret_cast<const uint32_t*>(base + L::kBs + rowB[ni] * 8 + h * 4);
-    }
-    uint4 fa[T::kFM], fb[T::kFN];
-#define MACAQ_DLDS_SUBSTEP(J)                                                                        \
-  {                                                                                                  \
-    _Pragma("unroll") for (int mi = 0; mi < T::kFM; ++mi) {                                          \
-      fa[mi] = *reinterpret_cast<const uint4*>(base + L::kA + rowA[mi] * 128 + (((4 * h + (J)) ^ sw) << 4)); \
-      if (zero_hi) fa[mi] = make_uint4(0, 0, 0, 0);                                                  \
-    }                                                                                                \
-    _Pragma("unroll") for (int ni = 0; ni < T::kFN; ++ni) fb[ni] =                                   \
-        *reinterpret_cast<const uint4*>(base + L::kB + rowB[ni] * 128 + (((4 * h + (J)) ^ sw) << 4)); \
-    mfma_substep<J>(acc, fa, fb, sa, sb);                                                            \
-  }
-    MACAQ_DLDS_SUBSTEP(0)
-    MACAQ_DLDS_SUBSTEP(1)
-    MACAQ_DLDS_SUBSTEP(2)
-    MACAQ_DLDS_SUBSTEP(3)
-#undef MACAQ_DLDS_SUBSTEP
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-  }
-
-#pragma unroll
-  for (int mi = 0; mi < T::kFM; ++mi) {
-#pragma unroll
-    for (int ni = 0; ni < T::kFN; ++ni) {
-      const int64_t n = n0 + wn * T::kTN + ni * 32 + r32;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int64_t m = row_begin + wm * T::kTM + mi * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
-        if (m < row_end && n < N) Y[m * N + n] = acc[mi][ni][r];
-      }
-    }
-  }
+  store_wave_tile<OUT>(acc, Y, row_begin + wm * T::kTM, row_end, n0 + wn * T::kTN, N, r32, h);
 }
 
 // ---------------------------------------------------------------------------
@@ -519,11 +464,11 @@ __device__ __forceinline__ void tile_of_block(int bid, int ntiles, int tiles_m, 
   *tn = in / gm;
 }
 
-template <int BM, int BN, int WAVES_M, int WAVES_N, int BK, int STAGES, int MINB = 1>
+template <int BM, int BN, int WAVES_M, int WAVES_N, int BK, int STAGES, int MINB = 1, int OUT = 0>
 __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, MINB) void gemm_mxfp4_pipe_kernel(
     const uint8_t* __restrict__ A, const uint8_t* __restrict__ As, const uint8_t* __restrict__ B,
     const uint8_t* __restrict__ Bs, const int32_t* __restrict__ offsets, int E, int64_t M,
-    int64_t N, int64_t K, float* __restrict__ Y, int tiles_m, int tiles_n, int group_m) {
+    int64_t N, int64_t K, void* __restrict__ Y, int tiles_m, int tiles_n, int group_m) {
   using T = GemmTile<BM, BN, WAVES_M, WAVES_N>;
   using L = PipeLayout<BM, BN, BK, 1>;
   constexpr int kWaves = WAVES_M * WAVES_N;
@@ -695,223 +640,13 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, MINB) void gemm_mxfp4_pipe_
 #undef MACAQ_PIPE_SUBSTEP
   }
 
-  // ---- epilogue: lane (r32, h) of a 32x32 block holds column r32 and rows
-  // 8*(r/4) + 4*h + (r%4) of accumulator register r
-  const bool interior = (row_begin + BM <= row_end) && (n0 + BN <= N);
-#pragma unroll
-  for (int mi = 0; mi < T::kFM; ++mi) {
-#pragma unroll
-    for (int ni = 0; ni < T::kFN; ++ni) {
-      const int64_t n = n0 + wn * T::kTN + ni * 32 + r32;
-      const int64_t mb = row_begin + wm * T::kTM + mi * 32 + 4 * h;
-      if (interior) {
-        float* yp = Y + mb * N + n;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) yp[(8 * (r >> 2) + (r & 3)) * N] = acc[mi][ni][r];
-      } else {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int64_t m = mb + 8 * (r >> 2) + (r & 3);
-          if (m < row_end && n < N) Y[m * N + n] = acc[mi][ni][r];
-        }
-      }
-    }
-  }
-}
-
-// ---------------------------------------------------------------------------
-// Two-stage, BK = 256 variant with register double-buffering of the MFMA
-// fragments: the LDS reads of sub-step j+1 are issued before the MFMAs of
-// sub-step j, so with one wave per SIMD the LDS latency hides behind the
-// matrix cores.  The copy of the next K-tile is issued unconditionally (the
-// last iteration re-reads the final tile into the idle buffer) so that the
-// loop body is a single basic block the scheduler can interleave.
-// SCHED != 0 adds scheduling groups that alternate LDS reads and MFMAs.
-template <int BM, int BN, int WAVES_M, int WAVES_N, int SCHED>
-__global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void gemm_mxfp4_db_kernel(
-    const uint8_t* __restrict__ A, const uint8_t* __restrict__ As, const uint8_t* __restrict__ B,
-    const uint8_t* __restrict__ Bs, const int32_t* __restrict__ offsets, int E, int64_t M,
-    int64_t N, int64_t K, float* __restrict__ Y, int tiles_m, int tiles_n, int group_m) {
-  constexpr int BK = 256;
-  using T = GemmTile<BM, BN, WAVES_M, WAVES_N>;
-  using L = PipeLayout<BM, BN, BK, 1>;
-  constexpr int kWaves = WAVES_M * WAVES_N;
-  constexpr int kCB = (L::kCodeBlocks + kWaves - 1) / kWaves;
-  constexpr int kSB = (L::kScaleBlocks + kWaves - 1) / kWaves;
-  extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];
-
-  if ((int)blockIdx.x >= tiles_m * tiles_n) return;
-  int tm, tn;
-  tile_of_block((int)blockIdx.x, tiles_m * tiles_n, tiles_m, tiles_n, group_m, &tm, &tn);
-  int64_t slot = tm;
-  int e = 0;
-  int64_t row_begin = 0, row_end = M;
-  if (offsets != nullptr) {
-    for (e = 0; e < E; ++e) {
-      const int64_t b = offsets[e], en = offsets[e + 1];
-      const int64_t t = (en - b + BM - 1) / BM;
-      if (slot < t) {
-        row_begin = b + slot * BM;
-        row_end = en;
-        break;
-      }
-      slot -= t;
-    }
-    if (e == E) return;
+  if constexpr (OUT == 0) {
+    store_wave_tile<0>(acc, Y, row_begin + wm * T::kTM, row_end, n0 + wn * T::kTN, N, r32, h);
   } else {
-    row_begin = slot * BM;
-    if (row_begin >= M) return;
-  }
-  const int64_t n0 = (int64_t)tn * BN;
-  if (n0 >= N) return;
-  const int64_t KB = K >> 1;
-  const int64_t KG = K >> 5;
-  const uint8_t* Bx = B + (int64_t)e * N * KB;
-  const uint8_t* Bsx = Bs + (int64_t)e * N * KG;
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wave / WAVES_N;
-  const int wn = wave % WAVES_N;
-  const int r32 = lane & 31;
-  const int h = lane >> 5;
-  const uint32_t lds_base = (uint32_t)(uintptr_t)smem;
-
-  const uint8_t* csrc[kCB];
-#pragma unroll
-  for (int i = 0; i < kCB; ++i) {
-    const int blk = (wave * kCB + i) % L::kCodeBlocks;
-    const int row = blk * 8 + (lane >> 3);
-    const int c = (lane & 7) ^ L::swz(row);
-    if (row < BM) {
-      int64_t gr = row_begin + row;
-      if (gr >= row_end) gr = row_end - 1;
-      csrc[i] = A + gr * KB + c * 16;
-    } else {
-      int64_t gn = n0 + (row - BM);
-      if (gn >= N) gn = N - 1;
-      csrc[i] = Bx + gn * KB + c * 16;
-    }
-  }
-  const uint8_t* ssrc[kSB];
-#pragma unroll
-  for (int i = 0; i < kSB; ++i) {
-    const int blk = (wave * kSB + i) % L::kScaleBlocks;
-    const int d = blk * 64 + lane;
-    const int row = d >> 1, part = d & 1;
-    if (row < BM) {
-      int64_t gr = row_begin + row;
-      if (gr >= row_end) gr = row_end - 1;
-      ssrc[i] = As + gr * KG + part * 4;
-    } else {
-      int64_t gn = n0 + (row - BM);
-      if (gn >= N) gn = N - 1;
-      ssrc[i] = Bsx + gn * KG + part * 4;
-    }
-  }
-  // K tail of 128 (K % 256 == 128): chunks / scale dwords past K read the
-  // last valid ones instead; lane half 1's A codes are zeroed for that tile.
-  const int my_c = (lane & 7) ^ L::swz(lane >> 3);
-  const int nk = (int)((K + BK - 1) / BK);
-
-  auto issue = [&](int kt, int st) {
-    const uint32_t base = lds_base + (uint32_t)(st * L::kStage);
-    const int64_t g0 = (int64_t)kt * 8;
-    const int64_t cofs = ((g0 + my_c < KG) ? g0 : (KG - 1 - my_c)) * 16;
-#pragma unroll
-    for (int i = 0; i < kCB; ++i)
-      dma16(csrc[i] + cofs, base + (uint32_t)(L::kA + ((wave * kCB + i) % L::kCodeBlocks) * 1024));
-#pragma unroll
-    for (int i = 0; i < kSB; ++i) {
-      const int part = lane & 1;
-      const int64_t sofs = (g0 + part * 4 < KG) ? g0 : (KG - 4 - part * 4);
-      dma4(ssrc[i] + sofs, base + (uint32_t)(L::kAs + ((wave * kSB + i) % L::kScaleBlocks) * 256));
-    }
-  };
-
-  v16f acc[T::kFM][T::kFN];
-#pragma unroll
-  for (int mi = 0; mi < T::kFM; ++mi)
-#pragma unroll
-    for (int ni = 0; ni < T::kFN; ++ni)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[mi][ni][r] = 0.0f;
-
-  int rowA[T::kFM], rowB[T::kFN];
-#pragma unroll
-  for (int mi = 0; mi < T::kFM; ++mi) rowA[mi] = wm * T::kTM + mi * 32 + r32;
-#pragma unroll
-  for (int ni = 0; ni < T::kFN; ++ni) rowB[ni] = wn * T::kTN + ni * 32 + r32;
-  const int sw = L::swz(r32);
-
-  issue(0, 0);
-  for (int kt = 0; kt < nk; ++kt) {
-    wait_vmcnt<0>();
-    __builtin_amdgcn_s_barrier();
-    issue(kt + 1 < nk ? kt + 1 : kt, (kt + 1) & 1);
-    const uint8_t* base = smem + (kt & 1) * L::kStage;
-    const bool zero_hi = (h == 1) && ((int64_t)kt * 8 + 4 >= KG);
-    uint32_t sa[T::kFM], sb[T::kFN];
-#pragma unroll
-    for (int mi = 0; mi < T::kFM; ++mi) sa[mi] = *reinterpret_cast<const uint32_t*>(base + L::kAs + rowA[mi] * 8 + h * 4);
-#pragma unroll
-    for (int ni = 0; ni < T::kFN; ++ni) sb[ni] = *reinterpret_cast<const uint32_t*>(base + L::kBs + rowB[ni] * 8 + h * 4);
-    uint4 fa[2][T::kFM], fb[2][T::kFN];
-    auto load_frags = [&](int j, int buf) {
-#pragma unroll
-      for (int mi = 0; mi < T::kFM; ++mi) {
-        fa[buf][mi] = *reinterpret_cast<const uint4*>(base + L::kA + rowA[mi] * 128 + (((4 * h + j) ^ sw) << 4));
-        if (zero_hi) fa[buf][mi] = make_uint4(0, 0, 0, 0);
-      }
-#pragma unroll
-      for (int ni = 0; ni < T::kFN; ++ni)
-        fb[buf][ni] = *reinterpret_cast<const uint4*>(base + L::kB + rowB[ni] * 128 + (((4 * h + j) ^ sw) << 4));
-    };
-    load_frags(0, 0);
-    load_frags(1, 1);
-    mfma_substep<0>(acc, fa[0], fb[0], sa, sb);
-    if (SCHED) {
-#pragma unroll
-      for (int q = 0; q < T::kFM + T::kFN; ++q) {
-        __builtin_amdgcn_sched_group_barrier(0x008, (T::kFM * T::kFN) / (T::kFM + T::kFN), 0);
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-      }
-    }
-    load_frags(2, 0);
-    mfma_substep<1>(acc, fa[1], fb[1], sa, sb);
-    if (SCHED) {
-#pragma unroll
-      for (int q = 0; q < T::kFM + T::kFN; ++q) {
-        __builtin_amdgcn_sched_group_barrier(0x008, (T::kFM * T::kFN) / (T::kFM + T::kFN), 0);
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-      }
-    }
-    load_frags(3, 1);
-    mfma_substep<2>(acc, fa[0], fb[0], sa, sb);
-    mfma_substep<3>(acc, fa[1], fb[1], sa, sb);
-  }
-  wait_vmcnt<0>();
-
-  const bool interior = (row_begin + BM <= row_end) && (n0 + BN <= N);
-#pragma unroll
-  for (int mi = 0; mi < T::kFM; ++mi) {
-#pragma unroll
-    for (int ni = 0; ni < T::kFN; ++ni) {
-      const int64_t n = n0 + wn * T::kTN + ni * 32 + r32;
-      const int64_t mb = row_begin + wm * T::kTM + mi * 32 + 4 * h;
-      if (interior) {
-        float* yp = Y + mb * N + n;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) yp[(8 * (r >> 2) + (r & 3)) * N] = acc[mi][ni][r];
-      } else {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int64_t m = mb + 8 * (r >> 2) + (r & 3);
-          if (m < row_end && n < N) Y[m * N + n] = acc[mi][ni][r];
-        }
-      }
-    }
+    static_assert(STAGES * L::kStage >= kWaves * kEpiLdsBytes, "epilogue tiles must fit in the stages");
+    __syncthreads();   // every wave is done reading the last K-tile
+    store_wave_tile_lds<OUT>(acc, reinterpret_cast<float*>(smem + wave * kEpiLdsBytes), Y, row_begin + wm * T::kTM,
+                             row_end, n0 + wn * T::kTN, N, lane);
   }
 }
 

@@ -147,6 +147,28 @@ __device__ __forceinline__ void dma4(const uint8_t* g, uint32_t lds_addr) {
   asm volatile("global_load_lds_dword %0, off" ::"v"(g), "{m0}"(lds_addr) : "memory");
 }
 
+// ---- GEMM output: fp32 or bf16, optionally SwiGLU over gate/up column pairs
+//
+// Output mode bits: kOutBf16 stores round-to-nearest-even bf16 instead of
+// fp32; kOutSwiGLU stores, for each pair of accumulated columns (2j, 2j+1) =
+// (gate, up), silu(gate) * up = gate / (1 + exp(-gate)) * up at column j of
+// a [M][N/2] output.
+constexpr int kOutBf16 = 1;
+constexpr int kOutSwiGLU = 2;
+
+__device__ __forceinline__ uint16_t f32_to_bf16_rne(float v) {
+  const uint32_t u = __float_as_uint(v);
+  if ((u & 0x7FFFFFFFu) > 0x7F800000u) return (uint16_t)((u >> 16) | 0x40u);   // NaN stays NaN
+  return (uint16_t)((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
+}
+
+__device__ __forceinline__ float silu_times(float g, float u) { return g / (1.0f + expf(-g)) * u; }
+
+__device__ __forceinline__ void store_out(void* y, int64_t i, float v, int mode) {
+  if (mode & kOutBf16) reinterpret_cast<uint16_t*>(y)[i] = f32_to_bf16_rne(v);
+  else reinterpret_cast<float*>(y)[i] = v;
+}
+
 __host__ __device__ constexpr int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 }  // namespace macaq

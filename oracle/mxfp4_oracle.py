@@ -53,6 +53,9 @@ design notes):
 Floating-point arithmetic that decides a code (the transform) is done in
 fp32 exactly as stated above, because the codes must be bit-exact; the GEMM
 is the dequantized product in fp64.
+
+The last section (bf16 output, SwiGLU over a gate/up projection) restates a
+consumer step after the layer; it is not from the pages.
 """
 from __future__ import annotations
 
@@ -288,3 +291,40 @@ def within_tolerance(y: np.ndarray, y_ref: np.ndarray, S: np.ndarray, rtol: floa
     nref = float(np.linalg.norm(y_ref))
     normwise = float(np.linalg.norm(y - y_ref) / nref) if nref > 0 else float(np.linalg.norm(y))
     return (worst <= rtol and normwise <= rtol), worst, normwise
+
+
+# --------------------------------------------------------------------------
+# consumer step after the layer (not part of the pages' method: what a
+# decoder layer does next with y -- store it as bf16, or combine a gate/up
+# projection with SwiGLU).  Readings: R21 bf16 is round-to-nearest-even of
+# the fp32 result; R22 weight rows (2j, 2j+1) are (gate, up) of output
+# column j, out = silu(g) * u with silu(g) = g / (1 + exp(-g)).
+# --------------------------------------------------------------------------
+
+def round_bf16(v) -> np.ndarray:
+    """fp32 values -> the nearest bf16 value (ties to even mantissa), as
+    float32 (finite inputs)."""
+    b = np.asarray(v, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    r = ((b + 0x7FFF + ((b >> 16) & 1)) >> 16) << 16
+    return r.astype(np.uint32).view(np.float32)
+
+
+def swiglu(y) -> np.ndarray:
+    """out[:, j] = silu(y[:, 2j]) * y[:, 2j+1], in fp64."""
+    y = np.asarray(y, dtype=np.float64)
+    g, u = y[:, 0::2], y[:, 1::2]
+    with np.errstate(over="ignore"):
+        return g / (1.0 + np.exp(-g)) * u
+
+
+def swiglu_bound(y_ref: np.ndarray, S: np.ndarray, rtol: float = 1e-5) -> np.ndarray:
+    """Elementwise bound on |swiglu(y) - swiglu(y_ref)| when each GEMM output
+    is within rtol * S of y_ref, plus fp32 rounding of the epilogue: silu has
+    |silu'| <= 1.1, so |d(silu(g) u)| <= 1.1 dg (|u| + du) + |silu(g)| du, and
+    the fp32 exp, add, divide and multiply add at most 8 units of 2^-24 of
+    the result (relative)."""
+    g, u = y_ref[:, 0::2], y_ref[:, 1::2]
+    dg, du = rtol * S[:, 0::2], rtol * S[:, 1::2]
+    with np.errstate(over="ignore"):   # exp(-g) = inf for very negative g gives silu = -0
+        sg = g / (1.0 + np.exp(-g))
+    return 1.1 * dg * (np.abs(u) + du) + np.abs(sg) * du + 8 * 2.0 ** -24 * np.abs(sg * u) + 1e-30

@@ -144,3 +144,17 @@ def test_forced_fused_path_refuses_what_it_cannot_serve():
     assert lin(A16, 0, A16, None, 1, A16, A16, 1, 512, 384, A16, None, 0, mx.PATH_FUSED, None) == UNSUPPORTED
     # M > 32 is not a decode shape
     assert lin(A16, 0, A16, None, 1, A16, A16, 33, 512, 1024, A16, None, 0, mx.PATH_FUSED, None) == UNSUPPORTED
+
+
+def test_output_dtype_and_epilogue_validation():
+    mx.lib()
+    ge = mx.macaq_gemm_ex
+    # unknown y dtype, unknown epilogue, SwiGLU with odd N, misaligned bf16/fp32 y
+    assert ge(A16, A16, None, 1, A16, A16, 4, 8, 256, A16, 7, 0, None, 0, None) == UNSUPPORTED
+    assert ge(A16, A16, None, 1, A16, A16, 4, 8, 256, A16, 1, 5, None, 0, None) == INVALID
+    assert ge(A16, A16, None, 1, A16, A16, 4, 9, 256, A16, 1, 1, None, 0, None) == INVALID
+    assert ge(A16, A16, None, 1, A16, A16, 4, 8, 256, A16 + 1, 0, 0, None, 0, None) == INVALID
+    assert ge(A16, A16, None, 1, A16, A16, 4, 8, 256, A16 + 2, 1, 0, None, 0, None) == INVALID
+    assert ge(A16, A16, None, 1, A16, A16, 0, 8, 256, A16 + 2, 0, 1, None, 0, None) == OK   # M == 0: no-op
+    le = mx.macaq_linear_ex
+    assert le(A16, 0, A16, None, 1, A16, A16, 4, 9, 256, A16, 0, 1, None, 0, 0, None) == INVALID

@@ -352,3 +352,42 @@ def test_within_tolerance_rejects_planted_error():
     y2 = y.copy()
     y2[3, 4] += 1e-3
     assert not oracle.within_tolerance(y2, y, S)[0]
+
+
+# ---------------------------------------------------------------- consumer step: bf16 output, SwiGLU
+
+def test_round_bf16_matches_torch_and_breaks_ties_to_even():
+    import torch
+    rng = np.random.default_rng(11)
+    v = (rng.standard_normal(200000) * np.exp2(rng.integers(-30, 30, 200000))).astype(np.float32)
+    ref = torch.from_numpy(v).to(torch.bfloat16).to(torch.float32).numpy()
+    assert np.array_equal(oracle.round_bf16(v), ref)
+    # exact halfway cases: 1 + 2^-8 lies between bf16 1 and 1 + 2^-7 -> even (1);
+    # 1 + 3*2^-8 lies between 1 + 2^-7 and 1 + 2^-6 -> even (1 + 2^-6)
+    half = np.array([1 + 2.0 ** -8, 1 + 3 * 2.0 ** -8, -(1 + 2.0 ** -8)], dtype=np.float32)
+    assert np.array_equal(oracle.round_bf16(half), np.array([1.0, 1 + 2.0 ** -6, -1.0], dtype=np.float32))
+
+
+def test_swiglu_matches_logistic_and_closed_forms():
+    from scipy.special import expit
+    rng = np.random.default_rng(12)
+    y = rng.standard_normal((7, 64)) * 4
+    g, u = y[:, 0::2], y[:, 1::2]
+    np.testing.assert_allclose(oracle.swiglu(y), g * expit(g) * u, rtol=1e-13, atol=1e-300)
+    assert oracle.swiglu(np.array([[0.0, 5.0]]))[0, 0] == 0.0
+    assert oracle.swiglu(np.array([[60.0, 2.0]]))[0, 0] == pytest.approx(120.0, rel=1e-12)
+    assert abs(oracle.swiglu(np.array([[-60.0, 2.0]]))[0, 0]) < 1e-20
+    # silu(1) = 1 / (1 + e^-1)
+    assert oracle.swiglu(np.array([[1.0, 1.0]]))[0, 0] == pytest.approx(1 / (1 + np.exp(-1.0)), rel=1e-15)
+
+
+def test_swiglu_bound_covers_perturbations_within_the_gemm_tolerance():
+    rng = np.random.default_rng(13)
+    y = rng.standard_normal((50, 40)) * 3
+    S = np.abs(y) * 5 + 1
+    y_pert = y + 1e-5 * S * rng.uniform(-1, 1, y.shape)
+    d = np.abs(oracle.swiglu(y_pert) - oracle.swiglu(y))
+    assert np.all(d <= oracle.swiglu_bound(y, S))
+    # and the bound is not vacuous: a 10x larger perturbation breaks it somewhere
+    y_far = y + 1e-4 * S
+    assert np.any(np.abs(oracle.swiglu(y_far) - oracle.swiglu(y)) > oracle.swiglu_bound(y, S))
