@@ -25,6 +25,14 @@ written from these sources (cited by page title and section):
   absorbed into the weights so the layer's external basis is unchanged.
 * [rtn]       "MACaQ Enables Streaming ..." section "Flip-Refinement":
   round-to-nearest maps a value to the numerically closest FP4 code.
+* [flip]      same page, section "Flip-Refinement: optimizing FP4 codes with
+  second-order information": the quantization loss of a vector is taken as
+  one half of (x - q)^T H (x - q), H the Hessian of the layer input from
+  calibration data.
+* [ablation]  "华为开源MACaQ:本地量化提速3倍", section "Flip-Refinement:不重算,
+  只改最值得改的 4-bit 数值": the Llama-3-8B ablation lists a Hessian exponent
+  search as the first step above plain round-to-nearest; the Hessian comes
+  from calibration statistics of the layer input.
 
 Readings taken where the pages are silent (each is also listed in the
 design notes):
@@ -49,13 +57,32 @@ design notes):
       two codes per byte, the even element in the low nibble.
 * R15 row-major layouts: codes [rows][K/2], scales [rows][K/32].
 * R5  weights use r = fp32(1 / s) (IEEE division) in place of s.
+* R23 the Hessian is that of the layer output error with respect to a
+      transformed weight row: H_e = X'^T X' over expert e's calibration rows,
+      X' the fp32 x' of the online transform.  The factor 2 and any division
+      by the token count are left out (a positive factor changes no choice).
+* R24 Hessian exponent search (the pages name it, give no rule): per weight
+      group the candidates are the plain byte b0 (R7) and b0 + 1, which stops
+      the saturation of values above 6 * 2^e at the cost of resolution.  Each
+      candidate's codes follow R8-R10; its error is q = d^T H_gg d with
+      d = x' - dequant(codes) and H_gg the group's 32x32 diagonal block of H
+      (a group's scale only moves that group's codes; cross-group terms are
+      left out so that every group is decided on its own).  b0 + 1 is kept
+      only when its q is strictly smaller.
+* R25 q is computed in fp64 in a fixed order (inner sums over j ascending,
+      then the outer sum over i ascending, no fused multiply-add), so that
+      the choice is reproducible; d is exact in fp64 (at most 28 significant
+      bits) and so is every product H_ij d_j.
 
 Floating-point arithmetic that decides a code (the transform) is done in
 fp32 exactly as stated above, because the codes must be bit-exact; the GEMM
 is the dequantized product in fp64.
 
-The last section (bf16 output, SwiGLU over a gate/up projection) restates a
-consumer step after the layer; it is not from the pages.
+The offline section (Hessian, exponent search) follows [flip] and
+[ablation] with readings R23-R25; its decisions are pinned by exact rational
+arithmetic in the tests.  The last section (bf16 output, SwiGLU over a
+gate/up projection) restates a consumer step after the layer; it is not from
+the pages.
 """
 from __future__ import annotations
 
@@ -161,14 +188,23 @@ def quantize_mxfp4(xp: np.ndarray) -> tuple[np.ndarray, np.ndarray]:
     g = xp.reshape(R, K // GROUP, GROUP)
     amax = np.abs(g).max(axis=-1)
     scales = e8m0_scale(amax)
+    return pack_codes(encode_groups(g, scales)), scales
+
+
+def encode_groups(g: np.ndarray, scales: np.ndarray) -> np.ndarray:
+    """4-bit codes of fp32 groups g [..., 32] at given scale bytes [...]:
+    sign << 3 | nearest E2M1 index of |x'| / 2^(b-127) (R8-R10, R14)."""
     # |x'| / 2^(b-127), computed as a multiply by an exact power of two in fp32
     inv = np.ldexp(np.float32(1.0), 127 - scales.astype(np.int32)).astype(np.float32)
     v = (np.abs(g) * inv[..., None]).astype(np.float32)
     mag = e2m1_nearest(v)
-    code = (np.signbit(g).astype(np.uint8) << 3) | mag
-    code = code.reshape(R, K)
-    packed = (code[:, 0::2] | (code[:, 1::2] << 4)).astype(np.uint8)
-    return packed, scales
+    return (np.signbit(g).astype(np.uint8) << 3) | mag
+
+
+def pack_codes(code: np.ndarray) -> np.ndarray:
+    """Codes [R, G, 32] -> bytes [R, 16 G], the even element in the low nibble."""
+    code = code.reshape(code.shape[0], -1)
+    return (code[:, 0::2] | (code[:, 1::2] << 4)).astype(np.uint8)
 
 
 def unpack_codes(packed: np.ndarray) -> np.ndarray:
@@ -291,6 +327,99 @@ def within_tolerance(y: np.ndarray, y_ref: np.ndarray, S: np.ndarray, rtol: floa
     nref = float(np.linalg.norm(y_ref))
     normwise = float(np.linalg.norm(y - y_ref) / nref) if nref > 0 else float(np.linalg.norm(y))
     return (worst <= rtol and normwise <= rtol), worst, normwise
+
+
+# --------------------------------------------------------------------------
+# offline: Hessian of the layer input and the Hessian exponent search for the
+# weights' E8M0 bytes ([flip], [ablation]; readings R23-R25)
+# --------------------------------------------------------------------------
+
+def hessian(xcal, s, offsets=None) -> np.ndarray:
+    """H_e = X'_e^T X'_e over the calibration rows of expert e, in fp64 (R23).
+
+    xcal: [T, K] bf16 bits (uint16) or float32, rows sorted by expert;
+    s: [E, K] float32; offsets: [E+1] row offsets (None for E = 1).  X' is
+    the fp32 activation after the online transform (the x' that the online
+    path quantizes).  Returns [E, K, K] float64; an expert without rows gets 0.
+    """
+    xf = as_f32(xcal)
+    T, K = xf.shape
+    s = np.asarray(s, dtype=np.float32).reshape(-1, K)
+    E = s.shape[0]
+    if offsets is None:
+        assert E == 1
+        offsets = np.array([0, T])
+    offsets = np.asarray(offsets, dtype=np.int64)
+    H = np.zeros((E, K, K))
+    for e in range(E):
+        r0, r1 = int(offsets[e]), int(offsets[e + 1])
+        if r1 > r0:
+            xp = transform(xf[r0:r1], s[e]).astype(np.float64)
+            H[e] = xp.T @ xp
+    return H
+
+
+def diagonal_blocks(h: np.ndarray) -> np.ndarray:
+    """[K, K] -> the K/32 diagonal 32x32 blocks [K/32, 32, 32]."""
+    K = h.shape[-1]
+    G = K // GROUP
+    return np.stack([h[GROUP * g:GROUP * (g + 1), GROUP * g:GROUP * (g + 1)] for g in range(G)])
+
+
+def dequantize_groups(code: np.ndarray, scales: np.ndarray) -> np.ndarray:
+    """Exact fp64 values of codes [..., 32] at scale bytes [...]."""
+    mag = E2M1_VALUES[code & 7]
+    sign = np.where(code & 8, -1.0, 1.0)
+    return sign * mag * np.ldexp(1.0, scales.astype(np.int64) - 127)[..., None]
+
+
+def hessian_error(delta: np.ndarray, hb: np.ndarray) -> np.ndarray:
+    """q = delta^T Hb delta per group, fp64, in the fixed order of R25:
+    u_i = sum_j Hb[i, j] delta_j (j = 0, 1, ..., 31), then q = sum_i delta_i
+    u_i (i = 0, 1, ..., 31), every product and sum rounded on its own.
+
+    delta: [..., G, 32] float64; hb: [G, 32, 32] (cast to float64).
+    """
+    hb = np.asarray(hb, dtype=np.float64)
+    q = np.zeros(delta.shape[:-1])
+    for i in range(GROUP):
+        u = np.zeros(delta.shape[:-1])
+        for j in range(GROUP):
+            u = u + hb[:, i, j] * delta[..., j]
+        q = q + delta[..., i] * u
+    return q
+
+
+def search_exponents(xp: np.ndarray, hb: np.ndarray) -> tuple[np.ndarray, np.ndarray]:
+    """Hessian exponent search over fp32 rows x' [R, K] with the diagonal
+    blocks hb [K/32, 32, 32] (R24): each group tries the plain scale byte b0
+    (R7) and b0 + 1 and keeps b0 + 1 only when its Hessian-weighted error is
+    strictly smaller.  Returns packed codes [R, K/2] and scale bytes [R, K/32].
+    """
+    assert xp.dtype == np.float32
+    R, K = xp.shape
+    g = xp.reshape(R, K // GROUP, GROUP)
+    b0 = e8m0_scale(np.abs(g).max(axis=-1)).astype(np.int64)
+    xd = g.astype(np.float64)
+    errs, codes = [], []
+    for b in (b0, b0 + 1):
+        c = encode_groups(g, b)
+        codes.append(c)
+        errs.append(hessian_error(xd - dequantize_groups(c, b), hb))
+    up = errs[1] < errs[0]
+    scales = np.where(up, b0 + 1, b0).astype(np.uint8)
+    code = np.where(up[..., None], codes[1], codes[0])
+    return pack_codes(code), scales
+
+
+def prepare_weights_hessian(w, s: np.ndarray, h: np.ndarray) -> tuple[np.ndarray, np.ndarray]:
+    """W' of one expert with Hessian-searched scale bytes: x' = W diag(1/s)
+    H_blk as in prepare_weights, then search_exponents with the diagonal
+    blocks of h [K, K] (the Hessian of the expert's transformed input)."""
+    wf = as_f32(w)
+    r = weight_reciprocal(np.asarray(s).reshape(-1))
+    xp = transform(wf, np.broadcast_to(r, wf.shape))
+    return search_exponents(xp, diagonal_blocks(np.asarray(h)))
 
 
 # --------------------------------------------------------------------------
