@@ -46,13 +46,25 @@ WORKLOADS = {
     "moe-token": (5, 0, None, "MoE E64 T8192 N1024 K3072 bf16, per-token Zipf(1.1) routing"),
 }
 
+# Offline weight preparation with the Hessian exponent search (Hessian of the
+# transformed calibration input, then the per-group scale search): the layer
+# weights of a workload above and its calibration draw.
+OFFLINE = {
+    "prep-gateup": (4, 0, "gate/up weights N25600 K5120, 4096 calibration rows, bf16"),
+    "prep-moe": (5, 0, "MoE weights E64 N1024 K3072, 512 calibration rows per expert, bf16"),
+}
+OFFLINE_METRIC = "offline W4A4 weight preparation with Hessian exponent search, ms per layer, 1 GPU"
+PEAK_FP64_TFLOPS = 78.6   # MI355X vector fp64, a fused multiply-add counted as 2
+PEAK_FP64_TOPS = 39.3     # separate fp64 add or multiply: 256 CUs x 64 lanes x 2.4 GHz
+SEARCH_OPS_PER_GROUP = 2 * (2 * 32 * 32 + 2 * 32)   # two candidates' quadratic forms
+
 
 def parse():
     p = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=200)
     p.add_argument("--warmup", type=int, default=20)
-    p.add_argument("--workload", default="attn", choices=sorted(WORKLOADS))
+    p.add_argument("--workload", default="attn", choices=sorted(WORKLOADS) + sorted(OFFLINE))
     p.add_argument("--path", default="auto", choices=["auto", "fused", "unfused"])
     p.add_argument("--out", default="f32", choices=["f32", "bf16"], help="dtype of y")
     p.add_argument("--epilogue", default="none", choices=["none", "swiglu"],
@@ -132,6 +144,126 @@ def cpu_baseline(wl, rows):
             "seconds": round(el, 2)}
 
 
+def cpu_baseline_offline(wl, rows, cols):
+    """The oracle's offline chain on a bounded sample, scaled to one layer:
+    the Hessian of `cols` input columns of expert 0's calibration rows (work
+    grows with cols^2), then the exponent search of `rows` weight rows."""
+    import numpy as np
+    import oracle
+    import workloads
+    from threadpoolctl import threadpool_info
+
+    K, N, E = wl.K, wl.N, wl.E
+    co = wl.cal_offsets.numpy()
+    xb = workloads.bf16_bits(wl.xcal[co[0]:co[1], :cols])
+    s = wl.s[0].numpy()
+    t0 = time.perf_counter()
+    h = oracle.hessian(xb, s[None, :cols])[0]
+    t_h = time.perf_counter() - t0
+    hk = np.zeros((K, K), np.float32)
+    hk[:cols, :cols] = h
+    w = workloads.bf16_bits(wl.w[0, :rows])
+    t0 = time.perf_counter()
+    oracle.prepare_weights_hessian(w, s, hk)
+    t_s = time.perf_counter() - t0
+    layer_s = E * (t_h * (K / cols) ** 2 + t_s * N / rows)
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    return {"value": round(layer_s * 1e3, 1), "unit": "ms per layer", "cores": int(threads), "kind": "oracle",
+            "sample": f"Hessian of {cols} of {K} columns over {co[1] - co[0]} calibration rows ({t_h:.2f} s, "
+                      f"scaled by (K/cols)^2) + search of {rows} of {N} weight rows ({t_s:.2f} s, scaled by "
+                      f"N/rows), times {E} expert(s)",
+            "seconds": round(t_h + t_s, 2)}
+
+
+def bench_offline(args):
+    """One step = macaq_hessian over the calibration rows, then
+    macaq_prepare_weights_hessian over all weight rows, for every expert."""
+    import numpy as np
+    import torch
+    import workloads
+    import mxfp4_w4a4_quantized_channel_amd as mx
+
+    cfg, variant, desc = OFFLINE[args.workload]
+    wl = workloads.make(cfg, variant=variant, M=1 if cfg == 4 else None, keep_calib=True)
+    N, K, E = wl.N, wl.K, wl.E
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    mx.lib()
+    xc = wl.xcal.to(dev)
+    s0 = wl.s.to(dev)
+    w = wl.w.to(dev)
+    T = xc.shape[0]
+    off = wl.cal_offsets.to(dev) if E > 1 else None
+    h = torch.empty((E, K, K), dtype=torch.float32, device=dev)
+    codes = torch.empty((E, N, K // 2), dtype=torch.uint8, device=dev)
+    scales = torch.empty((E, N, K // 32), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    sp = ctypes.c_void_p(stream.cuda_stream)
+    p = ctypes.c_void_p
+    off_p = p(off.data_ptr()) if off is not None else None
+    xdt = mx.BF16 if xc.dtype == torch.bfloat16 else mx.F32
+
+    def hess(i):
+        if mx.macaq_hessian(p(xc.data_ptr()), xdt, p(s0.data_ptr()), off_p, E, T, K, p(h.data_ptr()), sp) != 0:
+            raise RuntimeError(mx.lib().macaq_last_error().decode())
+
+    def search(i):
+        if mx.macaq_prepare_weights_hessian(p(w.data_ptr()), xdt, p(s0.data_ptr()), p(h.data_ptr()), E, N, K,
+                                            p(codes.data_ptr()), p(scales.data_ptr()), sp) != 0:
+            raise RuntimeError(mx.lib().macaq_last_error().decode())
+
+    def chain(i):
+        hess(i)
+        search(i)
+
+    for i in range(args.warmup):
+        chain(i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        chain(i)
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) / args.steps * 1e3
+
+    def kernel_us(fn):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for i in range(args.steps):
+            fn(i)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / args.steps * 1e3
+
+    h_us = kernel_us(hess)
+    s_us = kernel_us(search)
+    h_flops = float(T) * K * (K + 1)           # one FMA per row for each distinct entry of the symmetric H
+    s_ops = float(E) * N * (K // 32) * SEARCH_OPS_PER_GROUP
+    h_ach = h_flops / h_us / 1e6
+    s_ach = s_ops / s_us / 1e6
+    moved = None
+    if E == 1:
+        plain = mx.prepare_weights(w, s0)[1]
+        moved = round(float((plain != scales).float().mean()), 4)
+    out = {
+        "metric": OFFLINE_METRIC, "value": round(ms, 4), "unit": "ms", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": False, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f64", "data": "synthetic",
+        "config": {"workload": desc, "N": N, "K": K, "experts": E, "calibration_rows": T,
+                   "parallelism": "none (one GPU)"},
+        "groups_moved_to_b0_plus_1": moved,
+    }
+    hk = {"kernel": "hessian_tile_kernel", "bound": "alu", "achieved": round(h_ach, 2), "peak": PEAK_FP64_TFLOPS,
+          "unit": "TFLOP/s", "frac": round(h_ach / PEAK_FP64_TFLOPS, 4), "us": round(h_us, 2), "traffic": None}
+    sk = {"kernel": "prep_hessian_kernel", "bound": "alu", "achieved": round(s_ach, 2), "peak": PEAK_FP64_TOPS,
+          "unit": "T fp64 op/s", "frac": round(s_ach / PEAK_FP64_TOPS, 4), "us": round(s_us, 2), "traffic": None}
+    out["roofline"] = hk if h_us >= s_us else sk     # the dominant kernel
+    out["kernels"] = {"hessian": hk, "search": sk}
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline_offline(wl, rows=min(1024, N), cols=min(1024, K))
+    print(json.dumps(out), flush=True)
+
+
 def transform_overhead(args, mx, L, wl, xs, wss, wcs, ys, s0, off_p, stream, sp, a_codes, a_scales, gemm_ws,
                        M, N, K, E, R, ydt, epi):
     """The pages quote MACaQ's cost over pure MXFP4 (same W4A4 layer without
@@ -192,6 +324,10 @@ def main():
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (the layer is data-parallel: "
               f"run one process per GPU on its own rows)", file=sys.stderr)
         sys.exit(2)
+
+    if args.workload in OFFLINE:
+        bench_offline(args)
+        return
 
     import torch
     import workloads

@@ -116,6 +116,48 @@ int macaq_prepare_weights(const void* w, macaq_dtype w_dtype, const float* s,
                           uint8_t* w_codes, uint8_t* w_scales, void* stream);
 
 /*
+ * Hessian of the layer input in the transformed basis, from calibration rows
+ * ("MACaQ Enables Streaming W4A4 Quantization ...", section
+ * "Flip-Refinement: optimizing FP4 codes with second-order information": the
+ * quantization loss of a vector v is one half of v^T H v, H the Hessian of the
+ * layer input; "华为开源MACaQ:本地量化提速3倍", section "Flip-Refinement:不重算,
+ * 只改最值得改的 4-bit 数值": H comes from calibration statistics).
+ *   h[e] = X'_e^T X'_e, X'_e the calibration rows of expert e after the online
+ *   transform (the fp32 x' that macaq_quant_act quantizes, with s[e]).  The
+ *   factor 2 of the second derivative and any division by the row count are
+ *   left out.  Accumulated in fp64, stored as fp32 (round to nearest even);
+ *   h[e] is exactly symmetric; an expert without rows gets h[e] = 0.
+ *   x [T][K] in x_dtype, rows sorted by expert; s [E][K] fp32;
+ *   expert_offsets [E+1] device int32 (NULL allowed when E == 1);
+ *   h [E][K][K] fp32 out (every entry written).
+ * Requires E >= 1, T >= 0, K % 128 == 0 (MACAQ_ERR_UNSUPPORTED otherwise),
+ * x and s 16-byte aligned, h 4-byte aligned.  Work: 2*T*K*K flops (fp64).
+ */
+int macaq_hessian(const void* x, macaq_dtype x_dtype, const float* s, const int32_t* expert_offsets,
+                  int64_t E, int64_t T, int64_t K, float* h, void* stream);
+
+/*
+ * Weight preparation with the Hessian exponent search ("华为开源MACaQ:本地量化
+ * 提速3倍", section "Flip-Refinement:不重算,只改最值得改的 4-bit 数值": the
+ * ablation's first step above round-to-nearest).  x' = W diag(1/s) H as in
+ * macaq_prepare_weights; for each 32-element group the scale byte is b0 (the
+ * plain rule) or b0 + 1, whichever gives the smaller q = d^T H_gg d, with
+ * d = x' - dequant(codes at that byte) exact in fp64 and H_gg the group's
+ * diagonal 32x32 block of h[e]; q is summed in fp64 with u_i = sum over
+ * j = 0..31 of H_ij d_j, then q = sum over i = 0..31 of d_i u_i, each product
+ * and sum rounded on its own; a tie keeps b0.  With h = 0 the result equals
+ * macaq_prepare_weights.
+ *   w [E][N][K] in w_dtype; s [E][K] fp32; h [E][K][K] fp32 (only the
+ *   diagonal blocks are read), e.g. from macaq_hessian;
+ *   w_codes [E][N][K/2] out; w_scales [E][N][K/32] out.
+ * Requires E >= 1, N >= 1, K % 32 == 0, w, s and w_codes 16-byte aligned,
+ * h 4-byte aligned.
+ */
+int macaq_prepare_weights_hessian(const void* w, macaq_dtype w_dtype, const float* s, const float* h,
+                                  int64_t E, int64_t N, int64_t K,
+                                  uint8_t* w_codes, uint8_t* w_scales, void* stream);
+
+/*
  * Online activation transform and MXFP4 quantization x' = (x diag(s_e) H),
  * codes/scales of x' ("Quantization mechanism": at inference the activation
  * is scaled and transformed before the FP4 matrix multiplication).

@@ -22,6 +22,7 @@ __all__ = [
     "lib", "MacaqError", "BF16", "F32", "PATH_AUTO", "PATH_FUSED", "PATH_UNFUSED",
     "prepare_weights", "quant_act", "gemm", "linear", "linear_workspace_bytes",
     "encode_e2m1", "quant_mxfp4", "version", "library_path", "EPI_NONE", "EPI_SWIGLU",
+    "hessian", "prepare_weights_hessian",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -70,6 +71,8 @@ def _load():
         "macaq_linear_ex": (ci, [vp, ci, vp, vp, i64, vp, vp, i64, i64, i64, vp, ci, u32, vp, sz, u32, vp]),
         "macaq_encode_e2m1": (ci, [vp, i64, vp, vp]),
         "macaq_quant_mxfp4": (ci, [vp, ci, i64, i64, vp, vp, vp]),
+        "macaq_hessian": (ci, [vp, ci, vp, vp, i64, i64, i64, vp, vp]),
+        "macaq_prepare_weights_hessian": (ci, [vp, ci, vp, vp, i64, i64, i64, vp, vp, vp]),
     }
     for name, (res, args) in sig.items():
         f = getattr(L, name)
@@ -143,6 +146,63 @@ def prepare_weights(w: torch.Tensor, s: torch.Tensor):
     scales = torch.empty((E, N, K // 32), dtype=torch.uint8, device=w.device)
     _check(macaq_prepare_weights(_ptr(w), _dtype_code(w), _ptr(s), E, N, K, _ptr(codes), _ptr(scales),
                                  _stream(w.device)), "macaq_prepare_weights")
+    return codes, scales
+
+
+def hessian(x: torch.Tensor, s: torch.Tensor, offsets: torch.Tensor | None = None, out=None):
+    """Hessian of the transformed layer input from calibration rows:
+    [E, K, K] fp32, h[e] = X'_e^T X'_e.
+
+    x: [T, K] bf16/fp32 (rows sorted by expert); s: [K] or [E, K] fp32;
+    offsets: [E+1] int32 GPU tensor (None when E == 1).
+    """
+    _load()
+    if s.dim() == 1:
+        s = s[None]
+    _need(x, "x", dim=2)
+    _need(s, "s", torch.float32, 2)
+    T, K = x.shape
+    E = s.shape[0]
+    if offsets is not None:
+        _need(offsets, "offsets", torch.int32, 1)
+        if offsets.numel() != E + 1:
+            raise ValueError("offsets must have E+1 entries")
+    if out is None:
+        out = torch.empty((E, K, K), dtype=torch.float32, device=x.device)
+    else:
+        _need(out, "out", torch.float32, 3)
+        if tuple(out.shape) != (E, K, K):
+            raise ValueError(f"out must be [{E}, {K}, {K}], got {tuple(out.shape)}")
+    _check(macaq_hessian(_ptr(x), _dtype_code(x), _ptr(s), _ptr(offsets), E, T, K, _ptr(out),
+                         _stream(x.device)), "macaq_hessian")
+    return out
+
+
+def prepare_weights_hessian(w: torch.Tensor, s: torch.Tensor, h: torch.Tensor):
+    """W' with Hessian-searched scale bytes -> (codes [E,N,K/2], scales [E,N,K/32]).
+
+    w: [N, K] or [E, N, K] bf16/fp32; s: [K] or [E, K] fp32; h: [K, K] or
+    [E, K, K] fp32 (only the diagonal 32x32 blocks are read).
+    """
+    _load()
+    if w.dim() == 2:
+        w = w[None]
+    if s.dim() == 1:
+        s = s[None]
+    if h.dim() == 2:
+        h = h[None]
+    _need(w, "w", dim=3)
+    _need(s, "s", torch.float32, 2)
+    _need(h, "h", torch.float32, 3)
+    E, N, K = w.shape
+    if tuple(s.shape) != (E, K):
+        raise ValueError(f"s must be [{E}, {K}], got {tuple(s.shape)}")
+    if tuple(h.shape) != (E, K, K):
+        raise ValueError(f"h must be [{E}, {K}, {K}], got {tuple(h.shape)}")
+    codes = torch.empty((E, N, K // 2), dtype=torch.uint8, device=w.device)
+    scales = torch.empty((E, N, K // 32), dtype=torch.uint8, device=w.device)
+    _check(macaq_prepare_weights_hessian(_ptr(w), _dtype_code(w), _ptr(s), _ptr(h), E, N, K, _ptr(codes),
+                                         _ptr(scales), _stream(w.device)), "macaq_prepare_weights_hessian")
     return codes, scales
 
 

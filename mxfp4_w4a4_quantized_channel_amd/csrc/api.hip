@@ -26,6 +26,10 @@ hipError_t launch_linear_fused(const void* x, bool x_f32, const float* s, const 
                                hipStream_t stream);
 bool linear_fused_supported(int64_t M, int64_t N, int64_t K, int64_t E);
 bool decode_supported(int64_t M, int64_t N, int64_t K, int64_t E);
+hipError_t launch_hessian(const void* x, bool x_f32, const float* s, const int32_t* offsets, int E, int64_t T,
+                          int64_t K, float* H, hipStream_t stream);
+hipError_t launch_prep_hessian(const void* w, bool w_f32, const float* s, const float* H, int E, int64_t N,
+                               int64_t K, uint8_t* codes, uint8_t* scales, hipStream_t stream);
 hipError_t launch_decode_gemm(const uint8_t* A, const uint8_t* As, const uint8_t* W, const uint8_t* Ws, int64_t M,
                               int64_t N, int64_t K, void* Y, int mode, hipStream_t stream);
 // output mode bits of the GEMM kernels (mx_common.h)
@@ -148,6 +152,46 @@ int macaq_prepare_weights(const void* w, macaq_dtype w_dtype, const float* s, in
   if (int st = check_device()) return st;
   return hip_status(macaq::launch_act_quant(w, w_dtype == MACAQ_F32, true, s, nullptr, (int)E, N, E * N, K,
                                             w_codes, w_scales, (hipStream_t)stream),
+                    fn);
+}
+
+int macaq_hessian(const void* x, macaq_dtype x_dtype, const float* s, const int32_t* expert_offsets, int64_t E,
+                  int64_t T, int64_t K, float* h, void* stream) {
+  const char* fn = "macaq_hessian";
+  if (int st = check_dtype(x_dtype, fn)) return st;
+  if (E < 1 || T < 0) return fail(MACAQ_ERR_INVALID_ARG, std::string(fn) + ": need E >= 1 and T >= 0");
+  if (E > 1 && expert_offsets == nullptr)
+    return fail(MACAQ_ERR_INVALID_ARG, std::string(fn) + ": expert_offsets required when E > 1");
+  if (int st = check_k(K, fn)) return st;
+  if (K % 128 != 0)
+    return fail(MACAQ_ERR_UNSUPPORTED, std::string(fn) + ": K must be a multiple of 128 (Hessian tile)");
+  if (!s || !h || (T > 0 && !x)) return fail(MACAQ_ERR_INVALID_ARG, std::string(fn) + ": null pointer");
+  if ((T > 0 && !aligned(x, 16)) || !aligned(s, 16) || !aligned(h, 4))
+    return fail(MACAQ_ERR_INVALID_ARG, std::string(fn) + ": x and s must be 16-byte aligned, h 4-byte aligned");
+  if (E > 4096 || K > (1 << 20))
+    return fail(MACAQ_ERR_UNSUPPORTED, std::string(fn) + ": sizes beyond the supported range");
+  if (int st = check_device()) return st;
+  return hip_status(macaq::launch_hessian(x, x_dtype == MACAQ_F32, s, E > 1 ? expert_offsets : nullptr, (int)E, T,
+                                          K, h, (hipStream_t)stream),
+                    fn);
+}
+
+int macaq_prepare_weights_hessian(const void* w, macaq_dtype w_dtype, const float* s, const float* h, int64_t E,
+                                  int64_t N, int64_t K, uint8_t* w_codes, uint8_t* w_scales, void* stream) {
+  const char* fn = "macaq_prepare_weights_hessian";
+  if (int st = check_dtype(w_dtype, fn)) return st;
+  if (E < 1 || N < 1) return fail(MACAQ_ERR_INVALID_ARG, std::string(fn) + ": need E >= 1 and N >= 1");
+  if (int st = check_k(K, fn)) return st;
+  if (!w || !s || !h || !w_codes || !w_scales)
+    return fail(MACAQ_ERR_INVALID_ARG, std::string(fn) + ": null pointer");
+  if (!aligned(w, 16) || !aligned(w_codes, 16) || !aligned(s, 16) || !aligned(h, 4))
+    return fail(MACAQ_ERR_INVALID_ARG,
+                std::string(fn) + ": w, s and w_codes must be 16-byte aligned, h 4-byte aligned");
+  if (E > 4096 || K / 32 > 65535 || N > INT32_MAX)
+    return fail(MACAQ_ERR_UNSUPPORTED, std::string(fn) + ": sizes beyond the supported range");
+  if (int st = check_device()) return st;
+  return hip_status(macaq::launch_prep_hessian(w, w_dtype == MACAQ_F32, s, h, (int)E, N, K, w_codes, w_scales,
+                                               (hipStream_t)stream),
                     fn);
 }
 

@@ -104,12 +104,42 @@ def test_prepare_weights_validation():
     assert pw(A16, 3, A16, 1, 8, 64, A16, A16, None) == UNSUPPORTED
 
 
+def test_hessian_validation():
+    mx.lib()
+    hs = mx.macaq_hessian
+    # x, dtype, s, offsets, E, T, K, h
+    assert hs(A16, 0, A16, None, 1, 16, 96, A16, None) == UNSUPPORTED    # K % 128 != 0
+    assert hs(A16, 0, A16, None, 1, 16, 100, A16, None) == INVALID       # K % 32 != 0
+    assert hs(A16, 0, A16, None, 0, 16, 128, A16, None) == INVALID       # E < 1
+    assert hs(A16, 0, A16, None, 1, -1, 128, A16, None) == INVALID       # T < 0
+    assert hs(A16, 0, A16, None, 2, 16, 128, A16, None) == INVALID       # offsets needed
+    assert hs(None, 0, A16, None, 1, 16, 128, A16, None) == INVALID
+    assert hs(A16, 0, A16, None, 1, 16, 128, None, None) == INVALID
+    assert hs(A16 + 4, 0, A16, None, 1, 16, 128, A16, None) == INVALID   # x misaligned
+    assert hs(A16, 0, A16, None, 1, 16, 128, A16 + 2, None) == INVALID   # h misaligned
+    assert hs(A16, 5, A16, None, 1, 16, 128, A16, None) == UNSUPPORTED
+
+
+def test_prepare_weights_hessian_validation():
+    mx.lib()
+    ph = mx.macaq_prepare_weights_hessian
+    # w, dtype, s, h, E, N, K, codes, scales
+    assert ph(A16, 0, A16, A16, 1, 8, 48, A16, A16, None) == INVALID
+    assert ph(A16, 0, A16, A16, 1, 0, 64, A16, A16, None) == INVALID
+    assert ph(A16, 0, A16, None, 1, 8, 64, A16, A16, None) == INVALID
+    assert ph(A16, 0, A16, A16 + 1, 1, 8, 64, A16, A16, None) == INVALID
+    assert ph(A16, 0, A16 + 4, A16, 1, 8, 64, A16, A16, None) == INVALID
+    assert ph(A16, 9, A16, A16, 1, 8, 64, A16, A16, None) == UNSUPPORTED
+
+
 def test_valid_calls_without_a_device_report_no_device():
     import torch
     if torch.cuda.is_available():
         pytest.skip("a device is present")
     assert qa() == NO_DEVICE
     assert gm() == NO_DEVICE
+    assert mx.macaq_hessian(A16, 0, A16, None, 1, 16, 128, A16, None) == NO_DEVICE
+    assert mx.macaq_prepare_weights_hessian(A16, 0, A16, A16, 1, 8, 64, A16, A16, None) == NO_DEVICE
     assert b"no HIP device" in mx.lib().macaq_last_error()
 
 

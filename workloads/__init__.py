@@ -49,6 +49,9 @@ class Workload:
     w:        [E, N, K] weights, same dtype family as x
     s:        [E, K] float32 per-channel scales (> 0)
     offsets:  [E+1] int32 row offsets of each expert in x (offsets[E] == M)
+    xcal:     [T, K] calibration activations s was derived from, rows sorted
+              by expert (only with make(..., keep_calib=True), else None)
+    cal_offsets: [E+1] int32 row offsets of each expert in xcal (or None)
     """
     name: str
     x: torch.Tensor
@@ -56,6 +59,8 @@ class Workload:
     s: torch.Tensor
     offsets: torch.Tensor
     outlier_channels: np.ndarray
+    xcal: torch.Tensor | None = None
+    cal_offsets: torch.Tensor | None = None
 
     @property
     def M(self) -> int:
@@ -159,7 +164,7 @@ CONFIG_NAMES = {
 
 def make(cfg: int, *, variant: int = 0, M: int | None = None, seed: int = 0,
          shape: tuple[int, int, int] | None = None, routing: str = "expert_zipf",
-         scale_rule: str = "smooth") -> Workload:
+         scale_rule: str = "smooth", keep_calib: bool = False) -> Workload:
     """Build the synthetic layer of config ``cfg`` (1..5).
 
     variant: config 4 only, 0 = gate/up (K5120 N25600), 1 = down (K25600 N5120).
@@ -170,6 +175,7 @@ def make(cfg: int, *, variant: int = 0, M: int | None = None, seed: int = 0,
              largest-remainder split; many experts empty) or "token_zipf"
              (each token draws a rank from Zipf(1.1) truncated to 64 experts).
     scale_rule: "smooth" (s = 1/sigma, default) or "literal" (s = sigma).
+    keep_calib: also return the calibration draw (xcal, cal_offsets).
     """
     if cfg == 1:
         Mx, N, K = shape or (16, 128, 256)
@@ -208,17 +214,22 @@ def make(cfg: int, *, variant: int = 0, M: int | None = None, seed: int = 0,
         else:
             raise ValueError(routing)
         x = _cast(_draw_acts(_rng(seed, cfg, variant, STREAM_X), Mx, K, dist, outl, factor), dtype)
-        ws, ss = [], []
+        ws, ss, cals = [], [], []
         for e in range(E):
             w_e = _cast(_rng(seed, cfg, variant, STREAM_W, e).standard_normal((N, K)) * w_std, dtype)
             cal = _cast(_draw_acts(_rng(seed, cfg, variant, STREAM_CALIB, e), n_cal, K, dist, outl, factor), dtype)
             ss.append(_scale(cal, w_e, scale_rule))
             ws.append(w_e)
+            if keep_calib:
+                cals.append(cal)
         w = torch.stack(ws)
         s = torch.from_numpy(np.stack(ss))
         offsets = torch.from_numpy(np.concatenate([[0], np.cumsum(counts)]).astype(np.int32))
         name = f"{CONFIG_NAMES[5]} routing={routing}"
-        return Workload(name, x, w, s, offsets, outl)
+        if not keep_calib:
+            return Workload(name, x, w, s, offsets, outl)
+        cal_off = torch.arange(E + 1, dtype=torch.int32) * n_cal
+        return Workload(name, x, w, s, offsets, outl, torch.cat(cals), cal_off)
 
     x_all = _draw_acts(_rng(seed, cfg, variant, STREAM_X), Mx, K, dist, outl, factor)
     if cfg == 4 and M is not None:
@@ -229,4 +240,7 @@ def make(cfg: int, *, variant: int = 0, M: int | None = None, seed: int = 0,
     s = torch.from_numpy(_scale(cal, w, scale_rule))[None, :].contiguous()
     offsets = torch.tensor([0, x.shape[0]], dtype=torch.int32)
     name = CONFIG_NAMES[cfg] if shape is None else f"cfg{cfg}-shaped M{x.shape[0]} N{N} K{K}"
-    return Workload(name, x, w[None].contiguous(), s, offsets, outl)
+    if not keep_calib:
+        return Workload(name, x, w[None].contiguous(), s, offsets, outl)
+    cal_off = torch.tensor([0, cal.shape[0]], dtype=torch.int32)
+    return Workload(name, x, w[None].contiguous(), s, offsets, outl, cal, cal_off)
