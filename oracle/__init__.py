@@ -7,4 +7,5 @@ from .mxfp4_oracle import (GROUP, E2M1_VALUES, E2M1_EMAX, C_NORM, sylvester_hada
                            gemm, linear, within_tolerance, round_bf16, swiglu, swiglu_bound,
                            encode_groups, pack_codes, hessian, diagonal_blocks,
                            dequantize_groups, hessian_error, search_exponents,
-                           prepare_weights_hessian)
+                           prepare_weights_hessian, E2M1_LEVELS, code_levels, level_code,
+                           flip_refine, layer_loss)

@@ -73,13 +73,28 @@ design notes):
       then the outer sum over i ascending, no fused multiply-add), so that
       the choice is reproducible; d is exact in fp64 (at most 28 significant
       bits) and so is every product H_ij d_j.
+* R26 Flip-Refinement loss of a weight row: 1/2 d^T H d, d = x' - dequant
+      (x' the fp32 transformed weight row, H the Hessian of R23, full K x K);
+      scale bytes stay fixed and only codes move.
+* R27 a move takes one code to the adjacent value of the signed E2M1 grid
+      (-6 .. -0.5, 0, 0.5 .. 6, times the group's scale); no move past +-6.
+      Each round a row applies its one best move if that lowers its loss,
+      else it stops; at most max_rounds moves (a caller's bound: the pages
+      give none).
+* R28 ties between equal gains go to the lowest coordinate, then to the
+      downward move; a move onto zero keeps the sign bit of the code it left.
+* R29 the gradient g = H^T d (= H d for the symmetric Hessian) is formed
+      once in fp64 (j ascending, products and sums rounded separately) and
+      then only updated, g -= delta H[k, :] (delta a signed power of two, so
+      each update is one rounding), as the pages describe; every gain is
+      delta g_k - delta^2 H_kk / 2 in fp64.
 
 Floating-point arithmetic that decides a code (the transform) is done in
 fp32 exactly as stated above, because the codes must be bit-exact; the GEMM
 is the dequantized product in fp64.
 
-The offline section (Hessian, exponent search) follows [flip] and
-[ablation] with readings R23-R25; its decisions are pinned by exact rational
+The offline sections (Hessian, exponent search, Flip-Refinement) follow
+[flip] and [ablation] with readings R23-R29; its decisions are pinned by exact rational
 arithmetic in the tests.  The last section (bf16 output, SwiGLU over a
 gate/up projection) restates a consumer step after the layer; it is not from
 the pages.
@@ -420,6 +435,88 @@ def prepare_weights_hessian(w, s: np.ndarray, h: np.ndarray) -> tuple[np.ndarray
     r = weight_reciprocal(np.asarray(s).reshape(-1))
     xp = transform(wf, np.broadcast_to(r, wf.shape))
     return search_exponents(xp, diagonal_blocks(np.asarray(h)))
+
+
+# --------------------------------------------------------------------------
+# offline: Flip-Refinement of the weight codes ([flip], [ablation];
+# readings R26-R29)
+# --------------------------------------------------------------------------
+
+# Signed E2M1 levels -7..7 (level L has value sign(L) * E2M1_VALUES[|L|]).
+E2M1_LEVELS = np.concatenate([-E2M1_VALUES[:0:-1], E2M1_VALUES])
+
+
+def code_levels(code: np.ndarray) -> np.ndarray:
+    """4-bit codes -> signed levels -7..7 (both zero codes give level 0)."""
+    mag = (code & 7).astype(np.int64)
+    return np.where(code & 8, -mag, mag)
+
+
+def level_code(level: np.ndarray, old_code: np.ndarray) -> np.ndarray:
+    """Signed level -> 4-bit code; level 0 keeps the sign bit of old_code (a
+    move onto zero keeps the sign of the code it came from) (R28)."""
+    mag = np.abs(level).astype(np.uint8)
+    sign = np.where(level < 0, 8, np.where(level > 0, 0, old_code & 8)).astype(np.uint8)
+    return sign | mag
+
+
+def flip_refine(xp: np.ndarray, codes: np.ndarray, scales: np.ndarray, h: np.ndarray,
+                max_rounds: int) -> tuple[np.ndarray, np.ndarray]:
+    """Flip-Refinement of MXFP4 rows (R26-R29).
+
+    xp: [R, K] fp32 x' of the weight rows; codes [R, K/2] packed start codes
+    (normally round-to-nearest); scales [R, K/32] kept fixed; h [K, K] the
+    Hessian of the transformed input.  For every row the loss is
+    L = 1/2 d^T H d with d = x' - dequant(codes).  The gradient g = H^T d is
+    formed once (fp64, g_i = sum over j ascending of h[j, i] d_j, multiply and
+    add rounded separately), then each round every active row takes its best
+    single move of one code to the adjacent signed E2M1 level: the gain of
+    moving coordinate k by delta is delta g_k - delta^2 h[k, k] / 2; the best
+    candidate (the first in the order k ascending, down before up, among the
+    largest gains) is applied when its gain is > 0, and the gradient is
+    updated by g -= delta h[k, :]; otherwise the row stops.  Returns the
+    refined packed codes and the number of moves of each row.
+    """
+    R, K = xp.shape
+    G = K // GROUP
+    hd = np.asarray(h, dtype=np.float64)
+    code = unpack_codes(codes).astype(np.uint8)
+    level = code_levels(code)
+    sc = np.repeat(np.ldexp(1.0, scales.astype(np.int64) - 127), GROUP, axis=1)   # [R, K]
+    d = xp.astype(np.float64) - E2M1_LEVELS[level + 7] * sc
+    g = np.zeros((R, K))
+    for j in range(K):
+        g = g + hd[j][None, :] * d[:, j:j + 1]
+    diag = np.diagonal(hd).copy()
+    moves = np.zeros(R, dtype=np.int64)
+    active = np.ones(R, dtype=bool)
+    rows = np.arange(R)
+    for _ in range(max_rounds):
+        if not active.any():
+            break
+        dn = np.where(level > -7, (E2M1_LEVELS[np.maximum(level - 1, -7) + 7] - E2M1_LEVELS[level + 7]) * sc, 0.0)
+        up = np.where(level < 7, (E2M1_LEVELS[np.minimum(level + 1, 7) + 7] - E2M1_LEVELS[level + 7]) * sc, 0.0)
+        gain = np.empty((R, 2 * K))
+        gain[:, 0::2] = np.where(level > -7, dn * g - 0.5 * dn * dn * diag, -np.inf)
+        gain[:, 1::2] = np.where(level < 7, up * g - 0.5 * up * up * diag, -np.inf)
+        best = np.argmax(gain, axis=1)
+        take = active & (gain[rows, best] > 0)
+        active = take
+        for r in np.nonzero(take)[0]:
+            k, is_up = divmod(int(best[r]), 2)
+            delta = up[r, k] if is_up else dn[r, k]
+            new_level = level[r, k] + (1 if is_up else -1)
+            code[r, k] = level_code(np.array(new_level), code[r, k])
+            level[r, k] = new_level
+            g[r] = g[r] - delta * hd[k]
+            moves[r] += 1
+    return pack_codes(code.reshape(R, G, GROUP)), moves
+
+
+def layer_loss(xp: np.ndarray, codes: np.ndarray, scales: np.ndarray, h: np.ndarray) -> np.ndarray:
+    """1/2 d^T H d per row with d = x' - dequant(codes), fp64 (library matmul)."""
+    d = xp.astype(np.float64) - dequantize_mxfp4(codes, scales)
+    return 0.5 * np.einsum("ri,ij,rj->r", d, np.asarray(h, dtype=np.float64), d)
 
 
 # --------------------------------------------------------------------------
