@@ -53,7 +53,8 @@ OFFLINE = {
     "prep-gateup": (4, 0, "gate/up weights N25600 K5120, 4096 calibration rows, bf16"),
     "prep-moe": (5, 0, "MoE weights E64 N1024 K3072, 512 calibration rows per expert, bf16"),
 }
-OFFLINE_METRIC = "offline W4A4 weight preparation with Hessian exponent search, ms per layer, 1 GPU"
+OFFLINE_METRIC = ("offline W4A4 weight preparation (Hessian, exponent search, Flip-Refinement), "
+                  "ms per layer, 1 GPU")
 PEAK_FP64_TFLOPS = 78.6   # MI355X vector fp64, a fused multiply-add counted as 2
 PEAK_FP64_TOPS = 39.3     # separate fp64 add or multiply: 256 CUs x 64 lanes x 2.4 GHz
 SEARCH_OPS_PER_GROUP = 2 * (2 * 32 * 32 + 2 * 32)   # two candidates' quadratic forms
@@ -72,6 +73,8 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-ablation", action="store_true", help="skip the pure-MXFP4 comparison")
     p.add_argument("--cpu-rows", type=int, default=256, help="row sample of the CPU oracle baseline")
+    p.add_argument("--flip-rounds", type=int, default=4096,
+                   help="offline workloads: at most this many Flip-Refinement moves per weight row")
     p.add_argument("--copy-calibration", action="store_true",
                    help="only run a plain 512 MiB device-to-device copy (5 times) so that HBM byte "
                         "counters can be scaled against a transfer of known size")
@@ -144,10 +147,12 @@ def cpu_baseline(wl, rows):
             "seconds": round(el, 2)}
 
 
-def cpu_baseline_offline(wl, rows, cols):
+def cpu_baseline_offline(wl, rows, cols, flip_rows, flip_rounds):
     """The oracle's offline chain on a bounded sample, scaled to one layer:
     the Hessian of `cols` input columns of expert 0's calibration rows (work
-    grows with cols^2), then the exponent search of `rows` weight rows."""
+    grows with cols^2), the exponent search of `rows` weight rows, and the
+    Flip-Refinement of `flip_rows` weight rows (their gradient over all K
+    and their rounds, against the full Hessian)."""
     import numpy as np
     import oracle
     import workloads
@@ -166,18 +171,27 @@ def cpu_baseline_offline(wl, rows, cols):
     t0 = time.perf_counter()
     oracle.prepare_weights_hessian(w, s, hk)
     t_s = time.perf_counter() - t0
-    layer_s = E * (t_h * (K / cols) ** 2 + t_s * N / rows)
+    hf = oracle.hessian(workloads.bf16_bits(wl.xcal[co[0]:co[1]]), s[None])[0].astype(np.float32)
+    wf = workloads.bf16_bits(wl.w[0, :flip_rows])
+    c0, s0 = oracle.prepare_weights_hessian(wf, s, hf)
+    xp = oracle.transform(oracle.as_f32(wf), np.broadcast_to(oracle.weight_reciprocal(s), (flip_rows, K)))
+    t0 = time.perf_counter()
+    oracle.flip_refine(xp, c0, s0, hf, flip_rounds)
+    t_f = time.perf_counter() - t0
+    layer_s = E * (t_h * (K / cols) ** 2 + t_s * N / rows + t_f * N / flip_rows)
     threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
     return {"value": round(layer_s * 1e3, 1), "unit": "ms per layer", "cores": int(threads), "kind": "oracle",
             "sample": f"Hessian of {cols} of {K} columns over {co[1] - co[0]} calibration rows ({t_h:.2f} s, "
                       f"scaled by (K/cols)^2) + search of {rows} of {N} weight rows ({t_s:.2f} s, scaled by "
-                      f"N/rows), times {E} expert(s)",
-            "seconds": round(t_h + t_s, 2)}
+                      f"N/rows) + Flip-Refinement of {flip_rows} rows, up to {flip_rounds} moves ({t_f:.2f} s, "
+                      f"scaled by N/rows), times {E} expert(s)",
+            "seconds": round(t_h + t_s + t_f, 2)}
 
 
 def bench_offline(args):
     """One step = macaq_hessian over the calibration rows, then
-    macaq_prepare_weights_hessian over all weight rows, for every expert."""
+    macaq_prepare_weights_hessian over all weight rows, then
+    macaq_flip_refine of those codes, for every expert."""
     import numpy as np
     import torch
     import workloads
@@ -197,6 +211,8 @@ def bench_offline(args):
     h = torch.empty((E, K, K), dtype=torch.float32, device=dev)
     codes = torch.empty((E, N, K // 2), dtype=torch.uint8, device=dev)
     scales = torch.empty((E, N, K // 32), dtype=torch.uint8, device=dev)
+    moves = torch.zeros((E, N), dtype=torch.int32, device=dev)
+    ws = torch.empty(mx.flip_refine_workspace_bytes(E * N, K), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream(dev)
     sp = ctypes.c_void_p(stream.cuda_stream)
     p = ctypes.c_void_p
@@ -212,9 +228,20 @@ def bench_offline(args):
                                             p(codes.data_ptr()), p(scales.data_ptr()), sp) != 0:
             raise RuntimeError(mx.lib().macaq_last_error().decode())
 
+    def flip(rounds):
+        if mx.macaq_flip_refine(p(w.data_ptr()), xdt, p(s0.data_ptr()), p(h.data_ptr()), E, N, K, rounds,
+                                p(codes.data_ptr()), p(scales.data_ptr()), p(moves.data_ptr()), p(ws.data_ptr()),
+                                ws.numel(), sp) != 0:
+            raise RuntimeError(mx.lib().macaq_last_error().decode())
+
+    def search_flip(i):
+        search(i)
+        flip(args.flip_rounds)
+
     def chain(i):
         hess(i)
         search(i)
+        flip(args.flip_rounds)
 
     for i in range(args.warmup):
         chain(i)
@@ -237,10 +264,20 @@ def bench_offline(args):
 
     h_us = kernel_us(hess)
     s_us = kernel_us(search)
+    sf_us = kernel_us(search_flip)
+    g_us = kernel_us(lambda i: flip(0))         # the gradient kernel (the rounds kernel exits at once)
+    f_us = sf_us - s_us
+    r_us = f_us - g_us
     h_flops = float(T) * K * (K + 1)           # one FMA per row for each distinct entry of the symmetric H
     s_ops = float(E) * N * (K // 32) * SEARCH_OPS_PER_GROUP
+    g_ops = 2.0 * E * N * K * K                # a multiply and an add per (row, j, i)
     h_ach = h_flops / h_us / 1e6
     s_ach = s_ops / s_us / 1e6
+    g_ach = g_ops / g_us / 1e6
+    search(0)
+    flip(args.flip_rounds)
+    torch.cuda.synchronize()
+    mv = moves.double()
     moved = None
     if E == 1:
         plain = mx.prepare_weights(w, s0)[1]
@@ -257,10 +294,21 @@ def bench_offline(args):
           "unit": "TFLOP/s", "frac": round(h_ach / PEAK_FP64_TFLOPS, 4), "us": round(h_us, 2), "traffic": None}
     sk = {"kernel": "prep_hessian_kernel", "bound": "alu", "achieved": round(s_ach, 2), "peak": PEAK_FP64_TOPS,
           "unit": "T fp64 op/s", "frac": round(s_ach / PEAK_FP64_TOPS, 4), "us": round(s_us, 2), "traffic": None}
-    out["roofline"] = hk if h_us >= s_us else sk     # the dominant kernel
-    out["kernels"] = {"hessian": hk, "search": sk}
+    gk = {"kernel": "flip_grad_kernel", "bound": "alu", "achieved": round(g_ach, 2), "peak": PEAK_FP64_TOPS,
+          "unit": "T fp64 op/s", "frac": round(g_ach / PEAK_FP64_TOPS, 4), "us": round(g_us, 2), "traffic": None}
+    rk = {"kernel": "flip_rounds_kernel", "bound": "latency (one reduction and one H row per move)",
+          "us": round(r_us, 2), "moves_per_row_mean": round(float(mv.mean()), 1),
+          "moves_per_row_max": int(mv.max()), "moves_total": int(mv.sum()),
+          "ns_per_move": round(r_us * 1e3 / max(float(mv.sum()), 1), 2),
+          "rows_at_max_rounds": int((moves == args.flip_rounds).sum())}
+    ks = {"hessian": hk, "search": sk, "flip_grad": gk, "flip_rounds": rk}
+    dom = max(("hessian", h_us), ("search", s_us), ("flip_grad", g_us), key=lambda t: t[1])[0]
+    out["roofline"] = ks[dom]     # the dominant kernel with a roofline
+    out["kernels"] = ks
+    out["config"]["flip_max_rounds"] = args.flip_rounds
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline_offline(wl, rows=min(1024, N), cols=min(1024, K))
+        out["cpu_baseline"] = cpu_baseline_offline(wl, rows=min(1024, N), cols=min(1024, K),
+                                                   flip_rows=min(32, N), flip_rounds=args.flip_rounds)
     print(json.dumps(out), flush=True)
 
 

@@ -158,6 +158,46 @@ int macaq_prepare_weights_hessian(const void* w, macaq_dtype w_dtype, const floa
                                   uint8_t* w_codes, uint8_t* w_scales, void* stream);
 
 /*
+ * Flip-Refinement of prepared weight codes ("MACaQ Enables Streaming W4A4
+ * Quantization ...", section "Flip-Refinement: optimizing FP4 codes with
+ * second-order information": coordinate descent moving single codes to
+ * adjacent representable values under the loss one half of
+ * (x - q)^T H (x - q); "华为开源MACaQ:本地量化提速3倍", section
+ * "Flip-Refinement:不重算,只改最值得改的 4-bit 数值": start from round-to-nearest,
+ * one best adjustment per output row and round, a row with no improving
+ * adjustment stops, the gradient is updated incrementally).
+ *   Per weight row: x' = W diag(1/s) H (as macaq_prepare_weights),
+ *   d = x' - dequant(codes), g_i = sum over j = 0..K-1 of h[j][i] d_j (fp64,
+ *   product and sum rounded separately).  Each round the row's candidate
+ *   moves (one code to the adjacent level of the signed E2M1 grid, scale
+ *   bytes fixed) are scored gain = delta g_k - delta^2 h[k][k] / 2 (fp64);
+ *   the largest gain wins, ties to the lowest k, then to the downward move;
+ *   if it is > 0 the code moves (a move onto zero keeps the sign bit of the
+ *   code it left) and g -= delta h[k][:]; else the row stops.  At most
+ *   max_rounds moves per row.
+ *   w [E][N][K] in w_dtype; s [E][K] fp32; h [E][K][K] fp32 (e.g. from
+ *   macaq_hessian); w_codes [E][N][K/2] in/out (normally the output of
+ *   macaq_prepare_weights or macaq_prepare_weights_hessian); w_scales
+ *   [E][N][K/32] in; moves [E][N] int32 out (moves made per row; may be
+ *   NULL); workspace: device memory of at least
+ *   macaq_flip_refine_workspace_bytes(128, K) bytes, 256-byte aligned, that
+ *   holds the fp64 gradient: with room for E * N rows all experts run in one
+ *   pair of launches, otherwise expert by expert in chunks of as many rows
+ *   as fit.
+ * Requires E >= 1, N >= 1, K % 128 == 0, K <= 32640, max_rounds >= 0;
+ * w, s and w_codes 16-byte aligned, h 4-byte aligned.  Calls that share a
+ * workspace must not overlap in time.
+ */
+int macaq_flip_refine(const void* w, macaq_dtype w_dtype, const float* s, const float* h,
+                      int64_t E, int64_t N, int64_t K, int32_t max_rounds,
+                      uint8_t* w_codes, const uint8_t* w_scales, int32_t* moves,
+                      void* workspace, size_t workspace_bytes, void* stream);
+
+/* Workspace bytes of macaq_flip_refine to process `rows` rows per chunk
+ * (rows rounded up to 128): rows * K * 8. */
+size_t macaq_flip_refine_workspace_bytes(int64_t rows, int64_t K);
+
+/*
  * Online activation transform and MXFP4 quantization x' = (x diag(s_e) H),
  * codes/scales of x' ("Quantization mechanism": at inference the activation
  * is scaled and transformed before the FP4 matrix multiplication).

@@ -22,7 +22,7 @@ __all__ = [
     "lib", "MacaqError", "BF16", "F32", "PATH_AUTO", "PATH_FUSED", "PATH_UNFUSED",
     "prepare_weights", "quant_act", "gemm", "linear", "linear_workspace_bytes",
     "encode_e2m1", "quant_mxfp4", "version", "library_path", "EPI_NONE", "EPI_SWIGLU",
-    "hessian", "prepare_weights_hessian",
+    "hessian", "prepare_weights_hessian", "flip_refine", "flip_refine_workspace_bytes",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -73,6 +73,8 @@ def _load():
         "macaq_quant_mxfp4": (ci, [vp, ci, i64, i64, vp, vp, vp]),
         "macaq_hessian": (ci, [vp, ci, vp, vp, i64, i64, i64, vp, vp]),
         "macaq_prepare_weights_hessian": (ci, [vp, ci, vp, vp, i64, i64, i64, vp, vp, vp]),
+        "macaq_flip_refine": (ci, [vp, ci, vp, vp, i64, i64, i64, ctypes.c_int32, vp, vp, vp, vp, sz, vp]),
+        "macaq_flip_refine_workspace_bytes": (sz, [i64, i64]),
     }
     for name, (res, args) in sig.items():
         f = getattr(L, name)
@@ -204,6 +206,49 @@ def prepare_weights_hessian(w: torch.Tensor, s: torch.Tensor, h: torch.Tensor):
     _check(macaq_prepare_weights_hessian(_ptr(w), _dtype_code(w), _ptr(s), _ptr(h), E, N, K, _ptr(codes),
                                          _ptr(scales), _stream(w.device)), "macaq_prepare_weights_hessian")
     return codes, scales
+
+
+def flip_refine_workspace_bytes(rows: int, K: int) -> int:
+    return int(_load().macaq_flip_refine_workspace_bytes(rows, K))
+
+
+def flip_refine(w: torch.Tensor, s: torch.Tensor, h: torch.Tensor, codes: torch.Tensor, scales: torch.Tensor,
+                max_rounds: int, workspace: torch.Tensor | None = None, chunk_rows: int | None = None):
+    """Flip-Refinement of prepared codes, in place -> moves per row [E, N] int32.
+
+    w: [N, K] or [E, N, K] bf16/fp32; s: [K] or [E, K]; h: [K, K] or
+    [E, K, K] fp32; codes [E, N, K/2] uint8 (refined in place); scales
+    [E, N, K/32] uint8.  The workspace (allocated here if not given) holds
+    the fp64 gradient of chunk_rows rows at a time (default: all E * N rows,
+    one pair of launches for all experts).
+    """
+    _load()
+    if w.dim() == 2:
+        w = w[None]
+    if s.dim() == 1:
+        s = s[None]
+    if h.dim() == 2:
+        h = h[None]
+    if codes.dim() == 2:
+        codes, scales = codes[None], scales[None]
+    _need(w, "w", dim=3)
+    _need(s, "s", torch.float32, 2)
+    _need(h, "h", torch.float32, 3)
+    _need(codes, "codes", torch.uint8, 3)
+    _need(scales, "scales", torch.uint8, 3)
+    E, N, K = w.shape
+    if tuple(s.shape) != (E, K) or tuple(h.shape) != (E, K, K):
+        raise ValueError("s must be [E, K] and h [E, K, K]")
+    if tuple(codes.shape) != (E, N, K // 2) or tuple(scales.shape) != (E, N, K // 32):
+        raise ValueError("codes must be [E, N, K/2] and scales [E, N, K/32]")
+    if workspace is None:
+        workspace = torch.empty(flip_refine_workspace_bytes(chunk_rows or E * N, K), dtype=torch.uint8,
+                                device=w.device)
+    moves = torch.empty((E, N), dtype=torch.int32, device=w.device)
+    _check(macaq_flip_refine(_ptr(w), _dtype_code(w), _ptr(s), _ptr(h), E, N, K, int(max_rounds), _ptr(codes),
+                             _ptr(scales), _ptr(moves), _ptr(workspace), workspace.numel(), _stream(w.device)),
+           "macaq_flip_refine")
+    return moves
 
 
 def quant_act(x: torch.Tensor, s: torch.Tensor, offsets: torch.Tensor | None = None):

@@ -4,6 +4,7 @@
 // the same way with or without a device.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <atomic>
 #include <cstdio>
 #include <cstdlib>
@@ -30,6 +31,12 @@ hipError_t launch_hessian(const void* x, bool x_f32, const float* s, const int32
                           int64_t K, float* H, hipStream_t stream);
 hipError_t launch_prep_hessian(const void* w, bool w_f32, const float* s, const float* H, int E, int64_t N,
                                int64_t K, uint8_t* codes, uint8_t* scales, hipStream_t stream);
+hipError_t launch_flip_grad(const void* w, bool w_f32, const float* s, const float* H, const uint8_t* codes,
+                            const uint8_t* scales, int E, int64_t row0, int64_t rows, int64_t N, int64_t K,
+                            double* G, hipStream_t stream);
+hipError_t launch_flip_rounds(const float* H, int E, int64_t row0, int64_t rows, int64_t N, int64_t K,
+                              int max_rounds, const double* G, uint8_t* codes, const uint8_t* scales, int32_t* moves,
+                              hipStream_t stream);
 hipError_t launch_decode_gemm(const uint8_t* A, const uint8_t* As, const uint8_t* W, const uint8_t* Ws, int64_t M,
                               int64_t N, int64_t K, void* Y, int mode, hipStream_t stream);
 // output mode bits of the GEMM kernels (mx_common.h)
@@ -353,6 +360,66 @@ int macaq_encode_e2m1(const float* v, int64_t n, uint8_t* codes, void* stream) {
   if (!v || !codes) return fail(MACAQ_ERR_INVALID_ARG, std::string(fn) + ": null pointer");
   if (int st = check_device()) return st;
   return hip_status(macaq::launch_encode_e2m1(v, n, codes, (hipStream_t)stream), fn);
+}
+
+size_t macaq_flip_refine_workspace_bytes(int64_t rows, int64_t K) {
+  if (rows <= 0 || K <= 0) return 0;
+  return (size_t)((rows + 127) / 128 * 128) * (size_t)K * sizeof(double);
+}
+
+int macaq_flip_refine(const void* w, macaq_dtype w_dtype, const float* s, const float* h, int64_t E, int64_t N,
+                      int64_t K, int32_t max_rounds, uint8_t* w_codes, const uint8_t* w_scales, int32_t* moves,
+                      void* workspace, size_t workspace_bytes, void* stream) {
+  const char* fn = "macaq_flip_refine";
+  if (int st = check_dtype(w_dtype, fn)) return st;
+  if (E < 1 || N < 1 || max_rounds < 0)
+    return fail(MACAQ_ERR_INVALID_ARG, std::string(fn) + ": need E >= 1, N >= 1 and max_rounds >= 0");
+  if (int st = check_k(K, fn)) return st;
+  if (K % 128 != 0 || K > 32640)
+    return fail(MACAQ_ERR_UNSUPPORTED, std::string(fn) + ": K must be a multiple of 128 and at most 32640");
+  if (!w || !s || !h || !w_codes || !w_scales)
+    return fail(MACAQ_ERR_INVALID_ARG, std::string(fn) + ": null pointer");
+  if (!aligned(w, 16) || !aligned(w_codes, 16) || !aligned(s, 16) || !aligned(h, 4))
+    return fail(MACAQ_ERR_INVALID_ARG,
+                std::string(fn) + ": w, s and w_codes must be 16-byte aligned, h 4-byte aligned");
+  if (E > 4096 || N > INT32_MAX)
+    return fail(MACAQ_ERR_UNSUPPORTED, std::string(fn) + ": sizes beyond the supported range");
+  const size_t row_bytes = (size_t)K * sizeof(double);
+  if (int st = check_workspace(workspace, workspace_bytes, macaq_flip_refine_workspace_bytes(128, K), fn))
+    return st;
+  if (int st = check_device()) return st;
+  const int64_t fit = (int64_t)(workspace_bytes / row_bytes);   // gradient rows the workspace holds
+  const bool f32 = w_dtype == MACAQ_F32;
+  hipStream_t st = (hipStream_t)stream;
+  double* G = static_cast<double*>(workspace);
+  if (fit >= E * N) {   // all experts in one pair of launches
+    if (int r = hip_status(macaq::launch_flip_grad(w, f32, s, h, w_codes, w_scales, (int)E, 0, N, N, K, G, st),
+                           "macaq_flip_refine (gradient)"))
+      return r;
+    return hip_status(macaq::launch_flip_rounds(h, (int)E, 0, N, N, K, max_rounds, G, w_codes, w_scales, moves, st),
+                      "macaq_flip_refine (rounds)");
+  }
+  // else expert by expert, in chunks of rows that fit (a multiple of 128)
+  const int64_t chunk = std::min<int64_t>(fit / 128 * 128, (N + 127) / 128 * 128);
+  const size_t eb = f32 ? 4 : 2;
+  for (int64_t e = 0; e < E; ++e) {
+    const void* we = static_cast<const uint8_t*>(w) + (size_t)e * N * K * eb;
+    const float* se = s + e * K;
+    const float* he = h + e * K * K;
+    uint8_t* ce = w_codes + e * N * (K / 2);
+    const uint8_t* sce = w_scales + e * N * (K / 32);
+    int32_t* me = moves ? moves + e * N : nullptr;
+    for (int64_t r0 = 0; r0 < N; r0 += chunk) {
+      const int64_t rows = std::min(chunk, N - r0);
+      if (int r = hip_status(macaq::launch_flip_grad(we, f32, se, he, ce, sce, 1, r0, rows, N, K, G, st),
+                             "macaq_flip_refine (gradient)"))
+        return r;
+      if (int r = hip_status(macaq::launch_flip_rounds(he, 1, r0, rows, N, K, max_rounds, G, ce, sce, me, st),
+                             "macaq_flip_refine (rounds)"))
+        return r;
+    }
+  }
+  return MACAQ_OK;
 }
 
 }  // extern "C"

@@ -1,0 +1,425 @@
+// Flip-Refinement of prepared MXFP4 weight codes: per weight row, greedy
+// single-code moves to the adjacent E2M1 level that lower the
+// Hessian-weighted quantization loss, with an incrementally updated
+// gradient.
+//
+// Sources: "MACaQ Enables Streaming W4A4 Quantization with 32.5GB GPU
+// Memory", section "Flip-Refinement: optimizing FP4 codes with second-order
+// information" (coordinate descent that moves single coordinates to adjacent
+// representable values, judged by the loss one half of (x - q)^T H (x - q));
+// "华为开源MACaQ:本地量化提速3倍", section "Flip-Refinement:不重算,只改最值得改的
+// 4-bit 数值" (starts from round-to-nearest; each round takes only the most
+// profitable adjustment of every output row; a row with no improving
+// adjustment stops early; the gradient is updated incrementally instead of
+// recomputing the matrix product).
+//
+// Readings: the loss of row n is 1/2 d^T H d, d = x' - dequant(codes), x'
+// the fp32 transformed weight row and H the Hessian of the transformed input
+// (K x K); scale bytes stay fixed.  A move takes one code to the adjacent
+// level of the signed grid -6 .. -0.5, 0, 0.5 .. 6 (times the group scale);
+// its gain is delta g_k - delta^2 H_kk / 2 with g = H^T d.  Ties go to the
+// lowest coordinate, down before up; a move onto zero keeps the sign bit of
+// the code it left.  All of it in fp64 in a fixed order: g_i = sum over j
+// ascending of H_ji d_j (product and sum rounded separately: the library is
+// built with -ffp-contract=off), then g -= delta H[k, :] per move (delta is a
+// signed power of two, so each update is one rounding).
+//
+// Two kernels per chunk of rows: flip_grad_kernel forms g for the chunk (a
+// tiled fp64 product with the transform of W and the dequantization fused
+// into its operand loads) into the caller's workspace; flip_rounds_kernel
+// then runs the rounds with one block per row, the row's g, codes and scale
+// bytes held in registers and H_kk in LDS.
+#include "mx_common.h"
+
+namespace macaq {
+
+namespace {
+
+constexpr int kGTile = 128;   // rows x columns of a gradient tile
+
+template <int EB>
+__device__ __forceinline__ void load_w_group(const void* base, int64_t elem, float (&t)[32]) {
+  if constexpr (EB == 2) {
+    const uint4* p = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(base) + elem);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const uint4 v = p[q];
+      t[8 * q + 0] = bf16_lo(v.x); t[8 * q + 1] = bf16_hi(v.x);
+      t[8 * q + 2] = bf16_lo(v.y); t[8 * q + 3] = bf16_hi(v.y);
+      t[8 * q + 4] = bf16_lo(v.z); t[8 * q + 5] = bf16_hi(v.z);
+      t[8 * q + 6] = bf16_lo(v.w); t[8 * q + 7] = bf16_hi(v.w);
+    }
+  } else {
+    const uint4* p = reinterpret_cast<const uint4*>(static_cast<const float*>(base) + elem);
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      const uint4 v = p[q];
+      t[4 * q + 0] = __uint_as_float(v.x); t[4 * q + 1] = __uint_as_float(v.y);
+      t[4 * q + 2] = __uint_as_float(v.z); t[4 * q + 3] = __uint_as_float(v.w);
+    }
+  }
+}
+
+// E2M1 magnitude of index m (0, 0.5, 1, 1.5, 2, 3, 4, 6).
+__device__ __forceinline__ float e2m1_mag(uint32_t m) {
+  return m < 2u ? 0.5f * (float)m : __uint_as_float((((m >> 1) + 126u) << 23) | ((m & 1u) << 22));
+}
+
+// 2^(b - 127) as fp64 (b <= 254).
+__device__ __forceinline__ double scale_f64(uint32_t b) { return __longlong_as_double((long long)(b + 896u) << 52); }
+
+// Distance from signed level L to L + 1 (L in -7..6), in units of the scale:
+// magnitude steps are 0.5 (below 2), 1 (2..4) and 2 (4..6).
+__device__ __forceinline__ double level_step_up(int L) {
+  const int m = L >= 0 ? L : -L - 1;
+  return m < 4 ? 0.5 : (m < 6 ? 1.0 : 2.0);
+}
+
+__device__ __forceinline__ int code_level(uint32_t c) {
+  const int m = (int)(c & 7u);
+  return (c & 8u) ? -m : m;
+}
+
+__device__ __forceinline__ uint32_t level_to_code(int L, uint32_t old_code) {
+  if (L > 0) return (uint32_t)L;
+  if (L < 0) return 8u | (uint32_t)(-L);
+  return old_code & 8u;
+}
+
+}  // namespace
+
+// ---------------------------------------------------------------------------
+// g[n][i] = sum_j H[j][i] d[n][j] for a 128x128 tile (rows n of the chunk,
+// columns i).  Per K-step of one 32-wide group: threads 0..127 each build one
+// row's d for the group (widen W, times r = 1/s, butterfly, times C, minus
+// the dequantized code) into LDS as fp64 [32][128]; all threads stage the
+// matching 32 rows of H (fp32 -> fp64) as [32][128]; every thread then
+// accumulates its 8x8 outputs (rows ty + 16a, columns tx + 16c) over the 32
+// values in order, a multiply then an add.
+template <int EB>
+__global__ __launch_bounds__(256) void flip_grad_kernel(const void* __restrict__ w, const float* __restrict__ s,
+                                                        const float* __restrict__ H, const uint8_t* __restrict__ codes,
+                                                        const uint8_t* __restrict__ scales, int64_t row0,
+                                                        int64_t rows, int64_t N, int64_t K, double* __restrict__ G) {
+  // expert blockIdx.z: its rows row0 .. row0 + rows - 1 of N, its gradient
+  // rows at G + e * rows * K
+  {
+    const int64_t e = blockIdx.z;
+    w = static_cast<const uint8_t*>(w) + e * N * K * EB;
+    s += e * K;
+    H += e * K * K;
+    codes += e * N * (K / 2);
+    scales += e * N * (K / 32);
+    G += e * rows * K;
+  }
+  __shared__ double da[32][kGTile];
+  __shared__ double hb[32][kGTile];
+  __shared__ float rs[32];
+  const int tid = threadIdx.x;
+  const int64_t n0 = (int64_t)blockIdx.x * kGTile;   // within the chunk
+  const int64_t i0 = (int64_t)blockIdx.y * kGTile;
+  const int ty = tid >> 4, tx = tid & 15;
+  const int64_t my_row = n0 + tid;                    // transform task (tid < 128)
+  const bool tasker = tid < kGTile && my_row < rows;
+
+  double acc[8][8];
+#pragma unroll
+  for (int a = 0; a < 8; ++a)
+#pragma unroll
+    for (int c = 0; c < 8; ++c) acc[a][c] = 0.0;
+
+  const int64_t G32 = K / 32;
+  for (int64_t g = 0; g < G32; ++g) {
+    const int64_t col = 32 * g;
+    if (tid < 32) rs[tid] = 1.0f / s[col + tid];
+    __syncthreads();
+    if (tid < kGTile) {
+      if (tasker) {
+        const int64_t row = row0 + my_row;
+        float t[32];
+        load_w_group<EB>(w, row * K + col, t);
+#pragma unroll
+        for (int i = 0; i < 32; ++i) t[i] = t[i] * rs[i];
+#pragma unroll
+        for (int hh = 1; hh < 32; hh <<= 1) {
+#pragma unroll
+          for (int i = 0; i < 32; ++i) {
+            if ((i & hh) == 0) {
+              const float a = t[i], b = t[i + hh];
+              t[i] = a + b;
+              t[i + hh] = a - b;
+            }
+          }
+        }
+        const float cn = hadamard_norm();
+        const uint4 cq = reinterpret_cast<const uint4*>(codes + row * (K / 2) + 16 * g)[0];
+        const uint32_t cw[4] = {cq.x, cq.y, cq.z, cq.w};
+        const double sc = scale_f64(scales[row * G32 + g]);
+#pragma unroll
+        for (int i = 0; i < 32; ++i) {
+          const uint32_t c = (cw[i >> 3] >> (4 * (i & 7))) & 0xFu;
+          const float m = e2m1_mag(c & 7u);
+          const double deq = (double)((c & 8u) ? -m : m) * sc;
+          da[i][tid] = (double)(t[i] * cn) - deq;
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < 32; ++i) da[i][tid] = 0.0;
+      }
+    }
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+      const int idx = tid + 256 * q;          // 32 x 128 entries
+      hb[idx >> 7][idx & 127] = (double)H[(col + (idx >> 7)) * K + i0 + (idx & 127)];
+    }
+    __syncthreads();
+#pragma unroll 4
+    for (int jj = 0; jj < 32; ++jj) {
+      double av[8], bv[8];
+#pragma unroll
+      for (int a = 0; a < 8; ++a) av[a] = da[jj][ty + 16 * a];
+#pragma unroll
+      for (int c = 0; c < 8; ++c) bv[c] = hb[jj][tx + 16 * c];
+#pragma unroll
+      for (int a = 0; a < 8; ++a)
+#pragma unroll
+        for (int c = 0; c < 8; ++c) acc[a][c] = acc[a][c] + av[a] * bv[c];
+    }
+    __syncthreads();
+  }
+#pragma unroll
+  for (int a = 0; a < 8; ++a) {
+    const int64_t n = n0 + ty + 16 * a;
+    if (n < rows) {
+#pragma unroll
+      for (int c = 0; c < 8; ++c) G[n * K + i0 + tx + 16 * c] = acc[a][c];
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Rounds: one block of NT threads per weight row; thread t owns coordinates
+// k = t + NT*m (m < KPT).  Per round every thread scans its coordinates'
+// down and up moves, the block reduces to the best (gain, candidate = 2k +
+// up), and when that gain is positive every thread updates its g entries
+// with row k of H while the owner of k moves its code.
+struct Best {
+  double gain;
+  double delta;
+  int cand;
+};
+
+__device__ __forceinline__ bool better(double g1, int c1, double g2, int c2) {
+  return g1 > g2 || (g1 == g2 && c1 < c2);
+}
+
+// DPP lane moves (quad_perm [1,0,3,2] = 0xB1, [2,3,0,1] = 0x4E; row_ror:4 =
+// 0x124, row_ror:8 = 0x128) and lane reads, for the in-wave reductions.
+template <int CTRL>
+__device__ __forceinline__ int dpp_i(int v) {
+  return __builtin_amdgcn_mov_dpp(v, CTRL, 0xF, 0xF, false);
+}
+template <int CTRL>
+__device__ __forceinline__ double dpp_d(double v) {
+  const long long u = __double_as_longlong(v);
+  const int lo = dpp_i<CTRL>((int)u), hi = dpp_i<CTRL>((int)(u >> 32));
+  return __longlong_as_double(((long long)hi << 32) | (unsigned)lo);
+}
+__device__ __forceinline__ double readlane_d(double v, int l) {
+  const long long u = __double_as_longlong(v);
+  const int lo = __builtin_amdgcn_readlane((int)u, l), hi = __builtin_amdgcn_readlane((int)(u >> 32), l);
+  return __longlong_as_double(((long long)hi << 32) | (unsigned)lo);
+}
+
+// Wave-uniform maximum of v (every lane gets it).
+__device__ __forceinline__ double wave_max_d(double v) {
+  v = fmax(v, dpp_d<0xB1>(v));
+  v = fmax(v, dpp_d<0x4E>(v));
+  v = fmax(v, dpp_d<0x124>(v));
+  v = fmax(v, dpp_d<0x128>(v));   // every lane holds its 16-lane row's maximum
+  return fmax(fmax(readlane_d(v, 0), readlane_d(v, 16)), fmax(readlane_d(v, 32), readlane_d(v, 48)));
+}
+__device__ __forceinline__ int wave_min_i(int v) {
+  v = min(v, dpp_i<0xB1>(v));
+  v = min(v, dpp_i<0x4E>(v));
+  v = min(v, dpp_i<0x124>(v));
+  v = min(v, dpp_i<0x128>(v));
+  return min(min(__builtin_amdgcn_readlane(v, 0), __builtin_amdgcn_readlane(v, 16)),
+             min(__builtin_amdgcn_readlane(v, 32), __builtin_amdgcn_readlane(v, 48)));
+}
+
+// Waves per SIMD the register budget aims at: more resident rows hide more of
+// each round's latency (256 threads: 3 waves fit up to 20 coordinates per
+// thread without spilling).
+template <int NT, int KPT>
+constexpr int flip_waves() { return NT == 256 && KPT <= 20 ? 3 : (NT == 256 ? 2 : 4); }
+
+template <int NT, int KPT>
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(flip_waves<NT, KPT>())))
+void flip_rounds_kernel(const float* __restrict__ H, int64_t row0, int64_t rows, int64_t N, int64_t K,
+                        int max_rounds, const double* __restrict__ G, uint8_t* __restrict__ codes,
+                        const uint8_t* __restrict__ scales, int32_t* __restrict__ moves_out) {
+  {  // expert blockIdx.y, laid out as in flip_grad_kernel
+    const int64_t e = blockIdx.y;
+    H += e * K * K;
+    G += e * rows * K;
+    codes += e * N * (K / 2);
+    scales += e * N * (K / 32);
+    if (moves_out) moves_out += e * N;
+  }
+  constexpr int NW = NT / 64;
+  __shared__ Best red[2][NW];
+  __shared__ float diag[KPT][NT];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int64_t rl = blockIdx.x;               // row within the chunk
+  const int64_t row = row0 + rl;
+  const int64_t G32 = K / 32;
+  const int Ki = (int)K;
+
+  double g[KPT];
+  uint32_t info[KPT];   // code | scale byte << 8; bit 31 marks a coordinate past K
+#pragma unroll
+  for (int m = 0; m < KPT; ++m) {
+    const int64_t k = tid + (int64_t)NT * m;
+    if (k < K) {
+      g[m] = G[rl * K + k];
+      diag[m][tid] = H[k * K + k];
+      const uint32_t byte = codes[row * (K / 2) + (k >> 1)];
+      info[m] = ((byte >> (4 * (k & 1))) & 0xFu) | ((uint32_t)scales[row * G32 + (k >> 5)] << 8);
+    } else {
+      g[m] = 0.0;
+      diag[m][tid] = 0.0f;
+      info[m] = 0x80000000u;
+    }
+  }
+
+  const double ninf = -__builtin_inf();
+  int moves = 0;
+  for (int r = 0; r < max_rounds; ++r) {
+    // keep per-coordinate values derived from info (level, scale) out of the
+    // registers between rounds: they are recomputed each round
+#pragma unroll
+    for (int m = 0; m < KPT; ++m) asm volatile("" : "+v"(info[m]));
+    // scan, without branches: candidates in the order k ascending, down
+    // (2k) before up (2k + 1); a later candidate replaces the best only if
+    // strictly better
+    double bg = ninf, bd = 0.0;
+    int bc = 0x7FFFFFFF;
+#pragma unroll
+    for (int m = 0; m < KPT; ++m) {
+      const uint32_t in = info[m];
+      const bool valid = !(in & 0x80000000u);
+      const int L = code_level(in & 0xFu);
+      const double sc = scale_f64((in >> 8) & 0xFFu);
+      const int k2 = 2 * (tid + NT * m);
+      const double hk = (double)diag[m][tid];
+      const double dl = -level_step_up(L - 1) * sc;
+      const double du = level_step_up(L) * sc;
+      double gl = dl * g[m] - 0.5 * dl * dl * hk;
+      double gu = du * g[m] - 0.5 * du * du * hk;
+      gl = (valid && L > -7) ? gl : ninf;
+      gu = (valid && L < 7) ? gu : ninf;
+      const bool tl = gl > bg;
+      bg = tl ? gl : bg; bd = tl ? dl : bd; bc = tl ? k2 : bc;
+      const bool tu = gu > bg;
+      bg = tu ? gu : bg; bd = tu ? du : bd; bc = tu ? k2 + 1 : bc;
+    }
+    // wave: the largest gain, then the lowest candidate holding it, then
+    // that candidate's step
+    const double wg = wave_max_d(bg);
+    const int wc = wave_min_i(bg == wg ? bc : 0x7FFFFFFF);
+    const unsigned long long owner = __ballot(bc == wc);
+    const double wd = readlane_d(bd, (int)__builtin_ctzll(owner | (1ull << 63)));
+    if (lane == 0) red[r & 1][wave] = Best{wg, wd, wc};
+    __syncthreads();
+    bg = red[r & 1][0].gain; bd = red[r & 1][0].delta; bc = red[r & 1][0].cand;
+#pragma unroll
+    for (int v = 1; v < NW; ++v) {
+      const Best o = red[r & 1][v];
+      if (better(o.gain, o.cand, bg, bc)) { bg = o.gain; bd = o.delta; bc = o.cand; }
+    }
+    if (!(bg > 0.0)) break;   // uniform: every thread holds the same best
+    const int kb = bc >> 1;
+    const float* hrow = H + (int64_t)kb * K;
+#pragma unroll
+    for (int m = 0; m < KPT; ++m) {
+      const int k = tid + NT * m;
+      g[m] = g[m] - bd * (double)hrow[k < Ki ? k : Ki - 1];   // entries past K are never read back
+      if (k == kb) {
+        const uint32_t old = info[m] & 0xFu;
+        const int L = code_level(old) + ((bc & 1) ? 1 : -1);
+        info[m] = (info[m] & ~0xFu) | level_to_code(L, old);
+      }
+    }
+    ++moves;
+  }
+
+  // codes back: coordinates k and k+1 sit in neighbouring lanes
+#pragma unroll
+  for (int m = 0; m < KPT; ++m) {
+    const int64_t k = tid + (int64_t)NT * m;
+    const uint32_t mine = info[m] & 0xFu;
+    const uint32_t other = (uint32_t)__shfl_xor((int)mine, 1);
+    if (k < K && (k & 1) == 0) codes[row * (K / 2) + (k >> 1)] = (uint8_t)(mine | (other << 4));
+  }
+  if (moves_out && tid == 0) moves_out[row] = moves;
+}
+
+// ---------------------------------------------------------------------------
+
+// Both launches cover rows row0 .. row0 + rows - 1 of each of E experts (N
+// rows each); G holds E * rows * K doubles.
+hipError_t launch_flip_grad(const void* w, bool w_f32, const float* s, const float* H, const uint8_t* codes,
+                            const uint8_t* scales, int E, int64_t row0, int64_t rows, int64_t N, int64_t K,
+                            double* G, hipStream_t stream) {
+  const dim3 grid((unsigned)ceil_div(rows, kGTile), (unsigned)(K / kGTile), (unsigned)E);
+  if (w_f32)
+    hipLaunchKernelGGL(flip_grad_kernel<4>, grid, dim3(256), 0, stream, w, s, H, codes, scales, row0, rows, N, K, G);
+  else
+    hipLaunchKernelGGL(flip_grad_kernel<2>, grid, dim3(256), 0, stream, w, s, H, codes, scales, row0, rows, N, K, G);
+  return hipGetLastError();
+}
+
+namespace {
+struct RoundsArgs {
+  const float* H; int E; int64_t row0, rows, N, K; int max_rounds; const double* G;
+  uint8_t* codes; const uint8_t* scales; int32_t* moves; hipStream_t stream;
+};
+
+template <int NT, int KPT>
+void launch_rounds_t(const RoundsArgs& a) {
+  hipLaunchKernelGGL((flip_rounds_kernel<NT, KPT>), dim3((unsigned)a.rows, (unsigned)a.E), dim3(NT), 0, a.stream,
+                     a.H, a.row0, a.rows, a.N, a.K, a.max_rounds, a.G, a.codes, a.scales, a.moves);
+}
+
+template <int NT>
+bool launch_rounds_nt(int kpt, const RoundsArgs& a) {
+  switch (kpt) {
+    case 4: launch_rounds_t<NT, 4>(a); return true;
+    case 8: launch_rounds_t<NT, 8>(a); return true;
+    case 12: launch_rounds_t<NT, 12>(a); return true;
+    case 16: launch_rounds_t<NT, 16>(a); return true;
+    case 20: launch_rounds_t<NT, 20>(a); return true;
+    case 24: launch_rounds_t<NT, 24>(a); return true;
+    case 28: launch_rounds_t<NT, 28>(a); return true;
+    case 32: launch_rounds_t<NT, 32>(a); return true;
+    default: return false;
+  }
+}
+}  // namespace
+
+// Rows per block thread layout: 256 threads up to K = 8192, 1024 threads up
+// to K = 32768; each thread holds ceil(K / threads) coordinates (rounded up
+// to a multiple of 4).
+hipError_t launch_flip_rounds(const float* H, int E, int64_t row0, int64_t rows, int64_t N, int64_t K,
+                              int max_rounds, const double* G, uint8_t* codes, const uint8_t* scales, int32_t* moves,
+                              hipStream_t stream) {
+  const int nt = K <= 8192 ? 256 : 1024;
+  const int kpt = (int)((ceil_div(K, nt) + 3) / 4 * 4);
+  const RoundsArgs a{H, E, row0, rows, N, K, max_rounds, G, codes, scales, moves, stream};
+  const bool ok = nt == 256 ? launch_rounds_nt<256>(kpt, a) : launch_rounds_nt<1024>(kpt, a);
+  if (!ok) return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+}  // namespace macaq

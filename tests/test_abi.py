@@ -132,6 +132,27 @@ def test_prepare_weights_hessian_validation():
     assert ph(A16, 9, A16, A16, 1, 8, 64, A16, A16, None) == UNSUPPORTED
 
 
+def test_flip_refine_validation_and_workspace():
+    mx.lib()
+    fr = mx.macaq_flip_refine
+    need = mx.flip_refine_workspace_bytes(128, 256)
+    assert need == 128 * 256 * 8
+    assert mx.flip_refine_workspace_bytes(1, 256) == need          # rounded up to 128 rows
+    assert mx.flip_refine_workspace_bytes(0, 256) == 0
+    # w, dtype, s, h, E, N, K, max_rounds, codes, scales, moves, ws, ws_bytes
+    assert fr(A16, 0, A16, A16, 1, 8, 96, 4, A16, A16, None, A16, need, None) == UNSUPPORTED   # K % 128
+    assert fr(A16, 0, A16, A16, 1, 8, 32768, 4, A16, A16, None, A16, 1 << 40, None) == UNSUPPORTED
+    assert fr(A16, 0, A16, A16, 1, 8, 100, 4, A16, A16, None, A16, need, None) == INVALID
+    assert fr(A16, 0, A16, A16, 1, 0, 256, 4, A16, A16, None, A16, need, None) == INVALID
+    assert fr(A16, 0, A16, A16, 1, 8, 256, -1, A16, A16, None, A16, need, None) == INVALID
+    assert fr(A16, 0, A16, None, 1, 8, 256, 4, A16, A16, None, A16, need, None) == INVALID
+    assert fr(A16, 0, A16, A16, 1, 8, 256, 4, A16 + 8, A16, None, A16, need, None) == INVALID
+    assert fr(A16, 0, A16, A16, 1, 8, 256, 4, A16, A16, None, A16, need - 1, None) == WORKSPACE
+    assert fr(A16, 0, A16, A16, 1, 8, 256, 4, A16, A16, None, None, need, None) == WORKSPACE
+    assert fr(A16, 0, A16, A16, 1, 8, 256, 4, A16, A16, None, A16 + 64, need, None) == INVALID   # ws alignment
+    assert fr(A16, 2, A16, A16, 1, 8, 256, 4, A16, A16, None, A16, need, None) == UNSUPPORTED
+
+
 def test_valid_calls_without_a_device_report_no_device():
     import torch
     if torch.cuda.is_available():
@@ -140,6 +161,7 @@ def test_valid_calls_without_a_device_report_no_device():
     assert gm() == NO_DEVICE
     assert mx.macaq_hessian(A16, 0, A16, None, 1, 16, 128, A16, None) == NO_DEVICE
     assert mx.macaq_prepare_weights_hessian(A16, 0, A16, A16, 1, 8, 64, A16, A16, None) == NO_DEVICE
+    assert mx.macaq_flip_refine(A16, 0, A16, A16, 1, 8, 256, 4, A16, A16, None, A16, 1 << 20, None) == NO_DEVICE
     assert b"no HIP device" in mx.lib().macaq_last_error()
 
 
