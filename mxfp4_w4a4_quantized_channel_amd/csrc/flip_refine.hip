@@ -68,13 +68,6 @@ __device__ __forceinline__ float e2m1_mag(uint32_t m) {
 // 2^(b - 127) as fp64 (b <= 254).
 __device__ __forceinline__ double scale_f64(uint32_t b) { return __longlong_as_double((long long)(b + 896u) << 52); }
 
-// Distance from signed level L to L + 1 (L in -7..6), in units of the scale:
-// magnitude steps are 0.5 (below 2), 1 (2..4) and 2 (4..6).
-__device__ __forceinline__ double level_step_up(int L) {
-  const int m = L >= 0 ? L : -L - 1;
-  return m < 4 ? 0.5 : (m < 6 ? 1.0 : 2.0);
-}
-
 __device__ __forceinline__ int code_level(uint32_t c) {
   const int m = (int)(c & 7u);
   return (c & 8u) ? -m : m;
@@ -205,7 +198,6 @@ __global__ __launch_bounds__(256) void flip_grad_kernel(const void* __restrict__
 // with row k of H while the owner of k moves its code.
 struct Best {
   double gain;
-  double delta;
   int cand;
 };
 
@@ -248,12 +240,37 @@ __device__ __forceinline__ int wave_min_i(int v) {
              min(__builtin_amdgcn_readlane(v, 32), __builtin_amdgcn_readlane(v, 48)));
 }
 
-// Waves per SIMD the register budget aims at: more resident rows hide more of
-// each round's latency (256 threads: 3 waves fit up to 20 coordinates per
-// thread without spilling).
-template <int NT, int KPT>
-constexpr int flip_waves() { return NT == 256 && KPT <= 20 ? 3 : (NT == 256 ? 2 : 4); }
+// Exponent (-1, 0 or 1) of the magnitude step from level L to L + 1 (0.5
+// below 2, 1 from 2 to 4, 2 from 4 to 6).
+__device__ __forceinline__ int step_exp(int L) {
+  const int m = L >= 0 ? L : -L - 1;
+  return (m >= 4) + (m >= 6) - 1;
+}
 
+// Waves per SIMD the register budget aims at: more resident rows hide more of
+// each round's latency (about 6 VGPRs per coordinate plus 25).
+template <int NT, int KPT>
+constexpr int flip_waves() { return NT == 1024 || KPT <= 20 ? 4 : (KPT <= 28 ? 3 : 2); }
+
+// A candidate move is keyed (k << 10) | (up << 9) | (p + 256): k and the
+// direction give the tie order (k ascending, down before up); p is the
+// exponent of |delta| = 2^p (delta = +-step * 2^(b - 127), a power of two),
+// carried so that every thread can rebuild delta from the winning key.  Every
+// product with delta is then an exact ldexp: delta g_k = +-ldexp(g_k, p),
+// delta^2 H_kk / 2 = ldexp(H_kk, 2p - 1), delta H[k, i] = +-ldexp(H[k, i], p).
+//
+// Per coordinate one word holds what the scan needs and what changes only
+// when that coordinate moves: the code (bits 0-3), the down key's low bits
+// pd + 256 (bits 4-12), the up key's low bits 512 | (pu + 256) (bits 13-22),
+// and whether a down / up move exists (bits 23 / 24; both clear past K).
+constexpr uint32_t kCanDown = 1u << 23, kCanUp = 1u << 24;
+
+__device__ __forceinline__ uint32_t coord_word(uint32_t code, int e0) {
+  const int L = code_level(code);
+  const int pd = step_exp(L - 1) + e0, pu = step_exp(L) + e0;
+  return code | ((uint32_t)(pd + 256) << 4) | ((uint32_t)(512 | (pu + 256)) << 13) |
+         (L > -7 ? kCanDown : 0u) | (L < 7 ? kCanUp : 0u);
+}
 template <int NT, int KPT>
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(flip_waves<NT, KPT>())))
 void flip_rounds_kernel(const float* __restrict__ H, int64_t row0, int64_t rows, int64_t N, int64_t K,
@@ -277,7 +294,7 @@ void flip_rounds_kernel(const float* __restrict__ H, int64_t row0, int64_t rows,
   const int Ki = (int)K;
 
   double g[KPT];
-  uint32_t info[KPT];   // code | scale byte << 8; bit 31 marks a coordinate past K
+  uint32_t info[KPT];   // coord_word of each coordinate
 #pragma unroll
   for (int m = 0; m < KPT; ++m) {
     const int64_t k = tid + (int64_t)NT * m;
@@ -285,70 +302,70 @@ void flip_rounds_kernel(const float* __restrict__ H, int64_t row0, int64_t rows,
       g[m] = G[rl * K + k];
       diag[m][tid] = H[k * K + k];
       const uint32_t byte = codes[row * (K / 2) + (k >> 1)];
-      info[m] = ((byte >> (4 * (k & 1))) & 0xFu) | ((uint32_t)scales[row * G32 + (k >> 5)] << 8);
+      info[m] = coord_word((byte >> (4 * (k & 1))) & 0xFu, (int)scales[row * G32 + (k >> 5)] - 127);
     } else {
       g[m] = 0.0;
       diag[m][tid] = 0.0f;
-      info[m] = 0x80000000u;
+      info[m] = 0u;
     }
   }
 
   const double ninf = -__builtin_inf();
   int moves = 0;
   for (int r = 0; r < max_rounds; ++r) {
-    // keep per-coordinate values derived from info (level, scale) out of the
-    // registers between rounds: they are recomputed each round
+    // keep per-coordinate values derived from info out of the registers
+    // between rounds: they are recomputed each round
 #pragma unroll
     for (int m = 0; m < KPT; ++m) asm volatile("" : "+v"(info[m]));
+    // likewise the coordinate indices (tid + NT * m): one register, rebuilt
+    int t_r = tid;
+    asm volatile("" : "+v"(t_r));
     // scan, without branches: candidates in the order k ascending, down
-    // (2k) before up (2k + 1); a later candidate replaces the best only if
-    // strictly better
-    double bg = ninf, bd = 0.0;
+    // before up; a later candidate replaces the best only if strictly better
+    double bg = ninf;
     int bc = 0x7FFFFFFF;
 #pragma unroll
     for (int m = 0; m < KPT; ++m) {
       const uint32_t in = info[m];
-      const bool valid = !(in & 0x80000000u);
-      const int L = code_level(in & 0xFu);
-      const double sc = scale_f64((in >> 8) & 0xFFu);
-      const int k2 = 2 * (tid + NT * m);
+      const int fd = (int)((in >> 4) & 511u), fu = (int)((in >> 13) & 1023u);
+      const int pd = fd - 256, pu = (fu & 511) - 256;
       const double hk = (double)diag[m][tid];
-      const double dl = -level_step_up(L - 1) * sc;
-      const double du = level_step_up(L) * sc;
-      double gl = dl * g[m] - 0.5 * dl * dl * hk;
-      double gu = du * g[m] - 0.5 * du * du * hk;
-      gl = (valid && L > -7) ? gl : ninf;
-      gu = (valid && L < 7) ? gu : ninf;
-      const bool tl = gl > bg;
-      bg = tl ? gl : bg; bd = tl ? dl : bd; bc = tl ? k2 : bc;
+      double gd = -ldexp(g[m], pd) - ldexp(hk, 2 * pd - 1);
+      double gu = ldexp(g[m], pu) - ldexp(hk, 2 * pu - 1);
+      gd = (in & kCanDown) ? gd : ninf;
+      gu = (in & kCanUp) ? gu : ninf;
+      const int kk = (t_r + NT * m) << 10;
+      const bool td = gd > bg;
+      bg = td ? gd : bg; bc = td ? (kk | fd) : bc;
       const bool tu = gu > bg;
-      bg = tu ? gu : bg; bd = tu ? du : bd; bc = tu ? k2 + 1 : bc;
+      bg = tu ? gu : bg; bc = tu ? (kk | fu) : bc;
     }
-    // wave: the largest gain, then the lowest candidate holding it, then
-    // that candidate's step
+    // wave: the largest gain, then the lowest key holding it
     const double wg = wave_max_d(bg);
     const int wc = wave_min_i(bg == wg ? bc : 0x7FFFFFFF);
-    const unsigned long long owner = __ballot(bc == wc);
-    const double wd = readlane_d(bd, (int)__builtin_ctzll(owner | (1ull << 63)));
-    if (lane == 0) red[r & 1][wave] = Best{wg, wd, wc};
+    if (lane == 0) red[r & 1][wave] = Best{wg, wc};
     __syncthreads();
-    bg = red[r & 1][0].gain; bd = red[r & 1][0].delta; bc = red[r & 1][0].cand;
+    bg = red[r & 1][0].gain; bc = red[r & 1][0].cand;
 #pragma unroll
     for (int v = 1; v < NW; ++v) {
       const Best o = red[r & 1][v];
-      if (better(o.gain, o.cand, bg, bc)) { bg = o.gain; bd = o.delta; bc = o.cand; }
+      if (better(o.gain, o.cand, bg, bc)) { bg = o.gain; bc = o.cand; }
     }
     if (!(bg > 0.0)) break;   // uniform: every thread holds the same best
-    const int kb = bc >> 1;
+    const int kb = bc >> 10;
+    const bool up = (bc >> 9) & 1;
+    const int p = (bc & 511) - 256;
     const float* hrow = H + (int64_t)kb * K;
 #pragma unroll
     for (int m = 0; m < KPT; ++m) {
-      const int k = tid + NT * m;
-      g[m] = g[m] - bd * (double)hrow[k < Ki ? k : Ki - 1];   // entries past K are never read back
+      const int k = t_r + NT * m;
+      const double t = ldexp((double)hrow[k < Ki ? k : Ki - 1], p);   // entries past K are never read back
+      g[m] = up ? g[m] - t : g[m] + t;                                // g - delta H[k, :]
       if (k == kb) {
         const uint32_t old = info[m] & 0xFu;
-        const int L = code_level(old) + ((bc & 1) ? 1 : -1);
-        info[m] = (info[m] & ~0xFu) | level_to_code(L, old);
+        const int L = code_level(old);
+        const int e0 = (int)((info[m] >> 4) & 511u) - 256 - step_exp(L - 1);   // scale exponent b - 127
+        info[m] = coord_word(level_to_code(L + (up ? 1 : -1), old), e0);
       }
     }
     ++moves;
