@@ -39,6 +39,14 @@ namespace macaq {
 
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v16f __attribute__((ext_vector_type(16)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+// y is written once and never read back by the GEMM: its stores are
+// non-temporal, so they stream past the caches instead of evicting the A and
+// W' panels the other blocks are still reading (measured: attn-proj 33.2 ->
+// 28.4 us, down-prefill 144 -> 125 us, MoE 39.9 -> 36.0 us).
 
 __device__ __forceinline__ v8i as_operand(const uint4& q) {
   v8i r;
@@ -98,7 +106,7 @@ __device__ __forceinline__ void store_wave_tile(const v16f (&acc)[FM][FN], void*
         for (int ni = 0; ni < FN; ++ni) {
           float* yp = reinterpret_cast<float*>(Y) + (m0 + mi * 32 + 4 * h) * N + n0 + ni * 32 + r32;
 #pragma unroll
-          for (int r = 0; r < 16; ++r) yp[(8 * (r >> 2) + (r & 3)) * N] = acc[mi][ni][r];
+          for (int r = 0; r < 16; ++r) __builtin_nontemporal_store(acc[mi][ni][r], &yp[(8 * (r >> 2) + (r & 3)) * N]);
         }
       return;
     }
@@ -110,7 +118,7 @@ __device__ __forceinline__ void store_wave_tile(const v16f (&acc)[FM][FN], void*
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int64_t m = m0 + mi * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
-          if (m < row_end && n < N) reinterpret_cast<float*>(Y)[m * N + n] = acc[mi][ni][r];
+          if (m < row_end && n < N) __builtin_nontemporal_store(acc[mi][ni][r], reinterpret_cast<float*>(Y) + m * N + n);
         }
       }
   } else {
@@ -193,7 +201,7 @@ __device__ __forceinline__ void store_wave_tile_lds(const v16f (&acc)[FM][FN], f
               uint2 q;
               q.x = (uint32_t)f32_to_bf16_rne(o[0]) | ((uint32_t)f32_to_bf16_rne(o[1]) << 16);
               q.y = (uint32_t)f32_to_bf16_rne(o[2]) | ((uint32_t)f32_to_bf16_rne(o[3]) << 16);
-              *reinterpret_cast<uint2*>(yp) = q;
+              __builtin_nontemporal_store(u32x2{q.x, q.y}, reinterpret_cast<u32x2*>(yp));
             } else {
 #pragma unroll
               for (int k = 0; k < 4; ++k)
@@ -202,7 +210,7 @@ __device__ __forceinline__ void store_wave_tile_lds(const v16f (&acc)[FM][FN], f
           } else {
             float* yp = reinterpret_cast<float*>(Y) + m * ldo + j0;
             if (n + 8 <= N && (reinterpret_cast<uintptr_t>(yp) & 15) == 0) {
-              *reinterpret_cast<float4*>(yp) = make_float4(o[0], o[1], o[2], o[3]);
+              __builtin_nontemporal_store(f32x4{o[0], o[1], o[2], o[3]}, reinterpret_cast<f32x4*>(yp));
             } else {
 #pragma unroll
               for (int k = 0; k < 4; ++k)
@@ -217,7 +225,7 @@ __device__ __forceinline__ void store_wave_tile_lds(const v16f (&acc)[FM][FN], f
             q.y = (uint32_t)f32_to_bf16_rne(v[2]) | ((uint32_t)f32_to_bf16_rne(v[3]) << 16);
             q.z = (uint32_t)f32_to_bf16_rne(v[4]) | ((uint32_t)f32_to_bf16_rne(v[5]) << 16);
             q.w = (uint32_t)f32_to_bf16_rne(v[6]) | ((uint32_t)f32_to_bf16_rne(v[7]) << 16);
-            *reinterpret_cast<uint4*>(yp) = q;
+            __builtin_nontemporal_store(u32x4{q.x, q.y, q.z, q.w}, reinterpret_cast<u32x4*>(yp));
           } else {
 #pragma unroll
             for (int k = 0; k < 8; ++k)
