@@ -88,7 +88,7 @@ __device__ __forceinline__ uint32_t level_to_code(int L, uint32_t old_code) {
 // the dequantized code) into LDS as fp64 [32][128]; all threads stage the
 // matching 32 rows of H (fp32 -> fp64) as [32][128]; every thread then
 // accumulates its 8x8 outputs (rows ty + 16a, columns tx + 16c) over the 32
-// values in order, a multiply then an add.
+// values in order, a multiply then an add (fused when that is exact).
 template <int EB>
 __global__ __launch_bounds__(256) void flip_grad_kernel(const void* __restrict__ w, const float* __restrict__ s,
                                                         const float* __restrict__ H, const uint8_t* __restrict__ codes,
@@ -126,6 +126,7 @@ __global__ __launch_bounds__(256) void flip_grad_kernel(const void* __restrict__
     const int64_t col = 32 * g;
     if (tid < 32) rs[tid] = 1.0f / s[col + tid];
     __syncthreads();
+    int exact = 1;   // every d of this step has at most 29 significant bits
     if (tid < kGTile) {
       if (tasker) {
         const int64_t row = row0 + my_row;
@@ -153,7 +154,9 @@ __global__ __launch_bounds__(256) void flip_grad_kernel(const void* __restrict__
           const uint32_t c = (cw[i >> 3] >> (4 * (i & 7))) & 0xFu;
           const float m = e2m1_mag(c & 7u);
           const double deq = (double)((c & 8u) ? -m : m) * sc;
-          da[i][tid] = (double)(t[i] * cn) - deq;
+          const double d = (double)(t[i] * cn) - deq;
+          exact &= (__double2loint(d) & 0xFFFFFF) == 0;
+          da[i][tid] = d;
         }
       } else {
 #pragma unroll
@@ -165,18 +168,37 @@ __global__ __launch_bounds__(256) void flip_grad_kernel(const void* __restrict__
       const int idx = tid + 256 * q;          // 32 x 128 entries
       hb[idx >> 7][idx & 127] = (double)H[(col + (idx >> 7)) * K + i0 + (idx & 127)];
     }
-    __syncthreads();
+    // A d with at most 29 significant bits times an fp32 H entry (24 bits)
+    // is exact in fp64, so a fused multiply-add rounds exactly like the
+    // multiply-then-add of the stated order; round-to-nearest start codes
+    // always qualify (d is a multiple of 2^(e-25) below 2^(e+3)).  Any other
+    // step takes the separate multiply and add.
+    if (__syncthreads_and(exact)) {
 #pragma unroll 4
-    for (int jj = 0; jj < 32; ++jj) {
-      double av[8], bv[8];
+      for (int jj = 0; jj < 32; ++jj) {
+        double av[8], bv[8];
 #pragma unroll
-      for (int a = 0; a < 8; ++a) av[a] = da[jj][ty + 16 * a];
+        for (int a = 0; a < 8; ++a) av[a] = da[jj][ty + 16 * a];
 #pragma unroll
-      for (int c = 0; c < 8; ++c) bv[c] = hb[jj][tx + 16 * c];
+        for (int c = 0; c < 8; ++c) bv[c] = hb[jj][tx + 16 * c];
 #pragma unroll
-      for (int a = 0; a < 8; ++a)
+        for (int a = 0; a < 8; ++a)
 #pragma unroll
-        for (int c = 0; c < 8; ++c) acc[a][c] = acc[a][c] + av[a] * bv[c];
+          for (int c = 0; c < 8; ++c) acc[a][c] = __builtin_fma(av[a], bv[c], acc[a][c]);
+      }
+    } else {
+#pragma unroll 4
+      for (int jj = 0; jj < 32; ++jj) {
+        double av[8], bv[8];
+#pragma unroll
+        for (int a = 0; a < 8; ++a) av[a] = da[jj][ty + 16 * a];
+#pragma unroll
+        for (int c = 0; c < 8; ++c) bv[c] = hb[jj][tx + 16 * c];
+#pragma unroll
+        for (int a = 0; a < 8; ++a)
+#pragma unroll
+          for (int c = 0; c < 8; ++c) acc[a][c] = acc[a][c] + av[a] * bv[c];
+      }
     }
     __syncthreads();
   }

@@ -114,6 +114,22 @@ def test_flip_experts_random_coupled_hessians_and_chunks():
         assert np.array_equal(moves[e].cpu().numpy(), out[e][1])
 
 
+def test_flip_arbitrary_start_codes():
+    """Start codes that are not round-to-nearest (random codes in some
+    groups): their residuals carry more than 29 significant bits, so the
+    gradient kernel takes the separate multiply and add for those column
+    steps; codes and moves stay bit-exact."""
+    wl, h = calib_case(2, 64, 512)
+    say("flip from arbitrary start codes N64 K512")
+    s = wl.s.numpy()
+    c0, s0 = oracle.prepare_weights(host(wl.w[0]), s[0])
+    rng = np.random.default_rng(np.random.SeedSequence([17, 3]))
+    c0 = c0.copy()
+    cols = np.concatenate([np.arange(16 * g, 16 * g + 16) for g in (1, 2, 9)])   # groups 1, 2 and 9
+    c0[:, cols] = rng.integers(0, 256, (c0.shape[0], cols.size), dtype=np.uint8)
+    assert check(run_both(wl.w, s, h, (c0[None], s0[None]), 10000), "arbitrary start") > 0
+
+
 def test_flip_wide_rows_1024_threads():
     """K = 8320 (above 8192: 1024 threads per row, 12 coordinates each, the
     last ones past K masked)."""
