@@ -332,6 +332,15 @@ void flip_rounds_kernel(const float* __restrict__ H, int64_t row0, int64_t rows,
     }
   }
 
+  // With H_kk >= 0 a move can gain only in the direction of g_k (the other
+  // gain is -|delta g_k| - delta^2 H_kk / 2 <= 0), and only positive gains
+  // can win, so one candidate per coordinate suffices.  A row with some
+  // H_kk < 0 scans both directions.
+  int neg_diag = 0;
+#pragma unroll
+  for (int m = 0; m < KPT; ++m) neg_diag |= diag[m][tid] < 0.0f;
+  const bool both = __syncthreads_or(neg_diag) != 0;
+
   const double ninf = -__builtin_inf();
   int moves = 0;
   for (int r = 0; r < max_rounds; ++r) {
@@ -342,25 +351,42 @@ void flip_rounds_kernel(const float* __restrict__ H, int64_t row0, int64_t rows,
     // likewise the coordinate indices (tid + NT * m): one register, rebuilt
     int t_r = tid;
     asm volatile("" : "+v"(t_r));
-    // scan, without branches: candidates in the order k ascending, down
-    // before up; a later candidate replaces the best only if strictly better
+    // scan, without branches: candidates in the order k ascending (down
+    // before up when both are scanned); a later candidate replaces the best
+    // only if strictly better
     double bg = ninf;
     int bc = 0x7FFFFFFF;
+    if (!both) {
 #pragma unroll
-    for (int m = 0; m < KPT; ++m) {
-      const uint32_t in = info[m];
-      const int fd = (int)((in >> 4) & 511u), fu = (int)((in >> 13) & 1023u);
-      const int pd = fd - 256, pu = (fu & 511) - 256;
-      const double hk = (double)diag[m][tid];
-      double gd = -ldexp(g[m], pd) - ldexp(hk, 2 * pd - 1);
-      double gu = ldexp(g[m], pu) - ldexp(hk, 2 * pu - 1);
-      gd = (in & kCanDown) ? gd : ninf;
-      gu = (in & kCanUp) ? gu : ninf;
-      const int kk = (t_r + NT * m) << 10;
-      const bool td = gd > bg;
-      bg = td ? gd : bg; bc = td ? (kk | fd) : bc;
-      const bool tu = gu > bg;
-      bg = tu ? gu : bg; bc = tu ? (kk | fu) : bc;
+      for (int m = 0; m < KPT; ++m) {
+        const uint32_t in = info[m];
+        const bool up = g[m] > 0.0;
+        const int f = up ? (int)((in >> 13) & 1023u) : (int)((in >> 4) & 511u);
+        const int p = (f & 511) - 256;
+        const double hk = (double)diag[m][tid];
+        // delta g_k = |delta| |g_k| in the chosen direction
+        double gn = ldexp(fabs(g[m]), p) - ldexp(hk, 2 * p - 1);
+        gn = (in & (up ? kCanUp : kCanDown)) ? gn : ninf;
+        const bool t = gn > bg;
+        bg = t ? gn : bg; bc = t ? (((t_r + NT * m) << 10) | f) : bc;
+      }
+    } else {
+#pragma unroll
+      for (int m = 0; m < KPT; ++m) {
+        const uint32_t in = info[m];
+        const int fd = (int)((in >> 4) & 511u), fu = (int)((in >> 13) & 1023u);
+        const int pd = fd - 256, pu = (fu & 511) - 256;
+        const double hk = (double)diag[m][tid];
+        double gd = -ldexp(g[m], pd) - ldexp(hk, 2 * pd - 1);
+        double gu = ldexp(g[m], pu) - ldexp(hk, 2 * pu - 1);
+        gd = (in & kCanDown) ? gd : ninf;
+        gu = (in & kCanUp) ? gu : ninf;
+        const int kk = (t_r + NT * m) << 10;
+        const bool td = gd > bg;
+        bg = td ? gd : bg; bc = td ? (kk | fd) : bc;
+        const bool tu = gu > bg;
+        bg = tu ? gu : bg; bc = tu ? (kk | fu) : bc;
+      }
     }
     // wave: the largest gain, then the lowest key holding it
     const double wg = wave_max_d(bg);

@@ -130,6 +130,24 @@ def test_flip_arbitrary_start_codes():
     assert check(run_both(wl.w, s, h, (c0[None], s0[None]), 10000), "arbitrary start") > 0
 
 
+def test_flip_negative_diagonal_scans_both_directions():
+    """A symmetric but indefinite H with some negative diagonal entries: a
+    move against the sign of g_k can then gain, so the kernel scans both
+    directions for such rows; codes and moves stay bit-exact."""
+    N, K = 48, 256
+    rng = np.random.default_rng(np.random.SeedSequence([17, 4]))
+    w = torch.from_numpy((rng.standard_normal((1, N, K)) * 0.02).astype(np.float32)).to(torch.bfloat16)
+    s = rng.uniform(0.5, 2.0, (1, K)).astype(np.float32)
+    a = rng.standard_normal((K, 64))
+    h = a @ a.T
+    neg = rng.choice(K, 12, replace=False)
+    h[neg, neg] = -rng.uniform(1.0, 30.0, 12)
+    h = h.astype(np.float32)[None]
+    start = oracle.prepare_weights(host(w[0]), s[0])
+    say(f"flip negative diagonal N{N} K{K}")
+    assert check(run_both(w, s, h, (start[0][None], start[1][None]), 300), "negative diagonal") > 0
+
+
 def test_flip_wide_rows_1024_threads():
     """K = 8320 (above 8192: 1024 threads per row, 12 coordinates each, the
     last ones past K masked)."""
