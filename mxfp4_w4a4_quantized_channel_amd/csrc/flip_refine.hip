@@ -407,13 +407,19 @@ void flip_rounds_kernel(const float* __restrict__ H, int64_t row0, int64_t rows,
 #pragma unroll
     for (int m = 0; m < KPT; ++m) {
       const int k = t_r + NT * m;
-      const double t = ldexp((double)hrow[k < Ki ? k : Ki - 1], p);   // entries past K are never read back
-      g[m] = up ? g[m] - t : g[m] + t;                                // g - delta H[k, :]
-      if (k == kb) {
-        const uint32_t old = info[m] & 0xFu;
-        const int L = code_level(old);
-        const int e0 = (int)((info[m] >> 4) & 511u) - 256 - step_exp(L - 1);   // scale exponent b - 127
-        info[m] = coord_word(level_to_code(L + (up ? 1 : -1), old), e0);
+      const float hv = hrow[k < Ki ? k : Ki - 1];                        // entries past K are never read back
+      g[m] = g[m] + ldexp((double)(up ? -hv : hv), p);                  // g - delta H[k, :]
+    }
+    const int mo = kb / NT;                                              // the owner's coordinate slot
+    if (kb - mo * NT == t_r) {
+#pragma unroll
+      for (int m = 0; m < KPT; ++m) {
+        if (m == mo) {
+          const uint32_t old = info[m] & 0xFu;
+          const int L = code_level(old);
+          const int e0 = (int)((info[m] >> 4) & 511u) - 256 - step_exp(L - 1);   // scale exponent b - 127
+          info[m] = coord_word(level_to_code(L + (up ? 1 : -1), old), e0);
+        }
       }
     }
     ++moves;
