@@ -262,12 +262,15 @@ def bench_offline(args):
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) / args.steps * 1e3
 
+    def search_grad(i):                        # flip with 0 rounds: the gradient kernel (the rounds
+        search(i)                              # kernel exits at once), on the codes the chain refines
+        flip(0)
+
     h_us = kernel_us(hess)
     s_us = kernel_us(search)
     sf_us = kernel_us(search_flip)
-    g_us = kernel_us(lambda i: flip(0))         # the gradient kernel (the rounds kernel exits at once)
-    f_us = sf_us - s_us
-    r_us = f_us - g_us
+    g_us = kernel_us(search_grad) - s_us
+    r_us = sf_us - s_us - g_us
     h_flops = float(T) * K * (K + 1)           # one FMA per row for each distinct entry of the symmetric H
     s_ops = float(E) * N * (K // 32) * SEARCH_OPS_PER_GROUP
     g_ops = 2.0 * E * N * K * K                # a multiply-add (2 flops) per (row, j, i)
