@@ -274,7 +274,7 @@ __device__ __forceinline__ int step_exp(int L) {
 template <int NT, int KPT>
 constexpr int flip_waves() { return NT == 1024 || KPT <= 20 ? 4 : (KPT <= 28 ? 3 : 2); }
 
-// A candidate move is keyed (k << 10) | (up << 9) | (p + 256): k and the
+// A candidate move is keyed (k << 12) | (up << 11) | (p + 1024): k and the
 // direction give the tie order (k ascending, down before up); p is the
 // exponent of |delta| = 2^p (delta = +-step * 2^(b - 127), a power of two),
 // carried so that every thread can rebuild delta from the winning key.  Every
@@ -283,15 +283,26 @@ constexpr int flip_waves() { return NT == 1024 || KPT <= 20 ? 4 : (KPT <= 28 ? 3
 //
 // Per coordinate one word holds what the scan needs and what changes only
 // when that coordinate moves: the code (bits 0-3), the down key's low bits
-// pd + 256 (bits 4-12), the up key's low bits 512 | (pu + 256) (bits 13-22),
-// and whether a down / up move exists (bits 23 / 24; both clear past K).
-constexpr uint32_t kCanDown = 1u << 23, kCanUp = 1u << 24;
+// p + 1024 (bits 4-15), the up key's low bits 2048 | (p + 1024) (bits
+// 16-27), and whether a down / up move exists (bits 28 / 29; both clear past
+// K).  A move that does not exist (past +-6, or past K) carries p = 700
+// instead: with H_kk > 0, ldexp(H_kk, 1399) is +inf and its gain is -inf or
+// NaN, which never compares greater, so the one-direction scan needs no test.
+constexpr uint32_t kCanDown = 1u << 28, kCanUp = 1u << 29;
+constexpr int kNoMove = 700;
 
 __device__ __forceinline__ uint32_t coord_word(uint32_t code, int e0) {
   const int L = code_level(code);
-  const int pd = step_exp(L - 1) + e0, pu = step_exp(L) + e0;
-  return code | ((uint32_t)(pd + 256) << 4) | ((uint32_t)(512 | (pu + 256)) << 13) |
+  const int pd = L > -7 ? step_exp(L - 1) + e0 : kNoMove, pu = L < 7 ? step_exp(L) + e0 : kNoMove;
+  return code | ((uint32_t)(pd + 1024) << 4) | ((uint32_t)(2048 | (pu + 1024)) << 16) |
          (L > -7 ? kCanDown : 0u) | (L < 7 ? kCanUp : 0u);
+}
+constexpr uint32_t kPastK = ((uint32_t)(kNoMove + 1024) << 4) | ((uint32_t)(2048 | (kNoMove + 1024)) << 16);
+
+// Scale exponent b - 127 of a coordinate, from whichever of its moves exists.
+__device__ __forceinline__ int coord_e0(uint32_t in) {
+  const int L = code_level(in & 0xFu);
+  return L > -7 ? (int)((in >> 4) & 2047u) - 1024 - step_exp(L - 1) : (int)((in >> 16) & 2047u) - 1024 - step_exp(L);
 }
 template <int NT, int KPT>
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(flip_waves<NT, KPT>())))
@@ -327,18 +338,19 @@ void flip_rounds_kernel(const float* __restrict__ H, int64_t row0, int64_t rows,
       info[m] = coord_word((byte >> (4 * (k & 1))) & 0xFu, (int)scales[row * G32 + (k >> 5)] - 127);
     } else {
       g[m] = 0.0;
-      diag[m][tid] = 0.0f;
-      info[m] = 0u;
+      diag[m][tid] = 1.0f;   // positive, so that the no-move exponent gives -inf
+      info[m] = kPastK;
     }
   }
 
   // With H_kk >= 0 a move can gain only in the direction of g_k (the other
   // gain is -|delta g_k| - delta^2 H_kk / 2 <= 0), and only positive gains
-  // can win, so one candidate per coordinate suffices.  A row with some
-  // H_kk < 0 scans both directions.
+  // can win, so one candidate per coordinate suffices; the no-move exponent
+  // needs H_kk > 0.  A row with some H_kk <= 0 scans both directions with
+  // explicit tests.
   int neg_diag = 0;
 #pragma unroll
-  for (int m = 0; m < KPT; ++m) neg_diag |= diag[m][tid] < 0.0f;
+  for (int m = 0; m < KPT; ++m) neg_diag |= !(diag[m][tid] > 0.0f);
   const bool both = __syncthreads_or(neg_diag) != 0;
 
   const double ninf = -__builtin_inf();
@@ -360,28 +372,26 @@ void flip_rounds_kernel(const float* __restrict__ H, int64_t row0, int64_t rows,
 #pragma unroll
       for (int m = 0; m < KPT; ++m) {
         const uint32_t in = info[m];
-        const bool up = g[m] > 0.0;
-        const int f = up ? (int)((in >> 13) & 1023u) : (int)((in >> 4) & 511u);
-        const int p = (f & 511) - 256;
+        const int f = (int)((in >> (g[m] > 0.0 ? 16 : 4)) & 4095u);   // the move toward g's sign
+        const int p = (f & 2047) - 1024;
         const double hk = (double)diag[m][tid];
         // delta g_k = |delta| |g_k| in the chosen direction
-        double gn = ldexp(fabs(g[m]), p) - ldexp(hk, 2 * p - 1);
-        gn = (in & (up ? kCanUp : kCanDown)) ? gn : ninf;
+        const double gn = ldexp(fabs(g[m]), p) - ldexp(hk, 2 * p - 1);
         const bool t = gn > bg;
-        bg = t ? gn : bg; bc = t ? (((t_r + NT * m) << 10) | f) : bc;
+        bg = t ? gn : bg; bc = t ? (((t_r + NT * m) << 12) | f) : bc;
       }
     } else {
 #pragma unroll
       for (int m = 0; m < KPT; ++m) {
         const uint32_t in = info[m];
-        const int fd = (int)((in >> 4) & 511u), fu = (int)((in >> 13) & 1023u);
-        const int pd = fd - 256, pu = (fu & 511) - 256;
+        const int fd = (int)((in >> 4) & 4095u), fu = (int)((in >> 16) & 4095u);
+        const int pd = fd - 1024, pu = (fu & 2047) - 1024;
         const double hk = (double)diag[m][tid];
         double gd = -ldexp(g[m], pd) - ldexp(hk, 2 * pd - 1);
         double gu = ldexp(g[m], pu) - ldexp(hk, 2 * pu - 1);
         gd = (in & kCanDown) ? gd : ninf;
         gu = (in & kCanUp) ? gu : ninf;
-        const int kk = (t_r + NT * m) << 10;
+        const int kk = (t_r + NT * m) << 12;
         const bool td = gd > bg;
         bg = td ? gd : bg; bc = td ? (kk | fd) : bc;
         const bool tu = gu > bg;
@@ -400,9 +410,9 @@ void flip_rounds_kernel(const float* __restrict__ H, int64_t row0, int64_t rows,
       if (better(o.gain, o.cand, bg, bc)) { bg = o.gain; bc = o.cand; }
     }
     if (!(bg > 0.0)) break;   // uniform: every thread holds the same best
-    const int kb = bc >> 10;
-    const bool up = (bc >> 9) & 1;
-    const int p = (bc & 511) - 256;
+    const int kb = bc >> 12;
+    const bool up = (bc >> 11) & 1;
+    const int p = (bc & 2047) - 1024;
     const float* hrow = H + (int64_t)kb * K;
 #pragma unroll
     for (int m = 0; m < KPT; ++m) {
@@ -416,9 +426,7 @@ void flip_rounds_kernel(const float* __restrict__ H, int64_t row0, int64_t rows,
       for (int m = 0; m < KPT; ++m) {
         if (m == mo) {
           const uint32_t old = info[m] & 0xFu;
-          const int L = code_level(old);
-          const int e0 = (int)((info[m] >> 4) & 511u) - 256 - step_exp(L - 1);   // scale exponent b - 127
-          info[m] = coord_word(level_to_code(L + (up ? 1 : -1), old), e0);
+          info[m] = coord_word(level_to_code(code_level(old) + (up ? 1 : -1), old), coord_e0(info[m]));
         }
       }
     }
