@@ -69,3 +69,52 @@ def test_full_size(name, kw):
         got = y_np[np.ix_(rows[sel], cols)]
         ok, worst, normwise = oracle.within_tolerance(got, y_ref, S, 1e-5)
         assert ok, f"expert {e}: worst {worst:.3g} normwise {normwise:.3g}"
+
+
+FULL_EPI = [
+    ("attn-proj bf16", dict(cfg=2), mx.EPI_NONE),
+    ("attn-proj SwiGLU", dict(cfg=2), mx.EPI_SWIGLU),
+    ("decode gate/up M1 SwiGLU", dict(cfg=4, variant=0, M=1), mx.EPI_SWIGLU),
+    ("decode gate/up M32 SwiGLU", dict(cfg=4, variant=0, M=32), mx.EPI_SWIGLU),
+    ("MoE E64 expert-Zipf SwiGLU", dict(cfg=5), mx.EPI_SWIGLU),
+]
+
+
+@pytest.mark.parametrize("name,kw,epi", FULL_EPI, ids=[n for n, _, _ in FULL_EPI])
+def test_full_size_epilogues(name, kw, epi):
+    """Full-size layers with a bf16 output and/or the SwiGLU epilogue, in the
+    benchmark's launch configuration: the bf16 output equals round-to-nearest-
+    even of the same path's fp32 output everywhere, and sampled fp32 outputs
+    are within the oracle's bound (GEMM bound carried through silu(g) * u)."""
+    print(f"[case] full size epilogue {name}", flush=True)
+    wl = workloads.make(**kw)
+    M, N, K, E = wl.M, wl.N, wl.K, wl.E
+    off = wl.offsets.to(DEV) if E > 1 else None
+    x, s = wl.x.to(DEV), wl.s.to(DEV)
+    wc, wsc = mx.prepare_weights(wl.w.to(DEV), s)
+    y32 = mx.linear(x, s, wc, wsc, off, out_dtype=torch.float32, epilogue=epi)
+    y16 = mx.linear(x, s, wc, wsc, off, out_dtype=torch.bfloat16, epilogue=epi)
+    torch.cuda.synchronize()
+    y32 = y32.cpu().numpy()
+    assert np.array_equal(workloads.bf16_bits(y16.cpu()), (oracle.round_bf16(y32).view(np.uint32) >> 16).astype(np.uint16))
+
+    rng = np.random.default_rng(4321)
+    offs = wl.offsets.numpy()
+    rows = np.unique(np.concatenate([rng.choice(M, min(M, 16), replace=False), [0, M - 1]]))
+    e_rows = oracle.expert_of_rows(offs, M)[rows] if E > 1 else np.zeros(len(rows), int)
+    width = N // 2 if epi == mx.EPI_SWIGLU else N
+    outs = np.unique(np.concatenate([rng.choice(width, min(width, 16), replace=False), [0, width - 1]]))
+    wrows = np.stack([2 * outs, 2 * outs + 1], axis=1).reshape(-1) if epi == mx.EPI_SWIGLU else outs
+    xs = host(wl.x)[rows]
+    for e in np.unique(e_rows):
+        sel = np.nonzero(e_rows == e)[0]
+        rac, ras = oracle.quant_act(xs[sel], wl.s[e:e + 1].numpy())
+        rwc, rws = oracle.prepare_weights(host(wl.w[e])[wrows], wl.s[e].numpy())
+        y_ref, S = oracle.gemm(rac, ras, rwc, rws)
+        got = y32[np.ix_(rows[sel], outs)].astype(np.float64)
+        if epi == mx.EPI_SWIGLU:
+            ref, tol = oracle.swiglu(y_ref), oracle.swiglu_bound(y_ref, S, 1e-5)
+        else:
+            ref, tol = y_ref, 1e-5 * S
+        bad = np.abs(got - ref) > tol
+        assert not bad.any(), f"expert {e}: {bad.sum()} outputs beyond the bound"
