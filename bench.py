@@ -22,6 +22,7 @@ import ctypes
 import hashlib
 import json
 import os
+import subprocess
 import sys
 import time
 
@@ -91,6 +92,30 @@ def copy_calibration():
         dst.copy_(src)
     torch.cuda.synchronize()
     print(json.dumps({"copy_calibration": {"bytes_read_per_copy": n, "bytes_written_per_copy": n, "copies": 5}}))
+
+
+def gpu_state():
+    """Clock, power and temperature of GPU 0 as amd-smi reports them at this
+    moment (None where amd-smi is missing or its output is not understood).
+    A snapshot, not an average: the clock under load is the counters' figure."""
+    try:
+        r = subprocess.run(["amd-smi", "metric", "-g", "0", "--clock", "--power", "--temperature", "--json"],
+                           capture_output=True, text=True, timeout=30)
+        d = json.loads(r.stdout)
+        g = d["gpu_data"][0] if isinstance(d, dict) else d[0]
+        val = lambda *path: _dig(g, path)
+        return {"sclk_mhz": val("clock", "gfx_0", "clk", "value"), "mclk_mhz": val("clock", "mem_0", "clk", "value"),
+                "power_w": val("power", "socket_power", "value"), "hotspot_c": val("temperature", "hotspot", "value")}
+    except Exception:
+        return None
+
+
+def _dig(d, path):
+    for k in path:
+        if not isinstance(d, dict) or k not in d:
+            return None
+        d = d[k]
+    return d
 
 
 def sources_sha256(paths):
@@ -243,6 +268,7 @@ def bench_offline(args):
         search(i)
         flip(args.flip_rounds)
 
+    state_before = gpu_state()
     for i in range(args.warmup):
         chain(i)
     torch.cuda.synchronize()
@@ -251,6 +277,7 @@ def bench_offline(args):
         chain(i)
     torch.cuda.synchronize()
     ms = (time.perf_counter() - t0) / args.steps * 1e3
+    state_after = gpu_state()
 
     def kernel_us(fn):
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -311,6 +338,7 @@ def bench_offline(args):
     out["roofline"] = ks[dom]     # the dominant kernel with a roofline
     out["kernels"] = ks
     out["config"]["flip_max_rounds"] = args.flip_rounds
+    out["gpu_state"] = {"before": state_before, "after": state_after}
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline_offline(wl, rows=min(1024, N), cols=min(1024, K),
                                                    flip_rows=min(32, N), flip_rounds=args.flip_rounds)
@@ -438,6 +466,7 @@ def main():
         if st != 0:
             raise RuntimeError(mx.lib().macaq_last_error().decode())
 
+    state_before = gpu_state()
     # ---- warmup
     for i in range(args.warmup):
         run_linear(i)
@@ -450,6 +479,7 @@ def main():
         run_linear(i)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    state_after = gpu_state()
     ms_per_step = wall / args.steps * 1e3
     flops = 2.0 * M * N * K
     value = flops / (wall / args.steps) / 1e12
@@ -537,6 +567,7 @@ def main():
     if not args.no_ablation and not fused:
         out["transform_overhead"] = transform_overhead(args, mx, L, wl, xs, wss, wcs, ys, s0, off_p, stream, sp,
                                                        a_codes, a_scales, gemm_ws, M, N, K, E, R, ydt, epi)
+    out["gpu_state"] = {"before": state_before, "after": state_after}
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(wl, min(args.cpu_rows, M))
     print(json.dumps(out), flush=True)
