@@ -144,7 +144,7 @@ __device__ __forceinline__ void store_wave_tile(const v16f (&acc)[FM][FN], void*
           } else {   // bf16 pair
             uint16_t* y16 = reinterpret_cast<uint16_t*>(Y) + m * N + np;
             if (np + 1 < N && (N & 1) == 0 && (reinterpret_cast<uintptr_t>(Y) & 3) == 0) {   // 4-byte aligned pair
-              *reinterpret_cast<uint32_t*>(y16) = (uint32_t)f32_to_bf16_rne(lo) | ((uint32_t)f32_to_bf16_rne(hi) << 16);
+              *reinterpret_cast<uint32_t*>(y16) = pk_bf16_rne(lo, hi);
             } else {
               y16[0] = f32_to_bf16_rne(lo);
               if (np + 1 < N) y16[1] = f32_to_bf16_rne(hi);
@@ -168,73 +168,94 @@ __device__ __forceinline__ void store_wave_tile(const v16f (&acc)[FM][FN], void*
 constexpr int kEpiStride = 36;                        // floats per LDS tile row
 constexpr int kEpiLdsBytes = 2 * 32 * kEpiStride * 4;  // per wave (two tiles)
 
-template <int OUT, int FM, int FN>
-__device__ __forceinline__ void store_wave_tile_lds(const v16f (&acc)[FM][FN], float* __restrict__ t,
-                                                    void* __restrict__ Y, int64_t m0, int64_t row_end, int64_t n0,
-                                                    int64_t N, int lane) {
-  static_assert(OUT != 0, "fp32 output is stored from the registers");
+// One 8-column piece of one output row from the LDS tile: 8 bf16 values (one
+// 16-byte store), or for SwiGLU the 4 results of its 4 (gate, up) pairs.
+// CHECKED handles rows past row_end, columns past N and unaligned rows; the
+// unchecked form is for wave tiles that lie wholly inside y with 16-byte
+// aligned rows.
+template <int OUT, bool CHECKED>
+__device__ __forceinline__ void store_epi_piece(const float* __restrict__ src, void* __restrict__ Y, int64_t m,
+                                                int64_t n, int64_t row_end, int64_t N) {
+  const float4 p0 = *reinterpret_cast<const float4*>(src);
+  const float4 p1 = *reinterpret_cast<const float4*>(src + 4);
+  const float v[8] = {p0.x, p0.y, p0.z, p0.w, p1.x, p1.y, p1.z, p1.w};
+  if (CHECKED && (m >= row_end || n >= N)) return;
+  if constexpr ((OUT & kOutSwiGLU) != 0) {
+    const int64_t ldo = N >> 1, j0 = n >> 1;   // 4 output columns j0..j0+3
+    float o[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) o[k] = silu_times(v[2 * k], v[2 * k + 1]);
+    if constexpr ((OUT & kOutBf16) != 0) {
+      uint16_t* yp = reinterpret_cast<uint16_t*>(Y) + m * ldo + j0;
+      if (!CHECKED || (n + 8 <= N && (reinterpret_cast<uintptr_t>(yp) & 7) == 0)) {
+        __builtin_nontemporal_store(u32x2{pk_bf16_rne(o[0], o[1]), pk_bf16_rne(o[2], o[3])},
+                                    reinterpret_cast<u32x2*>(yp));
+      } else {
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+          if (n + 2 * k < N) yp[k] = f32_to_bf16_rne(o[k]);
+      }
+    } else {
+      float* yp = reinterpret_cast<float*>(Y) + m * ldo + j0;
+      if (!CHECKED || (n + 8 <= N && (reinterpret_cast<uintptr_t>(yp) & 15) == 0)) {
+        __builtin_nontemporal_store(f32x4{o[0], o[1], o[2], o[3]}, reinterpret_cast<f32x4*>(yp));
+      } else {
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+          if (n + 2 * k < N) yp[k] = o[k];
+      }
+    }
+  } else {   // bf16
+    uint16_t* yp = reinterpret_cast<uint16_t*>(Y) + m * N + n;
+    if (!CHECKED || (n + 8 <= N && (reinterpret_cast<uintptr_t>(yp) & 15) == 0)) {
+      __builtin_nontemporal_store(u32x4{pk_bf16_rne(v[0], v[1]), pk_bf16_rne(v[2], v[3]), pk_bf16_rne(v[4], v[5]),
+                                        pk_bf16_rne(v[6], v[7])},
+                                  reinterpret_cast<u32x4*>(yp));
+    } else {
+#pragma unroll
+      for (int k = 0; k < 8; ++k)
+        if (n + k < N) yp[k] = f32_to_bf16_rne(v[k]);
+    }
+  }
+}
+
+template <int OUT, bool CHECKED, int FM, int FN>
+__device__ __forceinline__ void store_wave_tile_lds_impl(const v16f (&acc)[FM][FN], float* __restrict__ t,
+                                                         void* __restrict__ Y, int64_t m0, int64_t row_end,
+                                                         int64_t n0, int64_t N, int lane) {
   const int r32 = lane & 31, h = lane >> 5;
 #pragma unroll
   for (int mi = 0; mi < FM; ++mi) {
 #pragma unroll
     for (int ni = 0; ni < FN; ++ni) {
-      float* tt = t + ((mi * FN + ni) & 1) * (32 * kEpiStride);
+      float* tt = static_cast<float*>(__builtin_assume_aligned(t + ((mi * FN + ni) & 1) * (32 * kEpiStride), 16));
 #pragma unroll
       for (int r = 0; r < 16; ++r) tt[(8 * (r >> 2) + 4 * h + (r & 3)) * kEpiStride + r32] = acc[mi][ni][r];
 #pragma unroll
       for (int it = 0; it < 2; ++it) {
         const int item = lane + 64 * it;        // 32 rows x 4 pieces of 8 columns
         const int row = item >> 2, c = (item & 3) * 8;
-        const float4 p0 = *reinterpret_cast<const float4*>(tt + row * kEpiStride + c);
-        const float4 p1 = *reinterpret_cast<const float4*>(tt + row * kEpiStride + c + 4);
-        const float v[8] = {p0.x, p0.y, p0.z, p0.w, p1.x, p1.y, p1.z, p1.w};
-        const int64_t m = m0 + mi * 32 + row, n = n0 + ni * 32 + c;
-        if (m >= row_end || n >= N) continue;
-        if constexpr ((OUT & kOutSwiGLU) != 0) {
-          const int64_t ldo = N >> 1, j0 = n >> 1;   // 4 output columns j0..j0+3
-          float o[4];
-#pragma unroll
-          for (int k = 0; k < 4; ++k) o[k] = silu_times(v[2 * k], v[2 * k + 1]);
-          if constexpr ((OUT & kOutBf16) != 0) {
-            uint16_t* yp = reinterpret_cast<uint16_t*>(Y) + m * ldo + j0;
-            if (n + 8 <= N && (reinterpret_cast<uintptr_t>(yp) & 7) == 0) {
-              uint2 q;
-              q.x = (uint32_t)f32_to_bf16_rne(o[0]) | ((uint32_t)f32_to_bf16_rne(o[1]) << 16);
-              q.y = (uint32_t)f32_to_bf16_rne(o[2]) | ((uint32_t)f32_to_bf16_rne(o[3]) << 16);
-              __builtin_nontemporal_store(u32x2{q.x, q.y}, reinterpret_cast<u32x2*>(yp));
-            } else {
-#pragma unroll
-              for (int k = 0; k < 4; ++k)
-                if (n + 2 * k < N) yp[k] = f32_to_bf16_rne(o[k]);
-            }
-          } else {
-            float* yp = reinterpret_cast<float*>(Y) + m * ldo + j0;
-            if (n + 8 <= N && (reinterpret_cast<uintptr_t>(yp) & 15) == 0) {
-              __builtin_nontemporal_store(f32x4{o[0], o[1], o[2], o[3]}, reinterpret_cast<f32x4*>(yp));
-            } else {
-#pragma unroll
-              for (int k = 0; k < 4; ++k)
-                if (n + 2 * k < N) yp[k] = o[k];
-            }
-          }
-        } else {   // bf16
-          uint16_t* yp = reinterpret_cast<uint16_t*>(Y) + m * N + n;
-          if (n + 8 <= N && (reinterpret_cast<uintptr_t>(yp) & 15) == 0) {
-            uint4 q;
-            q.x = (uint32_t)f32_to_bf16_rne(v[0]) | ((uint32_t)f32_to_bf16_rne(v[1]) << 16);
-            q.y = (uint32_t)f32_to_bf16_rne(v[2]) | ((uint32_t)f32_to_bf16_rne(v[3]) << 16);
-            q.z = (uint32_t)f32_to_bf16_rne(v[4]) | ((uint32_t)f32_to_bf16_rne(v[5]) << 16);
-            q.w = (uint32_t)f32_to_bf16_rne(v[6]) | ((uint32_t)f32_to_bf16_rne(v[7]) << 16);
-            __builtin_nontemporal_store(u32x4{q.x, q.y, q.z, q.w}, reinterpret_cast<u32x4*>(yp));
-          } else {
-#pragma unroll
-            for (int k = 0; k < 8; ++k)
-              if (n + k < N) yp[k] = f32_to_bf16_rne(v[k]);
-          }
-        }
+        store_epi_piece<OUT, CHECKED>(tt + row * kEpiStride + c, Y, m0 + mi * 32 + row, n0 + ni * 32 + c, row_end, N);
       }
     }
   }
+}
+
+template <int OUT, int FM, int FN>
+__device__ __forceinline__ void store_wave_tile_lds(const v16f (&acc)[FM][FN], float* __restrict__ t,
+                                                    void* __restrict__ Y, int64_t m0, int64_t row_end, int64_t n0,
+                                                    int64_t N, int lane) {
+  static_assert(OUT != 0, "fp32 output is stored from the registers");
+  // Unchecked when the wave tile lies inside y and every piece's store is
+  // aligned: with N % 8 == 0 and a 16-byte aligned y, the 16-byte bf16
+  // pieces, the 8-byte SwiGLU bf16 pieces and the 16-byte SwiGLU fp32 pieces
+  // all start on their own size (piece columns are multiples of 8).
+  const bool interior = (m0 + FM * 32 <= row_end) && (n0 + FN * 32 <= N) && (N % 8) == 0 &&
+                        (reinterpret_cast<uintptr_t>(Y) & 15) == 0;
+  if (interior)
+    store_wave_tile_lds_impl<OUT, false>(acc, t, Y, m0, row_end, n0, N, lane);
+  else
+    store_wave_tile_lds_impl<OUT, true>(acc, t, Y, m0, row_end, n0, N, lane);
 }
 
 template <int BM, int BN, int WAVES_M, int WAVES_N, int OUT = 0>

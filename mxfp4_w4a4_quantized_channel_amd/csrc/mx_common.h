@@ -162,6 +162,16 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float v) {
   return (uint16_t)((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
 }
 
+// Two fp32 values rounded to the nearest bf16 (ties to even) and packed, lo in
+// bits 0..15: one v_cvt_pk_bf16_f32.  For finite inputs this is bit-identical
+// to f32_to_bf16_rne.
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t pk_bf16_rne(float lo, float hi) {
+  const f32x2_t v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
+}
+
 __device__ __forceinline__ float silu_times(float g, float u) { return g / (1.0f + expf(-g)) * u; }
 
 __device__ __forceinline__ void store_out(void* y, int64_t i, float v, int mode) {
