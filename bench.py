@@ -76,6 +76,9 @@ def parse():
     p.add_argument("--cpu-rows", type=int, default=256, help="row sample of the CPU oracle baseline")
     p.add_argument("--flip-rounds", type=int, default=4096,
                    help="offline workloads: at most this many Flip-Refinement moves per weight row")
+    p.add_argument("--library-compare", action="store_true",
+                   help="only time our prefill GEMM against the vendor library's MXFP4 GEMM (hipBLASLt through "
+                        "torch._scaled_mm) on the same operands, attn-proj and down-prefill, bf16 output")
     p.add_argument("--copy-calibration", action="store_true",
                    help="only run a plain 512 MiB device-to-device copy (5 times) so that HBM byte "
                         "counters can be scaled against a transfer of known size")
@@ -92,6 +95,83 @@ def copy_calibration():
         dst.copy_(src)
     torch.cuda.synchronize()
     print(json.dumps({"copy_calibration": {"bytes_read_per_copy": n, "bytes_written_per_copy": n, "copies": 5}}))
+
+
+def library_compare(steps):
+    """Our prefill GEMM next to the vendor library's MXFP4 GEMM (hipBLASLt, as
+    torch._scaled_mm runs it for float4_e2m1fn_x2 operands with e8m0 block
+    scales) on the same operands: the attn-proj and down-prefill layers'
+    activation codes (from macaq_quant_act) and prepared weights.  A
+    comparison leg only; nothing of the layer runs through the library.
+
+    The library call spends longer on the host than its kernel takes on the
+    GPU, so both sides are timed behind a GPU busy-wait long enough to hide
+    the host: the K launches queue up and run back to back between the two
+    events."""
+    import torch
+    import workloads
+    import mxfp4_w4a4_quantized_channel_amd as mx
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    rows = []
+    for name in ("attn", "down"):
+        cfg, variant, _, desc = WORKLOADS[name]
+        wl = workloads.make(cfg, variant=variant)
+        M, N, K = wl.M, wl.N, wl.K
+        s = wl.s.to(dev)
+        ac, asc = mx.quant_act(wl.x.to(dev), s)
+        wc, wsc = mx.prepare_weights(wl.w.to(dev), s)
+        a4 = ac.view(torch.float4_e2m1fn_x2)
+        w4 = wc.reshape(N, K // 2).view(torch.float4_e2m1fn_x2)
+        sa = asc.view(torch.float8_e8m0fnu)
+        sw = wsc.reshape(N, K // 32).view(torch.float8_e8m0fnu)
+        y16 = torch.empty(M, N, dtype=torch.bfloat16, device=dev)
+        y32 = torch.empty(M, N, dtype=torch.float32, device=dev)
+        ours16 = lambda: mx.gemm(ac, asc, wc, wsc, out=y16, out_dtype=torch.bfloat16)
+        ours32 = lambda: mx.gemm(ac, asc, wc, wsc, out=y32, out_dtype=torch.float32)
+        lib16 = lambda: torch._scaled_mm(a4, w4.t(), scale_a=sa, scale_b=sw, out_dtype=torch.bfloat16)
+
+        def gpu_us(fn):
+            for _ in range(3):
+                fn()
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            fn()
+            torch.cuda.synchronize()
+            host_us = (time.perf_counter() - t0) * 1e6
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            torch.cuda._sleep(int(2.5e3 * host_us * steps))   # about (steps x host time) at 2.5 GHz, doubled below
+            torch.cuda._sleep(int(2.5e3 * host_us * steps))
+            e0.record()
+            for _ in range(steps):
+                fn()
+            e1.record()
+            torch.cuda.synchronize()
+            return e0.elapsed_time(e1) / steps * 1e3
+
+        ours32()
+        y_lib = lib16()
+        ours16()
+        torch.cuda.synchronize()
+        rel = ((y_lib.float() - y32).abs() / y32.abs().clamp_min(1e-30))
+        t = {k: [] for k in ("ours_bf16", "library_bf16", "ours_fp32")}
+        for _ in range(3):   # interleaved, to share clock and thermal conditions
+            t["ours_bf16"].append(gpu_us(ours16))
+            t["library_bf16"].append(gpu_us(lib16))
+            t["ours_fp32"].append(gpu_us(ours32))
+        flops = 2.0 * M * N * K
+        med = {k: sorted(v)[1] for k, v in t.items()}
+        rows.append({"workload": desc, "M": M, "N": N, "K": K,
+                     **{f"{k}_us": round(v, 2) for k, v in med.items()},
+                     **{f"{k}_tflops": round(flops / v / 1e6, 1) for k, v in med.items()},
+                     "library_over_ours_bf16": round(med["library_bf16"] / med["ours_bf16"], 3),
+                     "agreement": {"ours_bf16_is_rne_of_ours_fp32": bool(torch.equal(y16, y32.to(torch.bfloat16))),
+                                   "library_max_rel_diff_vs_ours_fp32": round(float(rel.max()), 5),
+                                   "library_bf16_equal_to_ours_bf16": round(float((y_lib == y16).float().mean()), 4)}})
+    print(json.dumps({"library_compare": rows, "library": "hipBLASLt via torch._scaled_mm "
+                      f"(torch {torch.__version__}, HIP {torch.version.hip}), MXFP4 x MXFP4, bf16 output",
+                      "steps": steps, "timing": "median of 3 interleaved rounds, each K launches behind a "
+                      "GPU busy-wait, HIP events"}), flush=True)
 
 
 def gpu_state():
@@ -400,6 +480,9 @@ def main():
     args = parse()
     if args.copy_calibration:
         copy_calibration()
+        return
+    if args.library_compare:
+        library_compare(min(args.steps, 100))
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (the layer is data-parallel: "
