@@ -413,12 +413,26 @@ void flip_rounds_kernel(const float* __restrict__ H, int64_t row0, int64_t rows,
     const int kb = bc >> 12;
     const bool up = (bc >> 11) & 1;
     const int p = (bc & 2047) - 1024;
+    // g - delta H[k, :]: delta H[k, i] = -+2^p H[k, i] is exact, so one fused
+    // multiply-add rounds the difference once, as the separate exact product
+    // and subtraction do
+    const double step = up ? -ldexp(1.0, p) : ldexp(1.0, p);
+    // KPT is ceil(K / NT) rounded up to a multiple of 4, so only the last 4
+    // slots can reach past K: the others take a uniform base per slot and one
+    // 32-bit lane offset, those 4 clamp (entries past K are never read back)
     const float* hrow = H + (int64_t)kb * K;
+    const char* hb = reinterpret_cast<const char*>(hrow);
+    const unsigned off = (unsigned)t_r * 4u;
 #pragma unroll
     for (int m = 0; m < KPT; ++m) {
-      const int k = t_r + NT * m;
-      const float hv = hrow[k < Ki ? k : Ki - 1];                        // entries past K are never read back
-      g[m] = g[m] + ldexp((double)(up ? -hv : hv), p);                  // g - delta H[k, :]
+      float hv;
+      if (m + 4 < KPT) {
+        hv = *reinterpret_cast<const float*>(hb + (size_t)NT * 4 * m + off);
+      } else {
+        const int k = t_r + NT * m;
+        hv = hrow[k < Ki ? k : Ki - 1];
+      }
+      g[m] = __builtin_fma((double)hv, step, g[m]);
     }
     const int mo = kb / NT;                                              // the owner's coordinate slot
     if (kb - mo * NT == t_r) {
