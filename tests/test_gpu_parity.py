@@ -114,6 +114,49 @@ def test_quant_act_rows_per_wave(steps, monkeypatch):
     assert np.array_equal(codes.cpu().numpy(), rc)
 
 
+LAYOUT_ACT = [
+    ("cfg2-shaped ragged K", dict(cfg=2, shape=(37, 64, 1312))),
+    ("tiny fp32", dict(cfg=1)),
+    ("cfg5 token routing", dict(cfg=5, shape=(300, 32, 256), routing="token_zipf")),
+    ("cfg5 expert routing K3072", dict(cfg=5, shape=(500, 32, 3072))),
+]
+
+
+@pytest.mark.parametrize("steps", [None, 1, 3])
+@pytest.mark.parametrize("shared", ["0", "1"])
+@pytest.mark.parametrize("name,kw", LAYOUT_ACT, ids=[n for n, _ in LAYOUT_ACT])
+def test_quant_act_both_layouts(name, kw, shared, steps, monkeypatch):
+    """Both wave layouts of the activation kernel, forced: s per wave in
+    registers, and s staged per block in LDS for the experts of the block's
+    first and last rows (token routing puts many more experts in a block, so
+    rows of other experts read s directly); also with 1 and 3 row blocks per
+    wave."""
+    say(f"quant_act {name} shared={shared} steps={steps}")
+    monkeypatch.setenv("MACAQ_ACT_SHARED_S", shared)
+    if steps is not None:
+        monkeypatch.setenv("MACAQ_ACT_ROWS_PER_WAVE", str(steps))
+    wl = workloads.make(**kw)
+    off = wl.offsets.to(DEV) if wl.E > 1 else None
+    codes, scales = mx.quant_act(wl.x.to(DEV), wl.s.to(DEV), off)
+    rc, rs = oracle.quant_act(host(wl.x), wl.s.numpy(), wl.offsets.numpy() if wl.E > 1 else None)
+    assert np.array_equal(scales.cpu().numpy(), rs)
+    assert np.array_equal(codes.cpu().numpy(), rc)
+
+
+@pytest.mark.parametrize("shared", ["0", "1"])
+def test_prepare_weights_both_layouts(shared, monkeypatch):
+    """Weight preparation (reciprocal factors, experts of N rows each) with
+    either wave layout forced."""
+    say(f"prepare_weights experts shared={shared}")
+    monkeypatch.setenv("MACAQ_ACT_SHARED_S", shared)
+    wl = workloads.make(cfg=5, shape=(64, 48, 256))
+    codes, scales = gpu_prepare(wl)
+    for e in range(wl.E):
+        rc, rs = oracle_prepare(wl, e)
+        assert np.array_equal(scales[e].cpu().numpy(), rs), e
+        assert np.array_equal(codes[e].cpu().numpy(), rc), e
+
+
 def test_quant_act_empty_is_noop():
     say("quant_act M=0")
     x = torch.empty((0, 256), dtype=torch.bfloat16, device=DEV)
