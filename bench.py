@@ -643,10 +643,22 @@ def main():
                            "unit": "GB/s", "frac": round(ach / PEAK_HBM_GBPS, 4), "us": round(gemm_us, 2),
                            "traffic": traffic_record(f"{args.workload}:{'fused' if fused else 'gemm'}{out_key}")}
     else:
-        ach = flops / gemm_us / 1e6
-        out["roofline"] = {"kernel": gemm_name, "bound": "mfma", "achieved": round(ach, 1),
-                           "peak": PEAK_MXFP4_TFLOPS, "unit": "TFLOP/s", "frac": round(ach / PEAK_MXFP4_TFLOPS, 4),
-                           "us": round(gemm_us, 2), "traffic": traffic_record(f"{args.workload}:gemm{out_key}")}
+        # the roofline is the larger of the MFMA time and the HBM time of the
+        # kernel's algorithmic bytes (A codes + scales, the active experts' W',
+        # y): dense prefill layers are MFMA-bound, the MoE layers HBM-bound
+        gemm_bytes = w_alg + M * K // 2 + M * K // 32 + M * y_cols * ys[0].element_size()
+        t_mfma, t_hbm = flops / PEAK_MXFP4_TFLOPS / 1e6, gemm_bytes / PEAK_HBM_GBPS / 1e3   # us
+        if t_mfma >= t_hbm:
+            ach = flops / gemm_us / 1e6
+            out["roofline"] = {"kernel": gemm_name, "bound": "mfma", "achieved": round(ach, 1),
+                               "peak": PEAK_MXFP4_TFLOPS, "unit": "TFLOP/s", "frac": round(ach / PEAK_MXFP4_TFLOPS, 4)}
+        else:
+            ach = gemm_bytes / gemm_us / 1e3
+            out["roofline"] = {"kernel": gemm_name, "bound": "hbm", "achieved": round(ach, 1),
+                               "peak": PEAK_HBM_GBPS, "unit": "GB/s", "frac": round(ach / PEAK_HBM_GBPS, 4),
+                               "tflops": round(flops / gemm_us / 1e6, 1)}
+        out["roofline"].update({"us": round(gemm_us, 2), "roofline_us": {"mfma": round(t_mfma, 2), "hbm": round(t_hbm, 2)},
+                                "traffic": traffic_record(f"{args.workload}:gemm{out_key}")})
     if not args.no_ablation and not fused:
         out["transform_overhead"] = transform_overhead(args, mx, L, wl, xs, wss, wcs, ys, s0, off_p, stream, sp,
                                                        a_codes, a_scales, gemm_ws, M, N, K, E, R, ydt, epi)
