@@ -54,6 +54,15 @@
  * device-resident values (s > 0, sorted offsets, finite inputs) are
  * preconditions that are not checked.
  *
+ * Debug mode: with the environment variable MACAQ_CHECK=1 (read at every
+ * call), each entry point first waits for `stream` and checks the
+ * device-resident preconditions it can read back cheaply: expert offsets
+ * start at 0, never decrease and end at the row count; every factor of s is
+ * finite and > 0 (MACAQ_ERR_INVALID_ARG otherwise, before any launch).  After
+ * launching, it waits for `stream` again, so that a fault in one of its
+ * kernels is reported as MACAQ_ERR_HIP by that call.  This is the only mode
+ * in which the library synchronizes.
+ *
  * Errors: a negative macaq_status.  macaq_last_error() returns a
  * thread-local description of the most recent failure on that thread.
  */

@@ -6,9 +6,11 @@
 
 #include <algorithm>
 #include <atomic>
+#include <cmath>
 #include <cstdio>
 #include <cstdlib>
 #include <string>
+#include <vector>
 
 #include "macaq.h"
 
@@ -77,6 +79,51 @@ int hip_status(hipError_t e, const char* where) {
 }
 
 size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+// ---- MACAQ_CHECK=1: the debug mode.  Before launching, the entry point waits
+// for its stream and checks the device-side preconditions it can read back
+// cheaply (expert offsets start at 0, never decrease and end at the row
+// count; every factor of s is finite and > 0); after launching, it waits for
+// the stream again, so that a kernel fault surfaces as MACAQ_ERR_HIP of the
+// call that caused it.  Without it no entry point synchronizes.
+bool check_mode() {
+  const char* v = std::getenv("MACAQ_CHECK");
+  return v != nullptr && v[0] == '1';
+}
+
+int check_inputs(const char* fn, hipStream_t stream, const int32_t* offsets, int64_t E, int64_t rows,
+                 const float* s, int64_t s_count) {
+  if (!check_mode()) return MACAQ_OK;
+  if (int st = hip_status(hipStreamSynchronize(stream), fn)) return st;
+  if (offsets != nullptr && E > 1) {
+    std::vector<int32_t> off((size_t)E + 1);
+    if (int st = hip_status(hipMemcpy(off.data(), offsets, off.size() * sizeof(int32_t), hipMemcpyDeviceToHost), fn))
+      return st;
+    if (off[0] != 0 || (int64_t)off[(size_t)E] != rows)
+      return fail(MACAQ_ERR_INVALID_ARG, std::string(fn) + ": expert_offsets must start at 0 and end at " +
+                                             std::to_string(rows) + " (MACAQ_CHECK)");
+    for (int64_t e = 0; e < E; ++e)
+      if (off[(size_t)e + 1] < off[(size_t)e])
+        return fail(MACAQ_ERR_INVALID_ARG, std::string(fn) + ": expert_offsets decrease at expert " +
+                                               std::to_string(e) + " (MACAQ_CHECK)");
+  }
+  if (s != nullptr && s_count > 0) {
+    std::vector<float> h((size_t)s_count);
+    if (int st = hip_status(hipMemcpy(h.data(), s, h.size() * sizeof(float), hipMemcpyDeviceToHost), fn)) return st;
+    for (size_t i = 0; i < h.size(); ++i)
+      if (!(std::isfinite(h[i]) && h[i] > 0.0f))
+        return fail(MACAQ_ERR_INVALID_ARG, std::string(fn) + ": s[" + std::to_string(i) +
+                                               "] is not a finite positive factor (MACAQ_CHECK)");
+  }
+  return MACAQ_OK;
+}
+
+// The status of a call that has enqueued its kernels; under MACAQ_CHECK a
+// fault while they run is reported here.
+int finish(const char* fn, hipStream_t stream, int status) {
+  if (status != MACAQ_OK || !check_mode()) return status;
+  return hip_status(hipStreamSynchronize(stream), fn);
+}
 
 int check_dtype(macaq_dtype d, const char* name) {
   if (d != MACAQ_BF16 && d != MACAQ_F32)
@@ -157,9 +204,11 @@ int macaq_prepare_weights(const void* w, macaq_dtype w_dtype, const float* s, in
   if (!aligned(w, 16) || !aligned(w_codes, 16) || !aligned(s, 16))
     return fail(MACAQ_ERR_INVALID_ARG, std::string(fn) + ": w, s and w_codes must be 16-byte aligned");
   if (int st = check_device()) return st;
-  return hip_status(macaq::launch_act_quant(w, w_dtype == MACAQ_F32, true, s, nullptr, (int)E, N, E * N, K,
-                                            w_codes, w_scales, (hipStream_t)stream),
-                    fn);
+  if (int st = check_inputs(fn, (hipStream_t)stream, nullptr, E, E * N, s, E * K)) return st;
+  return finish(fn, (hipStream_t)stream,
+                hip_status(macaq::launch_act_quant(w, w_dtype == MACAQ_F32, true, s, nullptr, (int)E, N, E * N, K,
+                                                   w_codes, w_scales, (hipStream_t)stream),
+                           fn));
 }
 
 int macaq_hessian(const void* x, macaq_dtype x_dtype, const float* s, const int32_t* expert_offsets, int64_t E,
@@ -178,9 +227,11 @@ int macaq_hessian(const void* x, macaq_dtype x_dtype, const float* s, const int3
   if (E > 4096 || K > (1 << 20))
     return fail(MACAQ_ERR_UNSUPPORTED, std::string(fn) + ": sizes beyond the supported range");
   if (int st = check_device()) return st;
-  return hip_status(macaq::launch_hessian(x, x_dtype == MACAQ_F32, s, E > 1 ? expert_offsets : nullptr, (int)E, T,
-                                          K, h, (hipStream_t)stream),
-                    fn);
+  if (int st = check_inputs(fn, (hipStream_t)stream, expert_offsets, E, T, s, E * K)) return st;
+  return finish(fn, (hipStream_t)stream,
+                hip_status(macaq::launch_hessian(x, x_dtype == MACAQ_F32, s, E > 1 ? expert_offsets : nullptr, (int)E,
+                                                 T, K, h, (hipStream_t)stream),
+                           fn));
 }
 
 int macaq_prepare_weights_hessian(const void* w, macaq_dtype w_dtype, const float* s, const float* h, int64_t E,
@@ -197,9 +248,11 @@ int macaq_prepare_weights_hessian(const void* w, macaq_dtype w_dtype, const floa
   if (E > 4096 || K / 32 > 65535 || N > INT32_MAX)
     return fail(MACAQ_ERR_UNSUPPORTED, std::string(fn) + ": sizes beyond the supported range");
   if (int st = check_device()) return st;
-  return hip_status(macaq::launch_prep_hessian(w, w_dtype == MACAQ_F32, s, h, (int)E, N, K, w_codes, w_scales,
-                                               (hipStream_t)stream),
-                    fn);
+  if (int st = check_inputs(fn, (hipStream_t)stream, nullptr, E, E * N, s, E * K)) return st;
+  return finish(fn, (hipStream_t)stream,
+                hip_status(macaq::launch_prep_hessian(w, w_dtype == MACAQ_F32, s, h, (int)E, N, K, w_codes, w_scales,
+                                                      (hipStream_t)stream),
+                           fn));
 }
 
 int macaq_quant_act(const void* x, macaq_dtype x_dtype, const float* s, const int32_t* expert_offsets,
@@ -216,9 +269,11 @@ int macaq_quant_act(const void* x, macaq_dtype x_dtype, const float* s, const in
     return fail(MACAQ_ERR_INVALID_ARG, std::string(fn) + ": x, s and a_codes must be 16-byte aligned");
   if (E > INT32_MAX) return fail(MACAQ_ERR_UNSUPPORTED, std::string(fn) + ": too many experts");
   if (int st = check_device()) return st;
-  return hip_status(macaq::launch_act_quant(x, x_dtype == MACAQ_F32, false, s, E > 1 ? expert_offsets : nullptr,
-                                            (int)E, 0, M, K, a_codes, a_scales, (hipStream_t)stream),
-                    fn);
+  if (int st = check_inputs(fn, (hipStream_t)stream, expert_offsets, E, M, s, E * K)) return st;
+  return finish(fn, (hipStream_t)stream,
+                hip_status(macaq::launch_act_quant(x, x_dtype == MACAQ_F32, false, s, E > 1 ? expert_offsets : nullptr,
+                                                   (int)E, 0, M, K, a_codes, a_scales, (hipStream_t)stream),
+                           fn));
 }
 
 size_t macaq_quant_act_bytes(int64_t M, int64_t K) {
@@ -278,8 +333,10 @@ int macaq_gemm_ex(const uint8_t* a_codes, const uint8_t* a_scales, const int32_t
   if (M == 0) return MACAQ_OK;
   if (int st = check_workspace(workspace, workspace_bytes, macaq_gemm_workspace_bytes(M, N, K, E), fn)) return st;
   if (int st = check_device()) return st;
-  return run_gemm(a_codes, a_scales, expert_offsets, E, w_codes, w_scales, M, N, K, y, mode, workspace,
-                  (hipStream_t)stream, fn);
+  if (int st = check_inputs(fn, (hipStream_t)stream, expert_offsets, E, M, nullptr, 0)) return st;
+  return finish(fn, (hipStream_t)stream,
+                run_gemm(a_codes, a_scales, expert_offsets, E, w_codes, w_scales, M, N, K, y, mode, workspace,
+                         (hipStream_t)stream, fn));
 }
 
 int macaq_gemm(const uint8_t* a_codes, const uint8_t* a_scales, const int32_t* expert_offsets, int64_t E,
@@ -315,10 +372,12 @@ int macaq_linear_ex(const void* x, macaq_dtype x_dtype, const float* s, const in
   if (int st = check_workspace(workspace, workspace_bytes, need, fn)) return st;
   if (int st = check_device()) return st;
   hipStream_t st = (hipStream_t)stream;
+  if (int r = check_inputs(fn, st, expert_offsets, E, M, s, E * K)) return r;
   if (fused)
-    return hip_status(
-        macaq::launch_linear_fused(x, x_dtype == MACAQ_F32, s, w_codes, w_scales, M, N, K, y, mode, st),
-        "macaq_linear (fused)");
+    return finish(fn, st,
+                  hip_status(macaq::launch_linear_fused(x, x_dtype == MACAQ_F32, s, w_codes, w_scales, M, N, K, y,
+                                                        mode, st),
+                             "macaq_linear (fused)"));
   uint8_t* a_codes = static_cast<uint8_t*>(workspace);
   uint8_t* a_scales = a_codes + round_up((size_t)M * (size_t)K / 2, 256);
   const int32_t* off = E > 1 ? expert_offsets : nullptr;
@@ -327,8 +386,9 @@ int macaq_linear_ex(const void* x, macaq_dtype x_dtype, const float* s, const in
                          "macaq_linear (transform)"))
     return r;
   void* gemm_ws = static_cast<uint8_t*>(workspace) + macaq_quant_act_bytes(M, K);
-  return run_gemm(a_codes, a_scales, off, E, w_codes, w_scales, M, N, K, y, mode, gemm_ws, st,
-                  "macaq_linear (gemm)");
+  return finish(fn, st,
+                run_gemm(a_codes, a_scales, off, E, w_codes, w_scales, M, N, K, y, mode, gemm_ws, st,
+                         "macaq_linear (gemm)"));
 }
 
 int macaq_linear(const void* x, macaq_dtype x_dtype, const float* s, const int32_t* expert_offsets, int64_t E,
@@ -349,8 +409,11 @@ int macaq_quant_mxfp4(const void* x, macaq_dtype x_dtype, int64_t M, int64_t K, 
   if (!aligned(x, 16) || !aligned(codes, 16))
     return fail(MACAQ_ERR_INVALID_ARG, std::string(fn) + ": x and codes must be 16-byte aligned");
   if (int st = check_device()) return st;
-  return hip_status(macaq::launch_quant_plain(x, x_dtype == MACAQ_F32, M, K, codes, scales, (hipStream_t)stream),
-                    fn);
+  if (int st = check_inputs(fn, (hipStream_t)stream, nullptr, 1, M, nullptr, 0)) return st;
+  return finish(fn, (hipStream_t)stream,
+                hip_status(macaq::launch_quant_plain(x, x_dtype == MACAQ_F32, M, K, codes, scales,
+                                                     (hipStream_t)stream),
+                           fn));
 }
 
 int macaq_encode_e2m1(const float* v, int64_t n, uint8_t* codes, void* stream) {
@@ -359,7 +422,8 @@ int macaq_encode_e2m1(const float* v, int64_t n, uint8_t* codes, void* stream) {
   if (n == 0) return MACAQ_OK;
   if (!v || !codes) return fail(MACAQ_ERR_INVALID_ARG, std::string(fn) + ": null pointer");
   if (int st = check_device()) return st;
-  return hip_status(macaq::launch_encode_e2m1(v, n, codes, (hipStream_t)stream), fn);
+  if (int st = check_inputs(fn, (hipStream_t)stream, nullptr, 1, 0, nullptr, 0)) return st;
+  return finish(fn, (hipStream_t)stream, hip_status(macaq::launch_encode_e2m1(v, n, codes, (hipStream_t)stream), fn));
 }
 
 size_t macaq_flip_refine_workspace_bytes(int64_t rows, int64_t K) {
@@ -388,6 +452,7 @@ int macaq_flip_refine(const void* w, macaq_dtype w_dtype, const float* s, const 
   if (int st = check_workspace(workspace, workspace_bytes, macaq_flip_refine_workspace_bytes(128, K), fn))
     return st;
   if (int st = check_device()) return st;
+  if (int st = check_inputs(fn, (hipStream_t)stream, nullptr, E, E * N, s, E * K)) return st;
   const int64_t fit = (int64_t)(workspace_bytes / row_bytes);   // gradient rows the workspace holds
   const bool f32 = w_dtype == MACAQ_F32;
   hipStream_t st = (hipStream_t)stream;
@@ -396,8 +461,10 @@ int macaq_flip_refine(const void* w, macaq_dtype w_dtype, const float* s, const 
     if (int r = hip_status(macaq::launch_flip_grad(w, f32, s, h, w_codes, w_scales, (int)E, 0, N, N, K, G, st),
                            "macaq_flip_refine (gradient)"))
       return r;
-    return hip_status(macaq::launch_flip_rounds(h, (int)E, 0, N, N, K, max_rounds, G, w_codes, w_scales, moves, st),
-                      "macaq_flip_refine (rounds)");
+    return finish(fn, st,
+                  hip_status(macaq::launch_flip_rounds(h, (int)E, 0, N, N, K, max_rounds, G, w_codes, w_scales,
+                                                       moves, st),
+                             "macaq_flip_refine (rounds)"));
   }
   // else expert by expert, in chunks of rows that fit (a multiple of 128)
   const int64_t chunk = std::min<int64_t>(fit / 128 * 128, (N + 127) / 128 * 128);
@@ -419,7 +486,7 @@ int macaq_flip_refine(const void* w, macaq_dtype w_dtype, const float* s, const 
         return r;
     }
   }
-  return MACAQ_OK;
+  return finish(fn, st, MACAQ_OK);
 }
 
 }  // extern "C"
