@@ -174,6 +174,17 @@ def library_compare(steps):
                       "GPU busy-wait, HIP events"}), flush=True)
 
 
+def cpu_model():
+    """The host CPU's model name from /proc/cpuinfo (None where unreadable)."""
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
 def gpu_state():
     """Clock, power and temperature of GPU 0 as amd-smi reports them at this
     moment (None where amd-smi is missing or its output is not understood).
@@ -249,7 +260,7 @@ def cpu_baseline(wl, rows):
     threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
     return {"value": round(flops / el / 1e12, 6), "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
             "sample": f"{rows} of {wl.M} rows x {reps} reps (transform+quant of the rows, fp64 GEMM vs full W')",
-            "seconds": round(el, 2)}
+            "seconds": round(el, 2), "cpu": cpu_model(), "affinity_cores": len(os.sched_getaffinity(0))}
 
 
 def cpu_baseline_offline(wl, rows, cols, flip_rows, flip_rounds):
@@ -290,7 +301,7 @@ def cpu_baseline_offline(wl, rows, cols, flip_rows, flip_rounds):
                       f"scaled by (K/cols)^2) + search of {rows} of {N} weight rows ({t_s:.2f} s, scaled by "
                       f"N/rows) + Flip-Refinement of {flip_rows} rows, up to {flip_rounds} moves ({t_f:.2f} s, "
                       f"scaled by N/rows), times {E} expert(s)",
-            "seconds": round(t_h + t_s + t_f, 2)}
+            "seconds": round(t_h + t_s + t_f, 2), "cpu": cpu_model(), "affinity_cores": len(os.sched_getaffinity(0))}
 
 
 def bench_offline(args):
