@@ -71,6 +71,10 @@ def parse():
     p.add_argument("--out", default="f32", choices=["f32", "bf16"], help="dtype of y")
     p.add_argument("--epilogue", default="none", choices=["none", "swiglu"],
                    help="swiglu: weight rows are (gate, up) pairs and y is [M][N/2] = silu(gate) * up")
+    p.add_argument("--w-layout", default="auto", choices=["auto", "tiled", "rowmajor"],
+                   help="prepared weights as macaq_prepare_weights writes them (row-major), or repacked offline by "
+                        "macaq_tile_weights (contiguous GEMM copies); auto: tiled for M > 32 when N % 32 == 0 and "
+                        "K % 256 == 0 (the decode kernels read row-major weights)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-ablation", action="store_true", help="skip the pure-MXFP4 comparison")
     p.add_argument("--cpu-rows", type=int, default=256, help="row sample of the CPU oracle baseline")
@@ -437,7 +441,7 @@ def bench_offline(args):
 
 
 def transform_overhead(args, mx, L, wl, xs, wss, wcs, ys, s0, off_p, stream, sp, a_codes, a_scales, gemm_ws,
-                       M, N, K, E, R, ydt, epi):
+                       M, N, K, E, R, ydt, epi, tiled=False):
     """The pages quote MACaQ's cost over pure MXFP4 (same W4A4 layer without
     the scale and the block Hadamard).  Time the online layer both ways on the
     same inputs: MACaQ = transform+quant kernel, then the GEMM against W';
@@ -449,8 +453,11 @@ def transform_overhead(args, mx, L, wl, xs, wss, wcs, ys, s0, off_p, stream, sp,
     xdt = mx.BF16 if xs[0].dtype == torch.bfloat16 else mx.F32
     wp = wl.w.reshape(E * N, K).to(xs[0].device)
     pc, ps = mx.quant_mxfp4(wp)
-    pcs = [pc.reshape(E, N, K // 2).clone() for _ in range(R)]
-    pss = [ps.reshape(E, N, K // 32).clone() for _ in range(R)]
+    pc, ps = pc.reshape(E, N, K // 2), ps.reshape(E, N, K // 32)
+    if tiled:   # the same weight layout as the MACaQ step
+        pc, ps = mx.tile_weights(pc, ps)
+    pcs = [pc.clone() for _ in range(R)]
+    pss = [ps.clone() for _ in range(R)]
 
     def macaq_step(i):
         j = i % R
@@ -526,6 +533,10 @@ def main():
     s0 = wl.s.to(dev)
     off = wl.offsets.to(dev) if E > 1 else None
     wc0, ws0 = mx.prepare_weights(wl.w.to(dev), s0)
+    tiled = args.w_layout == "tiled" or (args.w_layout == "auto" and M > 32 and N % 32 == 0 and K % 256 == 0)
+    if tiled:   # offline repack, outside the timed region like the preparation itself
+        wc0, ws0 = mx.tile_weights(wc0, ws0)
+        flags |= mx.W_TILED
     set_bytes = x0.numel() * x0.element_size() + wc0.numel() + ws0.numel() + M * N * 4   # y at most fp32 [M][N]
     R = max(2, min(64, -(-(4 * MALL_BYTES) // set_bytes)))
     xs = [x0] + [x0.clone() for _ in range(R - 1)]
@@ -534,6 +545,7 @@ def main():
     y_dtype = torch.float32 if args.out == "f32" else torch.bfloat16
     ydt = mx.F32 if args.out == "f32" else mx.BF16
     epi = mx.EPI_SWIGLU if args.epilogue == "swiglu" else mx.EPI_NONE
+    gemm_epi = epi | (mx.W_TILED if tiled else 0)   # macaq_gemm_ex takes the layout bit with the epilogue
     y_cols = N // 2 if epi == mx.EPI_SWIGLU else N
     ys = [torch.empty((M, y_cols), dtype=y_dtype, device=dev) for _ in range(R)]
     need = L.macaq_linear_workspace_bytes(M, N, K, E, flags)
@@ -591,7 +603,7 @@ def main():
     def gemm_only(i):
         _, wcp, wsp, yp = step_args(i)
         if mx.macaq_gemm_ex(p(a_codes.data_ptr()), p(a_scales.data_ptr()), off_p, E, wcp, wsp, M, N, K, yp, ydt,
-                            epi, p(gemm_ws.data_ptr()), gemm_ws.numel(), sp) != 0:
+                            gemm_epi, p(gemm_ws.data_ptr()), gemm_ws.numel(), sp) != 0:
             raise RuntimeError(mx.lib().macaq_last_error().decode())
 
     def kernel_us(fn):
@@ -634,6 +646,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": desc, "M": M, "N": N, "K": K, "experts": E, "x_dtype": str(x0.dtype).split(".")[-1],
                    "path": "fused" if fused else "unfused", "replicas": R,
+                   "w_layout": "tiled" if tiled else "row-major",
                    "y": f"{args.out} [{M}][{y_cols}]" + (" swiglu" if epi == mx.EPI_SWIGLU else ""),
                    "parallelism": "none (one GPU)"},
     }
@@ -672,7 +685,8 @@ def main():
                                 "traffic": traffic_record(f"{args.workload}:gemm{out_key}")})
     if not args.no_ablation and not fused:
         out["transform_overhead"] = transform_overhead(args, mx, L, wl, xs, wss, wcs, ys, s0, off_p, stream, sp,
-                                                       a_codes, a_scales, gemm_ws, M, N, K, E, R, ydt, epi)
+                                                       a_codes, a_scales, gemm_ws, M, N, K, E, R, ydt, gemm_epi,
+                                                       tiled=tiled)
     out["gpu_state"] = {"before": state_before, "after": state_after}
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(wl, min(args.cpu_rows, M))

@@ -100,6 +100,12 @@ enum {
   MACAQ_EPI_SWIGLU = 1  /* weight rows are (gate, up) pairs: y[m][j] = silu(out[m][2j]) * out[m][2j+1] */
 };
 
+/* Layout bit: w_codes / w_scales are in the tiled layout made by
+ * macaq_tile_weights.  OR'ed into the flags of macaq_linear / macaq_linear_ex
+ * / macaq_linear_path / macaq_linear_workspace_bytes and into the epilogue
+ * argument of macaq_gemm_ex. */
+#define MACAQ_W_TILED 0x100u
+
 /* Library version as major*10000 + minor*100 + patch. */
 int macaq_version(void);
 
@@ -310,6 +316,24 @@ int macaq_linear_ex(const void* x, macaq_dtype x_dtype, const float* s,
                     const uint8_t* w_codes, const uint8_t* w_scales,
                     int64_t M, int64_t N, int64_t K, void* y, macaq_dtype y_dtype, uint32_t epilogue,
                     void* workspace, size_t workspace_bytes, uint32_t flags, void* stream);
+
+/*
+ * Repack of prepared weights into the tiled layout that the prefill and
+ * grouped GEMMs read with contiguous copies (an offline step beside
+ * macaq_prepare_weights; the codes and scale bytes themselves are unchanged,
+ * only their places).  Per expert, for 32-row group g and 256-wide K-tile t:
+ * 4096 bytes of codes at (g * K/256 + t) * 4096, where row r of the group
+ * has its 128 bytes at 128 r with its 16-byte chunk c (32 values) at
+ * position c ^ ((r >> 1) & 7); and 256 bytes of scales at
+ * (g * K/256 + t) * 256, row r's 8 bytes at 8 r.
+ *   w_codes [E][N][K/2], w_scales [E][N][K/32] (macaq_prepare_weights'
+ *   layout) in; t_codes, t_scales (same sizes) out; no aliasing.
+ * Requires N % 32 == 0, K % 256 == 0, code pointers 16-byte and scale
+ * pointers 4-byte aligned.  Layers with tiled weights (MACAQ_W_TILED) always
+ * take the unfused path and the prefill / grouped GEMM, also for M <= 32.
+ */
+int macaq_tile_weights(const uint8_t* w_codes, const uint8_t* w_scales, int64_t E, int64_t N, int64_t K,
+                       uint8_t* t_codes, uint8_t* t_scales, void* stream);
 
 /*
  * Plain OCP MXFP4 quantization of rows, without the scale and the Hadamard

@@ -31,6 +31,7 @@ library_path = os.path.join(_HERE, "libmacaq.so")
 BF16, F32 = 0, 1
 PATH_AUTO, PATH_FUSED, PATH_UNFUSED = 0, 1, 2
 EPI_NONE, EPI_SWIGLU = 0, 1
+W_TILED = 0x100   # weights in macaq_tile_weights' layout (OR into linear's flags / gemm's epilogue)
 STATUS = {0: "ok", -1: "invalid argument", -2: "unsupported", -3: "no device", -4: "HIP error",
           -5: "workspace too small"}
 
@@ -75,6 +76,7 @@ def _load():
         "macaq_prepare_weights_hessian": (ci, [vp, ci, vp, vp, i64, i64, i64, vp, vp, vp]),
         "macaq_flip_refine": (ci, [vp, ci, vp, vp, i64, i64, i64, ctypes.c_int32, vp, vp, vp, vp, sz, vp]),
         "macaq_flip_refine_workspace_bytes": (sz, [i64, i64]),
+        "macaq_tile_weights": (ci, [vp, vp, i64, i64, i64, vp, vp, vp]),
     }
     for name, (res, args) in sig.items():
         f = getattr(L, name)
@@ -286,7 +288,7 @@ def _w_shape(w_codes, w_scales):
 def _out(M, N, out_dtype, epilogue, device, out):
     if out_dtype not in (torch.float32, torch.bfloat16):
         raise TypeError(f"out_dtype must be float32 or bfloat16, got {out_dtype}")
-    width = N // 2 if epilogue == EPI_SWIGLU else N
+    width = N // 2 if (epilogue & ~W_TILED) == EPI_SWIGLU else N
     if out is None:
         return torch.empty((M, width), dtype=out_dtype, device=device)
     _need(out, "out", out_dtype, 2)
@@ -345,6 +347,21 @@ def linear(x, s, w_codes, w_scales, offsets=None, flags=PATH_AUTO, out=None, wor
                            M, N, K, _ptr(y), ydt, epilogue, _ptr(workspace), ws_bytes, flags, _stream(x.device)),
            "macaq_linear")
     return y
+
+
+def tile_weights(w_codes, w_scales):
+    """Prepared weights (row-major codes [E, N, K/2], scales [E, N, K/32])
+    repacked into the tiled layout the prefill and grouped GEMMs read with
+    contiguous copies; same shapes and bytes, other places.  Use the result
+    with W_TILED in linear's flags or gemm's epilogue.  N % 32 == 0 and
+    K % 256 == 0."""
+    _load()
+    w_codes, w_scales = _w_shape(w_codes, w_scales)
+    E, N, KH = w_codes.shape
+    tc, ts = torch.empty_like(w_codes), torch.empty_like(w_scales)
+    _check(macaq_tile_weights(_ptr(w_codes), _ptr(w_scales), E, N, 2 * KH, _ptr(tc), _ptr(ts),
+                              _stream(w_codes.device)), "macaq_tile_weights")
+    return tc, ts
 
 
 def quant_mxfp4(x: torch.Tensor):

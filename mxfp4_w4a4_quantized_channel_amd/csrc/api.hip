@@ -41,6 +41,11 @@ hipError_t launch_flip_rounds(const float* H, int E, int64_t row0, int64_t rows,
                               hipStream_t stream);
 hipError_t launch_decode_gemm(const uint8_t* A, const uint8_t* As, const uint8_t* W, const uint8_t* Ws, int64_t M,
                               int64_t N, int64_t K, void* Y, int mode, hipStream_t stream);
+hipError_t launch_gemm_tiled(const uint8_t* A, const uint8_t* As, const int32_t* offsets, int E, const uint8_t* B,
+                             const uint8_t* Bs, int64_t M, int64_t N, int64_t K, void* Y, int mode,
+                             hipStream_t stream);
+hipError_t launch_tile_weights(const uint8_t* wc, const uint8_t* ws, int64_t E, int64_t N, int64_t K, uint8_t* tc,
+                               uint8_t* ts, hipStream_t stream);
 // output mode bits of the GEMM kernels (mx_common.h)
 constexpr int kOutBf16 = 1;
 constexpr int kOutSwiGLU = 2;
@@ -174,6 +179,13 @@ int validate_gemm(const uint8_t* a_codes, const uint8_t* a_scales, const int32_t
   return MACAQ_OK;
 }
 
+// Shape rule of the tiled W' layout.
+int check_tiled(int64_t N, int64_t K, const char* fn) {
+  if (N % 32 != 0 || K % 256 != 0)
+    return fail(MACAQ_ERR_UNSUPPORTED, std::string(fn) + ": tiled weights need N % 32 == 0 and K % 256 == 0");
+  return MACAQ_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -287,13 +299,16 @@ size_t macaq_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, int64_t E) {
 }
 
 int macaq_linear_path(int64_t M, int64_t N, int64_t K, int64_t E, uint32_t flags) {
+  const bool tiled = (flags & MACAQ_W_TILED) != 0;
+  flags &= ~MACAQ_W_TILED;
   if (flags > MACAQ_PATH_UNFUSED) return fail(MACAQ_ERR_INVALID_ARG, "macaq_linear_path: unknown flags");
+  if (tiled) return MACAQ_PATH_UNFUSED;   // tiled weights: transform kernel, then the prefill / grouped GEMM
   if (flags != MACAQ_PATH_AUTO) return (int)flags;
   return (macaq::linear_fused_supported(M, N, K, E) && M <= kMaxFusedM) ? MACAQ_PATH_FUSED : MACAQ_PATH_UNFUSED;
 }
 
 size_t macaq_linear_workspace_bytes(int64_t M, int64_t N, int64_t K, int64_t E, uint32_t flags) {
-  if (M <= 0 || N <= 0 || K <= 0 || E <= 0) return 0;
+  if (M <= 0 || N <= 0 || K <= 0 || E <= 0) return 0;   // (MACAQ_W_TILED: the unfused path's workspace)
   const int path = macaq_linear_path(M, N, K, E, flags);
   if (path == MACAQ_PATH_FUSED) return 0;
   if (path == MACAQ_PATH_UNFUSED) return macaq_quant_act_bytes(M, K) + macaq_gemm_workspace_bytes(M, N, K, E);
@@ -303,8 +318,12 @@ size_t macaq_linear_workspace_bytes(int64_t M, int64_t N, int64_t K, int64_t E, 
 namespace {
 int run_gemm(const uint8_t* a_codes, const uint8_t* a_scales, const int32_t* expert_offsets, int64_t E,
              const uint8_t* w_codes, const uint8_t* w_scales, int64_t M, int64_t N, int64_t K, void* y, int mode,
-             void* workspace, hipStream_t stream, const char* fn) {
+             void* workspace, hipStream_t stream, const char* fn, bool w_tiled = false) {
   (void)workspace;
+  if (w_tiled)
+    return hip_status(macaq::launch_gemm_tiled(a_codes, a_scales, E > 1 ? expert_offsets : nullptr, (int)E, w_codes,
+                                               w_scales, M, N, K, y, mode, stream),
+                      fn);
   if (macaq::decode_supported(M, N, K, E))
     return hip_status(macaq::launch_decode_gemm(a_codes, a_scales, w_codes, w_scales, M, N, K, y, mode, stream), fn);
   return hip_status(macaq::launch_gemm(a_codes, a_scales, E > 1 ? expert_offsets : nullptr, (int)E, w_codes,
@@ -327,16 +346,20 @@ int macaq_gemm_ex(const uint8_t* a_codes, const uint8_t* a_scales, const int32_t
                   const uint8_t* w_codes, const uint8_t* w_scales, int64_t M, int64_t N, int64_t K, void* y,
                   macaq_dtype y_dtype, uint32_t epilogue, void* workspace, size_t workspace_bytes, void* stream) {
   const char* fn = "macaq_gemm";
+  const bool w_tiled = (epilogue & MACAQ_W_TILED) != 0;
+  epilogue &= ~MACAQ_W_TILED;
   if (int st = validate_gemm(a_codes, a_scales, expert_offsets, E, w_codes, w_scales, M, N, K, y, fn)) return st;
   int mode = 0;
   if (int st = output_mode(y_dtype, epilogue, N, y, fn, &mode)) return st;
+  if (w_tiled)
+    if (int st = check_tiled(N, K, fn)) return st;
   if (M == 0) return MACAQ_OK;
   if (int st = check_workspace(workspace, workspace_bytes, macaq_gemm_workspace_bytes(M, N, K, E), fn)) return st;
   if (int st = check_device()) return st;
   if (int st = check_inputs(fn, (hipStream_t)stream, expert_offsets, E, M, nullptr, 0)) return st;
   return finish(fn, (hipStream_t)stream,
                 run_gemm(a_codes, a_scales, expert_offsets, E, w_codes, w_scales, M, N, K, y, mode, workspace,
-                         (hipStream_t)stream, fn));
+                         (hipStream_t)stream, fn, w_tiled));
 }
 
 int macaq_gemm(const uint8_t* a_codes, const uint8_t* a_scales, const int32_t* expert_offsets, int64_t E,
@@ -352,7 +375,9 @@ int macaq_linear_ex(const void* x, macaq_dtype x_dtype, const float* s, const in
                     void* stream) {
   const char* fn = "macaq_linear";
   if (int st = check_dtype(x_dtype, fn)) return st;
-  if (flags > MACAQ_PATH_UNFUSED) return fail(MACAQ_ERR_INVALID_ARG, std::string(fn) + ": unknown flags");
+  const bool w_tiled = (flags & MACAQ_W_TILED) != 0;
+  if ((flags & ~MACAQ_W_TILED) > MACAQ_PATH_UNFUSED)
+    return fail(MACAQ_ERR_INVALID_ARG, std::string(fn) + ": unknown flags");
   if (!x && M > 0) return fail(MACAQ_ERR_INVALID_ARG, std::string(fn) + ": null x");
   if (!s) return fail(MACAQ_ERR_INVALID_ARG, std::string(fn) + ": null s");
   if (M > 0 && (!aligned(x, 16) || !aligned(s, 16)))
@@ -362,6 +387,11 @@ int macaq_linear_ex(const void* x, macaq_dtype x_dtype, const float* s, const in
   if (int st = validate_gemm(dummy, w_scales, expert_offsets, E, w_codes, w_scales, M, N, K, y, fn)) return st;
   int mode = 0;
   if (int st = output_mode(y_dtype, epilogue, N, y, fn, &mode)) return st;
+  if (w_tiled) {
+    if (int st = check_tiled(N, K, fn)) return st;
+    if ((flags & ~MACAQ_W_TILED) == MACAQ_PATH_FUSED)
+      return fail(MACAQ_ERR_UNSUPPORTED, std::string(fn) + ": the fused decode path reads row-major weights");
+  }
   if (M == 0) return MACAQ_OK;
   if (flags == MACAQ_PATH_FUSED && !macaq::linear_fused_supported(M, N, K, E))
     return fail(MACAQ_ERR_UNSUPPORTED, std::string(fn) +
@@ -388,7 +418,7 @@ int macaq_linear_ex(const void* x, macaq_dtype x_dtype, const float* s, const in
   void* gemm_ws = static_cast<uint8_t*>(workspace) + macaq_quant_act_bytes(M, K);
   return finish(fn, st,
                 run_gemm(a_codes, a_scales, off, E, w_codes, w_scales, M, N, K, y, mode, gemm_ws, st,
-                         "macaq_linear (gemm)"));
+                         "macaq_linear (gemm)", w_tiled));
 }
 
 int macaq_linear(const void* x, macaq_dtype x_dtype, const float* s, const int32_t* expert_offsets, int64_t E,
@@ -396,6 +426,30 @@ int macaq_linear(const void* x, macaq_dtype x_dtype, const float* s, const int32
                  void* workspace, size_t workspace_bytes, uint32_t flags, void* stream) {
   return macaq_linear_ex(x, x_dtype, s, expert_offsets, E, w_codes, w_scales, M, N, K, y, MACAQ_F32, MACAQ_EPI_NONE,
                          workspace, workspace_bytes, flags, stream);
+}
+
+int macaq_tile_weights(const uint8_t* w_codes, const uint8_t* w_scales, int64_t E, int64_t N, int64_t K,
+                       uint8_t* t_codes, uint8_t* t_scales, void* stream) {
+  const char* fn = "macaq_tile_weights";
+  if (E < 1 || N < 1) return fail(MACAQ_ERR_INVALID_ARG, std::string(fn) + ": need E >= 1 and N >= 1");
+  if (int st = check_k(K, fn)) return st;
+  if (int st = check_tiled(N, K, fn)) return st;
+  if (!w_codes || !w_scales || !t_codes || !t_scales)
+    return fail(MACAQ_ERR_INVALID_ARG, std::string(fn) + ": null pointer");
+  if (!aligned(w_codes, 16) || !aligned(t_codes, 16) || !aligned(w_scales, 4) || !aligned(t_scales, 4))
+    return fail(MACAQ_ERR_INVALID_ARG, std::string(fn) + ": code pointers must be 16-byte, scale pointers 4-byte aligned");
+  if (E > 4096 || E * N > INT32_MAX)
+    return fail(MACAQ_ERR_UNSUPPORTED, std::string(fn) + ": sizes beyond the supported range");
+  const uint8_t* wc_end = w_codes + (size_t)E * N * (K / 2);
+  const uint8_t* tc_end = t_codes + (size_t)E * N * (K / 2);
+  if (t_codes < wc_end && w_codes < tc_end)
+    return fail(MACAQ_ERR_INVALID_ARG, std::string(fn) + ": t_codes must not overlap w_codes");
+  if (int st = check_device()) return st;
+  if (int st = check_inputs(fn, (hipStream_t)stream, nullptr, 1, 0, nullptr, 0)) return st;
+  return finish(fn, (hipStream_t)stream,
+                hip_status(macaq::launch_tile_weights(w_codes, w_scales, E, N, K, t_codes, t_scales,
+                                                      (hipStream_t)stream),
+                           fn));
 }
 
 int macaq_quant_mxfp4(const void* x, macaq_dtype x_dtype, int64_t M, int64_t K, uint8_t* codes, uint8_t* scales,

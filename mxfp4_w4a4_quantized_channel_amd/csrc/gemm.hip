@@ -8,38 +8,66 @@ namespace macaq {
 
 namespace {
 
-template <int BM, int BN, int WM, int WN, int BK, int S, int MINB, int OUT>
+template <int BM, int BN, int WM, int WN, int BK, int S, int MINB, int OUT, bool BT>
 hipError_t launch_pipe_out(const uint8_t* A, const uint8_t* As, const int32_t* offsets, int E, const uint8_t* B,
                            const uint8_t* Bs, int64_t M, int64_t N, int64_t K, void* Y, hipStream_t stream) {
   using L = PipeLayout<BM, BN, BK, 1>;
   constexpr int lds = S * L::kStage;
   static const hipError_t attr =
-      hipFuncSetAttribute((const void*)gemm_mxfp4_pipe_kernel<BM, BN, WM, WN, BK, S, MINB, OUT>,
+      hipFuncSetAttribute((const void*)gemm_mxfp4_pipe_kernel<BM, BN, WM, WN, BK, S, MINB, OUT, BT>,
                           hipFuncAttributeMaxDynamicSharedMemorySize, lds);
   if (attr != hipSuccess) return attr;
   const int tiles_n = (int)ceil_div(N, BN);
   int64_t tiles_m = ceil_div(M, BM);
   if (offsets != nullptr) tiles_m += E;  // each expert may add one partial row tile
   const int64_t blocks = tiles_m * tiles_n;
-  gemm_mxfp4_pipe_kernel<BM, BN, WM, WN, BK, S, MINB, OUT>
+  gemm_mxfp4_pipe_kernel<BM, BN, WM, WN, BK, S, MINB, OUT, BT>
       <<<dim3((unsigned)blocks), dim3(64 * WM * WN), lds, stream>>>(A, As, B, Bs, offsets, E, M, N, K, Y,
                                                                     (int)tiles_m, tiles_n, 4);
   return hipGetLastError();
 }
 
 // output mode (run time) -> kernel instantiation
-template <int BM, int BN, int WM, int WN, int BK, int S, int MINB = 1>
+template <int BM, int BN, int WM, int WN, int BK, int S, int MINB = 1, bool BT = false>
 hipError_t launch_pipe(const uint8_t* A, const uint8_t* As, const int32_t* offsets, int E, const uint8_t* B,
                        const uint8_t* Bs, int64_t M, int64_t N, int64_t K, void* Y, int mode, hipStream_t stream) {
   switch (mode) {
-    case 0: return launch_pipe_out<BM, BN, WM, WN, BK, S, MINB, 0>(A, As, offsets, E, B, Bs, M, N, K, Y, stream);
+    case 0: return launch_pipe_out<BM, BN, WM, WN, BK, S, MINB, 0, BT>(A, As, offsets, E, B, Bs, M, N, K, Y, stream);
     case kOutBf16:
-      return launch_pipe_out<BM, BN, WM, WN, BK, S, MINB, kOutBf16>(A, As, offsets, E, B, Bs, M, N, K, Y, stream);
+      return launch_pipe_out<BM, BN, WM, WN, BK, S, MINB, kOutBf16, BT>(A, As, offsets, E, B, Bs, M, N, K, Y, stream);
     case kOutSwiGLU:
-      return launch_pipe_out<BM, BN, WM, WN, BK, S, MINB, kOutSwiGLU>(A, As, offsets, E, B, Bs, M, N, K, Y, stream);
+      return launch_pipe_out<BM, BN, WM, WN, BK, S, MINB, kOutSwiGLU, BT>(A, As, offsets, E, B, Bs, M, N, K, Y,
+                                                                          stream);
     default:
-      return launch_pipe_out<BM, BN, WM, WN, BK, S, MINB, kOutBf16 | kOutSwiGLU>(A, As, offsets, E, B, Bs, M, N, K,
-                                                                                  Y, stream);
+      return launch_pipe_out<BM, BN, WM, WN, BK, S, MINB, kOutBf16 | kOutSwiGLU, BT>(A, As, offsets, E, B, Bs, M, N,
+                                                                                      K, Y, stream);
+  }
+}
+
+// Repack of prepared W' (row-major codes [E][N][K/2], scales [E][N][K/32])
+// into the tiled layout: per expert, for each 32-row group g and 256-wide
+// K-tile t, 4 KiB of codes (row r of the group at byte 128 r, its 16-byte
+// chunk c at position c ^ ((r >> 1) & 7)) and 256 bytes of scales (row r's 8
+// bytes at 8 r).  One thread per 16-byte code chunk (and per 4 scale bytes).
+__global__ void tile_weights_kernel(const uint8_t* __restrict__ wc, const uint8_t* __restrict__ ws, int64_t rows,
+                                    int64_t K, uint8_t* __restrict__ tc, uint8_t* __restrict__ ts) {
+  const int64_t KT = K >> 8;                       // K-tiles per row
+  const int64_t chunks = rows * (K >> 5);          // 16-byte code chunks (= 32-value groups)
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < chunks) {
+    const int64_t row = i / (K >> 5), c_all = i % (K >> 5);    // row over all experts (N % 32 == 0)
+    const int64_t t = c_all >> 3;
+    const int c = (int)(c_all & 7);
+    const int r = (int)(row & 31);
+    const int64_t dst = ((row >> 5) * KT + t) * 4096 + r * 128 + ((c ^ ((r >> 1) & 7)) << 4);
+    *reinterpret_cast<uint4*>(tc + dst) = *reinterpret_cast<const uint4*>(wc + row * (K >> 1) + c_all * 16);
+  }
+  if (i < rows * (K >> 7)) {   // 4-byte scale words: (row, K-tile, half)
+    const int64_t row = i / (K >> 7), w = i % (K >> 7);
+    const int64_t t = w >> 1;
+    const int half = (int)(w & 1);
+    const int64_t dst = ((row >> 5) * KT + t) * 256 + (row & 31) * 8 + half * 4;
+    *reinterpret_cast<uint32_t*>(ts + dst) = *reinterpret_cast<const uint32_t*>(ws + row * (K >> 5) + w * 4);
   }
 }
 
@@ -57,6 +85,37 @@ hipError_t launch_v1(const uint8_t* A, const uint8_t* As, const int32_t* offsets
 }
 
 }  // namespace
+
+hipError_t launch_tile_weights(const uint8_t* wc, const uint8_t* ws, int64_t E, int64_t N, int64_t K, uint8_t* tc,
+                               uint8_t* ts, hipStream_t stream) {
+  const int64_t rows = E * N;
+  const int64_t threads = rows * (K >> 5);   // >= the scale words rows * K / 128
+  if (threads <= 0) return hipSuccess;
+  tile_weights_kernel<<<dim3((unsigned)ceil_div(threads, 256)), dim3(256), 0, stream>>>(wc, ws, rows, K, tc, ts);
+  return hipGetLastError();
+}
+
+// GEMM with W' in the tiled layout (N % 32 == 0, K % 256 == 0): 256x256 when
+// that gives about one tile per CU, else 128x128 with two blocks per CU
+// (with contiguous W' copies the smaller tile is faster than 256x128:
+// attn-proj 25.3 against 29.6 us on random operands).
+hipError_t launch_gemm_tiled(const uint8_t* A, const uint8_t* As, const int32_t* offsets, int E, const uint8_t* B,
+                             const uint8_t* Bs, int64_t M, int64_t N, int64_t K, void* Y, int mode,
+                             hipStream_t stream) {
+  if (M <= 0) return hipSuccess;
+  const int64_t t256 = ceil_div(M, 256) * ceil_div(N, 256);
+  int choice = (offsets == nullptr && t256 >= 240) ? 0 : 2;
+  if (const char* force = getenv("MACAQ_GEMM_TILE")) {
+    if (strcmp(force, "256x256") == 0) choice = 0;
+    else if (strcmp(force, "256x128") == 0) choice = 1;
+    else if (strcmp(force, "128x128") == 0) choice = 2;
+  }
+  switch (choice) {
+    case 0: return launch_pipe<256, 256, 2, 2, 256, 2, 1, true>(A, As, offsets, E, B, Bs, M, N, K, Y, mode, stream);
+    case 1: return launch_pipe<256, 128, 2, 2, 256, 2, 1, true>(A, As, offsets, E, B, Bs, M, N, K, Y, mode, stream);
+    default: return launch_pipe<128, 128, 2, 2, 256, 2, 2, true>(A, As, offsets, E, B, Bs, M, N, K, Y, mode, stream);
+  }
+}
 
 hipError_t launch_gemm(const uint8_t* A, const uint8_t* As, const int32_t* offsets, int E,
                        const uint8_t* B, const uint8_t* Bs, int64_t M, int64_t N, int64_t K,

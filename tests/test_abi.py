@@ -162,6 +162,7 @@ def test_valid_calls_without_a_device_report_no_device():
     assert mx.macaq_hessian(A16, 0, A16, None, 1, 16, 128, A16, None) == NO_DEVICE
     assert mx.macaq_prepare_weights_hessian(A16, 0, A16, A16, 1, 8, 64, A16, A16, None) == NO_DEVICE
     assert mx.macaq_flip_refine(A16, 0, A16, A16, 1, 8, 256, 4, A16, A16, None, A16, 1 << 20, None) == NO_DEVICE
+    assert mx.macaq_tile_weights(A16, A16, 1, 64, 512, A16 * 16, A16 * 16, None) == NO_DEVICE
     assert b"no HIP device" in mx.lib().macaq_last_error()
 
 
@@ -210,3 +211,32 @@ def test_output_dtype_and_epilogue_validation():
     assert ge(A16, A16, None, 1, A16, A16, 0, 8, 256, A16 + 2, 0, 1, None, 0, None) == OK   # M == 0: no-op
     le = mx.macaq_linear_ex
     assert le(A16, 0, A16, None, 1, A16, A16, 4, 9, 256, A16, 0, 1, None, 0, 0, None) == INVALID
+
+
+def test_tiled_weights_validation():
+    """macaq_tile_weights and the MACAQ_W_TILED layout bit: shape rule
+    (N % 32 == 0, K % 256 == 0), pointers, aliasing; layers with tiled
+    weights take the two-launch path and refuse the fused decode path."""
+    mx.lib()
+    tw = mx.macaq_tile_weights
+    A2 = A16 * 16
+    assert tw(A16, A16, 1, 48, 512, A2, A2, None) == UNSUPPORTED      # N % 32 != 0
+    assert tw(A16, A16, 1, 64, 384, A2, A2, None) == UNSUPPORTED      # K % 256 != 0
+    assert tw(A16, A16, 1, 64, 48, A2, A2, None) == INVALID           # K % 32 != 0
+    assert tw(A16, A16, 0, 64, 512, A2, A2, None) == INVALID
+    assert tw(None, A16, 1, 64, 512, A2, A2, None) == INVALID
+    assert tw(A16 + 4, A16, 1, 64, 512, A2, A2, None) == INVALID      # misaligned codes
+    assert tw(A16, A16 + 2, 1, 64, 512, A2, A2, None) == INVALID      # misaligned scales
+    assert tw(A16, A16, 1, 64, 512, A16 + 256, A2, None) == INVALID   # output overlaps input
+    T = mx.W_TILED
+    ge = mx.macaq_gemm_ex
+    assert ge(A16, A16, None, 1, A16, A16, 4, 48, 256, A16, 0, T, None, 0, None) == UNSUPPORTED
+    assert ge(A16, A16, None, 1, A16, A16, 4, 64, 384, A16, 0, T, None, 0, None) == UNSUPPORTED
+    assert ge(A16, A16, None, 1, A16, A16, 4, 64, 256, A16, 0, T | 4, None, 0, None) == INVALID   # unknown epilogue
+    assert ge(A16, A16, None, 1, A16, A16, 0, 64, 256, A16, 0, T, None, 0, None) == OK           # M == 0
+    le = mx.macaq_linear_ex
+    assert le(A16, 0, A16, None, 1, A16, A16, 1, 64, 256, A16, 0, 0, None, 0, mx.PATH_FUSED | T, None) == UNSUPPORTED
+    assert le(A16, 0, A16, None, 1, A16, A16, 1, 64, 256, A16, 0, 0, None, 0, 8 | T, None) == INVALID
+    L = mx.lib()
+    assert L.macaq_linear_path(1, 25600, 5120, 1, mx.PATH_AUTO | T) == mx.PATH_UNFUSED
+    assert L.macaq_linear_workspace_bytes(1, 25600, 5120, 1, mx.PATH_AUTO | T) == L.macaq_quant_act_bytes(1, 5120)

@@ -1,0 +1,155 @@
+"""Tiled W' (macaq_tile_weights and MACAQ_W_TILED) on the GPU, through the C
+ABI.  The repack is a permutation of bytes: it must equal a re-layout of
+the row-major codes and scales written out here in numpy.  The GEMM reads
+the same LDS tiles from either layout, so for a given tile shape its output
+must be bitwise equal to the row-major GEMM's, and both are within the
+oracle's bound."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+import mxfp4_w4a4_quantized_channel_amd as mx
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+RTOL = 1e-5
+
+
+def say(msg):
+    print(f"[case] {msg}", flush=True)
+
+
+def host(t: torch.Tensor) -> np.ndarray:
+    t = t.detach().cpu().contiguous()
+    if t.dtype == torch.bfloat16:
+        return workloads.bf16_bits(t)
+    return t.numpy()
+
+
+def tiled_reference(codes: np.ndarray, scales: np.ndarray):
+    """The tiled layout as the header defines it: per expert, per 32-row group
+    and 256-wide K-tile, 32 rows of 128 code bytes whose 16-byte chunk c sits
+    at position c ^ ((r >> 1) & 7), then 32 rows of 8 scale bytes."""
+    E, N, KH = codes.shape
+    G, T = N // 32, KH // 128
+    c = codes.reshape(E, G, 32, T, 8, 16).transpose(0, 1, 3, 2, 4, 5)    # [E, G, T, r, chunk, 16]
+    r = np.arange(32)[:, None]
+    p = np.arange(8)[None, :]
+    src = p ^ ((r >> 1) & 7)                                             # chunk held at position p
+    c = np.take_along_axis(c, np.broadcast_to(src[None, None, None, :, :, None], c.shape), axis=4)
+    s = scales.reshape(E, G, 32, T, 8).transpose(0, 1, 3, 2, 4)          # [E, G, T, r, 8]
+    return np.ascontiguousarray(c).reshape(E, N, KH), np.ascontiguousarray(s).reshape(E, N, KH // 16)
+
+
+@pytest.mark.parametrize("E,N,K", [(1, 32, 256), (2, 96, 768), (3, 128, 3072)])
+def test_tile_weights_layout(E, N, K):
+    say(f"tile_weights E{E} N{N} K{K}")
+    rng = np.random.default_rng(E * 1000 + N + K)
+    codes = rng.integers(0, 256, (E, N, K // 2), dtype=np.uint8)
+    scales = rng.integers(0, 256, (E, N, K // 32), dtype=np.uint8)
+    tc, ts = mx.tile_weights(torch.from_numpy(codes).to(DEV), torch.from_numpy(scales).to(DEV))
+    rc, rs = tiled_reference(codes, scales)
+    assert np.array_equal(tc.cpu().numpy(), rc)
+    assert np.array_equal(ts.cpu().numpy(), rs)
+
+
+def _operands(M, N, K, E=1, seed=0, offsets=None):
+    rng = np.random.default_rng(seed)
+    x = torch.from_numpy(rng.standard_normal((M, K)).astype(np.float32)).to(torch.bfloat16).to(DEV)
+    w = torch.from_numpy((rng.standard_normal((E, N, K)) * 0.02).astype(np.float32)).to(torch.bfloat16).to(DEV)
+    s = torch.from_numpy(rng.uniform(0.5, 2.0, (E, K)).astype(np.float32)).to(DEV)
+    ac, asc = mx.quant_act(x, s, offsets)
+    wc, wsc = mx.prepare_weights(w, s)
+    return x, s, ac, asc, wc, wsc
+
+
+TILED_SHAPES = [
+    ("one 128 tile", (128, 128, 256)),
+    ("ragged M, N tail of 32", (300, 224, 1024)),
+    ("M=1", (1, 64, 512)),
+    ("several 256 tiles", (520, 544, 2048)),
+]
+
+
+@pytest.mark.parametrize("tile", ["256x256", "256x128", "128x128"])
+@pytest.mark.parametrize("name,shape", TILED_SHAPES, ids=[n for n, _ in TILED_SHAPES])
+def test_tiled_gemm_equals_row_major(name, shape, tile, monkeypatch):
+    """Each tile variant: the tiled GEMM's fp32 y equals the row-major GEMM's
+    bit for bit, and is within the oracle's bound."""
+    M, N, K = shape
+    say(f"tiled gemm {name} M{M} N{N} K{K} tile {tile}")
+    monkeypatch.setenv("MACAQ_GEMM_TILE", tile)
+    x, s, ac, asc, wc, wsc = _operands(M, N, K, seed=M + N)
+    tc, ts = mx.tile_weights(wc, wsc)
+    y_t = mx.gemm(ac, asc, tc, ts, epilogue=mx.W_TILED)
+    if M > 32:   # at M <= 32 the row-major call takes the decode kernel: compare with the oracle only
+        y_r = mx.gemm(ac, asc, wc, wsc)
+        torch.cuda.synchronize()
+        assert torch.equal(y_t, y_r)
+    y_ref, S = oracle.gemm(ac.cpu().numpy(), asc.cpu().numpy(), wc[0].cpu().numpy(), wsc[0].cpu().numpy())
+    ok, worst, normwise = oracle.within_tolerance(y_t.cpu().numpy(), y_ref, S, RTOL)
+    assert ok, f"worst {worst:.3g}"
+
+
+def test_tiled_grouped_gemm_with_empty_experts():
+    """Grouped layer with ragged and empty experts: tiled equals row-major."""
+    say("tiled grouped gemm")
+    E, N, K = 5, 160, 512
+    counts = np.array([70, 0, 131, 1, 0])
+    off = torch.from_numpy(np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)).to(DEV)
+    M = int(counts.sum())
+    x, s, ac, asc, wc, wsc = _operands(M, N, K, E=E, seed=7, offsets=off)
+    tc, ts = mx.tile_weights(wc, wsc)
+    y_t = mx.gemm(ac, asc, tc, ts, off, epilogue=mx.W_TILED)
+    y_r = mx.gemm(ac, asc, wc, wsc, off)
+    torch.cuda.synchronize()
+    assert torch.equal(y_t, y_r)
+
+
+@pytest.mark.parametrize("epi,dt", [(mx.EPI_NONE, torch.float32), (mx.EPI_NONE, torch.bfloat16),
+                                    (mx.EPI_SWIGLU, torch.bfloat16), (mx.EPI_SWIGLU, torch.float32)])
+def test_tiled_linear_epilogues(epi, dt):
+    """The whole layer with tiled weights (two launches) equals the row-major
+    two-launch layer in every output form."""
+    say(f"tiled linear epilogue {epi} {dt}")
+    M, N, K = 200, 256, 1024
+    x, s, ac, asc, wc, wsc = _operands(M, N, K, seed=11)
+    tc, ts = mx.tile_weights(wc, wsc)
+    y_t = mx.linear(x, s, tc, ts, flags=mx.PATH_AUTO | mx.W_TILED, out_dtype=dt, epilogue=epi)
+    y_r = mx.linear(x, s, wc, wsc, flags=mx.PATH_UNFUSED, out_dtype=dt, epilogue=epi)
+    torch.cuda.synchronize()
+    assert torch.equal(y_t, y_r)
+
+
+def test_tiled_linear_decode_rows():
+    """M <= 32 with tiled weights takes the prefill GEMM (the decode kernel
+    reads row-major weights): within the oracle's bound."""
+    say("tiled linear M4")
+    M, N, K = 4, 128, 1024
+    x, s, ac, asc, wc, wsc = _operands(M, N, K, seed=3)
+    tc, ts = mx.tile_weights(wc, wsc)
+    y = mx.linear(x, s, tc, ts, flags=mx.W_TILED)
+    y_ref, S = oracle.gemm(ac.cpu().numpy(), asc.cpu().numpy(), wc[0].cpu().numpy(), wsc[0].cpu().numpy())
+    ok, worst, _ = oracle.within_tolerance(y.cpu().numpy(), y_ref, S, RTOL)
+    assert ok, f"worst {worst:.3g}"
+
+
+def test_tiled_full_size_attention_sampled():
+    """attn-proj at full size (M2048 N4096 K4096) with tiled weights in the
+    benchmark's default tile choice: bitwise equal to the row-major GEMM with
+    the same tile, and sampled rows within the oracle's bound."""
+    say("tiled full size attn-proj")
+    wl = workloads.make(2)
+    x, s = wl.x.to(DEV), wl.s.to(DEV)
+    ac, asc = mx.quant_act(x, s)
+    wc, wsc = mx.prepare_weights(wl.w.to(DEV), s)
+    tc, ts = mx.tile_weights(wc, wsc)
+    y_t = mx.gemm(ac, asc, tc, ts, epilogue=mx.W_TILED)
+    torch.cuda.synchronize()
+    rows = np.unique(np.concatenate([[0, wl.M - 1], np.random.default_rng(5).choice(wl.M, 14, replace=False)]))
+    a_np, as_np = ac.cpu().numpy()[rows], asc.cpu().numpy()[rows]
+    y_ref, S = oracle.gemm(a_np, as_np, wc[0].cpu().numpy(), wsc[0].cpu().numpy())
+    ok, worst, _ = oracle.within_tolerance(y_t.cpu().numpy()[rows], y_ref, S, RTOL)
+    assert ok, f"worst {worst:.3g}"
