@@ -499,6 +499,57 @@ __device__ __forceinline__ void tile_of_block(int bid, int ntiles, int tiles_m, 
 // scales.  A copy instruction then reads 1 KiB of contiguous codes (and a
 // scale copy 256 contiguous bytes) instead of 8 (32) rows' pieces: measured
 // 56 against 33 B/clk per CU for such copies in isolation.
+// Inclusive prefix sum of v over the wave's 64 lanes.
+__device__ __forceinline__ int wave_prefix_sum(int v, int lane) {
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int o = __shfl_up(v, d, 64);
+    if (lane >= d) v += o;
+  }
+  return v;
+}
+
+// Row tiles of BM rows per expert, from the device-side offsets, 64 experts
+// per step (lane l takes expert e0 + l; every wave computes the same result):
+// the total, and the expert, first row and end row of row tile `tm`.  Loads
+// and prefix sums run across the lanes, so a block pays two rounds of
+// parallel loads instead of 2E dependent ones.
+template <int BM>
+__device__ __forceinline__ int grouped_row_tiles(const int32_t* __restrict__ offsets, int E, int lane) {
+  int total = 0;
+  for (int e0 = 0; e0 < E; e0 += 64) {
+    const int e = e0 + lane;
+    const int t = e < E ? (int)(((int64_t)offsets[e + 1] - offsets[e] + BM - 1) / BM) : 0;
+    total += __shfl(wave_prefix_sum(t, lane), 63, 64);
+  }
+  return total;
+}
+template <int BM>
+__device__ __forceinline__ bool grouped_tile(const int32_t* __restrict__ offsets, int E, int lane, int tm, int* e_out,
+                                             int64_t* row_begin, int64_t* row_end) {
+  int base = 0;
+  for (int e0 = 0; e0 < E; e0 += 64) {
+    const int e = e0 + lane;
+    int64_t b = 0, en = 0;
+    if (e < E) {
+      b = offsets[e];
+      en = offsets[e + 1];
+    }
+    const int t = e < E ? (int)((en - b + BM - 1) / BM) : 0;
+    const int incl = base + wave_prefix_sum(t, lane), excl = incl - t;
+    const unsigned long long hit = __ballot(t > 0 && tm >= excl && tm < incl);
+    if (hit != 0ull) {
+      const int l = __ffsll(hit) - 1;
+      *e_out = e0 + l;
+      *row_begin = __shfl(b, l, 64) + (int64_t)(tm - __shfl(excl, l, 64)) * BM;
+      *row_end = __shfl(en, l, 64);
+      return true;
+    }
+    base = __shfl(incl, 63, 64);
+  }
+  return false;
+}
+
 template <int BM, int BN, int WAVES_M, int WAVES_N, int BK, int STAGES, int MINB = 1, int OUT = 0, bool BT = false>
 __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, MINB) void gemm_mxfp4_pipe_kernel(
     const uint8_t* __restrict__ A, const uint8_t* __restrict__ As, const uint8_t* __restrict__ B,
@@ -522,31 +573,17 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, MINB) void gemm_mxfp4_pipe_
   // ---- tile -> (expert, rows, columns).  Grouped: the active row tiles are
   // counted from the device-side offsets, so that the XCD-aware order spreads
   // only real tiles over the XCDs; surplus blocks exit.
-  int active_m = tiles_m;
-  if (offsets != nullptr) {
-    active_m = 0;
-    for (int e2 = 0; e2 < E; ++e2) active_m += (int)((offsets[e2 + 1] - offsets[e2] + BM - 1) / BM);
-  }
+  const int lane0 = (int)threadIdx.x & 63;
+  const int active_m = offsets != nullptr ? grouped_row_tiles<BM>(offsets, E, lane0) : tiles_m;
   if ((int)blockIdx.x >= active_m * tiles_n) return;
   int tm, tn;
   tile_of_block((int)blockIdx.x, active_m * tiles_n, active_m, tiles_n, group_m, &tm, &tn);
-  int64_t slot = tm;
   int e = 0;
   int64_t row_begin = 0, row_end = M;
   if (offsets != nullptr) {
-    for (e = 0; e < E; ++e) {
-      const int64_t b = offsets[e], en = offsets[e + 1];
-      const int64_t t = (en - b + BM - 1) / BM;
-      if (slot < t) {
-        row_begin = b + slot * BM;
-        row_end = en;
-        break;
-      }
-      slot -= t;
-    }
-    if (e == E) return;
+    if (!grouped_tile<BM>(offsets, E, lane0, tm, &e, &row_begin, &row_end)) return;
   } else {
-    row_begin = slot * BM;
+    row_begin = (int64_t)tm * BM;
     if (row_begin >= M) return;
   }
   const int64_t n0 = (int64_t)tn * BN;

@@ -153,3 +153,35 @@ def test_tiled_full_size_attention_sampled():
     y_ref, S = oracle.gemm(a_np, as_np, wc[0].cpu().numpy(), wsc[0].cpu().numpy())
     ok, worst, _ = oracle.within_tolerance(y_t.cpu().numpy()[rows], y_ref, S, RTOL)
     assert ok, f"worst {worst:.3g}"
+
+
+@pytest.mark.parametrize("E", [63, 64, 65, 130])
+def test_grouped_gemm_many_experts(E):
+    """The grouped GEMM finds each row tile's expert 64 experts at a time:
+    expert counts on both sides of 64, with runs of empty experts, ragged
+    counts and an expert past the first 64 that owns several row tiles.
+    Each expert's rows are within the oracle's bound against that expert's
+    weights, and the tiled layout equals the row-major one bit for bit."""
+    say(f"grouped gemm E{E}")
+    N, K = 64, 256
+    rng = np.random.default_rng(E)
+    counts = rng.integers(0, 40, E)
+    counts[rng.random(E) < 0.4] = 0
+    counts[E - 2] = 300
+    counts[0] = 0
+    off_np = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    off = torch.from_numpy(off_np).to(DEV)
+    M = int(counts.sum())
+    x, s, ac, asc, wc, wsc = _operands(M, N, K, E=E, seed=E + 1, offsets=off)
+    y = mx.gemm(ac, asc, wc, wsc, off)
+    tc, ts = mx.tile_weights(wc, wsc)
+    y_t = mx.gemm(ac, asc, tc, ts, off, epilogue=mx.W_TILED)
+    torch.cuda.synchronize()
+    assert torch.equal(y, y_t)
+    a_np, as_np, y_np = ac.cpu().numpy(), asc.cpu().numpy(), y.cpu().numpy()
+    wc_np, ws_np = wc.cpu().numpy(), wsc.cpu().numpy()
+    for e in np.nonzero(counts)[0]:
+        r0, r1 = off_np[e], off_np[e + 1]
+        y_ref, S = oracle.gemm(a_np[r0:r1], as_np[r0:r1], wc_np[e], ws_np[e])
+        ok, worst, _ = oracle.within_tolerance(y_np[r0:r1], y_ref, S, RTOL)
+        assert ok, f"expert {e}: worst {worst:.3g}"
