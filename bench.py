@@ -22,7 +22,6 @@ import ctypes
 import hashlib
 import json
 import os
-import subprocess
 import sys
 import time
 
@@ -189,28 +188,28 @@ def cpu_model():
     return None
 
 
+_SMI = {}
+
+
 def gpu_state():
-    """Clock, power and temperature of GPU 0 as amd-smi reports them at this
-    moment (None where amd-smi is missing or its output is not understood).
-    A snapshot, not an average: the clock under load is the counters' figure."""
+    """Clock, power and temperature of the first GPU as the AMD SMI library
+    reports them at this moment, read in-process (no child process), or None
+    where the library is missing or fails.  A snapshot, not an average: the
+    clock under load is the counters' figure."""
     try:
-        r = subprocess.run(["amd-smi", "metric", "-g", "0", "--clock", "--power", "--temperature", "--json"],
-                           capture_output=True, text=True, timeout=30)
-        d = json.loads(r.stdout)
-        g = d["gpu_data"][0] if isinstance(d, dict) else d[0]
-        val = lambda *path: _dig(g, path)
-        return {"sclk_mhz": val("clock", "gfx_0", "clk", "value"), "mclk_mhz": val("clock", "mem_0", "clk", "value"),
-                "power_w": val("power", "socket_power", "value"), "hotspot_c": val("temperature", "hotspot", "value")}
+        import amdsmi as smi
+        if "h" not in _SMI:
+            smi.amdsmi_init()
+            _SMI["h"] = smi.amdsmi_get_processor_handles()[0]
+        h = _SMI["h"]
+        power = smi.amdsmi_get_power_info(h)
+        return {"sclk_mhz": smi.amdsmi_get_clock_info(h, smi.AmdSmiClkType.GFX)["clk"],
+                "mclk_mhz": smi.amdsmi_get_clock_info(h, smi.AmdSmiClkType.MEM)["clk"],
+                "power_w": power.get("socket_power", power.get("current_socket_power")),
+                "hotspot_c": smi.amdsmi_get_temp_metric(h, smi.AmdSmiTemperatureType.HOTSPOT,
+                                                        smi.AmdSmiTemperatureMetric.CURRENT)}
     except Exception:
         return None
-
-
-def _dig(d, path):
-    for k in path:
-        if not isinstance(d, dict) or k not in d:
-            return None
-        d = d[k]
-    return d
 
 
 def sources_sha256(paths):

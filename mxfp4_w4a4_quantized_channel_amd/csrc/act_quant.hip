@@ -31,12 +31,14 @@ __global__ void encode_e2m1_kernel(const float* __restrict__ v, int64_t n, uint8
 }
 
 // ---------------------------------------------------------------------------
-// One-lane-per-group kernel.  A wave's 64 groups are read with coalesced
-// 16-byte loads, written to a wave-private LDS buffer whose 32-value groups
-// sit 16 bytes apart more than their size (no bank conflicts on the
-// per-group reads), and each lane then reads its own group.  All five
-// butterfly stages run in the lane's registers.  The next rows' loads are in
-// flight while the current ones are transformed.
+// One-lane-per-group kernel.  A wave's 64 groups are copied straight from
+// global memory into a wave-private LDS ring (global_load_lds_dwordx4,
+// coalesced: each copy instruction moves 1 KiB of consecutive bytes), and
+// each lane then reads its own group from there.  Within a group the 16-byte
+// chunks are XOR-swizzled so that the lanes' per-group reads hit every LDS
+// bank once per phase.  All five butterfly stages run in the lane's
+// registers.  The ring holds up to kDepth row blocks, so that many are in
+// flight while one is transformed, without holding registers for them.
 //
 // Normalization folded into the quantization multiply: amax(x') equals
 // RNE(max|u| * C) because rounding is monotone, and for scale bytes 3..250
@@ -47,10 +49,25 @@ __global__ void encode_e2m1_kernel(const float* __restrict__ v, int64_t n, uint8
 template <int EB>  // bytes per input element (2 = bf16, 4 = fp32)
 struct GroupIo {
   static constexpr int kGroupBytes = 32 * EB;
-  static constexpr int kLdsGroup = kGroupBytes + 16;         // padded stride
-  static constexpr int kWaveLds = 64 * kLdsGroup;            // one row segment
-  static constexpr int kLoads = 64 * kGroupBytes / 1024;     // 16-byte loads per lane
+  static constexpr int kChunks = 2 * EB;                     // 16-byte chunks per group
+  static constexpr int kBlockLds = 64 * kGroupBytes;         // one row block of a wave (4 or 8 KiB)
+  static constexpr int kLoads = kBlockLds / 1024;            // 16-byte copies per lane per row block
+  // LDS slot (16-byte unit) of chunk c of group g: chunk positions are
+  // XOR-swizzled by the group's index within its 128-byte bank line, so
+  // the 8 lanes of a read phase (8 consecutive groups, same c) cover 8
+  // distinct 16-byte bank groups.  The XOR is its own inverse: position p
+  // of group g holds chunk p ^ swz(g).
+  static __device__ __forceinline__ int swz(int g) { return (g / (8 / kChunks)) & (kChunks - 1); }
+  static __device__ __forceinline__ int slot(int g, int c) { return g * kChunks + (c ^ swz(g)); }
 };
+
+// Row blocks in flight per wave, and the block's LDS: each wave's ring, plus
+// (SHARED) two staged slices of s, within the 64 KiB a block may take
+// without an attribute: 48 KiB (bf16) or 64 KiB (fp32); with the staged
+// factors one row block (measured on attn-proj: 7.2 us, against 8.4 with
+// two, which allow fewer blocks per CU), 34 or 50 KiB.
+template <int EB, bool SHARED>
+constexpr int act_depth() { return SHARED ? 1 : (EB == 2 ? 3 : 2); }
 
 template <int EB>
 __device__ __forceinline__ void widen_group(const uint4 (&q)[EB * 2], float (&t)[32]) {
@@ -168,6 +185,23 @@ __device__ __forceinline__ void quantize_group_plain(const float (&u)[32], uint4
 // baseline against which the online transform's cost is measured.
 constexpr int kSStride = 36;                      // floats per staged group (144 B: conflict-free reads)
 constexpr int kSLds = 64 * kSStride * 4;          // one staged slice of s, bytes
+template <int EB, bool SHARED>
+constexpr int act_lds_bytes() { return (SHARED ? 2 * kSLds : 0) + 4 * act_depth<EB, SHARED>() * GroupIo<EB>::kBlockLds; }
+
+// Copy 16 bytes per lane from global memory to LDS at M0 + 16 * lane,
+// non-temporal (x is read once).
+__device__ __forceinline__ void dma16_nt(const uint8_t* g, uint32_t lds_addr) {
+  asm volatile("global_load_lds_dwordx4 %0, off nt" ::"v"(g), "{m0}"(lds_addr) : "memory");
+}
+
+// Wait until at most `later` row blocks' copies of this wave are in flight.
+template <int LOADS>
+__device__ __forceinline__ void wait_row_blocks(int later) {
+  if (later >= 2) wait_vmcnt<2 * LOADS>();
+  else if (later == 1) wait_vmcnt<LOADS>();
+  else wait_vmcnt<0>();
+  asm volatile("" ::: "memory");   // no LDS read moves above the wait
+}
 
 template <int EB, bool RECIP, bool PLAIN = false, bool SHARED = false>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(SHARED && EB == 2 && !RECIP ? 4 : (EB == 2 ? 3 : 2))))
@@ -179,7 +213,7 @@ void act_quant_lane_kernel(
   using IO = GroupIo<EB>;
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
   const int lane = threadIdx.x & 63;
-  const int wave_in_block = threadIdx.x >> 6;
+  const int wave_in_block = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform (SGPR)
   const int64_t KG = K >> 5;
   const int gs = 1 << gs_log2;
   const int rw = 64 >> gs_log2;                      // rows per block step
@@ -204,7 +238,9 @@ void act_quant_lane_kernel(
   const int seg_log2 = gs_log2 + 5 + (EB == 4 ? 2 : 1);   // log2 bytes of one row's segment
   const int64_t seg_groups = (KG - seg * gs < gs ? KG - seg * gs : gs);
   const int64_t seg_valid = seg_groups * IO::kGroupBytes;
-  uint8_t* buf = lds + (SHARED ? 2 * kSLds : 0) + wave_in_block * IO::kWaveLds;
+  constexpr int kDepth = act_depth<EB, SHARED>();
+  const uint32_t ring_off = (SHARED ? 2 * kSLds : 0) + (uint32_t)wave_in_block * kDepth * IO::kBlockLds;
+  const uint32_t ring_lds = (uint32_t)(uintptr_t)lds + ring_off;
   const float* s_lds = reinterpret_cast<const float*>(lds);
 
   // expert of a row (rows sorted by expert)
@@ -219,38 +255,81 @@ void act_quant_lane_kernel(
     return lo;
   };
 
-  uint4 ld[IO::kLoads];
-  auto issue_loads = [&](int64_t ra) {
+  // Copy i of a row block: lane L fills slot 64 i + L, which is position
+  // L % kChunks of concatenated group gp = (64 i + L) / kChunks and holds
+  // that group's chunk position ^ swz(gp).  Concatenated group gp is group
+  // gp % gs of the segment in row gp / gs of the block: the group of lane gp.
+  int64_t src_off[IO::kLoads];
+  int src_row[IO::kLoads];
+#pragma unroll
+  for (int i = 0; i < IO::kLoads; ++i) {
+    const int p = 64 * i + lane, gp = p / IO::kChunks, c = (p % IO::kChunks) ^ IO::swz(gp);
+    const int bpos = gp * IO::kGroupBytes + 16 * c;
+    const int row_l = bpos >> seg_log2, o = bpos & ((1 << seg_log2) - 1);
+    src_row[i] = o < seg_valid ? row_l : 64;      // 64: past every row block
+    src_off[i] = (int64_t)row_l * K * EB + o;
+  }
+  auto issue_copies = [&](int64_t ra, int slot) {
     const uint8_t* base = reinterpret_cast<const uint8_t*>(x) + (ra * K + seg * gs * 32) * EB;
+    const int64_t rows_left = r1 - ra;
 #pragma unroll
     for (int i = 0; i < IO::kLoads; ++i) {
-      const int bpos = 1024 * i + 16 * lane;
-      const int row_l = bpos >> seg_log2, o = bpos & ((1 << seg_log2) - 1);
-      if (ra + row_l < r1 && o < seg_valid) {
-        // x is read once: non-temporal loads (measured: the GEMM that follows
-        // starts sooner, e.g. the MoE layer step 67.7 -> 62 us)
-        typedef unsigned v4u __attribute__((ext_vector_type(4)));
-        const v4u v = __builtin_nontemporal_load(reinterpret_cast<const v4u*>(base + (int64_t)row_l * K * EB + o));
-        ld[i] = make_uint4(v.x, v.y, v.z, v.w);
-      } else {
-        ld[i] = make_uint4(0, 0, 0, 0);
-      }
+      // a chunk past the wave's rows or the row's last group belongs to a
+      // lane that stores nothing: copy the block's first chunk in its place
+      const uint8_t* src = src_row[i] < rows_left ? base + src_off[i] : base;
+      dma16_nt(src, ring_lds + (uint32_t)(slot * IO::kBlockLds + 1024 * i));
     }
   };
 
   // experts: of this lane's first row, and (SHARED) of the block's first and
   // last rows; looked up before any x load, which the lookups would otherwise
-  // wait for
+  // wait for.  e_end is the end of the lane's expert (rows sorted by expert):
+  // the expert walk in the loop loads an offset only when a row crosses it.
   int e = 0, e_a = 0, e_b = 0;
+  int64_t e_end = 0;
   if constexpr (!PLAIN) {
-    e = expert_of(r0 + lr < M ? r0 + lr : M - 1);
+    const int64_t rl = r0 + lr < M ? r0 + lr : M - 1;   // this lane's first row
+    if (rows_per_expert > 0) {
+      e = (int)(rl / rows_per_expert);
+    } else if (offsets != nullptr) {
+      // the wave's first row is wave-uniform: a binary search on scalar
+      // loads; a lane whose first row lies past that expert walks on
+      e = expert_of(r0 < M ? r0 : M - 1);
+      e_end = offsets[e + 1];
+      while (e + 1 < E && rl >= e_end) e_end = offsets[++e + 1];
+    }
     if constexpr (SHARED) {
       const int64_t rl = (rb + 4 * rows_per_wave < M ? rb + 4 * rows_per_wave : M) - 1;
       e_a = expert_of(rb < M ? rb : M - 1);
       e_b = expert_of(rl);
     }
   }
-  if (r0 < M) issue_loads(r0);
+  // per-wave layout: the lane's factors are loaded before the first copies
+  // and waited for together with them
+  int cur_e = -1;
+  float sc[32];
+  if constexpr (!PLAIN && !SHARED) {
+    if (g_ok && r0 + lr < r1) {
+      cur_e = e;
+      const float4* sp = reinterpret_cast<const float4*>(s + (int64_t)e * K + g * 32);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const float4 f = sp[i];
+        sc[4 * i] = f.x; sc[4 * i + 1] = f.y; sc[4 * i + 2] = f.z; sc[4 * i + 3] = f.w;
+      }
+    }
+  }
+  const int nblk = r0 < M ? (int)ceil_div(r1 - r0, (int64_t)rw) : 0;   // row blocks of this wave
+  for (int j = 0; j < kDepth && j < nblk; ++j) issue_copies(r0 + (int64_t)j * rw, j);
+  if constexpr (!PLAIN && !SHARED) {
+    wait_vmcnt<0>();
+#pragma unroll
+    for (int i = 0; i < 32; ++i) asm volatile("" : "+v"(sc[i]));   // no use of sc moves above the wait
+    if (RECIP && cur_e >= 0) {
+#pragma unroll
+      for (int i = 0; i < 32; ++i) sc[i] = 1.0f / sc[i];  // IEEE-correct fp32 division
+    }
+  }
   if constexpr (SHARED) {
     // stage the segment's factors of experts e_a and e_b (when it differs)
     // while x is in flight: thread t copies bytes 16 t + 4096 p of a slice
@@ -273,23 +352,25 @@ void act_quant_lane_kernel(
     if (r0 >= M) return;
   }
 
-  int cur_e = -1;
-  float sc[32];
-  for (int64_t ra = r0; ra < r1; ra += rw) {
-    // scatter the block's segments into the padded per-group layout
+  for (int j = 0; j < nblk; ++j) {
+    const int64_t ra = r0 + (int64_t)j * rw;
+    const int slot = j % kDepth;
+    wait_row_blocks<IO::kLoads>(kDepth - 1 < nblk - 1 - j ? kDepth - 1 : nblk - 1 - j);
+    uint4 q[EB * 2];
 #pragma unroll
-    for (int i = 0; i < IO::kLoads; ++i) {
-      const int off = 1024 * i + 16 * lane;
-      const int grp = off / IO::kGroupBytes, part = off % IO::kGroupBytes;
-      *reinterpret_cast<uint4*>(buf + grp * IO::kLdsGroup + part) = ld[i];
+    for (int c = 0; c < EB * 2; ++c)
+      q[c] = *reinterpret_cast<const uint4*>(lds + ring_off + slot * IO::kBlockLds + 16 * IO::slot(lane, c));
+    if (j + kDepth < nblk) {
+      wait_lgkmcnt0();   // the slot's reads have landed before it is refilled
+      issue_copies(ra + (int64_t)kDepth * rw, slot);
     }
-    if (ra + rw < r1) issue_loads(ra + rw);
     const int64_t r = ra + lr;                       // this lane's row
     const bool active = g_ok && r < r1;
     if constexpr (!PLAIN) {
       // expert of row r
       if (rows_per_expert > 0) e = (int)(r / rows_per_expert);
-      else if (offsets != nullptr) while (e + 1 < E && r >= (int64_t)offsets[e + 1]) ++e;
+      else if (offsets != nullptr)
+        while (e + 1 < E && r >= e_end) e_end = offsets[++e + 1];
     }
     if constexpr (!PLAIN && !SHARED) {
       // this lane's factors, reloaded when its row's expert changes
@@ -305,11 +386,12 @@ void act_quant_lane_kernel(
 #pragma unroll
           for (int i = 0; i < 32; ++i) sc[i] = 1.0f / sc[i];  // IEEE-correct fp32 division
         }
+        // wait here, on the rare reload: left to the compiler, the wait for
+        // these loads lands after the branch, where it would run on every row
+        // block and drain the ring's copies each time
+        wait_vmcnt<0>();
       }
     }
-    uint4 q[EB * 2];
-#pragma unroll
-    for (int i = 0; i < EB * 2; ++i) q[i] = *reinterpret_cast<const uint4*>(buf + lane * IO::kLdsGroup + 16 * i);
     float t[32];
     widen_group<EB>(q, t);
     uint4 cw;
@@ -373,21 +455,26 @@ struct ActLaunch {
   dim3 grid;
 };
 
-// Row blocks per wave: units / 3072 clamped to 2..6 (measured on MI355X for
-// 4K..30K units; longer waves also amortise the per-lane load of s).  Waves
-// of 2 row blocks share s per block (measured: attn-proj activation 9.7 ->
-// 8.5 us, decode M32 -5%); longer waves keep the per-wave layout, which
-// reads x with better locality (down-prefill 37.9 vs 39.3 us, MoE per-token
-// routing 19.8 vs 22.6 us).
+// Row blocks per wave: units / 3072 rounded up, so that the grid is about
+// one round of 3 blocks on each of the 256 CUs, clamped to 2..12, or 1 for
+// grids of at most 1024 units (measured on MI355X with the copy ring:
+// down-prefill 10 row blocks 32.0 us against 33.3 at 6 and 35.2 at 12; MoE
+// 4 row blocks 19.0 us against 21.3 at 2 and 8; decode M32 1 row block
+// 4.1 us against 5.2 at 2).  Waves of at most 2 row blocks share s per block
+// (measured: attn-proj activation 9.7 -> 8.5 us before the copy ring,
+// 7.2 us with it); longer waves keep the per-wave layout, which reads x
+// with better locality (down-prefill 37.9 vs 39.3 us, MoE per-token routing
+// 19.8 vs 22.6 us).
 static ActLaunch act_launch(int64_t M, int64_t K, bool plain) {
   ActLaunch a;
   a.gs_log2 = act_gs_log2(K / 32);
   const int64_t rw = 64 >> a.gs_log2;
   const int64_t nseg = ceil_div(K / 32, (int64_t)1 << a.gs_log2);
   const int64_t blocks = ceil_div(M, rw);
-  int64_t steps = nseg * blocks / 3072;
-  if (steps < 2) steps = 2;
-  if (steps > 6) steps = 6;
+  const int64_t units = nseg * blocks;
+  int64_t steps = ceil_div(units, (int64_t)3072);
+  if (steps < 2) steps = units <= 1024 ? 1 : 2;
+  if (steps > 12) steps = 12;
   if (steps > blocks) steps = blocks;
   if (const char* force = getenv("MACAQ_ACT_ROWS_PER_WAVE")) steps = atoi(force) > 0 ? atoi(force) : steps;  // tuning knob
   a.steps = (int)steps;
@@ -403,11 +490,11 @@ static void launch_act_t(const ActLaunch& a, const void* x, const float* s, cons
                          int64_t rows_per_expert, int64_t M, int64_t K, uint8_t* codes, uint8_t* scales,
                          hipStream_t stream) {
   if (a.shared)
-    act_quant_lane_kernel<EB, RECIP, false, true><<<a.grid, dim3(256), 2 * kSLds + 4 * GroupIo<EB>::kWaveLds,
+    act_quant_lane_kernel<EB, RECIP, false, true><<<a.grid, dim3(256), act_lds_bytes<EB, true>(),
                                                     stream>>>(x, s, offsets, E, rows_per_expert, M, K, codes, scales,
                                                               a.gs_log2, a.steps);
   else
-    act_quant_lane_kernel<EB, RECIP, false, false><<<a.grid, dim3(256), 4 * GroupIo<EB>::kWaveLds, stream>>>(
+    act_quant_lane_kernel<EB, RECIP, false, false><<<a.grid, dim3(256), act_lds_bytes<EB, false>(), stream>>>(
         x, s, offsets, E, rows_per_expert, M, K, codes, scales, a.gs_log2, a.steps);
 }
 
@@ -431,10 +518,10 @@ hipError_t launch_quant_plain(const void* x, bool x_f32, int64_t M, int64_t K, u
   if (M <= 0) return hipSuccess;
   const ActLaunch a = act_launch(M, K, true);
   if (x_f32)
-    act_quant_lane_kernel<4, false, true><<<a.grid, dim3(256), 4 * GroupIo<4>::kWaveLds, stream>>>(
+    act_quant_lane_kernel<4, false, true><<<a.grid, dim3(256), act_lds_bytes<4, false>(), stream>>>(
         x, nullptr, nullptr, 1, 0, M, K, codes, scales, a.gs_log2, a.steps);
   else
-    act_quant_lane_kernel<2, false, true><<<a.grid, dim3(256), 4 * GroupIo<2>::kWaveLds, stream>>>(
+    act_quant_lane_kernel<2, false, true><<<a.grid, dim3(256), act_lds_bytes<2, false>(), stream>>>(
         x, nullptr, nullptr, 1, 0, M, K, codes, scales, a.gs_log2, a.steps);
   return hipGetLastError();
 }
