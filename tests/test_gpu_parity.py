@@ -143,6 +143,32 @@ def test_quant_act_both_layouts(name, kw, shared, steps, monkeypatch):
     assert np.array_equal(codes.cpu().numpy(), rc)
 
 
+@pytest.mark.parametrize("steps", [None, 7])
+@pytest.mark.parametrize("shared", ["0", "1"])
+def test_quant_act_many_experts(shared, steps, monkeypatch):
+    """130 experts with runs of empty ones and ragged counts: the wave's
+    first expert comes from a binary search over the offsets, and lanes walk
+    on across expert ends inside a row block, a wave and a block; 7 row
+    blocks per wave refill each slot of the copy ring twice."""
+    say(f"quant_act E130 shared={shared} steps={steps}")
+    monkeypatch.setenv("MACAQ_ACT_SHARED_S", shared)
+    if steps is not None:
+        monkeypatch.setenv("MACAQ_ACT_ROWS_PER_WAVE", str(steps))
+    E, K = 130, 768
+    rng = np.random.default_rng(130)
+    counts = rng.integers(0, 9, E)
+    counts[rng.random(E) < 0.4] = 0
+    counts[[0, E - 1]] = [0, 5]
+    off = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    M = int(off[-1])
+    x = torch.from_numpy(rng.standard_normal((M, K)).astype(np.float32)).to(torch.bfloat16)
+    s = rng.uniform(0.25, 4.0, (E, K)).astype(np.float32)
+    codes, scales = mx.quant_act(x.to(DEV), torch.from_numpy(s).to(DEV), torch.from_numpy(off).to(DEV))
+    rc, rs = oracle.quant_act(host(x), s, off)
+    assert np.array_equal(scales.cpu().numpy(), rs)
+    assert np.array_equal(codes.cpu().numpy(), rc)
+
+
 @pytest.mark.parametrize("shared", ["0", "1"])
 def test_prepare_weights_both_layouts(shared, monkeypatch):
     """Weight preparation (reciprocal factors, experts of N rows each) with
