@@ -54,6 +54,11 @@
  * device-resident values (s > 0, sorted offsets, finite inputs) are
  * preconditions that are not checked.
  *
+ * Graph capture: outside the debug mode below, a call launches kernels
+ * only (no allocation, no memset, no synchronization), so it may be
+ * captured into a HIP graph and replayed.  Make one call of each kind
+ * before capturing: the first call sets a kernel attribute once.
+ *
  * Debug mode: with the environment variable MACAQ_CHECK=1 (read at every
  * call), each entry point first waits for `stream` and checks the
  * device-resident preconditions it can read back cheaply: expert offsets
