@@ -188,12 +188,6 @@ constexpr int kSLds = 64 * kSStride * 4;          // one staged slice of s, byte
 template <int EB, bool SHARED>
 constexpr int act_lds_bytes() { return (SHARED ? 2 * kSLds : 0) + 4 * act_depth<EB, SHARED>() * GroupIo<EB>::kBlockLds; }
 
-// Copy 16 bytes per lane from global memory to LDS at M0 + 16 * lane,
-// non-temporal (x is read once).
-__device__ __forceinline__ void dma16_nt(const uint8_t* g, uint32_t lds_addr) {
-  asm volatile("global_load_lds_dwordx4 %0, off nt" ::"v"(g), "{m0}"(lds_addr) : "memory");
-}
-
 // Wait until at most `later` row blocks' copies of this wave are in flight.
 template <int LOADS>
 __device__ __forceinline__ void wait_row_blocks(int later) {
@@ -299,9 +293,9 @@ void act_quant_lane_kernel(
       while (e + 1 < E && rl >= e_end) e_end = offsets[++e + 1];
     }
     if constexpr (SHARED) {
-      const int64_t rl = (rb + 4 * rows_per_wave < M ? rb + 4 * rows_per_wave : M) - 1;
+      const int64_t r_last = (rb + 4 * rows_per_wave < M ? rb + 4 * rows_per_wave : M) - 1;   // block's last row
       e_a = expert_of(rb < M ? rb : M - 1);
-      e_b = expert_of(rl);
+      e_b = expert_of(r_last);
     }
   }
   // per-wave layout: the lane's factors are loaded before the first copies

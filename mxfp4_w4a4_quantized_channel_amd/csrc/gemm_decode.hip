@@ -45,12 +45,9 @@
 
 namespace macaq {
 
-// W' is read exactly once per call: its copies carry the non-temporal hint so
-// that the streamed weights do not evict the activation and scale lines the
-// other blocks still read from L2.
-__device__ __forceinline__ void dma16_stream(const uint8_t* g, uint32_t lds_addr) {
-  asm volatile("global_load_lds_dwordx4 %0, off nt" ::"v"(g), "{m0}"(lds_addr) : "memory");
-}
+// W' is read exactly once per call: its copies carry the non-temporal hint
+// (dma16_nt) so that the streamed weights do not evict the activation and
+// scale lines the other blocks still read from L2.
 
 
 typedef int v8i_d __attribute__((ext_vector_type(8)));
@@ -261,7 +258,7 @@ __global__ __launch_bounds__(64 * WAVES) void decode_gemm_kernel(
     const uint32_t base = ring_addr + (uint32_t)(((c - c0) % STAGES) * S::kBytes);
     const int64_t co = (int64_t)c * 128, so = (int64_t)c * 8;
 #pragma unroll
-    for (int i = 0; i < 4 * RT; ++i) dma16_stream(wsrc[i] + co, base + S::kW + i * 1024);
+    for (int i = 0; i < 4 * RT; ++i) dma16_nt(wsrc[i] + co, base + S::kW + i * 1024);
 #pragma unroll
     for (int i = 0; i < RT; ++i) issue_slab((c - c0) / kSeg + 1, ((c - c0) % kSeg) * RT + i);
     if constexpr (AK == 1) {

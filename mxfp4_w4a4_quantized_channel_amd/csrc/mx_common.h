@@ -143,6 +143,12 @@ __device__ __forceinline__ void wait_lgkmcnt0() { __builtin_amdgcn_s_waitcnt(0xF
 __device__ __forceinline__ void dma16(const uint8_t* g, uint32_t lds_addr) {
   asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(g), "{m0}"(lds_addr) : "memory");
 }
+// Non-temporal form, for bytes read exactly once (the streamed weights of
+// the decode kernel, the activation rows): they do not evict lines that
+// other blocks still read from L2.
+__device__ __forceinline__ void dma16_nt(const uint8_t* g, uint32_t lds_addr) {
+  asm volatile("global_load_lds_dwordx4 %0, off nt" ::"v"(g), "{m0}"(lds_addr) : "memory");
+}
 __device__ __forceinline__ void dma4(const uint8_t* g, uint32_t lds_addr) {
   asm volatile("global_load_lds_dword %0, off" ::"v"(g), "{m0}"(lds_addr) : "memory");
 }
