@@ -491,8 +491,12 @@ static size_t decode_lds_bytes(const DecodeConfig& d, int64_t M, int64_t K) {
 // Otherwise 32 rows and 4 or 8 waves (for small activations the extra waves
 // keep more of W' in flight, which matters more).  Each wave keeps STAGES - 1 chunks in flight; the ring is made as
 // deep as LDS allows (2 to 4 slots), within half of the CU's LDS when the
-// grid has more blocks than CUs, within all of it otherwise; 8 waves drop to
-// 4 where even 2 slots do not fit.
+// grid has more blocks than CUs, within all of it otherwise.  8 waves drop
+// to 4 where 2 slots do not fit, and, with more than 8 staged activation
+// rows, where they would get only 2 slots: 4 waves with 4 slots keep 12
+// chunks in flight per block instead of 8 (measured on down-proj M32
+// N5120 K25600: 25.7 us against 29.7; the fused M1 down-proj keeps 8 waves
+// of 2 slots, 18.3 us against 21.9 with 4 of 4).
 static DecodeConfig decode_config(int64_t M, int64_t N, int64_t K, bool fused, int eb) {
   DecodeConfig d;
   d.ak = decode_ak(M, fused);
@@ -504,7 +508,7 @@ static DecodeConfig decode_config(int64_t M, int64_t N, int64_t K, bool fused, i
   const size_t budget = ceil_div(N, kDecRows * d.rt) > 256 ? kDecLdsMax / 2 : kDecLdsMax;
   d.stages = max_stages;
   while (d.stages > 2 && decode_lds_bytes(d, M, K) > budget) --d.stages;
-  if (decode_lds_bytes(d, M, K) > kDecLdsMax && d.waves > 4) {
+  if (d.waves > 4 && ((d.ak > 8 && d.stages < 3) || decode_lds_bytes(d, M, K) > kDecLdsMax)) {
     d.waves = 4;
     d.stages = max_stages;
     while (d.stages > 2 && decode_lds_bytes(d, M, K) > budget) --d.stages;

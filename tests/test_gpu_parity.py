@@ -382,8 +382,28 @@ DECODE_SHAPES = [
     ("M32 2 chunks", (32, 20000, 512)),
     ("M8 odd chunks", (8, 96, 256 * 7)),
     ("M5 16 waves", (5, 70, 256 * 65)),
-    ("M32 8 waves", (32, 64, 256 * 25)),
+    ("M32 25 chunks, 4 waves of 4 slots", (32, 64, 256 * 25)),
 ]
+
+
+@pytest.mark.parametrize("waves,stages", [(8, 2), (4, 2), (4, 3)])
+def test_gemm_decode_forced_rings(waves, stages, monkeypatch):
+    """Decode rings forced on one M = 32 shape: 8 waves of 2 slots (no longer
+    the default choice at M = 32) and 4 waves of 2 or 3 slots; each within
+    the oracle's bound (the K split over the waves differs between them, so
+    their fp32 sums are not compared bit for bit)."""
+    say(f"gemm decode forced waves={waves} stages={stages}")
+    monkeypatch.setenv("MACAQ_DECODE_WAVES", str(waves))
+    monkeypatch.setenv("MACAQ_DECODE_STAGES", str(stages))
+    M, N, K = 32, 96, 256 * 26
+    rng = np.random.default_rng(2600 + waves)
+    ac = rng.integers(0, 256, (M, K // 2), dtype=np.uint8)
+    asc = rng.integers(110, 140, (M, K // 32), dtype=np.uint8)
+    wc = rng.integers(0, 256, (N, K // 2), dtype=np.uint8)
+    wsc = rng.integers(110, 140, (N, K // 32), dtype=np.uint8)
+    y = mx.gemm(*[torch.from_numpy(a).to(DEV) for a in (ac, asc, wc, wsc)])
+    y_ref, S = oracle.gemm(ac, asc, wc, wsc)
+    _check_y(y.cpu().numpy(), y_ref, S)
 
 
 @pytest.mark.parametrize("name,shape", DECODE_SHAPES, ids=[n for n, _ in DECODE_SHAPES])
