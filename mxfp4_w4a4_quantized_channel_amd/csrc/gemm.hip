@@ -21,9 +21,11 @@ hipError_t launch_pipe_out(const uint8_t* A, const uint8_t* As, const int32_t* o
   int64_t tiles_m = ceil_div(M, BM);
   if (offsets != nullptr) tiles_m += E;  // each expert may add one partial row tile
   const int64_t blocks = tiles_m * tiles_n;
+  int group_m = 4;   // tile rows per XCD group (blocks of a group share A and W' panels in one L2)
+  if (const char* e = getenv("MACAQ_GEMM_GROUP_M")) group_m = atoi(e) > 0 ? atoi(e) : group_m;   // tuning knob
   gemm_mxfp4_pipe_kernel<BM, BN, WM, WN, BK, S, MINB, OUT, BT>
       <<<dim3((unsigned)blocks), dim3(64 * WM * WN), lds, stream>>>(A, As, B, Bs, offsets, E, M, N, K, Y,
-                                                                    (int)tiles_m, tiles_n, 4);
+                                                                    (int)tiles_m, tiles_n, group_m);
   return hipGetLastError();
 }
 

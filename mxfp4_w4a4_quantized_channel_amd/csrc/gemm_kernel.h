@@ -493,12 +493,6 @@ __device__ __forceinline__ void tile_of_block(int bid, int ntiles, int tiles_m, 
   *tn = in / gm;
 }
 
-// BT: W' in the tiled layout (see macaq_tile_weights): per expert, blocks of
-// 32 rows x one 256-wide K-tile, 4 KiB of codes (each row's 16-byte chunks
-// stored in the XOR-swizzled order the LDS tile uses) and 256 bytes of
-// scales.  A copy instruction then reads 1 KiB of contiguous codes (and a
-// scale copy 256 contiguous bytes) instead of 8 (32) rows' pieces: measured
-// 56 against 33 B/clk per CU for such copies in isolation.
 // Inclusive prefix sum of v over the wave's 64 lanes.
 __device__ __forceinline__ int wave_prefix_sum(int v, int lane) {
 #pragma unroll
@@ -550,6 +544,12 @@ __device__ __forceinline__ bool grouped_tile(const int32_t* __restrict__ offsets
   return false;
 }
 
+// BT: W' in the tiled layout (see macaq_tile_weights): per expert, blocks of
+// 32 rows x one 256-wide K-tile, 4 KiB of codes (each row's 16-byte chunks
+// stored in the XOR-swizzled order the LDS tile uses) and 256 bytes of
+// scales.  A copy instruction then reads 1 KiB of contiguous codes (and a
+// scale copy 256 contiguous bytes) instead of 8 (32) rows' pieces: measured
+// 56 against 33 B/clk per CU for such copies in isolation.
 template <int BM, int BN, int WAVES_M, int WAVES_N, int BK, int STAGES, int MINB = 1, int OUT = 0, bool BT = false>
 __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, MINB) void gemm_mxfp4_pipe_kernel(
     const uint8_t* __restrict__ A, const uint8_t* __restrict__ As, const uint8_t* __restrict__ B,
