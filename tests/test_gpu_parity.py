@@ -170,6 +170,23 @@ def test_quant_act_many_experts(shared, steps, monkeypatch):
 
 
 @pytest.mark.parametrize("shared", ["0", "1"])
+@pytest.mark.parametrize("M,K", [(7, 32), (13, 96), (5, 160), (9, 2080)])
+def test_quant_act_narrow_rows(M, K, shared, monkeypatch):
+    """Rows of 1, 3, 5 and 65 groups: most lanes of a segment are past the
+    row's last group, and their copies of the ring are stand-ins that no
+    lane stores; M is not a multiple of the rows per block step."""
+    say(f"quant_act narrow M{M} K{K} shared={shared}")
+    monkeypatch.setenv("MACAQ_ACT_SHARED_S", shared)
+    rng = np.random.default_rng(M * K)
+    x = torch.from_numpy(rng.standard_normal((M, K)).astype(np.float32)).to(torch.bfloat16)
+    s = rng.uniform(0.25, 4.0, (1, K)).astype(np.float32)
+    codes, scales = mx.quant_act(x.to(DEV), torch.from_numpy(s).to(DEV))
+    rc, rs = oracle.quant_act(host(x), s, None)
+    assert np.array_equal(scales.cpu().numpy(), rs)
+    assert np.array_equal(codes.cpu().numpy(), rc)
+
+
+@pytest.mark.parametrize("shared", ["0", "1"])
 def test_prepare_weights_both_layouts(shared, monkeypatch):
     """Weight preparation (reciprocal factors, experts of N rows each) with
     either wave layout forced."""
