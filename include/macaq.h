@@ -111,8 +111,44 @@ enum {
  * argument of macaq_gemm_ex. */
 #define MACAQ_W_TILED 0x100u
 
+/* Knobs of macaq_set_tuning.  Value 0 of every knob is the library's own
+ * choice; other values force one kernel variant:
+ *   MACAQ_TUNE_GEMM_TILE          prefill / grouped GEMM block tile:
+ *                                 1 = 256x256, 2 = 256x128, 3 = 128x128
+ *   MACAQ_TUNE_GEMM_GROUP_M       tile rows per XCD group of the GEMM (1..64)
+ *   MACAQ_TUNE_ACT_ROWS_PER_WAVE  row blocks per wave of the activation
+ *                                 kernel (1..64)
+ *   MACAQ_TUNE_ACT_SHARED_S       activation kernel's per-channel factors:
+ *                                 1 = per lane in registers, 2 = staged per
+ *                                 block in LDS
+ *   MACAQ_TUNE_DECODE_WAVES       waves per decode block (4 or 8; 32-row blocks)
+ *   MACAQ_TUNE_DECODE_STAGES      ring slots per decode wave (2..4; 32-row blocks)
+ *   MACAQ_TUNE_DECODE_ROWS        weight rows per decode block (32 or 64) */
+enum {
+  MACAQ_TUNE_GEMM_TILE = 0,
+  MACAQ_TUNE_GEMM_GROUP_M = 1,
+  MACAQ_TUNE_ACT_ROWS_PER_WAVE = 2,
+  MACAQ_TUNE_ACT_SHARED_S = 3,
+  MACAQ_TUNE_DECODE_WAVES = 4,
+  MACAQ_TUNE_DECODE_STAGES = 5,
+  MACAQ_TUNE_DECODE_ROWS = 6,
+  MACAQ_TUNE_COUNT = 7
+};
+
 /* Library version as major*10000 + minor*100 + patch. */
 int macaq_version(void);
+
+/*
+ * Process-wide override of one kernel choice, for tests and tuning sweeps
+ * (the library reads no environment variable for these).  Every later call
+ * on every thread uses it until it is set back to 0.  Codes and scale bytes
+ * do not depend on any knob; the GEMM's fp32 summation order, and so the
+ * last bits of y, can (tile shape, decode waves).  A forced choice that
+ * cannot serve a shape is replaced by the automatic one.
+ * Returns the previous value of the knob, or MACAQ_ERR_INVALID_ARG for an
+ * unknown knob or a value outside the range listed above.
+ */
+int macaq_set_tuning(int knob, int value);
 
 /* Static description of a status code (never NULL). */
 const char* macaq_status_string(int status);

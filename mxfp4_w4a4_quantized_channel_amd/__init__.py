@@ -23,6 +23,8 @@ __all__ = [
     "prepare_weights", "quant_act", "gemm", "linear", "linear_workspace_bytes",
     "encode_e2m1", "quant_mxfp4", "version", "library_path", "EPI_NONE", "EPI_SWIGLU",
     "hessian", "prepare_weights_hessian", "flip_refine", "flip_refine_workspace_bytes",
+    "set_tuning", "TUNE_GEMM_TILE", "TUNE_GEMM_GROUP_M", "TUNE_ACT_ROWS_PER_WAVE", "TUNE_ACT_SHARED_S",
+    "TUNE_DECODE_WAVES", "TUNE_DECODE_STAGES", "TUNE_DECODE_ROWS", "GEMM_TILES",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -32,6 +34,10 @@ BF16, F32 = 0, 1
 PATH_AUTO, PATH_FUSED, PATH_UNFUSED = 0, 1, 2
 EPI_NONE, EPI_SWIGLU = 0, 1
 W_TILED = 0x100   # weights in macaq_tile_weights' layout (OR into linear's flags / gemm's epilogue)
+# knobs of macaq_set_tuning (0 = the library's own choice)
+(TUNE_GEMM_TILE, TUNE_GEMM_GROUP_M, TUNE_ACT_ROWS_PER_WAVE, TUNE_ACT_SHARED_S, TUNE_DECODE_WAVES,
+ TUNE_DECODE_STAGES, TUNE_DECODE_ROWS) = range(7)
+GEMM_TILES = {"256x256": 1, "256x128": 2, "128x128": 3}   # values of TUNE_GEMM_TILE
 STATUS = {0: "ok", -1: "invalid argument", -2: "unsupported", -3: "no device", -4: "HIP error",
           -5: "workspace too small"}
 
@@ -58,6 +64,7 @@ def _load():
     ci = ctypes.c_int
     sig = {
         "macaq_version": (ci, []),
+        "macaq_set_tuning": (ci, [ci, ci]),
         "macaq_status_string": (ctypes.c_char_p, [ci]),
         "macaq_last_error": (ctypes.c_char_p, []),
         "macaq_prepare_weights": (ci, [vp, ci, vp, i64, i64, i64, vp, vp, vp]),
@@ -94,6 +101,15 @@ def lib():
 
 def version() -> int:
     return _load().macaq_version()
+
+
+def set_tuning(knob: int, value: int) -> int:
+    """Force one kernel choice process-wide (0 restores the automatic one);
+    returns the knob's previous value."""
+    prev = _load().macaq_set_tuning(int(knob), int(value))
+    if prev < 0:
+        _check(prev, "macaq_set_tuning")
+    return prev
 
 
 def _check(status: int, where: str):

@@ -12,8 +12,6 @@
 // segment of 64, 32 or 16 groups in each of 1, 2 or 4 consecutive rows (see
 // act_quant_lane_kernel below).  The kernel is HBM-bound: per element it
 // reads 2 bytes (bf16) and writes 17/32 bytes.
-#include <cstdlib>
-
 #include "mx_common.h"
 
 namespace macaq {
@@ -194,7 +192,6 @@ __device__ __forceinline__ void wait_row_blocks(int later) {
   if (later >= 2) wait_vmcnt<2 * LOADS>();
   else if (later == 1) wait_vmcnt<LOADS>();
   else wait_vmcnt<0>();
-  asm volatile("" ::: "memory");   // no LDS read moves above the wait
 }
 
 template <int EB, bool RECIP, bool PLAIN = false, bool SHARED = false>
@@ -470,10 +467,10 @@ static ActLaunch act_launch(int64_t M, int64_t K, bool plain) {
   if (steps < 2) steps = units <= 1024 ? 1 : 2;
   if (steps > 12) steps = 12;
   if (steps > blocks) steps = blocks;
-  if (const char* force = getenv("MACAQ_ACT_ROWS_PER_WAVE")) steps = atoi(force) > 0 ? atoi(force) : steps;  // tuning knob
+  if (const int force = tuning(MACAQ_TUNE_ACT_ROWS_PER_WAVE)) steps = force;
   a.steps = (int)steps;
   a.shared = !plain && steps <= 2;
-  if (const char* force = getenv("MACAQ_ACT_SHARED_S")) a.shared = !plain && atoi(force) != 0;   // tuning knob
+  if (const int force = tuning(MACAQ_TUNE_ACT_SHARED_S)) a.shared = !plain && force == 2;
   const int64_t chunks = ceil_div(blocks, steps);   // row ranges of one wave
   a.grid = a.shared ? dim3((unsigned)(nseg * ceil_div(chunks, 4))) : dim3((unsigned)ceil_div(nseg * chunks, 4));
   return a;

@@ -49,6 +49,12 @@ hipError_t launch_tile_weights(const uint8_t* wc, const uint8_t* ws, int64_t E, 
 // output mode bits of the GEMM kernels (mx_common.h)
 constexpr int kOutBf16 = 1;
 constexpr int kOutSwiGLU = 2;
+
+// Tuning overrides of the launchers (macaq_set_tuning); 0 = automatic.
+namespace {
+std::atomic<int> g_tuning[MACAQ_TUNE_COUNT];
+}
+int tuning(int knob) { return g_tuning[knob].load(std::memory_order_relaxed); }
 }  // namespace macaq
 
 namespace {
@@ -191,6 +197,16 @@ int check_tiled(int64_t N, int64_t K, const char* fn) {
 extern "C" {
 
 int macaq_version(void) { return kVersion; }
+
+int macaq_set_tuning(int knob, int value) {
+  static const int kMax[MACAQ_TUNE_COUNT] = {3, 64, 64, 2, 8, 4, 64};
+  if (knob < 0 || knob >= MACAQ_TUNE_COUNT)
+    return fail(MACAQ_ERR_INVALID_ARG, "macaq_set_tuning: unknown knob " + std::to_string(knob));
+  if (value < 0 || value > kMax[knob])
+    return fail(MACAQ_ERR_INVALID_ARG, "macaq_set_tuning: value " + std::to_string(value) + " out of range for knob " +
+                                           std::to_string(knob));
+  return macaq::g_tuning[knob].exchange(value, std::memory_order_relaxed);
+}
 
 const char* macaq_status_string(int status) {
   switch (status) {
@@ -369,11 +385,14 @@ int macaq_gemm(const uint8_t* a_codes, const uint8_t* a_scales, const int32_t* e
                        MACAQ_EPI_NONE, workspace, workspace_bytes, stream);
 }
 
-int macaq_linear_ex(const void* x, macaq_dtype x_dtype, const float* s, const int32_t* expert_offsets, int64_t E,
-                    const uint8_t* w_codes, const uint8_t* w_scales, int64_t M, int64_t N, int64_t K, void* y,
-                    macaq_dtype y_dtype, uint32_t epilogue, void* workspace, size_t workspace_bytes, uint32_t flags,
-                    void* stream) {
-  const char* fn = "macaq_linear";
+}  // extern "C"
+
+namespace {
+
+int linear_impl(const void* x, macaq_dtype x_dtype, const float* s, const int32_t* expert_offsets, int64_t E,
+                const uint8_t* w_codes, const uint8_t* w_scales, int64_t M, int64_t N, int64_t K, void* y,
+                macaq_dtype y_dtype, uint32_t epilogue, void* workspace, size_t workspace_bytes, uint32_t flags,
+                void* stream, const char* fn) {
   if (int st = check_dtype(x_dtype, fn)) return st;
   const bool w_tiled = (flags & MACAQ_W_TILED) != 0;
   if ((flags & ~MACAQ_W_TILED) > MACAQ_PATH_UNFUSED)
@@ -419,6 +438,18 @@ int macaq_linear_ex(const void* x, macaq_dtype x_dtype, const float* s, const in
   return finish(fn, st,
                 run_gemm(a_codes, a_scales, off, E, w_codes, w_scales, M, N, K, y, mode, gemm_ws, st,
                          "macaq_linear (gemm)", w_tiled));
+}
+
+}  // namespace
+
+extern "C" {
+
+int macaq_linear_ex(const void* x, macaq_dtype x_dtype, const float* s, const int32_t* expert_offsets, int64_t E,
+                    const uint8_t* w_codes, const uint8_t* w_scales, int64_t M, int64_t N, int64_t K, void* y,
+                    macaq_dtype y_dtype, uint32_t epilogue, void* workspace, size_t workspace_bytes, uint32_t flags,
+                    void* stream) {
+  return linear_impl(x, x_dtype, s, expert_offsets, E, w_codes, w_scales, M, N, K, y, y_dtype, epilogue, workspace,
+                     workspace_bytes, flags, stream, "macaq_linear");
 }
 
 int macaq_linear(const void* x, macaq_dtype x_dtype, const float* s, const int32_t* expert_offsets, int64_t E,

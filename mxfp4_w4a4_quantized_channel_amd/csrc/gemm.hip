@@ -1,7 +1,4 @@
 // Launcher of the MXFP4 GEMM (kernel template in gemm_kernel.h).
-#include <cstdlib>
-#include <cstring>
-
 #include "gemm_kernel.h"
 
 namespace macaq {
@@ -21,8 +18,8 @@ hipError_t launch_pipe_out(const uint8_t* A, const uint8_t* As, const int32_t* o
   int64_t tiles_m = ceil_div(M, BM);
   if (offsets != nullptr) tiles_m += E;  // each expert may add one partial row tile
   const int64_t blocks = tiles_m * tiles_n;
-  int group_m = 4;   // tile rows per XCD group (blocks of a group share A and W' panels in one L2)
-  if (const char* e = getenv("MACAQ_GEMM_GROUP_M")) group_m = atoi(e) > 0 ? atoi(e) : group_m;   // tuning knob
+  // tile rows per XCD group (blocks of a group share A and W' panels in one L2)
+  const int group_m = tuning(MACAQ_TUNE_GEMM_GROUP_M) > 0 ? tuning(MACAQ_TUNE_GEMM_GROUP_M) : 4;
   gemm_mxfp4_pipe_kernel<BM, BN, WM, WN, BK, S, MINB, OUT, BT>
       <<<dim3((unsigned)blocks), dim3(64 * WM * WN), lds, stream>>>(A, As, B, Bs, offsets, E, M, N, K, Y,
                                                                     (int)tiles_m, tiles_n, group_m);
@@ -73,19 +70,6 @@ __global__ void tile_weights_kernel(const uint8_t* __restrict__ wc, const uint8_
   }
 }
 
-template <int OUT>
-hipError_t launch_v1(const uint8_t* A, const uint8_t* As, const int32_t* offsets, int E, const uint8_t* B,
-                     const uint8_t* Bs, int64_t M, int64_t N, int64_t K, void* Y, hipStream_t stream) {
-  constexpr int BM = 128, BN = 128;
-  const int n_tiles_n = (int)ceil_div(N, BN);
-  int64_t m_slots = ceil_div(M, BM);
-  if (offsets != nullptr) m_slots += E;  // each expert may add one partial tile
-  const int64_t blocks = m_slots * n_tiles_n;
-  gemm_mxfp4_kernel<BM, BN, 2, 2, OUT><<<dim3((unsigned)blocks), dim3(256), 0, stream>>>(A, As, B, Bs, offsets, E, M,
-                                                                                        N, K, Y, n_tiles_n);
-  return hipGetLastError();
-}
-
 }  // namespace
 
 hipError_t launch_tile_weights(const uint8_t* wc, const uint8_t* ws, int64_t E, int64_t N, int64_t K, uint8_t* tc,
@@ -107,11 +91,7 @@ hipError_t launch_gemm_tiled(const uint8_t* A, const uint8_t* As, const int32_t*
   if (M <= 0) return hipSuccess;
   const int64_t t256 = ceil_div(M, 256) * ceil_div(N, 256);
   int choice = (offsets == nullptr && t256 >= 240) ? 0 : 2;
-  if (const char* force = getenv("MACAQ_GEMM_TILE")) {
-    if (strcmp(force, "256x256") == 0) choice = 0;
-    else if (strcmp(force, "256x128") == 0) choice = 1;
-    else if (strcmp(force, "128x128") == 0) choice = 2;
-  }
+  if (const int force = tuning(MACAQ_TUNE_GEMM_TILE)) choice = force - 1;
   switch (choice) {
     case 0: return launch_pipe<256, 256, 2, 2, 256, 2, 1, true>(A, As, offsets, E, B, Bs, M, N, K, Y, mode, stream);
     case 1: return launch_pipe<256, 128, 2, 2, 256, 2, 1, true>(A, As, offsets, E, B, Bs, M, N, K, Y, mode, stream);
@@ -127,21 +107,15 @@ hipError_t launch_gemm(const uint8_t* A, const uint8_t* As, const int32_t* offse
   // tile per CU (largest tiles, least LDS and L2 traffic per FLOP); else
   // 256x128; grouped layers and small shapes use 128x128 with two blocks per
   // CU, whose finer granularity keeps ragged experts from leaving CUs idle.
-  // MACAQ_GEMM_TILE=256x256 | 256x128 | 128x128 | 128x128v1 forces one (the
-  // tests use it to cover every kernel on small shapes).
+  // macaq_set_tuning(MACAQ_TUNE_GEMM_TILE) forces one.
   const int64_t t256 = ceil_div(M, 256) * ceil_div(N, 256);
   const int64_t t128 = ceil_div(M, 256) * ceil_div(N, 128);
-  int choice;  // 0: 256x256, 1: 256x128, 2: 128x128 pipelined, 3: 128x128 register-staged
+  int choice;  // 0: 256x256, 1: 256x128, 2: 128x128
   if (offsets != nullptr) choice = 2;
   else if (t256 >= 240) choice = 0;
   else if (t128 >= 200) choice = 1;
   else choice = 2;
-  if (const char* force = getenv("MACAQ_GEMM_TILE")) {
-    if (strcmp(force, "256x256") == 0) choice = 0;
-    else if (strcmp(force, "256x128") == 0) choice = 1;
-    else if (strcmp(force, "128x128") == 0) choice = 2;
-    else if (strcmp(force, "128x128v1") == 0) choice = 3;
-  }
+  if (const int force = tuning(MACAQ_TUNE_GEMM_TILE)) choice = force - 1;
   const bool k256 = K % 256 == 0;
   switch (choice) {
     case 0:
@@ -150,16 +124,9 @@ hipError_t launch_gemm(const uint8_t* A, const uint8_t* As, const int32_t* offse
     case 1:
       return k256 ? launch_pipe<256, 128, 2, 2, 256, 2>(A, As, offsets, E, B, Bs, M, N, K, Y, mode, stream)
                   : launch_pipe<256, 128, 2, 2, 128, 4>(A, As, offsets, E, B, Bs, M, N, K, Y, mode, stream);
-    case 2:
+    default:
       return k256 ? launch_pipe<128, 128, 2, 2, 256, 2, 2>(A, As, offsets, E, B, Bs, M, N, K, Y, mode, stream)
                   : launch_pipe<128, 128, 2, 2, 128, 4, 2>(A, As, offsets, E, B, Bs, M, N, K, Y, mode, stream);
-    default: break;
-  }
-  switch (mode) {
-    case 0: return launch_v1<0>(A, As, offsets, E, B, Bs, M, N, K, Y, stream);
-    case kOutBf16: return launch_v1<kOutBf16>(A, As, offsets, E, B, Bs, M, N, K, Y, stream);
-    case kOutSwiGLU: return launch_v1<kOutSwiGLU>(A, As, offsets, E, B, Bs, M, N, K, Y, stream);
-    default: return launch_v1<kOutBf16 | kOutSwiGLU>(A, As, offsets, E, B, Bs, M, N, K, Y, stream);
   }
 }
 

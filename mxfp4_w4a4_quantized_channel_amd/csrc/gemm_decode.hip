@@ -39,8 +39,6 @@
 // first weight chunk is in flight; the B fragments then come from LDS.
 // Every block repeats that transform, so the fused variant pays off only for
 // very small M.
-#include <cstdlib>
-
 #include "mx_common.h"
 
 namespace macaq {
@@ -502,7 +500,7 @@ static DecodeConfig decode_config(int64_t M, int64_t N, int64_t K, bool fused, i
   d.ak = decode_ak(M, fused);
   d.eb = eb;
   d.rt = (d.ak > 8 && ceil_div(N, kDecRows) > 512) ? 2 : 1;
-  if (const char* e = getenv("MACAQ_DECODE_ROWS")) d.rt = atoi(e) == 64 ? 2 : 1;   // tuning knob
+  if (const int force = tuning(MACAQ_TUNE_DECODE_ROWS)) d.rt = force == 64 ? 2 : 1;
   const int max_stages = d.rt == 2 ? 3 : 4;
   d.waves = d.rt == 2 ? 2 : (K / 256 >= 24 ? 8 : 4);
   const size_t budget = ceil_div(N, kDecRows * d.rt) > 256 ? kDecLdsMax / 2 : kDecLdsMax;
@@ -513,9 +511,11 @@ static DecodeConfig decode_config(int64_t M, int64_t N, int64_t K, bool fused, i
     d.stages = max_stages;
     while (d.stages > 2 && decode_lds_bytes(d, M, K) > budget) --d.stages;
   }
-  if (d.rt == 1) {   // tuning knobs
-    if (const char* e = getenv("MACAQ_DECODE_WAVES")) d.waves = atoi(e) == 8 ? 8 : 4;
-    if (const char* e = getenv("MACAQ_DECODE_STAGES")) d.stages = atoi(e) >= 4 ? 4 : (atoi(e) == 3 ? 3 : 2);
+  if (d.rt == 1) {   // forced ring shapes, kept only where they fit in LDS
+    DecodeConfig f = d;
+    if (const int force = tuning(MACAQ_TUNE_DECODE_WAVES)) f.waves = force == 8 ? 8 : 4;
+    if (const int force = tuning(MACAQ_TUNE_DECODE_STAGES)) f.stages = force >= 4 ? 4 : (force == 3 ? 3 : 2);
+    if (decode_lds_bytes(f, M, K) <= kDecLdsMax) d = f;
   }
   return d;
 }

@@ -21,11 +21,8 @@
 //
 // Tiling: a block computes a BM x BN tile of y with WAVES_M x WAVES_N waves;
 // each wave owns a (BM/WAVES_M) x (BN/WAVES_N) sub-tile of 32x32 MFMA
-// blocks with fp32 accumulators in registers.  K-tiles of 256 are staged in
-// LDS, double-buffered: the global loads of tile k+1 are in flight while
-// tile k feeds the MFMAs.  In LDS each 128-byte tile row holds 8 chunks of
-// 16 bytes, chunk c of row r stored at position c ^ (r & 7), so the
-// fragment reads of 8 consecutive rows hit 8 different bank groups.
+// blocks with fp32 accumulators in registers.  K-tiles are staged in an LDS
+// ring filled by direct-to-LDS copies (see gemm_mxfp4_pipe_kernel below).
 //
 // Grouped (mixture-of-experts) operation: rows are sorted by expert and the
 // block index enumerates (expert, row-tile) pairs on the device from the
@@ -82,78 +79,36 @@ __device__ __forceinline__ void mfma_substep(v16f (&acc)[FM][FN], const uint4 (&
           as_operand(fa[mi]), as_operand(fb[ni]), acc[mi][ni], 4, 4, J, (int)sa[mi], J, (int)sb[ni]);
 }
 
-// Epilogue of a wave's FM x FN block of 32x32 accumulators whose first row
-// is m0 and first column n0 (rows below row_end and columns below N are
+// fp32 epilogue of a wave's FM x FN block of 32x32 accumulators whose first
+// row is m0 and first column n0 (rows below row_end and columns below N are
 // stored): lane (r32, h) holds column r32 and rows 8*(r/4) + 4*h + (r%4) of
-// accumulator register r.  OUT: output bits (fp32/bf16, SwiGLU), a template
-// parameter so that the fp32 kernel carries none of the other modes' code.
-//
-// bf16 and SwiGLU work on column pairs (2j, 2j+1), which sit in lanes
-// (2i, 2i+1).  The two lanes swap one register with a DPP move: the even lane
-// then holds both columns of rows 0..7 of the register file, the odd lane
-// both columns of rows 8..15, and each lane stores one result per row: a
-// packed pair of bf16 values, or silu(gate) * up for output column j of the
-// [M][N/2] SwiGLU output.
-template <int OUT, int FM, int FN>
-__device__ __forceinline__ void store_wave_tile(const v16f (&acc)[FM][FN], void* __restrict__ Y,
-                                                int64_t m0, int64_t row_end, int64_t n0, int64_t N, int r32, int h) {
+// accumulator register r.
+template <int FM, int FN>
+__device__ __forceinline__ void store_wave_tile_f32(const v16f (&acc)[FM][FN], void* __restrict__ Y, int64_t m0,
+                                                    int64_t row_end, int64_t n0, int64_t N, int r32, int h) {
   const bool interior = (m0 + FM * 32 <= row_end) && (n0 + FN * 32 <= N);
-  if constexpr (OUT == 0) {
-    if (interior) {
-#pragma unroll
-      for (int mi = 0; mi < FM; ++mi)
-#pragma unroll
-        for (int ni = 0; ni < FN; ++ni) {
-          float* yp = reinterpret_cast<float*>(Y) + (m0 + mi * 32 + 4 * h) * N + n0 + ni * 32 + r32;
-#pragma unroll
-          for (int r = 0; r < 16; ++r) __builtin_nontemporal_store(acc[mi][ni][r], &yp[(8 * (r >> 2) + (r & 3)) * N]);
-        }
-      return;
-    }
+  if (interior) {
 #pragma unroll
     for (int mi = 0; mi < FM; ++mi)
 #pragma unroll
       for (int ni = 0; ni < FN; ++ni) {
-        const int64_t n = n0 + ni * 32 + r32;
+        float* yp = reinterpret_cast<float*>(Y) + (m0 + mi * 32 + 4 * h) * N + n0 + ni * 32 + r32;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int64_t m = m0 + mi * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
-          if (m < row_end && n < N) __builtin_nontemporal_store(acc[mi][ni][r], reinterpret_cast<float*>(Y) + m * N + n);
-        }
+        for (int r = 0; r < 16; ++r) __builtin_nontemporal_store(acc[mi][ni][r], &yp[(8 * (r >> 2) + (r & 3)) * N]);
       }
-  } else {
-    const bool odd = (r32 & 1) != 0;
+    return;
+  }
 #pragma unroll
-    for (int mi = 0; mi < FM; ++mi) {
+  for (int mi = 0; mi < FM; ++mi)
 #pragma unroll
-      for (int ni = 0; ni < FN; ++ni) {
-        const int64_t np = n0 + ni * 32 + (r32 & ~1);   // even column of this lane's pair
+    for (int ni = 0; ni < FN; ++ni) {
+      const int64_t n = n0 + ni * 32 + r32;
 #pragma unroll
-        for (int r = 0; r < 8; ++r) {
-          // even lane: row register r; odd lane: row register r + 8
-          const float give = odd ? acc[mi][ni][r] : acc[mi][ni][r + 8];
-          const float got = quad_xor1(give);
-          const float own = odd ? acc[mi][ni][r + 8] : acc[mi][ni][r];
-          const float lo = odd ? got : own;   // column np
-          const float hi = odd ? own : got;   // column np + 1
-          const int rr = odd ? r + 8 : r;
-          const int64_t m = m0 + mi * 32 + 8 * (rr >> 2) + 4 * h + (rr & 3);
-          if (m >= row_end || np >= N) continue;
-          if constexpr ((OUT & kOutSwiGLU) != 0) {
-            store_out(Y, m * (N >> 1) + (np >> 1), silu_times(lo, hi), OUT);
-          } else {   // bf16 pair
-            uint16_t* y16 = reinterpret_cast<uint16_t*>(Y) + m * N + np;
-            if (np + 1 < N && (N & 1) == 0 && (reinterpret_cast<uintptr_t>(Y) & 3) == 0) {   // 4-byte aligned pair
-              *reinterpret_cast<uint32_t*>(y16) = pk_bf16_rne(lo, hi);
-            } else {
-              y16[0] = f32_to_bf16_rne(lo);
-              if (np + 1 < N) y16[1] = f32_to_bf16_rne(hi);
-            }
-          }
-        }
+      for (int r = 0; r < 16; ++r) {
+        const int64_t m = m0 + mi * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
+        if (m < row_end && n < N) __builtin_nontemporal_store(acc[mi][ni][r], reinterpret_cast<float*>(Y) + m * N + n);
       }
     }
-  }
 }
 
 // bf16 / SwiGLU epilogue staged through LDS (the pipelined kernel's stages
@@ -256,184 +211,6 @@ __device__ __forceinline__ void store_wave_tile_lds(const v16f (&acc)[FM][FN], f
     store_wave_tile_lds_impl<OUT, false>(acc, t, Y, m0, row_end, n0, N, lane);
   else
     store_wave_tile_lds_impl<OUT, true>(acc, t, Y, m0, row_end, n0, N, lane);
-}
-
-template <int BM, int BN, int WAVES_M, int WAVES_N, int OUT = 0>
-__global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_mxfp4_kernel(
-    const uint8_t* __restrict__ A, const uint8_t* __restrict__ As, const uint8_t* __restrict__ B,
-    const uint8_t* __restrict__ Bs, const int32_t* __restrict__ offsets, int E, int64_t M,
-    int64_t N, int64_t K, void* __restrict__ Y, int n_tiles_n) {
-  using T = GemmTile<BM, BN, WAVES_M, WAVES_N>;
-  __shared__ __attribute__((aligned(16))) uint8_t smA[2][BM * 128];
-  __shared__ __attribute__((aligned(16))) uint8_t smB[2][BN * 128];
-  __shared__ uint32_t smAs[2][BM * 2];
-  __shared__ uint32_t smBs[2][BN * 2];
-
-  // ---- tile -> (expert, rows, columns)
-  const int tn = (int)(blockIdx.x % (unsigned)n_tiles_n);
-  int64_t slot = blockIdx.x / (unsigned)n_tiles_n;
-  int e = 0;
-  int64_t row_begin = 0, row_end = M;
-  if (offsets != nullptr) {
-    for (e = 0; e < E; ++e) {
-      const int64_t b = offsets[e], en = offsets[e + 1];
-      const int64_t t = (en - b + BM - 1) / BM;
-      if (slot < t) {
-        row_begin = b + slot * BM;
-        row_end = en;
-        break;
-      }
-      slot -= t;
-    }
-    if (e == E) return;
-  } else {
-    row_begin = slot * BM;
-    if (row_begin >= M) return;
-  }
-  const int64_t n0 = (int64_t)tn * BN;
-  const int64_t KB = K >> 1;   // code bytes per row
-  const int64_t KG = K >> 5;   // groups (scale bytes) per row
-  const uint8_t* Bx = B + (int64_t)e * N * KB;
-  const uint8_t* Bsx = Bs + (int64_t)e * N * KG;
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = tid >> 6;
-  const int wm = wave / WAVES_N;
-  const int wn = wave % WAVES_N;
-  const int r32 = lane & 31;
-  const int h = lane >> 5;
-
-  // ---- per-thread global source offsets (rows clamped into the valid range)
-  int64_t offA[T::kAChunks], offB[T::kBChunks];
-  int ldsA[T::kAChunks], ldsB[T::kBChunks];
-#pragma unroll
-  for (int i = 0; i < T::kAChunks; ++i) {
-    const int idx = tid + i * T::kThreads;
-    const int row = idx >> 3;
-    int64_t gr = row_begin + row;
-    if (gr >= row_end) gr = row_end - 1;
-    offA[i] = gr * KB + (idx & 7) * 16;
-    ldsA[i] = row * 128 + (((idx & 7) ^ (row & 7)) << 4);
-  }
-#pragma unroll
-  for (int i = 0; i < T::kBChunks; ++i) {
-    const int idx = tid + i * T::kThreads;
-    const int row = idx >> 3;
-    int64_t gn = n0 + row;
-    if (gn >= N) gn = N - 1;
-    offB[i] = gn * KB + (idx & 7) * 16;
-    ldsB[i] = row * 128 + (((idx & 7) ^ (row & 7)) << 4);
-  }
-  // chunk c of a thread is the same for all its chunks: idx & 7 == tid & 7
-  const int my_c = tid & 7;
-  int64_t offAs[T::kASc], offBs[T::kBSc];
-#pragma unroll
-  for (int i = 0; i < T::kASc; ++i) {
-    const int idx = tid + i * T::kThreads;
-    const int row = idx < BM * 2 ? (idx >> 1) : 0;
-    int64_t gr = row_begin + row;
-    if (gr >= row_end) gr = row_end - 1;
-    offAs[i] = gr * KG + (idx & 1) * 4;
-  }
-#pragma unroll
-  for (int i = 0; i < T::kBSc; ++i) {
-    const int idx = tid + i * T::kThreads;
-    const int row = idx < BN * 2 ? (idx >> 1) : 0;
-    int64_t gn = n0 + row;
-    if (gn >= N) gn = N - 1;
-    offBs[i] = gn * KG + (idx & 1) * 4;
-  }
-  const int my_half = tid & 1;
-
-  uint4 ra[T::kAChunks], rb[T::kBChunks];
-  uint32_t ras[T::kASc], rbs[T::kBSc];
-
-#define MACAQ_LOAD_TILE(KT)                                                                          \
-  {                                                                                                  \
-    const int64_t g0 = (int64_t)(KT) * 8;                                                            \
-    const bool cok = g0 + my_c < KG;                                                                 \
-    const bool sok = g0 + my_half * 4 < KG;                                                          \
-    _Pragma("unroll") for (int i = 0; i < T::kAChunks; ++i) {                                        \
-      ra[i] = cok ? *reinterpret_cast<const uint4*>(A + offA[i] + g0 * 16) : make_uint4(0, 0, 0, 0); \
-    }                                                                                                \
-    _Pragma("unroll") for (int i = 0; i < T::kBChunks; ++i) {                                        \
-      rb[i] = cok ? *reinterpret_cast<const uint4*>(Bx + offB[i] + g0 * 16) : make_uint4(0, 0, 0, 0); \
-    }                                                                                                \
-    _Pragma("unroll") for (int i = 0; i < T::kASc; ++i) {                                            \
-      ras[i] = sok ? *reinterpret_cast<const uint32_t*>(As + offAs[i] + g0) : 0u;                    \
-    }                                                                                                \
-    _Pragma("unroll") for (int i = 0; i < T::kBSc; ++i) {                                            \
-      rbs[i] = sok ? *reinterpret_cast<const uint32_t*>(Bsx + offBs[i] + g0) : 0u;                   \
-    }                                                                                                \
-  }
-#define MACAQ_STORE_TILE(ST)                                                                         \
-  {                                                                                                  \
-    _Pragma("unroll") for (int i = 0; i < T::kAChunks; ++i)                                          \
-        *reinterpret_cast<uint4*>(&smA[ST][ldsA[i]]) = ra[i];                                        \
-    _Pragma("unroll") for (int i = 0; i < T::kBChunks; ++i)                                          \
-        *reinterpret_cast<uint4*>(&smB[ST][ldsB[i]]) = rb[i];                                        \
-    _Pragma("unroll") for (int i = 0; i < T::kASc; ++i) {                                            \
-      if (tid + i * T::kThreads < BM * 2) smAs[ST][tid + i * T::kThreads] = ras[i];                  \
-    }                                                                                                \
-    _Pragma("unroll") for (int i = 0; i < T::kBSc; ++i) {                                            \
-      if (tid + i * T::kThreads < BN * 2) smBs[ST][tid + i * T::kThreads] = rbs[i];                  \
-    }                                                                                                \
-  }
-
-  v16f acc[T::kFM][T::kFN];
-#pragma unroll
-  for (int mi = 0; mi < T::kFM; ++mi)
-#pragma unroll
-    for (int ni = 0; ni < T::kFN; ++ni)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[mi][ni][r] = 0.0f;
-
-  const int nk = (int)((K + 255) / 256);
-  MACAQ_LOAD_TILE(0)
-  MACAQ_STORE_TILE(0)
-  __syncthreads();
-
-  for (int kt = 0; kt < nk; ++kt) {
-    const int st = kt & 1;
-    if (kt + 1 < nk) MACAQ_LOAD_TILE(kt + 1)
-
-    uint32_t sa[T::kFM], sb[T::kFN];
-    int rowA[T::kFM], rowB[T::kFN];
-#pragma unroll
-    for (int mi = 0; mi < T::kFM; ++mi) {
-      rowA[mi] = wm * T::kTM + mi * 32 + r32;
-      sa[mi] = smAs[st][rowA[mi] * 2 + h];
-    }
-#pragma unroll
-    for (int ni = 0; ni < T::kFN; ++ni) {
-      rowB[ni] = wn * T::kTN + ni * 32 + r32;
-      sb[ni] = smBs[st][rowB[ni] * 2 + h];
-    }
-    const int sw = r32 & 7;
-    uint4 fa[T::kFM], fb[T::kFN];
-#define MACAQ_SUBSTEP(J)                                                                      \
-  {                                                                                           \
-    _Pragma("unroll") for (int mi = 0; mi < T::kFM; ++mi) fa[mi] =                            \
-        *reinterpret_cast<const uint4*>(&smA[st][rowA[mi] * 128 + (((4 * h + (J)) ^ sw) << 4)]); \
-    _Pragma("unroll") for (int ni = 0; ni < T::kFN; ++ni) fb[ni] =                            \
-        *reinterpret_cast<const uint4*>(&smB[st][rowB[ni] * 128 + (((4 * h + (J)) ^ sw) << 4)]); \
-    mfma_substep<J>(acc, fa, fb, sa, sb);                                                     \
-  }
-    MACAQ_SUBSTEP(0)
-    MACAQ_SUBSTEP(1)
-    MACAQ_SUBSTEP(2)
-    MACAQ_SUBSTEP(3)
-#undef MACAQ_SUBSTEP
-
-    if (kt + 1 < nk) MACAQ_STORE_TILE(st ^ 1)
-    __syncthreads();
-  }
-
-#undef MACAQ_LOAD_TILE
-#undef MACAQ_STORE_TILE
-
-  store_wave_tile<OUT>(acc, Y, row_begin + wm * T::kTM, row_end, n0 + wn * T::kTN, N, r32, h);
 }
 
 // ---------------------------------------------------------------------------
@@ -701,7 +478,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, MINB) void gemm_mxfp4_pipe_
     } else {
       wait_vmcnt<0>();
     }
-    __builtin_amdgcn_s_barrier();
+    block_barrier();
     if (kt + STAGES - 1 < nk) issue(kt + STAGES - 1, (kt + STAGES - 1) % STAGES);
 
     const uint8_t* base = smem + (kt % STAGES) * L::kStage;
@@ -731,7 +508,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, MINB) void gemm_mxfp4_pipe_
   }
 
   if constexpr (OUT == 0) {
-    store_wave_tile<0>(acc, Y, row_begin + wm * T::kTM, row_end, n0 + wn * T::kTN, N, r32, h);
+    store_wave_tile_f32(acc, Y, row_begin + wm * T::kTM, row_end, n0 + wn * T::kTN, N, r32, h);
   } else {
     static_assert(STAGES * L::kStage >= kWaves * kEpiLdsBytes, "epilogue tiles must fit in the stages");
     __syncthreads();   // every wave is done reading the last K-tile

@@ -16,7 +16,12 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "macaq.h"
+
 namespace macaq {
+
+// Launcher override set by macaq_set_tuning (MACAQ_TUNE_*): 0 = automatic.
+int tuning(int knob);
 
 // 1/sqrt(32) rounded to fp32.
 __device__ __forceinline__ float hadamard_norm() { return __uint_as_float(0x3E3504F3u); }
@@ -128,17 +133,33 @@ __device__ __forceinline__ uint32_t quantize_quad(float (&t)[8], uint32_t* scale
 // issued after such copies makes the compiler's own waits stricter (it does
 // not count the copies), never weaker.
 
+// The waitcnt and barrier builtins do not touch memory as far as the
+// compiler's IR is concerned, so each is followed by an empty asm statement
+// with a memory clobber: no load or store of LDS or global memory is moved
+// across the wait (a read of a DMA-filled slot above the wait for its copy,
+// or a copy into a slot above the wait for that slot's last reads).
 template <int VM>
 __device__ __forceinline__ void wait_vmcnt() {
   static_assert(VM >= 0 && VM < 64, "vmcnt range");
   // gfx9 s_waitcnt: vmcnt[3:0] at bits 3:0, vmcnt[5:4] at bits 15:14,
   // expcnt (7) and lgkmcnt (15) left at their maxima (no wait).
   __builtin_amdgcn_s_waitcnt((VM & 0xF) | ((VM >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+  asm volatile("" ::: "memory");
 }
 
 // Wait until every LDS (and scalar-memory) access of this wave completed;
 // vmcnt and expcnt are left at their maxima.
-__device__ __forceinline__ void wait_lgkmcnt0() { __builtin_amdgcn_s_waitcnt(0xF | (0x3 << 14) | (0x7 << 4)); }
+__device__ __forceinline__ void wait_lgkmcnt0() {
+  __builtin_amdgcn_s_waitcnt(0xF | (0x3 << 14) | (0x7 << 4));
+  asm volatile("" ::: "memory");
+}
+
+// s_barrier with the same compiler ordering (no memory access moves across).
+__device__ __forceinline__ void block_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
 
 __device__ __forceinline__ void dma16(const uint8_t* g, uint32_t lds_addr) {
   asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(g), "{m0}"(lds_addr) : "memory");

@@ -27,3 +27,19 @@ def pytest_collection_modifyitems(config, items):
     for item in items:
         if "gpu" in item.keywords:
             item.add_marker(skip)
+
+
+@pytest.fixture
+def tune():
+    """tune(knob, value): force a kernel choice through macaq_set_tuning for
+    the rest of the test; every knob touched is set back afterwards."""
+    import mxfp4_w4a4_quantized_channel_amd as mx
+    before = {}
+
+    def set_knob(knob, value):
+        prev = mx.set_tuning(knob, value)
+        before.setdefault(knob, prev)
+
+    yield set_knob
+    for knob, value in before.items():
+        mx.set_tuning(knob, value)

@@ -240,3 +240,32 @@ def test_tiled_weights_validation():
     L = mx.lib()
     assert L.macaq_linear_path(1, 25600, 5120, 1, mx.PATH_AUTO | T) == mx.PATH_UNFUSED
     assert L.macaq_linear_workspace_bytes(1, 25600, 5120, 1, mx.PATH_AUTO | T) == L.macaq_quant_act_bytes(1, 5120)
+
+
+def test_set_tuning_validation_and_restore():
+    """macaq_set_tuning: unknown knobs and out-of-range values are refused;
+    a valid value returns the previous one, and 0 restores the automatic
+    choice."""
+    mx.lib()
+    assert mx.macaq_set_tuning(-1, 0) == INVALID
+    assert mx.macaq_set_tuning(7, 0) == INVALID
+    assert mx.macaq_set_tuning(mx.TUNE_GEMM_TILE, 4) == INVALID
+    assert mx.macaq_set_tuning(mx.TUNE_ACT_SHARED_S, -1) == INVALID
+    assert mx.set_tuning(mx.TUNE_GEMM_TILE, 3) == 0
+    assert mx.set_tuning(mx.TUNE_GEMM_TILE, 1) == 3
+    assert mx.set_tuning(mx.TUNE_GEMM_TILE, 0) == 1
+    assert mx.set_tuning(mx.TUNE_DECODE_ROWS, 64) == 0
+    assert mx.set_tuning(mx.TUNE_DECODE_ROWS, 0) == 64
+    with pytest.raises(mx.MacaqError):
+        mx.set_tuning(mx.TUNE_DECODE_WAVES, 9)
+
+
+def test_no_tuning_environment_on_the_launch_path():
+    """The kernel choices read no environment variable (only the MACAQ_CHECK
+    debug switch is read by the entry points)."""
+    csrc = os.path.join(ROOT, "mxfp4_w4a4_quantized_channel_amd", "csrc")
+    for f in os.listdir(csrc):
+        text = open(os.path.join(csrc, f)).read()
+        for m in re.finditer(r"getenv\(\s*\"([A-Z_]+)\"", text):
+            assert m.group(1) == "MACAQ_CHECK", (f, m.group(1))
+

@@ -102,11 +102,11 @@ def test_quant_act_bit_exact(name, kw):
 
 
 @pytest.mark.parametrize("steps", [1, 5])
-def test_quant_act_rows_per_wave(steps, monkeypatch):
+def test_quant_act_rows_per_wave(steps, tune):
     """Waves of 1 and of 5 row steps (segments of 16 groups over 4 rows), with
     expert boundaries inside a step and inside a wave."""
     say(f"quant_act steps={steps}")
-    monkeypatch.setenv("MACAQ_ACT_ROWS_PER_WAVE", str(steps))
+    tune(mx.TUNE_ACT_ROWS_PER_WAVE, steps)
     wl = workloads.make(cfg=5, shape=(333, 32, 256))
     codes, scales = mx.quant_act(wl.x.to(DEV), wl.s.to(DEV), wl.offsets.to(DEV))
     rc, rs = oracle.quant_act(host(wl.x), wl.s.numpy(), wl.offsets.numpy())
@@ -125,16 +125,16 @@ LAYOUT_ACT = [
 @pytest.mark.parametrize("steps", [None, 1, 3])
 @pytest.mark.parametrize("shared", ["0", "1"])
 @pytest.mark.parametrize("name,kw", LAYOUT_ACT, ids=[n for n, _ in LAYOUT_ACT])
-def test_quant_act_both_layouts(name, kw, shared, steps, monkeypatch):
+def test_quant_act_both_layouts(name, kw, shared, steps, tune):
     """Both wave layouts of the activation kernel, forced: s per wave in
     registers, and s staged per block in LDS for the experts of the block's
     first and last rows (token routing puts many more experts in a block, so
     rows of other experts read s directly); also with 1 and 3 row blocks per
     wave."""
     say(f"quant_act {name} shared={shared} steps={steps}")
-    monkeypatch.setenv("MACAQ_ACT_SHARED_S", shared)
+    tune(mx.TUNE_ACT_SHARED_S, 2 if shared == "1" else 1)
     if steps is not None:
-        monkeypatch.setenv("MACAQ_ACT_ROWS_PER_WAVE", str(steps))
+        tune(mx.TUNE_ACT_ROWS_PER_WAVE, steps)
     wl = workloads.make(**kw)
     off = wl.offsets.to(DEV) if wl.E > 1 else None
     codes, scales = mx.quant_act(wl.x.to(DEV), wl.s.to(DEV), off)
@@ -145,15 +145,15 @@ def test_quant_act_both_layouts(name, kw, shared, steps, monkeypatch):
 
 @pytest.mark.parametrize("steps", [None, 7])
 @pytest.mark.parametrize("shared", ["0", "1"])
-def test_quant_act_many_experts(shared, steps, monkeypatch):
+def test_quant_act_many_experts(shared, steps, tune):
     """130 experts with runs of empty ones and ragged counts: the wave's
     first expert comes from a binary search over the offsets, and lanes walk
     on across expert ends inside a row block, a wave and a block; 7 row
     blocks per wave refill each slot of the copy ring twice."""
     say(f"quant_act E130 shared={shared} steps={steps}")
-    monkeypatch.setenv("MACAQ_ACT_SHARED_S", shared)
+    tune(mx.TUNE_ACT_SHARED_S, 2 if shared == "1" else 1)
     if steps is not None:
-        monkeypatch.setenv("MACAQ_ACT_ROWS_PER_WAVE", str(steps))
+        tune(mx.TUNE_ACT_ROWS_PER_WAVE, steps)
     E, K = 130, 768
     rng = np.random.default_rng(130)
     counts = rng.integers(0, 9, E)
@@ -171,12 +171,12 @@ def test_quant_act_many_experts(shared, steps, monkeypatch):
 
 @pytest.mark.parametrize("shared", ["0", "1"])
 @pytest.mark.parametrize("M,K", [(7, 32), (13, 96), (5, 160), (9, 2080)])
-def test_quant_act_narrow_rows(M, K, shared, monkeypatch):
+def test_quant_act_narrow_rows(M, K, shared, tune):
     """Rows of 1, 3, 5 and 65 groups: most lanes of a segment are past the
     row's last group, and their copies of the ring are stand-ins that no
     lane stores; M is not a multiple of the rows per block step."""
     say(f"quant_act narrow M{M} K{K} shared={shared}")
-    monkeypatch.setenv("MACAQ_ACT_SHARED_S", shared)
+    tune(mx.TUNE_ACT_SHARED_S, 2 if shared == "1" else 1)
     rng = np.random.default_rng(M * K)
     x = torch.from_numpy(rng.standard_normal((M, K)).astype(np.float32)).to(torch.bfloat16)
     s = rng.uniform(0.25, 4.0, (1, K)).astype(np.float32)
@@ -187,11 +187,11 @@ def test_quant_act_narrow_rows(M, K, shared, monkeypatch):
 
 
 @pytest.mark.parametrize("shared", ["0", "1"])
-def test_prepare_weights_both_layouts(shared, monkeypatch):
+def test_prepare_weights_both_layouts(shared, tune):
     """Weight preparation (reciprocal factors, experts of N rows each) with
     either wave layout forced."""
     say(f"prepare_weights experts shared={shared}")
-    monkeypatch.setenv("MACAQ_ACT_SHARED_S", shared)
+    tune(mx.TUNE_ACT_SHARED_S, 2 if shared == "1" else 1)
     wl = workloads.make(cfg=5, shape=(64, 48, 256))
     codes, scales = gpu_prepare(wl)
     for e in range(wl.E):
@@ -347,7 +347,7 @@ def test_linear_deterministic():
 
 # ------------------------------------------------------------ every GEMM kernel variant
 
-TILES = ["256x256", "256x128", "128x128", "128x128v1"]
+TILES = ["256x256", "256x128", "128x128"]
 TILE_SHAPES = [
     ("ragged M N", (300, 260, 1024)),
     ("K tail 128", (257, 129, 640)),
@@ -357,9 +357,9 @@ TILE_SHAPES = [
 
 @pytest.mark.parametrize("tile", TILES)
 @pytest.mark.parametrize("name,shape", TILE_SHAPES, ids=[n for n, _ in TILE_SHAPES])
-def test_gemm_each_tile_variant(tile, name, shape, monkeypatch):
+def test_gemm_each_tile_variant(tile, name, shape, tune):
     say(f"gemm tile={tile} {name} {shape}")
-    monkeypatch.setenv("MACAQ_GEMM_TILE", tile)
+    tune(mx.TUNE_GEMM_TILE, mx.GEMM_TILES[tile])
     M, N, K = shape
     rng = np.random.default_rng(M + N + K)
     ac = rng.integers(0, 256, (M, K // 2), dtype=np.uint8)
@@ -372,9 +372,9 @@ def test_gemm_each_tile_variant(tile, name, shape, monkeypatch):
 
 
 @pytest.mark.parametrize("tile", TILES)
-def test_gemm_grouped_each_tile_variant(tile, monkeypatch):
+def test_gemm_grouped_each_tile_variant(tile, tune):
     say(f"gemm grouped tile={tile}")
-    monkeypatch.setenv("MACAQ_GEMM_TILE", tile)
+    tune(mx.TUNE_GEMM_TILE, mx.GEMM_TILES[tile])
     E, N, K = 5, 200, 512
     counts = np.array([3, 0, 270, 1, 300])
     off = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
@@ -404,14 +404,14 @@ DECODE_SHAPES = [
 
 
 @pytest.mark.parametrize("waves,stages", [(8, 2), (4, 2), (4, 3)])
-def test_gemm_decode_forced_rings(waves, stages, monkeypatch):
+def test_gemm_decode_forced_rings(waves, stages, tune):
     """Decode rings forced on one M = 32 shape: 8 waves of 2 slots (no longer
     the default choice at M = 32) and 4 waves of 2 or 3 slots; each within
     the oracle's bound (the K split over the waves differs between them, so
     their fp32 sums are not compared bit for bit)."""
     say(f"gemm decode forced waves={waves} stages={stages}")
-    monkeypatch.setenv("MACAQ_DECODE_WAVES", str(waves))
-    monkeypatch.setenv("MACAQ_DECODE_STAGES", str(stages))
+    tune(mx.TUNE_DECODE_WAVES, waves)
+    tune(mx.TUNE_DECODE_STAGES, stages)
     M, N, K = 32, 96, 256 * 26
     rng = np.random.default_rng(2600 + waves)
     ac = rng.integers(0, 256, (M, K // 2), dtype=np.uint8)
@@ -475,11 +475,11 @@ ROWS64_LINEAR = [
 
 
 @pytest.mark.parametrize("shape", ROWS64_GEMM, ids=[f"M{m} N{n} K{k}" for m, n, k in ROWS64_GEMM])
-def test_gemm_decode_64_row_blocks(shape, monkeypatch):
+def test_gemm_decode_64_row_blocks(shape, tune):
     """Blocks of 64 weight rows (two MFMA row tiles per activation chunk),
     ragged N included."""
     say(f"gemm decode 64-row blocks {shape}")
-    monkeypatch.setenv("MACAQ_DECODE_ROWS", "64")
+    tune(mx.TUNE_DECODE_ROWS, 64)
     M, N, K = shape
     rng = np.random.default_rng(M * 17 + N)
     ac = rng.integers(0, 256, (M, K // 2), dtype=np.uint8)
@@ -493,9 +493,9 @@ def test_gemm_decode_64_row_blocks(shape, monkeypatch):
 
 @pytest.mark.parametrize("flags", [mx.PATH_FUSED, mx.PATH_UNFUSED])
 @pytest.mark.parametrize("name,kw", ROWS64_LINEAR, ids=[n for n, _ in ROWS64_LINEAR])
-def test_linear_decode_64_row_blocks(name, kw, flags, monkeypatch):
+def test_linear_decode_64_row_blocks(name, kw, flags, tune):
     say(f"linear decode 64-row blocks {name} flags={flags}")
-    monkeypatch.setenv("MACAQ_DECODE_ROWS", "64")
+    tune(mx.TUNE_DECODE_ROWS, 64)
     wl = workloads.make(**kw)
     wc, wsc = gpu_prepare(wl)
     y = mx.linear(wl.x.to(DEV), wl.s.to(DEV), wc, wsc, flags=flags)

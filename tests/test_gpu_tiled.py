@@ -75,12 +75,12 @@ TILED_SHAPES = [
 
 @pytest.mark.parametrize("tile", ["256x256", "256x128", "128x128"])
 @pytest.mark.parametrize("name,shape", TILED_SHAPES, ids=[n for n, _ in TILED_SHAPES])
-def test_tiled_gemm_equals_row_major(name, shape, tile, monkeypatch):
+def test_tiled_gemm_equals_row_major(name, shape, tile, tune):
     """Each tile variant: the tiled GEMM's fp32 y equals the row-major GEMM's
     bit for bit, and is within the oracle's bound."""
     M, N, K = shape
     say(f"tiled gemm {name} M{M} N{N} K{K} tile {tile}")
-    monkeypatch.setenv("MACAQ_GEMM_TILE", tile)
+    tune(mx.TUNE_GEMM_TILE, mx.GEMM_TILES[tile])
     x, s, ac, asc, wc, wsc = _operands(M, N, K, seed=M + N)
     tc, ts = mx.tile_weights(wc, wsc)
     y_t = mx.gemm(ac, asc, tc, ts, epilogue=mx.W_TILED)
