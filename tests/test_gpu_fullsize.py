@@ -1,12 +1,17 @@
 """Parity at the full workload sizes, in the launch configuration the
-benchmark times: codes of sampled rows bit-exact, sampled outputs of the
-whole layer within the GEMM tolerance.  The oracle quantizes only the
-sampled activation rows and weight rows."""
+benchmark times (tiled W' for the prefill and grouped layers, as bench.py
+runs them, and the row-major layout beside it): every activation and weight
+code and scale byte bit-exact against the oracle, and layer outputs within
+the GEMM tolerance — all outputs of the decode and tiny layers, whole rows
+of outputs for a row sample of the prefill and grouped layers.  The oracle
+runs in row chunks on a thread pool (tests/oracle_rows.py); weights and
+references shared by several cases are computed once."""
 import numpy as np
 import pytest
 import torch
 
 import oracle
+import oracle_rows
 import workloads
 import mxfp4_w4a4_quantized_channel_amd as mx
 
@@ -20,55 +25,113 @@ def host(t):
 
 
 FULL = [
-    ("attn-proj M2048 N4096 K4096", dict(cfg=2)),
-    ("down-prefill M4096 N4096 K14336", dict(cfg=3)),
-    ("decode gate/up M1", dict(cfg=4, variant=0, M=1)),
-    ("decode gate/up M8", dict(cfg=4, variant=0, M=8)),
-    ("decode gate/up M32", dict(cfg=4, variant=0, M=32)),
-    ("decode down M1", dict(cfg=4, variant=1, M=1)),
-    ("decode down M32", dict(cfg=4, variant=1, M=32)),
-    ("MoE E64 expert-Zipf", dict(cfg=5)),
-    ("MoE E64 token-Zipf", dict(cfg=5, routing="token_zipf")),
+    ("tiny M16 N128 K256 fp32", dict(cfg=1), "rowmajor"),
+    ("attn-proj M2048 N4096 K4096 tiled", dict(cfg=2), "tiled"),
+    ("attn-proj M2048 N4096 K4096 row-major", dict(cfg=2), "rowmajor"),
+    ("attn-proj literal s=sigma tiled", dict(cfg=2, scale_rule="literal"), "tiled"),
+    ("down-prefill M4096 N4096 K14336 tiled", dict(cfg=3), "tiled"),
+    ("down-prefill M4096 N4096 K14336 row-major", dict(cfg=3), "rowmajor"),
+    ("decode gate/up M1", dict(cfg=4, variant=0, M=1), "rowmajor"),
+    ("decode gate/up M8", dict(cfg=4, variant=0, M=8), "rowmajor"),
+    ("decode gate/up M32", dict(cfg=4, variant=0, M=32), "rowmajor"),
+    ("decode down M1", dict(cfg=4, variant=1, M=1), "rowmajor"),
+    ("decode down M8", dict(cfg=4, variant=1, M=8), "rowmajor"),
+    ("decode down M32", dict(cfg=4, variant=1, M=32), "rowmajor"),
+    ("MoE E64 expert-Zipf tiled", dict(cfg=5), "tiled"),
+    ("MoE E64 expert-Zipf row-major", dict(cfg=5), "rowmajor"),
+    ("MoE E64 token-Zipf tiled", dict(cfg=5, routing="token_zipf"), "tiled"),
+    ("MoE E64 token-Zipf row-major", dict(cfg=5, routing="token_zipf"), "rowmajor"),
 ]
 
+_WL, _W, _A, _Y = {}, {}, {}, {}
 
-@pytest.mark.parametrize("name,kw", FULL, ids=[n for n, _ in FULL])
-def test_full_size(name, kw):
+
+def _key(kw, *drop):
+    return tuple(sorted((k, v) for k, v in kw.items() if k not in drop))
+
+
+def workload(kw):
+    k = _key(kw)
+    if k not in _WL:
+        _WL[k] = workloads.make(**kw)
+    return _WL[k]
+
+
+def oracle_weights(kw, wl):
+    """Oracle W' of every expert; shared by the cases with the same weights
+    (decode M and MoE routing do not change them)."""
+    k = _key(kw, "M", "routing")
+    if k not in _W:
+        _W[k] = [oracle_rows.prepare_weights(host(wl.w[e]), wl.s[e].numpy()) for e in range(wl.E)]
+    return _W[k]
+
+
+def oracle_acts(kw, wl):
+    k = _key(kw)
+    if k not in _A:
+        _A[k] = oracle_rows.quant_act(host(wl.x), wl.s.numpy(), wl.offsets.numpy() if wl.E > 1 else None)
+    return _A[k]
+
+
+def sample_rows(wl):
+    """Rows whose outputs are compared: all of a decode or tiny layer; else
+    32 random rows plus the first and last row of every non-empty expert."""
+    M = wl.M
+    if M <= 32:
+        return np.arange(M)
+    rng = np.random.default_rng(1234)
+    off = wl.offsets.numpy().astype(np.int64)
+    edges = [r for e in range(wl.E) if off[e + 1] > off[e] for r in (off[e], off[e + 1] - 1)]
+    return np.unique(np.concatenate([rng.choice(M, 32, replace=False), edges]))
+
+
+def oracle_outputs(kw, wl, rows, rac, ras, rw):
+    """fp64 reference y and S for whole output rows `rows`, per expert."""
+    k = _key(kw)
+    if k not in _Y:
+        e_rows = oracle.expert_of_rows(wl.offsets.numpy(), wl.M)[rows] if wl.E > 1 else np.zeros(len(rows), int)
+        y_ref = np.empty((len(rows), wl.N))
+        S = np.empty_like(y_ref)
+        for e in np.unique(e_rows):
+            sel = np.nonzero(e_rows == e)[0]
+            y_ref[sel], S[sel] = oracle.gemm(rac[rows[sel]], ras[rows[sel]], *rw[e])
+        _Y[k] = (y_ref, S)
+    return _Y[k]
+
+
+@pytest.mark.parametrize("name,kw,layout", FULL, ids=[n for n, _, _ in FULL])
+def test_full_size(name, kw, layout):
     print(f"[case] full size {name}", flush=True)
-    wl = workloads.make(**kw)
+    wl = workload(kw)
     M, N, K, E = wl.M, wl.N, wl.K, wl.E
     off = wl.offsets.to(DEV) if E > 1 else None
     x, s = wl.x.to(DEV), wl.s.to(DEV)
     wc, wsc = mx.prepare_weights(wl.w.to(DEV), s)
     ac, asc = mx.quant_act(x, s, off)
-    y = mx.linear(x, s, wc, wsc, off)
+    flags = mx.PATH_AUTO
+    if layout == "tiled":
+        assert M > 32 and N % 32 == 0 and K % 256 == 0   # the benchmark's rule for tiled W'
+        tc, ts = mx.tile_weights(wc, wsc)
+        y = mx.linear(x, s, tc, ts, off, flags=flags | mx.W_TILED)
+    else:
+        y = mx.linear(x, s, wc, wsc, off, flags=flags)
     torch.cuda.synchronize()
 
-    rng = np.random.default_rng(1234)
-    offs = wl.offsets.numpy()
-    rows = np.unique(np.concatenate([rng.choice(M, min(M, 24), replace=False), [0, M - 1]]))
-    xs = host(wl.x)[rows]
-    e_rows = oracle.expert_of_rows(offs, M)[rows] if E > 1 else np.zeros(len(rows), int)
-    # activation codes of the sampled rows
-    rac = np.empty((len(rows), K // 2), np.uint8)
-    ras = np.empty((len(rows), K // 32), np.uint8)
-    for i, (r, e) in enumerate(zip(rows, e_rows)):
-        c, sc = oracle.quant_act(xs[i:i + 1], wl.s[e:e + 1].numpy())
-        rac[i], ras[i] = c[0], sc[0]
-    assert np.array_equal(ac[rows].cpu().numpy(), rac)
-    assert np.array_equal(asc[rows].cpu().numpy(), ras)
-    # sampled outputs: weight rows of each sampled row's expert
-    cols = np.unique(np.concatenate([rng.choice(N, min(N, 24), replace=False), [0, N - 1]]))
-    y_np = y.cpu().numpy()
-    for e in np.unique(e_rows):
-        sel = np.nonzero(e_rows == e)[0]
-        rwc, rws = oracle.prepare_weights(host(wl.w[e])[cols], wl.s[e].numpy())
-        assert np.array_equal(wc[e][cols].cpu().numpy(), rwc)
-        assert np.array_equal(wsc[e][cols].cpu().numpy(), rws)
-        y_ref, S = oracle.gemm(rac[sel], ras[sel], rwc, rws)
-        got = y_np[np.ix_(rows[sel], cols)]
-        ok, worst, normwise = oracle.within_tolerance(got, y_ref, S, 1e-5)
-        assert ok, f"expert {e}: worst {worst:.3g} normwise {normwise:.3g}"
+    # every code and scale byte of the activation and of every expert's W'
+    rac, ras = oracle_acts(kw, wl)
+    assert np.array_equal(asc.cpu().numpy(), ras)
+    assert np.array_equal(ac.cpu().numpy(), rac)
+    rw = oracle_weights(kw, wl)
+    wc_h, wsc_h = wc.cpu().numpy(), wsc.cpu().numpy()
+    for e in range(E):
+        assert np.array_equal(wsc_h[e], rw[e][1]), f"expert {e} weight scales"
+        assert np.array_equal(wc_h[e], rw[e][0]), f"expert {e} weight codes"
+
+    # whole output rows within the GEMM tolerance
+    rows = sample_rows(wl)
+    y_ref, S = oracle_outputs(kw, wl, rows, rac, ras, rw)
+    ok, worst, normwise = oracle.within_tolerance(y.cpu().numpy()[rows], y_ref, S, 1e-5)
+    assert ok, f"{len(rows)} rows: worst {worst:.3g} normwise {normwise:.3g}"
 
 
 FULL_EPI = [
@@ -83,17 +146,22 @@ FULL_EPI = [
 @pytest.mark.parametrize("name,kw,epi", FULL_EPI, ids=[n for n, _, _ in FULL_EPI])
 def test_full_size_epilogues(name, kw, epi):
     """Full-size layers with a bf16 output and/or the SwiGLU epilogue, in the
-    benchmark's launch configuration: the bf16 output equals round-to-nearest-
-    even of the same path's fp32 output everywhere, and sampled fp32 outputs
-    are within the oracle's bound (GEMM bound carried through silu(g) * u)."""
+    benchmark's launch configuration (tiled W' above 32 rows): the bf16
+    output equals round-to-nearest-even of the same path's fp32 output
+    everywhere, and sampled fp32 outputs are within the oracle's bound (GEMM
+    bound carried through silu(g) * u)."""
     print(f"[case] full size epilogue {name}", flush=True)
-    wl = workloads.make(**kw)
+    wl = workload(kw)
     M, N, K, E = wl.M, wl.N, wl.K, wl.E
     off = wl.offsets.to(DEV) if E > 1 else None
     x, s = wl.x.to(DEV), wl.s.to(DEV)
     wc, wsc = mx.prepare_weights(wl.w.to(DEV), s)
-    y32 = mx.linear(x, s, wc, wsc, off, out_dtype=torch.float32, epilogue=epi)
-    y16 = mx.linear(x, s, wc, wsc, off, out_dtype=torch.bfloat16, epilogue=epi)
+    flags = mx.PATH_AUTO
+    if M > 32:
+        wc, wsc = mx.tile_weights(wc, wsc)
+        flags |= mx.W_TILED
+    y32 = mx.linear(x, s, wc, wsc, off, flags=flags, out_dtype=torch.float32, epilogue=epi)
+    y16 = mx.linear(x, s, wc, wsc, off, flags=flags, out_dtype=torch.bfloat16, epilogue=epi)
     torch.cuda.synchronize()
     y32 = y32.cpu().numpy()
     assert np.array_equal(workloads.bf16_bits(y16.cpu()), (oracle.round_bf16(y32).view(np.uint32) >> 16).astype(np.uint16))
