@@ -4,8 +4,8 @@
 A step is one pass of the whole online layer over one batch: the activation
 transform + MXFP4 quantization kernel, then the MXFP4 GEMM against weights
 prepared offline (untimed, like the pages' offline weight preparation).
-The default workload is the attention projection M2048 N4096 K4096 with
-bf16 activations.  Inputs are seeded synthetic tensors (module `workloads`)
+The default workload is the MLP down-projection prefill M4096 N4096 K14336
+with bf16 activations, the largest layer (481 GFLOP per step).  Inputs are seeded synthetic tensors (module `workloads`)
 resident in HBM before the timed region; R replicas of (x, W', y) are
 cycled so that the working set exceeds the 256 MB Infinity Cache.
 
@@ -13,7 +13,9 @@ Prints one JSON line:
   value        = 2*M*N*K / (wall time per step)      [TFLOP/s]
   act_transform= algorithmic bytes / act-kernel time  [GB/s]
   roofline     = the GEMM kernel (dominant) against the dense MXFP4 MFMA peak
-  cpu_baseline = the CPU oracle on a bounded row sample of the same layer
+  cpu_baseline = the CPU oracle on a bounded sample of the same layer: its
+                 transform + quantization (GB/s) and its fp64 GEMM
+                 (TFLOP/s), combined into the layer's TFLOP/s
 """
 from __future__ import annotations
 
@@ -35,12 +37,14 @@ MALL_BYTES = 256 << 20
 
 WORKLOADS = {
     # name: (config, variant, M, description)
+    "tiny": (1, 0, None, "tiny M16 N128 K256 fp32 (latency-bound)"),
     "attn": (2, 0, None, "attn-proj M2048 N4096 K4096 bf16"),
     "down": (3, 0, None, "down-prefill M4096 N4096 K14336 bf16"),
     "decode-gateup-m1": (4, 0, 1, "decode gate/up M1 N25600 K5120 bf16"),
     "decode-gateup-m8": (4, 0, 8, "decode gate/up M8 N25600 K5120 bf16"),
     "decode-gateup-m32": (4, 0, 32, "decode gate/up M32 N25600 K5120 bf16"),
     "decode-down-m1": (4, 1, 1, "decode down M1 N5120 K25600 bf16"),
+    "decode-down-m8": (4, 1, 8, "decode down M8 N5120 K25600 bf16"),
     "decode-down-m32": (4, 1, 32, "decode down M32 N5120 K25600 bf16"),
     "moe": (5, 0, None, "MoE E64 T8192 N1024 K3072 bf16, Zipf(1.1) per-expert routing"),
     "moe-token": (5, 0, None, "MoE E64 T8192 N1024 K3072 bf16, per-token Zipf(1.1) routing"),
@@ -65,18 +69,22 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=200)
     p.add_argument("--warmup", type=int, default=20)
-    p.add_argument("--workload", default="attn", choices=sorted(WORKLOADS) + sorted(OFFLINE))
+    p.add_argument("--workload", default="down", choices=sorted(WORKLOADS) + sorted(OFFLINE))
+    p.add_argument("--scale-rule", default="smooth", choices=["smooth", "literal"],
+                   help="per-channel factor of the synthetic layer: smooth s = 1/sigma (default) or literal "
+                        "s = sigma, sigma = sqrt(max|x_cal| / max|w|) per channel")
     p.add_argument("--path", default="auto", choices=["auto", "fused", "unfused"])
     p.add_argument("--out", default="f32", choices=["f32", "bf16"], help="dtype of y")
     p.add_argument("--epilogue", default="none", choices=["none", "swiglu"],
                    help="swiglu: weight rows are (gate, up) pairs and y is [M][N/2] = silu(gate) * up")
     p.add_argument("--w-layout", default="auto", choices=["auto", "tiled", "rowmajor"],
                    help="prepared weights as macaq_prepare_weights writes them (row-major), or repacked offline by "
-                        "macaq_tile_weights (contiguous GEMM copies); auto: tiled for M > 32 when N % 32 == 0 and "
-                        "K % 256 == 0 (the decode kernels read row-major weights)")
+                        "macaq_tile_weights (contiguous GEMM copies); auto: tiled for M > 32 when N %% 32 == 0 and "
+                        "K %% 256 == 0 (the decode kernels read row-major weights)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-ablation", action="store_true", help="skip the pure-MXFP4 comparison")
-    p.add_argument("--cpu-rows", type=int, default=256, help="row sample of the CPU oracle baseline")
+    p.add_argument("--cpu-rows", type=int, default=256, help="activation rows of the CPU oracle baseline")
+    p.add_argument("--cpu-wrows", type=int, default=512, help="weight rows of the CPU oracle baseline's GEMM")
     p.add_argument("--flip-rounds", type=int, default=4096,
                    help="offline workloads: at most this many Flip-Refinement moves per weight row")
     p.add_argument("--library-compare", action="store_true",
@@ -234,36 +242,58 @@ def traffic_record(kernel_key):
     return rec["bytes_per_launch"]
 
 
-def cpu_baseline(wl, rows):
-    """The oracle as it stands on `rows` activation rows of the same layer:
-    transform + quantization of the rows, then the fp64 dequantized GEMM
-    against the full prepared weight (prepared untimed)."""
+def cpu_baseline(wl, rows, wrows, seconds=6.0):
+    """The oracle as it stands, timed on a bounded sample of the same layer
+    and scaled to the whole layer:
+      * transform + MXFP4 quantization of `rows` activation rows, in GB/s
+        of the kernel's algorithmic bytes (x read, codes and scales written);
+      * the dequantized fp64 GEMM of those rows against `wrows` weight rows
+        prepared by the oracle (untimed, like the offline preparation), in
+        TFLOP/s of 2 * rows * wrows * K;
+    each repeated for about `seconds`.  value = the layer's 2MNK over the
+    time the two stages would take on all M rows and N weight rows at these
+    rates.  The transform runs in numpy's single-threaded array operations,
+    the GEMM in the BLAS thread pool."""
     import numpy as np
     import oracle
     import workloads
     from threadpoolctl import threadpool_info
 
     import torch
+    M, N, K = wl.M, wl.N, wl.K
+    rows, wrows = min(rows, M), min(wrows, N)
     xb = workloads.bf16_bits(wl.x[:rows]) if wl.x.dtype == torch.bfloat16 else wl.x[:rows].numpy()
     off = wl.offsets.numpy()
     e0 = int(np.searchsorted(off, 0, side="right") - 1)
-    w = workloads.bf16_bits(wl.w[e0]) if wl.w.dtype == torch.bfloat16 else wl.w[e0].numpy()
+    w = workloads.bf16_bits(wl.w[e0, :wrows]) if wl.w.dtype == torch.bfloat16 else wl.w[e0, :wrows].numpy()
     wc, ws = oracle.prepare_weights(w, wl.s[e0].numpy())
     s = wl.s[e0:e0 + 1].numpy()
-    t0 = time.perf_counter()
-    reps = 0
-    while True:
-        ac, asc = oracle.quant_act(xb, s)
-        oracle.gemm(ac, asc, wc, ws)
-        reps += 1
-        el = time.perf_counter() - t0
-        if el > 10.0 or reps >= 50:
-            break
-    flops = 2.0 * rows * wl.N * wl.K * reps
+
+    def timed(fn):
+        t0, reps = time.perf_counter(), 0
+        while True:
+            out = fn()
+            reps += 1
+            el = time.perf_counter() - t0
+            if el > seconds or reps >= 200:
+                return out, el / reps, reps
+
+    (ac, asc), t_act, n_act = timed(lambda: oracle.quant_act(xb, s))
+    _, t_gemm, n_gemm = timed(lambda: oracle.gemm(ac, asc, wc, ws))
+    xbytes = xb.dtype.itemsize
+    act_bytes = rows * K * xbytes + rows * K // 2 + rows * K // 32 + 4 * K
+    act_gbps = act_bytes / t_act / 1e9
+    gemm_tflops = 2.0 * rows * wrows * K / t_gemm / 1e12
+    layer_s = t_act * M / rows + t_gemm * (M / rows) * (N / wrows)
     threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
-    return {"value": round(flops / el / 1e12, 6), "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"{rows} of {wl.M} rows x {reps} reps (transform+quant of the rows, fp64 GEMM vs full W')",
-            "seconds": round(el, 2), "cpu": cpu_model(), "affinity_cores": len(os.sched_getaffinity(0))}
+    return {"value": round(2.0 * M * N * K / layer_s / 1e12, 6), "unit": "TFLOP/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"transform+quant of {rows} of {M} rows ({n_act} reps), fp64 GEMM of those rows against "
+                      f"{wrows} of {N} oracle-prepared weight rows ({n_gemm} reps); scaled to the layer",
+            "act_transform": {"GBps": round(act_gbps, 4), "us_per_row": round(t_act / rows * 1e6, 2), "cores": 1},
+            "gemm": {"TFLOPs": round(gemm_tflops, 6), "cores": int(threads)},
+            "layer_s": round(layer_s, 3), "seconds": round(t_act * n_act + t_gemm * n_gemm, 2), "cpu": cpu_model(),
+            "affinity_cores": len(os.sched_getaffinity(0))}
 
 
 def cpu_baseline_offline(wl, rows, cols, flip_rows, flip_rounds):
@@ -520,7 +550,7 @@ def main():
         kw["M"] = Mdec
     if args.workload == "moe-token":
         kw["routing"] = "token_zipf"
-    wl = workloads.make(cfg, **kw)
+    wl = workloads.make(cfg, scale_rule=args.scale_rule, **kw)
     M, N, K, E = wl.M, wl.N, wl.K, wl.E
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
@@ -647,6 +677,7 @@ def main():
                    "path": "fused" if fused else "unfused", "replicas": R,
                    "w_layout": "tiled" if tiled else "row-major",
                    "y": f"{args.out} [{M}][{y_cols}]" + (" swiglu" if epi == mx.EPI_SWIGLU else ""),
+                   "scale_rule": {"smooth": "s = 1/sigma", "literal": "s = sigma"}[args.scale_rule],
                    "parallelism": "none (one GPU)"},
     }
     if act_us is not None:
@@ -688,7 +719,7 @@ def main():
                                                        tiled=tiled)
     out["gpu_state"] = {"before": state_before, "after": state_after}
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(wl, min(args.cpu_rows, M))
+        out["cpu_baseline"] = cpu_baseline(wl, args.cpu_rows, args.cpu_wrows)
     print(json.dumps(out), flush=True)
 
 
