@@ -333,6 +333,36 @@ int macaq_linear(const void* x, macaq_dtype x_dtype, const float* s,
                  int64_t M, int64_t N, int64_t K, float* y,
                  void* workspace, size_t workspace_bytes, uint32_t flags, void* stream);
 
+/* Size of the static scratch array of macaq_linear_noalloc: 32 MiB per
+ * device, enough for the unfused path's activation codes and scales of
+ * M * K <= 58.7 million values (e.g. M = 4096 rows of K = 14336). */
+#define MACAQ_NOALLOC_SCRATCH_BYTES (32u << 20)
+
+/*
+ * macaq_linear_ex without a workspace argument, for callers that cannot
+ * allocate device memory or hand one in: code under HIP graph capture, tight
+ * serving loops, harnesses that forbid allocation.  Same arguments (minus
+ * workspace and workspace_bytes), rules, kernels and results (bit for bit)
+ * as macaq_linear_ex.  The staging that macaq_linear_ex keeps in the
+ * caller's workspace (macaq_linear_workspace_bytes(M, N, K, E, flags) bytes:
+ * the activation codes and scales on the unfused path; nothing on the fused
+ * path) lives instead in a static device array of
+ * MACAQ_NOALLOC_SCRATCH_BYTES that the library holds on each device it runs
+ * on until the process ends; a shape that needs more returns
+ * MACAQ_ERR_WORKSPACE before anything is launched.  The call never
+ * allocates or frees memory; its first call on a device looks up that
+ * device's copy of the array (make it before a graph capture).  Every call
+ * on one device shares that device's array: calls that overlap in time on
+ * one device (on different streams, or from different threads) race and
+ * must be serialized by the caller.  Nothing in the array needs to start at
+ * zero: the transform writes every byte the GEMM reads.
+ */
+int macaq_linear_noalloc(const void* x, macaq_dtype x_dtype, const float* s,
+                         const int32_t* expert_offsets, int64_t E,
+                         const uint8_t* w_codes, const uint8_t* w_scales,
+                         int64_t M, int64_t N, int64_t K, void* y, macaq_dtype y_dtype, uint32_t epilogue,
+                         uint32_t flags, void* stream);
+
 /*
  * macaq_gemm and macaq_linear with a chosen output (the layer's consumer
  * step, after the pages' y = x W^T: a bf16 output and a SwiGLU over the

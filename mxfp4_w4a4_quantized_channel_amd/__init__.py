@@ -23,7 +23,8 @@ __all__ = [
     "prepare_weights", "quant_act", "gemm", "linear", "linear_workspace_bytes",
     "encode_e2m1", "quant_mxfp4", "version", "library_path", "EPI_NONE", "EPI_SWIGLU",
     "hessian", "prepare_weights_hessian", "flip_refine", "flip_refine_workspace_bytes",
-    "set_tuning", "TUNE_GEMM_TILE", "TUNE_GEMM_GROUP_M", "TUNE_ACT_ROWS_PER_WAVE", "TUNE_ACT_SHARED_S",
+    "set_tuning", "linear_noalloc", "NOALLOC_SCRATCH_BYTES", "TUNE_GEMM_TILE", "TUNE_GEMM_GROUP_M",
+    "TUNE_ACT_ROWS_PER_WAVE", "TUNE_ACT_SHARED_S",
     "TUNE_DECODE_WAVES", "TUNE_DECODE_STAGES", "TUNE_DECODE_ROWS", "GEMM_TILES",
 ]
 
@@ -33,6 +34,7 @@ library_path = os.path.join(_HERE, "libmacaq.so")
 BF16, F32 = 0, 1
 PATH_AUTO, PATH_FUSED, PATH_UNFUSED = 0, 1, 2
 EPI_NONE, EPI_SWIGLU = 0, 1
+NOALLOC_SCRATCH_BYTES = 32 << 20   # static staging of macaq_linear_noalloc, per device
 W_TILED = 0x100   # weights in macaq_tile_weights' layout (OR into linear's flags / gemm's epilogue)
 # knobs of macaq_set_tuning (0 = the library's own choice)
 (TUNE_GEMM_TILE, TUNE_GEMM_GROUP_M, TUNE_ACT_ROWS_PER_WAVE, TUNE_ACT_SHARED_S, TUNE_DECODE_WAVES,
@@ -77,6 +79,7 @@ def _load():
         "macaq_linear": (ci, [vp, ci, vp, vp, i64, vp, vp, i64, i64, i64, vp, vp, sz, u32, vp]),
         "macaq_gemm_ex": (ci, [vp, vp, vp, i64, vp, vp, i64, i64, i64, vp, ci, u32, vp, sz, vp]),
         "macaq_linear_ex": (ci, [vp, ci, vp, vp, i64, vp, vp, i64, i64, i64, vp, ci, u32, vp, sz, u32, vp]),
+        "macaq_linear_noalloc": (ci, [vp, ci, vp, vp, i64, vp, vp, i64, i64, i64, vp, ci, u32, u32, vp]),
         "macaq_encode_e2m1": (ci, [vp, i64, vp, vp]),
         "macaq_quant_mxfp4": (ci, [vp, ci, i64, i64, vp, vp, vp]),
         "macaq_hessian": (ci, [vp, ci, vp, vp, i64, i64, i64, vp, vp]),
@@ -362,6 +365,26 @@ def linear(x, s, w_codes, w_scales, offsets=None, flags=PATH_AUTO, out=None, wor
     _check(macaq_linear_ex(_ptr(x), _dtype_code(x), _ptr(s), _ptr(offsets), E, _ptr(w_codes), _ptr(w_scales),
                            M, N, K, _ptr(y), ydt, epilogue, _ptr(workspace), ws_bytes, flags, _stream(x.device)),
            "macaq_linear")
+    return y
+
+
+def linear_noalloc(x, s, w_codes, w_scales, offsets=None, flags=PATH_AUTO, out=None,
+                   out_dtype=torch.float32, epilogue=EPI_NONE):
+    """linear() through macaq_linear_noalloc: no workspace; the unfused
+    path's staging lives in the library's static device array."""
+    _load()
+    if s.dim() == 1:
+        s = s[None]
+    w_codes, w_scales = _w_shape(w_codes, w_scales)
+    _need(x, "x", dim=2)
+    _need(s, "s", torch.float32, 2)
+    M, K = x.shape
+    E, N, _ = w_codes.shape
+    y = _out(M, N, out_dtype, epilogue, x.device, out)
+    ydt = F32 if out_dtype == torch.float32 else BF16
+    _check(macaq_linear_noalloc(_ptr(x), _dtype_code(x), _ptr(s), _ptr(offsets), E, _ptr(w_codes), _ptr(w_scales),
+                                M, N, K, _ptr(y), ydt, epilogue, flags, _stream(x.device)),
+           "macaq_linear_noalloc")
     return y
 
 

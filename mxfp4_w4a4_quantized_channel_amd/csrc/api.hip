@@ -6,6 +6,7 @@
 
 #include <algorithm>
 #include <atomic>
+#include <mutex>
 #include <cmath>
 #include <cstdio>
 #include <cstdlib>
@@ -387,12 +388,39 @@ int macaq_gemm(const uint8_t* a_codes, const uint8_t* a_scales, const int32_t* e
 
 }  // extern "C"
 
+// ---- static scratch of the allocation-free entry point.  The unfused
+// path's staging (the activation codes and scales between its two kernels)
+// lives in this file-scope device array instead of a caller's workspace; each
+// device holds its own copy for the life of the process.  In host code
+// `scratch` only names the symbol: its device address is looked up once per
+// device with hipGetSymbolAddress, and only that address is handed to
+// kernels.
 namespace {
+constexpr int kMaxDevices = 64;
+static __device__ __align__(256) uint8_t scratch[MACAQ_NOALLOC_SCRATCH_BYTES];
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];   // device address of `scratch` per device (nullptr until looked up)
+
+int scratch_for_current_device(void** out, const char* fn) {
+  int dev = -1;
+  if (int st = hip_status(hipGetDevice(&dev), fn)) return st;
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(MACAQ_ERR_UNSUPPORTED, std::string(fn) + ": device index " + std::to_string(dev) + " out of range");
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    if (int st = hip_status(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)), fn)) return st;
+    if (p == nullptr) return fail(MACAQ_ERR_HIP, std::string(fn) + ": no device address for the scratch array");
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return MACAQ_OK;
+}
 
 int linear_impl(const void* x, macaq_dtype x_dtype, const float* s, const int32_t* expert_offsets, int64_t E,
                 const uint8_t* w_codes, const uint8_t* w_scales, int64_t M, int64_t N, int64_t K, void* y,
                 macaq_dtype y_dtype, uint32_t epilogue, void* workspace, size_t workspace_bytes, uint32_t flags,
-                void* stream, const char* fn) {
+                void* stream, const char* fn, bool noalloc) {
   if (int st = check_dtype(x_dtype, fn)) return st;
   const bool w_tiled = (flags & MACAQ_W_TILED) != 0;
   if ((flags & ~MACAQ_W_TILED) > MACAQ_PATH_UNFUSED)
@@ -418,6 +446,20 @@ int linear_impl(const void* x, macaq_dtype x_dtype, const float* s, const int32_
                                            "the quantized activation fitting in LDS");
   const bool fused = macaq_linear_path(M, N, K, E, flags) == MACAQ_PATH_FUSED;
   const size_t need = macaq_linear_workspace_bytes(M, N, K, E, flags);
+  if (noalloc) {   // staging in the static scratch array instead of a workspace
+    if (need > (size_t)MACAQ_NOALLOC_SCRATCH_BYTES)
+      return fail(MACAQ_ERR_WORKSPACE, std::string(fn) + ": this shape needs " + std::to_string(need) +
+                                           " bytes of staging, more than the " +
+                                           std::to_string((size_t)MACAQ_NOALLOC_SCRATCH_BYTES) +
+                                           " of the static scratch array; use macaq_linear_ex with a workspace");
+    if (int st = check_device()) return st;
+    workspace = nullptr;
+    workspace_bytes = 0;
+    if (need > 0) {
+      if (int st = scratch_for_current_device(&workspace, fn)) return st;
+      workspace_bytes = need;
+    }
+  }
   if (int st = check_workspace(workspace, workspace_bytes, need, fn)) return st;
   if (int st = check_device()) return st;
   hipStream_t st = (hipStream_t)stream;
@@ -449,7 +491,14 @@ int macaq_linear_ex(const void* x, macaq_dtype x_dtype, const float* s, const in
                     macaq_dtype y_dtype, uint32_t epilogue, void* workspace, size_t workspace_bytes, uint32_t flags,
                     void* stream) {
   return linear_impl(x, x_dtype, s, expert_offsets, E, w_codes, w_scales, M, N, K, y, y_dtype, epilogue, workspace,
-                     workspace_bytes, flags, stream, "macaq_linear");
+                     workspace_bytes, flags, stream, "macaq_linear", false);
+}
+
+int macaq_linear_noalloc(const void* x, macaq_dtype x_dtype, const float* s, const int32_t* expert_offsets,
+                         int64_t E, const uint8_t* w_codes, const uint8_t* w_scales, int64_t M, int64_t N, int64_t K,
+                         void* y, macaq_dtype y_dtype, uint32_t epilogue, uint32_t flags, void* stream) {
+  return linear_impl(x, x_dtype, s, expert_offsets, E, w_codes, w_scales, M, N, K, y, y_dtype, epilogue, nullptr, 0,
+                     flags, stream, "macaq_linear_noalloc", true);
 }
 
 int macaq_linear(const void* x, macaq_dtype x_dtype, const float* s, const int32_t* expert_offsets, int64_t E,

@@ -269,3 +269,16 @@ def test_no_tuning_environment_on_the_launch_path():
         for m in re.finditer(r"getenv\(\s*\"([A-Z_]+)\"", text):
             assert m.group(1) == "MACAQ_CHECK", (f, m.group(1))
 
+
+def test_noalloc_validation_before_any_device_call():
+    """macaq_linear_noalloc checks its arguments and refuses a shape whose
+    staging exceeds the static scratch array before touching a device."""
+    mx.lib()
+    la = lambda M=4, N=8, K=256, E=1, flags=0, x=A16: mx.macaq_linear_noalloc(
+        x, 0, A16, None, E, A16, A16, M, N, K, A16, 1, 0, flags, None)
+    assert la(K=100) == INVALID
+    assert la(flags=7) == INVALID
+    assert la(x=None) == INVALID
+    assert la(M=0) == OK
+    assert la(M=8192, K=16384, flags=2) == WORKSPACE
+    assert b"static scratch" in mx.macaq_last_error()
