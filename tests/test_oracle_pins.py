@@ -356,6 +356,47 @@ def test_within_tolerance_rejects_planted_error():
 
 # ---------------------------------------------------------------- consumer step: bf16 output, SwiGLU
 
+def test_gemm_single_product_closed_form_over_all_scale_bytes():
+    """One nonzero value per row and K = 32: the dequantized fp64 GEMM equals
+    (-1)^(sa^sw) val_a val_w 2^(ba + bw - 254) (E2M1 value by its bit
+    fields, scale 2^(b - 127) per the OCP E8M0 definition) for every scale
+    byte 0..254 on both sides, including products far outside fp32's range."""
+    import math
+    rng = np.random.default_rng(30)
+    ba = np.arange(0, 255, dtype=np.uint8)
+    bw = rng.permutation(ba)
+    ca = rng.integers(0, 16, ba.size).astype(np.uint8)
+    cw = rng.integers(0, 16, ba.size).astype(np.uint8)
+    pa = np.zeros((ba.size, 16), np.uint8)
+    pw = np.zeros((ba.size, 16), np.uint8)
+    pa[:, 0], pw[:, 0] = ca, cw                     # element 0 in the low nibble
+    y, S = oracle.gemm(pa, ba[:, None], pw, bw[:, None])
+
+    def value(code):   # E2M1: sign bit 3, exponent bits 2:1 (bias 1), mantissa bit 0
+        e, m = (int(code) >> 1) & 3, int(code) & 1
+        mag = (m / 2.0) if e == 0 else (1 + m / 2.0) * 2.0 ** (e - 1)
+        return -mag if code & 8 else mag
+    for i in range(ba.size):
+        for j in range(ba.size):
+            want = math.ldexp(value(ca[i]) * value(cw[j]), int(ba[i]) + int(bw[j]) - 254)
+            assert y[i, j] == want and S[i, j] == abs(want)
+
+
+def test_within_tolerance_underflow_term():
+    """R30: with groups = g the bound gains g * 2^-150 (absolute); without it
+    a zero reference demands an exact zero, and anything beyond the bound is
+    rejected."""
+    zero = np.zeros((1, 1))
+    tiny = np.array([[2.0 ** -150]])
+    assert not oracle.within_tolerance(tiny, zero, zero, 1e-5)[0]
+    assert oracle.within_tolerance(tiny, zero, zero, 1e-5, groups=1)[0]
+    assert not oracle.within_tolerance(2 * tiny, zero, zero, 1e-5, groups=1)[0]
+    assert oracle.within_tolerance(4 * tiny, zero, zero, 1e-5, groups=4)[0]
+    ref, S = np.array([[1.0]]), np.array([[1.0]])
+    assert oracle.within_tolerance(ref + 0.9e-5, ref, S, 1e-5, groups=8)[0]
+    assert not oracle.within_tolerance(ref + 1.1e-5, ref, S, 1e-5, groups=8)[0]
+
+
 def test_round_bf16_matches_torch_and_breaks_ties_to_even():
     import torch
     rng = np.random.default_rng(11)
