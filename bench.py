@@ -579,9 +579,13 @@ def main():
     ys = [torch.empty((M, y_cols), dtype=y_dtype, device=dev) for _ in range(R)]
     need = L.macaq_linear_workspace_bytes(M, N, K, E, flags)
     ws_buf = torch.zeros(max(need, 256), dtype=torch.uint8, device=dev)
-    a_codes = ws_buf[: M * K // 2]
+    # the linear call's staging of the activation: tiled (whole 32-row blocks)
+    # for a dense layer with tiled weights, else row-major
+    a_tiled = tiled and E == 1
+    stage_rows = -(-M // 32) * 32 if a_tiled else M
+    a_codes = ws_buf[: stage_rows * K // 2]
     fused = L.macaq_linear_path(M, N, K, E, flags) == mx.PATH_FUSED
-    a_scales = ws_buf[(M * K // 2 + 255) // 256 * 256:]
+    a_scales = ws_buf[(stage_rows * K // 2 + 255) // 256 * 256:]
     gemm_ws = torch.zeros(max(int(L.macaq_gemm_workspace_bytes(M, N, K, E)), 256), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream(dev)
     sp = ctypes.c_void_p(stream.cuda_stream)
@@ -625,14 +629,21 @@ def main():
     # macaq_linear makes on that path)
     def act_only(i):
         xp = step_args(i)[0]
-        if mx.macaq_quant_act(xp, xdt, p(s0.data_ptr()), off_p, E, M, K, p(a_codes.data_ptr()),
-                              p(a_scales.data_ptr()), sp) != 0:
+        if a_tiled:
+            st = mx.macaq_quant_act_tiled(xp, xdt, p(s0.data_ptr()), M, K, p(a_codes.data_ptr()),
+                                          p(a_scales.data_ptr()), sp)
+        else:
+            st = mx.macaq_quant_act(xp, xdt, p(s0.data_ptr()), off_p, E, M, K, p(a_codes.data_ptr()),
+                                    p(a_scales.data_ptr()), sp)
+        if st != 0:
             raise RuntimeError(mx.lib().macaq_last_error().decode())
+
+    gemm_layout = gemm_epi | (mx.A_TILED if a_tiled else 0)
 
     def gemm_only(i):
         _, wcp, wsp, yp = step_args(i)
         if mx.macaq_gemm_ex(p(a_codes.data_ptr()), p(a_scales.data_ptr()), off_p, E, wcp, wsp, M, N, K, yp, ydt,
-                            gemm_epi, p(gemm_ws.data_ptr()), gemm_ws.numel(), sp) != 0:
+                            gemm_layout, p(gemm_ws.data_ptr()), gemm_ws.numel(), sp) != 0:
             raise RuntimeError(mx.lib().macaq_last_error().decode())
 
     def kernel_us(fn):
@@ -676,6 +687,7 @@ def main():
         "config": {"workload": desc, "M": M, "N": N, "K": K, "experts": E, "x_dtype": str(x0.dtype).split(".")[-1],
                    "path": "fused" if fused else "unfused", "replicas": R,
                    "w_layout": "tiled" if tiled else "row-major",
+                   "act_staging": "tiled" if a_tiled else ("none (fused)" if fused else "row-major"),
                    "y": f"{args.out} [{M}][{y_cols}]" + (" swiglu" if epi == mx.EPI_SWIGLU else ""),
                    "scale_rule": {"smooth": "s = 1/sigma", "literal": "s = sigma"}[args.scale_rule],
                    "parallelism": "none (one GPU)"},
@@ -714,8 +726,12 @@ def main():
         out["roofline"].update({"us": round(gemm_us, 2), "roofline_us": {"mfma": round(t_mfma, 2), "hbm": round(t_hbm, 2)},
                                 "traffic": traffic_record(f"{args.workload}:gemm{out_key}")})
     if not args.no_ablation and not fused:
+        # both sides row-major activation codes into the same GEMM kernel:
+        # the comparison isolates the transform against the plain quantizer
+        rm_codes = ws_buf[: M * K // 2]
+        rm_scales = ws_buf[(M * K // 2 + 255) // 256 * 256:]
         out["transform_overhead"] = transform_overhead(args, mx, L, wl, xs, wss, wcs, ys, s0, off_p, stream, sp,
-                                                       a_codes, a_scales, gemm_ws, M, N, K, E, R, ydt, gemm_epi,
+                                                       rm_codes, rm_scales, gemm_ws, M, N, K, E, R, ydt, gemm_epi,
                                                        tiled=tiled)
     out["gpu_state"] = {"before": state_before, "after": state_after}
     if not args.no_cpu_baseline:

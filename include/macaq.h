@@ -111,6 +111,12 @@ enum {
  * argument of macaq_gemm_ex. */
 #define MACAQ_W_TILED 0x100u
 
+/* Layout bit: a_codes / a_scales of macaq_gemm_ex are in the tiled layout
+ * (the layout of macaq_tile_weights applied to the activation rows, as
+ * macaq_quant_act_tiled writes it).  OR'ed into the epilogue argument of
+ * macaq_gemm_ex together with MACAQ_W_TILED; dense layers only (E == 1). */
+#define MACAQ_A_TILED 0x200u
+
 /* Knobs of macaq_set_tuning.  Value 0 of every knob is the library's own
  * choice; other values force one kernel variant:
  *   MACAQ_TUNE_GEMM_TILE          prefill / grouped GEMM block tile:
@@ -268,6 +274,24 @@ int macaq_quant_act(const void* x, macaq_dtype x_dtype, const float* s,
                     uint8_t* a_codes, uint8_t* a_scales, void* stream);
 
 /*
+ * macaq_quant_act for a dense layer (one expert) with the codes and scales
+ * in the tiled layout that the prefill GEMM copies with contiguous reads: per
+ * 32-row block b and 256-wide K-tile t, 4096 bytes of codes at
+ * (b * K/256 + t) * 4096, row r of the block at 128 r with its 16-byte chunk
+ * c (32 values) at position c ^ ((r >> 1) & 7), and 256 bytes of scales at
+ * (b * K/256 + t) * 256, row r's 8 bytes at 8 r.  The same codes and scale
+ * bytes as macaq_quant_act, in other places.  The macaq_linear unfused path
+ * of a dense layer with tiled weights stages its activation this way.
+ *   x [M][K] in x_dtype; s [K] fp32;
+ *   a_codes: ceil(M/32) * 32 * K/2 bytes out; a_scales: ceil(M/32) * 32 *
+ *   K/32 bytes out (the rows past M of the last block are not written).
+ * Requires M >= 0, K % 256 == 0 (MACAQ_ERR_UNSUPPORTED otherwise), x and
+ * a_codes 16-byte aligned.  M == 0 is a no-op.
+ */
+int macaq_quant_act_tiled(const void* x, macaq_dtype x_dtype, const float* s, int64_t M, int64_t K,
+                          uint8_t* a_codes, uint8_t* a_scales, void* stream);
+
+/*
  * MXFP4 x MXFP4 GEMM y = A' W'^T per expert ("Quantization mechanism": the
  * FP4 matrix multiplication; "华为开源MACaQ:本地量化提速3倍", section
  * "现在还不能把它当成通用量化工厂": dense and grouped W4A4 matmul).
@@ -373,6 +397,8 @@ int macaq_linear_noalloc(const void* x, macaq_dtype x_dtype, const float* s,
  *   weight row 2j is the gate and row 2j+1 the up projection of output
  *   column j; y [M][N/2] = silu(g) * u with g, u the fp32 results of those
  *   rows and silu(g) = g / (1 + exp(-g)) in fp32 (expf, IEEE division).
+ * The epilogue argument of macaq_gemm_ex also carries the layout bits
+ * MACAQ_W_TILED and MACAQ_A_TILED (the latter only with the former, E == 1).
  * Other arguments, rules and errors as macaq_gemm / macaq_linear; y must be
  * aligned to its element size.  macaq_gemm and macaq_linear are these calls
  * with MACAQ_F32 and MACAQ_EPI_NONE.

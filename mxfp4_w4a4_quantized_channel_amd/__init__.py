@@ -23,7 +23,7 @@ __all__ = [
     "prepare_weights", "quant_act", "gemm", "linear", "linear_workspace_bytes",
     "encode_e2m1", "quant_mxfp4", "version", "library_path", "EPI_NONE", "EPI_SWIGLU",
     "hessian", "prepare_weights_hessian", "flip_refine", "flip_refine_workspace_bytes",
-    "set_tuning", "linear_noalloc", "NOALLOC_SCRATCH_BYTES", "TUNE_GEMM_TILE", "TUNE_GEMM_GROUP_M",
+    "set_tuning", "linear_noalloc", "quant_act_tiled", "A_TILED", "W_TILED", "NOALLOC_SCRATCH_BYTES", "TUNE_GEMM_TILE", "TUNE_GEMM_GROUP_M",
     "TUNE_ACT_ROWS_PER_WAVE", "TUNE_ACT_SHARED_S",
     "TUNE_DECODE_WAVES", "TUNE_DECODE_STAGES", "TUNE_DECODE_ROWS", "GEMM_TILES",
 ]
@@ -35,6 +35,7 @@ BF16, F32 = 0, 1
 PATH_AUTO, PATH_FUSED, PATH_UNFUSED = 0, 1, 2
 EPI_NONE, EPI_SWIGLU = 0, 1
 NOALLOC_SCRATCH_BYTES = 32 << 20   # static staging of macaq_linear_noalloc, per device
+A_TILED = 0x200   # activation codes in the tiled layout (gemm's epilogue argument, with W_TILED, E == 1)
 W_TILED = 0x100   # weights in macaq_tile_weights' layout (OR into linear's flags / gemm's epilogue)
 # knobs of macaq_set_tuning (0 = the library's own choice)
 (TUNE_GEMM_TILE, TUNE_GEMM_GROUP_M, TUNE_ACT_ROWS_PER_WAVE, TUNE_ACT_SHARED_S, TUNE_DECODE_WAVES,
@@ -73,6 +74,7 @@ def _load():
         "macaq_quant_act": (ci, [vp, ci, vp, vp, i64, i64, i64, vp, vp, vp]),
         "macaq_gemm": (ci, [vp, vp, vp, i64, vp, vp, i64, i64, i64, vp, vp, sz, vp]),
         "macaq_quant_act_bytes": (sz, [i64, i64]),
+        "macaq_quant_act_tiled": (ci, [vp, ci, vp, i64, i64, vp, vp, vp]),
         "macaq_gemm_workspace_bytes": (sz, [i64, i64, i64, i64]),
         "macaq_linear_workspace_bytes": (sz, [i64, i64, i64, i64, u32]),
         "macaq_linear_path": (ci, [i64, i64, i64, i64, u32]),
@@ -296,6 +298,24 @@ def quant_act(x: torch.Tensor, s: torch.Tensor, offsets: torch.Tensor | None = N
     return codes, scales
 
 
+def quant_act_tiled(x: torch.Tensor, s: torch.Tensor):
+    """quant_act of a dense layer in the tiled layout the prefill GEMM reads
+    -> (codes [ceil(M/32)*32*K/2] uint8, scales [ceil(M/32)*32*K/32] uint8),
+    flat.  Use with gemm(..., epilogue=W_TILED | A_TILED)."""
+    _load()
+    if s.dim() == 1:
+        s = s[None]
+    _need(x, "x", dim=2)
+    _need(s, "s", torch.float32, 2)
+    M, K = x.shape
+    rows = (M + 31) // 32 * 32
+    codes = torch.empty(rows * K // 2, dtype=torch.uint8, device=x.device)
+    scales = torch.empty(rows * K // 32, dtype=torch.uint8, device=x.device)
+    _check(macaq_quant_act_tiled(_ptr(x), _dtype_code(x), _ptr(s), M, K, _ptr(codes), _ptr(scales),
+                                 _stream(x.device)), "macaq_quant_act_tiled")
+    return codes, scales
+
+
 def _w_shape(w_codes, w_scales):
     if w_codes.dim() == 2:
         w_codes, w_scales = w_codes[None], w_scales[None]
@@ -307,7 +327,7 @@ def _w_shape(w_codes, w_scales):
 def _out(M, N, out_dtype, epilogue, device, out):
     if out_dtype not in (torch.float32, torch.bfloat16):
         raise TypeError(f"out_dtype must be float32 or bfloat16, got {out_dtype}")
-    width = N // 2 if (epilogue & ~W_TILED) == EPI_SWIGLU else N
+    width = N // 2 if (epilogue & ~(W_TILED | A_TILED)) == EPI_SWIGLU else N
     if out is None:
         return torch.empty((M, width), dtype=out_dtype, device=device)
     _need(out, "out", out_dtype, 2)
@@ -317,17 +337,28 @@ def _out(M, N, out_dtype, epilogue, device, out):
 
 
 def gemm(a_codes, a_scales, w_codes, w_scales, offsets=None, out=None, workspace=None,
-         out_dtype=torch.float32, epilogue=EPI_NONE):
+         out_dtype=torch.float32, epilogue=EPI_NONE, M=None):
     """y = A' W'^T from MXFP4 operands: [M, N] (or [M, N/2] with EPI_SWIGLU)
     in out_dtype (float32 or bfloat16).  A workspace, when one is needed, is
-    zero-filled here; a caller-provided one must start zeroed."""
+    zero-filled here; a caller-provided one must start zeroed.  With A_TILED
+    in the epilogue argument, a_codes / a_scales are quant_act_tiled's flat
+    buffers and M must be given."""
     _load()
     w_codes, w_scales = _w_shape(w_codes, w_scales)
-    _need(a_codes, "a_codes", torch.uint8, 2)
-    _need(a_scales, "a_scales", torch.uint8, 2)
     E, N, KH = w_codes.shape
-    M = a_codes.shape[0]
     K = 2 * KH
+    if epilogue & A_TILED:
+        _need(a_codes, "a_codes", torch.uint8, 1)
+        _need(a_scales, "a_scales", torch.uint8, 1)
+        if M is None:
+            raise ValueError("M is needed with tiled activation codes")
+        rows = (M + 31) // 32 * 32
+        if a_codes.numel() < rows * K // 2 or a_scales.numel() < rows * K // 32:
+            raise ValueError("tiled activation buffers too small")
+    else:
+        _need(a_codes, "a_codes", torch.uint8, 2)
+        _need(a_scales, "a_scales", torch.uint8, 2)
+        M = a_codes.shape[0]
     y = _out(M, N, out_dtype, epilogue, a_codes.device, out)
     need = int(_load().macaq_gemm_workspace_bytes(M, N, K, E))
     if workspace is None and need > 0:

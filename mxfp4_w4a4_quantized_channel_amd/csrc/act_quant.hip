@@ -194,7 +194,12 @@ __device__ __forceinline__ void wait_row_blocks(int later) {
   else wait_vmcnt<0>();
 }
 
-template <int EB, bool RECIP, bool PLAIN = false, bool SHARED = false>
+// TILED: codes and scales in the tiled layout the prefill GEMM copies with
+// contiguous 1 KiB reads (macaq_tile_weights' layout, applied to the
+// activation rows): per 32-row block and 256-wide K-tile, 4 KiB of codes
+// (row r at 128 r, group chunk c at position c ^ ((r >> 1) & 7)) and 256
+// bytes of scales (row r's 8 bytes at 8 r).  K % 256 == 0.
+template <int EB, bool RECIP, bool PLAIN = false, bool SHARED = false, bool TILED = false>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(SHARED && EB == 2 && !RECIP ? 4 : (EB == 2 ? 3 : 2))))
 void act_quant_lane_kernel(
     const void* __restrict__ x, const float* __restrict__ s, const int32_t* __restrict__ offsets, int E,
@@ -417,8 +422,15 @@ void act_quant_lane_kernel(
       quantize_group(t, &cw, &b);
     }
     if (active) {
-      *reinterpret_cast<uint4*>(codes + r * (K >> 1) + g * 16) = cw;
-      scales[r * KG + g] = (uint8_t)b;
+      if constexpr (TILED) {
+        const int64_t blk = (r >> 5) * (K >> 8) + (g >> 3);
+        const int rr = (int)(r & 31), c = (int)(g & 7);
+        *reinterpret_cast<uint4*>(codes + blk * 4096 + rr * 128 + ((c ^ ((rr >> 1) & 7)) << 4)) = cw;
+        scales[blk * 256 + rr * 8 + c] = (uint8_t)b;
+      } else {
+        *reinterpret_cast<uint4*>(codes + r * (K >> 1) + g * 16) = cw;
+        scales[r * KG + g] = (uint8_t)b;
+      }
     }
   }
 }
@@ -476,16 +488,16 @@ static ActLaunch act_launch(int64_t M, int64_t K, bool plain) {
   return a;
 }
 
-template <int EB, bool RECIP>
+template <int EB, bool RECIP, bool TILED = false>
 static void launch_act_t(const ActLaunch& a, const void* x, const float* s, const int32_t* offsets, int E,
                          int64_t rows_per_expert, int64_t M, int64_t K, uint8_t* codes, uint8_t* scales,
                          hipStream_t stream) {
   if (a.shared)
-    act_quant_lane_kernel<EB, RECIP, false, true><<<a.grid, dim3(256), act_lds_bytes<EB, true>(),
-                                                    stream>>>(x, s, offsets, E, rows_per_expert, M, K, codes, scales,
-                                                              a.gs_log2, a.steps);
+    act_quant_lane_kernel<EB, RECIP, false, true, TILED><<<a.grid, dim3(256), act_lds_bytes<EB, true>(),
+                                                           stream>>>(x, s, offsets, E, rows_per_expert, M, K, codes,
+                                                                     scales, a.gs_log2, a.steps);
   else
-    act_quant_lane_kernel<EB, RECIP, false, false><<<a.grid, dim3(256), act_lds_bytes<EB, false>(), stream>>>(
+    act_quant_lane_kernel<EB, RECIP, false, false, TILED><<<a.grid, dim3(256), act_lds_bytes<EB, false>(), stream>>>(
         x, s, offsets, E, rows_per_expert, M, K, codes, scales, a.gs_log2, a.steps);
 }
 
@@ -501,6 +513,18 @@ hipError_t launch_act_quant(const void* x, bool x_f32, bool reciprocal, const fl
     if (reciprocal) launch_act_t<2, true>(a, x, s, offsets, E, rows_per_expert, M, K, codes, scales, stream);
     else launch_act_t<2, false>(a, x, s, offsets, E, rows_per_expert, M, K, codes, scales, stream);
   }
+  return hipGetLastError();
+}
+
+// The online transform of a dense layer (one expert) with its output in the
+// tiled layout of the prefill GEMM (K % 256 == 0).  The codes and scales
+// hold ceil(M / 32) * 32 rows; the rows past M are not written.
+hipError_t launch_act_quant_tiled(const void* x, bool x_f32, const float* s, int64_t M, int64_t K, uint8_t* codes,
+                                  uint8_t* scales, hipStream_t stream) {
+  if (M <= 0) return hipSuccess;
+  const ActLaunch a = act_launch(M, K, false);
+  if (x_f32) launch_act_t<4, false, true>(a, x, s, nullptr, 1, 0, M, K, codes, scales, stream);
+  else launch_act_t<2, false, true>(a, x, s, nullptr, 1, 0, M, K, codes, scales, stream);
   return hipGetLastError();
 }
 

@@ -43,8 +43,10 @@ hipError_t launch_flip_rounds(const float* H, int E, int64_t row0, int64_t rows,
 hipError_t launch_decode_gemm(const uint8_t* A, const uint8_t* As, const uint8_t* W, const uint8_t* Ws, int64_t M,
                               int64_t N, int64_t K, void* Y, int mode, hipStream_t stream);
 hipError_t launch_gemm_tiled(const uint8_t* A, const uint8_t* As, const int32_t* offsets, int E, const uint8_t* B,
-                             const uint8_t* Bs, int64_t M, int64_t N, int64_t K, void* Y, int mode,
+                             const uint8_t* Bs, int64_t M, int64_t N, int64_t K, void* Y, int mode, bool a_tiled,
                              hipStream_t stream);
+hipError_t launch_act_quant_tiled(const void* x, bool x_f32, const float* s, int64_t M, int64_t K, uint8_t* codes,
+                                  uint8_t* scales, hipStream_t stream);
 hipError_t launch_tile_weights(const uint8_t* wc, const uint8_t* ws, int64_t E, int64_t N, int64_t K, uint8_t* tc,
                                uint8_t* ts, hipStream_t stream);
 // output mode bits of the GEMM kernels (mx_common.h)
@@ -305,6 +307,25 @@ int macaq_quant_act(const void* x, macaq_dtype x_dtype, const float* s, const in
                            fn));
 }
 
+int macaq_quant_act_tiled(const void* x, macaq_dtype x_dtype, const float* s, int64_t M, int64_t K, uint8_t* a_codes,
+                          uint8_t* a_scales, void* stream) {
+  const char* fn = "macaq_quant_act_tiled";
+  if (int st = check_dtype(x_dtype, fn)) return st;
+  if (M < 0) return fail(MACAQ_ERR_INVALID_ARG, std::string(fn) + ": need M >= 0");
+  if (int st = check_k(K, fn)) return st;
+  if (K % 256 != 0) return fail(MACAQ_ERR_UNSUPPORTED, std::string(fn) + ": the tiled layout needs K % 256 == 0");
+  if (M == 0) return MACAQ_OK;
+  if (!x || !s || !a_codes || !a_scales) return fail(MACAQ_ERR_INVALID_ARG, std::string(fn) + ": null pointer");
+  if (!aligned(x, 16) || !aligned(a_codes, 16) || !aligned(s, 16))
+    return fail(MACAQ_ERR_INVALID_ARG, std::string(fn) + ": x, s and a_codes must be 16-byte aligned");
+  if (int st = check_device()) return st;
+  if (int st = check_inputs(fn, (hipStream_t)stream, nullptr, 1, M, s, K)) return st;
+  return finish(fn, (hipStream_t)stream,
+                hip_status(macaq::launch_act_quant_tiled(x, x_dtype == MACAQ_F32, s, M, K, a_codes, a_scales,
+                                                         (hipStream_t)stream),
+                           fn));
+}
+
 size_t macaq_quant_act_bytes(int64_t M, int64_t K) {
   if (M <= 0 || K <= 0) return 0;
   return round_up((size_t)M * (size_t)K / 2, 256) + round_up((size_t)M * (size_t)K / 32, 256);
@@ -324,22 +345,44 @@ int macaq_linear_path(int64_t M, int64_t N, int64_t K, int64_t E, uint32_t flags
   return (macaq::linear_fused_supported(M, N, K, E) && M <= kMaxFusedM) ? MACAQ_PATH_FUSED : MACAQ_PATH_UNFUSED;
 }
 
+}  // extern "C"
+
+namespace {
+// The unfused path of a dense layer with tiled weights stages the activation
+// in the same tiled layout (whole 32-row blocks); every other unfused path
+// stages it row-major.
+bool stage_tiled(int64_t E, uint32_t flags) { return E == 1 && (flags & MACAQ_W_TILED) != 0; }
+
+// Staging of the activation codes and scales: their bytes, and where the
+// scales start.
+size_t stage_code_bytes(int64_t M, int64_t K, bool tiled) {
+  const int64_t rows = tiled ? (M + 31) / 32 * 32 : M;
+  return round_up((size_t)rows * (size_t)K / 2, 256);
+}
+size_t stage_bytes(int64_t M, int64_t K, bool tiled) {
+  const int64_t rows = tiled ? (M + 31) / 32 * 32 : M;
+  return stage_code_bytes(M, K, tiled) + round_up((size_t)rows * (size_t)K / 32, 256);
+}
+}  // namespace
+
+extern "C" {
+
 size_t macaq_linear_workspace_bytes(int64_t M, int64_t N, int64_t K, int64_t E, uint32_t flags) {
   if (M <= 0 || N <= 0 || K <= 0 || E <= 0) return 0;   // (MACAQ_W_TILED: the unfused path's workspace)
   const int path = macaq_linear_path(M, N, K, E, flags);
   if (path == MACAQ_PATH_FUSED) return 0;
-  if (path == MACAQ_PATH_UNFUSED) return macaq_quant_act_bytes(M, K) + macaq_gemm_workspace_bytes(M, N, K, E);
+  if (path == MACAQ_PATH_UNFUSED) return stage_bytes(M, K, stage_tiled(E, flags)) + macaq_gemm_workspace_bytes(M, N, K, E);
   return 0;
 }
 
 namespace {
 int run_gemm(const uint8_t* a_codes, const uint8_t* a_scales, const int32_t* expert_offsets, int64_t E,
              const uint8_t* w_codes, const uint8_t* w_scales, int64_t M, int64_t N, int64_t K, void* y, int mode,
-             void* workspace, hipStream_t stream, const char* fn, bool w_tiled = false) {
+             void* workspace, hipStream_t stream, const char* fn, bool w_tiled = false, bool a_tiled = false) {
   (void)workspace;
   if (w_tiled)
     return hip_status(macaq::launch_gemm_tiled(a_codes, a_scales, E > 1 ? expert_offsets : nullptr, (int)E, w_codes,
-                                               w_scales, M, N, K, y, mode, stream),
+                                               w_scales, M, N, K, y, mode, a_tiled, stream),
                       fn);
   if (macaq::decode_supported(M, N, K, E))
     return hip_status(macaq::launch_decode_gemm(a_codes, a_scales, w_codes, w_scales, M, N, K, y, mode, stream), fn);
@@ -364,7 +407,10 @@ int macaq_gemm_ex(const uint8_t* a_codes, const uint8_t* a_scales, const int32_t
                   macaq_dtype y_dtype, uint32_t epilogue, void* workspace, size_t workspace_bytes, void* stream) {
   const char* fn = "macaq_gemm";
   const bool w_tiled = (epilogue & MACAQ_W_TILED) != 0;
-  epilogue &= ~MACAQ_W_TILED;
+  const bool a_tiled = (epilogue & MACAQ_A_TILED) != 0;
+  epilogue &= ~(MACAQ_W_TILED | MACAQ_A_TILED);
+  if (a_tiled && (!w_tiled || E != 1))
+    return fail(MACAQ_ERR_UNSUPPORTED, std::string(fn) + ": tiled activations need tiled weights and E == 1");
   if (int st = validate_gemm(a_codes, a_scales, expert_offsets, E, w_codes, w_scales, M, N, K, y, fn)) return st;
   int mode = 0;
   if (int st = output_mode(y_dtype, epilogue, N, y, fn, &mode)) return st;
@@ -376,7 +422,7 @@ int macaq_gemm_ex(const uint8_t* a_codes, const uint8_t* a_scales, const int32_t
   if (int st = check_inputs(fn, (hipStream_t)stream, expert_offsets, E, M, nullptr, 0)) return st;
   return finish(fn, (hipStream_t)stream,
                 run_gemm(a_codes, a_scales, expert_offsets, E, w_codes, w_scales, M, N, K, y, mode, workspace,
-                         (hipStream_t)stream, fn, w_tiled));
+                         (hipStream_t)stream, fn, w_tiled, a_tiled));
 }
 
 int macaq_gemm(const uint8_t* a_codes, const uint8_t* a_scales, const int32_t* expert_offsets, int64_t E,
@@ -469,17 +515,19 @@ int linear_impl(const void* x, macaq_dtype x_dtype, const float* s, const int32_
                   hip_status(macaq::launch_linear_fused(x, x_dtype == MACAQ_F32, s, w_codes, w_scales, M, N, K, y,
                                                         mode, st),
                              "macaq_linear (fused)"));
+  const bool a_tiled = stage_tiled(E, flags);
   uint8_t* a_codes = static_cast<uint8_t*>(workspace);
-  uint8_t* a_scales = a_codes + round_up((size_t)M * (size_t)K / 2, 256);
+  uint8_t* a_scales = a_codes + stage_code_bytes(M, K, a_tiled);
   const int32_t* off = E > 1 ? expert_offsets : nullptr;
-  if (int r = hip_status(macaq::launch_act_quant(x, x_dtype == MACAQ_F32, false, s, off, (int)E, 0, M, K,
-                                                 a_codes, a_scales, st),
+  if (int r = hip_status(a_tiled ? macaq::launch_act_quant_tiled(x, x_dtype == MACAQ_F32, s, M, K, a_codes, a_scales, st)
+                                 : macaq::launch_act_quant(x, x_dtype == MACAQ_F32, false, s, off, (int)E, 0, M, K,
+                                                           a_codes, a_scales, st),
                          "macaq_linear (transform)"))
     return r;
-  void* gemm_ws = static_cast<uint8_t*>(workspace) + macaq_quant_act_bytes(M, K);
+  void* gemm_ws = static_cast<uint8_t*>(workspace) + stage_bytes(M, K, a_tiled);
   return finish(fn, st,
                 run_gemm(a_codes, a_scales, off, E, w_codes, w_scales, M, N, K, y, mode, gemm_ws, st,
-                         "macaq_linear (gemm)", w_tiled));
+                         "macaq_linear (gemm)", w_tiled, a_tiled));
 }
 
 }  // namespace

@@ -5,13 +5,13 @@ namespace macaq {
 
 namespace {
 
-template <int BM, int BN, int WM, int WN, int BK, int S, int MINB, int OUT, bool BT>
+template <int BM, int BN, int WM, int WN, int BK, int S, int MINB, int OUT, bool BT, bool AT>
 hipError_t launch_pipe_out(const uint8_t* A, const uint8_t* As, const int32_t* offsets, int E, const uint8_t* B,
                            const uint8_t* Bs, int64_t M, int64_t N, int64_t K, void* Y, hipStream_t stream) {
   using L = PipeLayout<BM, BN, BK, 1>;
   constexpr int lds = S * L::kStage;
   static const hipError_t attr =
-      hipFuncSetAttribute((const void*)gemm_mxfp4_pipe_kernel<BM, BN, WM, WN, BK, S, MINB, OUT, BT>,
+      hipFuncSetAttribute((const void*)gemm_mxfp4_pipe_kernel<BM, BN, WM, WN, BK, S, MINB, OUT, BT, AT>,
                           hipFuncAttributeMaxDynamicSharedMemorySize, lds);
   if (attr != hipSuccess) return attr;
   const int tiles_n = (int)ceil_div(N, BN);
@@ -20,26 +20,28 @@ hipError_t launch_pipe_out(const uint8_t* A, const uint8_t* As, const int32_t* o
   const int64_t blocks = tiles_m * tiles_n;
   // tile rows per XCD group (blocks of a group share A and W' panels in one L2)
   const int group_m = tuning(MACAQ_TUNE_GEMM_GROUP_M) > 0 ? tuning(MACAQ_TUNE_GEMM_GROUP_M) : 4;
-  gemm_mxfp4_pipe_kernel<BM, BN, WM, WN, BK, S, MINB, OUT, BT>
+  gemm_mxfp4_pipe_kernel<BM, BN, WM, WN, BK, S, MINB, OUT, BT, AT>
       <<<dim3((unsigned)blocks), dim3(64 * WM * WN), lds, stream>>>(A, As, B, Bs, offsets, E, M, N, K, Y,
                                                                     (int)tiles_m, tiles_n, group_m);
   return hipGetLastError();
 }
 
 // output mode (run time) -> kernel instantiation
-template <int BM, int BN, int WM, int WN, int BK, int S, int MINB = 1, bool BT = false>
+template <int BM, int BN, int WM, int WN, int BK, int S, int MINB = 1, bool BT = false, bool AT = false>
 hipError_t launch_pipe(const uint8_t* A, const uint8_t* As, const int32_t* offsets, int E, const uint8_t* B,
                        const uint8_t* Bs, int64_t M, int64_t N, int64_t K, void* Y, int mode, hipStream_t stream) {
   switch (mode) {
-    case 0: return launch_pipe_out<BM, BN, WM, WN, BK, S, MINB, 0, BT>(A, As, offsets, E, B, Bs, M, N, K, Y, stream);
+    case 0:
+      return launch_pipe_out<BM, BN, WM, WN, BK, S, MINB, 0, BT, AT>(A, As, offsets, E, B, Bs, M, N, K, Y, stream);
     case kOutBf16:
-      return launch_pipe_out<BM, BN, WM, WN, BK, S, MINB, kOutBf16, BT>(A, As, offsets, E, B, Bs, M, N, K, Y, stream);
+      return launch_pipe_out<BM, BN, WM, WN, BK, S, MINB, kOutBf16, BT, AT>(A, As, offsets, E, B, Bs, M, N, K, Y,
+                                                                            stream);
     case kOutSwiGLU:
-      return launch_pipe_out<BM, BN, WM, WN, BK, S, MINB, kOutSwiGLU, BT>(A, As, offsets, E, B, Bs, M, N, K, Y,
-                                                                          stream);
+      return launch_pipe_out<BM, BN, WM, WN, BK, S, MINB, kOutSwiGLU, BT, AT>(A, As, offsets, E, B, Bs, M, N, K, Y,
+                                                                              stream);
     default:
-      return launch_pipe_out<BM, BN, WM, WN, BK, S, MINB, kOutBf16 | kOutSwiGLU, BT>(A, As, offsets, E, B, Bs, M, N,
-                                                                                      K, Y, stream);
+      return launch_pipe_out<BM, BN, WM, WN, BK, S, MINB, kOutBf16 | kOutSwiGLU, BT, AT>(A, As, offsets, E, B, Bs, M,
+                                                                                          N, K, Y, stream);
   }
 }
 
@@ -84,14 +86,23 @@ hipError_t launch_tile_weights(const uint8_t* wc, const uint8_t* ws, int64_t E, 
 // GEMM with W' in the tiled layout (N % 32 == 0, K % 256 == 0): 256x256 when
 // that gives about one tile per CU, else 128x128 with two blocks per CU
 // (with contiguous W' copies the smaller tile is faster than 256x128:
-// attn-proj 25.3 against 29.6 us on random operands).
+// attn-proj 25.3 against 29.6 us on random operands).  a_tiled: the
+// activation codes and scales are in the same tiled layout (dense only).
 hipError_t launch_gemm_tiled(const uint8_t* A, const uint8_t* As, const int32_t* offsets, int E, const uint8_t* B,
-                             const uint8_t* Bs, int64_t M, int64_t N, int64_t K, void* Y, int mode,
+                             const uint8_t* Bs, int64_t M, int64_t N, int64_t K, void* Y, int mode, bool a_tiled,
                              hipStream_t stream) {
   if (M <= 0) return hipSuccess;
+  if (a_tiled && offsets != nullptr) return hipErrorInvalidValue;
   const int64_t t256 = ceil_div(M, 256) * ceil_div(N, 256);
   int choice = (offsets == nullptr && t256 >= 240) ? 0 : 2;
   if (const int force = tuning(MACAQ_TUNE_GEMM_TILE)) choice = force - 1;
+  if (a_tiled) {
+    switch (choice) {
+      case 0: return launch_pipe<256, 256, 2, 2, 256, 2, 1, true, true>(A, As, offsets, E, B, Bs, M, N, K, Y, mode, stream);
+      case 1: return launch_pipe<256, 128, 2, 2, 256, 2, 1, true, true>(A, As, offsets, E, B, Bs, M, N, K, Y, mode, stream);
+      default: return launch_pipe<128, 128, 2, 2, 256, 2, 2, true, true>(A, As, offsets, E, B, Bs, M, N, K, Y, mode, stream);
+    }
+  }
   switch (choice) {
     case 0: return launch_pipe<256, 256, 2, 2, 256, 2, 1, true>(A, As, offsets, E, B, Bs, M, N, K, Y, mode, stream);
     case 1: return launch_pipe<256, 128, 2, 2, 256, 2, 1, true>(A, As, offsets, E, B, Bs, M, N, K, Y, mode, stream);

@@ -30,6 +30,8 @@
 // expert's tiles exit at once.
 #pragma once
 
+#include <type_traits>
+
 #include "mx_common.h"
 
 namespace macaq {
@@ -66,18 +68,6 @@ struct GemmTile {
   static_assert(kTM % 32 == 0 && kTN % 32 == 0, "wave tile must be a multiple of 32");
   static_assert(BM * 8 % kThreads == 0 && BN * 8 % kThreads == 0, "chunks must divide evenly");
 };
-
-template <int J, int FM, int FN>
-__device__ __forceinline__ void mfma_substep(v16f (&acc)[FM][FN], const uint4 (&fa)[FM],
-                                             const uint4 (&fb)[FN], const uint32_t (&sa)[FM],
-                                             const uint32_t (&sb)[FN]) {
-#pragma unroll
-  for (int mi = 0; mi < FM; ++mi)
-#pragma unroll
-    for (int ni = 0; ni < FN; ++ni)
-      acc[mi][ni] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-          as_operand(fa[mi]), as_operand(fb[ni]), acc[mi][ni], 4, 4, J, (int)sa[mi], J, (int)sb[ni]);
-}
 
 // fp32 epilogue of a wave's FM x FN block of 32x32 accumulators whose first
 // row is m0 and first column n0 (rows below row_end and columns below N are
@@ -214,14 +204,21 @@ __device__ __forceinline__ void store_wave_tile_lds(const v16f (&acc)[FM][FN], f
 }
 
 // ---------------------------------------------------------------------------
-// Pipelined variant: a ring of STAGES LDS buffers of K-tiles of BK (128 or
+// Pipelined kernel: a ring of STAGES LDS buffers of K-tiles of BK (128 or
 // 256) filled by direct-to-LDS copies issued with inline assembly.  The
 // copies have no register results; their completion is tracked explicitly
-// with s_waitcnt vmcnt(n), so up to STAGES-1 K-tiles are in flight while a
-// tile is consumed (the builtin form makes the compiler wait for every
-// outstanding copy before any LDS read, which serializes the ring).  One
-// s_barrier per K-tile both publishes the newest tile and retires the buffer
-// the next copy overwrites.
+// with s_waitcnt vmcnt(n) (the builtin form makes the compiler wait for
+// every outstanding copy before any LDS read, which serializes the ring).
+//
+// Schedule of a K-tile (NSUB = BK/64 MFMA sub-steps): the MFMAs of sub-step
+// j run while the fragments of sub-step j+1 are read from LDS into a second
+// register set.  In the last sub-step every wave already holds its
+// fragments, so the stage is free: the wave waits for the next tile's
+// copies, meets the others at the one barrier of the tile, issues the copy
+// of tile kt+STAGES into the freed stage and reads the next tile's scales
+// and first fragments, all interleaved with that sub-step's MFMAs.  Past the
+// last tile the freed stages receive copies of the last tile again, so that
+// every wait counts the same number of outstanding copies.
 //
 // LDS row of a K-tile: BK/2 bytes = CPR chunks of 16 bytes (CPR = BK/32
 // groups); chunk c of row r sits at position c ^ f(r), f(r) = (r / (8/CPR))
@@ -326,8 +323,34 @@ __device__ __forceinline__ bool grouped_tile(const int32_t* __restrict__ offsets
 // stored in the XOR-swizzled order the LDS tile uses) and 256 bytes of
 // scales.  A copy instruction then reads 1 KiB of contiguous codes (and a
 // scale copy 256 contiguous bytes) instead of 8 (32) rows' pieces: measured
-// 56 against 33 B/clk per CU for such copies in isolation.
-template <int BM, int BN, int WAVES_M, int WAVES_N, int BK, int STAGES, int MINB = 1, int OUT = 0, bool BT = false>
+// 56 against 33 B/clk per CU for such copies in isolation.  AT: the
+// activation codes and scales in the same tiled layout (dense layers only:
+// row tiles start at multiples of 32).
+
+// The MFMAs of one sub-step, J the sub-step (op_sel picks scale byte J).
+template <int J, int FM, int FN>
+__device__ __forceinline__ void mfma_substep_t(v16f (&acc)[FM][FN], const uint4 (&fa)[FM], const uint4 (&fb)[FN],
+                                               const uint32_t (&sa)[FM], const uint32_t (&sb)[FN]) {
+#pragma unroll
+  for (int mi = 0; mi < FM; ++mi)
+#pragma unroll
+    for (int ni = 0; ni < FN; ++ni)
+      acc[mi][ni] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(as_operand(fa[mi]), as_operand(fb[ni]), acc[mi][ni],
+                                                                     4, 4, J, (int)sa[mi], J, (int)sb[ni]);
+}
+
+// Calls f(std::integral_constant<int, I>) for I = 0 .. N-1 (compile-time
+// indices for op_sel and register-set selection).
+template <int N, typename F, int I = 0>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (I < N) {
+    f(std::integral_constant<int, I>{});
+    static_for<N, F, I + 1>(static_cast<F&&>(f));
+  }
+}
+
+template <int BM, int BN, int WAVES_M, int WAVES_N, int BK, int STAGES, int MINB = 1, int OUT = 0, bool BT = false,
+          bool AT = false>
 __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, MINB) void gemm_mxfp4_pipe_kernel(
     const uint8_t* __restrict__ A, const uint8_t* __restrict__ As, const uint8_t* __restrict__ B,
     const uint8_t* __restrict__ Bs, const int32_t* __restrict__ offsets, int E, int64_t M,
@@ -336,6 +359,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, MINB) void gemm_mxfp4_pipe_
   using L = PipeLayout<BM, BN, BK, 1>;
   constexpr int kWaves = WAVES_M * WAVES_N;
   constexpr int kCPR = L::kCPR;
+  constexpr int NSUB = kCPR / 2;   // MFMA sub-steps per K-tile
   // Copies per wave per K-tile.  When a stage's blocks do not split evenly
   // over the waves, the last waves repeat blocks of the first ones (identical
   // bytes to the same LDS place), so every wave issues the same number of
@@ -344,7 +368,8 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, MINB) void gemm_mxfp4_pipe_
   constexpr int kSB = (L::kScaleBlocks + kWaves - 1) / kWaves;
   constexpr int kLPT = kCB + kSB;
   static_assert((STAGES - 2) * kLPT < 64, "vmcnt range");
-  static_assert(!BT || BK == 256, "the tiled W' layout has 256-wide K-tiles");
+  static_assert(!(BT || AT) || BK == 256, "the tiled layouts have 256-wide K-tiles");
+  static_assert(NSUB % 2 == 0, "an even number of sub-steps per K-tile");
   extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];
 
   // ---- tile -> (expert, rows, columns).  Grouped: the active row tiles are
@@ -380,13 +405,13 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, MINB) void gemm_mxfp4_pipe_
   const uint32_t lds_base = (uint32_t)(uintptr_t)smem;
 
   // ---- per-lane copy sources for K-tile 0 (advance by BK/2 code bytes and
-  // CPR scale bytes per K-tile; tiled W' by 4 KiB and 256 bytes) and
-  // wave-uniform LDS offsets within a stage.  Tiled W' rows sit at (row / 32,
+  // CPR scale bytes per K-tile; tiled operands by 4 KiB and 256 bytes) and
+  // wave-uniform LDS offsets within a stage.  Tiled rows sit at (row / 32,
   // K-tile, row % 32) with their chunks already in the LDS order, so the
   // lanes read them in memory order (tile rows start at multiples of 32, so a
   // row's swizzle in the LDS tile equals its swizzle in memory).
   const uint8_t* csrc[kCB];
-  uint32_t ctile = 0, stile = 0;   // copies of tiled W' (wave-uniform bits)
+  uint32_t ctile = 0, stile = 0;   // copies of tiled operands (wave-uniform bits)
 #pragma unroll
   for (int i = 0; i < kCB; ++i) {
     const int blk = (wave * kCB + i) % L::kCodeBlocks;
@@ -396,7 +421,12 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, MINB) void gemm_mxfp4_pipe_
     if (row < BM) {
       int64_t gr = row_begin + row;
       if (gr >= row_end) gr = row_end - 1;
-      csrc[i] = A + gr * KB + c * 16;
+      if constexpr (AT) {
+        csrc[i] = A + (gr >> 5) * (K >> 8) * 4096 + (gr & 31) * 128 + (lane % kCPR) * 16;
+        ctile |= 1u << i;
+      } else {
+        csrc[i] = A + gr * KB + c * 16;
+      }
     } else {
       int64_t gn = n0 + (row - BM);
       if (gn >= N) gn = N - 1;
@@ -417,7 +447,12 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, MINB) void gemm_mxfp4_pipe_
     if (row < BM) {
       int64_t gr = row_begin + row;
       if (gr >= row_end) gr = row_end - 1;
-      ssrc[i] = As + gr * KG + part * 4;
+      if constexpr (AT) {
+        ssrc[i] = As + (gr >> 5) * (K >> 8) * 256 + (gr & 31) * 8 + part * 4;
+        stile |= 1u << i;
+      } else {
+        ssrc[i] = As + gr * KG + part * 4;
+      }
     } else {
       int64_t gn = n0 + (row - BM);
       if (gn >= N) gn = N - 1;
@@ -453,9 +488,10 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, MINB) void gemm_mxfp4_pipe_
       for (int r = 0; r < 16; ++r) acc[mi][ni][r] = 0.0f;
 
   const int nk = (int)(K / BK);
+  // prologue: every stage receives a tile (the last tile again where there
+  // are fewer tiles than stages), so each stage is one counted group of copies
 #pragma unroll
-  for (int s = 0; s < STAGES - 1; ++s)
-    if (s < nk) issue(s, s);
+  for (int s = 0; s < STAGES; ++s) issue(s < nk ? s : nk - 1, s);
 
   int rowA[T::kFM], rowB[T::kFN];
 #pragma unroll
@@ -466,46 +502,70 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, MINB) void gemm_mxfp4_pipe_
   const int sshift = (kCPR == 4) ? 16 * h : 0;   // scale bytes of lane half h
   const int sofs_h = (kCPR == 8) ? 4 * h : 0;
 
-  for (int kt = 0; kt < nk; ++kt) {
-    // tile kt has landed once at most min(STAGES-2, nk-1-kt) later tiles remain in flight
-    const int ahead = nk - 1 - kt;
-    if (ahead >= STAGES - 2) {
-      wait_vmcnt<(STAGES - 2) * kLPT>();
-    } else if (STAGES > 3 && ahead == 2) {
-      wait_vmcnt<(STAGES > 3 ? 2 : 0) * kLPT>();
-    } else if (STAGES > 2 && ahead == 1) {
-      wait_vmcnt<kLPT>();
-    } else {
-      wait_vmcnt<0>();
-    }
-    block_barrier();
-    if (kt + STAGES - 1 < nk) issue(kt + STAGES - 1, (kt + STAGES - 1) % STAGES);
-
+  uint32_t sa[2][T::kFM], sb[2][T::kFN];      // scales: this tile's [0], the next tile's [1]
+  uint4 fa[2][T::kFM], fb[2][T::kFN];         // fragments: two sub-steps' sets
+  auto load_scales = [&](int kt, int set) {
     const uint8_t* base = smem + (kt % STAGES) * L::kStage;
-    uint32_t sa[T::kFM], sb[T::kFN];
 #pragma unroll
     for (int mi = 0; mi < T::kFM; ++mi)
-      sa[mi] = *reinterpret_cast<const uint32_t*>(base + L::kAs + rowA[mi] * kCPR + sofs_h) >> sshift;
+      sa[set][mi] = *reinterpret_cast<const uint32_t*>(base + L::kAs + rowA[mi] * kCPR + sofs_h) >> sshift;
 #pragma unroll
     for (int ni = 0; ni < T::kFN; ++ni)
-      sb[ni] = *reinterpret_cast<const uint32_t*>(base + L::kBs + rowB[ni] * kCPR + sofs_h) >> sshift;
-    uint4 fa[T::kFM], fb[T::kFN];
-#define MACAQ_PIPE_SUBSTEP(J)                                                                         \
-  {                                                                                                   \
-    _Pragma("unroll") for (int mi = 0; mi < T::kFM; ++mi) fa[mi] = *reinterpret_cast<const uint4*>(   \
-        base + L::kA + rowA[mi] * L::kRowBytes + (((h * (kCPR / 2) + (J)) ^ sw) << 4));               \
-    _Pragma("unroll") for (int ni = 0; ni < T::kFN; ++ni) fb[ni] = *reinterpret_cast<const uint4*>(   \
-        base + L::kB + rowB[ni] * L::kRowBytes + (((h * (kCPR / 2) + (J)) ^ sw) << 4));               \
-    mfma_substep<J>(acc, fa, fb, sa, sb);                                                             \
+      sb[set][ni] = *reinterpret_cast<const uint32_t*>(base + L::kBs + rowB[ni] * kCPR + sofs_h) >> sshift;
+  };
+  auto load_frags = [&](int kt, int j, int set) {
+    const uint8_t* base = smem + (kt % STAGES) * L::kStage;
+#pragma unroll
+    for (int mi = 0; mi < T::kFM; ++mi)
+      fa[set][mi] = *reinterpret_cast<const uint4*>(base + L::kA + rowA[mi] * L::kRowBytes +
+                                                     (((h * (kCPR / 2) + j) ^ sw) << 4));
+#pragma unroll
+    for (int ni = 0; ni < T::kFN; ++ni)
+      fb[set][ni] = *reinterpret_cast<const uint4*>(base + L::kB + rowB[ni] * L::kRowBytes +
+                                                     (((h * (kCPR / 2) + j) ^ sw) << 4));
+  };
+
+  // tile 0 has landed once at most STAGES-1 later groups remain in flight
+  if constexpr (STAGES == 2) wait_vmcnt<kLPT>();
+  else if constexpr (STAGES == 3) wait_vmcnt<2 * kLPT>();
+  else wait_vmcnt<3 * kLPT>();
+  block_barrier();
+  load_scales(0, 0);
+  load_frags(0, 0, 0);
+
+  constexpr int kMF = T::kFM * T::kFN;   // MFMAs per sub-step
+  constexpr int kRD = T::kFM + T::kFN;   // fragment reads per sub-step
+  static_assert(kRD <= kMF, "interleave pattern");
+  for (int kt = 0; kt < nk; ++kt) {
+    static_for<NSUB>([&](auto jc) {
+      constexpr int j = decltype(jc)::value;
+      constexpr int cur = j & 1;
+      if constexpr (j < NSUB - 1) {
+        load_frags(kt, j + 1, cur ^ 1);
+      } else {
+        // every wave holds this tile's last fragments: stage kt % STAGES is
+        // free once all waves are here.  Tiles up to kt-1+STAGES are issued.
+        wait_vmcnt<(STAGES - 2) * kLPT>();   // tile kt+1 has landed
+        block_barrier();
+        issue(kt + STAGES < nk ? kt + STAGES : nk - 1, kt % STAGES);
+        load_scales(kt + 1, 1);              // past the last tile: unused, in-bounds LDS bytes
+        load_frags(kt + 1, 0, cur ^ 1);
+      }
+      mfma_substep_t<j>(acc, fa[cur], fb[cur], sa[0], sb[0]);
+      // interleave: one MFMA, then that MFMA's share of the reads above
+#pragma unroll
+      for (int q = 0; q < kRD; ++q) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, j == NSUB - 1 ? 2 : 1, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, kMF - kRD, 0);
+    });
+#pragma unroll
+    for (int mi = 0; mi < T::kFM; ++mi) sa[0][mi] = sa[1][mi];
+#pragma unroll
+    for (int ni = 0; ni < T::kFN; ++ni) sb[0][ni] = sb[1][ni];
   }
-    MACAQ_PIPE_SUBSTEP(0)
-    MACAQ_PIPE_SUBSTEP(1)
-    if constexpr (kCPR == 8) {
-      MACAQ_PIPE_SUBSTEP(2)
-      MACAQ_PIPE_SUBSTEP(3)
-    }
-#undef MACAQ_PIPE_SUBSTEP
-  }
+  wait_vmcnt<0>();   // no copy into LDS outlives the loop (the stages are reused below)
 
   if constexpr (OUT == 0) {
     store_wave_tile_f32(acc, Y, row_begin + wm * T::kTM, row_end, n0 + wn * T::kTN, N, r32, h);

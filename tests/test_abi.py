@@ -239,7 +239,10 @@ def test_tiled_weights_validation():
     assert le(A16, 0, A16, None, 1, A16, A16, 1, 64, 256, A16, 0, 0, None, 0, 8 | T, None) == INVALID
     L = mx.lib()
     assert L.macaq_linear_path(1, 25600, 5120, 1, mx.PATH_AUTO | T) == mx.PATH_UNFUSED
-    assert L.macaq_linear_workspace_bytes(1, 25600, 5120, 1, mx.PATH_AUTO | T) == L.macaq_quant_act_bytes(1, 5120)
+    # a dense layer with tiled weights stages its activation tiled: whole 32-row blocks
+    assert L.macaq_linear_workspace_bytes(1, 25600, 5120, 1, mx.PATH_AUTO | T) == L.macaq_quant_act_bytes(32, 5120)
+    assert L.macaq_linear_workspace_bytes(33, 4096, 4096, 1, T) == L.macaq_quant_act_bytes(64, 4096)
+    assert L.macaq_linear_workspace_bytes(33, 1024, 3072, 4, T) == L.macaq_quant_act_bytes(33, 3072)   # grouped: row-major
 
 
 def test_set_tuning_validation_and_restore():

@@ -185,3 +185,79 @@ def test_grouped_gemm_many_experts(E):
         y_ref, S = oracle.gemm(a_np[r0:r1], as_np[r0:r1], wc_np[e], ws_np[e])
         ok, worst, _ = oracle.within_tolerance(y_np[r0:r1], y_ref, S, RTOL)
         assert ok, f"expert {e}: worst {worst:.3g}"
+
+
+def tiled_rows_reference(codes: np.ndarray, scales: np.ndarray, M: int):
+    """The activation rows in the tiled layout, padded to whole 32-row blocks
+    (the padding rows are left out of the comparison by the caller)."""
+    rows = (M + 31) // 32 * 32
+    pc = np.zeros((1, rows, codes.shape[1]), np.uint8)
+    ps = np.zeros((1, rows, scales.shape[1]), np.uint8)
+    pc[0, :M], ps[0, :M] = codes, scales
+    rc, rs = tiled_reference(pc, ps)
+    return rc.reshape(-1), rs.reshape(-1)
+
+
+def _valid_row_mask(M: int, K: int, per_row: int):
+    """Mask of the bytes of real rows (< M) in a tiled buffer of whole blocks;
+    per_row = bytes of one row in one 256-wide K-tile (128 codes or 8 scales)."""
+    rows = (M + 31) // 32 * 32
+    T = K // 256
+    r = np.arange(rows).reshape(rows // 32, 1, 32, 1)
+    mask = np.broadcast_to(r < M, (rows // 32, T, 32, per_row))
+    return mask.reshape(-1)
+
+
+@pytest.mark.parametrize("M,K,dt", [(1, 256, torch.bfloat16), (37, 1024, torch.bfloat16), (64, 512, torch.float32),
+                                    (300, 3072, torch.bfloat16), (33, 14336, torch.bfloat16)])
+def test_quant_act_tiled_bit_exact(M, K, dt):
+    """macaq_quant_act_tiled writes the oracle's codes and scale bytes in the
+    tiled layout (rows past M of the last block are not compared)."""
+    say(f"quant_act_tiled M{M} K{K} {dt}")
+    rng = np.random.default_rng(M + K)
+    xf = rng.standard_normal((M, K)) * np.where(rng.random(K) < 0.01, 50.0, 1.0)
+    x = torch.from_numpy(xf).to(dt)
+    s = torch.from_numpy(rng.uniform(0.25, 4.0, K).astype(np.float32))
+    codes, scales = mx.quant_act_tiled(x.to(DEV), s.to(DEV))
+    rc, rs = oracle.quant_act(host(x), s.numpy()[None])
+    tc, ts = tiled_rows_reference(rc, rs, M)
+    mc, ms = _valid_row_mask(M, K, 128), _valid_row_mask(M, K, 8)
+    assert np.array_equal(codes.cpu().numpy()[mc], tc[mc])
+    assert np.array_equal(scales.cpu().numpy()[ms], ts[ms])
+
+
+A_TILED_SHAPES = [
+    ("one 128 tile", (128, 128, 256)),
+    ("ragged M, N tail of 32", (300, 224, 1024)),
+    ("M=1", (1, 64, 512)),
+    ("several 256 tiles", (520, 544, 2048)),
+    ("M not a multiple of 32, deep K", (100, 256, 7168)),
+]
+
+
+@pytest.mark.parametrize("out", ["f32", "bf16", "swiglu"])
+@pytest.mark.parametrize("tile", ["256x256", "256x128", "128x128"])
+@pytest.mark.parametrize("name,shape", A_TILED_SHAPES, ids=[n for n, _ in A_TILED_SHAPES])
+def test_tiled_activation_gemm_equals_row_major(name, shape, tile, out, tune):
+    """The GEMM reading tiled activations (MACAQ_A_TILED, as the dense
+    linear path stages them) equals the same tile's GEMM on row-major
+    activations bit for bit (the LDS tiles are the same), for each output
+    form; the linear call with tiled weights equals both."""
+    say(f"A-tiled gemm tile={tile} out={out} {name} {shape}")
+    tune(mx.TUNE_GEMM_TILE, mx.GEMM_TILES[tile])
+    M, N, K = shape
+    x, s, ac, asc, wc, wsc = _operands(M, N, K, seed=M + N)
+    tc, ts = mx.tile_weights(wc, wsc)
+    atc, ats = mx.quant_act_tiled(x, s)
+    odt = torch.float32 if out == "f32" else torch.bfloat16
+    epi = mx.EPI_SWIGLU if out == "swiglu" else mx.EPI_NONE
+    y_rm = mx.gemm(ac, asc, tc, ts, out_dtype=odt, epilogue=epi | mx.W_TILED)
+    y_at = mx.gemm(atc, ats, tc, ts, out_dtype=odt, epilogue=epi | mx.W_TILED | mx.A_TILED, M=M)
+    y_lin = mx.linear(x, s, tc, ts, flags=mx.W_TILED, out_dtype=odt, epilogue=epi)
+    torch.cuda.synchronize()
+    assert torch.equal(y_at, y_rm)
+    assert torch.equal(y_lin, y_rm)
+    if out == "f32":
+        y_ref, S = oracle.gemm(ac.cpu().numpy(), asc.cpu().numpy(), wc[0].cpu().numpy(), wsc[0].cpu().numpy())
+        ok, worst, nw = oracle.within_tolerance(y_at.cpu().numpy(), y_ref, S, RTOL)
+        assert ok, f"worst {worst:.3g} normwise {nw:.3g}"
