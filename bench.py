@@ -80,7 +80,7 @@ def parse():
     p.add_argument("--w-layout", default="auto", choices=["auto", "tiled", "rowmajor"],
                    help="prepared weights as macaq_prepare_weights writes them (row-major), or repacked offline by "
                         "macaq_tile_weights (contiguous GEMM copies); auto: tiled for M > 32 when N %% 32 == 0 and "
-                        "K %% 256 == 0 (the decode kernels read row-major weights)")
+                        "K %% 128 == 0 (the decode kernels read row-major weights)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-ablation", action="store_true", help="skip the pure-MXFP4 comparison")
     p.add_argument("--cpu-rows", type=int, default=256, help="activation rows of the CPU oracle baseline")
@@ -562,7 +562,7 @@ def main():
     s0 = wl.s.to(dev)
     off = wl.offsets.to(dev) if E > 1 else None
     wc0, ws0 = mx.prepare_weights(wl.w.to(dev), s0)
-    tiled = args.w_layout == "tiled" or (args.w_layout == "auto" and M > 32 and N % 32 == 0 and K % 256 == 0)
+    tiled = args.w_layout == "tiled" or (args.w_layout == "auto" and M > 32 and N % 32 == 0 and K % 128 == 0)
     if tiled:   # offline repack, outside the timed region like the preparation itself
         wc0, ws0 = mx.tile_weights(wc0, ws0)
         flags |= mx.W_TILED

@@ -276,16 +276,16 @@ int macaq_quant_act(const void* x, macaq_dtype x_dtype, const float* s,
 /*
  * macaq_quant_act for a dense layer (one expert) with the codes and scales
  * in the tiled layout that the prefill GEMM copies with contiguous reads: per
- * 32-row block b and 256-wide K-tile t, 4096 bytes of codes at
- * (b * K/256 + t) * 4096, row r of the block at 128 r with its 16-byte chunk
- * c (32 values) at position c ^ ((r >> 1) & 7), and 256 bytes of scales at
- * (b * K/256 + t) * 256, row r's 8 bytes at 8 r.  The same codes and scale
+ * 32-row block b and 128-wide K-tile t, 2048 bytes of codes at
+ * (b * K/128 + t) * 2048, row r of the block at 64 r with its 16-byte chunk
+ * c (32 values) at position c ^ ((r >> 2) & 3), and 128 bytes of scales at
+ * (b * K/128 + t) * 128, row r's 4 bytes at 4 r.  The same codes and scale
  * bytes as macaq_quant_act, in other places.  The macaq_linear unfused path
  * of a dense layer with tiled weights stages its activation this way.
  *   x [M][K] in x_dtype; s [K] fp32;
  *   a_codes: ceil(M/32) * 32 * K/2 bytes out; a_scales: ceil(M/32) * 32 *
  *   K/32 bytes out (the rows past M of the last block are not written).
- * Requires M >= 0, K % 256 == 0 (MACAQ_ERR_UNSUPPORTED otherwise), x and
+ * Requires M >= 0, K % 128 == 0 (MACAQ_ERR_UNSUPPORTED otherwise), x and
  * a_codes 16-byte aligned.  M == 0 is a no-op.
  */
 int macaq_quant_act_tiled(const void* x, macaq_dtype x_dtype, const float* s, int64_t M, int64_t K,
@@ -418,14 +418,14 @@ int macaq_linear_ex(const void* x, macaq_dtype x_dtype, const float* s,
  * Repack of prepared weights into the tiled layout that the prefill and
  * grouped GEMMs read with contiguous copies (an offline step beside
  * macaq_prepare_weights; the codes and scale bytes themselves are unchanged,
- * only their places).  Per expert, for 32-row group g and 256-wide K-tile t:
- * 4096 bytes of codes at (g * K/256 + t) * 4096, where row r of the group
- * has its 128 bytes at 128 r with its 16-byte chunk c (32 values) at
- * position c ^ ((r >> 1) & 7); and 256 bytes of scales at
- * (g * K/256 + t) * 256, row r's 8 bytes at 8 r.
+ * only their places).  Per expert, for 32-row group g and 128-wide K-tile t:
+ * 2048 bytes of codes at (g * K/128 + t) * 2048, where row r of the group
+ * has its 64 bytes at 64 r with its 16-byte chunk c (32 values) at
+ * position c ^ ((r >> 2) & 3); and 128 bytes of scales at
+ * (g * K/128 + t) * 128, row r's 4 bytes at 4 r.
  *   w_codes [E][N][K/2], w_scales [E][N][K/32] (macaq_prepare_weights'
  *   layout) in; t_codes, t_scales (same sizes) out; no aliasing.
- * Requires N % 32 == 0, K % 256 == 0, code pointers 16-byte and scale
+ * Requires N % 32 == 0, K % 128 == 0, code pointers 16-byte and scale
  * pointers 4-byte aligned.  Layers with tiled weights (MACAQ_W_TILED) always
  * take the unfused path and the prefill / grouped GEMM, also for M <= 32.
  */

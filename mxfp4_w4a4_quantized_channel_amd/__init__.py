@@ -424,7 +424,7 @@ def tile_weights(w_codes, w_scales):
     repacked into the tiled layout the prefill and grouped GEMMs read with
     contiguous copies; same shapes and bytes, other places.  Use the result
     with W_TILED in linear's flags or gemm's epilogue.  N % 32 == 0 and
-    K % 256 == 0."""
+    K % 128 == 0."""
     _load()
     w_codes, w_scales = _w_shape(w_codes, w_scales)
     E, N, KH = w_codes.shape

@@ -196,9 +196,9 @@ __device__ __forceinline__ void wait_row_blocks(int later) {
 
 // TILED: codes and scales in the tiled layout the prefill GEMM copies with
 // contiguous 1 KiB reads (macaq_tile_weights' layout, applied to the
-// activation rows): per 32-row block and 256-wide K-tile, 4 KiB of codes
-// (row r at 128 r, group chunk c at position c ^ ((r >> 1) & 7)) and 256
-// bytes of scales (row r's 8 bytes at 8 r).  K % 256 == 0.
+// activation rows): per 32-row block and 128-wide K-tile, 2 KiB of codes
+// (row r at 64 r, group chunk c at position c ^ ((r >> 2) & 3)) and 128
+// bytes of scales (row r's 4 bytes at 4 r).  K % 128 == 0.
 template <int EB, bool RECIP, bool PLAIN = false, bool SHARED = false, bool TILED = false>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(SHARED && EB == 2 && !RECIP ? 4 : (EB == 2 ? 3 : 2))))
 void act_quant_lane_kernel(
@@ -423,10 +423,10 @@ void act_quant_lane_kernel(
     }
     if (active) {
       if constexpr (TILED) {
-        const int64_t blk = (r >> 5) * (K >> 8) + (g >> 3);
-        const int rr = (int)(r & 31), c = (int)(g & 7);
-        *reinterpret_cast<uint4*>(codes + blk * 4096 + rr * 128 + ((c ^ ((rr >> 1) & 7)) << 4)) = cw;
-        scales[blk * 256 + rr * 8 + c] = (uint8_t)b;
+        const int64_t blk = (r >> 5) * (K >> 7) + (g >> 2);
+        const int rr = (int)(r & 31), c = (int)(g & 3);
+        *reinterpret_cast<uint4*>(codes + blk * 2048 + rr * 64 + ((c ^ ((rr >> 2) & 3)) << 4)) = cw;
+        scales[blk * 128 + rr * 4 + c] = (uint8_t)b;
       } else {
         *reinterpret_cast<uint4*>(codes + r * (K >> 1) + g * 16) = cw;
         scales[r * KG + g] = (uint8_t)b;
@@ -517,7 +517,7 @@ hipError_t launch_act_quant(const void* x, bool x_f32, bool reciprocal, const fl
 }
 
 // The online transform of a dense layer (one expert) with its output in the
-// tiled layout of the prefill GEMM (K % 256 == 0).  The codes and scales
+// tiled layout of the prefill GEMM (K % 128 == 0).  The codes and scales
 // hold ceil(M / 32) * 32 rows; the rows past M are not written.
 hipError_t launch_act_quant_tiled(const void* x, bool x_f32, const float* s, int64_t M, int64_t K, uint8_t* codes,
                                   uint8_t* scales, hipStream_t stream) {

@@ -190,8 +190,8 @@ int validate_gemm(const uint8_t* a_codes, const uint8_t* a_scales, const int32_t
 
 // Shape rule of the tiled W' layout.
 int check_tiled(int64_t N, int64_t K, const char* fn) {
-  if (N % 32 != 0 || K % 256 != 0)
-    return fail(MACAQ_ERR_UNSUPPORTED, std::string(fn) + ": tiled weights need N % 32 == 0 and K % 256 == 0");
+  if (N % 32 != 0 || K % 128 != 0)
+    return fail(MACAQ_ERR_UNSUPPORTED, std::string(fn) + ": tiled weights need N % 32 == 0 and K % 128 == 0");
   return MACAQ_OK;
 }
 
@@ -313,7 +313,7 @@ int macaq_quant_act_tiled(const void* x, macaq_dtype x_dtype, const float* s, in
   if (int st = check_dtype(x_dtype, fn)) return st;
   if (M < 0) return fail(MACAQ_ERR_INVALID_ARG, std::string(fn) + ": need M >= 0");
   if (int st = check_k(K, fn)) return st;
-  if (K % 256 != 0) return fail(MACAQ_ERR_UNSUPPORTED, std::string(fn) + ": the tiled layout needs K % 256 == 0");
+  if (K % 128 != 0) return fail(MACAQ_ERR_UNSUPPORTED, std::string(fn) + ": the tiled layout needs K % 128 == 0");
   if (M == 0) return MACAQ_OK;
   if (!x || !s || !a_codes || !a_scales) return fail(MACAQ_ERR_INVALID_ARG, std::string(fn) + ": null pointer");
   if (!aligned(x, 16) || !aligned(a_codes, 16) || !aligned(s, 16))

@@ -46,29 +46,27 @@ hipError_t launch_pipe(const uint8_t* A, const uint8_t* As, const int32_t* offse
 }
 
 // Repack of prepared W' (row-major codes [E][N][K/2], scales [E][N][K/32])
-// into the tiled layout: per expert, for each 32-row group g and 256-wide
-// K-tile t, 4 KiB of codes (row r of the group at byte 128 r, its 16-byte
-// chunk c at position c ^ ((r >> 1) & 7)) and 256 bytes of scales (row r's 8
-// bytes at 8 r).  One thread per 16-byte code chunk (and per 4 scale bytes).
+// into the tiled layout: per expert, for each 32-row group g and 128-wide
+// K-tile t, 2 KiB of codes (row r of the group at byte 64 r, its 16-byte
+// chunk c at position c ^ ((r >> 2) & 3)) and 128 bytes of scales (row r's
+// 4 bytes at 4 r).  One thread per 16-byte code chunk (and per 4 scale bytes).
 __global__ void tile_weights_kernel(const uint8_t* __restrict__ wc, const uint8_t* __restrict__ ws, int64_t rows,
                                     int64_t K, uint8_t* __restrict__ tc, uint8_t* __restrict__ ts) {
-  const int64_t KT = K >> 8;                       // K-tiles per row
+  const int64_t KT = K >> 7;                       // K-tiles per row
   const int64_t chunks = rows * (K >> 5);          // 16-byte code chunks (= 32-value groups)
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (i < chunks) {
     const int64_t row = i / (K >> 5), c_all = i % (K >> 5);    // row over all experts (N % 32 == 0)
-    const int64_t t = c_all >> 3;
-    const int c = (int)(c_all & 7);
+    const int64_t t = c_all >> 2;
+    const int c = (int)(c_all & 3);
     const int r = (int)(row & 31);
-    const int64_t dst = ((row >> 5) * KT + t) * 4096 + r * 128 + ((c ^ ((r >> 1) & 7)) << 4);
+    const int64_t dst = ((row >> 5) * KT + t) * 2048 + r * 64 + ((c ^ ((r >> 2) & 3)) << 4);
     *reinterpret_cast<uint4*>(tc + dst) = *reinterpret_cast<const uint4*>(wc + row * (K >> 1) + c_all * 16);
   }
-  if (i < rows * (K >> 7)) {   // 4-byte scale words: (row, K-tile, half)
-    const int64_t row = i / (K >> 7), w = i % (K >> 7);
-    const int64_t t = w >> 1;
-    const int half = (int)(w & 1);
-    const int64_t dst = ((row >> 5) * KT + t) * 256 + (row & 31) * 8 + half * 4;
-    *reinterpret_cast<uint32_t*>(ts + dst) = *reinterpret_cast<const uint32_t*>(ws + row * (K >> 5) + w * 4);
+  if (i < rows * KT) {   // 4-byte scale words: (row, K-tile)
+    const int64_t row = i / KT, t = i % KT;
+    const int64_t dst = ((row >> 5) * KT + t) * 128 + (row & 31) * 4;
+    *reinterpret_cast<uint32_t*>(ts + dst) = *reinterpret_cast<const uint32_t*>(ws + row * (K >> 5) + t * 4);
   }
 }
 
@@ -83,11 +81,12 @@ hipError_t launch_tile_weights(const uint8_t* wc, const uint8_t* ws, int64_t E, 
   return hipGetLastError();
 }
 
-// GEMM with W' in the tiled layout (N % 32 == 0, K % 256 == 0): 256x256 when
-// that gives about one tile per CU, else 128x128 with two blocks per CU
-// (with contiguous W' copies the smaller tile is faster than 256x128:
-// attn-proj 25.3 against 29.6 us on random operands).  a_tiled: the
-// activation codes and scales are in the same tiled layout (dense only).
+// GEMM with W' in the tiled layout (N % 32 == 0, K % 128 == 0): 128-wide
+// K-tiles in a 4-deep ring (the tiled copies are contiguous, so the shorter
+// tiles cost no copy efficiency and keep three tiles in flight); 256x256
+// when that gives about one tile per CU, else 128x128 with two blocks per
+// CU.  a_tiled: the activation codes and scales are in the same tiled
+// layout (dense only).
 hipError_t launch_gemm_tiled(const uint8_t* A, const uint8_t* As, const int32_t* offsets, int E, const uint8_t* B,
                              const uint8_t* Bs, int64_t M, int64_t N, int64_t K, void* Y, int mode, bool a_tiled,
                              hipStream_t stream) {
@@ -98,15 +97,15 @@ hipError_t launch_gemm_tiled(const uint8_t* A, const uint8_t* As, const int32_t*
   if (const int force = tuning(MACAQ_TUNE_GEMM_TILE)) choice = force - 1;
   if (a_tiled) {
     switch (choice) {
-      case 0: return launch_pipe<256, 256, 2, 2, 256, 2, 1, true, true>(A, As, offsets, E, B, Bs, M, N, K, Y, mode, stream);
-      case 1: return launch_pipe<256, 128, 2, 2, 256, 2, 1, true, true>(A, As, offsets, E, B, Bs, M, N, K, Y, mode, stream);
-      default: return launch_pipe<128, 128, 2, 2, 256, 2, 2, true, true>(A, As, offsets, E, B, Bs, M, N, K, Y, mode, stream);
+      case 0: return launch_pipe<256, 256, 2, 2, 128, 4, 1, true, true>(A, As, offsets, E, B, Bs, M, N, K, Y, mode, stream);
+      case 1: return launch_pipe<256, 128, 2, 2, 128, 4, 1, true, true>(A, As, offsets, E, B, Bs, M, N, K, Y, mode, stream);
+      default: return launch_pipe<128, 128, 2, 2, 128, 4, 2, true, true>(A, As, offsets, E, B, Bs, M, N, K, Y, mode, stream);
     }
   }
   switch (choice) {
-    case 0: return launch_pipe<256, 256, 2, 2, 256, 2, 1, true>(A, As, offsets, E, B, Bs, M, N, K, Y, mode, stream);
-    case 1: return launch_pipe<256, 128, 2, 2, 256, 2, 1, true>(A, As, offsets, E, B, Bs, M, N, K, Y, mode, stream);
-    default: return launch_pipe<128, 128, 2, 2, 256, 2, 2, true>(A, As, offsets, E, B, Bs, M, N, K, Y, mode, stream);
+    case 0: return launch_pipe<256, 256, 2, 2, 128, 4, 1, true>(A, As, offsets, E, B, Bs, M, N, K, Y, mode, stream);
+    case 1: return launch_pipe<256, 128, 2, 2, 128, 4, 1, true>(A, As, offsets, E, B, Bs, M, N, K, Y, mode, stream);
+    default: return launch_pipe<128, 128, 2, 2, 128, 4, 2, true>(A, As, offsets, E, B, Bs, M, N, K, Y, mode, stream);
   }
 }
 

@@ -319,11 +319,13 @@ __device__ __forceinline__ bool grouped_tile(const int32_t* __restrict__ offsets
 }
 
 // BT: W' in the tiled layout (see macaq_tile_weights): per expert, blocks of
-// 32 rows x one 256-wide K-tile, 4 KiB of codes (each row's 16-byte chunks
-// stored in the XOR-swizzled order the LDS tile uses) and 256 bytes of
+// 32 rows x one 128-wide K-tile, 2 KiB of codes (each row's 16-byte chunks
+// stored in the XOR-swizzled order the LDS tile uses) and 128 bytes of
 // scales.  A copy instruction then reads 1 KiB of contiguous codes (and a
-// scale copy 256 contiguous bytes) instead of 8 (32) rows' pieces: measured
-// 56 against 33 B/clk per CU for such copies in isolation.  AT: the
+// scale copy 256 contiguous bytes) instead of 16 (64) rows' pieces
+// (measured with 256-wide tiles: 56 against 33 B/clk per CU for such copies
+// in isolation; the down-prefill layer's copies alone take 38 us of loop
+// time tiled against 118 us row-major with 128-wide K-tiles).  AT: the
 // activation codes and scales in the same tiled layout (dense layers only:
 // row tiles start at multiples of 32).
 
@@ -368,7 +370,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, MINB) void gemm_mxfp4_pipe_
   constexpr int kSB = (L::kScaleBlocks + kWaves - 1) / kWaves;
   constexpr int kLPT = kCB + kSB;
   static_assert((STAGES - 2) * kLPT < 64, "vmcnt range");
-  static_assert(!(BT || AT) || BK == 256, "the tiled layouts have 256-wide K-tiles");
+  static_assert(!(BT || AT) || BK == 128, "the tiled layouts have 128-wide K-tiles");
   static_assert(NSUB % 2 == 0, "an even number of sub-steps per K-tile");
   extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];
 
@@ -422,7 +424,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, MINB) void gemm_mxfp4_pipe_
       int64_t gr = row_begin + row;
       if (gr >= row_end) gr = row_end - 1;
       if constexpr (AT) {
-        csrc[i] = A + (gr >> 5) * (K >> 8) * 4096 + (gr & 31) * 128 + (lane % kCPR) * 16;
+        csrc[i] = A + (gr >> 5) * (K >> 7) * 2048 + (gr & 31) * 64 + (lane % kCPR) * 16;
         ctile |= 1u << i;
       } else {
         csrc[i] = A + gr * KB + c * 16;
@@ -431,7 +433,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, MINB) void gemm_mxfp4_pipe_
       int64_t gn = n0 + (row - BM);
       if (gn >= N) gn = N - 1;
       if constexpr (BT) {
-        csrc[i] = Bx + (gn >> 5) * (K >> 8) * 4096 + (gn & 31) * 128 + (lane % kCPR) * 16;
+        csrc[i] = Bx + (gn >> 5) * (K >> 7) * 2048 + (gn & 31) * 64 + (lane % kCPR) * 16;
         ctile |= 1u << i;
       } else {
         csrc[i] = Bx + gn * KB + c * 16;
@@ -448,7 +450,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, MINB) void gemm_mxfp4_pipe_
       int64_t gr = row_begin + row;
       if (gr >= row_end) gr = row_end - 1;
       if constexpr (AT) {
-        ssrc[i] = As + (gr >> 5) * (K >> 8) * 256 + (gr & 31) * 8 + part * 4;
+        ssrc[i] = As + (gr >> 5) * (K >> 7) * 128 + (gr & 31) * 4 + part * 4;
         stile |= 1u << i;
       } else {
         ssrc[i] = As + gr * KG + part * 4;
@@ -457,7 +459,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, MINB) void gemm_mxfp4_pipe_
       int64_t gn = n0 + (row - BM);
       if (gn >= N) gn = N - 1;
       if constexpr (BT) {
-        ssrc[i] = Bsx + (gn >> 5) * (K >> 8) * 256 + (gn & 31) * 8 + part * 4;
+        ssrc[i] = Bsx + (gn >> 5) * (K >> 7) * 128 + (gn & 31) * 4 + part * 4;
         stile |= 1u << i;
       } else {
         ssrc[i] = Bsx + gn * KG + part * 4;
@@ -467,8 +469,8 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, MINB) void gemm_mxfp4_pipe_
 
   auto issue = [&](int kt, int st) {
     const uint32_t base = lds_base + (uint32_t)(st * L::kStage);
-    const int64_t cofs = (int64_t)kt * L::kRowBytes, cofs_t = (int64_t)kt * 4096;
-    const int64_t sofs = (int64_t)kt * kCPR, sofs_t = (int64_t)kt * 256;
+    const int64_t cofs = (int64_t)kt * L::kRowBytes, cofs_t = (int64_t)kt * 2048;
+    const int64_t sofs = (int64_t)kt * kCPR, sofs_t = (int64_t)kt * 128;
 #pragma unroll
     for (int i = 0; i < kCB; ++i)
       dma16(csrc[i] + (((ctile >> i) & 1u) ? cofs_t : cofs),
@@ -544,7 +546,10 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, MINB) void gemm_mxfp4_pipe_
         load_frags(kt, j + 1, cur ^ 1);
       } else {
         // every wave holds this tile's last fragments: stage kt % STAGES is
-        // free once all waves are here.  Tiles up to kt-1+STAGES are issued.
+        // free once all waves are here with their reads of it returned (the
+        // barrier may be scheduled right after those reads are issued).
+        // Tiles up to kt-1+STAGES are issued.
+        wait_lgkmcnt0();
         wait_vmcnt<(STAGES - 2) * kLPT>();   // tile kt+1 has landed
         block_barrier();
         issue(kt + STAGES < nk ? kt + STAGES : nk - 1, kt % STAGES);

@@ -215,13 +215,13 @@ def test_output_dtype_and_epilogue_validation():
 
 def test_tiled_weights_validation():
     """macaq_tile_weights and the MACAQ_W_TILED layout bit: shape rule
-    (N % 32 == 0, K % 256 == 0), pointers, aliasing; layers with tiled
+    (N % 32 == 0, K % 128 == 0), pointers, aliasing; layers with tiled
     weights take the two-launch path and refuse the fused decode path."""
     mx.lib()
     tw = mx.macaq_tile_weights
     A2 = A16 * 16
     assert tw(A16, A16, 1, 48, 512, A2, A2, None) == UNSUPPORTED      # N % 32 != 0
-    assert tw(A16, A16, 1, 64, 384, A2, A2, None) == UNSUPPORTED      # K % 256 != 0
+    assert tw(A16, A16, 1, 64, 416, A2, A2, None) == UNSUPPORTED      # K % 128 != 0
     assert tw(A16, A16, 1, 64, 48, A2, A2, None) == INVALID           # K % 32 != 0
     assert tw(A16, A16, 0, 64, 512, A2, A2, None) == INVALID
     assert tw(None, A16, 1, 64, 512, A2, A2, None) == INVALID
@@ -231,7 +231,7 @@ def test_tiled_weights_validation():
     T = mx.W_TILED
     ge = mx.macaq_gemm_ex
     assert ge(A16, A16, None, 1, A16, A16, 4, 48, 256, A16, 0, T, None, 0, None) == UNSUPPORTED
-    assert ge(A16, A16, None, 1, A16, A16, 4, 64, 384, A16, 0, T, None, 0, None) == UNSUPPORTED
+    assert ge(A16, A16, None, 1, A16, A16, 4, 64, 416, A16, 0, T, None, 0, None) == UNSUPPORTED   # K % 128 != 0
     assert ge(A16, A16, None, 1, A16, A16, 4, 64, 256, A16, 0, T | 4, None, 0, None) == INVALID   # unknown epilogue
     assert ge(A16, A16, None, 1, A16, A16, 0, 64, 256, A16, 0, T, None, 0, None) == OK           # M == 0
     le = mx.macaq_linear_ex

@@ -30,20 +30,20 @@ def host(t: torch.Tensor) -> np.ndarray:
 
 def tiled_reference(codes: np.ndarray, scales: np.ndarray):
     """The tiled layout as the header defines it: per expert, per 32-row group
-    and 256-wide K-tile, 32 rows of 128 code bytes whose 16-byte chunk c sits
-    at position c ^ ((r >> 1) & 7), then 32 rows of 8 scale bytes."""
+    and 128-wide K-tile, 32 rows of 64 code bytes whose 16-byte chunk c sits
+    at position c ^ ((r >> 2) & 3), then 32 rows of 4 scale bytes."""
     E, N, KH = codes.shape
-    G, T = N // 32, KH // 128
-    c = codes.reshape(E, G, 32, T, 8, 16).transpose(0, 1, 3, 2, 4, 5)    # [E, G, T, r, chunk, 16]
+    G, T = N // 32, KH // 64
+    c = codes.reshape(E, G, 32, T, 4, 16).transpose(0, 1, 3, 2, 4, 5)    # [E, G, T, r, chunk, 16]
     r = np.arange(32)[:, None]
-    p = np.arange(8)[None, :]
-    src = p ^ ((r >> 1) & 7)                                             # chunk held at position p
+    p = np.arange(4)[None, :]
+    src = p ^ ((r >> 2) & 3)                                             # chunk held at position p
     c = np.take_along_axis(c, np.broadcast_to(src[None, None, None, :, :, None], c.shape), axis=4)
-    s = scales.reshape(E, G, 32, T, 8).transpose(0, 1, 3, 2, 4)          # [E, G, T, r, 8]
+    s = scales.reshape(E, G, 32, T, 4).transpose(0, 1, 3, 2, 4)          # [E, G, T, r, 4]
     return np.ascontiguousarray(c).reshape(E, N, KH), np.ascontiguousarray(s).reshape(E, N, KH // 16)
 
 
-@pytest.mark.parametrize("E,N,K", [(1, 32, 256), (2, 96, 768), (3, 128, 3072)])
+@pytest.mark.parametrize("E,N,K", [(1, 32, 128), (1, 32, 256), (2, 96, 768), (3, 128, 3072)])
 def test_tile_weights_layout(E, N, K):
     say(f"tile_weights E{E} N{N} K{K}")
     rng = np.random.default_rng(E * 1000 + N + K)
@@ -200,15 +200,15 @@ def tiled_rows_reference(codes: np.ndarray, scales: np.ndarray, M: int):
 
 def _valid_row_mask(M: int, K: int, per_row: int):
     """Mask of the bytes of real rows (< M) in a tiled buffer of whole blocks;
-    per_row = bytes of one row in one 256-wide K-tile (128 codes or 8 scales)."""
+    per_row = bytes of one row in one 128-wide K-tile (64 codes or 4 scales)."""
     rows = (M + 31) // 32 * 32
-    T = K // 256
+    T = K // 128
     r = np.arange(rows).reshape(rows // 32, 1, 32, 1)
     mask = np.broadcast_to(r < M, (rows // 32, T, 32, per_row))
     return mask.reshape(-1)
 
 
-@pytest.mark.parametrize("M,K,dt", [(1, 256, torch.bfloat16), (37, 1024, torch.bfloat16), (64, 512, torch.float32),
+@pytest.mark.parametrize("M,K,dt", [(1, 256, torch.bfloat16), (37, 1152, torch.bfloat16), (64, 512, torch.float32),
                                     (300, 3072, torch.bfloat16), (33, 14336, torch.bfloat16)])
 def test_quant_act_tiled_bit_exact(M, K, dt):
     """macaq_quant_act_tiled writes the oracle's codes and scale bytes in the
@@ -221,7 +221,7 @@ def test_quant_act_tiled_bit_exact(M, K, dt):
     codes, scales = mx.quant_act_tiled(x.to(DEV), s.to(DEV))
     rc, rs = oracle.quant_act(host(x), s.numpy()[None])
     tc, ts = tiled_rows_reference(rc, rs, M)
-    mc, ms = _valid_row_mask(M, K, 128), _valid_row_mask(M, K, 8)
+    mc, ms = _valid_row_mask(M, K, 64), _valid_row_mask(M, K, 4)
     assert np.array_equal(codes.cpu().numpy()[mc], tc[mc])
     assert np.array_equal(scales.cpu().numpy()[ms], ts[ms])
 
@@ -232,6 +232,7 @@ A_TILED_SHAPES = [
     ("M=1", (1, 64, 512)),
     ("several 256 tiles", (520, 544, 2048)),
     ("M not a multiple of 32, deep K", (100, 256, 7168)),
+    ("K an odd number of 128-wide tiles", (96, 160, 1152)),
 ]
 
 
