@@ -97,6 +97,10 @@ def parse():
 
 
 def copy_calibration():
+    """A plain 512 MiB device-to-device copy (torch's copy kernel): the
+    reference transfer of known size that scales the HBM byte counters, and
+    the achievable streaming bandwidth (read + write) on this GPU, which
+    bounds what an HBM-bound kernel can reach in practice."""
     import torch
     n = 512 << 20
     src = torch.empty(n, dtype=torch.uint8, device="cuda:0").fill_(1)
@@ -105,7 +109,18 @@ def copy_calibration():
     for _ in range(5):
         dst.copy_(src)
     torch.cuda.synchronize()
-    print(json.dumps({"copy_calibration": {"bytes_read_per_copy": n, "bytes_written_per_copy": n, "copies": 5}}))
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    reps = 20
+    e0.record()
+    for _ in range(reps):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) / reps * 1e3
+    print(json.dumps({"copy_calibration": {"bytes_read_per_copy": n, "bytes_written_per_copy": n, "copies": 5 + reps,
+                                           "us_per_copy": round(us, 2),
+                                           "GBps_read_plus_write": round(2 * n / us / 1e3, 1),
+                                           "frac_of_hbm_peak": round(2 * n / us / 1e3 / PEAK_HBM_GBPS, 4)}}))
 
 
 def library_compare(steps):
@@ -581,8 +596,8 @@ def main():
     ws_buf = torch.zeros(max(need, 256), dtype=torch.uint8, device=dev)
     # the linear call's staging of the activation: tiled (whole 32-row blocks)
     # for a dense layer with tiled weights, else row-major
-    a_tiled = tiled and E == 1
-    stage_rows = -(-M // 32) * 32 if a_tiled else M
+    a_tiled = tiled
+    stage_rows = int(L.macaq_quant_act_tiled_rows(M, E)) if a_tiled else M
     a_codes = ws_buf[: stage_rows * K // 2]
     fused = L.macaq_linear_path(M, N, K, E, flags) == mx.PATH_FUSED
     a_scales = ws_buf[(stage_rows * K // 2 + 255) // 256 * 256:]
@@ -630,7 +645,7 @@ def main():
     def act_only(i):
         xp = step_args(i)[0]
         if a_tiled:
-            st = mx.macaq_quant_act_tiled(xp, xdt, p(s0.data_ptr()), M, K, p(a_codes.data_ptr()),
+            st = mx.macaq_quant_act_tiled(xp, xdt, p(s0.data_ptr()), off_p, E, M, K, p(a_codes.data_ptr()),
                                           p(a_scales.data_ptr()), sp)
         else:
             st = mx.macaq_quant_act(xp, xdt, p(s0.data_ptr()), off_p, E, M, K, p(a_codes.data_ptr()),

@@ -111,10 +111,10 @@ enum {
  * argument of macaq_gemm_ex. */
 #define MACAQ_W_TILED 0x100u
 
-/* Layout bit: a_codes / a_scales of macaq_gemm_ex are in the tiled layout
- * (the layout of macaq_tile_weights applied to the activation rows, as
- * macaq_quant_act_tiled writes it).  OR'ed into the epilogue argument of
- * macaq_gemm_ex together with MACAQ_W_TILED; dense layers only (E == 1). */
+/* Layout bit: a_codes / a_scales of macaq_gemm_ex are in the tiled,
+ * expert-padded layout that macaq_quant_act_tiled writes (the layout of
+ * macaq_tile_weights applied to the activation rows).  OR'ed into the
+ * epilogue argument of macaq_gemm_ex together with MACAQ_W_TILED. */
 #define MACAQ_A_TILED 0x200u
 
 /* Knobs of macaq_set_tuning.  Value 0 of every knob is the library's own
@@ -129,7 +129,9 @@ enum {
  *                                 block in LDS
  *   MACAQ_TUNE_DECODE_WAVES       waves per decode block (4 or 8; 32-row blocks)
  *   MACAQ_TUNE_DECODE_STAGES      ring slots per decode wave (2..4; 32-row blocks)
- *   MACAQ_TUNE_DECODE_ROWS        weight rows per decode block (32 or 64) */
+ *   MACAQ_TUNE_DECODE_ROWS        weight rows per decode block (32 or 64)
+ *   MACAQ_TUNE_ACT_SEGMENT        groups per row segment of a wave of the
+ *                                 activation kernel (16, 32 or 64) */
 enum {
   MACAQ_TUNE_GEMM_TILE = 0,
   MACAQ_TUNE_GEMM_GROUP_M = 1,
@@ -138,7 +140,8 @@ enum {
   MACAQ_TUNE_DECODE_WAVES = 4,
   MACAQ_TUNE_DECODE_STAGES = 5,
   MACAQ_TUNE_DECODE_ROWS = 6,
-  MACAQ_TUNE_COUNT = 7
+  MACAQ_TUNE_ACT_SEGMENT = 7,
+  MACAQ_TUNE_COUNT = 8
 };
 
 /* Library version as major*10000 + minor*100 + patch. */
@@ -274,22 +277,32 @@ int macaq_quant_act(const void* x, macaq_dtype x_dtype, const float* s,
                     uint8_t* a_codes, uint8_t* a_scales, void* stream);
 
 /*
- * macaq_quant_act for a dense layer (one expert) with the codes and scales
- * in the tiled layout that the prefill GEMM copies with contiguous reads: per
- * 32-row block b and 128-wide K-tile t, 2048 bytes of codes at
- * (b * K/128 + t) * 2048, row r of the block at 64 r with its 16-byte chunk
- * c (32 values) at position c ^ ((r >> 2) & 3), and 128 bytes of scales at
- * (b * K/128 + t) * 128, row r's 4 bytes at 4 r.  The same codes and scale
- * bytes as macaq_quant_act, in other places.  The macaq_linear unfused path
- * of a dense layer with tiled weights stages its activation this way.
- *   x [M][K] in x_dtype; s [K] fp32;
- *   a_codes: ceil(M/32) * 32 * K/2 bytes out; a_scales: ceil(M/32) * 32 *
- *   K/32 bytes out (the rows past M of the last block are not written).
- * Requires M >= 0, K % 128 == 0 (MACAQ_ERR_UNSUPPORTED otherwise), x and
- * a_codes 16-byte aligned.  M == 0 is a no-op.
+ * macaq_quant_act with the codes and scales in the tiled layout that the
+ * prefill and grouped GEMMs copy with contiguous reads: per 32-row block b
+ * and 128-wide K-tile t, 2048 bytes of codes at (b * K/128 + t) * 2048, row
+ * r of the block at 64 r with its 16-byte chunk c (32 values) at position
+ * c ^ ((r >> 2) & 3), and 128 bytes of scales at (b * K/128 + t) * 128, row
+ * r's 4 bytes at 4 r.  Rows are padded per expert: expert e's rows start at
+ * padded row P_e = sum over e' < e of ceil(rows_e' / 32) * 32 (P_0 = 0; for
+ * E == 1 the padded rows are the rows), so every expert starts a block.
+ * The same codes and scale bytes as macaq_quant_act, in other places.  The
+ * macaq_linear unfused path of a layer with tiled weights stages its
+ * activation this way.
+ *   x [M][K] in x_dtype, rows sorted by expert; s [E][K] fp32;
+ *   expert_offsets [E+1] device int32 (NULL allowed when E == 1);
+ *   a_codes: macaq_quant_act_tiled_rows(M, E) * K/2 bytes out; a_scales:
+ *   macaq_quant_act_tiled_rows(M, E) * K/32 bytes out (padding rows are not
+ *   written).
+ * Requires E >= 1, M >= 0, K % 128 == 0 (MACAQ_ERR_UNSUPPORTED otherwise),
+ * x, s and a_codes 16-byte aligned.  M == 0 is a no-op.
  */
-int macaq_quant_act_tiled(const void* x, macaq_dtype x_dtype, const float* s, int64_t M, int64_t K,
-                          uint8_t* a_codes, uint8_t* a_scales, void* stream);
+int macaq_quant_act_tiled(const void* x, macaq_dtype x_dtype, const float* s, const int32_t* expert_offsets,
+                          int64_t E, int64_t M, int64_t K, uint8_t* a_codes, uint8_t* a_scales, void* stream);
+
+/* Rows that macaq_quant_act_tiled's buffers hold for M rows over E experts:
+ * ceil(M / 32) * 32 for E == 1, else ceil((M + 31 E) / 32) * 32 (an upper
+ * bound of the padded rows for any split of the M rows). */
+size_t macaq_quant_act_tiled_rows(int64_t M, int64_t E);
 
 /*
  * MXFP4 x MXFP4 GEMM y = A' W'^T per expert ("Quantization mechanism": the
@@ -398,7 +411,7 @@ int macaq_linear_noalloc(const void* x, macaq_dtype x_dtype, const float* s,
  *   column j; y [M][N/2] = silu(g) * u with g, u the fp32 results of those
  *   rows and silu(g) = g / (1 + exp(-g)) in fp32 (expf, IEEE division).
  * The epilogue argument of macaq_gemm_ex also carries the layout bits
- * MACAQ_W_TILED and MACAQ_A_TILED (the latter only with the former, E == 1).
+ * MACAQ_W_TILED and MACAQ_A_TILED (the latter only with the former).
  * Other arguments, rules and errors as macaq_gemm / macaq_linear; y must be
  * aligned to its element size.  macaq_gemm and macaq_linear are these calls
  * with MACAQ_F32 and MACAQ_EPI_NONE.

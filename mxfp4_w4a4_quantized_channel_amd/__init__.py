@@ -25,7 +25,7 @@ __all__ = [
     "hessian", "prepare_weights_hessian", "flip_refine", "flip_refine_workspace_bytes",
     "set_tuning", "linear_noalloc", "quant_act_tiled", "A_TILED", "W_TILED", "NOALLOC_SCRATCH_BYTES", "TUNE_GEMM_TILE", "TUNE_GEMM_GROUP_M",
     "TUNE_ACT_ROWS_PER_WAVE", "TUNE_ACT_SHARED_S",
-    "TUNE_DECODE_WAVES", "TUNE_DECODE_STAGES", "TUNE_DECODE_ROWS", "GEMM_TILES",
+    "TUNE_DECODE_WAVES", "TUNE_DECODE_STAGES", "TUNE_DECODE_ROWS", "TUNE_ACT_SEGMENT", "GEMM_TILES",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -39,7 +39,7 @@ A_TILED = 0x200   # activation codes in the tiled layout (gemm's epilogue argume
 W_TILED = 0x100   # weights in macaq_tile_weights' layout (OR into linear's flags / gemm's epilogue)
 # knobs of macaq_set_tuning (0 = the library's own choice)
 (TUNE_GEMM_TILE, TUNE_GEMM_GROUP_M, TUNE_ACT_ROWS_PER_WAVE, TUNE_ACT_SHARED_S, TUNE_DECODE_WAVES,
- TUNE_DECODE_STAGES, TUNE_DECODE_ROWS) = range(7)
+ TUNE_DECODE_STAGES, TUNE_DECODE_ROWS, TUNE_ACT_SEGMENT) = range(8)
 GEMM_TILES = {"256x256": 1, "256x128": 2, "128x128": 3}   # values of TUNE_GEMM_TILE
 STATUS = {0: "ok", -1: "invalid argument", -2: "unsupported", -3: "no device", -4: "HIP error",
           -5: "workspace too small"}
@@ -74,7 +74,8 @@ def _load():
         "macaq_quant_act": (ci, [vp, ci, vp, vp, i64, i64, i64, vp, vp, vp]),
         "macaq_gemm": (ci, [vp, vp, vp, i64, vp, vp, i64, i64, i64, vp, vp, sz, vp]),
         "macaq_quant_act_bytes": (sz, [i64, i64]),
-        "macaq_quant_act_tiled": (ci, [vp, ci, vp, i64, i64, vp, vp, vp]),
+        "macaq_quant_act_tiled": (ci, [vp, ci, vp, vp, i64, i64, i64, vp, vp, vp]),
+        "macaq_quant_act_tiled_rows": (sz, [i64, i64]),
         "macaq_gemm_workspace_bytes": (sz, [i64, i64, i64, i64]),
         "macaq_linear_workspace_bytes": (sz, [i64, i64, i64, i64, u32]),
         "macaq_linear_path": (ci, [i64, i64, i64, i64, u32]),
@@ -298,20 +299,24 @@ def quant_act(x: torch.Tensor, s: torch.Tensor, offsets: torch.Tensor | None = N
     return codes, scales
 
 
-def quant_act_tiled(x: torch.Tensor, s: torch.Tensor):
-    """quant_act of a dense layer in the tiled layout the prefill GEMM reads
-    -> (codes [ceil(M/32)*32*K/2] uint8, scales [ceil(M/32)*32*K/32] uint8),
-    flat.  Use with gemm(..., epilogue=W_TILED | A_TILED)."""
+def quant_act_tiled(x: torch.Tensor, s: torch.Tensor, offsets: torch.Tensor | None = None):
+    """quant_act in the tiled, expert-padded layout the prefill and grouped
+    GEMMs read -> (codes [rows*K/2] uint8, scales [rows*K/32] uint8), flat,
+    rows = macaq_quant_act_tiled_rows(M, E).  Use with
+    gemm(..., epilogue=W_TILED | A_TILED, M=M)."""
     _load()
     if s.dim() == 1:
         s = s[None]
     _need(x, "x", dim=2)
     _need(s, "s", torch.float32, 2)
     M, K = x.shape
-    rows = (M + 31) // 32 * 32
+    E = s.shape[0]
+    if offsets is not None:
+        _need(offsets, "offsets", torch.int32, 1)
+    rows = int(_load().macaq_quant_act_tiled_rows(M, E))
     codes = torch.empty(rows * K // 2, dtype=torch.uint8, device=x.device)
     scales = torch.empty(rows * K // 32, dtype=torch.uint8, device=x.device)
-    _check(macaq_quant_act_tiled(_ptr(x), _dtype_code(x), _ptr(s), M, K, _ptr(codes), _ptr(scales),
+    _check(macaq_quant_act_tiled(_ptr(x), _dtype_code(x), _ptr(s), _ptr(offsets), E, M, K, _ptr(codes), _ptr(scales),
                                  _stream(x.device)), "macaq_quant_act_tiled")
     return codes, scales
 
@@ -352,7 +357,7 @@ def gemm(a_codes, a_scales, w_codes, w_scales, offsets=None, out=None, workspace
         _need(a_scales, "a_scales", torch.uint8, 1)
         if M is None:
             raise ValueError("M is needed with tiled activation codes")
-        rows = (M + 31) // 32 * 32
+        rows = int(_load().macaq_quant_act_tiled_rows(M, E))
         if a_codes.numel() < rows * K // 2 or a_scales.numel() < rows * K // 32:
             raise ValueError("tiled activation buffers too small")
     else:

@@ -283,6 +283,17 @@ void act_quant_lane_kernel(
   // the expert walk in the loop loads an offset only when a row crosses it.
   int e = 0, e_a = 0, e_b = 0;
   int64_t e_end = 0;
+  // TILED with experts: the lane's expert's first row (e_beg) and first
+  // padded row (e_pad): expert e's rows start at padded row sum over
+  // e' < e of ceil(rows_e' / 32) * 32, so that every expert starts a block
+  int64_t e_beg = 0, e_pad = 0;
+  auto next_expert = [&]() {   // the lane's row crossed e_end
+    if constexpr (TILED) {
+      e_pad += (e_end - e_beg + 31) / 32 * 32;
+      e_beg = e_end;
+    }
+    e_end = offsets[++e + 1];
+  };
   if constexpr (!PLAIN) {
     const int64_t rl = r0 + lr < M ? r0 + lr : M - 1;   // this lane's first row
     if (rows_per_expert > 0) {
@@ -292,7 +303,19 @@ void act_quant_lane_kernel(
       // loads; a lane whose first row lies past that expert walks on
       e = expert_of(r0 < M ? r0 : M - 1);
       e_end = offsets[e + 1];
-      while (e + 1 < E && rl >= e_end) e_end = offsets[++e + 1];
+      if constexpr (TILED) {
+        e_beg = offsets[e];
+        // padded rows of the experts before e, summed over the wave's lanes
+        int64_t p = 0;
+        for (int e0 = 0; e0 < e; e0 += 64) {
+          const int ei = e0 + lane;
+          if (ei < e) p += ((int64_t)offsets[ei + 1] - offsets[ei] + 31) / 32 * 32;
+        }
+#pragma unroll
+        for (int d = 32; d >= 1; d >>= 1) p += __shfl_xor(p, d, 64);
+        e_pad = p;
+      }
+      while (e + 1 < E && rl >= e_end) next_expert();
     }
     if constexpr (SHARED) {
       const int64_t r_last = (rb + 4 * rows_per_wave < M ? rb + 4 * rows_per_wave : M) - 1;   // block's last row
@@ -366,7 +389,7 @@ void act_quant_lane_kernel(
       // expert of row r
       if (rows_per_expert > 0) e = (int)(r / rows_per_expert);
       else if (offsets != nullptr)
-        while (e + 1 < E && r >= e_end) e_end = offsets[++e + 1];
+        while (e + 1 < E && r >= e_end) next_expert();
     }
     if constexpr (!PLAIN && !SHARED) {
       // this lane's factors, reloaded when its row's expert changes
@@ -423,8 +446,9 @@ void act_quant_lane_kernel(
     }
     if (active) {
       if constexpr (TILED) {
-        const int64_t blk = (r >> 5) * (K >> 7) + (g >> 2);
-        const int rr = (int)(r & 31), c = (int)(g & 3);
+        const int64_t pr = offsets != nullptr ? e_pad + (r - e_beg) : r;   // (padded) row
+        const int64_t blk = (pr >> 5) * (K >> 7) + (g >> 2);
+        const int rr = (int)(pr & 31), c = (int)(g & 3);
         *reinterpret_cast<uint4*>(codes + blk * 2048 + rr * 64 + ((c ^ ((rr >> 2) & 3)) << 4)) = cw;
         scales[blk * 128 + rr * 4 + c] = (uint8_t)b;
       } else {
@@ -468,9 +492,19 @@ struct ActLaunch {
 // 7.2 us with it); longer waves keep the per-wave layout, which reads x
 // with better locality (down-prefill 37.9 vs 39.3 us, MoE per-token routing
 // 19.8 vs 22.6 us).
-static ActLaunch act_launch(int64_t M, int64_t K, bool plain) {
+static ActLaunch act_launch(int64_t M, int64_t K, bool plain, bool tiled = false) {
   ActLaunch a;
   a.gs_log2 = act_gs_log2(K / 32);
+  // tiled output: four rows per step (16-group segments) where that tiles a
+  // row as well as 32, so that a store instruction writes whole 128-byte
+  // lines (rows r and r+1 of a 128-wide K-tile are adjacent 64-byte halves
+  // of one line); measured on down-prefill M4096 K14336: 30.3 us against
+  // 31.0 (32 groups) and 33.6 (64 groups)
+  if (tiled && a.gs_log2 > 4) {
+    const int64_t KG = K / 32;
+    a.gs_log2 = (ceil_div(KG, 16) * 16 - KG <= ceil_div(KG, 32) * 32 - KG) ? 4 : 5;
+  }
+  if (const int force = tuning(MACAQ_TUNE_ACT_SEGMENT)) a.gs_log2 = force >= 64 ? 6 : (force >= 32 ? 5 : 4);
   const int64_t rw = 64 >> a.gs_log2;
   const int64_t nseg = ceil_div(K / 32, (int64_t)1 << a.gs_log2);
   const int64_t blocks = ceil_div(M, rw);
@@ -516,15 +550,16 @@ hipError_t launch_act_quant(const void* x, bool x_f32, bool reciprocal, const fl
   return hipGetLastError();
 }
 
-// The online transform of a dense layer (one expert) with its output in the
-// tiled layout of the prefill GEMM (K % 128 == 0).  The codes and scales
-// hold ceil(M / 32) * 32 rows; the rows past M are not written.
-hipError_t launch_act_quant_tiled(const void* x, bool x_f32, const float* s, int64_t M, int64_t K, uint8_t* codes,
-                                  uint8_t* scales, hipStream_t stream) {
+// The online transform with its output in the tiled layout of the prefill
+// and grouped GEMMs (K % 128 == 0).  Dense: ceil(M / 32) * 32 rows; grouped
+// (offsets != nullptr): expert e's rows start at padded row sum over e' < e
+// of ceil(rows_e' / 32) * 32.  Padding rows are not written.
+hipError_t launch_act_quant_tiled(const void* x, bool x_f32, const float* s, const int32_t* offsets, int E, int64_t M,
+                                  int64_t K, uint8_t* codes, uint8_t* scales, hipStream_t stream) {
   if (M <= 0) return hipSuccess;
-  const ActLaunch a = act_launch(M, K, false);
-  if (x_f32) launch_act_t<4, false, true>(a, x, s, nullptr, 1, 0, M, K, codes, scales, stream);
-  else launch_act_t<2, false, true>(a, x, s, nullptr, 1, 0, M, K, codes, scales, stream);
+  const ActLaunch a = act_launch(M, K, false, true);
+  if (x_f32) launch_act_t<4, false, true>(a, x, s, offsets, E, 0, M, K, codes, scales, stream);
+  else launch_act_t<2, false, true>(a, x, s, offsets, E, 0, M, K, codes, scales, stream);
   return hipGetLastError();
 }
 

@@ -45,8 +45,8 @@ hipError_t launch_decode_gemm(const uint8_t* A, const uint8_t* As, const uint8_t
 hipError_t launch_gemm_tiled(const uint8_t* A, const uint8_t* As, const int32_t* offsets, int E, const uint8_t* B,
                              const uint8_t* Bs, int64_t M, int64_t N, int64_t K, void* Y, int mode, bool a_tiled,
                              hipStream_t stream);
-hipError_t launch_act_quant_tiled(const void* x, bool x_f32, const float* s, int64_t M, int64_t K, uint8_t* codes,
-                                  uint8_t* scales, hipStream_t stream);
+hipError_t launch_act_quant_tiled(const void* x, bool x_f32, const float* s, const int32_t* offsets, int E, int64_t M,
+                                  int64_t K, uint8_t* codes, uint8_t* scales, hipStream_t stream);
 hipError_t launch_tile_weights(const uint8_t* wc, const uint8_t* ws, int64_t E, int64_t N, int64_t K, uint8_t* tc,
                                uint8_t* ts, hipStream_t stream);
 // output mode bits of the GEMM kernels (mx_common.h)
@@ -202,7 +202,7 @@ extern "C" {
 int macaq_version(void) { return kVersion; }
 
 int macaq_set_tuning(int knob, int value) {
-  static const int kMax[MACAQ_TUNE_COUNT] = {3, 64, 64, 2, 8, 4, 64};
+  static const int kMax[MACAQ_TUNE_COUNT] = {3, 64, 64, 2, 8, 4, 64, 64};
   if (knob < 0 || knob >= MACAQ_TUNE_COUNT)
     return fail(MACAQ_ERR_INVALID_ARG, "macaq_set_tuning: unknown knob " + std::to_string(knob));
   if (value < 0 || value > kMax[knob])
@@ -307,23 +307,31 @@ int macaq_quant_act(const void* x, macaq_dtype x_dtype, const float* s, const in
                            fn));
 }
 
-int macaq_quant_act_tiled(const void* x, macaq_dtype x_dtype, const float* s, int64_t M, int64_t K, uint8_t* a_codes,
-                          uint8_t* a_scales, void* stream) {
+int macaq_quant_act_tiled(const void* x, macaq_dtype x_dtype, const float* s, const int32_t* expert_offsets, int64_t E,
+                          int64_t M, int64_t K, uint8_t* a_codes, uint8_t* a_scales, void* stream) {
   const char* fn = "macaq_quant_act_tiled";
   if (int st = check_dtype(x_dtype, fn)) return st;
-  if (M < 0) return fail(MACAQ_ERR_INVALID_ARG, std::string(fn) + ": need M >= 0");
+  if (E < 1 || M < 0) return fail(MACAQ_ERR_INVALID_ARG, std::string(fn) + ": need E >= 1 and M >= 0");
+  if (E > 1 && expert_offsets == nullptr)
+    return fail(MACAQ_ERR_INVALID_ARG, std::string(fn) + ": expert_offsets required when E > 1");
   if (int st = check_k(K, fn)) return st;
   if (K % 128 != 0) return fail(MACAQ_ERR_UNSUPPORTED, std::string(fn) + ": the tiled layout needs K % 128 == 0");
   if (M == 0) return MACAQ_OK;
   if (!x || !s || !a_codes || !a_scales) return fail(MACAQ_ERR_INVALID_ARG, std::string(fn) + ": null pointer");
   if (!aligned(x, 16) || !aligned(a_codes, 16) || !aligned(s, 16))
     return fail(MACAQ_ERR_INVALID_ARG, std::string(fn) + ": x, s and a_codes must be 16-byte aligned");
+  if (E > 4096) return fail(MACAQ_ERR_UNSUPPORTED, std::string(fn) + ": too many experts");
   if (int st = check_device()) return st;
-  if (int st = check_inputs(fn, (hipStream_t)stream, nullptr, 1, M, s, K)) return st;
+  if (int st = check_inputs(fn, (hipStream_t)stream, expert_offsets, E, M, s, E * K)) return st;
   return finish(fn, (hipStream_t)stream,
-                hip_status(macaq::launch_act_quant_tiled(x, x_dtype == MACAQ_F32, s, M, K, a_codes, a_scales,
-                                                         (hipStream_t)stream),
+                hip_status(macaq::launch_act_quant_tiled(x, x_dtype == MACAQ_F32, s, E > 1 ? expert_offsets : nullptr,
+                                                         (int)E, M, K, a_codes, a_scales, (hipStream_t)stream),
                            fn));
+}
+
+size_t macaq_quant_act_tiled_rows(int64_t M, int64_t E) {
+  if (M <= 0 || E <= 0) return 0;
+  return (size_t)(E == 1 ? (M + 31) / 32 * 32 : (M + 31 * E + 31) / 32 * 32);
 }
 
 size_t macaq_quant_act_bytes(int64_t M, int64_t K) {
@@ -348,20 +356,19 @@ int macaq_linear_path(int64_t M, int64_t N, int64_t K, int64_t E, uint32_t flags
 }  // extern "C"
 
 namespace {
-// The unfused path of a dense layer with tiled weights stages the activation
-// in the same tiled layout (whole 32-row blocks); every other unfused path
-// stages it row-major.
-bool stage_tiled(int64_t E, uint32_t flags) { return E == 1 && (flags & MACAQ_W_TILED) != 0; }
+// The unfused path of a layer with tiled weights stages the activation in the
+// same tiled layout (whole 32-row blocks, each expert starting a block);
+// every other unfused path stages it row-major.
+bool stage_tiled(uint32_t flags) { return (flags & MACAQ_W_TILED) != 0; }
 
 // Staging of the activation codes and scales: their bytes, and where the
 // scales start.
-size_t stage_code_bytes(int64_t M, int64_t K, bool tiled) {
-  const int64_t rows = tiled ? (M + 31) / 32 * 32 : M;
-  return round_up((size_t)rows * (size_t)K / 2, 256);
+int64_t stage_rows(int64_t M, int64_t E, bool tiled) { return tiled ? (int64_t)macaq_quant_act_tiled_rows(M, E) : M; }
+size_t stage_code_bytes(int64_t M, int64_t E, int64_t K, bool tiled) {
+  return round_up((size_t)stage_rows(M, E, tiled) * (size_t)K / 2, 256);
 }
-size_t stage_bytes(int64_t M, int64_t K, bool tiled) {
-  const int64_t rows = tiled ? (M + 31) / 32 * 32 : M;
-  return stage_code_bytes(M, K, tiled) + round_up((size_t)rows * (size_t)K / 32, 256);
+size_t stage_bytes(int64_t M, int64_t E, int64_t K, bool tiled) {
+  return stage_code_bytes(M, E, K, tiled) + round_up((size_t)stage_rows(M, E, tiled) * (size_t)K / 32, 256);
 }
 }  // namespace
 
@@ -371,7 +378,7 @@ size_t macaq_linear_workspace_bytes(int64_t M, int64_t N, int64_t K, int64_t E, 
   if (M <= 0 || N <= 0 || K <= 0 || E <= 0) return 0;   // (MACAQ_W_TILED: the unfused path's workspace)
   const int path = macaq_linear_path(M, N, K, E, flags);
   if (path == MACAQ_PATH_FUSED) return 0;
-  if (path == MACAQ_PATH_UNFUSED) return stage_bytes(M, K, stage_tiled(E, flags)) + macaq_gemm_workspace_bytes(M, N, K, E);
+  if (path == MACAQ_PATH_UNFUSED) return stage_bytes(M, E, K, stage_tiled(flags)) + macaq_gemm_workspace_bytes(M, N, K, E);
   return 0;
 }
 
@@ -409,8 +416,8 @@ int macaq_gemm_ex(const uint8_t* a_codes, const uint8_t* a_scales, const int32_t
   const bool w_tiled = (epilogue & MACAQ_W_TILED) != 0;
   const bool a_tiled = (epilogue & MACAQ_A_TILED) != 0;
   epilogue &= ~(MACAQ_W_TILED | MACAQ_A_TILED);
-  if (a_tiled && (!w_tiled || E != 1))
-    return fail(MACAQ_ERR_UNSUPPORTED, std::string(fn) + ": tiled activations need tiled weights and E == 1");
+  if (a_tiled && !w_tiled)
+    return fail(MACAQ_ERR_UNSUPPORTED, std::string(fn) + ": tiled activations need tiled weights");
   if (int st = validate_gemm(a_codes, a_scales, expert_offsets, E, w_codes, w_scales, M, N, K, y, fn)) return st;
   int mode = 0;
   if (int st = output_mode(y_dtype, epilogue, N, y, fn, &mode)) return st;
@@ -515,16 +522,17 @@ int linear_impl(const void* x, macaq_dtype x_dtype, const float* s, const int32_
                   hip_status(macaq::launch_linear_fused(x, x_dtype == MACAQ_F32, s, w_codes, w_scales, M, N, K, y,
                                                         mode, st),
                              "macaq_linear (fused)"));
-  const bool a_tiled = stage_tiled(E, flags);
+  const bool a_tiled = stage_tiled(flags);
   uint8_t* a_codes = static_cast<uint8_t*>(workspace);
-  uint8_t* a_scales = a_codes + stage_code_bytes(M, K, a_tiled);
+  uint8_t* a_scales = a_codes + stage_code_bytes(M, E, K, a_tiled);
   const int32_t* off = E > 1 ? expert_offsets : nullptr;
-  if (int r = hip_status(a_tiled ? macaq::launch_act_quant_tiled(x, x_dtype == MACAQ_F32, s, M, K, a_codes, a_scales, st)
+  if (int r = hip_status(a_tiled ? macaq::launch_act_quant_tiled(x, x_dtype == MACAQ_F32, s, off, (int)E, M, K, a_codes,
+                                                                 a_scales, st)
                                  : macaq::launch_act_quant(x, x_dtype == MACAQ_F32, false, s, off, (int)E, 0, M, K,
                                                            a_codes, a_scales, st),
                          "macaq_linear (transform)"))
     return r;
-  void* gemm_ws = static_cast<uint8_t*>(workspace) + stage_bytes(M, K, a_tiled);
+  void* gemm_ws = static_cast<uint8_t*>(workspace) + stage_bytes(M, E, K, a_tiled);
   return finish(fn, st,
                 run_gemm(a_codes, a_scales, off, E, w_codes, w_scales, M, N, K, y, mode, gemm_ws, st,
                          "macaq_linear (gemm)", w_tiled, a_tiled));

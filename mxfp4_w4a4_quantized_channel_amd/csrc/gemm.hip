@@ -86,12 +86,11 @@ hipError_t launch_tile_weights(const uint8_t* wc, const uint8_t* ws, int64_t E, 
 // tiles cost no copy efficiency and keep three tiles in flight); 256x256
 // when that gives about one tile per CU, else 128x128 with two blocks per
 // CU.  a_tiled: the activation codes and scales are in the same tiled
-// layout (dense only).
+// layout (expert-padded for grouped layers).
 hipError_t launch_gemm_tiled(const uint8_t* A, const uint8_t* As, const int32_t* offsets, int E, const uint8_t* B,
                              const uint8_t* Bs, int64_t M, int64_t N, int64_t K, void* Y, int mode, bool a_tiled,
                              hipStream_t stream) {
   if (M <= 0) return hipSuccess;
-  if (a_tiled && offsets != nullptr) return hipErrorInvalidValue;
   const int64_t t256 = ceil_div(M, 256) * ceil_div(N, 256);
   int choice = (offsets == nullptr && t256 >= 240) ? 0 : 2;
   if (const int force = tuning(MACAQ_TUNE_GEMM_TILE)) choice = force - 1;

@@ -292,10 +292,13 @@ __device__ __forceinline__ int grouped_row_tiles(const int32_t* __restrict__ off
   }
   return total;
 }
+// Also the padded first row of the tile's expert minus its first row
+// (*a_shift): in the expert-padded tiled activation layout, expert e's rows
+// start at padded row P_e = sum over e' < e of ceil(rows_e' / 32) * 32.
 template <int BM>
 __device__ __forceinline__ bool grouped_tile(const int32_t* __restrict__ offsets, int E, int lane, int tm, int* e_out,
-                                             int64_t* row_begin, int64_t* row_end) {
-  int base = 0;
+                                             int64_t* row_begin, int64_t* row_end, int64_t* a_shift) {
+  int base = 0, pbase = 0;
   for (int e0 = 0; e0 < E; e0 += 64) {
     const int e = e0 + lane;
     int64_t b = 0, en = 0;
@@ -304,16 +307,21 @@ __device__ __forceinline__ bool grouped_tile(const int32_t* __restrict__ offsets
       en = offsets[e + 1];
     }
     const int t = e < E ? (int)((en - b + BM - 1) / BM) : 0;
+    const int pc = e < E ? (int)((en - b + 31) / 32 * 32) : 0;   // padded rows of expert e
     const int incl = base + wave_prefix_sum(t, lane), excl = incl - t;
+    const int pincl = pbase + wave_prefix_sum(pc, lane), pexcl = pincl - pc;
     const unsigned long long hit = __ballot(t > 0 && tm >= excl && tm < incl);
     if (hit != 0ull) {
       const int l = __ffsll(hit) - 1;
       *e_out = e0 + l;
-      *row_begin = __shfl(b, l, 64) + (int64_t)(tm - __shfl(excl, l, 64)) * BM;
+      const int64_t first = __shfl(b, l, 64);
+      *row_begin = first + (int64_t)(tm - __shfl(excl, l, 64)) * BM;
       *row_end = __shfl(en, l, 64);
+      *a_shift = (int64_t)__shfl(pexcl, l, 64) - first;
       return true;
     }
     base = __shfl(incl, 63, 64);
+    pbase = __shfl(pincl, 63, 64);
   }
   return false;
 }
@@ -326,8 +334,9 @@ __device__ __forceinline__ bool grouped_tile(const int32_t* __restrict__ offsets
 // (measured with 256-wide tiles: 56 against 33 B/clk per CU for such copies
 // in isolation; the down-prefill layer's copies alone take 38 us of loop
 // time tiled against 118 us row-major with 128-wide K-tiles).  AT: the
-// activation codes and scales in the same tiled layout (dense layers only:
-// row tiles start at multiples of 32).
+// activation codes and scales in the same tiled layout; for grouped layers
+// every expert's rows start on a 32-row block (expert-padded), so that row
+// tiles, which start at expert boundaries, start on blocks too.
 
 // The MFMAs of one sub-step, J the sub-step (op_sel picks scale byte J).
 template <int J, int FM, int FN>
@@ -383,9 +392,9 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, MINB) void gemm_mxfp4_pipe_
   int tm, tn;
   tile_of_block((int)blockIdx.x, active_m * tiles_n, active_m, tiles_n, group_m, &tm, &tn);
   int e = 0;
-  int64_t row_begin = 0, row_end = M;
+  int64_t row_begin = 0, row_end = M, a_shift = 0;   // a_shift: tiled activation row = row + a_shift
   if (offsets != nullptr) {
-    if (!grouped_tile<BM>(offsets, E, lane0, tm, &e, &row_begin, &row_end)) return;
+    if (!grouped_tile<BM>(offsets, E, lane0, tm, &e, &row_begin, &row_end, &a_shift)) return;
   } else {
     row_begin = (int64_t)tm * BM;
     if (row_begin >= M) return;
@@ -424,7 +433,8 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, MINB) void gemm_mxfp4_pipe_
       int64_t gr = row_begin + row;
       if (gr >= row_end) gr = row_end - 1;
       if constexpr (AT) {
-        csrc[i] = A + (gr >> 5) * (K >> 7) * 2048 + (gr & 31) * 64 + (lane % kCPR) * 16;
+        const int64_t pr = gr + a_shift;
+        csrc[i] = A + (pr >> 5) * (K >> 7) * 2048 + (pr & 31) * 64 + (lane % kCPR) * 16;
         ctile |= 1u << i;
       } else {
         csrc[i] = A + gr * KB + c * 16;
@@ -450,7 +460,8 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, MINB) void gemm_mxfp4_pipe_
       int64_t gr = row_begin + row;
       if (gr >= row_end) gr = row_end - 1;
       if constexpr (AT) {
-        ssrc[i] = As + (gr >> 5) * (K >> 7) * 128 + (gr & 31) * 4 + part * 4;
+        const int64_t pr = gr + a_shift;
+        ssrc[i] = As + (pr >> 5) * (K >> 7) * 128 + (pr & 31) * 4 + part * 4;
         stile |= 1u << i;
       } else {
         ssrc[i] = As + gr * KG + part * 4;

@@ -242,7 +242,9 @@ def test_tiled_weights_validation():
     # a dense layer with tiled weights stages its activation tiled: whole 32-row blocks
     assert L.macaq_linear_workspace_bytes(1, 25600, 5120, 1, mx.PATH_AUTO | T) == L.macaq_quant_act_bytes(32, 5120)
     assert L.macaq_linear_workspace_bytes(33, 4096, 4096, 1, T) == L.macaq_quant_act_bytes(64, 4096)
-    assert L.macaq_linear_workspace_bytes(33, 1024, 3072, 4, T) == L.macaq_quant_act_bytes(33, 3072)   # grouped: row-major
+    # grouped: every expert starts a 32-row block, at most ceil((M + 31 E) / 32) * 32 rows
+    assert L.macaq_quant_act_tiled_rows(33, 4) == 160
+    assert L.macaq_linear_workspace_bytes(33, 1024, 3072, 4, T) == L.macaq_quant_act_bytes(160, 3072)
 
 
 def test_set_tuning_validation_and_restore():
@@ -251,7 +253,7 @@ def test_set_tuning_validation_and_restore():
     choice."""
     mx.lib()
     assert mx.macaq_set_tuning(-1, 0) == INVALID
-    assert mx.macaq_set_tuning(7, 0) == INVALID
+    assert mx.macaq_set_tuning(8, 0) == INVALID
     assert mx.macaq_set_tuning(mx.TUNE_GEMM_TILE, 4) == INVALID
     assert mx.macaq_set_tuning(mx.TUNE_ACT_SHARED_S, -1) == INVALID
     assert mx.set_tuning(mx.TUNE_GEMM_TILE, 3) == 0

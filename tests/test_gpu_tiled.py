@@ -187,41 +187,54 @@ def test_grouped_gemm_many_experts(E):
         assert ok, f"expert {e}: worst {worst:.3g}"
 
 
-def tiled_rows_reference(codes: np.ndarray, scales: np.ndarray, M: int):
-    """The activation rows in the tiled layout, padded to whole 32-row blocks
-    (the padding rows are left out of the comparison by the caller)."""
-    rows = (M + 31) // 32 * 32
+def padded_rows(offsets, M: int):
+    """Padded row of every row (expert e's rows start at the sum over e' < e
+    of ceil(rows_e' / 32) * 32) and the buffer's row count, as the header
+    defines them."""
+    if offsets is None:
+        return np.arange(M), (M + 31) // 32 * 32
+    off = np.asarray(offsets, dtype=np.int64)
+    E = len(off) - 1
+    cnt = np.diff(off)
+    pstart = np.concatenate([[0], np.cumsum((cnt + 31) // 32 * 32)])
+    e_of = np.searchsorted(off, np.arange(M), side="right") - 1
+    return pstart[e_of] + (np.arange(M) - off[e_of]), (M + 31 * E + 31) // 32 * 32
+
+
+def tiled_rows_reference(codes: np.ndarray, scales: np.ndarray, M: int, offsets=None):
+    """The activation rows in the tiled layout at their padded rows, and a
+    mask of the bytes that belong to real rows (padding is not compared)."""
+    prow, rows = padded_rows(offsets, M)
     pc = np.zeros((1, rows, codes.shape[1]), np.uint8)
     ps = np.zeros((1, rows, scales.shape[1]), np.uint8)
-    pc[0, :M], ps[0, :M] = codes, scales
+    pc[0, prow], ps[0, prow] = codes, scales
+    real = np.zeros((1, rows, 1), bool)
+    real[0, prow] = True
     rc, rs = tiled_reference(pc, ps)
-    return rc.reshape(-1), rs.reshape(-1)
+    mc, ms = tiled_reference(np.broadcast_to(real, pc.shape).astype(np.uint8),
+                             np.broadcast_to(real, ps.shape).astype(np.uint8))
+    return rc.reshape(-1), rs.reshape(-1), mc.reshape(-1) == 1, ms.reshape(-1) == 1
 
 
-def _valid_row_mask(M: int, K: int, per_row: int):
-    """Mask of the bytes of real rows (< M) in a tiled buffer of whole blocks;
-    per_row = bytes of one row in one 128-wide K-tile (64 codes or 4 scales)."""
-    rows = (M + 31) // 32 * 32
-    T = K // 128
-    r = np.arange(rows).reshape(rows // 32, 1, 32, 1)
-    mask = np.broadcast_to(r < M, (rows // 32, T, 32, per_row))
-    return mask.reshape(-1)
-
-
-@pytest.mark.parametrize("M,K,dt", [(1, 256, torch.bfloat16), (37, 1152, torch.bfloat16), (64, 512, torch.float32),
-                                    (300, 3072, torch.bfloat16), (33, 14336, torch.bfloat16)])
-def test_quant_act_tiled_bit_exact(M, K, dt):
+@pytest.mark.parametrize("M,K,dt,counts", [(1, 256, torch.bfloat16, None), (37, 1152, torch.bfloat16, None),
+                                           (64, 512, torch.float32, None), (300, 3072, torch.bfloat16, None),
+                                           (33, 14336, torch.bfloat16, None),
+                                           (300, 1024, torch.bfloat16, [3, 0, 130, 33, 0, 1, 133]),
+                                           (96, 3072, torch.bfloat16, [0, 32, 0, 64, 0])])
+def test_quant_act_tiled_bit_exact(M, K, dt, counts):
     """macaq_quant_act_tiled writes the oracle's codes and scale bytes in the
-    tiled layout (rows past M of the last block are not compared)."""
-    say(f"quant_act_tiled M{M} K{K} {dt}")
+    tiled layout, each expert from its padded row on (padding rows are not
+    compared)."""
+    say(f"quant_act_tiled M{M} K{K} {dt} counts={counts}")
     rng = np.random.default_rng(M + K)
+    E = 1 if counts is None else len(counts)
+    off = None if counts is None else np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
     xf = rng.standard_normal((M, K)) * np.where(rng.random(K) < 0.01, 50.0, 1.0)
     x = torch.from_numpy(xf).to(dt)
-    s = torch.from_numpy(rng.uniform(0.25, 4.0, K).astype(np.float32))
-    codes, scales = mx.quant_act_tiled(x.to(DEV), s.to(DEV))
-    rc, rs = oracle.quant_act(host(x), s.numpy()[None])
-    tc, ts = tiled_rows_reference(rc, rs, M)
-    mc, ms = _valid_row_mask(M, K, 64), _valid_row_mask(M, K, 4)
+    s = torch.from_numpy(rng.uniform(0.25, 4.0, (E, K)).astype(np.float32))
+    codes, scales = mx.quant_act_tiled(x.to(DEV), s.to(DEV), None if off is None else torch.from_numpy(off).to(DEV))
+    rc, rs = oracle.quant_act(host(x), s.numpy(), off)
+    tc, ts, mc, ms = tiled_rows_reference(rc, rs, M, off)
     assert np.array_equal(codes.cpu().numpy()[mc], tc[mc])
     assert np.array_equal(scales.cpu().numpy()[ms], ts[ms])
 
@@ -262,3 +275,28 @@ def test_tiled_activation_gemm_equals_row_major(name, shape, tile, out, tune):
         y_ref, S = oracle.gemm(ac.cpu().numpy(), asc.cpu().numpy(), wc[0].cpu().numpy(), wsc[0].cpu().numpy())
         ok, worst, nw = oracle.within_tolerance(y_at.cpu().numpy(), y_ref, S, RTOL)
         assert ok, f"worst {worst:.3g} normwise {nw:.3g}"
+
+
+@pytest.mark.parametrize("counts", [[70, 0, 131, 1, 0], [0, 3, 0, 0, 300, 29, 64, 1], [8177, 12, 3]])
+def test_grouped_tiled_activation_gemm(counts):
+    """The grouped GEMM on expert-padded tiled activations equals the grouped
+    GEMM on row-major activations (same tiled weights) bit for bit, the
+    linear call with tiled weights equals both, and each expert's rows are
+    within the oracle's bound."""
+    say(f"grouped A-tiled gemm counts={counts}")
+    E, N, K = len(counts), 96, 1024
+    off_np = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    off = torch.from_numpy(off_np).to(DEV)
+    M = int(off_np[-1])
+    x, s, ac, asc, wc, wsc = _operands(M, N, K, E=E, seed=M + E, offsets=off)
+    tc, ts = mx.tile_weights(wc, wsc)
+    atc, ats = mx.quant_act_tiled(x, s, off)
+    y_rm = mx.gemm(ac, asc, tc, ts, off, epilogue=mx.W_TILED)
+    y_at = mx.gemm(atc, ats, tc, ts, off, epilogue=mx.W_TILED | mx.A_TILED, M=M)
+    y_lin = mx.linear(x, s, tc, ts, off, flags=mx.W_TILED)
+    torch.cuda.synchronize()
+    assert torch.equal(y_at, y_rm)
+    assert torch.equal(y_lin, y_rm)
+    y_ref, S = oracle.gemm(ac.cpu().numpy(), asc.cpu().numpy(), wc.cpu().numpy(), wsc.cpu().numpy(), off_np)
+    ok, worst, nw = oracle.within_tolerance(y_at.cpu().numpy(), y_ref, S, RTOL)
+    assert ok, f"worst {worst:.3g} normwise {nw:.3g}"
