@@ -131,7 +131,9 @@ enum {
  *   MACAQ_TUNE_DECODE_STAGES      ring slots per decode wave (2..4; 32-row blocks)
  *   MACAQ_TUNE_DECODE_ROWS        weight rows per decode block (32 or 64)
  *   MACAQ_TUNE_ACT_SEGMENT        groups per row segment of a wave of the
- *                                 activation kernel (16, 32 or 64) */
+ *                                 activation kernel (16, 32 or 64)
+ *   MACAQ_TUNE_DECODE_SPLIT       K split of the decode GEMM: the number of
+ *                                 blocks per row tile (1..16; 1 = no split) */
 enum {
   MACAQ_TUNE_GEMM_TILE = 0,
   MACAQ_TUNE_GEMM_GROUP_M = 1,
@@ -141,7 +143,8 @@ enum {
   MACAQ_TUNE_DECODE_STAGES = 5,
   MACAQ_TUNE_DECODE_ROWS = 6,
   MACAQ_TUNE_ACT_SEGMENT = 7,
-  MACAQ_TUNE_COUNT = 8
+  MACAQ_TUNE_DECODE_SPLIT = 8,
+  MACAQ_TUNE_COUNT = 9
 };
 
 /* Library version as major*10000 + minor*100 + patch. */
@@ -315,7 +318,11 @@ size_t macaq_quant_act_tiled_rows(int64_t M, int64_t E);
  *   w_scales [E][N][K/32]; expert_offsets [E+1] device (NULL when E == 1);
  *   y [M][N] fp32 out.
  * workspace: device scratch of macaq_gemm_workspace_bytes(M, N, K, E) bytes,
- * 256-byte aligned; NULL when that is 0 (the current kernels need none).
+ * 256-byte aligned; NULL when that is 0.  The decode GEMM (M <= 32, E == 1,
+ * row-major weights) splits K over two blocks per 32-row tile when the row
+ * tiles cannot fill the GPU; the two fp32 partial sums (2 * M * N * 4 bytes)
+ * go to the workspace and a second kernel adds them, part 0 first.
+ * Calls that share a workspace must not overlap in time.
  * Requires K % 128 == 0; K >= 128; all code pointers 16-byte aligned and
  * scale pointers 4-byte aligned.
  */

@@ -27,7 +27,8 @@ hipError_t launch_gemm(const uint8_t* A, const uint8_t* As, const int32_t* offse
                        void* Y, int mode, hipStream_t stream);
 hipError_t launch_linear_fused(const void* x, bool x_f32, const float* s, const uint8_t* B,
                                const uint8_t* Bs, int64_t M, int64_t N, int64_t K, void* Y, int mode,
-                               hipStream_t stream);
+                               float* part_ws, hipStream_t stream);
+size_t decode_workspace_bytes(int64_t M, int64_t N, int64_t K, bool fused);
 bool linear_fused_supported(int64_t M, int64_t N, int64_t K, int64_t E);
 bool decode_supported(int64_t M, int64_t N, int64_t K, int64_t E);
 hipError_t launch_hessian(const void* x, bool x_f32, const float* s, const int32_t* offsets, int E, int64_t T,
@@ -41,7 +42,7 @@ hipError_t launch_flip_rounds(const float* H, int E, int64_t row0, int64_t rows,
                               int max_rounds, const double* G, uint8_t* codes, const uint8_t* scales, int32_t* moves,
                               hipStream_t stream);
 hipError_t launch_decode_gemm(const uint8_t* A, const uint8_t* As, const uint8_t* W, const uint8_t* Ws, int64_t M,
-                              int64_t N, int64_t K, void* Y, int mode, hipStream_t stream);
+                              int64_t N, int64_t K, void* Y, int mode, float* part_ws, hipStream_t stream);
 hipError_t launch_gemm_tiled(const uint8_t* A, const uint8_t* As, const int32_t* offsets, int E, const uint8_t* B,
                              const uint8_t* Bs, int64_t M, int64_t N, int64_t K, void* Y, int mode, bool a_tiled,
                              hipStream_t stream);
@@ -202,7 +203,7 @@ extern "C" {
 int macaq_version(void) { return kVersion; }
 
 int macaq_set_tuning(int knob, int value) {
-  static const int kMax[MACAQ_TUNE_COUNT] = {3, 64, 64, 2, 8, 4, 64, 64};
+  static const int kMax[MACAQ_TUNE_COUNT] = {3, 64, 64, 2, 8, 4, 64, 64, 16};
   if (knob < 0 || knob >= MACAQ_TUNE_COUNT)
     return fail(MACAQ_ERR_INVALID_ARG, "macaq_set_tuning: unknown knob " + std::to_string(knob));
   if (value < 0 || value > kMax[knob])
@@ -340,8 +341,9 @@ size_t macaq_quant_act_bytes(int64_t M, int64_t K) {
 }
 
 size_t macaq_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, int64_t E) {
-  (void)M; (void)N; (void)K; (void)E;
-  return 0;  // no GEMM kernel needs scratch memory
+  // the decode GEMM's K-split partial sums (row-major weights, M <= 32, few row tiles)
+  if (M <= 0 || N <= 0 || K <= 0 || E != 1 || !macaq::decode_supported(M, N, K, E)) return 0;
+  return round_up(macaq::decode_workspace_bytes(M, N, K, false), 256);
 }
 
 int macaq_linear_path(int64_t M, int64_t N, int64_t K, int64_t E, uint32_t flags) {
@@ -377,7 +379,7 @@ extern "C" {
 size_t macaq_linear_workspace_bytes(int64_t M, int64_t N, int64_t K, int64_t E, uint32_t flags) {
   if (M <= 0 || N <= 0 || K <= 0 || E <= 0) return 0;   // (MACAQ_W_TILED: the unfused path's workspace)
   const int path = macaq_linear_path(M, N, K, E, flags);
-  if (path == MACAQ_PATH_FUSED) return 0;
+  if (path == MACAQ_PATH_FUSED) return round_up(macaq::decode_workspace_bytes(M, N, K, true), 256);
   if (path == MACAQ_PATH_UNFUSED) return stage_bytes(M, E, K, stage_tiled(flags)) + macaq_gemm_workspace_bytes(M, N, K, E);
   return 0;
 }
@@ -386,13 +388,14 @@ namespace {
 int run_gemm(const uint8_t* a_codes, const uint8_t* a_scales, const int32_t* expert_offsets, int64_t E,
              const uint8_t* w_codes, const uint8_t* w_scales, int64_t M, int64_t N, int64_t K, void* y, int mode,
              void* workspace, hipStream_t stream, const char* fn, bool w_tiled = false, bool a_tiled = false) {
-  (void)workspace;
   if (w_tiled)
     return hip_status(macaq::launch_gemm_tiled(a_codes, a_scales, E > 1 ? expert_offsets : nullptr, (int)E, w_codes,
                                                w_scales, M, N, K, y, mode, a_tiled, stream),
                       fn);
   if (macaq::decode_supported(M, N, K, E))
-    return hip_status(macaq::launch_decode_gemm(a_codes, a_scales, w_codes, w_scales, M, N, K, y, mode, stream), fn);
+    return hip_status(macaq::launch_decode_gemm(a_codes, a_scales, w_codes, w_scales, M, N, K, y, mode,
+                                                static_cast<float*>(workspace), stream),
+                      fn);
   return hip_status(macaq::launch_gemm(a_codes, a_scales, E > 1 ? expert_offsets : nullptr, (int)E, w_codes,
                                        w_scales, M, N, K, y, mode, stream),
                     fn);
@@ -520,7 +523,7 @@ int linear_impl(const void* x, macaq_dtype x_dtype, const float* s, const int32_
   if (fused)
     return finish(fn, st,
                   hip_status(macaq::launch_linear_fused(x, x_dtype == MACAQ_F32, s, w_codes, w_scales, M, N, K, y,
-                                                        mode, st),
+                                                        mode, static_cast<float*>(workspace), st),
                              "macaq_linear (fused)"));
   const bool a_tiled = stage_tiled(flags);
   uint8_t* a_codes = static_cast<uint8_t*>(workspace);

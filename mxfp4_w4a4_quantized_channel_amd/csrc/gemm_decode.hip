@@ -167,7 +167,7 @@ __global__ __launch_bounds__(64 * WAVES) void decode_gemm_kernel(
     const uint8_t* __restrict__ A, const uint8_t* __restrict__ As,     // activation codes/scales (unfused)
     const void* __restrict__ x, const float* __restrict__ s,           // activations and scale (fused)
     const uint8_t* __restrict__ W, const uint8_t* __restrict__ Ws, int64_t M, int64_t N, int64_t K,
-    void* __restrict__ Y, int out_mode) {
+    void* __restrict__ Y, int out_mode, float* __restrict__ part_ws, int ksplit) {
   constexpr int EB = dec_eb<XT>;
   using S = DecStage<AK, EB, RT>;
   constexpr bool FUSED = AK == 0;     // resident activation, transformed before the loop
@@ -199,9 +199,12 @@ __global__ __launch_bounds__(64 * WAVES) void decode_gemm_kernel(
 
   // ---- this wave's chunks and the copy sources of chunk 0 (rows past N or
   // M repeat the last row; their results are not stored)
-  const int per_wave = (kc + WAVES - 1) / WAVES;
-  const int c0 = wave * per_wave;
-  const int c1 = (c0 + per_wave) < kc ? (c0 + per_wave) : kc;
+  // K split over blockIdx.y (ksplit parts of the chunks), then over the waves
+  const int part = (int)blockIdx.y;
+  const int cb0 = (int)((int64_t)kc * part / ksplit), cb1 = (int)((int64_t)kc * (part + 1) / ksplit);
+  const int per_wave = (cb1 - cb0 + WAVES - 1) / WAVES;
+  const int c0 = cb0 + wave * per_wave;
+  const int c1 = (c0 + per_wave) < cb1 ? (c0 + per_wave) : cb1;
   const uint8_t* wsrc[4 * RT];
 #pragma unroll
   for (int i = 0; i < 4 * RT; ++i) {
@@ -422,6 +425,19 @@ __global__ __launch_bounds__(64 * WAVES) void decode_gemm_kernel(
     }
   }
   __syncthreads();
+  if (ksplit > 1) {
+    // this part's fp32 sums of the block's columns, [part][M][N]; the split
+    // reduce kernel adds the parts in order and applies the output mode
+    float* pw = part_ws + (int64_t)part * M * N;
+    for (int idx = tid; idx < kRows * 32; idx += kThreads) {
+      const int n = idx % kRows, m = idx / kRows;
+      float v = red[n * 32 + m];
+#pragma unroll
+      for (int w = 1; w < WAVES; ++w) v = v + red[(w * kRows + n) * 32 + m];
+      if (m < M && n0 + n < N) pw[(int64_t)m * N + n0 + n] = v;
+    }
+    return;
+  }
   if (out_mode & kOutSwiGLU) {
     // columns (2j, 2j+1) = (gate, up) -> column n0/2 + j of the [M][N/2] output
     constexpr int kPairs = kRows / 2;
@@ -444,6 +460,31 @@ __global__ __launch_bounds__(64 * WAVES) void decode_gemm_kernel(
     for (int w = 1; w < WAVES; ++w) v = v + red[(w * kRows + n) * 32 + m];
     if (m < M && n0 + n < N) store_out(Y, (int64_t)m * N + n0 + n, v, out_mode);
   }
+}
+
+// Sum of the K-split parts of a decode GEMM, in part order, with the output
+// mode: y[m][n] = p0[m][n] + p1[m][n] (+ ...), or for SwiGLU
+// y[m][j] = silu(g) * u over the summed column pair (2j, 2j+1).
+__global__ void decode_split_reduce_kernel(const float* __restrict__ part_ws, int ksplit, int64_t M, int64_t N,
+                                           void* __restrict__ Y, int out_mode) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t MN = M * N;
+  if (out_mode & kOutSwiGLU) {
+    const int64_t half = N >> 1;
+    if (i >= M * half) return;
+    const int64_t m = i / half, j = i % half;
+    float g = part_ws[m * N + 2 * j], u = part_ws[m * N + 2 * j + 1];
+    for (int p = 1; p < ksplit; ++p) {
+      g = g + part_ws[p * MN + m * N + 2 * j];
+      u = u + part_ws[p * MN + m * N + 2 * j + 1];
+    }
+    store_out(Y, i, silu_times(g, u), out_mode);
+    return;
+  }
+  if (i >= MN) return;
+  float v = part_ws[i];
+  for (int p = 1; p < ksplit; ++p) v = v + part_ws[p * MN + i];
+  store_out(Y, i, v, out_mode);
 }
 
 // ---------------------------------------------------------------- host side
@@ -473,8 +514,30 @@ static size_t wave_lds_bytes(int stages, int ak, int eb, int rt) {
 }
 
 struct DecodeConfig {
-  int waves, stages, ak, eb, rt;
+  int waves, stages, ak, eb, rt, ksplit;
 };
+
+// K split of the decode GEMM: with fewer 32-row blocks than the 256 CUs, the
+// K range of each row tile is cut into `ksplit` parts taken by as many blocks
+// (the largest split up to 4 whose blocks fit two per CU and still leave each
+// of a block's 4 waves 8 or more 256-wide chunks), so that every CU streams
+// weights.  The parts' fp32 partial sums go to the caller's workspace and a
+// second kernel adds them in part order.  Measured on down-proj N5120 K25600
+// (160 row tiles, split 3): fused M1 17.1 us against 18.4 unsplit, M8 21.7
+// against 22.9, M32 29.9 against 30.4; a split into 2 (320 blocks, a second
+// wave of 64) was slower than none.  macaq_set_tuning(MACAQ_TUNE_DECODE_SPLIT)
+// forces the number of parts (1 = no split).
+constexpr int kDecCUs = 256;
+constexpr int kDecSplitWaves = 4;
+static int decode_ksplit(int64_t N, int64_t K, int rt) {
+  const int64_t tiles = ceil_div(N, kDecRows * rt);
+  const int kc = (int)(K >> 8);
+  int ks = 1;
+  if (rt == 1 && tiles < kDecCUs)
+    while (ks < 4 && tiles * (ks + 1) <= 2 * kDecCUs && kc / ((ks + 1) * kDecSplitWaves) >= 8) ++ks;
+  if (const int force = tuning(MACAQ_TUNE_DECODE_SPLIT)) ks = force;
+  return ks < kc ? ks : kc;   // at least one chunk per part
+}
 
 static size_t decode_lds_bytes(const DecodeConfig& d, int64_t M, int64_t K) {
   size_t b = (size_t)d.waves * wave_lds_bytes(d.stages, d.ak, d.eb, d.rt);
@@ -511,6 +574,13 @@ static DecodeConfig decode_config(int64_t M, int64_t N, int64_t K, bool fused, i
     d.stages = max_stages;
     while (d.stages > 2 && decode_lds_bytes(d, M, K) > budget) --d.stages;
   }
+  d.ksplit = decode_ksplit(N, K, d.rt);
+  if (d.ksplit > 1 && d.rt == 1) {   // split blocks: 4 waves, two blocks per CU
+    d.waves = kDecSplitWaves;
+    const size_t split_budget = ceil_div(N, kDecRows) * d.ksplit > kDecCUs ? kDecLdsMax / 2 : kDecLdsMax;
+    d.stages = max_stages;
+    while (d.stages > 2 && decode_lds_bytes(d, M, K) > split_budget) --d.stages;
+  }
   if (d.rt == 1) {   // forced ring shapes, kept only where they fit in LDS
     DecodeConfig f = d;
     if (const int force = tuning(MACAQ_TUNE_DECODE_WAVES)) f.waves = force == 8 ? 8 : 4;
@@ -527,47 +597,62 @@ bool decode_supported(int64_t M, int64_t N, int64_t K, int64_t E) {
 template <int WAVES, int STAGES, int AK, typename XT, int RT>
 static hipError_t launch_decode_w(const uint8_t* A, const uint8_t* As, const void* x, const float* s,
                                   const uint8_t* W, const uint8_t* Ws, int64_t M, int64_t N, int64_t K, void* Y,
-                                  int mode, size_t lds, hipStream_t stream) {
+                                  int mode, size_t lds, float* part_ws, int ksplit, hipStream_t stream) {
   static_assert(DecWaveLds<STAGES, AK, dec_eb<XT>, RT>::kBytes >= 32 * RT * 32 * 4,
                 "partial sums must fit in the rings");
   static const hipError_t attr = hipFuncSetAttribute((const void*)decode_gemm_kernel<WAVES, STAGES, AK, XT, RT>,
                                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)kDecLdsMax);
   if (attr != hipSuccess) return attr;
   decode_gemm_kernel<WAVES, STAGES, AK, XT, RT>
-      <<<dim3((unsigned)ceil_div(N, kDecRows * RT)), dim3(64 * WAVES), lds, stream>>>(A, As, x, s, W, Ws, M, N, K, Y,
-                                                                                      mode);
+      <<<dim3((unsigned)ceil_div(N, kDecRows * RT), (unsigned)ksplit), dim3(64 * WAVES), lds, stream>>>(
+          A, As, x, s, W, Ws, M, N, K, Y, mode, part_ws, ksplit);
+  if (ksplit > 1) {
+    if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
+    const int64_t outs = (mode & kOutSwiGLU) ? M * (N >> 1) : M * N;
+    decode_split_reduce_kernel<<<dim3((unsigned)ceil_div(outs, 256)), dim3(256), 0, stream>>>(part_ws, ksplit, M, N, Y,
+                                                                                              mode);
+  }
   return hipGetLastError();
 }
 
 template <int AK, typename XT>
 static hipError_t launch_decode_impl(const DecodeConfig& d, const uint8_t* A, const uint8_t* As, const void* x,
                                      const float* s, const uint8_t* W, const uint8_t* Ws, int64_t M, int64_t N,
-                                     int64_t K, void* Y, int mode, hipStream_t stream) {
+                                     int64_t K, void* Y, int mode, float* part_ws, hipStream_t stream) {
+  if (d.ksplit > 1 && part_ws == nullptr) return hipErrorInvalidValue;
   const size_t lds = decode_lds_bytes(d, M, K);
   if (lds > kDecLdsMax) return hipErrorInvalidValue;
   if (d.rt == 2) {
-    if (d.stages >= 3) return launch_decode_w<2, 3, AK, XT, 2>(A, As, x, s, W, Ws, M, N, K, Y, mode, lds, stream);
-    return launch_decode_w<2, 2, AK, XT, 2>(A, As, x, s, W, Ws, M, N, K, Y, mode, lds, stream);
+    if (d.stages >= 3) return launch_decode_w<2, 3, AK, XT, 2>(A, As, x, s, W, Ws, M, N, K, Y, mode, lds, part_ws, d.ksplit, stream);
+    return launch_decode_w<2, 2, AK, XT, 2>(A, As, x, s, W, Ws, M, N, K, Y, mode, lds, part_ws, d.ksplit, stream);
   }
   if (d.waves == 8) {
-    if (d.stages == 4) return launch_decode_w<8, 4, AK, XT, 1>(A, As, x, s, W, Ws, M, N, K, Y, mode, lds, stream);
-    if (d.stages == 3) return launch_decode_w<8, 3, AK, XT, 1>(A, As, x, s, W, Ws, M, N, K, Y, mode, lds, stream);
-    return launch_decode_w<8, 2, AK, XT, 1>(A, As, x, s, W, Ws, M, N, K, Y, mode, lds, stream);
+    if (d.stages == 4) return launch_decode_w<8, 4, AK, XT, 1>(A, As, x, s, W, Ws, M, N, K, Y, mode, lds, part_ws, d.ksplit, stream);
+    if (d.stages == 3) return launch_decode_w<8, 3, AK, XT, 1>(A, As, x, s, W, Ws, M, N, K, Y, mode, lds, part_ws, d.ksplit, stream);
+    return launch_decode_w<8, 2, AK, XT, 1>(A, As, x, s, W, Ws, M, N, K, Y, mode, lds, part_ws, d.ksplit, stream);
   }
-  if (d.stages == 4) return launch_decode_w<4, 4, AK, XT, 1>(A, As, x, s, W, Ws, M, N, K, Y, mode, lds, stream);
-  if (d.stages == 3) return launch_decode_w<4, 3, AK, XT, 1>(A, As, x, s, W, Ws, M, N, K, Y, mode, lds, stream);
-  return launch_decode_w<4, 2, AK, XT, 1>(A, As, x, s, W, Ws, M, N, K, Y, mode, lds, stream);
+  if (d.stages == 4) return launch_decode_w<4, 4, AK, XT, 1>(A, As, x, s, W, Ws, M, N, K, Y, mode, lds, part_ws, d.ksplit, stream);
+  if (d.stages == 3) return launch_decode_w<4, 3, AK, XT, 1>(A, As, x, s, W, Ws, M, N, K, Y, mode, lds, part_ws, d.ksplit, stream);
+  return launch_decode_w<4, 2, AK, XT, 1>(A, As, x, s, W, Ws, M, N, K, Y, mode, lds, part_ws, d.ksplit, stream);
 }
 
 hipError_t launch_decode_gemm(const uint8_t* A, const uint8_t* As, const uint8_t* W, const uint8_t* Ws, int64_t M,
-                              int64_t N, int64_t K, void* Y, int mode, hipStream_t stream) {
+                              int64_t N, int64_t K, void* Y, int mode, float* part_ws, hipStream_t stream) {
   const DecodeConfig d = decode_config(M, N, K, false, 2);
   switch (d.ak) {
-    case 1: return launch_decode_impl<1, DecBf16>(d, A, As, nullptr, nullptr, W, Ws, M, N, K, Y, mode, stream);
-    case 8: return launch_decode_impl<8, DecBf16>(d, A, As, nullptr, nullptr, W, Ws, M, N, K, Y, mode, stream);
-    case 16: return launch_decode_impl<16, DecBf16>(d, A, As, nullptr, nullptr, W, Ws, M, N, K, Y, mode, stream);
-    default: return launch_decode_impl<32, DecBf16>(d, A, As, nullptr, nullptr, W, Ws, M, N, K, Y, mode, stream);
+    case 1: return launch_decode_impl<1, DecBf16>(d, A, As, nullptr, nullptr, W, Ws, M, N, K, Y, mode, part_ws, stream);
+    case 8: return launch_decode_impl<8, DecBf16>(d, A, As, nullptr, nullptr, W, Ws, M, N, K, Y, mode, part_ws, stream);
+    case 16: return launch_decode_impl<16, DecBf16>(d, A, As, nullptr, nullptr, W, Ws, M, N, K, Y, mode, part_ws, stream);
+    default: return launch_decode_impl<32, DecBf16>(d, A, As, nullptr, nullptr, W, Ws, M, N, K, Y, mode, part_ws, stream);
   }
+}
+
+// Workspace (fp32 partial sums of the K-split parts) the decode GEMM needs
+// for this shape: 0 without a split.
+size_t decode_workspace_bytes(int64_t M, int64_t N, int64_t K, bool fused) {
+  if (!decode_supported(M, N, K, 1)) return 0;
+  const DecodeConfig d = decode_config(M, N, K, fused, 2);
+  return d.ksplit > 1 ? (size_t)d.ksplit * (size_t)M * (size_t)N * sizeof(float) : 0;
 }
 
 // -------- fused transform + GEMM entry used by macaq_linear
@@ -581,14 +666,14 @@ bool linear_fused_supported(int64_t M, int64_t N, int64_t K, int64_t E) {
 }
 
 hipError_t launch_linear_fused(const void* x, bool x_f32, const float* s, const uint8_t* B, const uint8_t* Bs,
-                               int64_t M, int64_t N, int64_t K, void* Y, int mode, hipStream_t stream) {
+                               int64_t M, int64_t N, int64_t K, void* Y, int mode, float* part_ws, hipStream_t stream) {
   const DecodeConfig d = decode_config(M, N, K, true, x_f32 ? 4 : 2);
   if (d.ak < 0) {
-    if (x_f32) return launch_decode_impl<-1, float>(d, nullptr, nullptr, x, s, B, Bs, M, N, K, Y, mode, stream);
-    return launch_decode_impl<-1, DecBf16>(d, nullptr, nullptr, x, s, B, Bs, M, N, K, Y, mode, stream);
+    if (x_f32) return launch_decode_impl<-1, float>(d, nullptr, nullptr, x, s, B, Bs, M, N, K, Y, mode, part_ws, stream);
+    return launch_decode_impl<-1, DecBf16>(d, nullptr, nullptr, x, s, B, Bs, M, N, K, Y, mode, part_ws, stream);
   }
-  if (x_f32) return launch_decode_impl<0, float>(d, nullptr, nullptr, x, s, B, Bs, M, N, K, Y, mode, stream);
-  return launch_decode_impl<0, DecBf16>(d, nullptr, nullptr, x, s, B, Bs, M, N, K, Y, mode, stream);
+  if (x_f32) return launch_decode_impl<0, float>(d, nullptr, nullptr, x, s, B, Bs, M, N, K, Y, mode, part_ws, stream);
+  return launch_decode_impl<0, DecBf16>(d, nullptr, nullptr, x, s, B, Bs, M, N, K, Y, mode, part_ws, stream);
 }
 
 }  // namespace macaq

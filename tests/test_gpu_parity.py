@@ -400,7 +400,22 @@ DECODE_SHAPES = [
     ("M8 odd chunks", (8, 96, 256 * 7)),
     ("M5 16 waves", (5, 70, 256 * 65)),
     ("M32 25 chunks, 4 waves of 4 slots", (32, 64, 256 * 25)),
+    ("M4 128 chunks, split 4", (4, 100, 256 * 128)),
 ]
+
+
+def decode_parts(N, K, split):
+    """Number of K parts the decode GEMM uses: the largest split up to 4 whose
+    blocks fit two per CU (256 CUs) with 8 or more 256-wide chunks for each of
+    a block's 4 waves, or the forced value, at most one part per chunk."""
+    tiles, kc = (N + 31) // 32, K // 256
+    ks = 1
+    if tiles < 256:
+        while ks < 4 and tiles * (ks + 1) <= 512 and kc // ((ks + 1) * 4) >= 8:
+            ks += 1
+    if split:
+        ks = split
+    return min(ks, kc)
 
 
 @pytest.mark.parametrize("waves,stages", [(8, 2), (4, 2), (4, 3)])
@@ -423,9 +438,16 @@ def test_gemm_decode_forced_rings(waves, stages, tune):
     _check_y(y.cpu().numpy(), y_ref, S)
 
 
+@pytest.mark.parametrize("split", [0, 1, 3])
 @pytest.mark.parametrize("name,shape", DECODE_SHAPES, ids=[n for n, _ in DECODE_SHAPES])
-def test_gemm_decode(name, shape):
-    say(f"gemm decode {name} {shape}")
+def test_gemm_decode(name, shape, split, tune):
+    """Decode GEMM with its automatic K split (row tiles too few to fill the
+    GPU, enough chunks per part), and with the split forced off and to 3
+    parts (parts of a few chunks, waves with none): within the oracle's
+    bound, and the same bits on a second call (the partial sums are added
+    in a fixed order)."""
+    say(f"gemm decode {name} {shape} split={split}")
+    tune(mx.TUNE_DECODE_SPLIT, split)
     M, N, K = shape
     rng = np.random.default_rng(M * 131 + N)
     ac = rng.integers(0, 256, (M, K // 2), dtype=np.uint8)
@@ -433,7 +455,9 @@ def test_gemm_decode(name, shape):
     wc = rng.integers(0, 256, (N, K // 2), dtype=np.uint8)
     wsc = rng.integers(110, 140, (N, K // 32), dtype=np.uint8)
     t = [torch.from_numpy(a).to(DEV) for a in (ac, asc, wc, wsc)]
-    assert mx.lib().macaq_gemm_workspace_bytes(M, N, K, 1) == 0
+    parts = decode_parts(N, K, split)
+    want = parts * M * N * 4 if parts > 1 else 0
+    assert mx.lib().macaq_gemm_workspace_bytes(M, N, K, 1) == (want + 255) // 256 * 256
     y1 = mx.gemm(*t)
     y2 = mx.gemm(*t)
     y_ref, S = oracle.gemm(ac, asc, wc, wsc)
