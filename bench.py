@@ -607,7 +607,6 @@ def main():
     xdt = mx.BF16 if x0.dtype == torch.bfloat16 else mx.F32
     p = ctypes.c_void_p
     off_p = p(off.data_ptr()) if off is not None else None
-    split = not fused  # two launches that are timed separately
 
     def step_args(i):
         j = i % R
@@ -671,12 +670,38 @@ def main():
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) / args.steps * 1e3
 
+    def in_step_us():
+        """Durations of the two kernels inside K more layer steps (the same
+        launches macaq_linear makes), with events before, between and after
+        them: the long MFMA-bound GEMM runs at the clock it keeps under the
+        layer's alternating load, which back-to-back GEMMs alone do not show."""
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+        torch.cuda.synchronize()
+        for i in range(args.steps):
+            evs[i][0].record(stream)
+            act_only(i)
+            evs[i][1].record(stream)
+            gemm_only(i)
+            evs[i][2].record(stream)
+        torch.cuda.synchronize()
+        act = sum(e[0].elapsed_time(e[1]) for e in evs) / args.steps * 1e3
+        gemm = sum(e[1].elapsed_time(e[2]) for e in evs) / args.steps * 1e3
+        return act, gemm
+
+    # per-kernel timing: the decode kernels (short, HBM-bound) back to back,
+    # where event packets between launches would add a few microseconds to
+    # each; the prefill and grouped layers inside layer steps
     act_us = None
-    if split:
+    if fused:
+        timing = "back-to-back launches of the fused kernel"
+        gemm_us = kernel_us(run_linear)
+    elif M <= 32:
+        timing = "back-to-back launches of each kernel"
         act_us = kernel_us(act_only)
         gemm_us = kernel_us(gemm_only)
     else:
-        gemm_us = kernel_us(run_linear)
+        timing = "events around each kernel inside layer steps"
+        act_us, gemm_us = in_step_us()
 
     # algorithmic bytes
     xb = M * K * x0.element_size()
@@ -705,6 +730,7 @@ def main():
                    "act_staging": "tiled" if a_tiled else ("none (fused)" if fused else "row-major"),
                    "y": f"{args.out} [{M}][{y_cols}]" + (" swiglu" if epi == mx.EPI_SWIGLU else ""),
                    "scale_rule": {"smooth": "s = 1/sigma", "literal": "s = sigma"}[args.scale_rule],
+                   "kernel_timing": timing,
                    "parallelism": "none (one GPU)"},
     }
     if act_us is not None:

@@ -108,6 +108,7 @@ LINEAR = [
     ("fused M1", dict(cfg=4, shape=(1, 640, 2048)), mx.PATH_FUSED),
     ("fused M2 fp32 x", dict(cfg=1, shape=(2, 96, 512)), mx.PATH_FUSED),
     ("fused M8 resident", dict(cfg=4, shape=(8, 256, 1024)), mx.PATH_FUSED),
+    ("fused M16 resident", dict(cfg=4, shape=(16, 256, 1024)), mx.PATH_FUSED),
     ("unfused M64", dict(cfg=2, shape=(64, 256, 1024)), mx.PATH_UNFUSED),
 ]
 

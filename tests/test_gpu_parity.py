@@ -470,6 +470,9 @@ DECODE_LINEAR = [
     ("M1", dict(cfg=4, shape=(1, 640, 2048))),
     ("M2 16 waves", dict(cfg=4, shape=(2, 300, 256 * 70))),
     ("M8", dict(cfg=4, shape=(8, 512, 1024))),
+    ("M5 ragged N", dict(cfg=4, shape=(5, 300, 256 * 9))),
+    ("M8 fp32 x", dict(cfg=1, shape=(8, 96, 512))),
+    ("M3 K split", dict(cfg=4, shape=(3, 100, 256 * 128))),
     ("M32", dict(cfg=4, shape=(32, 256, 2560))),
 ]
 
