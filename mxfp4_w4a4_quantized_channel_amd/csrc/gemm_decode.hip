@@ -517,24 +517,33 @@ struct DecodeConfig {
   int waves, stages, ak, eb, rt, ksplit;
 };
 
-// K split of the decode GEMM: with fewer 32-row blocks than the 256 CUs, the
-// K range of each row tile is cut into `ksplit` parts taken by as many blocks
-// (the largest split up to 4 whose blocks fit two per CU and still leave each
-// of a block's 4 waves 8 or more 256-wide chunks), so that every CU streams
-// weights.  The parts' fp32 partial sums go to the caller's workspace and a
-// second kernel adds them in part order.  Measured on down-proj N5120 K25600
-// (160 row tiles, split 3): fused M1 17.1 us against 18.4 unsplit, M8 21.7
-// against 22.9, M32 29.9 against 30.4; a split into 2 (320 blocks, a second
-// wave of 64) was slower than none.  macaq_set_tuning(MACAQ_TUNE_DECODE_SPLIT)
-// forces the number of parts (1 = no split).
+// K split of the decode GEMM: with fewer row tiles than the 256 CUs, the K
+// range of each row tile is cut into `ksplit` parts taken by as many blocks,
+// so that every CU streams weights.  32-row blocks (4 waves) take the largest
+// split up to 4 whose blocks fit two per CU and still leave each wave 8 or
+// more 256-wide chunks; 64-row blocks (2 waves) the largest whose blocks fit
+// one per CU.  The parts' fp32 partial sums go to the caller's workspace and
+// a second kernel adds them in part order.  Measured on down-proj N5120
+// K25600: fused M1 17.1 us against 18.4 unsplit (32-row blocks, 3 parts);
+// M32 20.7 us with 64-row blocks in 3 parts (240 blocks), against 24.1 with
+// 32-row blocks in 3 parts and 25.7 unsplit; M16 18.0 against 19.3 and 21.3.
+// Grids just past one block per CU slot were slower than no split (32-row
+// blocks in 2 parts: 30.5 us at M32; 64-row blocks in 4 parts: 29.1 us).
+// macaq_set_tuning(MACAQ_TUNE_DECODE_SPLIT) forces the number of parts
+// (1 = no split).
 constexpr int kDecCUs = 256;
 constexpr int kDecSplitWaves = 4;
 static int decode_ksplit(int64_t N, int64_t K, int rt) {
   const int64_t tiles = ceil_div(N, kDecRows * rt);
   const int kc = (int)(K >> 8);
   int ks = 1;
-  if (rt == 1 && tiles < kDecCUs)
-    while (ks < 4 && tiles * (ks + 1) <= 2 * kDecCUs && kc / ((ks + 1) * kDecSplitWaves) >= 8) ++ks;
+  if (tiles < kDecCUs) {
+    if (rt == 1) {
+      while (ks < 4 && tiles * (ks + 1) <= 2 * kDecCUs && kc / ((ks + 1) * kDecSplitWaves) >= 8) ++ks;
+    } else {
+      while (ks < 4 && tiles * (ks + 1) <= kDecCUs && kc / ((ks + 1) * 2) >= 8) ++ks;
+    }
+  }
   if (const int force = tuning(MACAQ_TUNE_DECODE_SPLIT)) ks = force;
   return ks < kc ? ks : kc;   // at least one chunk per part
 }
@@ -548,21 +557,25 @@ static size_t decode_lds_bytes(const DecodeConfig& d, int64_t M, int64_t K) {
 // Block height: 64 weight rows (two MFMA row tiles sharing each activation
 // chunk, which halves the activation's L2-to-LDS traffic) for more than 8
 // staged activation rows when 32-row blocks would number more than two per
-// CU; then 2 waves per block, so that two blocks stay resident per CU.
+// CU, or when they would number fewer than the CUs and the K split applies
+// (the split then makes about one block per CU); 2 waves per block.
 // Otherwise 32 rows and 4 or 8 waves (for small activations the extra waves
-// keep more of W' in flight, which matters more).  Each wave keeps STAGES - 1 chunks in flight; the ring is made as
-// deep as LDS allows (2 to 4 slots), within half of the CU's LDS when the
-// grid has more blocks than CUs, within all of it otherwise.  8 waves drop
-// to 4 where 2 slots do not fit, and, with more than 8 staged activation
-// rows, where they would get only 2 slots: 4 waves with 4 slots keep 12
-// chunks in flight per block instead of 8 (measured on down-proj M32
-// N5120 K25600: 25.7 us against 29.7; the fused M1 down-proj keeps 8 waves
-// of 2 slots, 18.3 us against 21.9 with 4 of 4).
+// keep more of W' in flight, which matters more).  Each wave keeps
+// STAGES - 1 chunks in flight; the ring is made as deep as LDS allows (2 to
+// 4 slots), within half of the CU's LDS when the grid has more blocks than
+// CUs, within all of it otherwise.  8 waves drop to 4 where 2 slots do not
+// fit, and, with more than 8 staged activation rows, where they would get
+// only 2 slots: 4 waves with 4 slots keep 12 chunks in flight per block
+// instead of 8 (measured on down-proj M32 N5120 K25600 without a split: 25.7
+// us against 29.7).  Split 32-row blocks take 4 waves.
 static DecodeConfig decode_config(int64_t M, int64_t N, int64_t K, bool fused, int eb) {
   DecodeConfig d;
   d.ak = decode_ak(M, fused);
   d.eb = eb;
-  d.rt = (d.ak > 8 && ceil_div(N, kDecRows) > 512) ? 2 : 1;
+  const int64_t t32 = ceil_div(N, kDecRows);
+  d.rt = (d.ak > 8 && t32 > 512) ? 2 : 1;
+  // narrow layers with more than 8 staged rows: 64-row blocks in K parts
+  if (d.ak > 8 && t32 < kDecCUs && decode_ksplit(N, K, 2) > 1) d.rt = 2;
   if (const int force = tuning(MACAQ_TUNE_DECODE_ROWS)) d.rt = force == 64 ? 2 : 1;
   const int max_stages = d.rt == 2 ? 3 : 4;
   d.waves = d.rt == 2 ? 2 : (K / 256 >= 24 ? 8 : 4);

@@ -404,14 +404,21 @@ DECODE_SHAPES = [
 ]
 
 
-def decode_parts(N, K, split):
-    """Number of K parts the decode GEMM uses: the largest split up to 4 whose
-    blocks fit two per CU (256 CUs) with 8 or more 256-wide chunks for each of
-    a block's 4 waves, or the forced value, at most one part per chunk."""
-    tiles, kc = (N + 31) // 32, K // 256
+def decode_parts(M, N, K, split):
+    """Number of K parts the decode GEMM uses with row-major activation codes:
+    with fewer row tiles than the 256 CUs, 32-row blocks (M <= 8) take the
+    largest split up to 4 whose blocks fit two per CU with 8 or more 256-wide
+    chunks for each of a block's 4 waves; above 8 rows, 64-row blocks of 2
+    waves the largest that fits one per CU.  A forced value replaces it; at
+    most one part per chunk."""
+    kc = K // 256
     ks = 1
-    if tiles < 256:
-        while ks < 4 and tiles * (ks + 1) <= 512 and kc // ((ks + 1) * 4) >= 8:
+    t32, t64 = (N + 31) // 32, (N + 63) // 64
+    if M <= 8 and t32 < 256:
+        while ks < 4 and t32 * (ks + 1) <= 512 and kc // ((ks + 1) * 4) >= 8:
+            ks += 1
+    elif M > 8 and t32 < 256:
+        while ks < 4 and t64 * (ks + 1) <= 256 and kc // ((ks + 1) * 2) >= 8:
             ks += 1
     if split:
         ks = split
@@ -455,7 +462,7 @@ def test_gemm_decode(name, shape, split, tune):
     wc = rng.integers(0, 256, (N, K // 2), dtype=np.uint8)
     wsc = rng.integers(110, 140, (N, K // 32), dtype=np.uint8)
     t = [torch.from_numpy(a).to(DEV) for a in (ac, asc, wc, wsc)]
-    parts = decode_parts(N, K, split)
+    parts = decode_parts(M, N, K, split)
     want = parts * M * N * 4 if parts > 1 else 0
     assert mx.lib().macaq_gemm_workspace_bytes(M, N, K, 1) == (want + 255) // 256 * 256
     y1 = mx.gemm(*t)
