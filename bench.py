@@ -670,38 +670,18 @@ def main():
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) / args.steps * 1e3
 
-    def in_step_us():
-        """Durations of the two kernels inside K more layer steps (the same
-        launches macaq_linear makes), with events before, between and after
-        them: the long MFMA-bound GEMM runs at the clock it keeps under the
-        layer's alternating load, which back-to-back GEMMs alone do not show."""
-        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
-        torch.cuda.synchronize()
-        for i in range(args.steps):
-            evs[i][0].record(stream)
-            act_only(i)
-            evs[i][1].record(stream)
-            gemm_only(i)
-            evs[i][2].record(stream)
-        torch.cuda.synchronize()
-        act = sum(e[0].elapsed_time(e[1]) for e in evs) / args.steps * 1e3
-        gemm = sum(e[1].elapsed_time(e[2]) for e in evs) / args.steps * 1e3
-        return act, gemm
-
-    # per-kernel timing: the decode kernels (short, HBM-bound) back to back,
-    # where event packets between launches would add a few microseconds to
-    # each; the prefill and grouped layers inside layer steps
+    # per-kernel timing: back-to-back launches of each kernel of the step (an
+    # unfused step's two kernels are macaq_quant_act(_tiled) and macaq_gemm,
+    # the launches macaq_linear makes on that path); events between the
+    # launches inside layer steps would add a few microseconds to each
     act_us = None
     if fused:
         timing = "back-to-back launches of the fused kernel"
         gemm_us = kernel_us(run_linear)
-    elif M <= 32:
+    else:
         timing = "back-to-back launches of each kernel"
         act_us = kernel_us(act_only)
         gemm_us = kernel_us(gemm_only)
-    else:
-        timing = "events around each kernel inside layer steps"
-        act_us, gemm_us = in_step_us()
 
     # algorithmic bytes
     xb = M * K * x0.element_size()
