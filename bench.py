@@ -746,14 +746,22 @@ def main():
                                "tflops": round(flops / gemm_us / 1e6, 1)}
         out["roofline"].update({"us": round(gemm_us, 2), "roofline_us": {"mfma": round(t_mfma, 2), "hbm": round(t_hbm, 2)},
                                 "traffic": traffic_record(f"{args.workload}:gemm{out_key}")})
-    if not args.no_ablation and not fused:
+    if not args.no_ablation:
         # both sides row-major activation codes into the same GEMM kernel:
-        # the comparison isolates the transform against the plain quantizer
-        rm_codes = ws_buf[: M * K // 2]
-        rm_scales = ws_buf[(M * K // 2 + 255) // 256 * 256:]
+        # the comparison isolates the transform against the plain quantizer.
+        # The plain quantizer has no fused form, so a layer that runs fused
+        # is compared on the two-launch path on both sides.
+        if fused:
+            rm_buf = torch.zeros(int(L.macaq_quant_act_bytes(M, K)), dtype=torch.uint8, device=dev)
+        else:
+            rm_buf = ws_buf
+        rm_codes = rm_buf[: M * K // 2]
+        rm_scales = rm_buf[(M * K // 2 + 255) // 256 * 256:]
         out["transform_overhead"] = transform_overhead(args, mx, L, wl, xs, wss, wcs, ys, s0, off_p, stream, sp,
                                                        rm_codes, rm_scales, gemm_ws, M, N, K, E, R, ydt, gemm_epi,
                                                        tiled=tiled)
+        if fused:
+            out["transform_overhead"]["path"] = "two launches on both sides (the layer itself runs fused)"
     out["gpu_state"] = {"before": state_before, "after": state_after}
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(wl, args.cpu_rows, args.cpu_wrows)

@@ -319,9 +319,9 @@ size_t macaq_quant_act_tiled_rows(int64_t M, int64_t E);
  *   y [M][N] fp32 out.
  * workspace: device scratch of macaq_gemm_workspace_bytes(M, N, K, E) bytes,
  * 256-byte aligned; NULL when that is 0.  The decode GEMM (M <= 32, E == 1,
- * row-major weights) splits K over two blocks per 32-row tile when the row
- * tiles cannot fill the GPU; the two fp32 partial sums (2 * M * N * 4 bytes)
- * go to the workspace and a second kernel adds them, part 0 first.
+ * row-major weights) splits K over up to 4 blocks per row tile when the row
+ * tiles cannot fill the GPU; the parts' fp32 partial sums (parts * M * N * 4
+ * bytes) go to the workspace and a second kernel adds them in part order.
  * Calls that share a workspace must not overlap in time.
  * Requires K % 128 == 0; K >= 128; all code pointers 16-byte aligned and
  * scale pointers 4-byte aligned.
@@ -367,9 +367,13 @@ int macaq_linear_path(int64_t M, int64_t N, int64_t K, int64_t E, uint32_t flags
  * activation into LDS, so it serves only when M * (K/2 + K/32 + 24) bytes fit
  * beside the weight staging in the 160 KiB of LDS (otherwise a forced
  * MACAQ_PATH_FUSED returns MACAQ_ERR_UNSUPPORTED).  AUTO takes it for
- * M <= 2, where one launch beats two.
+ * M <= 2, and for small layers where ceil(N / 32) * M * K <= 2^20 (every
+ * 32-row block repeats the transform of the whole activation): there one
+ * launch beats two.
  * Requires the argument rules of macaq_quant_act and macaq_gemm and a
- * workspace of macaq_linear_workspace_bytes(M, N, K, E, flags) bytes.
+ * workspace of macaq_linear_workspace_bytes(M, N, K, E, flags) bytes (the
+ * unfused path's activation staging, and on either decode path the partial
+ * sums of a K split, as in macaq_gemm).
  */
 int macaq_linear(const void* x, macaq_dtype x_dtype, const float* s,
                  const int32_t* expert_offsets, int64_t E,
@@ -389,8 +393,8 @@ int macaq_linear(const void* x, macaq_dtype x_dtype, const float* s,
  * workspace and workspace_bytes), rules, kernels and results (bit for bit)
  * as macaq_linear_ex.  The staging that macaq_linear_ex keeps in the
  * caller's workspace (macaq_linear_workspace_bytes(M, N, K, E, flags) bytes:
- * the activation codes and scales on the unfused path; nothing on the fused
- * path) lives instead in a static device array of
+ * the activation codes and scales on the unfused path, and the partial sums
+ * of a decode K split on either decode path) lives instead in a static device array of
  * MACAQ_NOALLOC_SCRATCH_BYTES that the library holds on each device it runs
  * on until the process ends; a shape that needs more returns
  * MACAQ_ERR_WORKSPACE before anything is launched.  The call never

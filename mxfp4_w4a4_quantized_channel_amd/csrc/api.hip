@@ -65,6 +65,10 @@ namespace {
 
 constexpr int kVersion = 10000;  // 1.0.0
 constexpr int64_t kMaxFusedM = 2;  // AUTO takes the fused path up to this M
+// ... and for small layers: every 32-row block of the fused kernel repeats
+// the transform of the whole activation, which below this many repeated
+// values costs less than the second launch of the unfused path
+constexpr int64_t kMaxFusedRepeat = int64_t(1) << 20;
 
 thread_local std::string g_last_error;
 
@@ -352,7 +356,9 @@ int macaq_linear_path(int64_t M, int64_t N, int64_t K, int64_t E, uint32_t flags
   if (flags > MACAQ_PATH_UNFUSED) return fail(MACAQ_ERR_INVALID_ARG, "macaq_linear_path: unknown flags");
   if (tiled) return MACAQ_PATH_UNFUSED;   // tiled weights: transform kernel, then the prefill / grouped GEMM
   if (flags != MACAQ_PATH_AUTO) return (int)flags;
-  return (macaq::linear_fused_supported(M, N, K, E) && M <= kMaxFusedM) ? MACAQ_PATH_FUSED : MACAQ_PATH_UNFUSED;
+  if (!macaq::linear_fused_supported(M, N, K, E)) return MACAQ_PATH_UNFUSED;
+  const int64_t repeat = (N + 31) / 32 * M * K;
+  return (M <= kMaxFusedM || repeat <= kMaxFusedRepeat) ? MACAQ_PATH_FUSED : MACAQ_PATH_UNFUSED;
 }
 
 }  // extern "C"

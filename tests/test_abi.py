@@ -168,13 +168,17 @@ def test_valid_calls_without_a_device_report_no_device():
 
 def test_linear_path_choice_and_workspace():
     """AUTO takes the one-launch fused path for M <= 2 on a dense layer with
-    K % 256 == 0, the two-launch path otherwise; only the latter needs a
-    workspace (the activation codes and scales)."""
+    K % 256 == 0, and for small layers (ceil(N/32) * M * K <= 2^20), the
+    two-launch path otherwise; only the latter needs a workspace for the
+    activation codes and scales."""
     L = mx.lib()
     P = L.macaq_linear_path
     assert P(1, 25600, 5120, 1, mx.PATH_AUTO) == mx.PATH_FUSED
     assert P(2, 5120, 25600, 1, mx.PATH_AUTO) == mx.PATH_FUSED
     assert P(3, 5120, 25600, 1, mx.PATH_AUTO) == mx.PATH_UNFUSED
+    assert P(16, 128, 256, 1, mx.PATH_AUTO) == mx.PATH_FUSED            # tiny: 4 * 16 * 256 repeated values
+    assert P(32, 1024, 1024, 1, mx.PATH_AUTO) == mx.PATH_FUSED          # exactly 2^20
+    assert P(32, 1056, 1024, 1, mx.PATH_AUTO) == mx.PATH_UNFUSED        # one 32-row block more
     assert P(1, 4096, 4096 + 128, 1, mx.PATH_AUTO) == mx.PATH_UNFUSED   # K % 256 != 0
     assert P(1, 1024, 3072, 64, mx.PATH_AUTO) == mx.PATH_UNFUSED        # grouped
     assert P(2048, 4096, 4096, 1, mx.PATH_AUTO) == mx.PATH_UNFUSED
