@@ -110,6 +110,9 @@ LINEAR = [
     ("fused M8 resident", dict(cfg=4, shape=(8, 256, 1024)), mx.PATH_FUSED),
     ("fused M16 resident", dict(cfg=4, shape=(16, 256, 1024)), mx.PATH_FUSED),
     ("unfused M64", dict(cfg=2, shape=(64, 256, 1024)), mx.PATH_UNFUSED),
+    ("fused M1, K split in 2", dict(cfg=4, shape=(1, 128, 16384)), mx.PATH_FUSED),
+    ("unfused M8, K split in 2", dict(cfg=4, shape=(8, 256, 16384)), mx.PATH_UNFUSED),
+    ("unfused M16, 64-row blocks, K split in 3", dict(cfg=4, shape=(16, 256, 256 * 48)), mx.PATH_UNFUSED),
 ]
 
 

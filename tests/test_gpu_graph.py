@@ -23,6 +23,7 @@ CASES = [
     ("prefill, tiled W'", dict(cfg=2, shape=(200, 256, 1024)), mx.PATH_AUTO, True),
     ("decode M1, fused", dict(cfg=4, shape=(1, 512, 2048)), mx.PATH_AUTO, False),
     ("decode M8, two launches", dict(cfg=4, shape=(8, 512, 2048)), mx.PATH_UNFUSED, False),
+    ("decode M32, K split in 3 with its reduce", dict(cfg=4, shape=(32, 256, 256 * 48)), mx.PATH_UNFUSED, False),
     ("MoE, grouped", dict(cfg=5, shape=(300, 64, 512), routing="token_zipf"), mx.PATH_AUTO, True),
 ]
 
