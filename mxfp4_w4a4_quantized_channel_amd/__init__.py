@@ -344,8 +344,9 @@ def _out(M, N, out_dtype, epilogue, device, out):
 def gemm(a_codes, a_scales, w_codes, w_scales, offsets=None, out=None, workspace=None,
          out_dtype=torch.float32, epilogue=EPI_NONE, M=None):
     """y = A' W'^T from MXFP4 operands: [M, N] (or [M, N/2] with EPI_SWIGLU)
-    in out_dtype (float32 or bfloat16).  A workspace, when one is needed, is
-    zero-filled here; a caller-provided one must start zeroed.  With A_TILED
+    in out_dtype (float32 or bfloat16).  A workspace, when one is needed (the
+    partial sums of a decode K split), is allocated here unless the caller
+    passes one; its contents need no initialization.  With A_TILED
     in the epilogue argument, a_codes / a_scales are quant_act_tiled's flat
     buffers and M must be given."""
     _load()
@@ -367,7 +368,7 @@ def gemm(a_codes, a_scales, w_codes, w_scales, offsets=None, out=None, workspace
     y = _out(M, N, out_dtype, epilogue, a_codes.device, out)
     need = int(_load().macaq_gemm_workspace_bytes(M, N, K, E))
     if workspace is None and need > 0:
-        workspace = torch.zeros(need, dtype=torch.uint8, device=a_codes.device)
+        workspace = torch.empty(need, dtype=torch.uint8, device=a_codes.device)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     ydt = F32 if out_dtype == torch.float32 else BF16
     _check(macaq_gemm_ex(_ptr(a_codes), _ptr(a_scales), _ptr(offsets), E, _ptr(w_codes), _ptr(w_scales),
