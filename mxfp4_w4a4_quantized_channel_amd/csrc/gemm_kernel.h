@@ -478,19 +478,29 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, MINB) void gemm_mxfp4_pipe_
     }
   }
 
-  auto issue = [&](int kt, int st) {
+  // copies q0 <= q < q1 of K-tile kt into stage st (q < kCB: code copy q,
+  // else scale copy q - kCB); the bounds are compile-time constants
+  auto issue_q = [&](int kt, int st, auto q0c, auto q1c) {
+    constexpr int q0 = decltype(q0c)::value, q1 = decltype(q1c)::value;
     const uint32_t base = lds_base + (uint32_t)(st * L::kStage);
     const int64_t cofs = (int64_t)kt * L::kRowBytes, cofs_t = (int64_t)kt * 2048;
     const int64_t sofs = (int64_t)kt * kCPR, sofs_t = (int64_t)kt * 128;
 #pragma unroll
     for (int i = 0; i < kCB; ++i)
-      dma16(csrc[i] + (((ctile >> i) & 1u) ? cofs_t : cofs),
-            base + (uint32_t)(L::kA + ((wave * kCB + i) % L::kCodeBlocks) * 1024));
+      if (i >= q0 && i < q1)
+        dma16(csrc[i] + (((ctile >> i) & 1u) ? cofs_t : cofs),
+              base + (uint32_t)(L::kA + ((wave * kCB + i) % L::kCodeBlocks) * 1024));
 #pragma unroll
     for (int i = 0; i < kSB; ++i)
-      dma4(ssrc[i] + (((stile >> i) & 1u) ? sofs_t : sofs),
-           base + (uint32_t)(L::kAs + ((wave * kSB + i) % L::kScaleBlocks) * 256));
+      if (kCB + i >= q0 && kCB + i < q1)
+        dma4(ssrc[i] + (((stile >> i) & 1u) ? sofs_t : sofs),
+             base + (uint32_t)(L::kAs + ((wave * kSB + i) % L::kScaleBlocks) * 256));
   };
+  auto issue = [&](int kt, int st) { issue_q(kt, st, std::integral_constant<int, 0>{}, std::integral_constant<int, kLPT>{}); };
+  // the refill of a stage is issued in two halves: the first right after the
+  // barrier that frees the stage, the second at the start of the next K-tile
+  // (the copies stay in K-tile order, so the vmcnt counts are unchanged)
+  constexpr int kHalf = (kLPT + 1) / 2;
 
   v16f acc[T::kFM][T::kFN];
 #pragma unroll
@@ -554,6 +564,13 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, MINB) void gemm_mxfp4_pipe_
       constexpr int j = decltype(jc)::value;
       constexpr int cur = j & 1;
       if constexpr (j < NSUB - 1) {
+        if constexpr (j == 0) {
+          if (kt > 0) {
+            const int pt = kt - 1 + STAGES;
+            issue_q(pt < nk ? pt : nk - 1, (kt - 1) % STAGES, std::integral_constant<int, kHalf>{},
+                    std::integral_constant<int, kLPT>{});
+          }
+        }
         load_frags(kt, j + 1, cur ^ 1);
       } else {
         // every wave holds this tile's last fragments: stage kt % STAGES is
@@ -563,7 +580,8 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, MINB) void gemm_mxfp4_pipe_
         wait_lgkmcnt0();
         wait_vmcnt<(STAGES - 2) * kLPT>();   // tile kt+1 has landed
         block_barrier();
-        issue(kt + STAGES < nk ? kt + STAGES : nk - 1, kt % STAGES);
+        issue_q(kt + STAGES < nk ? kt + STAGES : nk - 1, kt % STAGES, std::integral_constant<int, 0>{},
+                std::integral_constant<int, kHalf>{});
         load_scales(kt + 1, 1);              // past the last tile: unused, in-bounds LDS bytes
         load_frags(kt + 1, 0, cur ^ 1);
       }
