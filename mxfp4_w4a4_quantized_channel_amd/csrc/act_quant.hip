@@ -484,10 +484,11 @@ struct ActLaunch {
 
 // Row blocks per wave: units / 3072 rounded up, so that the grid is about
 // one round of 3 blocks on each of the 256 CUs, clamped to 2..12, or 1 for
-// grids of at most 1024 units (measured on MI355X with the copy ring:
+// grids of at most 4096 units (measured on MI355X with the copy ring:
 // down-prefill 10 row blocks 32.0 us against 33.3 at 6 and 35.2 at 12; MoE
 // 4 row blocks 19.0 us against 21.3 at 2 and 8; decode M32 1 row block
-// 4.1 us against 5.2 at 2).  Waves of at most 2 row blocks share s per block
+// 4.1 us against 5.2 at 2; attn-proj M2048 K4096 with tiled output, 4096
+// units, 1 row block 6.4 us against 7.1 at 2).  Waves of at most 2 row blocks share s per block
 // (measured: attn-proj activation 9.7 -> 8.5 us before the copy ring,
 // 7.2 us with it); longer waves keep the per-wave layout, which reads x
 // with better locality (down-prefill 37.9 vs 39.3 us, MoE per-token routing
@@ -510,7 +511,8 @@ static ActLaunch act_launch(int64_t M, int64_t K, bool plain, bool tiled = false
   const int64_t blocks = ceil_div(M, rw);
   const int64_t units = nseg * blocks;
   int64_t steps = ceil_div(units, (int64_t)3072);
-  if (steps < 2) steps = units <= 1024 ? 1 : 2;
+  if (steps < 2) steps = 2;
+  if (units <= 4096) steps = 1;
   if (steps > 12) steps = 12;
   if (steps > blocks) steps = blocks;
   if (const int force = tuning(MACAQ_TUNE_ACT_ROWS_PER_WAVE)) steps = force;
