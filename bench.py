@@ -90,6 +90,9 @@ def parse():
     p.add_argument("--library-compare", action="store_true",
                    help="only time our prefill GEMM against the vendor library's MXFP4 GEMM (hipBLASLt through "
                         "torch._scaled_mm) on the same operands, attn-proj and down-prefill, bf16 output")
+    p.add_argument("--mfma-probe", action="store_true",
+                   help="time the block-scaled FP4 MFMA alone (from registers, random and zero operands): "
+                        "the MFMA throughput the chip sustains, next to the 10.1 PFLOP/s datasheet figure")
     p.add_argument("--copy-calibration", action="store_true",
                    help="only run a plain 512 MiB device-to-device copy (5 times) so that HBM byte "
                         "counters can be scaled against a transfer of known size")
@@ -538,10 +541,65 @@ def transform_overhead(args, mx, L, wl, xs, wss, wcs, ys, s0, off_p, stream, sp,
             "pages_figure": "2.3% end-to-end (Qwen3-32B, vLLM); about 8% on a 0.6B model"}
 
 
+def mfma_probe(reps=50):
+    """macaq_probe_mfma: 256 blocks (one per CU), each SIMD running 3584
+    MFMAs (the down-prefill GEMM's count per SIMD: 481 GFLOP / 131072 FLOP
+    / 1024 SIMDs) with one wave per SIMD, or two waves of half as many, and
+    no memory traffic.  Operand codes: zeros, uniformly random bytes, or the
+    codes of the down-prefill layer's own activation and prepared weight
+    (a 64-row slice of the same synthetic distribution).  The clock under
+    MFMA load follows the power drawn, which follows how many operand bits
+    toggle."""
+    import torch
+    import workloads
+    import mxfp4_w4a4_quantized_channel_amd as mx
+    dev = "cuda:0"
+    L = mx.lib()
+    stream = torch.cuda.current_stream(dev)
+    sp = ctypes.c_void_p(stream.cuda_stream)
+    gen = torch.Generator(device="cpu").manual_seed(7)
+    wl = workloads.make(3, shape=(64, 64, 14336))
+    ac, _ = mx.quant_act(wl.x.to(dev), wl.s.to(dev))
+    wc, _ = mx.prepare_weights(wl.w.to(dev), wl.s.to(dev))
+    # lane l: 64 bytes of activation codes, then 64 bytes of weight codes
+    layer = torch.stack([ac.reshape(-1)[:4096].reshape(64, 64), wc.reshape(-1)[:4096].reshape(64, 64)], 1).reshape(-1)
+    sources = {"zero": torch.zeros(8192, dtype=torch.uint8, device=dev),
+               "random": torch.randint(0, 256, (8192,), dtype=torch.uint8, generator=gen).to(dev),
+               "down-prefill codes": layer.contiguous()}
+    res = {}
+    for data, src in sources.items():
+        for waves, iters, m in ((4, 224, 16), (8, 224, 8)):
+            out = torch.empty(256 * waves * 64, dtype=torch.float32, device=dev)
+
+            def launch():
+                if L.macaq_probe_mfma(ctypes.c_void_p(src.data_ptr()), 256, waves, iters,
+                                      ctypes.c_void_p(out.data_ptr()), sp) != 0:
+                    raise RuntimeError(L.macaq_last_error().decode())
+            for _ in range(5):
+                launch()
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for _ in range(reps):
+                launch()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            us = e0.elapsed_time(e1) / reps * 1e3
+            flops = 256 * waves * iters * m * 131072
+            res[f"{data}, {waves // 4} wave(s) per SIMD"] = {
+                "us": round(us, 2), "TFLOPs": round(flops / us / 1e6, 1),
+                "frac_of_peak": round(flops / us / 1e6 / PEAK_MXFP4_TFLOPS, 4)}
+    print(json.dumps({"mfma_probe": res, "mfmas_per_simd": 3584, "flop_per_launch": 256 * 4 * 224 * 16 * 131072,
+                      "peak_TFLOPs": PEAK_MXFP4_TFLOPS, "launches": reps}), flush=True)
+
+
 def main():
     args = parse()
     if args.copy_calibration:
         copy_calibration()
+        return
+    if args.mfma_probe:
+        mfma_probe()
         return
     if args.library_compare:
         library_compare(min(args.steps, 100))

@@ -14,6 +14,7 @@
 #include <vector>
 
 #include "macaq.h"
+#include "macaq_probe.h"
 
 namespace macaq {
 hipError_t launch_act_quant(const void* x, bool x_f32, bool reciprocal, const float* s,
@@ -48,6 +49,7 @@ hipError_t launch_gemm_tiled(const uint8_t* A, const uint8_t* As, const int32_t*
                              hipStream_t stream);
 hipError_t launch_act_quant_tiled(const void* x, bool x_f32, const float* s, const int32_t* offsets, int E, int64_t M,
                                   int64_t K, uint8_t* codes, uint8_t* scales, hipStream_t stream);
+hipError_t launch_probe_mfma(const void* src, int64_t blocks, int waves, int iters, float* out, hipStream_t stream);
 hipError_t launch_tile_weights(const uint8_t* wc, const uint8_t* ws, int64_t E, int64_t N, int64_t K, uint8_t* tc,
                                uint8_t* ts, hipStream_t stream);
 // output mode bits of the GEMM kernels (mx_common.h)
@@ -205,6 +207,18 @@ int check_tiled(int64_t N, int64_t K, const char* fn) {
 extern "C" {
 
 int macaq_version(void) { return kVersion; }
+
+int macaq_probe_mfma(const void* src, int64_t blocks, int waves_per_block, int iters, float* out, void* stream) {
+  const char* fn = "macaq_probe_mfma";
+  if (src == nullptr || out == nullptr) return fail(MACAQ_ERR_INVALID_ARG, std::string(fn) + ": null pointer");
+  if (reinterpret_cast<uintptr_t>(src) % 16 != 0) return fail(MACAQ_ERR_INVALID_ARG, std::string(fn) + ": src not 16-byte aligned");
+  if (blocks < 1 || blocks > (int64_t(1) << 20)) return fail(MACAQ_ERR_INVALID_ARG, std::string(fn) + ": blocks out of range");
+  if (waves_per_block != 4 && waves_per_block != 8)
+    return fail(MACAQ_ERR_INVALID_ARG, std::string(fn) + ": waves_per_block must be 4 or 8");
+  if (iters < 1) return fail(MACAQ_ERR_INVALID_ARG, std::string(fn) + ": iters must be >= 1");
+  if (int st = check_device()) return st;
+  return hip_status(macaq::launch_probe_mfma(src, blocks, waves_per_block, iters, out, (hipStream_t)stream), fn);
+}
 
 int macaq_set_tuning(int knob, int value) {
   static const int kMax[MACAQ_TUNE_COUNT] = {3, 64, 64, 2, 8, 4, 64, 64, 16};

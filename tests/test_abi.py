@@ -1,4 +1,4 @@
-"""The C ABI library loads, exports every function include/macaq.h declares,
+"""The C ABI library loads, exports every function include/*.h declares,
 and validates arguments on the host (no GPU needed: nothing is launched)."""
 import ctypes
 import os
@@ -10,15 +10,27 @@ import mxfp4_w4a4_quantized_channel_amd as mx
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "macaq.h")
+HEADERS = sorted(os.path.join(ROOT, "include", f) for f in os.listdir(os.path.join(ROOT, "include")) if f.endswith(".h"))
 
 OK, INVALID, UNSUPPORTED, NO_DEVICE, HIPERR, WORKSPACE = 0, -1, -2, -3, -4, -5
 A16 = 0x10000  # a fake, 256-byte aligned, non-null "device pointer" (never dereferenced)
 
 
 def declared_functions():
-    text = open(HEADER).read()
+    text = "".join(open(h).read() for h in HEADERS)
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     return sorted(set(re.findall(r"\b(macaq_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_probe_validation():
+    """The MFMA probe (a measurement aid) rejects bad arguments on the host."""
+    mx.lib()
+    assert mx.macaq_probe_mfma(None, 256, 4, 1, A16, None) == INVALID
+    assert mx.macaq_probe_mfma(A16 + 4, 256, 4, 1, A16, None) == INVALID
+    assert mx.macaq_probe_mfma(A16, 0, 4, 1, A16, None) == INVALID
+    assert mx.macaq_probe_mfma(A16, 256, 6, 1, A16, None) == INVALID
+    assert mx.macaq_probe_mfma(A16, 256, 4, 0, A16, None) == INVALID
+    assert mx.macaq_probe_mfma(A16, 256, 8, 10, A16, None) == NO_DEVICE
 
 
 def test_header_declares_the_boundary():
