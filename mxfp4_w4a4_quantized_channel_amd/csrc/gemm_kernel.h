@@ -350,6 +350,18 @@ __device__ __forceinline__ void mfma_substep_t(v16f (&acc)[FM][FN], const uint4 
                                                                      4, 4, J, (int)sa[mi], J, (int)sb[ni]);
 }
 
+// MFMAs LO .. HI-1 of one sub-step (index mi * FN + ni).
+template <int J, int LO, int HI, int FM, int FN>
+__device__ __forceinline__ void mfma_range_t(v16f (&acc)[FM][FN], const uint4 (&fa)[FM], const uint4 (&fb)[FN],
+                                             const uint32_t (&sa)[FM], const uint32_t (&sb)[FN]) {
+#pragma unroll
+  for (int i = LO; i < HI; ++i) {
+    const int mi = i / FN, ni = i % FN;
+    acc[mi][ni] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(as_operand(fa[mi]), as_operand(fb[ni]), acc[mi][ni],
+                                                                  4, 4, J, (int)sa[mi], J, (int)sb[ni]);
+  }
+}
+
 // Calls f(std::integral_constant<int, I>) for I = 0 .. N-1 (compile-time
 // indices for op_sel and register-set selection).
 template <int N, typename F, int I = 0>
@@ -558,11 +570,17 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, MINB) void gemm_mxfp4_pipe_
 
   constexpr int kMF = T::kFM * T::kFN;   // MFMAs per sub-step
   constexpr int kRD = T::kFM + T::kFN;   // fragment reads per sub-step
-  static_assert(kRD <= kMF, "interleave pattern");
+  constexpr int kPre = kMF >= 16 ? 4 : (kMF >= 8 ? 2 : 1);   // MFMAs ahead of a sub-step's copies and barrier
+  constexpr int kSlots = kRD < kMF - kPre ? kRD : kMF - kPre;   // MFMAs that each carry some of the reads
   for (int kt = 0; kt < nk; ++kt) {
     static_for<NSUB>([&](auto jc) {
       constexpr int j = decltype(jc)::value;
       constexpr int cur = j & 1;
+      // the first kPre MFMAs of each sub-step go ahead of its copies, waits
+      // and barrier: they keep the SIMD's MFMA pipe busy while the wave
+      // issues copies or waits
+      mfma_range_t<j, 0, kPre>(acc, fa[cur], fb[cur], sa[0], sb[0]);
+      __builtin_amdgcn_sched_barrier(0);
       if constexpr (j < NSUB - 1) {
         if constexpr (j == 0) {
           if (kt > 0) {
@@ -585,14 +603,16 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, MINB) void gemm_mxfp4_pipe_
         load_scales(kt + 1, 1);              // past the last tile: unused, in-bounds LDS bytes
         load_frags(kt + 1, 0, cur ^ 1);
       }
-      mfma_substep_t<j>(acc, fa[cur], fb[cur], sa[0], sb[0]);
+      mfma_range_t<j, kPre, kMF>(acc, fa[cur], fb[cur], sa[0], sb[0]);
       // interleave: one MFMA, then that MFMA's share of the reads above
+      constexpr int kReads = (j == NSUB - 1 ? 2 : 1) * kRD;
+      constexpr int kPerSlot = (kReads + kSlots - 1) / kSlots;
 #pragma unroll
-      for (int q = 0; q < kRD; ++q) {
+      for (int q = 0; q < kSlots; ++q) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x100, j == NSUB - 1 ? 2 : 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, kPerSlot, 0);
       }
-      __builtin_amdgcn_sched_group_barrier(0x008, kMF - kRD, 0);
+      if constexpr (kMF - kPre - kSlots > 0) __builtin_amdgcn_sched_group_barrier(0x008, kMF - kPre - kSlots, 0);
     });
 #pragma unroll
     for (int mi = 0; mi < T::kFM; ++mi) sa[0][mi] = sa[1][mi];
