@@ -287,12 +287,29 @@ void act_quant_lane_kernel(
   // padded row (e_pad): expert e's rows start at padded row sum over
   // e' < e of ceil(rows_e' / 32) * 32, so that every expert starts a block
   int64_t e_beg = 0, e_pad = 0;
-  auto next_expert = [&]() {   // the lane's row crossed e_end
-    if constexpr (TILED) {
-      e_pad += (e_end - e_beg + 31) / 32 * 32;
-      e_beg = e_end;
+  // offsets[e_tbl + l] in lane l (the wave's first expert e_tbl and the 63
+  // after it), so that walking over experts, runs of empty ones included,
+  // reads a register of another lane instead of global memory (a load there
+  // would wait for every copy in flight)
+  int e_tbl = 0;
+  int32_t tbl = 0;
+  // advance every lane whose row r lies past its expert's end; the loop is
+  // wave-uniform so that the lane shuffle sees every lane's table entry
+  auto walk_experts = [&](int64_t r) {
+    for (;;) {
+      const bool adv = e + 1 < E && r >= e_end;
+      if (!__any(adv)) break;
+      const int k = e + 2 - e_tbl;                       // table index of the next expert's end
+      const int32_t next_end = __shfl(tbl, k < 64 ? k : 0, 64);
+      if (adv) {
+        if constexpr (TILED) {
+          e_pad += (e_end - e_beg + 31) / 32 * 32;
+          e_beg = e_end;
+        }
+        ++e;
+        e_end = k < 64 ? next_end : offsets[e + 1];
+      }
     }
-    e_end = offsets[++e + 1];
   };
   if constexpr (!PLAIN) {
     const int64_t rl = r0 + lr < M ? r0 + lr : M - 1;   // this lane's first row
@@ -303,6 +320,8 @@ void act_quant_lane_kernel(
       // loads; a lane whose first row lies past that expert walks on
       e = expert_of(r0 < M ? r0 : M - 1);
       e_end = offsets[e + 1];
+      e_tbl = e;
+      tbl = e_tbl + lane <= E ? offsets[e_tbl + lane] : 0;
       if constexpr (TILED) {
         e_beg = offsets[e];
         // padded rows of the experts before e, summed over the wave's lanes
@@ -315,7 +334,7 @@ void act_quant_lane_kernel(
         for (int d = 32; d >= 1; d >>= 1) p += __shfl_xor(p, d, 64);
         e_pad = p;
       }
-      while (e + 1 < E && rl >= e_end) next_expert();
+      walk_experts(rl);
     }
     if constexpr (SHARED) {
       const int64_t r_last = (rb + 4 * rows_per_wave < M ? rb + 4 * rows_per_wave : M) - 1;   // block's last row
@@ -389,7 +408,7 @@ void act_quant_lane_kernel(
       // expert of row r
       if (rows_per_expert > 0) e = (int)(r / rows_per_expert);
       else if (offsets != nullptr)
-        while (e + 1 < E && r >= e_end) next_expert();
+        walk_experts(r);
     }
     if constexpr (!PLAIN && !SHARED) {
       // this lane's factors, reloaded when its row's expert changes

@@ -170,6 +170,28 @@ def test_quant_act_many_experts(shared, steps, tune):
 
 
 @pytest.mark.parametrize("shared", ["0", "1"])
+@pytest.mark.parametrize("counts", [[5] + [0] * 100 + [7] + [0] * 20 + [4],
+                                    [0] * 6 + [8177, 3] + [0] * 12 + [12] + [0] * 43],
+                         ids=["runs of 100 and 20 empty experts in one wave", "expert-Zipf-like"])
+def test_quant_act_long_runs_of_empty_experts(counts, shared, tune):
+    """Rows of one wave separated by long runs of empty experts: the walk
+    over experts reads the wave's table of 64 offsets, and past it global
+    memory (the run of 100)."""
+    say(f"quant_act long empty runs E{len(counts)} shared={shared}")
+    tune(mx.TUNE_ACT_SHARED_S, 2 if shared == "1" else 1)
+    E, K = len(counts), 3072
+    off = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    M = int(off[-1])
+    rng = np.random.default_rng(M + E)
+    x = torch.from_numpy(rng.standard_normal((M, K)).astype(np.float32)).to(torch.bfloat16)
+    s = rng.uniform(0.25, 4.0, (E, K)).astype(np.float32)
+    codes, scales = mx.quant_act(x.to(DEV), torch.from_numpy(s).to(DEV), torch.from_numpy(off).to(DEV))
+    rc, rs = oracle.quant_act(host(x), s, off)
+    assert np.array_equal(scales.cpu().numpy(), rs)
+    assert np.array_equal(codes.cpu().numpy(), rc)
+
+
+@pytest.mark.parametrize("shared", ["0", "1"])
 @pytest.mark.parametrize("M,K", [(7, 32), (13, 96), (5, 160), (9, 2080)])
 def test_quant_act_narrow_rows(M, K, shared, tune):
     """Rows of 1, 3, 5 and 65 groups: most lanes of a segment are past the

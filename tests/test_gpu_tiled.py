@@ -220,7 +220,9 @@ def tiled_rows_reference(codes: np.ndarray, scales: np.ndarray, M: int, offsets=
                                            (64, 512, torch.float32, None), (300, 3072, torch.bfloat16, None),
                                            (33, 14336, torch.bfloat16, None),
                                            (300, 1024, torch.bfloat16, [3, 0, 130, 33, 0, 1, 133]),
-                                           (96, 3072, torch.bfloat16, [0, 32, 0, 64, 0])])
+                                           (96, 3072, torch.bfloat16, [0, 32, 0, 64, 0]),
+                                           (16, 512, torch.bfloat16, [5] + [0] * 100 + [7] + [0] * 20 + [4]),
+                                           (8192, 3072, torch.bfloat16, [0] * 6 + [8177, 3] + [0] * 12 + [12] + [0] * 43)])
 def test_quant_act_tiled_bit_exact(M, K, dt, counts):
     """macaq_quant_act_tiled writes the oracle's codes and scale bytes in the
     tiled layout, each expert from its padded row on (padding rows are not
