@@ -86,11 +86,12 @@ hipError_t launch_tile_weights(const uint8_t* wc, const uint8_t* ws, int64_t E, 
 // tiles cost no copy efficiency and keep three tiles in flight); 256x256
 // when that gives about one tile per CU, else 128x128 with two blocks per
 // CU.  a_tiled: the activation codes and scales are in the same tiled
-// layout (expert-padded for grouped layers); there the 128x128 tiles run
-// three blocks per CU with 3-deep rings (MoE E64 T8192 N1024 K3072: 24.3
-// against 27.2 us with two blocks of 4-deep rings, whose 528 tiles took one
-// round of 512 slots and a tail of 16; per-token routing 42.7 against 43.5;
-// attn-proj equal).
+// layout (expert-padded for grouped layers); there the grouped 128x128
+// tiles run three blocks per CU with 3-deep rings (MoE E64 T8192 N1024
+// K3072: 24.7 against 27.2 us with two blocks of 4-deep rings, whose 528
+// tiles took one round of 512 slots and a tail of 16; per-token routing
+// 45.8 against 45.0), dense ones two per CU (attn-proj 24.1 against 25.3);
+// same box, operands rotated past the Infinity Cache.
 hipError_t launch_gemm_tiled(const uint8_t* A, const uint8_t* As, const int32_t* offsets, int E, const uint8_t* B,
                              const uint8_t* Bs, int64_t M, int64_t N, int64_t K, void* Y, int mode, bool a_tiled,
                              hipStream_t stream) {
@@ -102,7 +103,10 @@ hipError_t launch_gemm_tiled(const uint8_t* A, const uint8_t* As, const int32_t*
     switch (choice) {
       case 0: return launch_pipe<256, 256, 2, 2, 128, 4, 1, true, true>(A, As, offsets, E, B, Bs, M, N, K, Y, mode, stream);
       case 1: return launch_pipe<256, 128, 2, 2, 128, 4, 1, true, true>(A, As, offsets, E, B, Bs, M, N, K, Y, mode, stream);
-      default: return launch_pipe<128, 128, 2, 2, 128, 3, 3, true, true>(A, As, offsets, E, B, Bs, M, N, K, Y, mode, stream);
+      default:
+        if (offsets != nullptr)
+          return launch_pipe<128, 128, 2, 2, 128, 3, 3, true, true>(A, As, offsets, E, B, Bs, M, N, K, Y, mode, stream);
+        return launch_pipe<128, 128, 2, 2, 128, 4, 2, true, true>(A, As, offsets, E, B, Bs, M, N, K, Y, mode, stream);
     }
   }
   switch (choice) {
