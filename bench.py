@@ -93,6 +93,9 @@ def parse():
     p.add_argument("--mfma-probe", action="store_true",
                    help="time the block-scaled FP4 MFMA alone (from registers, random and zero operands): "
                         "the MFMA throughput the chip sustains, next to the 10.1 PFLOP/s datasheet figure")
+    p.add_argument("--tune", action="append", default=[], metavar="KNOB=VALUE",
+                   help="override a launch shape for this run (macaq_set_tuning), e.g. GEMM_GROUP_M=8 or "
+                        "ACT_SEGMENT=32; repeatable; recorded in the line's config")
     p.add_argument("--copy-calibration", action="store_true",
                    help="only run a plain 512 MiB device-to-device copy (5 times) so that HBM byte "
                         "counters can be scaled against a transfer of known size")
@@ -629,6 +632,11 @@ def main():
     torch.cuda.set_device(dev)
     L = mx.lib()
     flags = {"auto": mx.PATH_AUTO, "fused": mx.PATH_FUSED, "unfused": mx.PATH_UNFUSED}[args.path]
+    tuned = {}
+    for t in args.tune:
+        knob, value = t.split("=")
+        mx.set_tuning(getattr(mx, "TUNE_" + knob.upper()), int(value))
+        tuned[knob.upper()] = int(value)
 
     # ---- resident inputs, R replicas so the rotation defeats the MALL
     x0 = wl.x.to(dev)
@@ -769,6 +777,7 @@ def main():
                    "y": f"{args.out} [{M}][{y_cols}]" + (" swiglu" if epi == mx.EPI_SWIGLU else ""),
                    "scale_rule": {"smooth": "s = 1/sigma", "literal": "s = sigma"}[args.scale_rule],
                    "kernel_timing": timing,
+                   **({"tuning": tuned} if tuned else {}),
                    "parallelism": "none (one GPU)"},
     }
     if act_us is not None:
