@@ -395,8 +395,8 @@ def linear(x, s, w_codes, w_scales, offsets=None, flags=PATH_AUTO, out=None, wor
     M, K = x.shape
     E, N, _ = w_codes.shape
     need = linear_workspace_bytes(M, N, K, E, flags)
-    if workspace is None and need > 0:
-        workspace = torch.zeros(need, dtype=torch.uint8, device=x.device)
+    if workspace is None and need > 0:   # (its contents need no initialization)
+        workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
     y = _out(M, N, out_dtype, epilogue, x.device, out)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     ydt = F32 if out_dtype == torch.float32 else BF16

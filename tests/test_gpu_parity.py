@@ -447,6 +447,7 @@ def decode_parts(M, N, K, split):
     return min(ks, kc)
 
 
+
 @pytest.mark.parametrize("waves,stages", [(8, 2), (4, 2), (4, 3)])
 def test_gemm_decode_forced_rings(waves, stages, tune):
     """Decode rings forced on one M = 32 shape: 8 waves of 2 slots (no longer
@@ -491,6 +492,46 @@ def test_gemm_decode(name, shape, split, tune):
     y2 = mx.gemm(*t)
     y_ref, S = oracle.gemm(ac, asc, wc, wsc)
     _check_y(y1.cpu().numpy(), y_ref, S)
+    assert torch.equal(y1, y2)
+
+
+SPLIT_STALE = [
+    ("M4 auto split 4", (4, 100, 256 * 128), 0, mx.EPI_NONE),
+    ("M32 64-row tiles 3 parts", (32, 130, 256 * 24), 3, mx.EPI_NONE),
+    ("M8 swiglu 2 parts", (8, 96, 256 * 16), 2, mx.EPI_SWIGLU),
+]
+
+
+@pytest.mark.parametrize("fill", ["ones", "random"])
+@pytest.mark.parametrize("name,shape,split,epi", SPLIT_STALE, ids=[n for n, *_ in SPLIT_STALE])
+def test_gemm_decode_split_stale_workspace(name, shape, split, epi, fill, tune):
+    """A K-split decode GEMM on a workspace whose bytes are left over from
+    something else (all 0xff, which reads as NaN, or random bytes): every
+    partial sum the split reads is written first, so y is within the
+    oracle's bound (SwiGLU: the bound carried through silu(g) u) and the
+    same bits on a second call."""
+    say(f"gemm decode split stale workspace {name} fill={fill}")
+    tune(mx.TUNE_DECODE_SPLIT, split)
+    M, N, K = shape
+    assert decode_parts(M, N, K, split) > 1
+    rng = np.random.default_rng(7100 + M + N)
+    ac = rng.integers(0, 256, (M, K // 2), dtype=np.uint8)
+    asc = rng.integers(110, 140, (M, K // 32), dtype=np.uint8)
+    wc = rng.integers(0, 256, (N, K // 2), dtype=np.uint8)
+    wsc = rng.integers(110, 140, (N, K // 32), dtype=np.uint8)
+    t = [torch.from_numpy(a).to(DEV) for a in (ac, asc, wc, wsc)]
+    need = int(mx.lib().macaq_gemm_workspace_bytes(M, N, K, 1))
+    host_ws = np.full(need, 0xFF, dtype=np.uint8) if fill == "ones" else rng.integers(0, 256, need, dtype=np.uint8)
+    ws = torch.from_numpy(host_ws).to(DEV)
+    y1 = mx.gemm(*t, workspace=ws, epilogue=epi)
+    y2 = mx.gemm(*t, workspace=ws, epilogue=epi)
+    y_ref, S = oracle.gemm(ac, asc, wc, wsc)
+    if epi == mx.EPI_SWIGLU:
+        bound = oracle.swiglu_bound(y_ref, S, RTOL)
+        err = np.abs(y1.cpu().numpy().astype(np.float64) - oracle.swiglu(y_ref))
+        assert (err <= bound).all(), f"{(err > bound).sum()} outputs beyond the bound"
+    else:
+        _check_y(y1.cpu().numpy(), y_ref, S)
     assert torch.equal(y1, y2)
 
 
