@@ -361,19 +361,27 @@ int macaq_linear_path(int64_t M, int64_t N, int64_t K, int64_t E, uint32_t flags
  *   macaq_prepare_weights, y [M][N] fp32 out.
  * flags: MACAQ_PATH_AUTO / _FUSED / _UNFUSED.  Both paths produce the same
  * activation codes; y may differ between paths only by fp32 summation order.
- * The fused path serves E == 1, M <= 32 and K % 256 == 0.  For M <= 2 the
- * kernel transforms each 256-wide chunk of the activation as the weights
- * stream past (any such K); for larger M it first transforms the whole
- * activation into LDS, so it serves only when M * (K/2 + K/32 + 24) bytes fit
- * beside the weight staging in the 160 KiB of LDS (otherwise a forced
- * MACAQ_PATH_FUSED returns MACAQ_ERR_UNSUPPORTED).  AUTO takes it for
- * M <= 2, and for small layers where ceil(N / 32) * M * K <= 2^20 (every
- * 32-row block repeats the transform of the whole activation): there one
- * launch beats two.
+ * The fused path serves E == 1, M <= 32 and K % 256 == 0, in one launch of
+ * the decode GEMM kernel (two with a K split, whose partial sums a second
+ * kernel adds).  For M <= 2 the kernel transforms each 256-wide chunk of the
+ * activation as the weights stream past.  For larger M, in small layers
+ * (ceil(N / 32) * M * K <= 2^20) where M * (K/2 + K/32 + 24) bytes fit beside
+ * the weight staging in the 160 KiB of LDS, every block first transforms
+ * the whole activation into its LDS.  Otherwise the first blocks of the
+ * launch transform it into the workspace (the same codes and scales as
+ * macaq_quant_act, stored device-coherent) and publish per-block done
+ * words; the other blocks start streaming weights, wait for the words,
+ * then run as on the unfused path, so y equals the unfused path's bit for
+ * bit.  AUTO takes the fused path for M <= 2 and for the small layers (one
+ * launch beats two there); for the other decode shapes the two launches
+ * measured faster than publishing within one.
  * Requires the argument rules of macaq_quant_act and macaq_gemm and a
  * workspace of macaq_linear_workspace_bytes(M, N, K, E, flags) bytes (the
- * unfused path's activation staging, and on either decode path the partial
- * sums of a K split, as in macaq_gemm).
+ * unfused path's activation staging; on either decode path the partial
+ * sums of a K split, as in macaq_gemm; on the fused path of the larger
+ * layers also the staged activation and 640 bytes of done words and
+ * counts).  The workspace needs no initial contents: done words hold a
+ * value unique to each launch and are cleared by the launch's last block.
  */
 int macaq_linear(const void* x, macaq_dtype x_dtype, const float* s,
                  const int32_t* expert_offsets, int64_t E,

@@ -28,7 +28,7 @@ hipError_t launch_gemm(const uint8_t* A, const uint8_t* As, const int32_t* offse
                        void* Y, int mode, hipStream_t stream);
 hipError_t launch_linear_fused(const void* x, bool x_f32, const float* s, const uint8_t* B,
                                const uint8_t* Bs, int64_t M, int64_t N, int64_t K, void* Y, int mode,
-                               float* part_ws, hipStream_t stream);
+                               void* ws, hipStream_t stream);
 size_t decode_workspace_bytes(int64_t M, int64_t N, int64_t K, bool fused);
 bool linear_fused_supported(int64_t M, int64_t N, int64_t K, int64_t E);
 bool decode_supported(int64_t M, int64_t N, int64_t K, int64_t E);
@@ -517,9 +517,7 @@ int linear_impl(const void* x, macaq_dtype x_dtype, const float* s, const int32_
   }
   if (M == 0) return MACAQ_OK;
   if (flags == MACAQ_PATH_FUSED && !macaq::linear_fused_supported(M, N, K, E))
-    return fail(MACAQ_ERR_UNSUPPORTED, std::string(fn) +
-                                           ": the fused path serves E == 1, M <= 32, K % 256 == 0 and, for M > 2, "
-                                           "the quantized activation fitting in LDS");
+    return fail(MACAQ_ERR_UNSUPPORTED, std::string(fn) + ": the fused path serves E == 1, M <= 32, K % 256 == 0");
   const bool fused = macaq_linear_path(M, N, K, E, flags) == MACAQ_PATH_FUSED;
   const size_t need = macaq_linear_workspace_bytes(M, N, K, E, flags);
   if (noalloc) {   // staging in the static scratch array instead of a workspace
@@ -543,7 +541,7 @@ int linear_impl(const void* x, macaq_dtype x_dtype, const float* s, const int32_
   if (fused)
     return finish(fn, st,
                   hip_status(macaq::launch_linear_fused(x, x_dtype == MACAQ_F32, s, w_codes, w_scales, M, N, K, y,
-                                                        mode, static_cast<float*>(workspace), st),
+                                                        mode, workspace, st),
                              "macaq_linear (fused)"));
   const bool a_tiled = stage_tiled(flags);
   uint8_t* a_codes = static_cast<uint8_t*>(workspace);

@@ -39,6 +39,8 @@
 // first weight chunk is in flight; the B fragments then come from LDS.
 // Every block repeats that transform, so the fused variant pays off only for
 // very small M.
+#include <atomic>
+
 #include "mx_common.h"
 
 namespace macaq {
@@ -160,14 +162,132 @@ struct DecWaveLds {
 
 __device__ __forceinline__ int dec_slot(int row, int piece) { return (row >> 3) * 1024 + (row & 7) * 128 + 16 * (piece ^ (row & 7)); }
 
+// ---- one-launch layer (PUB): the first blocks of the grid transform the
+// activation into the staging buffer, the rest wait for it.
+//
+// Synchronization words in the workspace (64-bit, device-coherent accesses,
+// no read-modify-write among the publishers):
+//   sync[0]       the blocks' finish count;
+//   sync[16 + p]  publisher p's done word: the launch's epoch once its slice
+//                 of the activation is stored (p < 64).
+// Publisher 0 first sets the finish count to 0; each publisher stores its
+// slice, waits for those stores, then stores its done word.  Wave 0 of every
+// block polls all done words with one load (lane p reads word p) until each
+// holds the epoch, so every block has seen publisher 0's reset before it adds
+// to the finish count.  Once all of a block's waves are past that wait, the
+// block adds 1 to the count; the block that completes it clears the done
+// words and the count, so a graph replay of a captured launch (whose epoch
+// is fixed) finds them clear.  The epoch is unique per launch in the
+// process, so done words left by another call, or whatever bytes the
+// workspace held, never read as done: the workspace needs no initial
+// contents.
+constexpr int kPubMax = 64;
+constexpr int kPubSyncWords = 16 + kPubMax;
+
+__device__ __forceinline__ void sync_store(unsigned long long* p, unsigned long long v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Poll the done words until all `pubs` hold this launch's epoch, about every
+// two microseconds (s_sleep 64; polling eight times as often was slower, the
+// polls themselves loading the memory path).  The publishing blocks are the
+// lowest block indices, which the dispatcher places first, and they wait on
+// nothing, so they are done within microseconds; the poll still gives up
+// after about a second (the result is then wrong, but the kernel ends).
+// Called by a whole wave.
+constexpr int kPubMaxPolls = 1 << 19;
+__device__ __forceinline__ void wait_published(unsigned long long* done, unsigned long long epoch, int pubs,
+                                               int lane) {
+  for (int i = 0; i < kPubMaxPolls; ++i) {
+    bool ok = true;
+    if (lane < pubs) ok = __hip_atomic_load(done + lane, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == epoch;
+    if (__builtin_amdgcn_ballot_w64(!ok) == 0) break;
+    __builtin_amdgcn_s_sleep(64);
+  }
+}
+
+// s_waitcnt vmcnt(n) for a wave-uniform n known only at run time.
+__device__ __forceinline__ void wait_vmcnt_rt(int n) {
+  switch (n) {
+#define MACAQ_VM_CASE(k) case k: wait_vmcnt<k>(); break;
+    MACAQ_VM_CASE(0) MACAQ_VM_CASE(1) MACAQ_VM_CASE(2) MACAQ_VM_CASE(3) MACAQ_VM_CASE(4) MACAQ_VM_CASE(5)
+    MACAQ_VM_CASE(6) MACAQ_VM_CASE(7) MACAQ_VM_CASE(8) MACAQ_VM_CASE(9) MACAQ_VM_CASE(10) MACAQ_VM_CASE(11)
+    MACAQ_VM_CASE(12) MACAQ_VM_CASE(13) MACAQ_VM_CASE(14) MACAQ_VM_CASE(15) MACAQ_VM_CASE(16) MACAQ_VM_CASE(17)
+    MACAQ_VM_CASE(18) MACAQ_VM_CASE(19) MACAQ_VM_CASE(20) MACAQ_VM_CASE(21) MACAQ_VM_CASE(22) MACAQ_VM_CASE(23)
+    MACAQ_VM_CASE(24) MACAQ_VM_CASE(25) MACAQ_VM_CASE(26) MACAQ_VM_CASE(27) MACAQ_VM_CASE(28) MACAQ_VM_CASE(29)
+    MACAQ_VM_CASE(30) MACAQ_VM_CASE(31) MACAQ_VM_CASE(32) MACAQ_VM_CASE(33) MACAQ_VM_CASE(34) MACAQ_VM_CASE(35)
+    MACAQ_VM_CASE(36) MACAQ_VM_CASE(37) MACAQ_VM_CASE(38) MACAQ_VM_CASE(39) MACAQ_VM_CASE(40) MACAQ_VM_CASE(41)
+    MACAQ_VM_CASE(42) MACAQ_VM_CASE(43) MACAQ_VM_CASE(44) MACAQ_VM_CASE(45) MACAQ_VM_CASE(46) MACAQ_VM_CASE(47)
+    MACAQ_VM_CASE(48) MACAQ_VM_CASE(49) MACAQ_VM_CASE(50) MACAQ_VM_CASE(51) MACAQ_VM_CASE(52) MACAQ_VM_CASE(53)
+    MACAQ_VM_CASE(54) MACAQ_VM_CASE(55) MACAQ_VM_CASE(56) MACAQ_VM_CASE(57) MACAQ_VM_CASE(58) MACAQ_VM_CASE(59)
+    MACAQ_VM_CASE(60) MACAQ_VM_CASE(61) MACAQ_VM_CASE(62)
+#undef MACAQ_VM_CASE
+    default: wait_vmcnt<63>();
+  }
+}
+
+// Publisher block b of `pubs`: 32-element groups [b * per, (b + 1) * per) of
+// the M x K/32 groups (row-major), one quad of lanes per group, batches of
+// 4 groups per quad whose loads overlap; the same scale, transform and
+// quantization as the activation kernel.  Codes [M][K/2] and scales
+// [M][K/32] are stored device-coherent (sc1), so that blocks on other XCDs
+// read them from memory once the count says they are there.
+template <typename XT>
+__device__ __forceinline__ void publish_slice(const void* x, const float* s, int64_t M, int64_t K, uint8_t* codes,
+                                              uint8_t* scales, int b, int pubs, int tid, int threads) {
+  constexpr int kBatch = 4;
+  const int quads = threads / 4;
+  const int64_t KG = K >> 5;
+  const int64_t tasks = M * KG;
+  const int64_t per = (tasks + pubs - 1) / pubs;
+  const int64_t t_begin = (int64_t)b * per;
+  const int64_t t_end = t_begin + per < tasks ? t_begin + per : tasks;
+  const uint32_t quad = (uint32_t)tid & 3u;
+  for (int64_t base = t_begin + (tid >> 2); base < t_end; base += (int64_t)kBatch * quads) {
+    float t[kBatch][8];
+    float4 sa[kBatch], sb[kBatch];
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j) {
+      const int64_t t0 = base + (int64_t)j * quads;   // the same for the quad's four lanes
+      if (t0 < t_end) {
+        const int64_t m = t0 / KG, g = t0 % KG;
+        const int64_t col = g * 32 + quad * 8;
+        dec_load8<XT>(x, m * K + col, t[j]);
+        const float4* sp = reinterpret_cast<const float4*>(s + col);
+        sa[j] = sp[0];
+        sb[j] = sp[1];
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j) {
+      const int64_t t0 = base + (int64_t)j * quads;
+      if (t0 < t_end) {
+        const int64_t m = t0 / KG, g = t0 % KG;
+        float* v = t[j];
+        v[0] = v[0] * sa[j].x; v[1] = v[1] * sa[j].y; v[2] = v[2] * sa[j].z; v[3] = v[3] * sa[j].w;
+        v[4] = v[4] * sb[j].x; v[5] = v[5] * sb[j].y; v[6] = v[6] * sb[j].z; v[7] = v[7] * sb[j].w;
+        hadamard32_quad(t[j], quad);
+        uint32_t e;
+        const uint32_t packed = quantize_quad(t[j], &e);
+        __hip_atomic_store(reinterpret_cast<uint32_t*>(codes + m * (K >> 1) + g * 16 + quad * 4), packed,
+                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (quad == 0)
+          __hip_atomic_store(scales + m * KG + g, (uint8_t)e, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+    }
+  }
+}
+
 // A block owns RT x 32 weight rows (RT MFMA row tiles sharing each
 // activation chunk).
-template <int WAVES, int STAGES, int AK, typename XT, int RT = 1>
+template <int WAVES, int STAGES, int AK, typename XT, int RT = 1, bool PUB = false>
 __global__ __launch_bounds__(64 * WAVES) void decode_gemm_kernel(
-    const uint8_t* __restrict__ A, const uint8_t* __restrict__ As,     // activation codes/scales (unfused)
+    const uint8_t* A, const uint8_t* As,                               // activation codes/scales (staged)
     const void* __restrict__ x, const float* __restrict__ s,           // activations and scale (fused)
     const uint8_t* __restrict__ W, const uint8_t* __restrict__ Ws, int64_t M, int64_t N, int64_t K,
-    void* __restrict__ Y, int out_mode, float* __restrict__ part_ws, int ksplit) {
+    void* __restrict__ Y, int out_mode, float* __restrict__ part_ws, int ksplit,
+    unsigned long long* sync, unsigned long long epoch, int pubs) {
+  static_assert(!PUB || AK >= 8, "the one-launch layer stages 8, 16 or 32 activation rows");
   constexpr int EB = dec_eb<XT>;
   using S = DecStage<AK, EB, RT>;
   constexpr bool FUSED = AK == 0;     // resident activation, transformed before the loop
@@ -254,14 +374,19 @@ __global__ __launch_bounds__(64 * WAVES) void decode_gemm_kernel(
     if (ofs > KG - 4) ofs = KG - 4;
     dma4(Ws + wn * KG + ofs, ring_addr + (uint32_t)(WL::kSlab0 + (seg % kSlabs) * WL::kSlabBytes + t * 256));
   };
-  // chunk c's copies, plus RT slab copies for the segment after c's
-  auto issue = [&](int c) {
+  // chunk c's copies: the weight part (codes, plus RT slab copies for the
+  // segment after c's), then the activation part
+  auto issue_w = [&](int c) {
     const uint32_t base = ring_addr + (uint32_t)(((c - c0) % STAGES) * S::kBytes);
-    const int64_t co = (int64_t)c * 128, so = (int64_t)c * 8;
+    const int64_t co = (int64_t)c * 128;
 #pragma unroll
     for (int i = 0; i < 4 * RT; ++i) dma16_nt(wsrc[i] + co, base + S::kW + i * 1024);
 #pragma unroll
     for (int i = 0; i < RT; ++i) issue_slab((c - c0) / kSeg + 1, ((c - c0) % kSeg) * RT + i);
+  };
+  auto issue_a = [&](int c) {
+    const uint32_t base = ring_addr + (uint32_t)(((c - c0) % STAGES) * S::kBytes);
+    const int64_t co = (int64_t)c * 128, so = (int64_t)c * 8;
     if constexpr (AK == 1) {
       dma4(asrc[0] + co, base + S::kA);
     } else if constexpr (AK >= 8) {
@@ -275,15 +400,51 @@ __global__ __launch_bounds__(64 * WAVES) void decode_gemm_kernel(
       for (int i = 0; i < EB / 2; ++i) dma16(xsrc[i] + (int64_t)c * 256 * EB, base + S::kX + i * 1024);
     }
   };
+  auto issue = [&](int c) {
+    issue_w(c);
+    issue_a(c);
+  };
+  // one-launch layer: a publishing block transforms its slice of x first
+  // (its loads then wait for no copy), stores it device-coherent, waits for
+  // the stores and adds to the count
+  if constexpr (PUB) {
+    const int flat = (int)(blockIdx.y * gridDim.x + blockIdx.x);
+    if (flat < pubs) {
+      if (flat == 0 && tid == 0) sync_store(sync, 0ull);
+      publish_slice<XT>(x, s, M, K, const_cast<uint8_t*>(A), const_cast<uint8_t*>(As), flat, pubs, tid, kThreads);
+      wait_vmcnt<0>();
+      __syncthreads();
+      if (tid == 0) sync_store(sync + 16 + flat, epoch);
+    }
+  }
+
   // segment 0's slab, then fill the ring (before the fused transform, which
-  // then overlaps the copies)
+  // then overlaps the copies).  One-launch layer: the weight copies of the
+  // first chunks, the wait for the published activation, then its copies.
   if (c0 < c1) {
 #pragma unroll
     for (int t = 0; t < kSeg * RT; ++t) issue_slab(0, t);
   }
+  // weight chunks issued before the wait: the whole prologue (1 or none
+  // measured no faster: the publishers' loads still queue behind the copies)
+  constexpr int kPre = STAGES - 1;
+  if constexpr (PUB) {
 #pragma unroll
-  for (int q = 0; q < STAGES - 1; ++q)
-    if (c0 + q < c1) issue(c0 + q);
+    for (int q = 0; q < kPre; ++q)
+      if (c0 + q < c1) issue_w(c0 + q);
+    if (wave == 0) wait_published(sync + 16, epoch, pubs, lane);
+    __syncthreads();   // (no wait for the copies in flight)
+#pragma unroll
+    for (int q = 0; q < kPre; ++q)
+      if (c0 + q < c1) issue_a(c0 + q);
+#pragma unroll
+    for (int q = kPre; q < STAGES - 1; ++q)
+      if (c0 + q < c1) issue(c0 + q);
+  } else {
+#pragma unroll
+    for (int q = 0; q < STAGES - 1; ++q)
+      if (c0 + q < c1) issue(c0 + q);
+  }
 
   if constexpr (FUSED) {
     // one quad of lanes per 32-element group; each quad loads the inputs of
@@ -346,7 +507,15 @@ __global__ __launch_bounds__(64 * WAVES) void decode_gemm_kernel(
     // wait until chunk c has landed: the copies of the chunks after it may
     // stay in flight
     const int ahead = (c1 - 1 - c) < (STAGES - 1) ? (c1 - 1 - c) : (STAGES - 1);
-    if (STAGES > 3 && ahead == 3) wait_vmcnt<(STAGES > 3 ? 3 : 0) * S::kCopies>();
+    const int n_ch = c1 - c0, p0 = n_ch < STAGES - 1 ? n_ch : STAGES - 1;
+    const int pre = kPre < p0 ? kPre : p0;
+    if (PUB && c - c0 < pre) {
+      // the first `pre` chunks' activation copies were issued after their
+      // weight copies: after chunk c's come the activation copies of the
+      // later ones, the prologue's whole chunks and the loop's so far
+      const int loop_chunks = n_ch - STAGES >= 0 ? ((c - c0) < n_ch - STAGES ? (c - c0) : n_ch - STAGES) + 1 : 0;
+      wait_vmcnt_rt((pre - 1 - (c - c0)) * S::kACopies + (p0 - pre + loop_chunks) * S::kCopies);
+    } else if (STAGES > 3 && ahead == 3) wait_vmcnt<(STAGES > 3 ? 3 : 0) * S::kCopies>();
     else if (STAGES > 2 && ahead == 2) wait_vmcnt<(STAGES > 2 ? 2 : 0) * S::kCopies>();
     else if (ahead == 1) wait_vmcnt<S::kCopies>();
     else wait_vmcnt<0>();
@@ -425,6 +594,19 @@ __global__ __launch_bounds__(64 * WAVES) void decode_gemm_kernel(
     }
   }
   __syncthreads();
+  if constexpr (PUB) {
+    // every wave of the block is past its wait for the activation: the last
+    // block of the launch to get here clears the words
+    if (tid < 64) {
+      unsigned long long before = 0;
+      if (tid == 0) before = __hip_atomic_fetch_add(sync, 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      before = __shfl(before, 0);
+      if (before == (unsigned long long)(gridDim.x * gridDim.y - 1)) {
+        if (tid < pubs) sync_store(sync + 16 + tid, 0ull);
+        if (tid == 0) sync_store(sync, 0ull);
+      }
+    }
+  }
   if (ksplit > 1) {
     // this part's fp32 sums of the block's columns, [part][M][N]; the split
     // reduce kernel adds the parts in order and applies the output mode
@@ -607,18 +789,35 @@ bool decode_supported(int64_t M, int64_t N, int64_t K, int64_t E) {
   return E == 1 && M >= 1 && M <= kDecMaxM && N >= 1 && K % 256 == 0;
 }
 
-template <int WAVES, int STAGES, int AK, typename XT, int RT>
+// One-launch layer: counts word pair, epoch and number of publishing blocks.
+struct PubLaunch {
+  unsigned long long* sync = nullptr;
+  unsigned long long epoch = 0;
+  int pubs = 0;
+};
+
+// Epoch of a one-launch layer: a 40-bit value unique within the process
+// (its start is arbitrary, away from the small integers that stale
+// workspace bytes often hold).
+static unsigned long long next_pub_epoch() {
+  static std::atomic<unsigned long long> epoch{0x5f3a9c6e1ull};
+  return epoch.fetch_add(1, std::memory_order_relaxed) & 0xffffffffffull;
+}
+
+template <int WAVES, int STAGES, int AK, typename XT, int RT, bool PUB>
 static hipError_t launch_decode_w(const uint8_t* A, const uint8_t* As, const void* x, const float* s,
                                   const uint8_t* W, const uint8_t* Ws, int64_t M, int64_t N, int64_t K, void* Y,
-                                  int mode, size_t lds, float* part_ws, int ksplit, hipStream_t stream) {
+                                  int mode, size_t lds, float* part_ws, int ksplit, const PubLaunch& pl,
+                                  hipStream_t stream) {
   static_assert(DecWaveLds<STAGES, AK, dec_eb<XT>, RT>::kBytes >= 32 * RT * 32 * 4,
                 "partial sums must fit in the rings");
-  static const hipError_t attr = hipFuncSetAttribute((const void*)decode_gemm_kernel<WAVES, STAGES, AK, XT, RT>,
-                                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)kDecLdsMax);
+  static const hipError_t attr = hipFuncSetAttribute(
+      (const void*)decode_gemm_kernel<WAVES, STAGES, AK, XT, RT, PUB>, hipFuncAttributeMaxDynamicSharedMemorySize,
+      (int)kDecLdsMax);
   if (attr != hipSuccess) return attr;
-  decode_gemm_kernel<WAVES, STAGES, AK, XT, RT>
+  decode_gemm_kernel<WAVES, STAGES, AK, XT, RT, PUB>
       <<<dim3((unsigned)ceil_div(N, kDecRows * RT), (unsigned)ksplit), dim3(64 * WAVES), lds, stream>>>(
-          A, As, x, s, W, Ws, M, N, K, Y, mode, part_ws, ksplit);
+          A, As, x, s, W, Ws, M, N, K, Y, mode, part_ws, ksplit, pl.sync, pl.epoch, pl.pubs);
   if (ksplit > 1) {
     if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
     const int64_t outs = (mode & kOutSwiGLU) ? M * (N >> 1) : M * N;
@@ -628,25 +827,29 @@ static hipError_t launch_decode_w(const uint8_t* A, const uint8_t* As, const voi
   return hipGetLastError();
 }
 
-template <int AK, typename XT>
+template <int AK, typename XT, bool PUB = false>
 static hipError_t launch_decode_impl(const DecodeConfig& d, const uint8_t* A, const uint8_t* As, const void* x,
                                      const float* s, const uint8_t* W, const uint8_t* Ws, int64_t M, int64_t N,
-                                     int64_t K, void* Y, int mode, float* part_ws, hipStream_t stream) {
+                                     int64_t K, void* Y, int mode, float* part_ws, hipStream_t stream,
+                                     const PubLaunch& pl = PubLaunch()) {
   if (d.ksplit > 1 && part_ws == nullptr) return hipErrorInvalidValue;
   const size_t lds = decode_lds_bytes(d, M, K);
   if (lds > kDecLdsMax) return hipErrorInvalidValue;
+#define MACAQ_DEC_LAUNCH(WV, ST, RTV) \
+  launch_decode_w<WV, ST, AK, XT, RTV, PUB>(A, As, x, s, W, Ws, M, N, K, Y, mode, lds, part_ws, d.ksplit, pl, stream)
   if (d.rt == 2) {
-    if (d.stages >= 3) return launch_decode_w<2, 3, AK, XT, 2>(A, As, x, s, W, Ws, M, N, K, Y, mode, lds, part_ws, d.ksplit, stream);
-    return launch_decode_w<2, 2, AK, XT, 2>(A, As, x, s, W, Ws, M, N, K, Y, mode, lds, part_ws, d.ksplit, stream);
+    if (d.stages >= 3) return MACAQ_DEC_LAUNCH(2, 3, 2);
+    return MACAQ_DEC_LAUNCH(2, 2, 2);
   }
   if (d.waves == 8) {
-    if (d.stages == 4) return launch_decode_w<8, 4, AK, XT, 1>(A, As, x, s, W, Ws, M, N, K, Y, mode, lds, part_ws, d.ksplit, stream);
-    if (d.stages == 3) return launch_decode_w<8, 3, AK, XT, 1>(A, As, x, s, W, Ws, M, N, K, Y, mode, lds, part_ws, d.ksplit, stream);
-    return launch_decode_w<8, 2, AK, XT, 1>(A, As, x, s, W, Ws, M, N, K, Y, mode, lds, part_ws, d.ksplit, stream);
+    if (d.stages == 4) return MACAQ_DEC_LAUNCH(8, 4, 1);
+    if (d.stages == 3) return MACAQ_DEC_LAUNCH(8, 3, 1);
+    return MACAQ_DEC_LAUNCH(8, 2, 1);
   }
-  if (d.stages == 4) return launch_decode_w<4, 4, AK, XT, 1>(A, As, x, s, W, Ws, M, N, K, Y, mode, lds, part_ws, d.ksplit, stream);
-  if (d.stages == 3) return launch_decode_w<4, 3, AK, XT, 1>(A, As, x, s, W, Ws, M, N, K, Y, mode, lds, part_ws, d.ksplit, stream);
-  return launch_decode_w<4, 2, AK, XT, 1>(A, As, x, s, W, Ws, M, N, K, Y, mode, lds, part_ws, d.ksplit, stream);
+  if (d.stages == 4) return MACAQ_DEC_LAUNCH(4, 4, 1);
+  if (d.stages == 3) return MACAQ_DEC_LAUNCH(4, 3, 1);
+  return MACAQ_DEC_LAUNCH(4, 2, 1);
+#undef MACAQ_DEC_LAUNCH
 }
 
 hipError_t launch_decode_gemm(const uint8_t* A, const uint8_t* As, const uint8_t* W, const uint8_t* Ws, int64_t M,
@@ -660,28 +863,95 @@ hipError_t launch_decode_gemm(const uint8_t* A, const uint8_t* As, const uint8_t
   }
 }
 
-// Workspace (fp32 partial sums of the K-split parts) the decode GEMM needs
-// for this shape: 0 without a split.
+// Fused variant of a decode-sized layer: -1 the streamed transform (M <= 2),
+// 0 the resident one (every block transforms the whole activation into its
+// LDS: small layers, where ceil(N / 32) * M * K <= 2^20 and it fits), 1 the
+// one-launch layer (the first blocks publish the transformed activation to
+// the workspace, the others wait for it).
+constexpr int64_t kDecResidentRepeat = int64_t(1) << 20;
+static int fused_kind(int64_t M, int64_t N, int64_t K) {
+  if (M <= 2) return -1;
+  const int64_t repeat = ceil_div(N, kDecRows) * M * K;
+  if (repeat <= kDecResidentRepeat) {
+    bool fits = true;
+    for (int eb : {2, 4})
+      if (decode_lds_bytes(decode_config(M, N, K, true, eb), M, K) > kDecLdsMax) fits = false;
+    if (fits) return 0;
+  }
+  return 1;
+}
+
+// One-launch workspace: activation codes [M][K/2] and scales [M][K/32] (each
+// from a 256-byte boundary), the split's partial sums, then the
+// synchronization words (two counts and eight ready-flag lines).
+struct PubLayout {
+  size_t scales, parts, sync, bytes;
+};
+static PubLayout pub_layout(int64_t M, int64_t N, int64_t K, const DecodeConfig& d) {
+  auto up = [](size_t b) { return (b + 255) / 256 * 256; };
+  PubLayout l;
+  l.scales = up((size_t)M * (size_t)K / 2);
+  l.parts = l.scales + up((size_t)M * (size_t)K / 32);
+  l.sync = l.parts + (d.ksplit > 1 ? up((size_t)d.ksplit * (size_t)M * (size_t)N * sizeof(float)) : 0);
+  l.bytes = l.sync + kPubSyncWords * sizeof(unsigned long long);
+  return l;
+}
+
+// Workspace the decode GEMM (fused: the fused layer) needs for this shape:
+// the fp32 partial sums of a K split, and for the one-launch layer the
+// staged activation and the counts; 0 when none.
 size_t decode_workspace_bytes(int64_t M, int64_t N, int64_t K, bool fused) {
   if (!decode_supported(M, N, K, 1)) return 0;
+  if (fused && fused_kind(M, N, K) == 1) return pub_layout(M, N, K, decode_config(M, N, K, false, 2)).bytes;
   const DecodeConfig d = decode_config(M, N, K, fused, 2);
   return d.ksplit > 1 ? (size_t)d.ksplit * (size_t)M * (size_t)N * sizeof(float) : 0;
 }
 
 // -------- fused transform + GEMM entry used by macaq_linear
 
-// Whether the fused path fits, for either activation dtype.
-bool linear_fused_supported(int64_t M, int64_t N, int64_t K, int64_t E) {
-  if (!decode_supported(M, N, K, E)) return false;
-  for (int eb : {2, 4})
-    if (decode_lds_bytes(decode_config(M, N, K, true, eb), M, K) > kDecLdsMax) return false;
-  return true;
+// Whether the fused path serves this shape (any decode-sized dense layer).
+bool linear_fused_supported(int64_t M, int64_t N, int64_t K, int64_t E) { return decode_supported(M, N, K, E); }
+
+// Whether the fused path of this shape is the one-launch layer.
+bool linear_fused_one_launch(int64_t M, int64_t N, int64_t K) { return fused_kind(M, N, K) == 1; }
+
+template <typename XT>
+static hipError_t launch_one_launch(const void* x, const float* s, const uint8_t* B, const uint8_t* Bs, int64_t M,
+                                    int64_t N, int64_t K, void* Y, int mode, uint8_t* ws, hipStream_t stream) {
+  // the unfused path's ring shapes, with the activation staged in the workspace
+  const DecodeConfig d = decode_config(M, N, K, false, 2);
+  const PubLayout l = pub_layout(M, N, K, d);
+  const int threads = 64 * (d.rt == 2 ? 2 : d.waves);
+  const int64_t blocks = ceil_div(N, kDecRows * d.rt) * d.ksplit;
+  const int64_t groups = M * (K / 32);
+  int64_t pubs = ceil_div(groups, threads);   // one batch of 4 groups per quad of lanes
+  if (pubs > kPubMax) pubs = kPubMax;
+  if (pubs > blocks) pubs = blocks;
+  PubLaunch pl;
+  pl.sync = reinterpret_cast<unsigned long long*>(ws + l.sync);
+  pl.epoch = next_pub_epoch();
+  pl.pubs = (int)pubs;
+  const uint8_t* A = ws;
+  const uint8_t* As = ws + l.scales;
+  float* part_ws = d.ksplit > 1 ? reinterpret_cast<float*>(ws + l.parts) : nullptr;
+  switch (d.ak) {
+    case 8: return launch_decode_impl<8, XT, true>(d, A, As, x, s, B, Bs, M, N, K, Y, mode, part_ws, stream, pl);
+    case 16: return launch_decode_impl<16, XT, true>(d, A, As, x, s, B, Bs, M, N, K, Y, mode, part_ws, stream, pl);
+    default: return launch_decode_impl<32, XT, true>(d, A, As, x, s, B, Bs, M, N, K, Y, mode, part_ws, stream, pl);
+  }
 }
 
 hipError_t launch_linear_fused(const void* x, bool x_f32, const float* s, const uint8_t* B, const uint8_t* Bs,
-                               int64_t M, int64_t N, int64_t K, void* Y, int mode, float* part_ws, hipStream_t stream) {
+                               int64_t M, int64_t N, int64_t K, void* Y, int mode, void* ws, hipStream_t stream) {
+  const int kind = fused_kind(M, N, K);
+  if (kind == 1) {
+    if (ws == nullptr) return hipErrorInvalidValue;
+    if (x_f32) return launch_one_launch<float>(x, s, B, Bs, M, N, K, Y, mode, static_cast<uint8_t*>(ws), stream);
+    return launch_one_launch<DecBf16>(x, s, B, Bs, M, N, K, Y, mode, static_cast<uint8_t*>(ws), stream);
+  }
+  float* part_ws = static_cast<float*>(ws);
   const DecodeConfig d = decode_config(M, N, K, true, x_f32 ? 4 : 2);
-  if (d.ak < 0) {
+  if (kind < 0) {
     if (x_f32) return launch_decode_impl<-1, float>(d, nullptr, nullptr, x, s, B, Bs, M, N, K, Y, mode, part_ws, stream);
     return launch_decode_impl<-1, DecBf16>(d, nullptr, nullptr, x, s, B, Bs, M, N, K, Y, mode, part_ws, stream);
   }

@@ -24,6 +24,8 @@ CASES = [
     ("decode M1, fused", dict(cfg=4, shape=(1, 512, 2048)), mx.PATH_AUTO, False),
     ("decode M8, two launches", dict(cfg=4, shape=(8, 512, 2048)), mx.PATH_UNFUSED, False),
     ("decode M32, K split in 3 with its reduce", dict(cfg=4, shape=(32, 256, 256 * 48)), mx.PATH_UNFUSED, False),
+    ("decode M8, one launch (published activation)", dict(cfg=4, shape=(8, 4160, 1024)), mx.PATH_FUSED, False),
+    ("decode M32, one launch with a K split in 3", dict(cfg=4, shape=(32, 1024, 256 * 48)), mx.PATH_FUSED, False),
     ("MoE, grouped", dict(cfg=5, shape=(300, 64, 512), routing="token_zipf"), mx.PATH_AUTO, True),
 ]
 

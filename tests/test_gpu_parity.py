@@ -562,6 +562,53 @@ def test_linear_decode_paths(name, kw, flags):
     assert torch.equal(y, y_again)
 
 
+ONE_LAUNCH = [
+    ("M8", dict(cfg=4, shape=(8, 4160, 1024))),
+    ("M3", dict(cfg=4, shape=(3, 4400, 2560))),
+    ("M5 ragged N", dict(cfg=4, shape=(5, 3000, 2304))),
+    ("M16", dict(cfg=4, shape=(16, 1000, 4096))),
+    ("M32", dict(cfg=4, shape=(32, 640, 2560))),
+    ("M8 K split 2", dict(cfg=4, shape=(8, 2048, 256 * 64))),
+    ("M32 64-row tiles, K split 3", dict(cfg=4, shape=(32, 1024, 256 * 48))),
+    ("M8 fp32 x", dict(cfg=1, shape=(8, 4160, 1024))),
+]
+
+
+@pytest.mark.parametrize("name,kw", ONE_LAUNCH, ids=[n for n, _ in ONE_LAUNCH])
+def test_linear_one_launch(name, kw):
+    """The fused path of a decode-sized layer too large for every block to
+    transform the whole activation (ceil(N/32) M K > 2^20): the first blocks
+    of the launch publish the transformed activation to the workspace and
+    the others wait for it.  On a workspace of stale bytes (all 0xff) and
+    again on the one the first call left: the staged codes and scales equal
+    macaq_quant_act's bit for bit, y equals the two-launch path's bit for
+    bit (same staged codes, same GEMM blocks and summation order), and
+    sampled columns of y are within the oracle's bound."""
+    say(f"linear one launch {name}")
+    wl = workloads.make(**kw)
+    M, N, K = wl.M, wl.N, wl.K
+    assert mx.lib().macaq_linear_path(M, N, K, 1, mx.PATH_FUSED) == mx.PATH_FUSED
+    wc, wsc = gpu_prepare(wl)
+    x, s = wl.x.to(DEV), wl.s.to(DEV)
+    need = mx.linear_workspace_bytes(M, N, K, 1, mx.PATH_FUSED)
+    assert need >= (M * K // 2 + 255) // 256 * 256 + (M * K // 32 + 255) // 256 * 256 + 16
+    ws = torch.full((need,), 0xFF, dtype=torch.uint8, device=DEV)
+    y1 = mx.linear(x, s, wc, wsc, flags=mx.PATH_FUSED, workspace=ws)
+    torch.cuda.synchronize()
+    codes, scales = mx.quant_act(x, s)
+    sofs = (M * K // 2 + 255) // 256 * 256
+    assert torch.equal(ws[: M * K // 2].view(M, K // 2), codes)
+    assert torch.equal(ws[sofs: sofs + M * K // 32].view(M, K // 32), scales)
+    y2 = mx.linear(x, s, wc, wsc, flags=mx.PATH_FUSED, workspace=ws)
+    y_two = mx.linear(x, s, wc, wsc, flags=mx.PATH_UNFUSED)
+    assert torch.equal(y1, y_two)
+    assert torch.equal(y1, y2)
+    rows = np.unique(np.concatenate([np.arange(0, N, max(1, N // 48)), np.arange(max(0, N - 40), N)]))
+    rwc, rws = oracle_prepare(wl, 0, rows)
+    y_ref, S = oracle.linear(host(wl.x), wl.s.numpy(), rwc, rws)
+    _check_y(y1.cpu().numpy()[:, rows], y_ref, S)
+
+
 ROWS64_GEMM = [(1, 1000, 2560), (3, 200, 2048), (12, 70, 256 * 7), (32, 1000, 2560)]
 ROWS64_LINEAR = [
     ("M1 fp32 tiny-shaped", dict(cfg=1, shape=(1, 96, 512))),

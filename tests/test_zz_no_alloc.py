@@ -2,8 +2,9 @@
 staging lives in the library's static device array) against macaq_linear_ex
 with a caller workspace: bit for bit on consecutive calls of different sizes
 (the array keeps the previous call's bytes), on the unfused prefill, grouped
-and decode paths and the fused decode path, with and without the decode K
-split (whose partial sums also live in the array)."""
+and decode paths and the fused decode paths (streamed, and one launch with
+the published activation and its counts in the array), with and without the
+decode K split (whose partial sums also live in the array)."""
 import numpy as np
 import pytest
 import torch
@@ -17,8 +18,11 @@ DEV = "cuda:0"
 CASES = [   # consecutive calls: each smaller than the one before
     ("attn-proj M2048 N4096 K4096, tiled W'", dict(cfg=2), True, mx.PATH_AUTO),
     ("MoE-shaped M300 N64 K1024", dict(cfg=5, shape=(300, 64, 1024)), False, mx.PATH_AUTO),
+    ("decode-shaped M32 N1024 K12288 one launch, K split in 3", dict(cfg=4, shape=(32, 1024, 256 * 48)), False,
+     mx.PATH_FUSED),
     ("decode-shaped M8 N256 K16384, K split in 2", dict(cfg=4, shape=(8, 256, 16384)), False, mx.PATH_AUTO),
     ("decode-shaped M8 N512 K2048", dict(cfg=4, shape=(8, 512, 2048)), False, mx.PATH_AUTO),
+    ("decode-shaped M8 N4160 K1024 one launch", dict(cfg=4, shape=(8, 4160, 1024)), False, mx.PATH_FUSED),
     ("decode-shaped M1 N128 K16384 fused, K split in 2", dict(cfg=4, shape=(1, 128, 16384)), False, mx.PATH_FUSED),
     ("decode-shaped M2 N256 K1024 fused", dict(cfg=4, shape=(2, 256, 1024)), False, mx.PATH_FUSED),
 ]
