@@ -669,6 +669,179 @@ __global__ void decode_split_reduce_kernel(const float* __restrict__ part_ws, in
   store_out(Y, i, v, out_mode);
 }
 
+// ---- decode GEMM for more than 8 activation rows, without a K split:
+// waves split rows, and share each staged activation chunk.
+//
+// With 16 or 32 activation rows the activation's part of a chunk is as
+// large as a 32-row tile's weights; when every wave stages its own copy
+// (waves splitting K, decode_gemm_kernel) it doubles the LDS fill per chunk
+// and halves the ring.  Here a block of WAVES waves owns 32 WAVES weight
+// rows, wave w the 32 rows from n0 + 32 w, and all waves walk all chunks of
+// K: the activation chunk (AK rows of codes and the 32 x 8 scale bytes) sits
+// once per ring slot in LDS shared by the waves.  Each wave's weights and W'
+// scale slabs are its own, as in decode_gemm_kernel.  Each wave issues its weight copies and a share of the
+// activation copies (instruction i of the AK / 8 goes to wave i % WAVES,
+// with waves past the last one repeating an instruction, and every wave
+// copying the scale bytes: identical bytes to the same place), so every
+// wave issues the same count per chunk.  One barrier per chunk: after each
+// wave has waited for its own copies of chunk c and for its reads of chunk
+// c - 1, the barrier makes the whole chunk visible and frees chunk c - 1's
+// slot, which the copies of chunk c + STAGES - 1 then refill.
+template <int WAVES, int STAGES, int AK>
+struct DecRowsLds {
+  static constexpr int kSeg = AK == 32 ? 4 : 8;                        // chunks per W' scale segment
+  static constexpr int kSlabsR = (STAGES - 2 + kSeg) / kSeg + 2;       // ceil((STAGES - 1) / kSeg) + 2
+  static constexpr int kSlabBytes = 32 * 8 * kSeg;
+  static constexpr int kWave = STAGES * 4096 + kSlabsR * kSlabBytes;   // a wave's weight slots and slabs
+  static constexpr int kAStage = AK * 128 + 256;                       // shared activation codes + scales
+  static constexpr int kShared0 = WAVES * kWave;
+  static constexpr int kBytes = kShared0 + STAGES * kAStage;
+  static constexpr int kAI = AK / 8;                                   // activation code copies per chunk
+  static constexpr int kAPerWave = (kAI + WAVES - 1) / WAVES;
+  static constexpr int kCopies = 4 + 1 + kAPerWave + 1;                // per wave per chunk
+};
+
+template <int WAVES, int STAGES, int AK>
+__global__ __launch_bounds__(64 * WAVES) void decode_rows_kernel(
+    const uint8_t* __restrict__ A, const uint8_t* __restrict__ As, const uint8_t* __restrict__ W,
+    const uint8_t* __restrict__ Ws, int64_t M, int64_t N, int64_t K, void* __restrict__ Y, int out_mode) {
+  static_assert(AK == 16 || AK == 32, "16 or 32 staged activation rows");
+  using L = DecRowsLds<WAVES, STAGES, AK>;
+  static_assert((STAGES - 2) * L::kCopies < 64, "vmcnt range");
+  static_assert(L::kBytes >= 32 * WAVES * 32 * 4, "the output tile must fit in the rings");
+  extern __shared__ __attribute__((aligned(16))) uint8_t dsm[];
+  constexpr int kThreads = 64 * WAVES;
+  constexpr int kRows = 32 * WAVES;
+  constexpr int kSeg = L::kSeg, kD = 2 * kSeg;
+  const int64_t KB = K >> 1, KG = K >> 5;
+  const int kc = (int)(K >> 8);
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int r32 = lane & 31;
+  const int h = lane >> 5;
+  const int64_t n0 = (int64_t)blockIdx.x * kRows;
+  const int64_t nw = n0 + 32 * wave;   // this wave's first weight row
+
+  uint8_t* ring = dsm + wave * L::kWave;
+  const uint32_t ring_addr = (uint32_t)(uintptr_t)ring;
+  const uint8_t* slabs = ring + STAGES * 4096;
+  const uint8_t* ash = dsm + L::kShared0;
+  const uint32_t ash_addr = (uint32_t)(uintptr_t)ash;
+
+  const int cb0 = 0, cb1 = kc;   // the block's chunks: the whole K range
+
+  // copy sources (rows past N or M repeat the last row; their results are not stored)
+  const uint8_t* wsrc[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int row = 8 * i + (lane >> 3);
+    const int64_t wn = nw + row < N ? nw + row : N - 1;
+    wsrc[i] = W + wn * KB + 16 * ((lane & 7) ^ (row & 7));
+  }
+  const int slab_lrow = lane / kD;
+  const int64_t slab_lofs = 4 * (lane % kD);
+  const uint8_t* asrc[L::kAPerWave];
+  int adst[L::kAPerWave];
+#pragma unroll
+  for (int j = 0; j < L::kAPerWave; ++j) {
+    const int i = (wave + j * WAVES) % L::kAI;   // activation copy instruction of this wave
+    const int row = 8 * i + (lane >> 3);
+    const int64_t am = row < M ? row : M - 1;
+    asrc[j] = A + am * KB + 16 * ((lane & 7) ^ (row & 7));
+    adst[j] = i * 1024;
+  }
+  const int64_t ams = (lane >> 1) < M ? (lane >> 1) : M - 1;
+  const uint8_t* assrc = As + ams * KG + 4 * (lane & 1);
+
+  auto issue_slab = [&](int seg, int t) {
+    const int row = t * (64 / kD) + slab_lrow;
+    const int64_t wn = nw + row < N ? nw + row : N - 1;
+    int64_t ofs = (int64_t)(cb0 + seg * kSeg) * 8 + slab_lofs;
+    if (ofs > KG - 4) ofs = KG - 4;
+    dma4(Ws + wn * KG + ofs, ring_addr + (uint32_t)(STAGES * 4096 + (seg % L::kSlabsR) * L::kSlabBytes + t * 256));
+  };
+  auto issue = [&](int c) {
+    const int slot = (c - cb0) % STAGES;
+    const int64_t co = (int64_t)c * 128, so = (int64_t)c * 8;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) dma16_nt(wsrc[i] + co, ring_addr + (uint32_t)(slot * 4096 + i * 1024));
+    issue_slab((c - cb0) / kSeg + 1, (c - cb0) % kSeg);
+    const uint32_t abase = ash_addr + (uint32_t)(slot * L::kAStage);
+#pragma unroll
+    for (int j = 0; j < L::kAPerWave; ++j) dma16(asrc[j] + co, abase + (uint32_t)adst[j]);
+    dma4(assrc + so, abase + (uint32_t)(AK * 128));
+  };
+
+  if (cb0 < cb1) {
+#pragma unroll
+    for (int t = 0; t < kSeg; ++t) issue_slab(0, t);
+  }
+#pragma unroll
+  for (int q = 0; q < STAGES - 1; ++q)
+    if (cb0 + q < cb1) issue(cb0 + q);
+
+  const int ar = r32 < M ? r32 : (int)M - 1;   // activation row of this lane's B column
+  v16f_d acc;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) acc[r] = 0.0f;
+
+  for (int c = cb0; c < cb1; ++c) {
+    // this wave's copies of chunk c have landed when at most the chunks
+    // after it (up to STAGES - 2, chunk c + STAGES - 1 not issued yet) are
+    // in flight; its reads of chunk c - 1 have returned
+    const int ahead = (cb1 - 1 - c) < (STAGES - 2) ? (cb1 - 1 - c) : (STAGES - 2);
+    wait_vmcnt_rt(ahead * L::kCopies);
+    wait_lgkmcnt0();
+    block_barrier();   // chunk c complete in LDS; chunk c - 1's slot free
+    if (c + STAGES - 1 < cb1) issue(c + STAGES - 1);
+    const int cs = c - cb0;
+    const uint8_t* st = ring + (cs % STAGES) * 4096;
+    const uint8_t* sa = ash + (cs % STAGES) * L::kAStage;
+    uint4 wa[4], xb[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) wa[j] = *reinterpret_cast<const uint4*>(st + dec_slot(r32, 2 * j + h));
+    const uint2 wsv = *reinterpret_cast<const uint2*>(slabs + ((cs / kSeg) % L::kSlabsR) * L::kSlabBytes +
+                                                      r32 * (8 * kSeg) + (cs % kSeg) * 8);
+    const uint32_t ws = gather_scales(wsv.x, wsv.y, h);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) xb[j] = *reinterpret_cast<const uint4*>(sa + dec_slot(ar, 2 * j + h));
+    const uint2 xsv = *reinterpret_cast<const uint2*>(sa + AK * 128 + ar * 8);
+    const uint32_t xs = gather_scales(xsv.x, xsv.y, h);
+    dec_mfma<0>(acc, wa, xb, ws, xs);
+    dec_mfma<1>(acc, wa, xb, ws, xs);
+    dec_mfma<2>(acc, wa, xb, ws, xs);
+    dec_mfma<3>(acc, wa, xb, ws, xs);
+  }
+
+  // ---- output: lane (r32, h), register r holds D[n = 8*(r/4) + 4*h + r%4]
+  // [m = r32] of this wave's 32 rows; through LDS ([block row n][m]) so that
+  // consecutive threads store consecutive columns of y.  Every copy has
+  // landed (the last chunk waited for all of them).
+  float* red = reinterpret_cast<float*>(dsm);
+  __syncthreads();
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const int n = 32 * wave + 8 * (r >> 2) + 4 * h + (r & 3);
+    red[n * 32 + r32] = acc[r];
+  }
+  __syncthreads();
+  if (out_mode & kOutSwiGLU) {
+    constexpr int kPairs = kRows / 2;
+    for (int idx = tid; idx < kPairs * 32; idx += kThreads) {
+      const int j = idx % kPairs, m = idx / kPairs;
+      if (m < M && n0 + 2 * j < N)
+        store_out(Y, (int64_t)m * (N >> 1) + (n0 >> 1) + j, silu_times(red[(2 * j) * 32 + m], red[(2 * j + 1) * 32 + m]),
+                  out_mode);
+    }
+  } else {
+    for (int idx = tid; idx < kRows * 32; idx += kThreads) {
+      const int n = idx % kRows, m = idx / kRows;
+      if (m < M && n0 + n < N) store_out(Y, (int64_t)m * N + n0 + n, red[n * 32 + m], out_mode);
+    }
+  }
+}
+
 // ---------------------------------------------------------------- host side
 
 // Activation kind: fused M <= 2 streams the transform through the loop;
@@ -852,8 +1025,82 @@ static hipError_t launch_decode_impl(const DecodeConfig& d, const uint8_t* A, co
 #undef MACAQ_DEC_LAUNCH
 }
 
+// More than 8 staged activation rows and no K split: decode_rows_kernel
+// (64-row blocks of 2 waves sharing each activation chunk), unless a ring
+// shape is forced (macaq_set_tuning DECODE_WAVES / DECODE_STAGES /
+// DECODE_ROWS select decode_gemm_kernel's shapes).  Measured on one box
+// against decode_gemm_kernel's 64-row blocks (each wave staging its own
+// activation, half the K range): gate/up M32 N25600 K5120 20.7-21.0 us with
+// 3 or 4 slots against 22.3 (5 slots 21.2); down-proj M32 N5120 K25600 in 3
+// K parts 21.8-24.5 us (3 to 8 slots) against 20.9, so split layers keep
+// decode_gemm_kernel.  Deeper rings were slower in both.
+constexpr int kRowsWaves = 2;
+constexpr int kRowsMaxStages = 4;
+static bool use_rows_kernel(int64_t M, int64_t N, int64_t K) {
+  return decode_ak(M, false) >= 16 && !tuning(MACAQ_TUNE_DECODE_WAVES) && !tuning(MACAQ_TUNE_DECODE_STAGES) &&
+         !tuning(MACAQ_TUNE_DECODE_ROWS) && decode_config(M, N, K, false, 2).ksplit == 1;
+}
+
+template <int AK>
+static size_t rows_lds_bytes_ak(int stages) {
+  switch (stages) {
+    case 2: return DecRowsLds<kRowsWaves, 2, AK>::kBytes;
+    case 3: return DecRowsLds<kRowsWaves, 3, AK>::kBytes;
+    default: return DecRowsLds<kRowsWaves, 4, AK>::kBytes;
+  }
+}
+static size_t rows_lds_bytes(int ak, int stages) {
+  return ak == 16 ? rows_lds_bytes_ak<16>(stages) : rows_lds_bytes_ak<32>(stages);
+}
+
+// The deepest ring of up to kRowsMaxStages slots within the LDS budget
+// (half of the CU's LDS when the blocks outnumber the CUs, so that two fit,
+// else all of it).
+struct DecRowsConfig {
+  int ak, stages;
+};
+static DecRowsConfig rows_config(int64_t M, int64_t N) {
+  DecRowsConfig r;
+  r.ak = decode_ak(M, false);
+  const int64_t blocks = ceil_div(N, 32 * kRowsWaves);
+  const size_t budget = blocks > kDecCUs ? kDecLdsMax / 2 : kDecLdsMax;
+  r.stages = kRowsMaxStages;
+  while (r.stages > 2 && rows_lds_bytes(r.ak, r.stages) > budget) --r.stages;
+  return r;
+}
+
+template <int STAGES, int AK>
+static hipError_t launch_rows_s(const uint8_t* A, const uint8_t* As, const uint8_t* W, const uint8_t* Ws, int64_t M,
+                                int64_t N, int64_t K, void* Y, int mode, hipStream_t stream) {
+  using L = DecRowsLds<kRowsWaves, STAGES, AK>;
+  static const hipError_t attr = hipFuncSetAttribute((const void*)decode_rows_kernel<kRowsWaves, STAGES, AK>,
+                                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)kDecLdsMax);
+  if (attr != hipSuccess) return attr;
+  decode_rows_kernel<kRowsWaves, STAGES, AK>
+      <<<dim3((unsigned)ceil_div(N, 32 * kRowsWaves)), dim3(64 * kRowsWaves), L::kBytes, stream>>>(A, As, W, Ws, M, N,
+                                                                                                 K, Y, mode);
+  return hipGetLastError();
+}
+
+template <int AK>
+static hipError_t launch_rows(const DecRowsConfig& r, const uint8_t* A, const uint8_t* As, const uint8_t* W,
+                              const uint8_t* Ws, int64_t M, int64_t N, int64_t K, void* Y, int mode,
+                              hipStream_t stream) {
+  switch (r.stages) {
+    case 2: return launch_rows_s<2, AK>(A, As, W, Ws, M, N, K, Y, mode, stream);
+    case 3: return launch_rows_s<3, AK>(A, As, W, Ws, M, N, K, Y, mode, stream);
+    default: return launch_rows_s<4, AK>(A, As, W, Ws, M, N, K, Y, mode, stream);
+  }
+}
+
 hipError_t launch_decode_gemm(const uint8_t* A, const uint8_t* As, const uint8_t* W, const uint8_t* Ws, int64_t M,
                               int64_t N, int64_t K, void* Y, int mode, float* part_ws, hipStream_t stream) {
+  if (use_rows_kernel(M, N, K)) {
+    const DecRowsConfig r = rows_config(M, N);
+    if (rows_lds_bytes(r.ak, r.stages) > kDecLdsMax) return hipErrorInvalidValue;
+    if (r.ak == 16) return launch_rows<16>(r, A, As, W, Ws, M, N, K, Y, mode, stream);
+    return launch_rows<32>(r, A, As, W, Ws, M, N, K, Y, mode, stream);
+  }
   const DecodeConfig d = decode_config(M, N, K, false, 2);
   switch (d.ak) {
     case 1: return launch_decode_impl<1, DecBf16>(d, A, As, nullptr, nullptr, W, Ws, M, N, K, Y, mode, part_ws, stream);

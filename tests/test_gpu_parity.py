@@ -609,6 +609,49 @@ def test_linear_one_launch(name, kw):
     _check_y(y1.cpu().numpy()[:, rows], y_ref, S)
 
 
+ROWS_SHARED = [   # (M, N, K): more than 8 staged rows, no K split -> decode_rows_kernel
+    (9, 1000, 2560),         # 16 staged rows, ragged N (last 64-row block half full)
+    (16, 20000, 512),        # 313 blocks: half-LDS budget, 2 chunks
+    (17, 640, 256 * 30),     # 32 staged rows, W' scale slabs reused many times
+    (31, 4096, 256 * 24),    # 64 blocks, whole LDS budget
+    (32, 96, 256 * 3),       # 3 chunks: a ring longer than K
+    (24, 300, 256 * 31),     # ragged N (last block 44 rows), odd chunk count
+]
+
+
+@pytest.mark.parametrize("M,N,K", ROWS_SHARED)
+@pytest.mark.parametrize("epi", ["f32", "bf16", "swiglu"])
+def test_gemm_decode_rows_kernel(M, N, K, epi):
+    """The decode GEMM above 8 rows without a K split (2-wave 64-row blocks
+    sharing each staged activation chunk): within the oracle's bound for fp32
+    y, within that bound plus one bf16 rounding for bf16 y, and SwiGLU within
+    the propagated bound; the same bits on a second call."""
+    say(f"gemm decode rows kernel M{M} N{N} K{K} {epi}")
+    assert decode_parts(M, N, K, 0) == 1
+    rng = np.random.default_rng(9100 + M * 7 + N)
+    ac = rng.integers(0, 256, (M, K // 2), dtype=np.uint8)
+    asc = rng.integers(110, 140, (M, K // 32), dtype=np.uint8)
+    wc = rng.integers(0, 256, (N, K // 2), dtype=np.uint8)
+    wsc = rng.integers(110, 140, (N, K // 32), dtype=np.uint8)
+    t = [torch.from_numpy(a).to(DEV) for a in (ac, asc, wc, wsc)]
+    assert mx.lib().macaq_gemm_workspace_bytes(M, N, K, 1) == 0
+    y_ref, S = oracle.gemm(ac, asc, wc, wsc)
+    if epi == "f32":
+        y1, y2 = mx.gemm(*t), mx.gemm(*t)
+        _check_y(y1.cpu().numpy(), y_ref, S)
+    elif epi == "bf16":
+        y1, y2 = mx.gemm(*t, out_dtype=torch.bfloat16), mx.gemm(*t, out_dtype=torch.bfloat16)
+        y = y1.float().cpu().numpy().astype(np.float64)
+        tol = RTOL * S + 2.0 ** -8 * (np.abs(y_ref) + RTOL * S)
+        assert (np.abs(y - y_ref) <= tol).all()
+    else:
+        y1, y2 = mx.gemm(*t, epilogue=mx.EPI_SWIGLU), mx.gemm(*t, epilogue=mx.EPI_SWIGLU)
+        bound = oracle.swiglu_bound(y_ref, S, RTOL)
+        err = np.abs(y1.cpu().numpy().astype(np.float64) - oracle.swiglu(y_ref))
+        assert (err <= bound).all(), f"{(err > bound).sum()} outputs beyond the bound"
+    assert torch.equal(y1, y2)
+
+
 ROWS64_GEMM = [(1, 1000, 2560), (3, 200, 2048), (12, 70, 256 * 7), (32, 1000, 2560)]
 ROWS64_LINEAR = [
     ("M1 fp32 tiny-shaped", dict(cfg=1, shape=(1, 96, 512))),
