@@ -669,13 +669,13 @@ __global__ void decode_split_reduce_kernel(const float* __restrict__ part_ws, in
   store_out(Y, i, v, out_mode);
 }
 
-// ---- decode GEMM for more than 8 activation rows, without a K split:
-// waves split rows, and share each staged activation chunk.
+// ---- decode GEMM for 3 to 32 activation rows, without a K split: waves
+// split rows, and share each staged activation chunk.
 //
-// With 16 or 32 activation rows the activation's part of a chunk is as
-// large as a 32-row tile's weights; when every wave stages its own copy
-// (waves splitting K, decode_gemm_kernel) it doubles the LDS fill per chunk
-// and halves the ring.  Here a block of WAVES waves owns 32 WAVES weight
+// With 32 activation rows the activation's part of a chunk is as large as
+// a 32-row tile's weights (with 8 rows a quarter); when every wave stages
+// its own copy (waves splitting K, decode_gemm_kernel) that adds to the LDS
+// fill per chunk and shortens the ring.  Here a block of WAVES waves owns 32 WAVES weight
 // rows, wave w the 32 rows from n0 + 32 w, and all waves walk all chunks of
 // K: the activation chunk (AK rows of codes and the 32 x 8 scale bytes) sits
 // once per ring slot in LDS shared by the waves.  Each wave's weights and W'
@@ -705,7 +705,7 @@ template <int WAVES, int STAGES, int AK>
 __global__ __launch_bounds__(64 * WAVES) void decode_rows_kernel(
     const uint8_t* __restrict__ A, const uint8_t* __restrict__ As, const uint8_t* __restrict__ W,
     const uint8_t* __restrict__ Ws, int64_t M, int64_t N, int64_t K, void* __restrict__ Y, int out_mode) {
-  static_assert(AK == 16 || AK == 32, "16 or 32 staged activation rows");
+  static_assert(AK == 8 || AK == 16 || AK == 32, "8, 16 or 32 staged activation rows");
   using L = DecRowsLds<WAVES, STAGES, AK>;
   static_assert((STAGES - 2) * L::kCopies < 64, "vmcnt range");
   static_assert(L::kBytes >= 32 * WAVES * 32 * 4, "the output tile must fit in the rings");
@@ -1025,19 +1025,20 @@ static hipError_t launch_decode_impl(const DecodeConfig& d, const uint8_t* A, co
 #undef MACAQ_DEC_LAUNCH
 }
 
-// More than 8 staged activation rows and no K split: decode_rows_kernel
-// (64-row blocks of 2 waves sharing each activation chunk), unless a ring
-// shape is forced (macaq_set_tuning DECODE_WAVES / DECODE_STAGES /
-// DECODE_ROWS select decode_gemm_kernel's shapes).  Measured on one box
-// against decode_gemm_kernel's 64-row blocks (each wave staging its own
-// activation, half the K range): gate/up M32 N25600 K5120 20.7-21.0 us with
-// 3 or 4 slots against 22.3 (5 slots 21.2); down-proj M32 N5120 K25600 in 3
-// K parts 21.8-24.5 us (3 to 8 slots) against 20.9, so split layers keep
-// decode_gemm_kernel.  Deeper rings were slower in both.
+// 3 to 32 rows (8, 16 or 32 staged activation rows) and no K split:
+// decode_rows_kernel (64-row blocks of 2 waves sharing each activation
+// chunk), unless a ring shape is forced (macaq_set_tuning DECODE_WAVES /
+// DECODE_STAGES / DECODE_ROWS select decode_gemm_kernel's shapes).  Measured
+// on one box against decode_gemm_kernel: gate/up M32 N25600 K5120 20.5 us
+// against 22.2 (64-row blocks, each wave staging its own activation over
+// half the K range; 5 slots 21.2, deeper rings slower), gate/up M8 16.0-16.2
+// against 17.0-17.2 (32-row blocks of 4 waves); down-proj M32 N5120 K25600
+// in 3 K parts 21.8-24.5 us (3 to 8 slots) against 20.9, so split layers
+// keep decode_gemm_kernel.
 constexpr int kRowsWaves = 2;
 constexpr int kRowsMaxStages = 4;
 static bool use_rows_kernel(int64_t M, int64_t N, int64_t K) {
-  return decode_ak(M, false) >= 16 && !tuning(MACAQ_TUNE_DECODE_WAVES) && !tuning(MACAQ_TUNE_DECODE_STAGES) &&
+  return decode_ak(M, false) >= 8 && !tuning(MACAQ_TUNE_DECODE_WAVES) && !tuning(MACAQ_TUNE_DECODE_STAGES) &&
          !tuning(MACAQ_TUNE_DECODE_ROWS) && decode_config(M, N, K, false, 2).ksplit == 1;
 }
 
@@ -1050,6 +1051,7 @@ static size_t rows_lds_bytes_ak(int stages) {
   }
 }
 static size_t rows_lds_bytes(int ak, int stages) {
+  if (ak == 8) return rows_lds_bytes_ak<8>(stages);
   return ak == 16 ? rows_lds_bytes_ak<16>(stages) : rows_lds_bytes_ak<32>(stages);
 }
 
@@ -1098,6 +1100,7 @@ hipError_t launch_decode_gemm(const uint8_t* A, const uint8_t* As, const uint8_t
   if (use_rows_kernel(M, N, K)) {
     const DecRowsConfig r = rows_config(M, N);
     if (rows_lds_bytes(r.ak, r.stages) > kDecLdsMax) return hipErrorInvalidValue;
+    if (r.ak == 8) return launch_rows<8>(r, A, As, W, Ws, M, N, K, Y, mode, stream);
     if (r.ak == 16) return launch_rows<16>(r, A, As, W, Ws, M, N, K, Y, mode, stream);
     return launch_rows<32>(r, A, As, W, Ws, M, N, K, Y, mode, stream);
   }

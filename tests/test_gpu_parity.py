@@ -609,7 +609,9 @@ def test_linear_one_launch(name, kw):
     _check_y(y1.cpu().numpy()[:, rows], y_ref, S)
 
 
-ROWS_SHARED = [   # (M, N, K): more than 8 staged rows, no K split -> decode_rows_kernel
+ROWS_SHARED = [   # (M, N, K): 3 to 32 rows, no K split -> decode_rows_kernel
+    (3, 2000, 2560),         # 8 staged rows (rows 3..7 repeat row 2)
+    (8, 20000, 512),         # 8 staged rows, 313 blocks
     (9, 1000, 2560),         # 16 staged rows, ragged N (last 64-row block half full)
     (16, 20000, 512),        # 313 blocks: half-LDS budget, 2 chunks
     (17, 640, 256 * 30),     # 32 staged rows, W' scale slabs reused many times
@@ -622,8 +624,8 @@ ROWS_SHARED = [   # (M, N, K): more than 8 staged rows, no K split -> decode_row
 @pytest.mark.parametrize("M,N,K", ROWS_SHARED)
 @pytest.mark.parametrize("epi", ["f32", "bf16", "swiglu"])
 def test_gemm_decode_rows_kernel(M, N, K, epi):
-    """The decode GEMM above 8 rows without a K split (2-wave 64-row blocks
-    sharing each staged activation chunk): within the oracle's bound for fp32
+    """The decode GEMM for 3 to 32 rows without a K split (2-wave 64-row
+    blocks sharing each staged activation chunk): within the oracle's bound for fp32
     y, within that bound plus one bf16 rounding for bf16 y, and SwiGLU within
     the propagated bound; the same bits on a second call."""
     say(f"gemm decode rows kernel M{M} N{N} K{K} {epi}")
