@@ -371,8 +371,10 @@ int macaq_linear_path(int64_t M, int64_t N, int64_t K, int64_t E, uint32_t flags
  * launch transform it into the workspace (the same codes and scales as
  * macaq_quant_act, stored device-coherent) and publish per-block done
  * words; the other blocks start streaming weights, wait for the words,
- * then run as on the unfused path, so y equals the unfused path's bit for
- * bit.  AUTO takes the fused path for M <= 2 and for the small layers (one
+ * then run decode_gemm_kernel's ring over the staged codes (the unfused
+ * path of an unsplit layer uses another kernel, so y may differ from it by
+ * fp32 summation order).  AUTO takes the fused path for M <= 2 and for the
+ * small layers (one
  * launch beats two there); for the other decode shapes the two launches
  * measured faster than publishing within one.
  * Requires the argument rules of macaq_quant_act and macaq_gemm and a
