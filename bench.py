@@ -96,6 +96,9 @@ def parse():
     p.add_argument("--tune", action="append", default=[], metavar="KNOB=VALUE",
                    help="override a launch shape for this run (macaq_set_tuning), e.g. GEMM_GROUP_M=8 or "
                         "ACT_SEGMENT=32; repeatable; recorded in the line's config")
+    p.add_argument("--stream-calibration", action="store_true",
+                   help="only run plain HBM streams (reads only, writes only, 4:1 and 1:1 read:write) through "
+                        "macaq_probe_stream: the achievable rate for each traffic mix")
     p.add_argument("--copy-calibration", action="store_true",
                    help="only run a plain 512 MiB device-to-device copy (5 times) so that HBM byte "
                         "counters can be scaled against a transfer of known size")
@@ -127,6 +130,65 @@ def copy_calibration():
                                            "us_per_copy": round(us, 2),
                                            "GBps_read_plus_write": round(2 * n / us / 1e3, 1),
                                            "frac_of_hbm_peak": round(2 * n / us / 1e3 / PEAK_HBM_GBPS, 4)}}))
+
+
+def stream_calibration(reps=10):
+    """macaq_probe_stream: plain HBM streams of known size with the read/write
+    mixes of the bandwidth-bound kernels: reads only (the decode GEMM's weight
+    stream), writes only, four bytes read per byte written (the online
+    transform reads about 3.8 bytes per byte of codes and scales it writes)
+    and one to one (a copy), 2 GiB read or 512 MiB written per launch, past
+    the 256 MB Infinity Cache; and 4:1 at the down-prefill transform's own
+    byte counts, each launch on the next window of the buffers.  Non-temporal
+    loads; a few grid sizes, each timed with HIP events around `reps` (or four
+    rounds of windows) launches on the launch stream."""
+    import torch
+    import mxfp4_w4a4_quantized_channel_amd as mx
+    dev = "cuda:0"
+    L = mx.lib()
+    stream = torch.cuda.current_stream(dev)
+    sp = ctypes.c_void_p(stream.cuda_stream)
+    src = torch.empty(2 << 30, dtype=torch.uint8, device=dev).fill_(3)
+    dst = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    forms = {"read only": (2 << 30, 0), "write only": (0, 512 << 20),
+             "read:write 4:1": (2 << 30, 512 << 20), "read:write 1:1": (512 << 20, 512 << 20)}
+    # the down-prefill transform's own traffic: 117.4 MB of bf16 read, 29.4 MB
+    # of codes written (4:1); consecutive launches take the next window of src
+    # and dst (17 windows), so no launch finds its bytes in the Infinity Cache
+    act_rb, act_wb = 4096 * 14336 * 2, 4096 * 14336 // 2
+    forms["read:write 4:1, down-prefill transform size"] = (act_rb, act_wb)
+    res = {}
+    for name, (rb, wb) in forms.items():
+        best = None
+        windows = min((2 << 30) // rb, (512 << 20) // wb) if 0 < rb < (512 << 20) and wb > 0 else 1
+        for blocks in (2048, 8192, 32768) if windows == 1 else (512, 1024, 2048, 4096, 8192):
+            out = torch.empty(blocks * 256, dtype=torch.int32, device=dev)
+            count = [0]
+
+            def launch():
+                w = count[0] % windows
+                count[0] += 1
+                if L.macaq_probe_stream(ctypes.c_void_p(src.data_ptr() + w * rb), rb,
+                                        ctypes.c_void_p(dst.data_ptr() + w * wb), wb,
+                                        blocks, ctypes.c_void_p(out.data_ptr()), sp) != 0:
+                    raise RuntimeError(L.macaq_last_error().decode())
+            launch()
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            n = reps if windows == 1 else 4 * windows
+            for _ in range(n):
+                launch()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            us = e0.elapsed_time(e1) / n * 1e3
+            gbps = (rb + wb) / us / 1e3
+            res[f"{name}, {blocks} blocks"] = {"us": round(us, 2), "GBps": round(gbps, 1)}
+            if best is None or gbps > best:
+                best = gbps
+        res[f"{name}, best"] = {"GBps": round(best, 1), "frac_of_hbm_peak": round(best / PEAK_HBM_GBPS, 4)}
+    print(json.dumps({"stream_calibration": res, "read_bytes": {k: v[0] for k, v in forms.items()},
+                      "write_bytes": {k: v[1] for k, v in forms.items()}, "launches": reps}), flush=True)
 
 
 def library_compare(steps):
@@ -603,6 +665,9 @@ def main():
         return
     if args.mfma_probe:
         mfma_probe()
+        return
+    if args.stream_calibration:
+        stream_calibration()
         return
     if args.library_compare:
         library_compare(min(args.steps, 100))

@@ -19,6 +19,23 @@
  * 131072 with m = 16 (4 waves per block) or 8 (8 waves per block).  Enqueued on `stream`;
  * returns MACAQ_OK or a negative status (invalid arguments are rejected on
  * the host before any launch).
+ *
+ * macaq_probe_stream: the HBM streaming rate for a given mix of reads and
+ * writes, the practical ceiling of the bandwidth-bound kernels (the online
+ * transform reads about 3.8 bytes per byte it writes).  `blocks` blocks of
+ * 256 threads stream over `src` (device, read_bytes) and `dst` (device,
+ * write_bytes), both 16-byte aligned with sizes multiples of 16, in 16-byte
+ * chunks (non-temporal loads, grid-stride loops):
+ *   write_bytes == 0: every chunk of src is read once;
+ *   read_bytes == 0:  every chunk c of dst is written with four copies of
+ *                     the 32-bit chunk index c;
+ *   otherwise read_bytes must be R * write_bytes (R a whole number) and
+ *                     chunk c of dst receives the XOR of src chunks
+ *                     c, c + n, ..., c + (R-1) n  (n = write_bytes / 16).
+ * Thread t of the grid writes to out[t] (device, blocks * 256 uint32) the
+ * XOR, folded over the four 32-bit words, of every chunk it read (reads
+ * only) or wrote (the other two forms).  Enqueued on `stream`; returns
+ * MACAQ_OK or a negative status (arguments checked on the host first).
  */
 #ifndef MACAQ_PROBE_H
 #define MACAQ_PROBE_H
@@ -30,6 +47,8 @@ extern "C" {
 #endif
 
 int macaq_probe_mfma(const void* src, int64_t blocks, int waves_per_block, int iters, float* out, void* stream);
+int macaq_probe_stream(const void* src, int64_t read_bytes, void* dst, int64_t write_bytes, int64_t blocks,
+                       uint32_t* out, void* stream);
 
 #ifdef __cplusplus
 }

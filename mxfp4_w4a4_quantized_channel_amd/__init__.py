@@ -91,6 +91,7 @@ def _load():
         "macaq_flip_refine_workspace_bytes": (sz, [i64, i64]),
         "macaq_tile_weights": (ci, [vp, vp, i64, i64, i64, vp, vp, vp]),
         "macaq_probe_mfma": (ci, [vp, i64, ci, ci, vp, vp]),
+        "macaq_probe_stream": (ci, [vp, i64, vp, i64, i64, vp, vp]),
     }
     for name, (res, args) in sig.items():
         f = getattr(L, name)

@@ -50,6 +50,8 @@ hipError_t launch_gemm_tiled(const uint8_t* A, const uint8_t* As, const int32_t*
 hipError_t launch_act_quant_tiled(const void* x, bool x_f32, const float* s, const int32_t* offsets, int E, int64_t M,
                                   int64_t K, uint8_t* codes, uint8_t* scales, hipStream_t stream);
 hipError_t launch_probe_mfma(const void* src, int64_t blocks, int waves, int iters, float* out, hipStream_t stream);
+hipError_t launch_probe_stream(const void* src, int64_t read_bytes, void* dst, int64_t write_bytes, int64_t blocks,
+                               uint32_t* out, hipStream_t stream);
 hipError_t launch_tile_weights(const uint8_t* wc, const uint8_t* ws, int64_t E, int64_t N, int64_t K, uint8_t* tc,
                                uint8_t* ts, hipStream_t stream);
 // output mode bits of the GEMM kernels (mx_common.h)
@@ -218,6 +220,23 @@ int macaq_probe_mfma(const void* src, int64_t blocks, int waves_per_block, int i
   if (iters < 1) return fail(MACAQ_ERR_INVALID_ARG, std::string(fn) + ": iters must be >= 1");
   if (int st = check_device()) return st;
   return hip_status(macaq::launch_probe_mfma(src, blocks, waves_per_block, iters, out, (hipStream_t)stream), fn);
+}
+
+int macaq_probe_stream(const void* src, int64_t read_bytes, void* dst, int64_t write_bytes, int64_t blocks,
+                       uint32_t* out, void* stream) {
+  const char* fn = "macaq_probe_stream";
+  if (read_bytes < 0 || write_bytes < 0 || read_bytes % 16 != 0 || write_bytes % 16 != 0)
+    return fail(MACAQ_ERR_INVALID_ARG, std::string(fn) + ": sizes must be non-negative multiples of 16");
+  if (read_bytes == 0 && write_bytes == 0) return fail(MACAQ_ERR_INVALID_ARG, std::string(fn) + ": nothing to stream");
+  if ((read_bytes > 0 && (src == nullptr || reinterpret_cast<uintptr_t>(src) % 16 != 0)) ||
+      (write_bytes > 0 && (dst == nullptr || reinterpret_cast<uintptr_t>(dst) % 16 != 0)))
+    return fail(MACAQ_ERR_INVALID_ARG, std::string(fn) + ": src / dst missing or not 16-byte aligned");
+  if (read_bytes > 0 && write_bytes > 0 && read_bytes % write_bytes != 0)
+    return fail(MACAQ_ERR_INVALID_ARG, std::string(fn) + ": read_bytes must be a whole multiple of write_bytes");
+  if (blocks < 1 || blocks > (int64_t(1) << 20)) return fail(MACAQ_ERR_INVALID_ARG, std::string(fn) + ": blocks out of range");
+  if (out == nullptr) return fail(MACAQ_ERR_INVALID_ARG, std::string(fn) + ": out is null");
+  if (int st = check_device()) return st;
+  return hip_status(macaq::launch_probe_stream(src, read_bytes, dst, write_bytes, blocks, out, (hipStream_t)stream), fn);
 }
 
 int macaq_set_tuning(int knob, int value) {

@@ -1,7 +1,8 @@
-// Measurement aid: MFMA throughput from registers (declared in
-// include/macaq_probe.h).  The GEMM kernels' roofline fraction is quoted
-// against the 10.1 PFLOP/s datasheet figure; this kernel shows what the
-// same block-scaled FP4 MFMA sustains on the chip with no memory traffic.
+// Measurement aids (declared in include/macaq_probe.h): MFMA throughput from
+// registers, and HBM streaming rates for a given read/write mix.  The
+// kernels' roofline fractions are quoted against the datasheet figures
+// (10.1 PFLOP/s, 8 TB/s); these kernels show what the chip sustains for the
+// same instruction with no memory traffic, and for plain streams.
 #include "mx_common.h"
 #include "macaq_probe.h"
 
@@ -53,6 +54,51 @@ __global__ __launch_bounds__(64 * WAVES) void mfma_probe_kernel(const uint4* __r
 #pragma unroll
       for (int r = 0; r < 16; ++r) sum += acc[mi][ni][r];
   out[(int64_t)blockIdx.x * blockDim.x + threadIdx.x] = sum;
+}
+
+// Streaming probe: grid-stride over 16-byte chunks, non-temporal loads.
+typedef unsigned int u32x4_p __attribute__((ext_vector_type(4)));
+
+__global__ __launch_bounds__(256) void stream_probe_kernel(const u32x4_p* __restrict__ src, int64_t nr,
+                                                           u32x4_p* __restrict__ dst, int64_t nw,
+                                                           uint32_t* __restrict__ out) {
+  const int64_t tid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  u32x4_p acc = {0u, 0u, 0u, 0u};
+  if (nw == 0) {
+    int64_t i = tid;
+    for (; i + 3 * stride < nr; i += 4 * stride) {   // four loads in flight per lane
+      const u32x4_p a = __builtin_nontemporal_load(&src[i]);
+      const u32x4_p b = __builtin_nontemporal_load(&src[i + stride]);
+      const u32x4_p c = __builtin_nontemporal_load(&src[i + 2 * stride]);
+      const u32x4_p d = __builtin_nontemporal_load(&src[i + 3 * stride]);
+      acc ^= a ^ b ^ c ^ d;
+    }
+    for (; i < nr; i += stride) acc ^= __builtin_nontemporal_load(&src[i]);
+  } else if (nr == 0) {
+    for (int64_t c = tid; c < nw; c += stride) {
+      const uint32_t v = (uint32_t)c;
+      const u32x4_p w = {v, v, v, v};
+      dst[c] = w;
+      acc ^= w;
+    }
+  } else {
+    const int64_t R = nr / nw;
+    for (int64_t c = tid; c < nw; c += stride) {
+      u32x4_p v = {0u, 0u, 0u, 0u};
+      for (int64_t k = 0; k < R; ++k) v ^= __builtin_nontemporal_load(&src[k * nw + c]);
+      dst[c] = v;
+      acc ^= v;
+    }
+  }
+  out[tid] = acc.x ^ acc.y ^ acc.z ^ acc.w;
+}
+
+hipError_t launch_probe_stream(const void* src, int64_t read_bytes, void* dst, int64_t write_bytes, int64_t blocks,
+                               uint32_t* out, hipStream_t stream) {
+  stream_probe_kernel<<<dim3((unsigned)blocks), dim3(256), 0, stream>>>(
+      static_cast<const u32x4_p*>(src), read_bytes / 16, static_cast<u32x4_p*>(dst), write_bytes / 16, out);
+  return hipGetLastError();
 }
 
 hipError_t launch_probe_mfma(const void* src, int64_t blocks, int waves, int iters, float* out, hipStream_t stream) {

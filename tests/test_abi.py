@@ -33,6 +33,24 @@ def test_probe_validation():
     assert mx.macaq_probe_mfma(A16, 256, 8, 10, A16, None) == NO_DEVICE
 
 
+def test_stream_probe_validation():
+    """The streaming probe (a measurement aid) rejects bad arguments on the
+    host: sizes not multiples of 16, nothing to stream, missing or misaligned
+    buffers, a read size that is not a whole multiple of the write size, a
+    block count out of range, a null out."""
+    mx.lib()
+    assert mx.macaq_probe_stream(A16, 100, A16, 16, 8, A16, None) == INVALID
+    assert mx.macaq_probe_stream(A16, 0, A16, 0, 8, A16, None) == INVALID
+    assert mx.macaq_probe_stream(None, 4096, None, 0, 8, A16, None) == INVALID
+    assert mx.macaq_probe_stream(A16 + 4, 4096, None, 0, 8, A16, None) == INVALID
+    assert mx.macaq_probe_stream(A16, 4096, A16 + 8, 1024, 8, A16, None) == INVALID
+    assert mx.macaq_probe_stream(A16, 4096, A16, 1536, 8, A16, None) == INVALID
+    assert mx.macaq_probe_stream(A16, 4096, A16, 1024, 0, A16, None) == INVALID
+    assert mx.macaq_probe_stream(A16, 4096, A16, 1024, 8, None, None) == INVALID
+    assert mx.macaq_probe_stream(A16, 4096, A16, 1024, 8, A16, None) == NO_DEVICE
+    assert mx.macaq_probe_stream(None, 0, A16, 1024, 8, A16, None) == NO_DEVICE
+
+
 def test_header_declares_the_boundary():
     names = declared_functions()
     for n in ["macaq_prepare_weights", "macaq_quant_act", "macaq_linear", "macaq_gemm",
