@@ -191,6 +191,66 @@ def stream_calibration(reps=10):
                       "write_bytes": {k: v[1] for k, v in forms.items()}, "launches": reps}), flush=True)
 
 
+def live_ceilings(L, sp, stream, act_read, act_us, gemm_flops, gemm_us, a_codes, w_codes):
+    """What the chip sustains for the same work, timed in the same run, next
+    to the kernels' times: a plain stream of the transform's traffic (its
+    activation bytes read, a quarter of that written: macaq_probe_stream,
+    each launch on the next window of a 2 GiB buffer, best of three grids)
+    and, for an MFMA-bound GEMM, the block-scaled FP4 MFMA alone on the
+    layer's own codes with the GEMM's MFMA count per SIMD (macaq_probe_mfma,
+    one 4-wave block per CU)."""
+    import torch
+    dev = "cuda:0"
+    res = {}
+
+    def timed(launch, n):
+        launch(0)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for i in range(n):
+            launch(i + 1)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / n * 1e3
+
+    if act_us is not None and act_read % 64 == 0 and (8 << 20) <= act_read <= (1 << 30):
+        rb, wb = act_read, act_read // 4
+        windows = max(1, min((2 << 30) // rb, (512 << 20) // wb, 64))
+        src = torch.empty(2 << 30, dtype=torch.uint8, device=dev).fill_(3)
+        dst = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+        best = None
+        for blocks in (1024, 2048, 4096):
+            out = torch.empty(blocks * 256, dtype=torch.int32, device=dev)
+
+            def launch(i, blocks=blocks, out=out):
+                w = i % windows
+                if L.macaq_probe_stream(ctypes.c_void_p(src.data_ptr() + w * rb), rb,
+                                        ctypes.c_void_p(dst.data_ptr() + w * wb), wb, blocks,
+                                        ctypes.c_void_p(out.data_ptr()), sp) != 0:
+                    raise RuntimeError(L.macaq_last_error().decode())
+            us = timed(launch, 4 * windows)
+            best = us if best is None else min(best, us)
+        del src, dst
+        res["act_plain_stream"] = {"read_bytes": rb, "write_bytes": wb, "us": round(best, 2),
+                                   "transform_frac_of_it": round(best / act_us, 4)}
+    if gemm_flops is not None:
+        per_simd = gemm_flops / 131072 / 1024
+        iters = max(1, int(round(per_simd / 16)))
+        # lane l: 64 bytes of the layer's activation codes, then 64 of its weight codes
+        ops = torch.stack([a_codes.reshape(-1)[:4096].reshape(64, 64), w_codes.reshape(-1)[:4096].reshape(64, 64)],
+                          1).reshape(-1).contiguous()
+        out = torch.empty(256 * 4 * 64, dtype=torch.float32, device=dev)
+
+        def launch(i):
+            if L.macaq_probe_mfma(ctypes.c_void_p(ops.data_ptr()), 256, 4, iters, ctypes.c_void_p(out.data_ptr()),
+                                  sp) != 0:
+                raise RuntimeError(L.macaq_last_error().decode())
+        us = timed(launch, 20)
+        res["mfma_only"] = {"mfmas_per_simd": iters * 16, "us": round(us, 2), "gemm_frac_of_it": round(us / gemm_us, 4)}
+    return res
+
+
 def library_compare(steps):
     """Our prefill GEMM next to the vendor library's MXFP4 GEMM (hipBLASLt, as
     torch._scaled_mm runs it for float4_e2m1fn_x2 operands with e8m0 block
@@ -878,6 +938,11 @@ def main():
                                "tflops": round(flops / gemm_us / 1e6, 1)}
         out["roofline"].update({"us": round(gemm_us, 2), "roofline_us": {"mfma": round(t_mfma, 2), "hbm": round(t_hbm, 2)},
                                 "traffic": traffic_record(f"{args.workload}:gemm{out_key}")})
+    if not fused:
+        mfma_bound = out["roofline"]["bound"] == "mfma"
+        ceil = live_ceilings(L, sp, stream, xb, act_us, flops if mfma_bound else None, gemm_us, a_codes, wcs[0])
+        if ceil:
+            out["ceilings"] = ceil
     if not args.no_ablation:
         # both sides row-major activation codes into the same GEMM kernel:
         # the comparison isolates the transform against the plain quantizer.
