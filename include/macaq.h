@@ -133,7 +133,12 @@ enum {
  *   MACAQ_TUNE_ACT_SEGMENT        groups per row segment of a wave of the
  *                                 activation kernel (16, 32 or 64)
  *   MACAQ_TUNE_DECODE_SPLIT       K split of the decode GEMM: the number of
- *                                 blocks per row tile (1..16; 1 = no split) */
+ *                                 blocks per row tile (1..16; 1 = no split)
+ *   MACAQ_TUNE_DECODE_POLLS       polls of the one-launch fused layer's wait
+ *                                 for the published activation before it
+ *                                 gives up: v - 1 (1..64; 1 = give up at
+ *                                 once).  For tests of the give-up path,
+ *                                 which writes NaN to every output. */
 enum {
   MACAQ_TUNE_GEMM_TILE = 0,
   MACAQ_TUNE_GEMM_GROUP_M = 1,
@@ -144,7 +149,8 @@ enum {
   MACAQ_TUNE_DECODE_ROWS = 6,
   MACAQ_TUNE_ACT_SEGMENT = 7,
   MACAQ_TUNE_DECODE_SPLIT = 8,
-  MACAQ_TUNE_COUNT = 9
+  MACAQ_TUNE_DECODE_POLLS = 9,
+  MACAQ_TUNE_COUNT = 10
 };
 
 /* Library version as major*10000 + minor*100 + patch. */
@@ -371,7 +377,12 @@ int macaq_linear_path(int64_t M, int64_t N, int64_t K, int64_t E, uint32_t flags
  * launch transform it into the workspace (the same codes and scales as
  * macaq_quant_act, stored device-coherent) and publish per-block done
  * words; the other blocks start streaming weights, wait for the words,
- * then run decode_gemm_kernel's ring over the staged codes (the unfused
+ * then run decode_gemm_kernel's ring over the staged codes (a block whose
+ * wait gives up, after about a second, writes NaN to every output it owns
+ * rather than a result of unpublished codes; such a launch may leave its
+ * done words set, which a later call's fresh value ignores but a replay of
+ * the same captured graph would not: clear the workspace before replaying
+ * a graph whose launch gave up; the unfused
  * path of an unsplit layer uses another kernel, so y may differ from it by
  * fp32 summation order).  AUTO takes the fused path for M <= 2 and for the
  * small layers (one

@@ -25,7 +25,8 @@ __all__ = [
     "hessian", "prepare_weights_hessian", "flip_refine", "flip_refine_workspace_bytes",
     "set_tuning", "linear_noalloc", "quant_act_tiled", "A_TILED", "W_TILED", "NOALLOC_SCRATCH_BYTES", "TUNE_GEMM_TILE", "TUNE_GEMM_GROUP_M",
     "TUNE_ACT_ROWS_PER_WAVE", "TUNE_ACT_SHARED_S",
-    "TUNE_DECODE_WAVES", "TUNE_DECODE_STAGES", "TUNE_DECODE_ROWS", "TUNE_ACT_SEGMENT", "TUNE_DECODE_SPLIT", "GEMM_TILES",
+    "TUNE_DECODE_WAVES", "TUNE_DECODE_STAGES", "TUNE_DECODE_ROWS", "TUNE_ACT_SEGMENT", "TUNE_DECODE_SPLIT",
+    "TUNE_DECODE_POLLS", "GEMM_TILES",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -39,7 +40,7 @@ A_TILED = 0x200   # activation codes in the tiled layout (gemm's epilogue argume
 W_TILED = 0x100   # weights in macaq_tile_weights' layout (OR into linear's flags / gemm's epilogue)
 # knobs of macaq_set_tuning (0 = the library's own choice)
 (TUNE_GEMM_TILE, TUNE_GEMM_GROUP_M, TUNE_ACT_ROWS_PER_WAVE, TUNE_ACT_SHARED_S, TUNE_DECODE_WAVES,
- TUNE_DECODE_STAGES, TUNE_DECODE_ROWS, TUNE_ACT_SEGMENT, TUNE_DECODE_SPLIT) = range(9)
+ TUNE_DECODE_STAGES, TUNE_DECODE_ROWS, TUNE_ACT_SEGMENT, TUNE_DECODE_SPLIT, TUNE_DECODE_POLLS) = range(10)
 GEMM_TILES = {"256x256": 1, "256x128": 2, "128x128": 3}   # values of TUNE_GEMM_TILE
 STATUS = {0: "ok", -1: "invalid argument", -2: "unsupported", -3: "no device", -4: "HIP error",
           -5: "workspace too small"}

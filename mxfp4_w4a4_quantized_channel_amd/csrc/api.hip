@@ -240,7 +240,7 @@ int macaq_probe_stream(const void* src, int64_t read_bytes, void* dst, int64_t w
 }
 
 int macaq_set_tuning(int knob, int value) {
-  static const int kMax[MACAQ_TUNE_COUNT] = {3, 64, 64, 2, 8, 4, 64, 64, 16};
+  static const int kMax[MACAQ_TUNE_COUNT] = {3, 64, 64, 2, 8, 4, 64, 64, 16, 64};
   if (knob < 0 || knob >= MACAQ_TUNE_COUNT)
     return fail(MACAQ_ERR_INVALID_ARG, "macaq_set_tuning: unknown knob " + std::to_string(knob));
   if (value < 0 || value > kMax[knob])

@@ -193,17 +193,20 @@ __device__ __forceinline__ void sync_store(unsigned long long* p, unsigned long 
 // polls themselves loading the memory path).  The publishing blocks are the
 // lowest block indices, which the dispatcher places first, and they wait on
 // nothing, so they are done within microseconds; the poll still gives up
-// after about a second (the result is then wrong, but the kernel ends).
-// Called by a whole wave.
+// after `max_polls` polls (about a second by default) and returns false, and
+// the block then writes NaN for every output it owns, so that a hand-over
+// that never completed shows in y instead of passing for a result.  Called
+// by a whole wave (the result is wave-uniform).
 constexpr int kPubMaxPolls = 1 << 19;
-__device__ __forceinline__ void wait_published(unsigned long long* done, unsigned long long epoch, int pubs,
-                                               int lane) {
-  for (int i = 0; i < kPubMaxPolls; ++i) {
+__device__ __forceinline__ bool wait_published(unsigned long long* done, unsigned long long epoch, int pubs,
+                                               int lane, int max_polls) {
+  for (int i = 0; i < max_polls; ++i) {
     bool ok = true;
     if (lane < pubs) ok = __hip_atomic_load(done + lane, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == epoch;
-    if (__builtin_amdgcn_ballot_w64(!ok) == 0) break;
+    if (__builtin_amdgcn_ballot_w64(!ok) == 0) return true;
     __builtin_amdgcn_s_sleep(64);
   }
+  return false;
 }
 
 // s_waitcnt vmcnt(n) for a wave-uniform n known only at run time.
@@ -286,7 +289,7 @@ __global__ __launch_bounds__(64 * WAVES) void decode_gemm_kernel(
     const void* __restrict__ x, const float* __restrict__ s,           // activations and scale (fused)
     const uint8_t* __restrict__ W, const uint8_t* __restrict__ Ws, int64_t M, int64_t N, int64_t K,
     void* __restrict__ Y, int out_mode, float* __restrict__ part_ws, int ksplit,
-    unsigned long long* sync, unsigned long long epoch, int pubs) {
+    unsigned long long* sync, unsigned long long epoch, int pubs, int max_polls) {
   static_assert(!PUB || AK >= 8, "the one-launch layer stages 8, 16 or 32 activation rows");
   constexpr int EB = dec_eb<XT>;
   using S = DecStage<AK, EB, RT>;
@@ -297,6 +300,7 @@ __global__ __launch_bounds__(64 * WAVES) void decode_gemm_kernel(
   constexpr int kThreads = 64 * WAVES;
   const int64_t n0 = (int64_t)blockIdx.x * kDecRows * RT;
   const int64_t KB = K >> 1, KG = K >> 5;
+  bool pub_ok = true;   // one-launch layer: the activation's hand-over completed (wave 0)
   const int kc = (int)(K >> 8);
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -432,7 +436,7 @@ __global__ __launch_bounds__(64 * WAVES) void decode_gemm_kernel(
 #pragma unroll
     for (int q = 0; q < kPre; ++q)
       if (c0 + q < c1) issue_w(c0 + q);
-    if (wave == 0) wait_published(sync + 16, epoch, pubs, lane);
+    if (wave == 0) pub_ok = wait_published(sync + 16, epoch, pubs, lane, max_polls);
     __syncthreads();   // (no wait for the copies in flight)
 #pragma unroll
     for (int q = 0; q < kPre; ++q)
@@ -585,12 +589,15 @@ __global__ __launch_bounds__(64 * WAVES) void decode_gemm_kernel(
   // rings and slabs can hold the partial sums.
   constexpr int kRows = 32 * RT;
   __syncthreads();
+  // one-launch layer whose wait gave up: wave 0's tile, which every output
+  // of the block (and every partial sum of a K split) adds, becomes NaN
+  const bool poisoned = PUB && !pub_ok;
 #pragma unroll
   for (int tt = 0; tt < RT; ++tt) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int n = 32 * tt + 8 * (r >> 2) + 4 * h + (r & 3);
-      red[(wave * kRows + n) * 32 + r32] = acc[tt][r];
+      red[(wave * kRows + n) * 32 + r32] = poisoned ? __builtin_nanf("") : acc[tt][r];
     }
   }
   __syncthreads();
@@ -967,6 +974,7 @@ struct PubLaunch {
   unsigned long long* sync = nullptr;
   unsigned long long epoch = 0;
   int pubs = 0;
+  int max_polls = kPubMaxPolls;
 };
 
 // Epoch of a one-launch layer: a 40-bit value unique within the process
@@ -990,7 +998,7 @@ static hipError_t launch_decode_w(const uint8_t* A, const uint8_t* As, const voi
   if (attr != hipSuccess) return attr;
   decode_gemm_kernel<WAVES, STAGES, AK, XT, RT, PUB>
       <<<dim3((unsigned)ceil_div(N, kDecRows * RT), (unsigned)ksplit), dim3(64 * WAVES), lds, stream>>>(
-          A, As, x, s, W, Ws, M, N, K, Y, mode, part_ws, ksplit, pl.sync, pl.epoch, pl.pubs);
+          A, As, x, s, W, Ws, M, N, K, Y, mode, part_ws, ksplit, pl.sync, pl.epoch, pl.pubs, pl.max_polls);
   if (ksplit > 1) {
     if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
     const int64_t outs = (mode & kOutSwiGLU) ? M * (N >> 1) : M * N;
@@ -1181,6 +1189,8 @@ static hipError_t launch_one_launch(const void* x, const float* s, const uint8_t
   pl.sync = reinterpret_cast<unsigned long long*>(ws + l.sync);
   pl.epoch = next_pub_epoch();
   pl.pubs = (int)pubs;
+  // a forced poll limit (tests of the give-up path): value v allows v - 1 polls
+  if (const int force = tuning(MACAQ_TUNE_DECODE_POLLS)) pl.max_polls = force - 1;
   const uint8_t* A = ws;
   const uint8_t* As = ws + l.scales;
   float* part_ws = d.ksplit > 1 ? reinterpret_cast<float*>(ws + l.parts) : nullptr;

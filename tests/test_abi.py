@@ -289,7 +289,8 @@ def test_set_tuning_validation_and_restore():
     choice."""
     mx.lib()
     assert mx.macaq_set_tuning(-1, 0) == INVALID
-    assert mx.macaq_set_tuning(9, 0) == INVALID
+    assert mx.macaq_set_tuning(10, 0) == INVALID
+    assert mx.macaq_set_tuning(mx.TUNE_DECODE_POLLS, 65) == INVALID
     assert mx.macaq_set_tuning(mx.TUNE_GEMM_TILE, 4) == INVALID
     assert mx.macaq_set_tuning(mx.TUNE_ACT_SHARED_S, -1) == INVALID
     assert mx.set_tuning(mx.TUNE_GEMM_TILE, 3) == 0

@@ -609,6 +609,32 @@ def test_linear_one_launch(name, kw):
     _check_y(y_two.cpu().numpy()[:, rows], y_ref, S)
 
 
+@pytest.mark.parametrize("name,kw", [ONE_LAUNCH[0], ONE_LAUNCH[5]], ids=[ONE_LAUNCH[0][0], ONE_LAUNCH[5][0]])
+def test_linear_one_launch_gives_up_loudly(name, kw, tune):
+    """The one-launch layer's wait for the published activation is bounded.
+    Forced to give up at once (MACAQ_TUNE_DECODE_POLLS = 1: no poll), every
+    block that waits writes NaN for each output it owns, so y is NaN
+    everywhere (with and without a K split) instead of a result of
+    unpublished codes; the launch still clears its done words, so the next
+    call with the default limit gives the same y as a call that never gave
+    up."""
+    say(f"linear one launch gives up {name}")
+    wl = workloads.make(**kw)
+    M, N, K = wl.M, wl.N, wl.K
+    wc, wsc = gpu_prepare(wl)
+    x, s = wl.x.to(DEV), wl.s.to(DEV)
+    ws = torch.zeros(mx.linear_workspace_bytes(M, N, K, 1, mx.PATH_FUSED), dtype=torch.uint8, device=DEV)
+    y_ok = mx.linear(x, s, wc, wsc, flags=mx.PATH_FUSED, workspace=ws)
+    tune(mx.TUNE_DECODE_POLLS, 1)
+    y_nan = mx.linear(x, s, wc, wsc, flags=mx.PATH_FUSED, workspace=ws)
+    torch.cuda.synchronize()
+    assert torch.isnan(y_nan).all()
+    tune(mx.TUNE_DECODE_POLLS, 0)
+    y_again = mx.linear(x, s, wc, wsc, flags=mx.PATH_FUSED, workspace=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(y_again, y_ok)
+
+
 ROWS_SHARED = [   # (M, N, K): 3 to 32 rows, no K split -> decode_rows_kernel
     (3, 2000, 2560),         # 8 staged rows (rows 3..7 repeat row 2)
     (8, 20000, 512),         # 8 staged rows, 313 blocks
