@@ -255,8 +255,10 @@ def library_compare(steps):
     """Our prefill GEMM next to the vendor library's MXFP4 GEMM (hipBLASLt, as
     torch._scaled_mm runs it for float4_e2m1fn_x2 operands with e8m0 block
     scales) on the same operands: the attn-proj and down-prefill layers'
-    activation codes (from macaq_quant_act) and prepared weights.  A
-    comparison leg only; nothing of the layer runs through the library.
+    activation codes (from macaq_quant_act) and prepared weights, row-major
+    as the library takes them; ours also on the tiled layouts the layer
+    itself uses (macaq_tile_weights offline, macaq_quant_act_tiled online).
+    A comparison leg only; nothing of the layer runs through the library.
 
     The library call spends longer on the host than its kernel takes on the
     GPU, so both sides are timed behind a GPU busy-wait long enough to hide
@@ -283,6 +285,13 @@ def library_compare(steps):
         y32 = torch.empty(M, N, dtype=torch.float32, device=dev)
         ours16 = lambda: mx.gemm(ac, asc, wc, wsc, out=y16, out_dtype=torch.bfloat16)
         ours32 = lambda: mx.gemm(ac, asc, wc, wsc, out=y32, out_dtype=torch.float32)
+        tc, ts = mx.tile_weights(wc, wsc)
+        atc, ats = mx.quant_act_tiled(wl.x.to(dev), s)
+        yt16 = torch.empty(M, N, dtype=torch.bfloat16, device=dev)
+        yt32 = torch.empty(M, N, dtype=torch.float32, device=dev)
+        tiled = mx.W_TILED | mx.A_TILED
+        tiled16 = lambda: mx.gemm(atc, ats, tc, ts, out=yt16, out_dtype=torch.bfloat16, epilogue=tiled, M=M)
+        tiled32 = lambda: mx.gemm(atc, ats, tc, ts, out=yt32, out_dtype=torch.float32, epilogue=tiled, M=M)
         lib16 = lambda: torch._scaled_mm(a4, w4.t(), scale_a=sa, scale_b=sw, out_dtype=torch.bfloat16)
 
         def gpu_us(fn):
@@ -306,20 +315,25 @@ def library_compare(steps):
         ours32()
         y_lib = lib16()
         ours16()
+        tiled32()
         torch.cuda.synchronize()
         rel = ((y_lib.float() - y32).abs() / y32.abs().clamp_min(1e-30))
-        t = {k: [] for k in ("ours_bf16", "library_bf16", "ours_fp32")}
+        t = {k: [] for k in ("ours_bf16", "library_bf16", "ours_fp32", "ours_tiled_bf16", "ours_tiled_fp32")}
         for _ in range(3):   # interleaved, to share clock and thermal conditions
             t["ours_bf16"].append(gpu_us(ours16))
             t["library_bf16"].append(gpu_us(lib16))
             t["ours_fp32"].append(gpu_us(ours32))
+            t["ours_tiled_bf16"].append(gpu_us(tiled16))
+            t["ours_tiled_fp32"].append(gpu_us(tiled32))
         flops = 2.0 * M * N * K
         med = {k: sorted(v)[1] for k, v in t.items()}
         rows.append({"workload": desc, "M": M, "N": N, "K": K,
                      **{f"{k}_us": round(v, 2) for k, v in med.items()},
                      **{f"{k}_tflops": round(flops / v / 1e6, 1) for k, v in med.items()},
                      "library_over_ours_bf16": round(med["library_bf16"] / med["ours_bf16"], 3),
+                     "library_over_ours_tiled_bf16": round(med["library_bf16"] / med["ours_tiled_bf16"], 3),
                      "agreement": {"ours_bf16_is_rne_of_ours_fp32": bool(torch.equal(y16, y32.to(torch.bfloat16))),
+                                   "ours_tiled_fp32_equal_to_ours_fp32": bool(torch.equal(yt32, y32)),
                                    "library_max_rel_diff_vs_ours_fp32": round(float(rel.max()), 5),
                                    "library_bf16_equal_to_ours_bf16": round(float((y_lib == y16).float().mean()), 4)}})
     print(json.dumps({"library_compare": rows, "library": "hipBLASLt via torch._scaled_mm "
