@@ -191,6 +191,22 @@ def stream_calibration(reps=10):
                       "write_bytes": {k: v[1] for k, v in forms.items()}, "launches": reps}), flush=True)
 
 
+STREAM_SRC_BYTES, STREAM_DST_BYTES = 2 << 30, 512 << 20   # the live ceilings' stream buffers
+
+
+def stream_windows(read_bytes, write_bytes, cap=64):
+    """Windows of the stream buffers for a transform-sized plain stream: the
+    number of disjoint (read_bytes, write_bytes) windows that fit in both
+    buffers, at most `cap`, or 0 when the stream is too small (< 8 MiB read)
+    or too large (> 1 GiB) to measure this way, or its sizes do not suit
+    macaq_probe_stream (multiples of 16, reads a whole multiple of writes)."""
+    if not ((8 << 20) <= read_bytes <= (1 << 30)) or write_bytes <= 0:
+        return 0
+    if read_bytes % 16 or write_bytes % 16 or read_bytes % write_bytes:
+        return 0
+    return max(1, min(STREAM_SRC_BYTES // read_bytes, STREAM_DST_BYTES // write_bytes, cap))
+
+
 def live_ceilings(L, sp, stream, act_read, act_us, gemm_flops, gemm_us, a_codes, w_codes):
     """What the chip sustains for the same work, timed in the same run, next
     to the kernels' times: a plain stream of the transform's traffic (its
@@ -214,11 +230,11 @@ def live_ceilings(L, sp, stream, act_read, act_us, gemm_flops, gemm_us, a_codes,
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) / n * 1e3
 
-    if act_us is not None and act_read % 64 == 0 and (8 << 20) <= act_read <= (1 << 30):
+    windows = stream_windows(act_read, act_read // 4) if act_us is not None and act_read % 64 == 0 else 0
+    if windows:
         rb, wb = act_read, act_read // 4
-        windows = max(1, min((2 << 30) // rb, (512 << 20) // wb, 64))
-        src = torch.empty(2 << 30, dtype=torch.uint8, device=dev).fill_(3)
-        dst = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+        src = torch.empty(STREAM_SRC_BYTES, dtype=torch.uint8, device=dev).fill_(3)
+        dst = torch.empty(STREAM_DST_BYTES, dtype=torch.uint8, device=dev)
         best = None
         for blocks in (1024, 2048, 4096):
             out = torch.empty(blocks * 256, dtype=torch.int32, device=dev)

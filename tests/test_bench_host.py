@@ -42,3 +42,19 @@ def test_committed_traffic_records_are_well_formed():
         assert os.path.exists(os.path.join(ROOT, "profiles", rec["summary"])), key
         for s in rec["sources"]:
             assert os.path.exists(os.path.join(ROOT, s)), (key, s)
+
+
+def test_stream_windows_stay_inside_the_buffers():
+    """The live ceilings' plain stream takes launch w's bytes at offset
+    w * size of each buffer: every window of every workload's transform
+    stays inside both buffers, and streams outside the measured range (under
+    8 MiB, over 1 GiB, sizes the probe refuses) get no windows."""
+    act_reads = [4096 * 14336 * 2, 2048 * 4096 * 2, 8192 * 3072 * 2, 8 << 20, 1 << 30, 3 * (8 << 20) + 64]
+    for rb in act_reads:
+        wb = rb // 4
+        n = bench.stream_windows(rb, wb)
+        assert 1 <= n <= 64, rb
+        assert n * rb <= bench.STREAM_SRC_BYTES and n * wb <= bench.STREAM_DST_BYTES, rb
+    for rb, wb in [(8192 * 2 * 8, 8192 * 4), ((1 << 30) + 64, 1 << 28), (0, 0), (16 << 20, 0),
+                   ((16 << 20) + 8, (4 << 20) + 2), (16 << 20, 3 << 20)]:
+        assert bench.stream_windows(rb, wb) == 0, (rb, wb)
